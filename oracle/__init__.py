@@ -1,0 +1,170 @@
+"""CPU oracle for the DSA lightning-indexer selector (DSA, MISA, HISA).
+
+TEST INFRASTRUCTURE ONLY.  The plain fp64 C definition lives in ``oracle.c``;
+this module compiles it with gcc (a second or so) and wraps it for numpy.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import it.  It shares no code with the HIP library and never
+imports it.
+
+Every function takes the seeded host arrays directly: ``q`` as uint16 bf16 bit
+patterns ``[Bt, T, H, d]``, ``w`` float32 ``[Bt, T, H]``, ``K`` uint16
+``[Bt, L, d]``.  Outputs per evaluated row are sorted by (score desc, index
+asc) and padded with -1 / -inf.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so next to its source (plain gcc, -O2, pthreads)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-Wall",
+             "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("K", ctypes.c_void_p),
+                ("Bt", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("causal_offset", ctypes.c_int32)]
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        _lib.oracle_dsa.argtypes = [P, i, P, i, P, P, P, i]
+        _lib.oracle_misa.argtypes = [P, i, i, i, i, P, i, P, P, P, P, P, P, P, P, i]
+        _lib.oracle_hisa.argtypes = [P, i, i, i, P, i, P, P, P, P, P, i]
+        _lib.oracle_pool.argtypes = [P, i, i, i, i, P]
+        for f in (_lib.oracle_dsa, _lib.oracle_misa, _lib.oracle_hisa, _lib.oracle_pool):
+            f.restype = ctypes.c_int
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Problem:
+    """Holds contiguous copies of (q, w, K) and the causal offset."""
+
+    def __init__(self, q, w, K, causal_offset):
+        self.q = np.ascontiguousarray(q, dtype=np.uint16)
+        self.w = np.ascontiguousarray(w, dtype=np.float32)
+        self.K = np.ascontiguousarray(K, dtype=np.uint16)
+        Bt, T, H, d = self.q.shape
+        assert self.w.shape == (Bt, T, H), self.w.shape
+        assert self.K.shape[0] == Bt and self.K.shape[2] == d, self.K.shape
+        self.Bt, self.T, self.H, self.d = Bt, T, H, d
+        self.L = self.K.shape[1]
+        self.offset = int(causal_offset)
+        self._c = _Problem(_ptr(self.q), _ptr(self.w), _ptr(self.K), Bt, T, H, d, self.L,
+                           self.offset)
+
+    def rows(self, rows):
+        if rows is None:
+            return None, self.Bt * self.T
+        r = np.ascontiguousarray(rows, dtype=np.int32)
+        assert r.ndim == 1 and (r.size == 0 or (r.min() >= 0 and r.max() < self.Bt * self.T))
+        return r, int(r.size)
+
+
+def _threads(nthreads):
+    if nthreads:
+        return int(nthreads)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError("%s rejected its arguments (code %d)" % (name, rc))
+
+
+def dsa(prob: Problem, topk: int, rows=None, want_rowscore=False, nthreads=0):
+    """DSA score + causal mask + token top-k.  Returns (idx, score[, rowscore])."""
+    lib = _load()
+    r, n = prob.rows(rows)
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    rs = np.empty((n, prob.L), np.float64) if want_rowscore else None
+    _check(lib.oracle_dsa(ctypes.byref(prob._c), topk, _ptr(r), n, _ptr(idx), _ptr(sc),
+                          _ptr(rs), _threads(nthreads)), "oracle_dsa")
+    return (idx, sc, rs) if want_rowscore else (idx, sc)
+
+
+def misa(prob: Problem, topk: int, B: int, h: int, kprime: int = 0, rows=None,
+         override_heads=None, override_pool=None, want_hatrow=False, nthreads=0):
+    """MISA / MISA-dagger.  Returns a dict with idx, score, heads, E, pool, hatrow."""
+    lib = _load()
+    r, n = prob.rows(rows)
+    oh = None if override_heads is None else np.ascontiguousarray(override_heads, np.int32)
+    op = None if override_pool is None else np.ascontiguousarray(override_pool, np.int32)
+    if oh is not None:
+        assert oh.shape == (n, h)
+    if op is not None:
+        assert kprime > 0 and op.shape == (n, kprime)
+    out = {
+        "idx": np.empty((n, topk), np.int32),
+        "score": np.empty((n, topk), np.float64),
+        "heads": np.empty((n, h), np.int32),
+        "E": np.empty((n, prob.H), np.float64),
+        "pool": np.empty((n, kprime), np.int32) if kprime else None,
+        "hatrow": np.empty((n, prob.L), np.float64) if want_hatrow else None,
+    }
+    _check(lib.oracle_misa(ctypes.byref(prob._c), topk, B, h, kprime, _ptr(r), n, _ptr(oh),
+                           _ptr(op), _ptr(out["heads"]), _ptr(out["E"]), _ptr(out["pool"]),
+                           _ptr(out["hatrow"]), _ptr(out["idx"]), _ptr(out["score"]),
+                           _threads(nthreads)), "oracle_misa")
+    return out
+
+
+def hisa(prob: Problem, topk: int, b: int, r: int, rows=None, override_blocks=None,
+         nthreads=0):
+    """HISA coarse (blocks) + fine (tokens).  Returns a dict with idx, score, blocks, J."""
+    lib = _load()
+    rr, n = prob.rows(rows)
+    ob = None if override_blocks is None else np.ascontiguousarray(override_blocks, np.int32)
+    if ob is not None:
+        assert ob.shape == (n, r)
+    nbmax = (prob.L + b - 1) // b
+    out = {
+        "idx": np.empty((n, topk), np.int32),
+        "score": np.empty((n, topk), np.float64),
+        "blocks": np.empty((n, r), np.int32),
+        "J": np.empty((n, nbmax), np.float64),
+    }
+    _check(lib.oracle_hisa(ctypes.byref(prob._c), topk, b, r, _ptr(rr), n, _ptr(ob),
+                           _ptr(out["blocks"]), _ptr(out["J"]), _ptr(out["idx"]),
+                           _ptr(out["score"]), _threads(nthreads)), "oracle_hisa")
+    return out
+
+
+def pool(K, block: int):
+    """Block means of K [Bt, L, d] (bf16 bits) -> float64 [Bt, ceil(L/block), d]."""
+    lib = _load()
+    K = np.ascontiguousarray(K, np.uint16)
+    Bt, L, d = K.shape
+    nb = (L + block - 1) // block
+    out = np.empty((Bt, nb, d), np.float64)
+    _check(lib.oracle_pool(_ptr(K), Bt, L, d, block, _ptr(out)), "oracle_pool")
+    return out

@@ -1,0 +1,67 @@
+/*
+ * CPU oracle for the DSA lightning-indexer selector (DSA, MISA, HISA).
+ *
+ * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg; never by the product path.  It shares no code
+ * with the HIP library.  All arithmetic is fp64; see oracle.c for the
+ * definitions and the pages each one follows.
+ *
+ * Row numbering: a "row" is a flat query row id b*T + i of a problem; its
+ * absolute position is t = causal_offset + i and its legal keys are s <= t.
+ * Every output row holds the selected indices sorted by (score desc, index
+ * asc), padded with -1 / -inf up to topk.
+ */
+#ifndef SA_ORACLE_H
+#define SA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ENOMEM (-2)
+
+typedef struct {
+    const uint16_t* q;  /* [Bt, T, H, d] bf16 bit patterns */
+    const float* w;     /* [Bt, T, H] */
+    const uint16_t* K;  /* [Bt, L, d] bf16 bit patterns, one shared key head */
+    int32_t Bt, T, H, d, L;
+    int32_t causal_offset; /* absolute position of row 0 of each sequence */
+} oracle_problem;
+
+/* rows: flat row ids to evaluate (NULL = every row, nrows ignored).
+ * Outputs are indexed by the position in `rows`.
+ * out_rowscore (nullable): [nrows, L] full score row, NaN past t. */
+int oracle_dsa(const oracle_problem* p, int topk, const int32_t* rows, int nrows,
+               int32_t* out_idx, double* out_score, double* out_rowscore, int nthreads);
+
+/* MISA (kprime == 0) or MISA-dagger (kprime >= topk).
+ * override_heads [nrows, h] / override_pool [nrows, kprime] (nullable, -1 entries
+ * skipped) replace the oracle's own discrete choice, for staged comparison.
+ * out_E [nrows, H], out_heads [nrows, h] (ascending), out_pool [nrows, kprime],
+ * out_hatrow [nrows, L] (routed score row, NaN past t): all nullable.
+ * out_score is the routed score for kprime == 0, the full score otherwise. */
+int oracle_misa(const oracle_problem* p, int topk, int B, int h, int kprime,
+                const int32_t* rows, int nrows, const int32_t* override_heads,
+                const int32_t* override_pool, int32_t* out_heads, double* out_E,
+                int32_t* out_pool, double* out_hatrow, int32_t* out_idx, double* out_score,
+                int nthreads);
+
+/* HISA.  override_blocks [nrows, r] (nullable, -1 skipped); out_blocks
+ * [nrows, r] in selection order, -1 padded; out_J [nrows, ceil(L/b)] block
+ * scores, NaN for blocks past t.  Rejects r*b < topk. */
+int oracle_hisa(const oracle_problem* p, int topk, int b, int r, const int32_t* rows,
+                int nrows, const int32_t* override_blocks, int32_t* out_blocks, double* out_J,
+                int32_t* out_idx, double* out_score, int nthreads);
+
+/* Means of consecutive blocks of `block` keys (last block truncated at L):
+ * out [Bt, ceil(L/block), d]. */
+int oracle_pool(const uint16_t* K, int Bt, int L, int d, int block, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif
