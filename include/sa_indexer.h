@@ -1,0 +1,172 @@
+/*
+ * sa_indexer.h -- C ABI of the MI355X (gfx950) DSA lightning-indexer selector.
+ *
+ * What it computes.  For a query row at absolute position t, every causal
+ * prefix token s <= t gets the indexer score
+ *
+ *     I[t,s] = sum_j w[t,j] * max(q[t,j] . k[s], 0)          (j < H, one shared key head)
+ *
+ * and the row keeps the token-level top-k (PaperTrace, "2.2.2 MISA, LISA and
+ * ResMiSA", section 1 and the two-head example of section 3.1; the
+ * Index -> Select -> Attend pipeline of the blog "The new bottleneck of
+ * sparse attention").  Two accelerations share the interface:
+ *   - MISA (summary page "MISA: Mixture of Indexer Sparse Attention",
+ *     method steps 1-6): block-pooled router picks h of the H heads per
+ *     query, tokens are scored with those heads only; MISA-dagger keeps a
+ *     k' pool and reranks it with all heads.
+ *   - HISA (PaperTrace section 2.1; blog "Route 1: HISA"): block
+ *     representatives are scored, r blocks are kept, their tokens are
+ *     rescored exactly, token top-k.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE memory owned by the caller, row-major
+ *     and contiguous; nothing is retained after the call returns.
+ *   - q    : bf16 bit patterns [batch, T, H, d]
+ *     w    : fp32 [batch, T, H]
+ *     keys : bf16 bit patterns [batch, L, d]    (one shared key head)
+ *   - d must be 128.  1 <= H <= 64.
+ *   - Query row i of a sequence sits at absolute position
+ *     t = causal_offset + i; its legal keys are 0..t (0 <= causal_offset,
+ *     causal_offset + T <= L).  Decode: T = 1, causal_offset = L - 1.
+ *   - Outputs out_idx [batch, T, topk] int32 and out_score [batch, T, topk]
+ *     fp32 hold, per row, the SET of the min(topk, t+1) selected positions
+ *     (order unspecified) and the score each was ranked by; unused slots are
+ *     -1 / -inf.  out_score may be NULL.  Among exactly equal scores the lower
+ *     position is kept.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream); outputs are valid once the stream has reached the call.
+ *   - The library allocates no device memory: each call takes a workspace
+ *     `ws` of at least the size its *_ws function reports (any alignment is
+ *     accepted; 256 B is recommended).  Workspace contents need no
+ *     initialisation and are clobbered.
+ *   - Inputs must be finite; NaN / inf scores give unspecified selections.
+ *   - Return value: SA_OK or a negative SA_E* code; sa_last_error() then
+ *     returns a message for the calling thread.  On error nothing has been
+ *     launched, except SA_EHIP, which reports a failed launch.
+ */
+#ifndef SA_INDEXER_H
+#define SA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_OK 0
+#define SA_EINVAL (-1)       /* bad argument: shape, budget, NULL pointer */
+#define SA_EUNSUPPORTED (-2) /* valid but not implemented: d != 128, H > 64 */
+#define SA_EWORKSPACE (-3)   /* ws_bytes smaller than the *_ws size */
+#define SA_EHIP (-4)         /* HIP launch failure */
+
+typedef struct sa_shape {
+    int32_t batch;         /* sequences */
+    int32_t T;             /* query rows per sequence */
+    int32_t H;             /* indexer heads H_I */
+    int32_t d;             /* indexer head dim, must be 128 */
+    int32_t L;             /* keys per sequence */
+    int32_t causal_offset; /* absolute position of query row 0 */
+    int32_t topk;          /* k >= 1 */
+} sa_shape;
+
+/* ---------------------------------------------------------------- DSA */
+
+/* Workspace bytes for indexer_score_topk on this shape. */
+int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes);
+
+/* DSA lightning indexer: score every causal prefix token with all H heads,
+ * keep the top-k (PaperTrace section 1; section 2.2 asks for score, causal
+ * mask and top-k fused so that no n^2 score matrix is written).
+ * Rows with T >= 16 per sequence take the fused prefill kernel (scores never
+ * leave the chip; survivors of a running per-row threshold are kept);
+ * smaller T take the decode scan, which writes one O(L) score row per query
+ * into the workspace. */
+int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
+                       const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- pooling */
+
+/* Block means of the keys, the cache-side state MISA (B = 1024) and HISA
+ * (b = 128) score against.  Block m covers keys [m*block, min((m+1)*block, L)).
+ * out: [batch, ceil(L/block), 2, d] bf16 bit patterns; per block the fp32
+ * mean is stored as hi = bf16(mean) followed by lo = bf16(mean - hi), so
+ * hi + lo carries the mean to about 2^-16 relative.  */
+int sa_pool_blocks(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, int32_t block,
+                   uint16_t* out, void* stream);
+
+/* Both pools in one pass over the keys: `large` must be a multiple of
+ * `small`; outputs as sa_pool_blocks for each block size. */
+int sa_pool_blocks2(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, int32_t small,
+                    int32_t large, uint16_t* out_small, uint16_t* out_large, void* stream);
+
+/* --------------------------------------------------------------- MISA */
+
+/* Workspace bytes for misa_route.  pooled_given: whether `pooled` will be
+ * passed (non-NULL) to misa_route. */
+int misa_route_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
+                  int32_t pooled_given, size_t* ws_bytes);
+
+/* MISA routed indexer ("MISA" summary page, method steps 1-6).
+ *   block_B  pooling block B (e.g. 1024); a block's pooled key is the mean
+ *            of its legal keys.
+ *   h        active heads per query, 1 <= h <= H.  Router:
+ *            A[j,m] = w_j * ReLU(q_j . pooled_m), E_j = mean_m |A[j,m]| over
+ *            the blocks that intersect [0, t]; the h largest E are routed
+ *            (ties -> lower head).
+ *   k_prime  0: one stage -- top-k of the routed score
+ *            Ihat[s] = sum_{j routed} w_j ReLU(q_j . k_s); out_score = Ihat.
+ *            >= topk: MISA-dagger -- top-k' by Ihat, rescored with all H
+ *            heads, top-k of that; out_score = I.
+ *   pooled   NULL (pool inside the call) or sa_pool_blocks(keys, ..., B)
+ *            output for these keys.
+ *   out_heads [batch, T, h] routed heads, ascending (nullable).
+ *   out_pool  [batch, T, k_prime] the k' pool, -1 padded (nullable; only for
+ *             k_prime > 0). */
+int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+               int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
+               int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------------------------------- HISA */
+
+/* Workspace bytes for hisa_coarse_fine.  reps_given: whether `reps` will be
+ * passed. */
+int hisa_coarse_fine_ws(const sa_shape* s, int32_t block_b, int32_t r, int32_t reps_given,
+                        size_t* ws_bytes);
+
+/* HISA block-then-token search (PaperTrace section 2.1; blog "Route 1:
+ * HISA").  Block representatives (means of block_b keys; a block cut by the
+ * causal bound is the mean of its legal keys) are scored with the full
+ * indexer formula; the min(r, #legal blocks) best blocks are kept (ties ->
+ * lower block); their legal tokens are rescored exactly and the token top-k
+ * is returned with out_score = I.  Requires r * block_b >= topk (PaperTrace
+ * section 2.3), else SA_EINVAL.
+ *   reps       NULL or sa_pool_blocks(keys, ..., block_b) output.
+ *   out_blocks [batch, T, r] kept blocks, -1 padded (nullable). */
+int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
+                     const sa_shape* s, int32_t block_b, int32_t r, const uint16_t* reps,
+                     int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------ diagnostics */
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* sa_last_error(void);
+
+/* Per-kernel timing with HIP events recorded on the launch stream around
+ * every kernel this library launches.  enable(1) resets the counters and
+ * starts recording; enable(0) stops.  sa_profile_read synchronises the
+ * recorded events and returns the summed duration and launch count of
+ * kernel `id` (0 <= id < sa_kernel_count()). */
+int sa_profile_enable(int32_t on);
+int sa_profile_read(int32_t id, double* total_ms, int64_t* launches);
+int32_t sa_kernel_count(void);
+const char* sa_kernel_name(int32_t id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,639 @@
+// C ABI of the gfx950 indexer library: argument validation, workspace
+// planning, kernel sequencing and the optional per-kernel event timing.
+// The operations and their sources are described in include/sa_indexer.h.
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/sa_indexer.h"
+#include "sa_common.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+    return fail(SA_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// ------------------------------------------------------------ profiling
+
+struct ProfRec {
+    int kid;
+    hipEvent_t start, stop;
+};
+
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_free_events;
+double g_ms[sa::K_COUNT];
+long long g_launches[sa::K_COUNT];
+int g_open = -1;  // index of the record awaiting its stop event
+
+hipEvent_t take_event() {
+    if (!g_free_events.empty()) {
+        hipEvent_t e = g_free_events.back();
+        g_free_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Move finished records into the totals (synchronises on each stop event).
+void drain_records() {
+    for (auto& r : g_recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.stop) == hipSuccess &&
+            hipEventElapsedTime(&ms, r.start, r.stop) == hipSuccess) {
+            g_ms[r.kid] += ms;
+            g_launches[r.kid] += 1;
+        }
+        g_free_events.push_back(r.start);
+        g_free_events.push_back(r.stop);
+    }
+    g_recs.clear();
+}
+
+const char* kKernelNames[sa::K_COUNT] = {
+    "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
+    "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused"};
+
+// ------------------------------------------------------------ workspace
+
+struct Carve {
+    char* base;
+    size_t off = 0;
+    explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+    template <class T>
+    T* take(size_t count) {
+        off = (off + 255) & ~size_t(255);
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+// ------------------------------------------------------------ validation
+
+int check_shape(const sa_shape* s) {
+    if (!s) return fail(SA_EINVAL, "shape is NULL");
+    if (s->batch < 1 || s->T < 1 || s->H < 1 || s->L < 1 || s->topk < 1)
+        return fail(SA_EINVAL, "batch, T, H, L and topk must be >= 1");
+    if (s->d != sa::kD) return fail(SA_EUNSUPPORTED, "d must be 128");
+    if (s->H > sa::kMaxH) return fail(SA_EUNSUPPORTED, "H must be <= 64");
+    if (s->causal_offset < 0 || (long long)s->causal_offset + s->T > s->L)
+        return fail(SA_EINVAL, "need 0 <= causal_offset and causal_offset + T <= L");
+    if ((long long)s->batch * s->T > (1LL << 30) || (long long)s->L > (1LL << 30))
+        return fail(SA_EUNSUPPORTED, "rows or L too large");
+    return SA_OK;
+}
+
+int check_ptrs(const void* q, const void* w, const void* k, const void* out_idx) {
+    if (!q || !w || !k || !out_idx) return fail(SA_EINVAL, "q, w, keys and out_idx must be non-NULL");
+    return SA_OK;
+}
+
+// Scan chunk: aim for about 1024 workgroups over all rows.
+int scan_chunk(long long rows, int maxn) {
+    long long per_row = (1024 + rows - 1) / rows;
+    long long c = (maxn + per_row - 1) / per_row;
+    c = ((c + 127) / 128) * 128;
+    if (c < 128) c = 128;
+    if (c > 8192) c = 8192;
+    return (int)c;
+}
+
+constexpr int kPrefillMinT = 16;
+
+// Rows whose last legal block is cut by the causal bound need a tail rep.
+bool any_partial(const sa_shape* s, int block) {
+    for (int i = 0; i < s->T; ++i) {
+        const long long t = (long long)s->causal_offset + i;
+        const long long last = std::min<long long>((t / block + 1) * (long long)block, s->L) - 1;
+        if (last > t) return true;
+    }
+    return false;
+}
+
+// ---------------------------------------------------------------- DSA
+
+struct DsaPlan {
+    bool prefill;
+    float* scores;
+    uint32_t* hist;
+    int* counters;
+    unsigned long long* cand;
+    float* surv_score;
+    int32_t* surv_idx;
+    int32_t* surv_count;
+    size_t bytes;
+};
+
+DsaPlan plan_dsa(const sa_shape* s, void* ws) {
+    DsaPlan p{};
+    Carve cv(ws);
+    const long long rows = (long long)s->batch * s->T;
+    const long long maxn = (long long)s->causal_offset + s->T;
+    p.prefill = s->T >= kPrefillMinT;
+    if (p.prefill) {
+        p.surv_score = cv.take<float>(rows * maxn);
+        p.surv_idx = cv.take<int32_t>(rows * maxn);
+        p.surv_count = cv.take<int32_t>(rows);
+    } else {
+        p.scores = cv.take<float>(rows * s->L);
+        p.hist = cv.take<uint32_t>(rows * (sa::kHist0Bins + 2));
+        p.counters = reinterpret_cast<int*>(p.hist ? p.hist + rows * sa::kHist0Bins : nullptr);
+        p.cand = cv.take<unsigned long long>(rows * maxn);
+    }
+    p.bytes = cv.off + 256;
+    return p;
+}
+
+// Decode-style path: score rows (+ first-digit histogram), filter, finish.
+hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* keys,
+                          const sa_shape* s, const int32_t* heads, int hsel, float* scores,
+                          uint32_t* hist, int* counters, unsigned long long* cand, int k,
+                          int32_t* out_idx, float* out_score, hipStream_t st) {
+    const long long rows = (long long)s->batch * s->T;
+    const int maxn = s->causal_offset + s->T;
+    hipError_t e = sa::launch_fill_u32(hist, rows * (sa::kHist0Bins + 2), 0u, st);
+    if (e != hipSuccess) return e;
+    sa::ScanArgs a{};
+    a.q = q;
+    a.w = w;
+    a.keys = keys;
+    a.seq_stride = (long long)s->L * sa::kD;
+    a.heads = heads;
+    a.hsel = hsel;
+    a.T = s->T;
+    a.H = s->H;
+    a.offset = s->causal_offset;
+    a.len_div = 1;
+    a.len_cap = s->L;
+    a.chunk = scan_chunk(rows, maxn);
+    a.scores = scores;
+    a.score_stride = s->L;
+    a.hist = hist;
+    const int nht = ((heads ? hsel : s->H) + 15) / 16;
+    e = sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
+    if (e != hipSuccess) return e;
+    sa::TopkArgs t{};
+    t.dense = scores;
+    t.dense_stride = s->L;
+    t.T = s->T;
+    t.offset = s->causal_offset;
+    t.len_div = 1;
+    t.len_cap = s->L;
+    t.hist0 = hist;
+    t.k = k;
+    t.out_idx = out_idx;
+    t.out_score = out_score;
+    t.out_stride = k;
+    t.cand_cap = maxn;
+    return sa::launch_topk_dense_filtered(t, (int)rows, maxn, counters, cand, st);
+}
+
+hipError_t run_list_topk(const float* ls, const int32_t* li, long long stride,
+                         const int32_t* counts, int cap, int rows, int k, int32_t* out_idx,
+                         float* out_score, hipStream_t st) {
+    sa::TopkArgs t{};
+    t.list_score = ls;
+    t.list_idx = li;
+    t.list_stride = stride;
+    t.list_count = counts;
+    t.list_cap = cap;
+    t.k = k;
+    t.out_idx = out_idx;
+    t.out_score = out_score;
+    t.out_stride = k;
+    return sa::launch_topk(t, rows, st);
+}
+
+// ---------------------------------------------------------------- MISA
+
+struct MisaPlan {
+    uint16_t* pooled;
+    uint16_t* tail;
+    uint8_t* flag;
+    int32_t* heads;
+    float* scores;
+    uint32_t* hist;
+    int* counters;
+    unsigned long long* cand;
+    int32_t* pool_idx;
+    float* list_score;
+    int32_t* list_idx;
+    size_t bytes;
+};
+
+MisaPlan plan_misa(const sa_shape* s, int B, int h, int kp, bool pooled_given, bool partial,
+                   void* ws) {
+    MisaPlan p{};
+    Carve cv(ws);
+    const long long rows = (long long)s->batch * s->T;
+    const long long maxn = (long long)s->causal_offset + s->T;
+    const long long nblk = (s->L + B - 1) / B;
+    if (!pooled_given) p.pooled = cv.take<uint16_t>(s->batch * nblk * 2 * sa::kD);
+    if (partial) {
+        p.tail = cv.take<uint16_t>(rows * 2 * sa::kD);
+        p.flag = cv.take<uint8_t>(rows);
+    }
+    p.heads = cv.take<int32_t>(rows * h);
+    p.scores = cv.take<float>(rows * s->L);
+    p.hist = cv.take<uint32_t>(rows * (sa::kHist0Bins + 2));
+    p.counters = reinterpret_cast<int*>(p.hist ? p.hist + rows * sa::kHist0Bins : nullptr);
+    p.cand = cv.take<unsigned long long>(rows * maxn);
+    if (kp > 0) {
+        p.pool_idx = cv.take<int32_t>(rows * kp);
+        p.list_score = cv.take<float>(rows * kp);
+        p.list_idx = cv.take<int32_t>(rows * kp);
+    }
+    p.bytes = cv.off + 256;
+    return p;
+}
+
+int check_misa(const sa_shape* s, int B, int h, int kp) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (B < 1) return fail(SA_EINVAL, "block_B must be >= 1");
+    if (h < 1 || h > s->H) return fail(SA_EINVAL, "need 1 <= h <= H");
+    if (kp != 0 && kp < s->topk) return fail(SA_EINVAL, "k_prime must be 0 or >= topk");
+    return SA_OK;
+}
+
+// ---------------------------------------------------------------- HISA
+
+struct HisaPlan {
+    uint16_t* reps;
+    uint16_t* tail;
+    uint8_t* flag;
+    float* bscores;
+    int32_t* blocks;
+    float* list_score;
+    int32_t* list_idx;
+    size_t bytes;
+};
+
+HisaPlan plan_hisa(const sa_shape* s, int b, int r, bool reps_given, bool partial, void* ws) {
+    HisaPlan p{};
+    Carve cv(ws);
+    const long long rows = (long long)s->batch * s->T;
+    const long long nblk = (s->L + b - 1) / b;
+    if (!reps_given) p.reps = cv.take<uint16_t>(s->batch * nblk * 2 * sa::kD);
+    if (partial) {
+        p.tail = cv.take<uint16_t>(rows * 2 * sa::kD);
+        p.flag = cv.take<uint8_t>(rows);
+    }
+    p.bscores = cv.take<float>(rows * nblk);
+    p.blocks = cv.take<int32_t>(rows * r);
+    p.list_score = cv.take<float>(rows * (long long)r * b);
+    p.list_idx = cv.take<int32_t>(rows * (long long)r * b);
+    p.bytes = cv.off + 256;
+    return p;
+}
+
+int check_hisa(const sa_shape* s, int b, int r) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (b < 1 || r < 1) return fail(SA_EINVAL, "block_b and r must be >= 1");
+    if ((long long)r * b < s->topk) return fail(SA_EINVAL, "need r * block_b >= topk");
+    if ((long long)r * b > (1LL << 30)) return fail(SA_EUNSUPPORTED, "r * block_b too large");
+    return SA_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- profiling
+
+namespace sa {
+
+void prof_begin(int kid, hipStream_t s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    hipEvent_t a = take_event(), b = take_event();
+    if (!a || !b) return;
+    (void)hipEventRecord(a, s);
+    g_recs.push_back(ProfRec{kid, a, b});
+    g_open = (int)g_recs.size() - 1;
+}
+
+void prof_end(int kid, hipStream_t s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (g_open < 0 || g_recs[g_open].kid != kid) return;
+    (void)hipEventRecord(g_recs[g_open].stop, s);
+    g_open = -1;
+}
+
+}  // namespace sa
+
+extern "C" {
+
+const char* sa_last_error(void) { return g_err.c_str(); }
+
+int sa_profile_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (on) {
+        drain_records();
+        for (int i = 0; i < sa::K_COUNT; ++i) {
+            g_ms[i] = 0.0;
+            g_launches[i] = 0;
+        }
+    }
+    g_prof_on = on != 0;
+    g_open = -1;
+    return SA_OK;
+}
+
+int sa_profile_read(int32_t id, double* total_ms, int64_t* launches) {
+    if (id < 0 || id >= sa::K_COUNT || !total_ms || !launches)
+        return fail(SA_EINVAL, "bad kernel id or NULL output");
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    drain_records();
+    *total_ms = g_ms[id];
+    *launches = g_launches[id];
+    return SA_OK;
+}
+
+int32_t sa_kernel_count(void) { return sa::K_COUNT; }
+
+const char* sa_kernel_name(int32_t id) {
+    if (id < 0 || id >= sa::K_COUNT) return "";
+    return kKernelNames[id];
+}
+
+// ------------------------------------------------------------------ DSA
+
+int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_dsa(s, nullptr).bytes;
+    return SA_OK;
+}
+
+int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
+                       const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    const size_t need = plan_dsa(s, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    DsaPlan p = plan_dsa(s, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int rows = s->batch * s->T;
+    hipError_t e;
+    if (p.prefill) {
+        sa::PrefillArgs a{};
+        a.q = q;
+        a.w = w;
+        a.keys = keys;
+        a.T = s->T;
+        a.H = s->H;
+        a.L = s->L;
+        a.offset = s->causal_offset;
+        a.k = s->topk;
+        a.qpw = 8;
+        a.surv_score = p.surv_score;
+        a.surv_idx = p.surv_idx;
+        a.surv_count = p.surv_count;
+        a.cap = (long long)s->causal_offset + s->T;
+        e = sa::launch_prefill(a, rows, st);
+        if (e != hipSuccess) return hip_fail(e, "prefill");
+        e = run_list_topk(p.surv_score, p.surv_idx, a.cap, p.surv_count, (int)a.cap, rows,
+                          s->topk, out_idx, out_score, st);
+        if (e != hipSuccess) return hip_fail(e, "prefill top-k");
+    } else {
+        e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.hist, p.counters, p.cand,
+                           s->topk, out_idx, out_score, st);
+        if (e != hipSuccess) return hip_fail(e, "decode scan");
+    }
+    return SA_OK;
+}
+
+// -------------------------------------------------------------- pooling
+
+int sa_pool_blocks(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, int32_t block,
+                   uint16_t* out, void* stream) {
+    if (!keys || !out) return fail(SA_EINVAL, "keys and out must be non-NULL");
+    if (batch < 1 || L < 1 || block < 1) return fail(SA_EINVAL, "batch, L, block must be >= 1");
+    if (d != sa::kD) return fail(SA_EUNSUPPORTED, "d must be 128");
+    hipError_t e = sa::launch_pool(keys, batch, L, block, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pool");
+    return SA_OK;
+}
+
+int sa_pool_blocks2(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, int32_t small,
+                    int32_t large, uint16_t* out_small, uint16_t* out_large, void* stream) {
+    if (!keys || !out_small || !out_large) return fail(SA_EINVAL, "NULL pointer");
+    if (batch < 1 || L < 1 || small < 1 || large < small || large % small != 0)
+        return fail(SA_EINVAL, "need batch, L >= 1 and large a multiple of small");
+    if (d != sa::kD) return fail(SA_EUNSUPPORTED, "d must be 128");
+    hipError_t e = sa::launch_pool2(keys, batch, L, small, large, out_small, out_large,
+                                    static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "pool2");
+    return SA_OK;
+}
+
+// ----------------------------------------------------------------- MISA
+
+int misa_route_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
+                  int32_t pooled_given, size_t* ws_bytes) {
+    int rc = check_misa(s, block_B, h, k_prime);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_misa(s, block_B, h, k_prime, pooled_given != 0, any_partial(s, block_B),
+                          nullptr)
+                    .bytes;
+    return SA_OK;
+}
+
+int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+               int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
+               int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
+               void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_misa(s, block_B, h, k_prime);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    const bool partial = any_partial(s, block_B);
+    const size_t need = plan_misa(s, block_B, h, k_prime, pooled != nullptr, partial, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    MisaPlan p = plan_misa(s, block_B, h, k_prime, pooled != nullptr, partial, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int rows = s->batch * s->T;
+    const int nblk = (s->L + block_B - 1) / block_B;
+    hipError_t e;
+    const uint16_t* reps = pooled;
+    if (!reps) {
+        e = sa::launch_pool(keys, s->batch, s->L, block_B, p.pooled, st);
+        if (e != hipSuccess) return hip_fail(e, "pool");
+        reps = p.pooled;
+    }
+    if (partial) {
+        e = sa::launch_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset, s->L,
+                            block_B, rows, p.tail, p.flag, st);
+        if (e != hipSuccess) return hip_fail(e, "tail pool");
+    }
+    int32_t* heads = out_heads ? out_heads : p.heads;
+    sa::RouterArgs ra{};
+    ra.q = q;
+    ra.w = w;
+    ra.reps = reps;
+    ra.seq_stride = (long long)nblk * 2 * sa::kD;
+    ra.tail = p.tail;
+    ra.tail_flag = p.flag;
+    ra.T = s->T;
+    ra.H = s->H;
+    ra.offset = s->causal_offset;
+    ra.B = block_B;
+    ra.nblk = nblk;
+    ra.h = h;
+    ra.heads_out = heads;
+    ra.E_out = nullptr;
+    e = sa::launch_router(ra, rows, st);
+    if (e != hipSuccess) return hip_fail(e, "router");
+    if (k_prime == 0) {
+        e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.hist, p.counters, p.cand,
+                           s->topk, out_idx, out_score, st);
+        if (e != hipSuccess) return hip_fail(e, "routed scan");
+        return SA_OK;
+    }
+    int32_t* pool_idx = out_pool ? out_pool : p.pool_idx;
+    e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.hist, p.counters, p.cand, k_prime,
+                       pool_idx, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "routed scan");
+    sa::GatherArgs ga{};
+    ga.q = q;
+    ga.w = w;
+    ga.keys = keys;
+    ga.seq_stride = (long long)s->L * sa::kD;
+    ga.list = pool_idx;
+    ga.list_len = k_prime;
+    ga.bsz = 1;
+    ga.ncand = k_prime;
+    ga.T = s->T;
+    ga.H = s->H;
+    ga.L = s->L;
+    ga.offset = s->causal_offset;
+    ga.chunk = 512;
+    ga.out_score = p.list_score;
+    ga.out_idx = p.list_idx;
+    e = sa::launch_gather(ga, rows, (s->H + 15) / 16, false, st);
+    if (e != hipSuccess) return hip_fail(e, "rerank");
+    e = run_list_topk(p.list_score, p.list_idx, k_prime, nullptr, k_prime, rows, s->topk,
+                      out_idx, out_score, st);
+    if (e != hipSuccess) return hip_fail(e, "rerank top-k");
+    return SA_OK;
+}
+
+// ----------------------------------------------------------------- HISA
+
+int hisa_coarse_fine_ws(const sa_shape* s, int32_t block_b, int32_t r, int32_t reps_given,
+                        size_t* ws_bytes) {
+    int rc = check_hisa(s, block_b, r);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_hisa(s, block_b, r, reps_given != 0, any_partial(s, block_b), nullptr).bytes;
+    return SA_OK;
+}
+
+int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
+                     const sa_shape* s, int32_t block_b, int32_t r, const uint16_t* reps,
+                     int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
+                     size_t ws_bytes, void* stream) {
+    int rc = check_hisa(s, block_b, r);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    const bool partial = any_partial(s, block_b);
+    const size_t need = plan_hisa(s, block_b, r, reps != nullptr, partial, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    HisaPlan p = plan_hisa(s, block_b, r, reps != nullptr, partial, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int rows = s->batch * s->T;
+    const int nblk = (s->L + block_b - 1) / block_b;
+    hipError_t e;
+    const uint16_t* rp = reps;
+    if (!rp) {
+        e = sa::launch_pool(keys, s->batch, s->L, block_b, p.reps, st);
+        if (e != hipSuccess) return hip_fail(e, "pool");
+        rp = p.reps;
+    }
+    if (partial) {
+        e = sa::launch_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset, s->L,
+                            block_b, rows, p.tail, p.flag, st);
+        if (e != hipSuccess) return hip_fail(e, "tail pool");
+    }
+    // Coarse stage: block scores with the full indexer formula.
+    sa::ScanArgs a{};
+    a.q = q;
+    a.w = w;
+    a.keys = rp;
+    a.seq_stride = (long long)nblk * 2 * sa::kD;
+    a.tail = p.tail;
+    a.tail_flag = p.flag;
+    a.T = s->T;
+    a.H = s->H;
+    a.offset = s->causal_offset;
+    a.len_div = block_b;
+    a.len_cap = nblk;
+    a.chunk = 128;
+    a.scores = p.bscores;
+    a.score_stride = nblk;
+    e = sa::launch_scan(a, rows, (s->H + 15) / 16, 8, false, st);
+    if (e != hipSuccess) return hip_fail(e, "block scores");
+    int32_t* blocks = out_blocks ? out_blocks : p.blocks;
+    sa::TopkArgs t{};
+    t.dense = p.bscores;
+    t.dense_stride = nblk;
+    t.T = s->T;
+    t.offset = s->causal_offset;
+    t.len_div = block_b;
+    t.len_cap = nblk;
+    t.k = r;
+    t.out_idx = blocks;
+    t.out_score = nullptr;
+    t.out_stride = r;
+    e = sa::launch_topk(t, rows, st);
+    if (e != hipSuccess) return hip_fail(e, "block top-r");
+    // Fine stage: exact scores on the legal tokens of the kept blocks.
+    sa::GatherArgs ga{};
+    ga.q = q;
+    ga.w = w;
+    ga.keys = keys;
+    ga.seq_stride = (long long)s->L * sa::kD;
+    ga.list = blocks;
+    ga.list_len = r;
+    ga.bsz = block_b;
+    ga.ncand = r * block_b;
+    ga.T = s->T;
+    ga.H = s->H;
+    ga.L = s->L;
+    ga.offset = s->causal_offset;
+    ga.chunk = 512;
+    ga.out_score = p.list_score;
+    ga.out_idx = p.list_idx;
+    e = sa::launch_gather(ga, rows, (s->H + 15) / 16, true, st);
+    if (e != hipSuccess) return hip_fail(e, "fine rescore");
+    e = run_list_topk(p.list_score, p.list_idx, (long long)r * block_b, nullptr, r * block_b,
+                      rows, s->topk, out_idx, out_score, st);
+    if (e != hipSuccess) return hip_fail(e, "fine top-k");
+    return SA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+// Shared device helpers and host-side launch plumbing of the gfx950 indexer
+// library.  Internal header: not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;          // indexer head dim (bf16 elements per key)
+constexpr int kMaxH = 64;        // heads supported
+constexpr int kHist0Bits = 12;   // first radix digit = top 12 bits of the ordered score
+constexpr int kHist0Bins = 1 << kHist0Bits;
+
+// ------------------------------------------------------------ scalars
+
+// Order-preserving map float -> uint32: a > b  <=>  ord(a) > ord(b)
+// (for non-NaN values; -0 sorts just below +0).
+__device__ __forceinline__ uint32_t ord_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord_to_f32(uint32_t o) {
+    uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ------------------------------------------------------------- MFMA
+
+// D[16x16] += A[16x32] * B[32x16], bf16 inputs, fp32 accumulate.
+// Lane l supplies A row (l & 15) and B column (l & 15), each with the 8
+// contraction elements of group (l >> 4); D lane l holds column (l & 15),
+// rows 4*(l >> 4) + 0..3.  A and B only need to agree on which contraction
+// element sits where, so callers may assign any 16-byte chunk to a group.
+__device__ __forceinline__ f32x4 mfma16x16x32(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// ------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Wave-aggregated append: every lane of the wave must call it.  Lanes with
+// pred get consecutive slots starting at an atomically reserved base.
+__device__ __forceinline__ int wave_append(bool pred, int* counter) {
+    unsigned long long m = __ballot(pred);
+    int lane = lane_id();
+    int rank = __popcll(m & ((1ull << lane) - 1ull));
+    int base = 0;
+    if (m) {
+        int leader = __ffsll((long long)m) - 1;
+        if (lane == leader) base = atomicAdd(counter, __popcll(m));
+        base = __shfl(base, leader);
+    }
+    return base + rank;
+}
+
+// ------------------------------------------------------ kernel ids
+
+enum KernelId {
+    K_FILL = 0,
+    K_SCAN,
+    K_SCAN_ROUTED,
+    K_BLOCK_SCORE,
+    K_TOPK,
+    K_TOPK_FILTER,
+    K_POOL,
+    K_POOL2,
+    K_TAIL,
+    K_ROUTER,
+    K_GATHER,
+    K_PREFILL,
+    K_COUNT
+};
+
+// Host side: bracket a launch with profiling events when enabled.
+void prof_begin(int kid, hipStream_t s);
+void prof_end(int kid, hipStream_t s);
+
+// ---------------------------------------------------- launch records
+
+// Score scan over a contiguous legal key range per query row.
+struct ScanArgs {
+    const uint16_t* q;      // [rows, H, 128]
+    const float* w;         // [rows, H]
+    const uint16_t* keys;   // key rows of kstep*32 bf16 each
+    long long seq_stride;   // elements between sequences in `keys`
+    const uint16_t* tail;   // block reps only: per-row partial rep [rows, 256] or null
+    const uint8_t* tail_flag;
+    const int32_t* heads;   // routed: [rows, hsel]
+    int hsel;
+    int T, H, offset;
+    int len_div, len_cap;   // legal count n = min(t / len_div + 1, len_cap)
+    int chunk;              // keys per workgroup (multiple of 128)
+    float* scores;          // [rows, score_stride]
+    long long score_stride;
+    uint32_t* hist;         // [rows, 4096] or null
+};
+
+struct GatherArgs {
+    const uint16_t* q;
+    const float* w;
+    const uint16_t* keys;   // [batch, L, 128]
+    long long seq_stride;
+    const int32_t* list;    // [rows, list_len]
+    int list_len;
+    int bsz;                // block mode: tokens per listed block
+    int ncand;              // candidates per row
+    int T, H, L, offset;
+    int chunk;
+    float* out_score;       // [rows, ncand]
+    int32_t* out_idx;       // [rows, ncand]
+};
+
+struct RouterArgs {
+    const uint16_t* q;
+    const float* w;
+    const uint16_t* reps;   // [batch, nblk, 256] hi/lo
+    long long seq_stride;
+    const uint16_t* tail;
+    const uint8_t* tail_flag;
+    int T, H, offset, B, nblk, h;
+    int32_t* heads_out;     // [rows, h]
+    float* E_out;           // [rows, H] or null
+};
+
+struct TopkArgs {
+    // dense source: scores[row * dense_stride + s], s < n(row)
+    const float* dense;
+    long long dense_stride;
+    int T, offset, len_div, len_cap;
+    // list source: (list_score, list_idx)[row * list_stride + u], u < count(row);
+    // entries with idx < 0 are skipped
+    const float* list_score;
+    const int32_t* list_idx;
+    long long list_stride;
+    const int32_t* list_count;  // per-row counts or null (then list_cap)
+    int list_cap;
+    const uint32_t* hist0;      // optional precomputed first-digit histogram [rows, 4096]
+    int k;
+    int32_t* out_idx;           // [rows, out_stride]
+    float* out_score;           // nullable
+    long long out_stride;
+    long long cand_cap;         // candidate keys per row (filter path)
+};
+
+struct PrefillArgs {
+    const uint16_t* q;
+    const float* w;
+    const uint16_t* keys;
+    int T, H, L, offset, k;
+    int qpw;                    // queries per workgroup
+    float* surv_score;          // [rows, cap]
+    int32_t* surv_idx;          // [rows, cap]
+    int32_t* surv_count;        // [rows]
+    long long cap;
+};
+
+// Launchers (defined next to their kernels).
+hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s);
+hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,
+                       hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
+                         hipStream_t s);
+hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s);
+hipError_t launch_tail(const uint16_t* keys, long long seq_stride, int T, int offset, int L,
+                       int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s);
+// Dense rows with a first-digit histogram: multi-workgroup filter + per-row finish.
+// counters: [rows, 2] int, zeroed; cand: [rows, a.cand_cap] keys.
+hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn, int* counters,
+                                      unsigned long long* cand, hipStream_t s);
+hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16_t* out,
+                       hipStream_t s);
+hipError_t launch_pool2(const uint16_t* keys, int batch, int L, int small, int large,
+                        uint16_t* out_small, uint16_t* out_large, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,355 @@
+// Score kernels of the gfx950 indexer: the streaming key scan (DSA decode,
+// MISA routed scan, HISA block scan), the gathered rescoring (MISA-dagger
+// pool, HISA fine stage), the MISA router, and the causal tail pooling.
+//
+// Every kernel computes I = sum_j w_j * ReLU(q_j . k) (PaperTrace, "2.2.2
+// MISA, LISA and ResMiSA", section 1) with the q . k contraction on the bf16
+// MFMA unit: one query's heads form the M dimension (16 per tile), 16 keys
+// form N, and the 128 key dims are the contraction, split in 4 steps of 32.
+// The ReLU, the w-weighted head sum and the causal bound are applied to the
+// accumulator registers; only one fp32 score per key leaves the kernel.
+#include "sa_frag.h"
+
+namespace sa {
+
+// ------------------------------------------------------------ scan
+
+// One workgroup = 4 waves scans keys [cs, ce) of one query row.  Each wave
+// takes 32 consecutive keys (two 16-key MFMA groups) per iteration and the
+// workgroup advances 128 keys (32 KiB of bf16 keys) per iteration, with the
+// next iteration's loads issued before the current one is computed.
+template <int NHT, int KSTEPS, bool HIST>
+__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+    constexpr int KROW = KSTEPS * 32;
+    const int row = blockIdx.y;
+    const int b = row / a.T;
+    const int t = a.offset + (row - b * a.T);
+    int n = t / a.len_div + 1;
+    if (n > a.len_cap) n = a.len_cap;
+    const int cs = blockIdx.x * a.chunk;
+    if (cs >= n) return;
+    const int ce = min(cs + a.chunk, n);
+
+    __shared__ uint32_t lhist[HIST ? kHist0Bins : 1];
+    if (HIST) {
+        for (int x = threadIdx.x; x < kHist0Bins; x += 256) lhist[x] = 0u;
+        __syncthreads();
+    }
+
+    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    const int32_t* heads = a.heads ? a.heads + (long long)row * a.hsel : nullptr;
+    QFrag<NHT> f;
+    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H, heads,
+                    a.hsel, g, c);
+
+    const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
+    const uint16_t* tailp =
+        (KSTEPS == 8 && a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
+    float* srow = a.scores + (long long)row * a.score_stride;
+
+    auto kptr = [&](int s) -> const uint16_t* {
+        if (KSTEPS == 8 && tailp && s == n - 1) return tailp;
+        return kseq + (long long)s * KROW;
+    };
+    auto load2 = [&](uint4 (&buf)[2][KSTEPS], int base) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int s = min(base + gi * 16 + c, ce - 1);
+            load_key<KSTEPS>(buf[gi], kptr(s), g);
+        }
+    };
+    auto compute2 = [&](const uint4 (&buf)[2][KSTEPS], int base) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+            const int s = base + gi * 16 + c;
+            const float sc = group_score<NHT, KSTEPS>(f, buf[gi]);
+            if (g == 0 && s < ce) {
+                srow[s] = sc;
+                if (HIST) atomicAdd(&lhist[ord_key(sc) >> (32 - kHist0Bits)], 1u);
+            }
+        }
+    };
+
+    int base = cs + wid * 32;
+    if (base < ce) {
+        uint4 bufA[2][KSTEPS], bufB[2][KSTEPS];
+        load2(bufA, base);
+        for (;;) {
+            int nb = base + 128;
+            if (nb < ce) load2(bufB, nb);
+            compute2(bufA, base);
+            base = nb;
+            if (base >= ce) break;
+            nb = base + 128;
+            if (nb < ce) load2(bufA, nb);
+            compute2(bufB, base);
+            base = nb;
+            if (base >= ce) break;
+        }
+    }
+
+    if (HIST) {
+        __syncthreads();
+        uint32_t* grow = a.hist + (long long)row * kHist0Bins;
+        for (int x = threadIdx.x; x < kHist0Bins; x += 256) {
+            const uint32_t v = lhist[x];
+            if (v) atomicAdd(&grow[x], v);
+        }
+    }
+}
+
+// ----------------------------------------------------------- gather
+
+// Rescore a per-row candidate list with all heads.  List mode: candidate u
+// is token list[u]; block mode: candidate u is token list[u / bsz] * bsz +
+// u % bsz.  Candidates past the causal bound, past L or with a negative id
+// get score -inf and index -1.
+template <int NHT, bool BLOCKS>
+__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+    const int row = blockIdx.y;
+    const int b = row / a.T;
+    const int t = a.offset + (row - b * a.T);
+    const int cs = blockIdx.x * a.chunk;
+    if (cs >= a.ncand) return;
+    const int ce = min(cs + a.chunk, a.ncand);
+    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    QFrag<NHT> f;
+    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
+                    nullptr, 0, g, c);
+    const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
+    const int32_t* lrow = a.list + (long long)row * a.list_len;
+    float* osc = a.out_score + (long long)row * a.ncand;
+    int32_t* oid = a.out_idx + (long long)row * a.ncand;
+    for (int base = cs + wid * 16; base < ce; base += 64) {
+        const int u = base + c;
+        int s = -1;
+        if (u < ce) {
+            if (BLOCKS) {
+                const int blk = lrow[u / a.bsz];
+                s = blk >= 0 ? blk * a.bsz + (u - (u / a.bsz) * a.bsz) : -1;
+            } else {
+                s = lrow[u];
+            }
+        }
+        const bool valid = s >= 0 && s <= t && s < a.L;
+        uint4 kb[4];
+        load_key<4>(kb, kseq + (long long)(valid ? s : 0) * kD, g);
+        const float sc = group_score<NHT, 4>(f, kb);
+        if (g == 0 && u < ce) {
+            osc[u] = valid ? sc : -INFINITY;
+            oid[u] = valid ? s : -1;
+        }
+    }
+}
+
+// ----------------------------------------------------------- router
+
+// MISA router for one query row (summary page "MISA", method steps 2-3):
+// E_j = |w_j| * mean_m ReLU(q_j . pooled_m) over the blocks that intersect
+// [0, t], then the h largest E (ties -> lower head), written ascending.
+template <int NHT>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
+    const int row = blockIdx.x;
+    const int b = row / a.T;
+    const int t = a.offset + (row - b * a.T);
+    const int Mt = min(t / a.B + 1, a.nblk);
+    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    QFrag<NHT> f;
+    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
+                    nullptr, 0, g, c);
+    const uint16_t* kseq = a.reps + (long long)b * a.seq_stride;
+    const uint16_t* tailp = (a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
+
+    float sum[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[ht][i] = 0.f;
+
+    for (int base = wid * 16; base < Mt; base += 64) {
+        const int m = base + c;
+        const bool valid = m < Mt;
+        const int ml = valid ? m : Mt - 1;
+        const uint16_t* kp = (tailp && ml == Mt - 1) ? tailp : kseq + (long long)ml * 256;
+        uint4 kb[8];
+        load_key<8>(kb, kp, g);
+        f32x4 acc[NHT];
+        group_dots<NHT, 8>(f, kb, acc);
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[ht][i] += valid ? fmaxf(acc[ht][i], 0.f) : 0.f;
+    }
+    __shared__ float part[4][kMaxH];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = sum[ht][i];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            v += __shfl_xor(v, 8);
+            if (c == 0) part[wid][ht * 16 + 4 * g + i] = v;
+        }
+    __syncthreads();
+    if (wid == 0) {
+        const int j = lane;
+        float E = -1.f;
+        if (j < a.H) {
+            const float S = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+            E = fabsf(a.w[(long long)row * a.H + j]) * S / (float)Mt;
+            if (a.E_out) a.E_out[(long long)row * a.H + j] = E;
+        }
+        int rank = 0;
+        for (int j2 = 0; j2 < 64; ++j2) {
+            const float e2 = __shfl(E, j2);
+            rank += (e2 > E) || (e2 == E && j2 < j);
+        }
+        const bool sel = j < a.H && rank < a.h;
+        const unsigned long long msk = __ballot(sel);
+        const int pos = __popcll(msk & ((1ull << lane) - 1ull));
+        if (sel) a.heads_out[(long long)row * a.h + pos] = j;
+    }
+}
+
+// ------------------------------------------------------------- tail
+
+// Causal tail of the block pooling: for a row whose last legal block is cut
+// by the causal bound (t is not the block's last key), the representative is
+// the mean of keys [m*block, t]; written as a hi/lo bf16 pair like the cached
+// representatives.  flag[row] tells the score kernels whether to use it.
+__global__ __launch_bounds__(256) void tail_kernel(const uint16_t* keys, long long seq_stride,
+                                                   int T, int offset, int L, int block,
+                                                   uint16_t* tail, uint8_t* flag) {
+    const int row = blockIdx.x;
+    const int b = row / T;
+    const int t = offset + (row - b * T);
+    const int lo = (t / block) * block;
+    const int last = min(lo + block, L) - 1;
+    const bool partial = last > t;
+    if (threadIdx.x == 0) flag[row] = partial ? 1 : 0;
+    if (!partial) return;
+    const int c16 = threadIdx.x & 15, kl = threadIdx.x >> 4;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const uint16_t* kseq = keys + (long long)b * seq_stride;
+    for (int s = lo + kl; s <= t; s += 16) {
+        const uint4 v = ldg16(kseq + (long long)s * kD + c16 * 8);
+        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16_bits_to_f32(wds[e] & 0xffffu);
+            acc[2 * e + 1] += bf16_bits_to_f32(wds[e] >> 16);
+        }
+    }
+    __shared__ float red[16][kD];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[kl][c16 * 8 + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < kD) {
+        float S = 0.f;
+        for (int r = 0; r < 16; ++r) S += red[r][threadIdx.x];
+        const float mean = S / (float)(t - lo + 1);
+        const uint32_t hi = f32_to_bf16_bits(mean);
+        const uint32_t lo16 = f32_to_bf16_bits(mean - bf16_bits_to_f32(hi));
+        tail[(long long)row * 256 + threadIdx.x] = (uint16_t)hi;
+        tail[(long long)row * 256 + kD + threadIdx.x] = (uint16_t)lo16;
+    }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, long long n, uint32_t v) {
+    for (long long x = blockIdx.x * (long long)blockDim.x + threadIdx.x; x < n;
+         x += (long long)gridDim.x * blockDim.x)
+        p[x] = v;
+}
+
+// ---------------------------------------------------------- launchers
+
+hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    long long blocks = (n + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    prof_begin(K_FILL, s);
+    fill_u32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
+    prof_end(K_FILL, s);
+    return hipGetLastError();
+}
+
+template <int NHT, int KS>
+static void scan_dispatch_hist(const ScanArgs& a, dim3 grid, hipStream_t s) {
+    if (a.hist)
+        scan_kernel<NHT, KS, true><<<grid, dim3(256), 0, s>>>(a);
+    else
+        scan_kernel<NHT, KS, false><<<grid, dim3(256), 0, s>>>(a);
+}
+
+hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,
+                       hipStream_t s) {
+    const int maxn = a.len_cap;
+    const dim3 grid((unsigned)((maxn + a.chunk - 1) / a.chunk), (unsigned)rows);
+    const int kid = ksteps == 8 ? K_BLOCK_SCORE : (routed ? K_SCAN_ROUTED : K_SCAN);
+    prof_begin(kid, s);
+    if (ksteps == 4) {
+        switch (nht) {
+            case 1: scan_dispatch_hist<1, 4>(a, grid, s); break;
+            case 2: scan_dispatch_hist<2, 4>(a, grid, s); break;
+            case 3: scan_dispatch_hist<3, 4>(a, grid, s); break;
+            default: scan_dispatch_hist<4, 4>(a, grid, s); break;
+        }
+    } else {
+        switch (nht) {
+            case 1: scan_dispatch_hist<1, 8>(a, grid, s); break;
+            case 2: scan_dispatch_hist<2, 8>(a, grid, s); break;
+            case 3: scan_dispatch_hist<3, 8>(a, grid, s); break;
+            default: scan_dispatch_hist<4, 8>(a, grid, s); break;
+        }
+    }
+    prof_end(kid, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
+                         hipStream_t s) {
+    const dim3 grid((unsigned)((a.ncand + a.chunk - 1) / a.chunk), (unsigned)rows);
+    prof_begin(K_GATHER, s);
+#define SA_GATHER(N)                                                            \
+    if (block_mode)                                                             \
+        gather_kernel<N, true><<<grid, dim3(256), 0, s>>>(a);                   \
+    else                                                                        \
+        gather_kernel<N, false><<<grid, dim3(256), 0, s>>>(a);
+    switch (nht) {
+        case 1: SA_GATHER(1) break;
+        case 2: SA_GATHER(2) break;
+        case 3: SA_GATHER(3) break;
+        default: SA_GATHER(4) break;
+    }
+#undef SA_GATHER
+    prof_end(K_GATHER, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s) {
+    const int nht = (a.H + 15) / 16;
+    prof_begin(K_ROUTER, s);
+    switch (nht) {
+        case 1: router_kernel<1><<<dim3(rows), dim3(256), 0, s>>>(a); break;
+        case 2: router_kernel<2><<<dim3(rows), dim3(256), 0, s>>>(a); break;
+        case 3: router_kernel<3><<<dim3(rows), dim3(256), 0, s>>>(a); break;
+        default: router_kernel<4><<<dim3(rows), dim3(256), 0, s>>>(a); break;
+    }
+    prof_end(K_ROUTER, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_tail(const uint16_t* keys, long long seq_stride, int T, int offset, int L,
+                       int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s) {
+    prof_begin(K_TAIL, s);
+    tail_kernel<<<dim3(rows), dim3(256), 0, s>>>(keys, seq_stride, T, offset, L, block, tail,
+                                                 flag);
+    prof_end(K_TAIL, s);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,236 @@
+"""Parity rule between the HIP path and the CPU oracle, plus GPU run helpers.
+
+Rule per query row (tolerance tol = 2e-3 * max |oracle score| over the row's
+candidates):
+* the GPU row holds exactly min(k, #candidates) distinct indices, all legal
+  (0 <= s <= t), padded with -1 / -inf;
+* every returned score is within tol of the oracle's score of that index;
+* the GPU set equals the oracle set, or else every GPU index has oracle score
+  >= S_k - tol (S_k = the oracle's k-th score) and every oracle index with
+  score > S_k + tol is in the GPU set (near-tie exchanges only).
+Discrete intermediate choices (MISA heads, the MISA-dagger k' pool, HISA
+blocks) are checked with the same near-tie rule on their own statistic, then
+the oracle is re-run with the GPU's choice ("override") for the next stage.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from sparse_attention_token_dsa_amd import synth
+
+TOL_REL = 2e-3
+
+
+# ------------------------------------------------------------------ rule
+
+def check_set(gidx, gsc, ref_idx, ref_sc, score_of, ncand, k, tol, t=None, cand_set=None,
+              what="row"):
+    """Check one GPU top-k row.  score_of(indices) -> oracle scores (float64).
+    Returns the number of near-tie exchanges."""
+    gidx = np.asarray(gidx)
+    m = min(k, ncand)
+    valid = gidx >= 0
+    sel = gidx[valid]
+    assert len(sel) == m, "%s: %d indices, expected %d" % (what, len(sel), m)
+    assert len(np.unique(sel)) == m, "%s: duplicate indices" % what
+    if gsc is not None:
+        gsc = np.asarray(gsc)
+        assert np.all(np.isneginf(gsc[~valid])), "%s: padding scores not -inf" % what
+    if m == 0:
+        return 0
+    if t is not None:
+        assert sel.min() >= 0 and sel.max() <= t, "%s: index outside [0, %d]" % (what, t)
+    if cand_set is not None:
+        extra = set(sel.tolist()) - cand_set
+        assert not extra, "%s: indices outside the candidate set: %s" % (what, sorted(extra)[:8])
+    osc = np.asarray(score_of(sel), dtype=np.float64)
+    if gsc is not None:
+        err = np.abs(gsc[valid].astype(np.float64) - osc)
+        assert np.all(err <= tol), "%s: score error %.3g > tol %.3g" % (what, err.max(), tol)
+    ref = np.asarray(ref_idx)[:m]
+    rsc = np.asarray(ref_sc)[:m]
+    assert np.all(ref >= 0)
+    gs, rs = set(sel.tolist()), set(ref.tolist())
+    if gs == rs:
+        return 0
+    s_k = rsc[-1]
+    low = osc < s_k - tol
+    assert not np.any(low), "%s: GPU index %s scores %.6g below S_k - tol = %.6g" % (
+        what, sel[low][:4], osc[low].min(), s_k - tol)
+    must = set(ref[rsc > s_k + tol].tolist())
+    missing = must - gs
+    assert not missing, "%s: clearly-in oracle indices missing: %s" % (what, sorted(missing)[:8])
+    return len(rs - gs)
+
+
+def check_choice(chosen, stat, n_legal, h, what):
+    """Near-tie rule for a discrete choice of h items ranked by stat (desc)."""
+    stat = np.asarray(stat, np.float64)[:n_legal]
+    chosen = np.asarray(chosen)
+    chosen = chosen[chosen >= 0]
+    m = min(h, n_legal)
+    assert len(chosen) == m and len(np.unique(chosen)) == m, "%s: bad choice %s" % (what, chosen)
+    assert chosen.max() < n_legal
+    tol = TOL_REL * np.max(np.abs(stat)) if stat.size else 0.0
+    order = np.lexsort((np.arange(n_legal), -stat))
+    kth = stat[order[m - 1]]
+    assert np.all(stat[chosen] >= kth - tol), "%s: chosen item far below the cutoff" % what
+    must = set(np.nonzero(stat > kth + tol)[0].tolist())
+    assert must <= set(chosen.tolist()), "%s: clearly-in items missing" % what
+
+
+# ------------------------------------------------------------ GPU helpers
+
+def to_device(p, device):
+    import torch
+    q = torch.from_numpy(np.ascontiguousarray(p["q"]).view(np.int16)).to(device)
+    w = torch.from_numpy(np.ascontiguousarray(p["w"])).to(device)
+    K = torch.from_numpy(np.ascontiguousarray(p["K"]).view(np.int16)).to(device)
+    return q, w, K
+
+
+def _np(t):
+    return None if t is None else t.cpu().numpy()
+
+
+def rows_of(p, sample=None, seed=0):
+    R = p["Bt"] * p["T"]
+    if sample is None or sample >= R:
+        return np.arange(R, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(R, size=sample, replace=False).tolist())
+    pick |= {0, R - 1}
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+def t_of_row(p, row):
+    return p["offset"] + row % p["T"]
+
+
+# ------------------------------------------------------------ per method
+
+def check_dsa(p, k, gidx, gsc, rows):
+    """gidx/gsc: GPU outputs [Bt, T, k]; rows: flat rows to check."""
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    oidx, osc, rs = oracle.dsa(prob, k, rows=rows, want_rowscore=True)
+    gi = gidx.reshape(-1, k)
+    gs = None if gsc is None else gsc.reshape(-1, k)
+    swaps = 0
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        srow = rs[u, : t + 1]
+        tol = TOL_REL * np.max(np.abs(srow))
+        swaps += check_set(gi[row], None if gs is None else gs[row], oidx[u], osc[u],
+                           lambda s, srow=srow: srow[s], t + 1, k, tol, t=t,
+                           what="dsa row %d" % row)
+    return swaps
+
+
+def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows):
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    base = oracle.misa(prob, k, B, h, kprime=0, rows=rows)
+    gh = gheads.reshape(-1, h)
+    for u, row in enumerate(rows):
+        check_choice(gh[row], base["E"][u], p["H"], h, "misa heads row %d" % row)
+    over_h = np.ascontiguousarray(gh[rows])
+    staged = oracle.misa(prob, k, B, h, kprime=kprime, rows=rows, override_heads=over_h,
+                         want_hatrow=True)
+    gi = gidx.reshape(-1, k)
+    gs = None if gsc is None else gsc.reshape(-1, k)
+    swaps = 0
+    if kprime == 0:
+        for u, row in enumerate(rows):
+            t = t_of_row(p, row)
+            hat = staged["hatrow"][u, : t + 1]
+            tol = TOL_REL * np.max(np.abs(hat))
+            swaps += check_set(gi[row], None if gs is None else gs[row], staged["idx"][u],
+                               staged["score"][u], lambda s, hat=hat: hat[s], t + 1, k, tol, t=t,
+                               what="misa row %d" % row)
+        return swaps
+    # MISA-dagger: the k' pool by the routed score, then the rerank.
+    gp = gpool.reshape(-1, kprime)
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        hat = staged["hatrow"][u, : t + 1]
+        tol = TOL_REL * np.max(np.abs(hat))
+        opool = staged["pool"][u]
+        check_set(gp[row], None, opool, hat[opool[opool >= 0]], lambda s, hat=hat: hat[s],
+                  t + 1, kprime, tol, t=t, what="misa-dagger pool row %d" % row)
+    over_p = np.ascontiguousarray(gp[rows])
+    final = oracle.misa(prob, k, B, h, kprime=kprime, rows=rows, override_heads=over_h,
+                        override_pool=over_p)
+    # all-heads score of every pool member (top-k' of the pool = the whole pool)
+    every = oracle.misa(prob, kprime, B, h, kprime=kprime, rows=rows, override_heads=over_h,
+                        override_pool=over_p)
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        pool = gp[row][gp[row] >= 0]
+        sc_of = dict(zip(every["idx"][u].tolist(), every["score"][u].tolist()))
+        sc_of.pop(-1, None)
+        tol = TOL_REL * max(abs(v) for v in sc_of.values())
+        swaps += check_set(gi[row], None if gs is None else gs[row], final["idx"][u],
+                           final["score"][u], lambda s, d=sc_of: np.array([d[int(x)] for x in s]),
+                           len(pool), k, tol, t=t, cand_set=set(pool.tolist()),
+                           what="misa-dagger row %d" % row)
+    return swaps
+
+
+def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows):
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    base = oracle.hisa(prob, k, b, r, rows=rows)
+    gb = gblocks.reshape(-1, r)
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        check_choice(gb[row], base["J"][u], t // b + 1, r, "hisa blocks row %d" % row)
+    over = np.ascontiguousarray(gb[rows])
+    staged = oracle.hisa(prob, k, b, r, rows=rows, override_blocks=over)
+    gi = gidx.reshape(-1, k)
+    gs = None if gsc is None else gsc.reshape(-1, k)
+    swaps = 0
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        blocks = gb[row][gb[row] >= 0]
+        cand = np.concatenate([np.arange(m * b, min((m + 1) * b, t + 1)) for m in blocks])
+        # exact scores of the candidates: from the staged oracle top-k over
+        # exactly these candidates (k = #candidates gives every score)
+        allc = oracle.hisa(prob, len(cand), b, r, rows=np.array([row], np.int32),
+                           override_blocks=over[u: u + 1])
+        sc_of = dict(zip(allc["idx"][0].tolist(), allc["score"][0].tolist()))
+        tol = TOL_REL * max(abs(v) for v in sc_of.values())
+        swaps += check_set(gi[row], None if gs is None else gs[row], staged["idx"][u],
+                           staged["score"][u], lambda s, d=sc_of: np.array([d[int(x)] for x in s]),
+                           len(cand), k, tol, t=t, cand_set=set(cand.tolist()),
+                           what="hisa row %d" % row)
+    return swaps
+
+
+# ------------------------------------------------------------------ smoke
+
+def smoke_run(device):
+    """One small call of every entry point on `device`, checked against the oracle."""
+    import torch
+    from sparse_attention_token_dsa_amd import api
+
+    p = synth.make_problem(7, Bt=2, T=1, L=3000, H=64, needles=8, needle_mode="decode")
+    q, w, K = to_device(p, device)
+    rows = rows_of(p)
+    idx, sc = api.indexer_score_topk(q, w, K, p["offset"], 64)
+    torch.cuda.synchronize(device)
+    check_dsa(p, 64, _np(idx), _np(sc), rows)
+
+    idx, sc, heads, pool = api.misa_route(q, w, K, p["offset"], 64, 256, 8, k_prime=256,
+                                          want_pool=True)
+    torch.cuda.synchronize(device)
+    check_misa(p, 64, 256, 8, 256, _np(idx), _np(sc), _np(heads), _np(pool), rows)
+
+    idx, sc, blocks = api.hisa_coarse_fine(q, w, K, p["offset"], 64, 64, 8)
+    torch.cuda.synchronize(device)
+    check_hisa(p, 64, 64, 8, _np(idx), _np(sc), _np(blocks), rows)
+
+    pp = synth.make_problem(8, Bt=1, T=64, L=700, H=64, needles=8, needle_mode="rows")
+    q, w, K = to_device(pp, device)
+    idx, sc = api.indexer_score_topk(q, w, K, pp["offset"], 48)
+    torch.cuda.synchronize(device)
+    check_dsa(pp, 48, _np(idx), _np(sc), rows_of(pp))
+    print("smoke ok: DSA decode, MISA-dagger, HISA and fused prefill match the oracle")

@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library is loaded (built first if missing), every function declared in
+include/sa_indexer.h must be exported, and argument validation must reject bad
+shapes and budgets with the documented codes before anything is launched.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa_indexer.h")
+
+
+@pytest.fixture(scope="module")
+def api():
+    from sparse_attention_token_dsa_amd import api as a
+    if not os.path.exists(a.LIB_PATH):
+        from sparse_attention_token_dsa_amd import build
+        build.build()
+    a.load()
+    return a
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("indexer_score_topk", "misa_route", "hisa_coarse_fine", "sa_pool_blocks",
+              "sa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(api):
+    lib = api.load()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(api.EXPORTS) == set(declared_functions())
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for n in declared_functions():
+        assert re.search(r"\bT %s$" % n, out, flags=re.M), n
+
+
+def shape(api, **kw):
+    d = dict(batch=2, T=1, H=64, d=128, L=4096, causal_offset=4095, topk=64)
+    d.update(kw)
+    return api.Shape(**d)
+
+
+def ws_rc(api, s):
+    n = ctypes.c_size_t()
+    return api.load().indexer_score_topk_ws(ctypes.byref(s), ctypes.byref(n)), n.value
+
+
+def test_workspace_sizes_and_shape_validation(api):
+    rc, n = ws_rc(api, shape(api))
+    assert rc == api.SA_OK and n > 0
+    # decode path: score row + histogram + candidates per row
+    assert n >= 2 * 4096 * 4
+    assert ws_rc(api, shape(api, d=64))[0] == api.SA_EUNSUPPORTED
+    assert ws_rc(api, shape(api, H=65))[0] == api.SA_EUNSUPPORTED
+    assert ws_rc(api, shape(api, causal_offset=4090, T=7))[0] == api.SA_EINVAL
+    assert ws_rc(api, shape(api, causal_offset=-1))[0] == api.SA_EINVAL
+    assert ws_rc(api, shape(api, topk=0))[0] == api.SA_EINVAL
+    assert ws_rc(api, shape(api, L=0, causal_offset=0))[0] == api.SA_EINVAL
+    assert "causal_offset" in api.last_error() or api.last_error()
+
+
+def test_budget_validation(api):
+    lib = api.load()
+    n = ctypes.c_size_t()
+    s = shape(api, topk=2048, L=131072, causal_offset=131071)
+    # MISA: h in [1, H], k' = 0 or >= k
+    assert lib.misa_route_ws(ctypes.byref(s), 1024, 8, 0, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.misa_route_ws(ctypes.byref(s), 1024, 8, 8192, 1, ctypes.byref(n)) == api.SA_OK
+    assert lib.misa_route_ws(ctypes.byref(s), 1024, 0, 0, 0, ctypes.byref(n)) == api.SA_EINVAL
+    assert lib.misa_route_ws(ctypes.byref(s), 1024, 65, 0, 0, ctypes.byref(n)) == api.SA_EINVAL
+    assert lib.misa_route_ws(ctypes.byref(s), 1024, 8, 1000, 0, ctypes.byref(n)) == api.SA_EINVAL
+    assert lib.misa_route_ws(ctypes.byref(s), 0, 8, 0, 0, ctypes.byref(n)) == api.SA_EINVAL
+    # HISA: r * b >= k (PaperTrace section 2.3)
+    assert lib.hisa_coarse_fine_ws(ctypes.byref(s), 128, 64, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.hisa_coarse_fine_ws(ctypes.byref(s), 128, 15, 0, ctypes.byref(n)) == api.SA_EINVAL
+    assert "r * block_b" in api.last_error()
+    assert lib.hisa_coarse_fine_ws(ctypes.byref(s), 0, 64, 0, ctypes.byref(n)) == api.SA_EINVAL
+
+
+def test_entry_points_reject_before_launch(api):
+    """Bad arguments return an error without touching the GPU."""
+    lib = api.load()
+    s = shape(api)
+    buf = ctypes.create_string_buffer(16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    # NULL q
+    assert lib.indexer_score_topk(None, p, p, ctypes.byref(s), p, None, p, 16, None) == \
+        api.SA_EINVAL
+    # workspace too small
+    assert lib.indexer_score_topk(p, p, p, ctypes.byref(s), p, None, p, 16, None) == \
+        api.SA_EWORKSPACE
+    assert "workspace" in api.last_error()
+    # bad shape
+    s2 = shape(api, d=96)
+    assert lib.indexer_score_topk(p, p, p, ctypes.byref(s2), p, None, p, 16, None) == \
+        api.SA_EUNSUPPORTED
+    assert lib.misa_route(p, p, p, ctypes.byref(s), 1024, 9999, 0, None, None, None, p, None,
+                          p, 16, None) == api.SA_EINVAL
+    assert lib.hisa_coarse_fine(p, p, p, ctypes.byref(s), 8, 2, None, None, p, None, p, 16,
+                                None) == api.SA_EINVAL
+    assert lib.sa_pool_blocks(p, 1, 100, 128, 0, p, None) == api.SA_EINVAL
+    assert lib.sa_pool_blocks2(p, 1, 100, 128, 128, 1000, p, p, None) == api.SA_EINVAL
+
+
+def test_kernel_names(api):
+    names = api.kernel_names()
+    assert "scan_dsa" in names and "prefill_fused" in names and "topk_select" in names
+    assert len(set(names)) == len(names)
