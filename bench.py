@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Throughput of the indexer hot path on one MI355X.
+
+Workload (one "step"): one decode batch at L = 131072 -- 8 sequences, one query
+each, H_I = 64 heads, d = 128, bf16 q / keys, fp32 w, k = 2048 -- pushed through
+every selector of the library, with all inputs resident in HBM:
+  1. block pooling of the keys (HISA b = 128 and MISA B = 1024, one pass),
+  2. DSA: score every causal prefix token with all heads, top-k,
+  3. MISA: router over the pooled keys, top-8 heads, routed scan, top-k,
+  4. MISA-dagger: routed top-k' (8192), rerank with all heads, top-k,
+  5. HISA: block scores, top-64 blocks, exact rescoring of their 8192 tokens,
+     top-k.
+value = logical indexer scores per second = (query, legal token) pairs that the
+four selectors rank per step / step time.
+
+Also reported: per-kernel HIP-event durations inside the timed region, the
+roofline fraction of the dominant kernel (the DSA decode scan, HBM-bound), the
+fused causal prefill (T = 4096 new queries over 28672 cached keys, MFMA-bound)
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "indexer scores/s (query·token) + top-k rows/s at L=128K; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "sparse_attention_token_dsa_amd", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-iters", type=int, default=10)
+    return ap.parse_args()
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_token_dsa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, digest):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the indexer shards by sequence with no communication); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_attention_token_dsa_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    api.load()
+    cfg = synth.CONFIGS["misa_128k_h64"]
+    p = synth.make_config("misa_128k_h64")
+    Bt, L, H, d, k = p["Bt"], p["L"], p["H"], p["d"], cfg["topk"]
+    off = p["offset"]
+    B, h, kp, b, r = 1024, 8, 8192, 128, 64
+    q = torch.from_numpy(p["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(p["w"]).to(dev)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
+
+    # Preallocated outputs and workspaces: nothing is allocated in the loop.
+    shape = api.Shape(Bt, 1, H, d, L, off, k)
+    ws_dsa = torch.empty(api.indexer_score_topk_ws(shape), dtype=torch.uint8, device=dev)
+    ws_m1 = torch.empty(api.misa_route_ws(shape, B, h, 0, True), dtype=torch.uint8, device=dev)
+    ws_m2 = torch.empty(api.misa_route_ws(shape, B, h, kp, True), dtype=torch.uint8, device=dev)
+    ws_hi = torch.empty(api.hisa_coarse_fine_ws(shape, b, r, True), dtype=torch.uint8,
+                        device=dev)
+    reps_b = torch.empty((Bt, L // b, 2, d), dtype=torch.int16, device=dev)
+    reps_B = torch.empty((Bt, L // B, 2, d), dtype=torch.int16, device=dev)
+    outs = {m: (torch.empty((Bt, 1, k), dtype=torch.int32, device=dev),
+                torch.empty((Bt, 1, k), dtype=torch.float32, device=dev))
+            for m in ("dsa", "misa", "misa_dagger", "hisa")}
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        api.pool_blocks2(K, b, B, out_small=reps_b, out_large=reps_B)
+        mark(1)
+        api.indexer_score_topk(q, w, K, off, k, *outs["dsa"], ws=ws_dsa)
+        mark(2)
+        api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
+                       out_idx=outs["misa"][0], out_score=outs["misa"][1], ws=ws_m1)
+        mark(3)
+        api.misa_route(q, w, K, off, k, B, h, kp, pooled=reps_B, want_heads=False,
+                       out_idx=outs["misa_dagger"][0], out_score=outs["misa_dagger"][1],
+                       ws=ws_m2)
+        mark(4)
+        api.hisa_coarse_fine(q, w, K, off, k, b, r, reps=reps_b, want_blocks=False,
+                             out_idx=outs["hisa"][0], out_score=outs["hisa"][1], ws=ws_hi)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # Timed region: exactly `steps` steps between two synchronisations, with
+    # per-kernel HIP events recorded by the library on the launch stream.
+    api.profile_enable(True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    kern = api.profile_read()
+    api.profile_enable(False)
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # Per-selector split (separate pass, torch events between the calls).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    split = {n: 0.0 for n in ("pool", "dsa", "misa", "misa_dagger", "hisa")}
+    nsplit = max(5, args.steps // 5)
+    for _ in range(nsplit):
+        step(ev)
+        torch.cuda.synchronize(dev)
+        for i, n in enumerate(split):
+            split[n] += ev[i].elapsed_time(ev[i + 1]) / nsplit
+
+    rows = Bt  # one query per sequence
+    logical_pairs = 4 * rows * L     # four selectors, every legal token of each row
+    value = logical_pairs / (ms_step * 1e-3)
+    kernels = {n: {"avg_us": 1e3 * t / c, "launches_per_step": c / args.steps}
+               for n, (t, c) in sorted(kern.items())}
+
+    # Roofline of the DSA decode scan: algorithmic bytes per launch.
+    kbytes = Bt * L * d * 2
+    scan_bytes = kbytes + Bt * H * d * 2 + Bt * H * 4 + Bt * L * 4
+    scan_us = kernels["scan_dsa"]["avg_us"]
+    scan_gbs = scan_bytes / (scan_us * 1e-6) / 1e9
+    digest = source_digest(["scan.hip", "sa_frag.h", "sa_common.h"])
+    roofline = {"kernel": "scan_dsa", "bound": "hbm", "achieved": round(scan_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic("scan_dsa", digest),
+                "algorithmic_bytes_per_launch": scan_bytes, "avg_us": round(scan_us, 2)}
+    other_hbm = {}
+    for name, nbytes in (("scan_routed", kbytes + Bt * h * d * 2 + Bt * H * 4 + Bt * L * 4),
+                         ("pool2", kbytes + Bt * (L // b + L // B) * 2 * d * 2)):
+        if name in kernels:
+            us = kernels[name]["avg_us"]
+            gbs = nbytes / (us * 1e-6) / 1e9
+            other_hbm[name] = {"avg_us": round(us, 2), "GB/s": round(gbs, 1),
+                               "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "scores/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_128k_b8_h64", "batch": Bt, "L": L, "H_I": H, "d": d,
+                   "topk": k, "misa": {"B": B, "h": h, "k_prime": kp},
+                   "hisa": {"b": b, "r": r},
+                   "step": "pool(b=128,B=1024) + DSA + MISA + MISA-dagger + HISA"},
+        "topk_rows_per_s": 4 * rows / (ms_step * 1e-3),
+        "selector_ms": {n: round(v, 4) for n, v in split.items()},
+        "selector_scores_per_s": {n: rows * L / (split[n] * 1e-3)
+                                  for n in ("dsa", "misa", "misa_dagger", "hisa")},
+        "kernels": kernels,
+        "roofline": roofline,
+        "hbm_kernels": other_hbm,
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(api, synth, torch, np, dev, args.prefill_iters)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(p, k, B, h, kp, b, r)
+
+    print(json.dumps(result))
+
+
+def bench_prefill(api, synth, torch, np, dev, iters):
+    """Fused causal prefill: T = 4096 queries over 28672 cached keys, k = 2048."""
+    p = synth.make_config("prefill_chunked")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(p["w"]).to(dev)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
+    T, L, H, d, off, k = p["T"], p["L"], p["H"], p["d"], p["offset"], 2048
+    shape = api.Shape(1, T, H, d, L, off, k)
+    ws = torch.empty(api.indexer_score_topk_ws(shape), dtype=torch.uint8, device=dev)
+    oi = torch.empty((1, T, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((1, T, k), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        api.indexer_score_topk(q, w, K, off, k, oi, osc, ws=ws)
+    torch.cuda.synchronize(dev)
+    api.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        api.indexer_score_topk(q, w, K, off, k, oi, osc, ws=ws)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    kern = api.profile_read()
+    api.profile_enable(False)
+    pairs = sum(off + i + 1 for i in range(T))          # legal (query, key) pairs
+    flops = 2.0 * pairs * H * d
+    pf_us = 1e3 * kern["prefill_fused"][0] / kern["prefill_fused"][1]
+    tk_us = 1e3 * kern["topk_select"][0] / kern["topk_select"][1]
+    tflops = flops / (pf_us * 1e-6) / 1e12
+    return {"workload": "prefill_chunked_T4096_P28672_h64", "ms_per_call": (t1 - t0) * 1e3 / iters,
+            "logical_scores_per_s": pairs / ((t1 - t0) / iters),
+            "topk_rows_per_s": T / ((t1 - t0) / iters),
+            "kernels_us": {"prefill_fused": round(pf_us, 2), "topk_select": round(tk_us, 2)},
+            "roofline": {"kernel": "prefill_fused", "bound": "mfma", "achieved": round(tflops, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": flops}}
+
+
+def cpu_baseline(p, k, B, h, kp, b, r):
+    """The fp64 CPU oracle on all 8 query rows of the same workload, through the
+    same four selectors (pooling included in its MISA / HISA calls)."""
+    import oracle
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    rows = p["Bt"] * p["T"]
+    threads = min(cores, rows)
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    t0 = time.perf_counter()
+    oracle.dsa(prob, k, nthreads=threads)
+    oracle.misa(prob, k, B, h, 0, nthreads=threads)
+    oracle.misa(prob, k, B, h, kp, nthreads=threads)
+    oracle.hisa(prob, k, b, r, nthreads=threads)
+    dt = time.perf_counter() - t0
+    pairs = 4 * rows * p["L"]
+    return {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "sample": "all %d query rows of the L=%d decode batch through DSA, MISA, "
+                      "MISA-dagger and HISA (fp64 C oracle, one thread per row); %.1f s wall"
+                      % (rows, p["L"], dt)}
+
+
+if __name__ == "__main__":
+    main()

@@ -5,7 +5,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/sa_indexer.h"
+#include "sa_indexer.h"
 #include "sa_common.h"
 
 namespace {
@@ -101,15 +101,9 @@ int check_ptrs(const void* q, const void* w, const void* k, const void* out_idx)
     return SA_OK;
 }
 
-// Scan chunk: aim for about 1024 workgroups over all rows.
-int scan_chunk(long long rows, int maxn) {
-    long long per_row = (1024 + rows - 1) / rows;
-    long long c = (maxn + per_row - 1) / per_row;
-    c = ((c + 127) / 128) * 128;
-    if (c < 128) c = 128;
-    if (c > 8192) c = 8192;
-    return (int)c;
-}
+// Scan chunk: a workgroup covers 4 waves x kScanSteps steps of 64 keys (16
+// for block representatives, which use two 16-key groups per step).
+int scan_chunk(int ksteps) { return 4 * (ksteps == 4 ? 64 : 32) * sa::kScanSteps; }
 
 constexpr int kPrefillMinT = 16;
 
@@ -178,7 +172,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.offset = s->causal_offset;
     a.len_div = 1;
     a.len_cap = s->L;
-    a.chunk = scan_chunk(rows, maxn);
+    a.chunk = scan_chunk(4);
     a.scores = scores;
     a.score_stride = s->L;
     a.hist = hist;
@@ -592,7 +586,7 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
     a.offset = s->causal_offset;
     a.len_div = block_b;
     a.len_cap = nblk;
-    a.chunk = 128;
+    a.chunk = scan_chunk(8);
     a.scores = p.bscores;
     a.score_stride = nblk;
     e = sa::launch_scan(a, rows, (s->H + 15) / 16, 8, false, st);

@@ -14,6 +14,8 @@ constexpr int kD = 128;          // indexer head dim (bf16 elements per key)
 constexpr int kMaxH = 64;        // heads supported
 constexpr int kHist0Bits = 12;   // first radix digit = top 12 bits of the ordered score
 constexpr int kHist0Bins = 1 << kHist0Bits;
+constexpr int kScanSteps = 4;        // unrolled steps per scan wave
+constexpr int kScanMaxChunk = 2048;  // keys per scan workgroup (LDS score staging)
 
 // ------------------------------------------------------------ scalars
 

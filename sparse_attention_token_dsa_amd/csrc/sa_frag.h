@@ -22,33 +22,60 @@ struct QFrag {
     float wv[NHT][4];
 };
 
-// Head of tile row u: identity over H, or entry u of a routed head list
-// (ids outside [0, H) are treated as absent).
-__device__ __forceinline__ int head_at(int u, int H, const int32_t* heads, int hsel) {
-    if (heads) {
-        const int v = u < hsel ? heads[u] : -1;
-        return (v >= 0 && v < H) ? v : -1;
+// Head of tile row u: identity over H, or entry u of a routed head list.
+// Returns a loadable head id (0 when absent) and sets `valid`.
+template <bool ROUTED>
+__device__ __forceinline__ int head_at(int u, int H, const int32_t* heads, int hsel, bool& valid) {
+    if (ROUTED) {
+        const int v = heads[u < hsel ? u : hsel - 1];
+        valid = u < hsel && v >= 0 && v < H;
+        return valid ? v : 0;
     }
-    return u < H ? u : -1;
+    valid = u < H;
+    return valid ? u : 0;
 }
 
-template <int NHT>
+// All head ids first, then every q / w load back to back (no branches), then
+// the zero-masking of absent heads.
+template <int NHT, bool ROUTED = false>
 __device__ __forceinline__ void load_qfrag(QFrag<NHT>& f, const uint16_t* qrow,
                                            const float* wrow, int H, const int32_t* heads,
                                            int hsel, int g, int c) {
+    int ha[NHT], hw[NHT][4];
+    bool va[NHT], vw[NHT][4];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-        const int hr = head_at(ht * 16 + c, H, heads, hsel);
+        ha[ht] = head_at<ROUTED>(ht * 16 + c, H, heads, hsel, va[ht]);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            f.a[ht][kk] = hr >= 0 ? ldg16(qrow + hr * kD + (kk * 4 + g) * 8)
-                                  : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hw = head_at(ht * 16 + 4 * g + i, H, heads, hsel);
-            f.wv[ht][i] = hw >= 0 ? wrow[hw] : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) hw[ht][i] = head_at<ROUTED>(ht * 16 + 4 * g + i, H, heads, hsel, vw[ht][i]);
     }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = ldg16(qrow + ha[ht] * kD + (kk * 4 + g) * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f.wv[ht][i] = wrow[hw[ht][i]];
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        if (!va[ht])
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (!vw[ht][i]) f.wv[ht][i] = 0.f;
+    }
+}
+
+// Sum of a value over the four 16-lane groups (lanes l, l^16, l^32, l^48),
+// returned in every lane: two gfx950 row swaps, no LDS traffic.
+__device__ __forceinline__ float sum_lane_groups(float v) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                              false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto r2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                               false);
+    return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
 // Raw per-head dot products of one 16-key group: acc[ht][i] = q_{ht*16+4g+i} . k_c.
@@ -74,9 +101,7 @@ __device__ __forceinline__ float group_score(const QFrag<NHT>& f, const uint4 (&
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc = fmaf(f.wv[ht][i], fmaxf(acc[ht][i], 0.f), sc);
-    sc += __shfl_xor(sc, 16);
-    sc += __shfl_xor(sc, 32);
-    return sc;
+    return sum_lane_groups(sc);
 }
 
 template <int KSTEPS>

@@ -14,13 +14,17 @@ namespace sa {
 
 // ------------------------------------------------------------ scan
 
-// One workgroup = 4 waves scans keys [cs, ce) of one query row.  Each wave
-// takes 32 consecutive keys (two 16-key MFMA groups) per iteration and the
-// workgroup advances 128 keys (32 KiB of bf16 keys) per iteration, with the
-// next iteration's loads issued before the current one is computed.
-template <int NHT, int KSTEPS, bool HIST>
+// One workgroup = 4 waves scans keys [cs, ce) of one query row (ce - cs <=
+// 4*G*16*kScanSteps).  Each wave takes G*16 consecutive keys per step and the
+// workgroup advances 4*G*16 keys per step; the next step's key loads are in
+// flight while the current step is computed (two register buffers).  Scores
+// are staged in LDS and written out coalesced at the end, so the loop issues
+// no global stores.
+template <int NHT, int KSTEPS, int G, bool HIST, bool ROUTED>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     constexpr int KROW = KSTEPS * 32;
+    constexpr int WKEYS = G * 16;
+    constexpr int STEP = 4 * WKEYS;
     const int row = blockIdx.y;
     const int b = row / a.T;
     const int t = a.offset + (row - b * a.T);
@@ -31,65 +35,66 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     const int ce = min(cs + a.chunk, n);
 
     __shared__ uint32_t lhist[HIST ? kHist0Bins : 1];
+    __shared__ float sbuf[kScanMaxChunk];
     if (HIST) {
         for (int x = threadIdx.x; x < kHist0Bins; x += 256) lhist[x] = 0u;
         __syncthreads();
     }
 
-    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    const int32_t* heads = a.heads ? a.heads + (long long)row * a.hsel : nullptr;
+    const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t* heads = ROUTED ? a.heads + (long long)row * a.hsel : nullptr;
     QFrag<NHT> f;
-    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H, heads,
-                    a.hsel, g, c);
+    load_qfrag<NHT, ROUTED>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
+                            heads, a.hsel, g, c);
 
     const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
     const uint16_t* tailp =
         (KSTEPS == 8 && a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
-    float* srow = a.scores + (long long)row * a.score_stride;
 
     auto kptr = [&](int s) -> const uint16_t* {
         if (KSTEPS == 8 && tailp && s == n - 1) return tailp;
         return kseq + (long long)s * KROW;
     };
-    auto load2 = [&](uint4 (&buf)[2][KSTEPS], int base) {
+    // Loads past the end re-read the last key, so they can be unconditional:
+    // the wait before each compute then covers exactly the older buffer.
+    auto loadG = [&](uint4 (&buf)[G][KSTEPS], int base) {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+        for (int gi = 0; gi < G; ++gi) {
             const int s = min(base + gi * 16 + c, ce - 1);
             load_key<KSTEPS>(buf[gi], kptr(s), g);
         }
     };
-    auto compute2 = [&](const uint4 (&buf)[2][KSTEPS], int base) {
+    auto computeG = [&](const uint4 (&buf)[G][KSTEPS], int base) {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+        for (int gi = 0; gi < G; ++gi) {
             const int s = base + gi * 16 + c;
             const float sc = group_score<NHT, KSTEPS>(f, buf[gi]);
             if (g == 0 && s < ce) {
-                srow[s] = sc;
+                sbuf[s - cs] = sc;
                 if (HIST) atomicAdd(&lhist[ord_key(sc) >> (32 - kHist0Bits)], 1u);
             }
         }
     };
 
-    int base = cs + wid * 32;
-    if (base < ce) {
-        uint4 bufA[2][KSTEPS], bufB[2][KSTEPS];
-        load2(bufA, base);
-        for (;;) {
-            int nb = base + 128;
-            if (nb < ce) load2(bufB, nb);
-            compute2(bufA, base);
-            base = nb;
-            if (base >= ce) break;
-            nb = base + 128;
-            if (nb < ce) load2(bufA, nb);
-            compute2(bufB, base);
-            base = nb;
-            if (base >= ce) break;
-        }
+    // kScanSteps steps per wave, fully unrolled and unconditional: steps past
+    // the end re-read the last key and store nothing, which keeps every load
+    // at its place in the pipeline (the compiler does not sink loads into
+    // guarded computes and its waits stay exact).
+    const int base = cs + wid * WKEYS;
+    uint4 bufA[G][KSTEPS], bufB[G][KSTEPS];
+    loadG(bufA, base);
+#pragma unroll
+    for (int it = 0; it < kScanSteps; it += 2) {
+        if (it + 1 < kScanSteps) loadG(bufB, base + (it + 1) * STEP);
+        computeG(bufA, base + it * STEP);
+        if (it + 2 < kScanSteps) loadG(bufA, base + (it + 2) * STEP);
+        if (it + 1 < kScanSteps) computeG(bufB, base + (it + 1) * STEP);
     }
-
+    __syncthreads();
+    float* srow = a.scores + (long long)row * a.score_stride;
+    for (int x = threadIdx.x; x < ce - cs; x += 256) srow[cs + x] = sbuf[x];
     if (HIST) {
-        __syncthreads();
         uint32_t* grow = a.hist + (long long)row * kHist0Bins;
         for (int x = threadIdx.x; x < kHist0Bins; x += 256) {
             const uint32_t v = lhist[x];
@@ -279,10 +284,18 @@ hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s) 
 
 template <int NHT, int KS>
 static void scan_dispatch_hist(const ScanArgs& a, dim3 grid, hipStream_t s) {
-    if (a.hist)
-        scan_kernel<NHT, KS, true><<<grid, dim3(256), 0, s>>>(a);
-    else
-        scan_kernel<NHT, KS, false><<<grid, dim3(256), 0, s>>>(a);
+    constexpr int G = KS == 4 ? 4 : 2;
+    if (a.heads) {
+        if (a.hist)
+            scan_kernel<NHT, KS, G, true, true><<<grid, dim3(256), 0, s>>>(a);
+        else
+            scan_kernel<NHT, KS, G, false, true><<<grid, dim3(256), 0, s>>>(a);
+    } else {
+        if (a.hist)
+            scan_kernel<NHT, KS, G, true, false><<<grid, dim3(256), 0, s>>>(a);
+        else
+            scan_kernel<NHT, KS, G, false, false><<<grid, dim3(256), 0, s>>>(a);
+    }
 }
 
 hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,

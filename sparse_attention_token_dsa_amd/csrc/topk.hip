@@ -27,7 +27,7 @@ namespace sa {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kFilterThreads = 256;
-constexpr int kFilterChunk = 8192;       // dense elements per filter workgroup
+constexpr int kFilterChunk = 4096;       // dense elements per filter workgroup
 constexpr int kLdsCand = 4096;           // keys per LDS candidate buffer
 
 __device__ __forceinline__ unsigned long long make_key(float sc, int idx) {
@@ -104,43 +104,65 @@ __device__ __forceinline__ int dense_len(int row, int T, int offset, int len_div
 // ------------------------------------------------------------ filter
 
 // Global counters per row: [0] = emitted so far, [1] = candidates appended.
+// Each workgroup counts its emits and candidates first, reserves its output
+// ranges with one atomic each, then writes: two passes over its slice (the
+// second hits L2) instead of a global atomic round trip per wave iteration.
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
                                                                      int* counters,
                                                                      unsigned long long* cand) {
     __shared__ uint32_t hist[kHist0Bins];
     __shared__ int s_wave[kFilterThreads / 64];
     __shared__ Thresh th;
+    __shared__ int s_base[2];
     const int row = blockIdx.y;
+    const int tid = threadIdx.x;
     const int n = dense_len(row, a.T, a.offset, a.len_div, a.len_cap);
     const int lo = blockIdx.x * kFilterChunk;
     if (lo >= n) return;
     const int hi = min(lo + kFilterChunk, n);
     const uint32_t* h0 = a.hist0 + (long long)row * kHist0Bins;
-    for (int x = threadIdx.x; x < kHist0Bins; x += kFilterThreads) hist[x] = h0[x];
+    for (int x = tid; x < kHist0Bins; x += kFilterThreads) hist[x] = h0[x];
     __syncthreads();
     const int need = min(a.k, n);
     find_threshold<kFilterThreads>(hist, kHist0Bins, need, s_wave, &th);
     const uint32_t d = (uint32_t)th.dstar;
     const bool take_all = th.gt + th.eq == need;
     const float* src = a.dense + (long long)row * a.dense_stride;
+
+    int ne = 0, nc = 0;
+    for (int u = lo + tid; u < hi; u += kFilterThreads) {
+        const uint32_t dig = ord_key(src[u]) >> (32 - kHist0Bits);
+        ne += (dig > d || (take_all && dig == d)) ? 1 : 0;
+        nc += (!take_all && dig == d) ? 1 : 0;
+    }
+    int E, C;
+    int pe = block_excl_scan<kFilterThreads>(ne, s_wave, &E);
+    int pc = block_excl_scan<kFilterThreads>(nc, s_wave, &C);
+    int* cnt = counters + 2 * row;
+    if (tid == 0) {
+        s_base[0] = E ? atomicAdd(&cnt[0], E) : 0;
+        s_base[1] = C ? atomicAdd(&cnt[1], C) : 0;
+    }
+    __syncthreads();
+    if (ne + nc == 0) return;
+    pe += s_base[0];
+    pc += s_base[1];
     int32_t* oidx = a.out_idx + (long long)row * a.out_stride;
     float* osc = a.out_score ? a.out_score + (long long)row * a.out_stride : nullptr;
     unsigned long long* crow = cand + (long long)row * a.cand_cap;
-    int* cnt = counters + 2 * row;
-    for (int ub = lo; ub < hi; ub += kFilterThreads) {
-        const int u = ub + threadIdx.x;
-        const bool in = u < hi;
-        const float sc = in ? src[u] : 0.f;
+    for (int u = lo + tid; u < hi; u += kFilterThreads) {
+        const float sc = src[u];
         const uint32_t dig = ord_key(sc) >> (32 - kHist0Bits);
-        const bool emit = in && (dig > d || (take_all && dig == d));
-        const bool app = in && !take_all && dig == d;
-        const int slot = wave_append(emit, &cnt[0]);
-        if (emit && slot < need) {
-            oidx[slot] = u;
-            if (osc) osc[slot] = sc;
+        if (dig > d || (take_all && dig == d)) {
+            if (pe < need) {
+                oidx[pe] = u;
+                if (osc) osc[pe] = sc;
+            }
+            ++pe;
+        } else if (dig == d) {
+            if (pc < a.cand_cap) crow[pc] = make_key(sc, u);
+            ++pc;
         }
-        const int cslot = wave_append(app, &cnt[1]);
-        if (app && cslot < a.cand_cap) crow[cslot] = make_key(sc, u);
     }
 }
 
