@@ -132,8 +132,8 @@ def main():
         step()
     torch.cuda.synchronize(dev)
 
-    # Timed region: exactly `steps` steps between two synchronisations, with
-    # per-kernel HIP events recorded by the library on the launch stream.
+    # Eager pass: per-kernel HIP events recorded by the library on the launch
+    # stream over exactly `steps` steps.
     api.profile_enable(True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
@@ -143,6 +143,34 @@ def main():
     t1 = time.perf_counter()
     kern = api.profile_read()
     api.profile_enable(False)
+    ms_eager = (t1 - t0) * 1e3 / args.steps
+
+    # The step captured once into a HIP graph (no allocation, no memset nodes:
+    # the library clears its state with a fill kernel), replayed for the
+    # timed value.  Every replay of the check below must match the eager
+    # result exactly (same kernels, same inputs).
+    ref = {m: (o[0].clone(), o[1].clone()) for m, o in outs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        for m, o in outs.items():
+            a_idx = torch.sort(o[0], -1)[0]
+            r_idx = torch.sort(ref[m][0], -1)[0]
+            if not torch.equal(a_idx, r_idx):
+                raise RuntimeError("graph replay differs from the eager step (%s)" % m)
+        step()  # eager work between replays
+        torch.cuda.synchronize(dev)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     # Per-selector split (separate pass, torch events between the calls).
@@ -190,6 +218,9 @@ def main():
                    "hisa": {"b": b, "r": r},
                    "step": "pool(b=128,B=1024) + DSA + MISA + MISA-dagger + HISA"},
         "topk_rows_per_s": 4 * rows / (ms_step * 1e-3),
+        "timing": "value and ms_per_step: the step replayed as one HIP graph; "
+                  "ms_per_step_eager and the kernel table: eager launches with HIP events",
+        "ms_per_step_eager": ms_eager,
         "selector_ms": {n: round(v, 4) for n, v in split.items()},
         "selector_scores_per_s": {n: rows * L / (split[n] * 1e-3)
                                   for n in ("dsa", "misa", "misa_dagger", "hisa")},

@@ -101,9 +101,9 @@ int check_ptrs(const void* q, const void* w, const void* k, const void* out_idx)
     return SA_OK;
 }
 
-// Scan chunk: a workgroup covers 4 waves x kScanSteps steps of 64 keys (16
-// for block representatives, which use two 16-key groups per step).
-int scan_chunk(int ksteps) { return 4 * (ksteps == 4 ? 64 : 32) * sa::kScanSteps; }
+// Dense score rows are padded to a multiple of 64 floats (aligned float4
+// reads in the top-k filter).
+long long score_stride(int L) { return ((long long)L + 63) / 64 * 64; }
 
 constexpr int kPrefillMinT = 16;
 
@@ -122,8 +122,7 @@ bool any_partial(const sa_shape* s, int block) {
 struct DsaPlan {
     bool prefill;
     float* scores;
-    uint32_t* hist;
-    int* counters;
+    uint32_t* state;
     unsigned long long* cand;
     float* surv_score;
     int32_t* surv_idx;
@@ -142,23 +141,22 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
         p.surv_idx = cv.take<int32_t>(rows * maxn);
         p.surv_count = cv.take<int32_t>(rows);
     } else {
-        p.scores = cv.take<float>(rows * s->L);
-        p.hist = cv.take<uint32_t>(rows * (sa::kHist0Bins + 2));
-        p.counters = reinterpret_cast<int*>(p.hist ? p.hist + rows * sa::kHist0Bins : nullptr);
+        p.scores = cv.take<float>(rows * score_stride(s->L));
+        p.state = cv.take<uint32_t>(rows * sa::kRowState);
         p.cand = cv.take<unsigned long long>(rows * maxn);
     }
     p.bytes = cv.off + 256;
     return p;
 }
 
-// Decode-style path: score rows (+ first-digit histogram), filter, finish.
+// Decode-style path: score rows (+ row state), filter, finish.
 hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                           const sa_shape* s, const int32_t* heads, int hsel, float* scores,
-                          uint32_t* hist, int* counters, unsigned long long* cand, int k,
-                          int32_t* out_idx, float* out_score, hipStream_t st) {
+                          uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
+                          float* out_score, hipStream_t st) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
-    hipError_t e = sa::launch_fill_u32(hist, rows * (sa::kHist0Bins + 2), 0u, st);
+    hipError_t e = sa::launch_fill_u32(state, rows * sa::kRowState, 0u, st);
     if (e != hipSuccess) return e;
     sa::ScanArgs a{};
     a.q = q;
@@ -172,27 +170,28 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.offset = s->causal_offset;
     a.len_div = 1;
     a.len_cap = s->L;
-    a.chunk = scan_chunk(4);
+    a.chunk = sa::scan_chunk(4);
     a.scores = scores;
-    a.score_stride = s->L;
-    a.hist = hist;
+    a.score_stride = score_stride(s->L);
+    a.state = state;
+    a.k = k;
     const int nht = ((heads ? hsel : s->H) + 15) / 16;
     e = sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
     if (e != hipSuccess) return e;
     sa::TopkArgs t{};
     t.dense = scores;
-    t.dense_stride = s->L;
+    t.dense_stride = score_stride(s->L);
     t.T = s->T;
     t.offset = s->causal_offset;
     t.len_div = 1;
     t.len_cap = s->L;
-    t.hist0 = hist;
+    t.state = state;
     t.k = k;
     t.out_idx = out_idx;
     t.out_score = out_score;
     t.out_stride = k;
     t.cand_cap = maxn;
-    return sa::launch_topk_dense_filtered(t, (int)rows, maxn, counters, cand, st);
+    return sa::launch_topk_dense_filtered(t, (int)rows, maxn, cand, st);
 }
 
 hipError_t run_list_topk(const float* ls, const int32_t* li, long long stride,
@@ -219,8 +218,7 @@ struct MisaPlan {
     uint8_t* flag;
     int32_t* heads;
     float* scores;
-    uint32_t* hist;
-    int* counters;
+    uint32_t* state;
     unsigned long long* cand;
     int32_t* pool_idx;
     float* list_score;
@@ -241,9 +239,8 @@ MisaPlan plan_misa(const sa_shape* s, int B, int h, int kp, bool pooled_given, b
         p.flag = cv.take<uint8_t>(rows);
     }
     p.heads = cv.take<int32_t>(rows * h);
-    p.scores = cv.take<float>(rows * s->L);
-    p.hist = cv.take<uint32_t>(rows * (sa::kHist0Bins + 2));
-    p.counters = reinterpret_cast<int*>(p.hist ? p.hist + rows * sa::kHist0Bins : nullptr);
+    p.scores = cv.take<float>(rows * score_stride(s->L));
+    p.state = cv.take<uint32_t>(rows * sa::kRowState);
     p.cand = cv.take<unsigned long long>(rows * maxn);
     if (kp > 0) {
         p.pool_idx = cv.take<int32_t>(rows * kp);
@@ -410,8 +407,8 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                           s->topk, out_idx, out_score, st);
         if (e != hipSuccess) return hip_fail(e, "prefill top-k");
     } else {
-        e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.hist, p.counters, p.cand,
-                           s->topk, out_idx, out_score, st);
+        e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand, s->topk,
+                           out_idx, out_score, st);
         if (e != hipSuccess) return hip_fail(e, "decode scan");
     }
     return SA_OK;
@@ -501,14 +498,14 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     e = sa::launch_router(ra, rows, st);
     if (e != hipSuccess) return hip_fail(e, "router");
     if (k_prime == 0) {
-        e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.hist, p.counters, p.cand,
-                           s->topk, out_idx, out_score, st);
+        e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, s->topk,
+                           out_idx, out_score, st);
         if (e != hipSuccess) return hip_fail(e, "routed scan");
         return SA_OK;
     }
     int32_t* pool_idx = out_pool ? out_pool : p.pool_idx;
-    e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.hist, p.counters, p.cand, k_prime,
-                       pool_idx, nullptr, st);
+    e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, k_prime, pool_idx,
+                       nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "routed scan");
     sa::GatherArgs ga{};
     ga.q = q;
@@ -523,7 +520,6 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     ga.H = s->H;
     ga.L = s->L;
     ga.offset = s->causal_offset;
-    ga.chunk = 512;
     ga.out_score = p.list_score;
     ga.out_idx = p.list_idx;
     e = sa::launch_gather(ga, rows, (s->H + 15) / 16, false, st);
@@ -586,7 +582,7 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
     a.offset = s->causal_offset;
     a.len_div = block_b;
     a.len_cap = nblk;
-    a.chunk = scan_chunk(8);
+    a.chunk = sa::scan_chunk(8);
     a.scores = p.bscores;
     a.score_stride = nblk;
     e = sa::launch_scan(a, rows, (s->H + 15) / 16, 8, false, st);
@@ -619,7 +615,6 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
     ga.H = s->H;
     ga.L = s->L;
     ga.offset = s->causal_offset;
-    ga.chunk = 512;
     ga.out_score = p.list_score;
     ga.out_idx = p.list_idx;
     e = sa::launch_gather(ga, rows, (s->H + 15) / 16, true, st);

@@ -14,8 +14,21 @@ constexpr int kD = 128;          // indexer head dim (bf16 elements per key)
 constexpr int kMaxH = 64;        // heads supported
 constexpr int kHist0Bits = 12;   // first radix digit = top 12 bits of the ordered score
 constexpr int kHist0Bins = 1 << kHist0Bits;
-constexpr int kScanSteps = 4;        // unrolled steps per scan wave
-constexpr int kScanMaxChunk = 2048;  // keys per scan workgroup (LDS score staging)
+constexpr int kScanMaxChunk = 1024;  // keys per scan workgroup (LDS score staging)
+constexpr int kGatherGroups = 4;     // 16-candidate groups per gather wave
+constexpr int kGatherChunk = 4 * 16 * kGatherGroups;
+// Per-row state of the dense top-k, zeroed before each scan: the first-digit
+// histogram, then control words.
+constexpr int kRowState = kHist0Bins + 8;
+enum RowCtl {
+    CTL_EMITTED = 0,  // winners written by the filter
+    CTL_CANDS = 1,    // threshold-digit candidates appended by the filter
+    CTL_DONE = 2,     // scan workgroups finished
+    CTL_NEED = 3,     // min(k, n)
+    CTL_DIGIT = 4,    // first-digit value holding the k-th score
+    CTL_GT = 5,       // scores above that digit
+    CTL_EQ = 6        // scores on that digit
+};
 
 // ------------------------------------------------------------ scalars
 
@@ -115,7 +128,9 @@ struct ScanArgs {
     int chunk;              // keys per workgroup (multiple of 128)
     float* scores;          // [rows, score_stride]
     long long score_stride;
-    uint32_t* hist;         // [rows, 4096] or null
+    uint32_t* state;        // [rows, kRowState] (zeroed) or null: build the first-digit
+                            // histogram and the k-th-score digit for the dense top-k
+    int k;                  // top-k size for the state
 };
 
 struct GatherArgs {
@@ -128,7 +143,6 @@ struct GatherArgs {
     int bsz;                // block mode: tokens per listed block
     int ncand;              // candidates per row
     int T, H, L, offset;
-    int chunk;
     float* out_score;       // [rows, ncand]
     int32_t* out_idx;       // [rows, ncand]
 };
@@ -157,7 +171,7 @@ struct TopkArgs {
     long long list_stride;
     const int32_t* list_count;  // per-row counts or null (then list_cap)
     int list_cap;
-    const uint32_t* hist0;      // optional precomputed first-digit histogram [rows, 4096]
+    uint32_t* state;            // dense filter path: per-row state left by the scan
     int k;
     int32_t* out_idx;           // [rows, out_stride]
     float* out_score;           // nullable
@@ -181,15 +195,16 @@ struct PrefillArgs {
 hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,
                        hipStream_t s);
+int scan_chunk(int ksteps);  // keys per scan workgroup for 4 (keys) or 8 (block reps) k-steps
 hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
                          hipStream_t s);
 hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s);
 hipError_t launch_tail(const uint16_t* keys, long long seq_stride, int T, int offset, int L,
                        int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s);
-// Dense rows with a first-digit histogram: multi-workgroup filter + per-row finish.
-// counters: [rows, 2] int, zeroed; cand: [rows, a.cand_cap] keys.
-hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn, int* counters,
+// Dense rows scanned with a row state: multi-workgroup filter + per-row finish.
+// cand: [rows, a.cand_cap] keys.
+hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn,
                                       unsigned long long* cand, hipStream_t s);
 hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16_t* out,
                        hipStream_t s);

@@ -9,18 +9,24 @@
 // The ReLU, the w-weighted head sum and the causal bound are applied to the
 // accumulator registers; only one fp32 score per key leaves the kernel.
 #include "sa_frag.h"
+#include "sa_select.h"
 
 namespace sa {
 
 // ------------------------------------------------------------ scan
 
 // One workgroup = 4 waves scans keys [cs, ce) of one query row (ce - cs <=
-// 4*G*16*kScanSteps).  Each wave takes G*16 consecutive keys per step and the
+// 4*G*16*NSTEP).  Each wave takes G*16 consecutive keys per step and the
 // workgroup advances 4*G*16 keys per step; the next step's key loads are in
 // flight while the current step is computed (two register buffers).  Scores
 // are staged in LDS and written out coalesced at the end, so the loop issues
 // no global stores.
-template <int NHT, int KSTEPS, int G, bool HIST, bool ROUTED>
+//
+// With a row state (HIST), the scores' first radix digit is histogrammed in
+// LDS and added to the row's global histogram; the last workgroup of the row
+// to finish then finds the digit that holds the row's k-th score, once, for
+// the top-k filter.
+template <int NHT, int KSTEPS, int G, int NSTEP, bool HIST, bool ROUTED>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     constexpr int KROW = KSTEPS * 32;
     constexpr int WKEYS = G * 16;
@@ -77,7 +83,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         }
     };
 
-    // kScanSteps steps per wave, fully unrolled and unconditional: steps past
+    // NSTEP steps per wave, fully unrolled and unconditional: steps past
     // the end re-read the last key and store nothing, which keeps every load
     // at its place in the pipeline (the compiler does not sink loads into
     // guarded computes and its waits stay exact).
@@ -85,20 +91,43 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     uint4 bufA[G][KSTEPS], bufB[G][KSTEPS];
     loadG(bufA, base);
 #pragma unroll
-    for (int it = 0; it < kScanSteps; it += 2) {
-        if (it + 1 < kScanSteps) loadG(bufB, base + (it + 1) * STEP);
+    for (int it = 0; it < NSTEP; it += 2) {
+        if (it + 1 < NSTEP) loadG(bufB, base + (it + 1) * STEP);
         computeG(bufA, base + it * STEP);
-        if (it + 2 < kScanSteps) loadG(bufA, base + (it + 2) * STEP);
-        if (it + 1 < kScanSteps) computeG(bufB, base + (it + 1) * STEP);
+        if (it + 2 < NSTEP) loadG(bufA, base + (it + 2) * STEP);
+        if (it + 1 < NSTEP) computeG(bufB, base + (it + 1) * STEP);
     }
     __syncthreads();
     float* srow = a.scores + (long long)row * a.score_stride;
     for (int x = threadIdx.x; x < ce - cs; x += 256) srow[cs + x] = sbuf[x];
     if (HIST) {
-        uint32_t* grow = a.hist + (long long)row * kHist0Bins;
+        uint32_t* grow = a.state + (long long)row * kRowState;
+        int* ctl = reinterpret_cast<int*>(grow + kHist0Bins);
         for (int x = threadIdx.x; x < kHist0Bins; x += 256) {
             const uint32_t v = lhist[x];
             if (v) atomicAdd(&grow[x], v);
+        }
+        __threadfence();
+        __syncthreads();
+        __shared__ int s_last;
+        const int nchunks = (n + a.chunk - 1) / a.chunk;
+        if (threadIdx.x == 0) s_last = atomicAdd(&ctl[CTL_DONE], 1) == nchunks - 1;
+        __syncthreads();
+        if (s_last) {
+            __threadfence();
+            for (int x = threadIdx.x; x < kHist0Bins; x += 256)
+                lhist[x] = __hip_atomic_load(&grow[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            __shared__ int s_wave[4];
+            __shared__ Thresh th;
+            const int need = min(a.k, n);
+            find_threshold<256>(lhist, kHist0Bins, need, s_wave, &th);
+            if (threadIdx.x == 0) {
+                ctl[CTL_NEED] = need;
+                ctl[CTL_DIGIT] = th.dstar;
+                ctl[CTL_GT] = th.gt;
+                ctl[CTL_EQ] = th.eq;
+            }
         }
     }
 }
@@ -108,41 +137,54 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 // Rescore a per-row candidate list with all heads.  List mode: candidate u
 // is token list[u]; block mode: candidate u is token list[u / bsz] * bsz +
 // u % bsz.  Candidates past the causal bound, past L or with a negative id
-// get score -inf and index -1.
+// get score -inf and index -1.  A workgroup takes kGatherChunk candidates;
+// each wave resolves its kGatherGroups x 16 candidate ids, issues every key
+// load (16 KiB in flight per wave), then runs the MFMA groups.
 template <int NHT, bool BLOCKS>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
+    constexpr int NG = kGatherGroups;
     const int row = blockIdx.y;
     const int b = row / a.T;
     const int t = a.offset + (row - b * a.T);
-    const int cs = blockIdx.x * a.chunk;
+    const int cs = blockIdx.x * kGatherChunk;
     if (cs >= a.ncand) return;
-    const int ce = min(cs + a.chunk, a.ncand);
-    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    QFrag<NHT> f;
-    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
-                    nullptr, 0, g, c);
-    const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
+    const int ce = min(cs + kGatherChunk, a.ncand);
+    const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t* lrow = a.list + (long long)row * a.list_len;
-    float* osc = a.out_score + (long long)row * a.ncand;
-    int32_t* oid = a.out_idx + (long long)row * a.ncand;
-    for (int base = cs + wid * 16; base < ce; base += 64) {
-        const int u = base + c;
+    int sid[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const int u = cs + (gi * 4 + wid) * 16 + c;
         int s = -1;
         if (u < ce) {
             if (BLOCKS) {
-                const int blk = lrow[u / a.bsz];
-                s = blk >= 0 ? blk * a.bsz + (u - (u / a.bsz) * a.bsz) : -1;
+                const int q = u / a.bsz;
+                const int blk = lrow[q];
+                s = blk >= 0 ? blk * a.bsz + (u - q * a.bsz) : -1;
             } else {
                 s = lrow[u];
             }
         }
-        const bool valid = s >= 0 && s <= t && s < a.L;
-        uint4 kb[4];
-        load_key<4>(kb, kseq + (long long)(valid ? s : 0) * kD, g);
-        const float sc = group_score<NHT, 4>(f, kb);
+        sid[gi] = (s >= 0 && s <= t && s < a.L) ? s : -1;
+    }
+    QFrag<NHT> f;
+    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
+                    nullptr, 0, g, c);
+    const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
+    uint4 kb[NG][4];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+        load_key<4>(kb[gi], kseq + (long long)(sid[gi] >= 0 ? sid[gi] : 0) * kD, g);
+    float* osc = a.out_score + (long long)row * a.ncand;
+    int32_t* oid = a.out_idx + (long long)row * a.ncand;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+        const int u = cs + (gi * 4 + wid) * 16 + c;
+        const float sc = group_score<NHT, 4>(f, kb[gi]);
         if (g == 0 && u < ce) {
-            osc[u] = valid ? sc : -INFINITY;
-            oid[u] = valid ? s : -1;
+            osc[u] = sid[gi] >= 0 ? sc : -INFINITY;
+            oid[u] = sid[gi];
         }
     }
 }
@@ -199,17 +241,22 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
         }
     __syncthreads();
     if (wid == 0) {
+        __shared__ float sE[kMaxH];
         const int j = lane;
-        float E = -1.f;
+        float E = -1.f;  // absent heads rank below every real head (E >= 0)
         if (j < a.H) {
             const float S = part[0][j] + part[1][j] + part[2][j] + part[3][j];
             E = fabsf(a.w[(long long)row * a.H + j]) * S / (float)Mt;
             if (a.E_out) a.E_out[(long long)row * a.H + j] = E;
         }
+        sE[j] = E;  // same wave writes then reads: LDS keeps the order
         int rank = 0;
-        for (int j2 = 0; j2 < 64; ++j2) {
-            const float e2 = __shfl(E, j2);
-            rank += (e2 > E) || (e2 == E && j2 < j);
+#pragma unroll
+        for (int j4 = 0; j4 < kMaxH; j4 += 4) {
+            const float4 e4 = *reinterpret_cast<const float4*>(&sE[j4]);
+            const float es[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rank += (es[u] > E) || (es[u] == E && j4 + u < j);
         }
         const bool sel = j < a.H && rank < a.h;
         const unsigned long long msk = __ballot(sel);
@@ -282,20 +329,34 @@ hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s) 
     return hipGetLastError();
 }
 
+// Keys (KSTEPS = 4): 4 groups x 4 steps per wave, 1024 keys per workgroup.
+// Block representatives (KSTEPS = 8, a few thousand per row at most): 2
+// groups x 1 step, 128 per workgroup, so the grid still covers the chip.
+template <int KS>
+constexpr int scan_groups() { return KS == 4 ? 4 : 2; }
+template <int KS>
+constexpr int scan_steps() { return KS == 4 ? 4 : 1; }
+
 template <int NHT, int KS>
 static void scan_dispatch_hist(const ScanArgs& a, dim3 grid, hipStream_t s) {
-    constexpr int G = KS == 4 ? 4 : 2;
+    constexpr int G = scan_groups<KS>();
+    constexpr int NS = scan_steps<KS>();
     if (a.heads) {
-        if (a.hist)
-            scan_kernel<NHT, KS, G, true, true><<<grid, dim3(256), 0, s>>>(a);
+        if (a.state)
+            scan_kernel<NHT, KS, G, NS, true, true><<<grid, dim3(256), 0, s>>>(a);
         else
-            scan_kernel<NHT, KS, G, false, true><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NS, false, true><<<grid, dim3(256), 0, s>>>(a);
     } else {
-        if (a.hist)
-            scan_kernel<NHT, KS, G, true, false><<<grid, dim3(256), 0, s>>>(a);
+        if (a.state)
+            scan_kernel<NHT, KS, G, NS, true, false><<<grid, dim3(256), 0, s>>>(a);
         else
-            scan_kernel<NHT, KS, G, false, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NS, false, false><<<grid, dim3(256), 0, s>>>(a);
     }
+}
+
+int scan_chunk(int ksteps) {
+    return ksteps == 4 ? 4 * 16 * scan_groups<4>() * scan_steps<4>()
+                       : 4 * 16 * scan_groups<8>() * scan_steps<8>();
 }
 
 hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,
@@ -325,7 +386,7 @@ hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool ro
 
 hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
                          hipStream_t s) {
-    const dim3 grid((unsigned)((a.ncand + a.chunk - 1) / a.chunk), (unsigned)rows);
+    const dim3 grid((unsigned)((a.ncand + kGatherChunk - 1) / kGatherChunk), (unsigned)rows);
     prof_begin(K_GATHER, s);
 #define SA_GATHER(N)                                                            \
     if (block_mode)                                                             \

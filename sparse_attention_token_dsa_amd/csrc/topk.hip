@@ -21,7 +21,7 @@
 //    scores) and (score, index) lists (rescored pools, prefill survivors).
 //    Candidates of later digits are compacted into LDS when they fit; if not,
 //    the source is rescanned with a prefix filter.
-#include "sa_common.h"
+#include "sa_select.h"
 
 namespace sa {
 
@@ -41,59 +41,6 @@ __device__ __forceinline__ float key_score(unsigned long long k) {
 __constant__ int kShift[6] = {52, 42, 32, 20, 10, 0};
 __constant__ int kWidth[6] = {12, 10, 10, 12, 10, 10};
 
-// Block-wide exclusive scan of one int per thread; *total gets the sum.
-// Every thread of the block must call it (it contains barriers).
-template <int NT>
-__device__ int block_excl_scan(int v, int* s_wave, int* total) {
-    const int lane = lane_id(), wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_wave[wid] = x;
-    __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        const int sw = s_wave[w];
-        if (w < wid) base += sw;
-        tot += sw;
-    }
-    __syncthreads();
-    *total = tot;
-    return base + x - v;
-}
-
-struct Thresh {
-    int dstar, gt, eq;
-};
-
-// Digit value holding the need-th largest key, scanning bins from the top.
-// Returns it in *out (written to shared memory by one thread, then synced).
-template <int NT>
-__device__ void find_threshold(const uint32_t* hist, int nbins, int need, int* s_wave,
-                               Thresh* out) {
-    const int per = nbins / NT;
-    const int tid = threadIdx.x;
-    int local = 0;
-    for (int j = 0; j < per; ++j) local += (int)hist[nbins - 1 - (tid * per + j)];
-    int total;
-    int cum = block_excl_scan<NT>(local, s_wave, &total);
-    for (int j = 0; j < per; ++j) {
-        const int bin = nbins - 1 - (tid * per + j);
-        const int h = (int)hist[bin];
-        if (cum < need && need <= cum + h) {
-            out->dstar = bin;
-            out->gt = cum;
-            out->eq = h;
-        }
-        cum += h;
-    }
-    __syncthreads();
-}
-
 __device__ __forceinline__ int dense_len(int row, int T, int offset, int len_div, int len_cap) {
     const int b = row / T;
     const int t = offset + (row - b * T);
@@ -103,66 +50,72 @@ __device__ __forceinline__ int dense_len(int row, int T, int offset, int len_div
 
 // ------------------------------------------------------------ filter
 
-// Global counters per row: [0] = emitted so far, [1] = candidates appended.
-// Each workgroup counts its emits and candidates first, reserves its output
-// ranges with one atomic each, then writes: two passes over its slice (the
-// second hits L2) instead of a global atomic round trip per wave iteration.
+// The scan left, per row, the digit d holding the k-th score (CTL_DIGIT),
+// the number of scores above it (CTL_GT) and on it (CTL_EQ).  Each workgroup
+// sweeps kFilterChunk scores (float4 loads, the row stride is a multiple of
+// 64), stages its winners (digit > d, or = d when those fit exactly) and its
+// candidates (digit = d) in LDS, reserves its output ranges with one atomic
+// each and copies them out.
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
-                                                                     int* counters,
                                                                      unsigned long long* cand) {
-    __shared__ uint32_t hist[kHist0Bins];
-    __shared__ int s_wave[kFilterThreads / 64];
-    __shared__ Thresh th;
-    __shared__ int s_base[2];
+    __shared__ int s_idx[kFilterChunk];
+    __shared__ float s_sc[kFilterChunk];
+    __shared__ unsigned long long s_cand[kFilterChunk];
+    __shared__ int s_ne, s_nc, s_base[2];
     const int row = blockIdx.y;
     const int tid = threadIdx.x;
     const int n = dense_len(row, a.T, a.offset, a.len_div, a.len_cap);
     const int lo = blockIdx.x * kFilterChunk;
     if (lo >= n) return;
     const int hi = min(lo + kFilterChunk, n);
-    const uint32_t* h0 = a.hist0 + (long long)row * kHist0Bins;
-    for (int x = tid; x < kHist0Bins; x += kFilterThreads) hist[x] = h0[x];
-    __syncthreads();
-    const int need = min(a.k, n);
-    find_threshold<kFilterThreads>(hist, kHist0Bins, need, s_wave, &th);
-    const uint32_t d = (uint32_t)th.dstar;
-    const bool take_all = th.gt + th.eq == need;
-    const float* src = a.dense + (long long)row * a.dense_stride;
-
-    int ne = 0, nc = 0;
-    for (int u = lo + tid; u < hi; u += kFilterThreads) {
-        const uint32_t dig = ord_key(src[u]) >> (32 - kHist0Bits);
-        ne += (dig > d || (take_all && dig == d)) ? 1 : 0;
-        nc += (!take_all && dig == d) ? 1 : 0;
-    }
-    int E, C;
-    int pe = block_excl_scan<kFilterThreads>(ne, s_wave, &E);
-    int pc = block_excl_scan<kFilterThreads>(nc, s_wave, &C);
-    int* cnt = counters + 2 * row;
+    int* ctl = reinterpret_cast<int*>(a.state + (long long)row * kRowState + kHist0Bins);
+    const int need = ctl[CTL_NEED];
+    const uint32_t d = (uint32_t)ctl[CTL_DIGIT];
+    const bool take_all = ctl[CTL_GT] + ctl[CTL_EQ] == need;
     if (tid == 0) {
-        s_base[0] = E ? atomicAdd(&cnt[0], E) : 0;
-        s_base[1] = C ? atomicAdd(&cnt[1], C) : 0;
+        s_ne = 0;
+        s_nc = 0;
     }
     __syncthreads();
-    if (ne + nc == 0) return;
-    pe += s_base[0];
-    pc += s_base[1];
+    const float* src = a.dense + (long long)row * a.dense_stride;
+    for (int u0 = lo + tid * 4; u0 < hi; u0 += kFilterThreads * 4) {
+        const float4 v4 = *reinterpret_cast<const float4*>(src + u0);
+        const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int u = u0 + j;
+            const bool in = u < hi;
+            const uint32_t dig = ord_key(vs[j]) >> (32 - kHist0Bits);
+            const bool emit = in && (dig > d || (take_all && dig == d));
+            const bool app = in && !take_all && dig == d;
+            const int slot = wave_append(emit, &s_ne);
+            if (emit) {
+                s_idx[slot] = u;
+                s_sc[slot] = vs[j];
+            }
+            const int cslot = wave_append(app, &s_nc);
+            if (app) s_cand[cslot] = make_key(vs[j], u);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        s_base[0] = s_ne ? atomicAdd(&ctl[CTL_EMITTED], s_ne) : 0;
+        s_base[1] = s_nc ? atomicAdd(&ctl[CTL_CANDS], s_nc) : 0;
+    }
+    __syncthreads();
     int32_t* oidx = a.out_idx + (long long)row * a.out_stride;
     float* osc = a.out_score ? a.out_score + (long long)row * a.out_stride : nullptr;
-    unsigned long long* crow = cand + (long long)row * a.cand_cap;
-    for (int u = lo + tid; u < hi; u += kFilterThreads) {
-        const float sc = src[u];
-        const uint32_t dig = ord_key(sc) >> (32 - kHist0Bits);
-        if (dig > d || (take_all && dig == d)) {
-            if (pe < need) {
-                oidx[pe] = u;
-                if (osc) osc[pe] = sc;
-            }
-            ++pe;
-        } else if (dig == d) {
-            if (pc < a.cand_cap) crow[pc] = make_key(sc, u);
-            ++pc;
+    for (int x = tid; x < s_ne; x += kFilterThreads) {
+        const int slot = s_base[0] + x;
+        if (slot < need) {
+            oidx[slot] = s_idx[x];
+            if (osc) osc[slot] = s_sc[x];
         }
+    }
+    unsigned long long* crow = cand + (long long)row * a.cand_cap;
+    for (int x = tid; x < s_nc; x += kFilterThreads) {
+        const long long cs = (long long)s_base[1] + x;
+        if (cs < a.cand_cap) crow[cs] = s_cand[x];
     }
 }
 
@@ -190,9 +143,8 @@ __device__ __forceinline__ unsigned long long src_key(int kind, const float* dsr
 }
 
 // mode: SRC_DENSE / SRC_LIST: full selection from level 0.
-//       SRC_KEYS: continue after topk_filter_kernel (candidates + hist0).
+//       SRC_KEYS: continue after topk_filter_kernel (its candidates + row state).
 __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, int kind,
-                                                                   const int* counters,
                                                                    const unsigned long long* cand) {
     __shared__ SelShared S;
     const int row = blockIdx.x;
@@ -220,23 +172,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
     unsigned long long pfx = 0ull;
     int pfx_shift = 64;  // 64: no prefix filter yet
     if (kind == SRC_KEYS) {
-        const uint32_t* h0 = a.hist0 + (long long)row * kHist0Bins;
-        for (int x = tid; x < kHist0Bins; x += kTopkThreads) S.hist[x] = h0[x];
-        __syncthreads();
-        need = min(a.k, nsrc0);
-        find_threshold<kTopkThreads>(S.hist, kHist0Bins, need, S.wave, &S.th);
+        const int* ctl = reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
+                                                      kHist0Bins);
+        need = ctl[CTL_NEED];
+        const int gt = ctl[CTL_GT];
         for (int u = need + tid; u < a.k; u += kTopkThreads) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
-        if (S.th.gt + S.th.eq == need) return;  // the filter emitted everything
-        need_rem = need - S.th.gt;
-        pfx = (unsigned long long)S.th.dstar;
+        if (gt + ctl[CTL_EQ] == need) return;  // the filter emitted everything
+        need_rem = need - gt;
+        pfx = (unsigned long long)ctl[CTL_DIGIT];
         pfx_shift = kShift[0];
         start_level = 1;
         ksrc = cand + (long long)row * a.cand_cap;
-        nsrc0 = (int)min((long long)counters[2 * row + 1], a.cand_cap);
-        if (tid == 0) S.out = S.th.gt;
+        nsrc0 = (int)min((long long)ctl[CTL_CANDS], a.cand_cap);
+        if (tid == 0) S.out = gt;
         __syncthreads();
     } else {
         for (int x = tid; x < kHist0Bins; x += kTopkThreads) S.hist[x] = 0u;
@@ -334,17 +285,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
     }
 }
 
-hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn, int* counters,
+hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn,
                                       unsigned long long* cand, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     prof_begin(K_TOPK_FILTER, s);
     topk_filter_kernel<<<dim3((maxn + kFilterChunk - 1) / kFilterChunk, rows),
-                         dim3(kFilterThreads), 0, s>>>(a, counters, cand);
+                         dim3(kFilterThreads), 0, s>>>(a, cand);
     prof_end(K_TOPK_FILTER, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_begin(K_TOPK, s);
-    topk_select_kernel<<<dim3(rows), dim3(kTopkThreads), 0, s>>>(a, SRC_KEYS, counters, cand);
+    topk_select_kernel<<<dim3(rows), dim3(kTopkThreads), 0, s>>>(a, SRC_KEYS, cand);
     prof_end(K_TOPK, s);
     return hipGetLastError();
 }
@@ -353,7 +304,7 @@ hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     const int kind = a.dense ? SRC_DENSE : SRC_LIST;
     prof_begin(K_TOPK, s);
-    topk_select_kernel<<<dim3(rows), dim3(kTopkThreads), 0, s>>>(a, kind, nullptr, nullptr);
+    topk_select_kernel<<<dim3(rows), dim3(kTopkThreads), 0, s>>>(a, kind, nullptr);
     prof_end(K_TOPK, s);
     return hipGetLastError();
 }
