@@ -9,7 +9,6 @@
 // The ReLU, the w-weighted head sum and the causal bound are applied to the
 // accumulator registers; only one fp32 score per key leaves the kernel.
 #include "sa_frag.h"
-#include "sa_select.h"
 
 namespace sa {
 
@@ -23,9 +22,8 @@ namespace sa {
 // no global stores.
 //
 // With a row state (HIST), the scores' first radix digit is histogrammed in
-// LDS and added to the row's global histogram; the last workgroup of the row
-// to finish then finds the digit that holds the row's k-th score, once, for
-// the top-k filter.
+// LDS and added to the row's global histogram for the top-k filter, which
+// runs after this kernel and so sees every workgroup's counts.
 template <int NHT, int KSTEPS, int G, int NSTEP, bool HIST, bool ROUTED>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     constexpr int KROW = KSTEPS * 32;
@@ -62,20 +60,50 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         if (KSTEPS == 8 && tailp && s == n - 1) return tailp;
         return kseq + (long long)s * KROW;
     };
+    // Keys (KSTEPS = 4): coalesced loads, 4 whole 256-byte rows per load
+    // instruction (lane l: key l/16 of the quad, 16-byte chunk l%16), then a
+    // per-wave LDS transpose into the MFMA B layout (lane (g, c) needs key c,
+    // chunk kk*4+g).  Loading the B layout directly would touch 16 rows per
+    // instruction with 64 bytes each, which costs about a third of the HBM
+    // rate.  The transpose tile is XOR-swizzled (chunk ^ key) so both the
+    // row writes and the column reads are free of bank conflicts.
+    __shared__ uint4 tbuf[KSTEPS == 4 ? 4 : 1][KSTEPS == 4 ? 256 : 1];
     // Loads past the end re-read the last key, so they can be unconditional:
     // the wait before each compute then covers exactly the older buffer.
     auto loadG = [&](uint4 (&buf)[G][KSTEPS], int base) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
-            const int s = min(base + gi * 16 + c, ce - 1);
-            load_key<KSTEPS>(buf[gi], kptr(s), g);
+            if (KSTEPS == 4) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = min(base + gi * 16 + 4 * j + (lane >> 4), ce - 1);
+                    buf[gi][j] = ldg16(kseq + (long long)s * kD + (lane & 15) * 8);
+                }
+            } else {
+                const int s = min(base + gi * 16 + c, ce - 1);
+                load_key<KSTEPS>(buf[gi], kptr(s), g);
+            }
         }
     };
     auto computeG = [&](const uint4 (&buf)[G][KSTEPS], int base) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             const int s = base + gi * 16 + c;
-            const float sc = group_score<NHT, KSTEPS>(f, buf[gi]);
+            float sc;
+            if (KSTEPS == 4) {
+                uint4* tp = tbuf[wid];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = 4 * j + (lane >> 4);
+                    tp[key * 16 + ((lane & 15) ^ key)] = buf[gi][j];
+                }
+                uint4 kb[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) kb[kk] = tp[c * 16 + ((kk * 4 + g) ^ c)];
+                sc = group_score<NHT, 4>(f, kb);
+            } else {
+                sc = group_score<NHT, KSTEPS>(f, buf[gi]);
+            }
             if (g == 0 && s < ce) {
                 sbuf[s - cs] = sc;
                 if (HIST) atomicAdd(&lhist[ord_key(sc) >> (32 - kHist0Bits)], 1u);
@@ -102,32 +130,9 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     for (int x = threadIdx.x; x < ce - cs; x += 256) srow[cs + x] = sbuf[x];
     if (HIST) {
         uint32_t* grow = a.state + (long long)row * kRowState;
-        int* ctl = reinterpret_cast<int*>(grow + kHist0Bins);
         for (int x = threadIdx.x; x < kHist0Bins; x += 256) {
             const uint32_t v = lhist[x];
             if (v) atomicAdd(&grow[x], v);
-        }
-        __threadfence();
-        __syncthreads();
-        __shared__ int s_last;
-        const int nchunks = (n + a.chunk - 1) / a.chunk;
-        if (threadIdx.x == 0) s_last = atomicAdd(&ctl[CTL_DONE], 1) == nchunks - 1;
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
-            for (int x = threadIdx.x; x < kHist0Bins; x += 256)
-                lhist[x] = __hip_atomic_load(&grow[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            __shared__ int s_wave[4];
-            __shared__ Thresh th;
-            const int need = min(a.k, n);
-            find_threshold<256>(lhist, kHist0Bins, need, s_wave, &th);
-            if (threadIdx.x == 0) {
-                ctl[CTL_NEED] = need;
-                ctl[CTL_DIGIT] = th.dstar;
-                ctl[CTL_GT] = th.gt;
-                ctl[CTL_EQ] = th.eq;
-            }
         }
     }
 }

@@ -50,28 +50,42 @@ __device__ __forceinline__ int dense_len(int row, int T, int offset, int len_div
 
 // ------------------------------------------------------------ filter
 
-// The scan left, per row, the digit d holding the k-th score (CTL_DIGIT),
-// the number of scores above it (CTL_GT) and on it (CTL_EQ).  Each workgroup
-// sweeps kFilterChunk scores (float4 loads, the row stride is a multiple of
-// 64), stages its winners (digit > d, or = d when those fit exactly) and its
+// The scan left, per row, the histogram of the scores' first digit.  Each
+// workgroup finds the digit d holding the row's k-th score from it, sweeps
+// kFilterChunk scores (float4 loads, the row stride is a multiple of 64),
+// stages its winners (digit > d, or = d when those fit exactly) and its
 // candidates (digit = d) in LDS, reserves its output ranges with one atomic
-// each and copies them out.
+// each and copies them out.  The first workgroup of the row also records d,
+// the count above it and the count on it for the finishing kernel.
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
                                                                      unsigned long long* cand) {
     __shared__ int s_idx[kFilterChunk];
     __shared__ float s_sc[kFilterChunk];
     __shared__ unsigned long long s_cand[kFilterChunk];
     __shared__ int s_ne, s_nc, s_base[2];
+    __shared__ int s_wave[kFilterThreads / 64];
+    __shared__ Thresh th;
     const int row = blockIdx.y;
     const int tid = threadIdx.x;
     const int n = dense_len(row, a.T, a.offset, a.len_div, a.len_cap);
     const int lo = blockIdx.x * kFilterChunk;
     if (lo >= n) return;
     const int hi = min(lo + kFilterChunk, n);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(s_cand);  // 16 KiB, reused below
+    const uint32_t* grow = a.state + (long long)row * kRowState;
+    for (int x = tid; x < kHist0Bins; x += kFilterThreads) hist[x] = grow[x];
+    __syncthreads();
+    const int need = min(a.k, n);
+    find_threshold<kFilterThreads>(hist, kHist0Bins, need, s_wave, &th);
     int* ctl = reinterpret_cast<int*>(a.state + (long long)row * kRowState + kHist0Bins);
-    const int need = ctl[CTL_NEED];
-    const uint32_t d = (uint32_t)ctl[CTL_DIGIT];
-    const bool take_all = ctl[CTL_GT] + ctl[CTL_EQ] == need;
+    const uint32_t d = (uint32_t)th.dstar;
+    const bool take_all = th.gt + th.eq == need;
+    if (blockIdx.x == 0 && tid == 0) {
+        ctl[CTL_NEED] = need;
+        ctl[CTL_DIGIT] = th.dstar;
+        ctl[CTL_GT] = th.gt;
+        ctl[CTL_EQ] = th.eq;
+    }
     if (tid == 0) {
         s_ne = 0;
         s_nc = 0;
