@@ -124,9 +124,7 @@ struct DsaPlan {
     float* scores;
     uint32_t* state;
     unsigned long long* cand;
-    float* surv_score;
-    int32_t* surv_idx;
-    int32_t* surv_count;
+    float* pscores;
     size_t bytes;
 };
 
@@ -137,9 +135,7 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
     const long long maxn = (long long)s->causal_offset + s->T;
     p.prefill = s->T >= kPrefillMinT;
     if (p.prefill) {
-        p.surv_score = cv.take<float>(rows * maxn);
-        p.surv_idx = cv.take<int32_t>(rows * maxn);
-        p.surv_count = cv.take<int32_t>(rows);
+        p.pscores = cv.take<float>(rows * score_stride((int)maxn));
     } else {
         p.scores = cv.take<float>(rows * score_stride(s->L));
         p.state = cv.take<uint32_t>(rows * sa::kRowState);
@@ -396,16 +392,13 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
         a.L = s->L;
         a.offset = s->causal_offset;
         a.k = s->topk;
-        a.qpw = 8;
-        a.surv_score = p.surv_score;
-        a.surv_idx = p.surv_idx;
-        a.surv_count = p.surv_count;
-        a.cap = (long long)s->causal_offset + s->T;
+        a.scores = p.pscores;
+        a.stride = score_stride(s->causal_offset + s->T);
+        a.out_idx = out_idx;
+        a.out_score = out_score;
+        a.out_stride = s->topk;
         e = sa::launch_prefill(a, rows, st);
         if (e != hipSuccess) return hip_fail(e, "prefill");
-        e = run_list_topk(p.surv_score, p.surv_idx, a.cap, p.surv_count, (int)a.cap, rows,
-                          s->topk, out_idx, out_score, st);
-        if (e != hipSuccess) return hip_fail(e, "prefill top-k");
     } else {
         e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand, s->topk,
                            out_idx, out_score, st);

@@ -184,11 +184,11 @@ struct PrefillArgs {
     const float* w;
     const uint16_t* keys;
     int T, H, L, offset, k;
-    int qpw;                    // queries per workgroup
-    float* surv_score;          // [rows, cap]
-    int32_t* surv_idx;          // [rows, cap]
-    int32_t* surv_count;        // [rows]
-    long long cap;
+    float* scores;              // [rows, stride] scores of the legal keys (workspace)
+    long long stride;           // >= offset + T, a multiple of 64
+    int32_t* out_idx;           // [rows, out_stride]
+    float* out_score;           // nullable
+    long long out_stride;
 };
 
 // Launchers (defined next to their kernels).
