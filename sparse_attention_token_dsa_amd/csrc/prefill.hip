@@ -7,22 +7,26 @@
 // sequence (two rows per wave, their heads held as MFMA A fragments in
 // registers: each B fragment read from LDS feeds both rows) and sweeps the
 // legal keys [0, max t] in tiles of 64 keys.  Each tile (16 KiB of bf16 keys)
-// is staged once in LDS for all 8 rows by direct global-to-LDS loads, two
-// stages deep (the next tile is in flight while one is computed), with a
+// is staged once in LDS for all 8 rows by direct global-to-LDS loads, with a
 // 16-byte XOR swizzle so the B-fragment reads are free of bank conflicts.
+// Column c of MFMA group gi is key 4c + gi, so that after the head sum every
+// lane holds the scores of 4 consecutive keys.  Four stages are used in pairs: one wait and one barrier per two tiles, and
+// the next pair's loads have two tiles of compute to arrive.
 //
 // Per tile and row the sweep does no selection work: each legal score is
-// added to the row's LDS histogram (bins of 1/16 octave over [2^-32, 2^32);
-// zero, negative and smaller scores share bin 0, larger ones the last bin)
-// and stored, one coalesced 256-byte store per row, to the row's score line
-// in the workspace (4 bytes per legal key, written once and read once).
+// added to the row's LDS histogram (bins of 1/8 octave over [2^-32, 2^32);
+// zero, negative and smaller scores share bin 0, which is not counted but
+// derived at the end, larger ones the last bin) and stored to the row's
+// score line in the workspace (4 bytes per legal key, written once and read
+// once; one 16-byte non-temporal store per lane per pair of tiles).
 //
 // Finish: after the sweep each wave selects its rows' exact top-k: the
 // histogram gives the bin holding the k-th score; one pass over the row emits
-// the scores above it and collects the ones in it, as 64-bit keys
-// ord(score) << 32 | ~position (ties -> lower position), into LDS; a radix
-// select on those keys (10-bit digits) settles the rest.  Only when the bin
-// holds more keys than the LDS buffer does a digit level re-read the row.
+// the scores above it (staged in LDS, written out 64 at a time) and collects
+// the ones in it, as 64-bit keys ord(score) << 32 | ~position (ties -> lower
+// position), into LDS; a radix select on those keys (9-bit digits) settles
+// the rest.  Only when the bin holds more keys than the LDS buffer does a
+// digit level re-read the row.
 #include "sa_frag.h"
 
 namespace sa {
@@ -31,21 +35,29 @@ constexpr int kPfWaves = 4;
 constexpr int kPfQpw = 2;  // query rows per wave
 constexpr int kPfRows = kPfWaves * kPfQpw;
 constexpr int kPfTile = 64;
-constexpr int kPfBins = 1024;
-// A bin is ord(score) >> 19: sign, exponent and 4 mantissa bits.
-constexpr int kPfBinShift = 19;
-// ord(2^-32) >> 19: prefix of the first inner bin.
+constexpr int kPfStage = kPfTile * 16;  // uint4 per stage (16 KiB)
+constexpr int kPfBins = 512;
+constexpr int kPfDigit = 9;  // radix digit of the finish: 2^9 = kPfBins
+// A bin is ord(score) >> 20: sign, exponent and 3 mantissa bits.
+constexpr int kPfBinShift = 20;
+// ord(2^-32) >> 20: prefix of the first inner bin.
 constexpr int kPfBase = (int)((0x80000000u | (95u << 23)) >> kPfBinShift);
 // Key bits fixed by an inner bin: 63 .. 32 + kPfBinShift.
 constexpr int kPfKeyTop = 32 + kPfBinShift;
-constexpr int kPfCand = 512;  // LDS candidate keys per row
-constexpr int kPfSweep = 8;   // float4 loads in flight per lane in a row pass
-static_assert(kPfRows / 2 * kPfCand * 8 == kPfTile * 16 * 16,
-              "half of the rows' candidate buffers fill one stage");
+constexpr int kPfCand = 1024;  // LDS candidate keys per row: two rows per stage
+constexpr int kPfSweep = 8;    // float4 loads in flight per lane in a row pass
+static_assert(2 * kPfCand * 8 == kPfStage * 16, "two rows' candidate buffers fill one stage");
+static_assert((1 << kPfDigit) == kPfBins, "digit histograms reuse the row histogram");
+static_assert(kPfQpw == 2 && kPfTile == 64, "the 4 lane groups store 2 rows x 2 tiles of a pair");
 
 __device__ __forceinline__ int pf_bin(float sc) {
     const int v = (int)(ord_key(sc) >> kPfBinShift) - kPfBase;
     return v < 0 ? 0 : (v > kPfBins - 1 ? kPfBins - 1 : v);
+}
+
+// Smallest score in bin b, 1 <= b < kPfBins.
+__device__ __forceinline__ float pf_edge(int b) {
+    return ord_to_f32((uint32_t)(b + kPfBase) << kPfBinShift);
 }
 
 __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
@@ -84,14 +96,14 @@ __device__ __forceinline__ void row_sweep(const float* sr, int cnt, F&& fn) {
     }
 }
 
-// Wave-level: the bin d of a 1024-bin histogram that holds the need-th
+// Wave-level: the bin d of a kPfBins-bin histogram that holds the need-th
 // largest element (bins scanned from the top); gt = elements above d,
 // eq = elements in d.  Wave-uniform results.
 __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int& d, int& gt, int& eq) {
     const int lane = lane_id();
     int local = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) local += (int)h[kPfBins - 1 - (lane * 16 + j)];
+    for (int j = 0; j < kPfBins / 64; ++j) local += (int)h[kPfBins - 1 - (lane * (kPfBins / 64) + j)];
     int incl = local;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -101,8 +113,8 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int&
     int cum = incl - local;
     int fd = -1, fg = 0, fe = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int bin = kPfBins - 1 - (lane * 16 + j);
+    for (int j = 0; j < kPfBins / 64; ++j) {
+        const int bin = kPfBins - 1 - (lane * (kPfBins / 64) + j);
         const int hv = (int)h[bin];
         if (cum < need && need <= cum + hv) {
             fd = bin;
@@ -125,11 +137,39 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
                                           int cnt, int need, int32_t* oidx, float* osc) {
     const int lane = lane_id();
     const unsigned long long lt = (1ull << lane) - 1ull;
+    {
+        // The sweep does not count bin 0: it holds the rest of the row.
+        int part = 0;
+        for (int x = lane; x < kPfBins; x += 64) part += x ? (int)h[x] : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+        if (lane == 0) h[0] = (uint32_t)(cnt - part);
+    }
     int d0, gt0, eq0;
     wave_threshold(h, need, d0, gt0, eq0);
+    // Bin d0 as a score interval [lo, hi).
+    const float lo = d0 == 0 ? -INFINITY : pf_edge(d0);
+    const float hi = d0 == kPfBins - 1 ? INFINITY : pf_edge(d0 + 1);
     bool take_all = gt0 + eq0 == need;
     const bool fits = !take_all && eq0 <= kPfCand;
     int out = 0, nc = 0;
+    // Level 0 emits up to k scores: they are staged as (position, score
+    // bits) pairs in the row histogram (free once d0 is known) and written
+    // out in full 64-lane stores.
+    uint2* ring = reinterpret_cast<uint2*>(h);
+    constexpr int kRing = kPfBins / 2;
+    int written = 0;
+    auto flush = [&](bool all) {
+        while (out - written >= 64 || (all && out > written)) {
+            const int j = written + lane;
+            if (j < out) {
+                const uint2 e = ring[j & (kRing - 1)];
+                oidx[j] = (int)e.x;
+                if (osc) osc[j] = __uint_as_float(e.y);
+            }
+            written += min(64, out - written);
+        }
+    };
     auto put = [&](bool emit, int s, float sc) {
         const unsigned long long me = __ballot(emit);
         if (emit) {
@@ -142,13 +182,17 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
         out += __popcll(me);
     };
     row_sweep(sr, cnt, [&](int u, float sc, bool in) {
-        const int bin = pf_bin(sc);
-        put(in && (bin > d0 || (take_all && bin == d0)), u, sc);
-        const bool app = in && fits && bin == d0;
+        const bool emit = in && (sc >= hi || (take_all && sc >= lo));
+        const unsigned long long me = __ballot(emit);
+        if (emit) ring[(out + __popcll(me & lt)) & (kRing - 1)] = make_uint2((uint32_t)u, __float_as_uint(sc));
+        out += __popcll(me);
+        flush(false);
+        const bool app = in && fits && sc >= lo && sc < hi;
         const unsigned long long ma = __ballot(app);
         if (app) cb[nc + __popcll(ma & lt)] = pf_key(sc, u);
         nc += __popcll(ma);
     });
+    flush(true);
     if (take_all) return;
 
     int need_rem = need - gt0;
@@ -161,11 +205,11 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
     bool inlds = fits;  // candidates in cb, else re-read the row
     int nsrc = fits ? nc : cnt;
     while (top > 0) {
-        const int width = top < 10 ? top : 10;
+        const int width = top < kPfDigit ? top : kPfDigit;
         const int shift = top - width;
         const unsigned long long mask = (1ull << width) - 1ull;
         auto live = [&](unsigned long long key, float sc) {
-            return pf_bin(sc) == d0 && (pshift == 64 || (key >> pshift) == pval);
+            return sc >= lo && sc < hi && (pshift == 64 || (key >> pshift) == pval);
         };
         for (int x = lane; x < kPfBins; x += 64) h[x] = 0u;
         if (inlds) {
@@ -217,10 +261,10 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
 
 template <int NHT>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
-    // Two stages as two distinct LDS objects: the compiler then tracks the
-    // direct-to-LDS loads per stage and places no wait of its own for the
-    // stage in flight before reads of the other.
-    __shared__ uint4 kt0[kPfTile * 16], kt1[kPfTile * 16];
+    // The stages are four distinct LDS objects: the compiler then tracks the
+    // direct-to-LDS loads per object and places no wait of its own for the
+    // pair in flight before reads of the other pair.
+    __shared__ uint4 kt0[kPfStage], kt1[kPfStage], kt2[kPfStage], kt3[kPfStage];
     __shared__ uint32_t hist[kPfRows][kPfBins];
 
     const int seq = blockIdx.y;
@@ -260,98 +304,108 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 
     const uint16_t* kseq = a.keys + (long long)seq * a.L * kD;
     // Stage fill: a wave's load instruction writes 1 KiB of LDS (64 lanes x
-    // 16 bytes at consecutive addresses) = 4 key rows.  Lane l lands at key
-    // 4*(4j + wave) + l/16, slot l%16 of the row, and fetches the chunk that
-    // belongs in that slot under the swizzle (slot ^ (key & 15)).  Tiles past
-    // the last are clamped re-reads, so every stage issues exactly kPfLoads
-    // loads per thread.
-    constexpr int kPfLoads = kPfTile * 16 / (64 * kPfWaves);
-    auto issue = [&](uint4* stage, int tile) {
+    // 16 bytes at consecutive addresses) = 4 key rows, block blk = 4j + wave.
+    // Lane l lands at key 4*blk + l/16, slot l%16 of the row, and fetches the
+    // chunk that belongs in that slot under the swizzle slot ^ (key/4 % 16),
+    // i.e. slot ^ blk.  Tiles past the last are clamped re-reads.
+    constexpr int kPfLoads = kPfStage / (64 * kPfWaves);
+    auto issue = [&](uint4* stage, int tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kPfLoads; ++j) {
             const int blk = kPfWaves * j + wid;
             const int key = 4 * blk + (lane >> 4);
             const int s = min(tile * kPfTile + key, tmax);
-            const int chunk = (lane & 15) ^ (key & 15);
+            const int chunk = (lane & 15) ^ blk;
             __builtin_amdgcn_global_load_lds(kseq + (long long)s * kD + chunk * 8,
                                              stage + blk * 64, 16, 0, 0);
         }
     };
 
-    // A tile's scores are stored at the top of the next tile, right after its
-    // stage wait, so the stores have a whole tile of compute to complete
-    // before the next wait (which counts them too) comes round.
-    float pend[kPfQpw];
-    int pend_base = -1;
-    auto put = [&]() {
-        if (pend_base < 0) return;
-        const int s = pend_base + lane;
+    // Scores of tile j of a pair: lane (g, c) keeps, for the row and tile of
+    // its lane group (row g & 1, tile g >> 1), the scores of keys 4c .. 4c+3
+    // (st, stored at the next pair), and adds the score of key 4c + g of each
+    // row to that row's histogram.
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+    auto tile_scores = [&](const uint4* ktile, int kbase, int j) __attribute__((always_inline)) {
+        float hv[kPfQpw];
 #pragma unroll
-        for (int qq = 0; qq < kPfQpw; ++qq)
-            if (s <= tq[qq]) srow[qq][s] = pend[qq];
+        for (int qq = 0; qq < kPfQpw; ++qq) hv[qq] = 0.f;
+#pragma unroll
+        for (int gi = 0; gi < kPfTile / 16; ++gi) {
+            uint4 kb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) kb[kk] = ktile[(4 * c + gi) * 16 + ((kk * 4 + g) ^ c)];
+#pragma unroll
+            for (int qq = 0; qq < kPfQpw; ++qq) {
+                // One row at a time keeps 16 accumulator registers live; the
+                // other wave on the SIMD fills the MFMA pipe meanwhile.
+                f32x4 acc[NHT];
+                group_dots<NHT, 4>(f[qq], kb, acc);
+                float sc = 0.f;
+#pragma unroll
+                for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sc = fmaf(f[qq].wv[ht][e], fmaxf(acc[ht][e], 0.f), sc);
+                sc = sum_lane_groups(sc);
+                hv[qq] = g == gi ? sc : hv[qq];
+                st[gi] = g == 2 * j + qq ? sc : st[gi];
+            }
+        }
+        const int s = kbase + 4 * c + g;
+#pragma unroll
+        for (int qq = 0; qq < kPfQpw; ++qq) {
+            // Positive scores only: bin = (float bits >> 20) - 760 there.
+            const int v = (int)(__float_as_uint(hv[qq]) >> kPfBinShift) - (kPfBase - 2048);
+            if (s <= tq[qq] && hv[qq] > 0.f && v > 0) lds_add_u32(&h[qq][min(v, kPfBins - 1)], 1u);
+        }
+    };
+
+    // A pair's scores are stored at the top of the next pair, right after its
+    // stage wait, so the stores have two tiles of compute to complete before
+    // the next wait (which counts them too) comes round.  Keys past the row's
+    // last legal one inside its last tile are stored too (the line has room
+    // up to the next multiple of 64) and never read.
+    int pend_base = -1;
+    auto put = [&]() __attribute__((always_inline)) {
+        if (pend_base < 0) return;
+        const int qs = g & 1;
+        const int kb0 = pend_base + (g >> 1) * kPfTile;
+        if (kb0 <= (qs ? tq[1] : tq[0]))
+            __builtin_nontemporal_store(st, reinterpret_cast<f32x4*>((qs ? srow[1] : srow[0]) + kb0 + 4 * c));
         pend_base = -1;
     };
 
-    // One barrier per tile: after it, this tile's data is visible to all and
-    // every wave is done with the other stage, which is refilled right away
-    // (its next tile then has this tile's compute time to arrive).
-    auto consume = [&](const uint4* ktile, uint4* other, int tile) {
+    // One barrier per pair: after it, the pair's data is visible to all and
+    // every wave is done with the other pair's stages, which are refilled
+    // right away.
+    auto pair = [&](const uint4* ka, const uint4* kb, uint4* na, uint4* nb, int tile)
+                    __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
-        issue(other, tile + 1);
+        issue(na, tile + 2);
+        issue(nb, tile + 3);
         put();
         const int kbase = tile * kPfTile;
         if (kbase <= tw) {
-            // Scores of the tile, parked so that lane l holds key kbase + l of
-            // each row: the 4 MFMA groups run branch-free.
-            float mine[kPfQpw];
-#pragma unroll
-            for (int qq = 0; qq < kPfQpw; ++qq) mine[qq] = 0.f;
-#pragma unroll
-            for (int gi = 0; gi < kPfTile / 16; ++gi) {
-                const int kl = gi * 16 + c;
-                uint4 kb[4];
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    kb[kk] = ktile[kl * 16 + ((kk * 4 + g) ^ (kl & 15))];
-#pragma unroll
-                for (int qq = 0; qq < kPfQpw; ++qq) {
-                    // One row at a time keeps 16 accumulator registers live; the
-                    // other wave on the SIMD fills the MFMA pipe meanwhile.
-                    f32x4 acc[NHT];
-                    group_dots<NHT, 4>(f[qq], kb, acc);
-                    float sc = 0.f;
-#pragma unroll
-                    for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sc = fmaf(f[qq].wv[ht][e], fmaxf(acc[ht][e], 0.f), sc);
-                    sc = sum_lane_groups(sc);
-                    mine[qq] = g == gi ? sc : mine[qq];
-                }
-            }
-            const int s = kbase + lane;
-#pragma unroll
-            for (int qq = 0; qq < kPfQpw; ++qq) {
-                if (s <= tq[qq]) lds_add_u32(&h[qq][pf_bin(mine[qq])], 1u);
-                pend[qq] = mine[qq];
-            }
-            pend_base = kbase;
+            tile_scores(ka, kbase, 0);
+            if (kbase + kPfTile <= tw) tile_scores(kb, kbase + kPfTile, 1);
+            pend_base = kbase;  // keys past tw are never stored
         }
     };
 
     issue(kt0, 0);
-    for (int tile = 0; tile < ntiles; tile += 2) {
-        consume(kt0, kt1, tile);
-        if (tile + 1 >= ntiles) break;
-        consume(kt1, kt0, tile + 1);
+    issue(kt1, 1);
+    for (int tile = 0; tile < ntiles; tile += 4) {
+        pair(kt0, kt1, kt2, kt3, tile);
+        if (tile + 2 >= ntiles) break;
+        pair(kt2, kt3, kt0, kt1, tile + 2);
     }
     put();
 
-    // The key tiles are free once every wave is past its last tile and the
-    // last (clamped) stage fill has landed: they hold the candidate buffers,
-    // rows 0-3 in kt0 and rows 4-7 in kt1.  Each wave finishes its own rows
-    // from the score lines it wrote.
+    // The key stages are free once every wave is past its last tile and the
+    // last (clamped) fills have landed: they hold the candidate buffers, two
+    // rows per stage.  Each wave finishes its own rows from the score lines
+    // it wrote.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -364,9 +418,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
-        const int r = wid * kPfQpw + qq;
-        unsigned long long* cb = reinterpret_cast<unsigned long long*>(r < kPfRows / 2 ? kt0 : kt1) +
-                                 (r % (kPfRows / 2)) * kPfCand;
+        uint4* stage = wid == 0 ? kt0 : (wid == 1 ? kt1 : (wid == 2 ? kt2 : kt3));
+        unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + qq * kPfCand;
         pf_finish(h[qq], cb, srow[qq], tq[qq] + 1, need, oidx, osc);
     }
 }
