@@ -27,6 +27,8 @@
 // position), into LDS; a radix select on those keys (9-bit digits) settles
 // the rest.  Only when the bin holds more keys than the LDS buffer does a
 // digit level re-read the row.
+#include <type_traits>
+
 #include "sa_frag.h"
 
 namespace sa {
@@ -45,7 +47,7 @@ constexpr int kPfBase = (int)((0x80000000u | (95u << 23)) >> kPfBinShift);
 // Key bits fixed by an inner bin: 63 .. 32 + kPfBinShift.
 constexpr int kPfKeyTop = 32 + kPfBinShift;
 constexpr int kPfCand = 1024;  // LDS candidate keys per row: two rows per stage
-constexpr int kPfSweep = 8;    // float4 loads in flight per lane in a row pass
+constexpr int kPfSweep = 4;    // float4 per lane per block of the level-0 pass (double-buffered)
 static_assert(2 * kPfCand * 8 == kPfStage * 16, "two rows' candidate buffers fill one stage");
 static_assert((1 << kPfDigit) == kPfBins, "digit histograms reuse the row histogram");
 static_assert(kPfQpw == 2 && kPfTile == 64, "the 4 lane groups store 2 rows x 2 tiles of a pair");
@@ -73,20 +75,21 @@ __device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
 }
 
 // One pass of a wave over a row's cnt scores: fn(position, score, valid) for
-// every lane and element, 4 consecutive scores per lane and kPfSweep loads in
-// flight.  Rows are padded to a multiple of 4 floats, so the clamped float4
-// reads stay inside the row.
+// every lane and element, 4 consecutive scores per lane, 4 loads in flight.
+// Rows are padded to a multiple of 4 floats, so the clamped float4 reads stay
+// inside the row.  Only rows whose threshold bin is crowded re-read the row.
 template <class F>
 __device__ __forceinline__ void row_sweep(const float* sr, int cnt, F&& fn) {
     const int lane = lane_id();
     const float4* sr4 = reinterpret_cast<const float4*>(sr);
     const int last4 = (cnt - 1) >> 2;
-    for (int ub = 0; ub < cnt; ub += 256 * kPfSweep) {
-        float4 v[kPfSweep];
+#pragma unroll 1
+    for (int ub = 0; ub < cnt; ub += 1024) {
+        float4 v[4];
 #pragma unroll
-        for (int j = 0; j < kPfSweep; ++j) v[j] = sr4[min((ub >> 2) + j * 64 + lane, last4)];
+        for (int j = 0; j < 4; ++j) v[j] = sr4[min((ub >> 2) + j * 64 + lane, last4)];
 #pragma unroll
-        for (int j = 0; j < kPfSweep; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const int u = ub + 4 * (j * 64 + lane);
             fn(u, v[j].x, u < cnt);
             fn(u + 1, v[j].y, u + 1 < cnt);
@@ -96,14 +99,16 @@ __device__ __forceinline__ void row_sweep(const float* sr, int cnt, F&& fn) {
     }
 }
 
-// Wave-level: the bin d of a kPfBins-bin histogram that holds the need-th
+// Wave-level: the bin d of an NB-bin histogram that holds the need-th
 // largest element (bins scanned from the top); gt = elements above d,
 // eq = elements in d.  Wave-uniform results.
+template <int NB>
 __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int& d, int& gt, int& eq) {
+    constexpr int kPer = NB / 64;
     const int lane = lane_id();
     int local = 0;
 #pragma unroll
-    for (int j = 0; j < kPfBins / 64; ++j) local += (int)h[kPfBins - 1 - (lane * (kPfBins / 64) + j)];
+    for (int j = 0; j < kPer; ++j) local += (int)h[NB - 1 - (lane * kPer + j)];
     int incl = local;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -113,8 +118,8 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int&
     int cum = incl - local;
     int fd = -1, fg = 0, fe = 0;
 #pragma unroll
-    for (int j = 0; j < kPfBins / 64; ++j) {
-        const int bin = kPfBins - 1 - (lane * (kPfBins / 64) + j);
+    for (int j = 0; j < kPer; ++j) {
+        const int bin = NB - 1 - (lane * kPer + j);
         const int hv = (int)h[bin];
         if (cum < need && need <= cum + hv) {
             fd = bin;
@@ -131,8 +136,17 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int&
 }
 
 // Exact top-`need` of one row by one wave (see the file header): h holds the
-// histogram of the row's cnt legal scores sr[0, cnt); cb is kPfCand keys of
-// LDS.  Output order is unspecified.
+// histogram of the row's cnt legal scores sr[0, cnt) (bin 0 not counted); cb
+// is kPfCand keys of LDS.  Output order is unspecified.
+//
+// Digit levels narrow the threshold bin down on the key ord(score) << 32 |
+// ~position: the keys still in play are those in [lo, hi) whose bits above
+// pshift equal pval.  When the bin holds more keys than cb, the level-0 pass
+// also counts their next kPfWide-bit digit, in cb used as a histogram, so
+// that one more pass settles the bin or shrinks it to LDS size.
+constexpr int kPfWide = 11;
+static_assert((1 << kPfWide) * 4 == kPfCand * 8, "the wide digit histogram fills cb");
+
 __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, const float* sr,
                                           int cnt, int need, int32_t* oidx, float* osc) {
     const int lane = lane_id();
@@ -146,30 +160,22 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
         if (lane == 0) h[0] = (uint32_t)(cnt - part);
     }
     int d0, gt0, eq0;
-    wave_threshold(h, need, d0, gt0, eq0);
+    wave_threshold<kPfBins>(h, need, d0, gt0, eq0);
     // Bin d0 as a score interval [lo, hi).
     const float lo = d0 == 0 ? -INFINITY : pf_edge(d0);
     const float hi = d0 == kPfBins - 1 ? INFINITY : pf_edge(d0 + 1);
     bool take_all = gt0 + eq0 == need;
     const bool fits = !take_all && eq0 <= kPfCand;
+    const bool wide = !take_all && !fits;
+    // An inner bin fixes the key bits above kPfKeyTop; the clamped end bins
+    // fix nothing.
+    const bool clamped = d0 == 0 || d0 == kPfBins - 1;
+    int top = clamped ? 64 : kPfKeyTop;
+    uint32_t* hw = reinterpret_cast<uint32_t*>(cb);
+    if (wide)
+        for (int x = lane; x < (1 << kPfWide); x += 64) hw[x] = 0u;
+
     int out = 0, nc = 0;
-    // Level 0 emits up to k scores: they are staged as (position, score
-    // bits) pairs in the row histogram (free once d0 is known) and written
-    // out in full 64-lane stores.
-    uint2* ring = reinterpret_cast<uint2*>(h);
-    constexpr int kRing = kPfBins / 2;
-    int written = 0;
-    auto flush = [&](bool all) {
-        while (out - written >= 64 || (all && out > written)) {
-            const int j = written + lane;
-            if (j < out) {
-                const uint2 e = ring[j & (kRing - 1)];
-                oidx[j] = (int)e.x;
-                if (osc) osc[j] = __uint_as_float(e.y);
-            }
-            written += min(64, out - written);
-        }
-    };
     auto put = [&](bool emit, int s, float sc) {
         const unsigned long long me = __ballot(emit);
         if (emit) {
@@ -181,48 +187,108 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
         }
         out += __popcll(me);
     };
-    row_sweep(sr, cnt, [&](int u, float sc, bool in) {
-        const bool emit = in && (sc >= hi || (take_all && sc >= lo));
-        const unsigned long long me = __ballot(emit);
-        if (emit) ring[(out + __popcll(me & lt)) & (kRing - 1)] = make_uint2((uint32_t)u, __float_as_uint(sc));
-        out += __popcll(me);
-        flush(false);
-        const bool app = in && fits && sc >= lo && sc < hi;
-        const unsigned long long ma = __ballot(app);
-        if (app) cb[nc + __popcll(ma & lt)] = pf_key(sc, u);
-        nc += __popcll(ma);
-    });
-    flush(true);
+    // Level 0, one pass over the row.  The scores to emit or to collect
+    // (at or above lo: bin d0 and above, about k + eq0 of them; above hi
+    // only when bin d0 is too crowded for cb) are staged as (position, score
+    // bits) pairs in a ring in the row histogram (free once d0 is known);
+    // whole 64-entry blocks of it are then sent, all lanes busy, to the
+    // output (above hi, or all when taking all) or to cb.  A crowded bin's
+    // keys are counted into the wide digit histogram where they are met.
+    const int wshift = top - kPfWide;
+    uint2* ring = reinterpret_cast<uint2*>(h);
+    constexpr int kRing = kPfBins / 2;
+    int staged = 0, done = 0;
+    auto drain = [&](bool all) {
+        while (staged - done >= 64 || (all && staged > done)) {
+            const int j = done + lane;
+            const bool ok = j < staged;
+            const uint2 e = ring[j & (kRing - 1)];
+            const float sc = __uint_as_float(e.y);
+            const bool up = ok && (take_all || sc >= hi);
+            put(up, (int)e.x, sc);
+            const bool app = ok && fits && !up;
+            const unsigned long long ma = __ballot(app);
+            if (app) cb[nc + __popcll(ma & lt)] = pf_key(sc, (int)e.x);
+            nc += __popcll(ma);
+            done += min(64, staged - done);
+        }
+    };
+    // The pass, instantiated for a crowded bin d0 (WIDE) and for the rest.
+    auto level0 = [&](auto wide_tag) __attribute__((always_inline)) {
+        constexpr bool WIDE = decltype(wide_tag)::value;
+        const float4* sr4 = reinterpret_cast<const float4*>(sr);
+        const int last4 = (cnt - 1) >> 2;
+        constexpr int kStep = 256 * kPfSweep;
+        float4 cur[kPfSweep], nxt[kPfSweep];
+#pragma unroll
+        for (int j = 0; j < kPfSweep; ++j) cur[j] = sr4[min(j * 64 + lane, last4)];
+        for (int ub = 0; ub < cnt; ub += kStep) {
+            // The next block is in flight while this one is sorted out
+            // (clamped: past the end it re-reads the last float4).
+#pragma unroll
+            for (int j = 0; j < kPfSweep; ++j)
+                nxt[j] = sr4[min(((ub + kStep) >> 2) + j * 64 + lane, last4)];
+#pragma unroll
+            for (int j = 0; j < kPfSweep; ++j) {
+                const int u = ub + 4 * (j * 64 + lane);
+                const float e4[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool in = u + i < cnt;
+                    if (WIDE && in && e4[i] >= lo && e4[i] < hi)
+                        lds_add_u32(&hw[(uint32_t)(pf_key(e4[i], u + i) >> wshift) & ((1u << kPfWide) - 1)], 1u);
+                    const bool keep = in & (e4[i] >= (WIDE ? hi : lo));
+                    const unsigned long long m = __ballot(keep);
+                    if (keep)
+                        ring[(staged + __popcll(m & lt)) & (kRing - 1)] =
+                            make_uint2((uint32_t)(u + i), __float_as_uint(e4[i]));
+                    staged += __popcll(m);
+                    // At most 63 + 2 x 64 entries pending: the ring holds 256.
+                    if (i & 1) drain(false);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kPfSweep; ++j) cur[j] = nxt[j];
+        }
+    };
+    if (wide)
+        level0(std::true_type{});
+    else
+        level0(std::false_type{});
+    {
+        drain(true);
+    }
     if (take_all) return;
 
     int need_rem = need - gt0;
-    // An inner bin fixes the key bits above kPfKeyTop; the clamped end bins
-    // fix nothing.
-    const bool clamped = d0 == 0 || d0 == kPfBins - 1;
-    int top = clamped ? 64 : kPfKeyTop;
     unsigned long long pval = clamped ? 0ull : (unsigned long long)(d0 + kPfBase);
     int pshift = top;
     bool inlds = fits;  // candidates in cb, else re-read the row
     int nsrc = fits ? nc : cnt;
+    bool first = wide;  // the wide digit's histogram is already in cb
     while (top > 0) {
-        const int width = top < kPfDigit ? top : kPfDigit;
+        const int width = first ? kPfWide : (top < kPfDigit ? top : kPfDigit);
         const int shift = top - width;
         const unsigned long long mask = (1ull << width) - 1ull;
         auto live = [&](unsigned long long key, float sc) {
             return sc >= lo && sc < hi && (pshift == 64 || (key >> pshift) == pval);
         };
-        for (int x = lane; x < kPfBins; x += 64) h[x] = 0u;
-        if (inlds) {
-            for (int u = lane; u < nsrc; u += 64)
-                lds_add_u32(&h[(uint32_t)((cb[u] >> shift) & mask)], 1u);
-        } else {
-            row_sweep(sr, cnt, [&](int u, float sc, bool in) {
-                const unsigned long long key = pf_key(sc, u);
-                if (in && live(key, sc)) lds_add_u32(&h[(uint32_t)((key >> shift) & mask)], 1u);
-            });
-        }
         int d, gt, eq;
-        wave_threshold(h, need_rem, d, gt, eq);
+        if (first) {
+            wave_threshold<(1 << kPfWide)>(hw, need_rem, d, gt, eq);
+        } else {
+            for (int x = lane; x < kPfBins; x += 64) h[x] = 0u;
+            if (inlds) {
+                for (int u = lane; u < nsrc; u += 64)
+                    lds_add_u32(&h[(uint32_t)((cb[u] >> shift) & mask)], 1u);
+            } else {
+                row_sweep(sr, cnt, [&](int u, float sc, bool in) {
+                    const unsigned long long key = pf_key(sc, u);
+                    if (in && live(key, sc)) lds_add_u32(&h[(uint32_t)((key >> shift) & mask)], 1u);
+                });
+            }
+            wave_threshold<kPfBins>(h, need_rem, d, gt, eq);
+        }
         take_all = gt + eq == need_rem;
         const bool fits_next = !take_all && eq <= kPfCand;
         int nn = 0;
@@ -256,6 +322,7 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
         top = shift;
         inlds = fits_next;
         nsrc = fits_next ? nn : cnt;
+        first = false;
     }
 }
 
@@ -408,19 +475,24 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     // it wrote.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
+#pragma unroll 1
     for (int qq = 0; qq < kPfQpw; ++qq) {
-        if (!act[qq]) continue;
-        const int need = min(a.k, tq[qq] + 1);
-        int32_t* oidx = a.out_idx + rowq[qq] * a.out_stride;
-        float* osc = a.out_score ? a.out_score + rowq[qq] * a.out_stride : nullptr;
+        // One copy of the finish for both rows (selects, not array indexing,
+        // keep the per-row values in registers).
+        const bool aq = qq ? act[1] : act[0];
+        if (!aq) continue;
+        const int tqq = qq ? tq[1] : tq[0];
+        const long long rq = qq ? rowq[1] : rowq[0];
+        const int need = min(a.k, tqq + 1);
+        int32_t* oidx = a.out_idx + rq * a.out_stride;
+        float* osc = a.out_score ? a.out_score + rq * a.out_stride : nullptr;
         for (int u = need + lane; u < a.k; u += 64) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
         uint4* stage = wid == 0 ? kt0 : (wid == 1 ? kt1 : (wid == 2 ? kt2 : kt3));
         unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + qq * kPfCand;
-        pf_finish(h[qq], cb, srow[qq], tq[qq] + 1, need, oidx, osc);
+        pf_finish(qq ? h[1] : h[0], cb, qq ? srow[1] : srow[0], tqq + 1, need, oidx, osc);
     }
 }
 
