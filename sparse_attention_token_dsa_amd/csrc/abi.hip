@@ -124,7 +124,7 @@ struct DsaPlan {
     float* scores;
     uint32_t* state;
     unsigned long long* cand;
-    float* pscores;
+    uint2* surv;
     size_t bytes;
 };
 
@@ -135,7 +135,7 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
     const long long maxn = (long long)s->causal_offset + s->T;
     p.prefill = s->T >= kPrefillMinT;
     if (p.prefill) {
-        p.pscores = cv.take<float>(rows * score_stride((int)maxn));
+        p.surv = cv.take<uint2>(rows * score_stride((int)maxn));
     } else {
         p.scores = cv.take<float>(rows * score_stride(s->L));
         p.state = cv.take<uint32_t>(rows * sa::kRowState);
@@ -392,8 +392,8 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
         a.L = s->L;
         a.offset = s->causal_offset;
         a.k = s->topk;
-        a.scores = p.pscores;
-        a.stride = score_stride(s->causal_offset + s->T);
+        a.surv = p.surv;
+        a.cap = score_stride(s->causal_offset + s->T);
         a.out_idx = out_idx;
         a.out_score = out_score;
         a.out_stride = s->topk;

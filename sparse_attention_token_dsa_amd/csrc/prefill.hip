@@ -1,7 +1,8 @@
 // Fused causal-prefill indexer: q . K contraction on bf16 MFMA, ReLU, the
-// w-weighted head sum and the causal mask in the epilogue, and the row's exact
-// top-k, in one kernel (PaperTrace, "2.2.2 MISA, LISA and ResMiSA", section
-// 2.2: score, causal mask and top-k fused into one pass).
+// w-weighted head sum and the causal mask in the epilogue, a streaming per-row
+// threshold and the row's exact top-k, in one kernel (PaperTrace, "2.2.2
+// MISA, LISA and ResMiSA", section 2.2: score, causal mask and top-k fused
+// into one pass, no n^2 score matrix written back).
 //
 // Layout: a workgroup of 4 waves owns 8 consecutive query rows of one
 // sequence (two rows per wave, their heads held as MFMA A fragments in
@@ -10,23 +11,28 @@
 // is staged once in LDS for all 8 rows by direct global-to-LDS loads, with a
 // 16-byte XOR swizzle so the B-fragment reads are free of bank conflicts.
 // Column c of MFMA group gi is key 4c + gi, so that after the head sum every
-// lane holds the scores of 4 consecutive keys.  Four stages are used in pairs: one wait and one barrier per two tiles, and
-// the next pair's loads have two tiles of compute to arrive.
+// lane holds the scores of 4 consecutive keys.  Four stages are used in
+// pairs: one wait and one barrier per two tiles, and the next pair's loads
+// have two tiles of compute to arrive.
 //
-// Per tile and row the sweep does no selection work: each legal score is
-// added to the row's LDS histogram (bins of 1/8 octave over [2^-32, 2^32);
-// zero, negative and smaller scores share bin 0, which is not counted but
-// derived at the end, larger ones the last bin) and stored to the row's
-// score line in the workspace (4 bytes per legal key, written once and read
-// once; one 16-byte non-temporal store per lane per pair of tiles).
+// Streaming threshold: each row keeps an LDS histogram of the scores it has
+// kept, over the bins below (monotone in the score).  tau is the highest bin
+// such that at least k kept scores lie in bins >= tau; a new score below bin
+// tau has k larger ones ahead of it and can never enter the row's top-k, so
+// it is dropped with one compare.  The rest (about k (1 + ln(n / k)) per row
+// for n keys in random order) are appended as (position, score) pairs to the
+// row's survivor list in the workspace; the scores themselves never leave the
+// chip.  The count of bin tau is mirrored in a register, so tau is re-derived
+// from the histogram only when it can move.
 //
-// Finish: after the sweep each wave selects its rows' exact top-k: the
-// histogram gives the bin holding the k-th score; one pass over the row emits
-// the scores above it (staged in LDS, written out 64 at a time) and collects
-// the ones in it, as 64-bit keys ord(score) << 32 | ~position (ties -> lower
-// position), into LDS; a radix select on those keys (9-bit digits) settles
-// the rest.  Only when the bin holds more keys than the LDS buffer does a
-// digit level re-read the row.
+// Finish: after the sweep each wave selects its rows' exact top-k from their
+// survivors: the histogram gives the bin holding the k-th score; one pass over
+// the list emits the scores above it (staged in LDS, written out 64 at a time)
+// and collects the ones in it, as 64-bit keys ord(score) << 32 | ~position
+// (ties -> lower position), into LDS; a radix select on those keys settles the
+// rest.  A bin too crowded for the LDS buffer has its next 11-bit digit counted
+// in the same pass, so one more pass over the list settles it or shrinks it to
+// LDS size.
 #include <type_traits>
 
 #include "sa_frag.h"
@@ -38,28 +44,52 @@ constexpr int kPfQpw = 2;  // query rows per wave
 constexpr int kPfRows = kPfWaves * kPfQpw;
 constexpr int kPfTile = 64;
 constexpr int kPfStage = kPfTile * 16;  // uint4 per stage (16 KiB)
-constexpr int kPfBins = 512;
-constexpr int kPfDigit = 9;  // radix digit of the finish: 2^9 = kPfBins
-// A bin is ord(score) >> 20: sign, exponent and 3 mantissa bits.
-constexpr int kPfBinShift = 20;
-// ord(2^-32) >> 20: prefix of the first inner bin.
-constexpr int kPfBase = (int)((0x80000000u | (95u << 23)) >> kPfBinShift);
-// Key bits fixed by an inner bin: 63 .. 32 + kPfBinShift.
-constexpr int kPfKeyTop = 32 + kPfBinShift;
-constexpr int kPfCand = 1024;  // LDS candidate keys per row: two rows per stage
-constexpr int kPfSweep = 4;    // float4 per lane per block of the level-0 pass (double-buffered)
+constexpr int kPfBins = 512;            // histogram size (bins 507 .. 511 stay empty)
+constexpr int kPfDigit = 9;             // radix digit of the finish over LDS candidates
+constexpr int kPfWide = 11;             // digit counted in the level-0 pass for crowded bins
+constexpr int kPfCand = 1024;           // LDS candidate keys per row: two rows per stage
+constexpr int kPfSweep = 4;             // uint4 per lane per block of the level-0 pass
 static_assert(2 * kPfCand * 8 == kPfStage * 16, "two rows' candidate buffers fill one stage");
 static_assert((1 << kPfDigit) == kPfBins, "digit histograms reuse the row histogram");
-static_assert(kPfQpw == 2 && kPfTile == 64, "the 4 lane groups store 2 rows x 2 tiles of a pair");
+static_assert((1 << kPfWide) * 4 == kPfCand * 8, "the wide digit histogram fills cb");
+static_assert(kPfQpw == 2 && kPfTile == 64, "the 4 lane groups hold 2 rows x 2 tiles of a pair");
 
-__device__ __forceinline__ int pf_bin(float sc) {
-    const int v = (int)(ord_key(sc) >> kPfBinShift) - kPfBase;
-    return v < 0 ? 0 : (v > kPfBins - 1 ? kPfBins - 1 : v);
+// Score bins, monotone in the score:
+//   0           x <= -2^32
+//   1 .. 64     negative x, one octave each: |x| in [2^(32-b), 2^(33-b))
+//   65          -2^-32 < x < 2^-23 (zero and the smallest magnitudes)
+//   66 .. 505   positive x in [2^-23, 2^32), 1/8 octave each
+//   506         x >= 2^32
+constexpr int kPfNegOct = 64;
+constexpr int kPfMid = 65;
+constexpr int kPfPos0 = 66;
+constexpr int kPfTop = 506;
+constexpr int kPfPosE = 104;  // biased exponent of 2^-23
+constexpr int kPfNegE = 95;   // biased exponent of 2^-32
+
+__device__ __forceinline__ int pf_bin(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const int e = (int)((u >> 23) & 255u);
+    const int pos = min(kPfPos0 + (int)(u >> 20) - (kPfPosE << 3), kPfTop);
+    const int neg = max(kPfNegOct - (e - kPfNegE), 0);
+    return (u >> 31) ? (e >= kPfNegE ? neg : kPfMid) : (e >= kPfPosE ? pos : kPfMid);
 }
 
-// Smallest score in bin b, 1 <= b < kPfBins.
-__device__ __forceinline__ float pf_edge(int b) {
-    return ord_to_f32((uint32_t)(b + kPfBase) << kPfBinShift);
+// Smallest order key ord(x) of bin b, 1 <= b <= kPfTop.
+__device__ __forceinline__ uint32_t pf_lo_ord(int b) {
+    return b <= kPfMid ? 0x80000000u - ((uint32_t)(kPfNegE + 1 + kPfNegOct - b) << 23)
+                       : 0x80000000u | ((uint32_t)(b - kPfPos0 + (kPfPosE << 3)) << 20);
+}
+
+// Bin b as the score interval [lo, hi).
+__device__ __forceinline__ float pf_lo(int b) { return b <= 0 ? -INFINITY : ord_to_f32(pf_lo_ord(b)); }
+__device__ __forceinline__ float pf_hi(int b) {
+    return b >= kPfTop ? INFINITY : ord_to_f32(pf_lo_ord(b + 1));
+}
+
+// Key bits a bin fixes: 63 .. top (top = 64: none).
+__device__ __forceinline__ int pf_top(int b) {
+    return (b >= kPfPos0 && b < kPfTop) ? 52 : ((b >= 1 && b <= kPfNegOct) ? 55 : 64);
 }
 
 __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
@@ -74,27 +104,26 @@ __device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
     asm volatile("ds_add_u32 %0, %1" : : "v"((uint32_t)(uintptr_t)p), "v"(v) : "memory");
 }
 
-// One pass of a wave over a row's cnt scores: fn(position, score, valid) for
-// every lane and element, 4 consecutive scores per lane, 4 loads in flight.
-// Rows are padded to a multiple of 4 floats, so the clamped float4 reads stay
-// inside the row.  Only rows whose threshold bin is crowded re-read the row.
+// One pass of a wave over a survivor list sl[0, cnt) of (position, score
+// bits) pairs: fn(position, score, valid) for every lane and element, 2
+// elements per 16-byte load, 4 loads in flight.  Lists have room for an even
+// number of entries, so the clamped 16-byte reads stay inside.  Only crowded
+// threshold bins re-read the list.
 template <class F>
-__device__ __forceinline__ void row_sweep(const float* sr, int cnt, F&& fn) {
+__device__ __forceinline__ void list_sweep(const uint2* sl, int cnt, F&& fn) {
     const int lane = lane_id();
-    const float4* sr4 = reinterpret_cast<const float4*>(sr);
-    const int last4 = (cnt - 1) >> 2;
+    const uint4* s4 = reinterpret_cast<const uint4*>(sl);
+    const int last = (cnt - 1) >> 1;
 #pragma unroll 1
-    for (int ub = 0; ub < cnt; ub += 1024) {
-        float4 v[4];
+    for (int ub = 0; ub < cnt; ub += 512) {
+        uint4 v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = sr4[min((ub >> 2) + j * 64 + lane, last4)];
+        for (int j = 0; j < 4; ++j) v[j] = s4[min((ub >> 1) + j * 64 + lane, last)];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int u = ub + 4 * (j * 64 + lane);
-            fn(u, v[j].x, u < cnt);
-            fn(u + 1, v[j].y, u + 1 < cnt);
-            fn(u + 2, v[j].z, u + 2 < cnt);
-            fn(u + 3, v[j].w, u + 3 < cnt);
+            const int u = ub + 2 * (j * 64 + lane);
+            fn((int)v[j].x, __uint_as_float(v[j].y), u < cnt);
+            fn((int)v[j].z, __uint_as_float(v[j].w), u + 1 < cnt);
         }
     }
 }
@@ -136,44 +165,28 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int&
 }
 
 // Exact top-`need` of one row by one wave (see the file header): h holds the
-// histogram of the row's cnt legal scores sr[0, cnt) (bin 0 not counted); cb
-// is kPfCand keys of LDS.  Output order is unspecified.
+// histogram of the row's cnt survivors sl[0, cnt), which include every legal
+// score at or above the final threshold; cb is kPfCand keys of LDS.  Output
+// order is unspecified.
 //
 // Digit levels narrow the threshold bin down on the key ord(score) << 32 |
 // ~position: the keys still in play are those in [lo, hi) whose bits above
-// pshift equal pval.  When the bin holds more keys than cb, the level-0 pass
-// also counts their next kPfWide-bit digit, in cb used as a histogram, so
-// that one more pass settles the bin or shrinks it to LDS size.
-constexpr int kPfWide = 11;
-static_assert((1 << kPfWide) * 4 == kPfCand * 8, "the wide digit histogram fills cb");
-
-__device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, const float* sr,
+// pshift equal pval.
+__device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, const uint2* sl,
                                           int cnt, int need, int32_t* oidx, float* osc) {
     const int lane = lane_id();
     const unsigned long long lt = (1ull << lane) - 1ull;
-    {
-        // The sweep does not count bin 0: it holds the rest of the row.
-        int part = 0;
-        for (int x = lane; x < kPfBins; x += 64) part += x ? (int)h[x] : 0;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        if (lane == 0) h[0] = (uint32_t)(cnt - part);
-    }
     int d0, gt0, eq0;
     wave_threshold<kPfBins>(h, need, d0, gt0, eq0);
-    // Bin d0 as a score interval [lo, hi).
-    const float lo = d0 == 0 ? -INFINITY : pf_edge(d0);
-    const float hi = d0 == kPfBins - 1 ? INFINITY : pf_edge(d0 + 1);
+    const float lo = pf_lo(d0), hi = pf_hi(d0);
     bool take_all = gt0 + eq0 == need;
     const bool fits = !take_all && eq0 <= kPfCand;
     const bool wide = !take_all && !fits;
-    // An inner bin fixes the key bits above kPfKeyTop; the clamped end bins
-    // fix nothing.
-    const bool clamped = d0 == 0 || d0 == kPfBins - 1;
-    int top = clamped ? 64 : kPfKeyTop;
+    int top = pf_top(d0);
     uint32_t* hw = reinterpret_cast<uint32_t*>(cb);
     if (wide)
         for (int x = lane; x < (1 << kPfWide); x += 64) hw[x] = 0u;
+    const int wshift = top - kPfWide;
 
     int out = 0, nc = 0;
     auto put = [&](bool emit, int s, float sc) {
@@ -187,14 +200,12 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
         }
         out += __popcll(me);
     };
-    // Level 0, one pass over the row.  The scores to emit or to collect
-    // (at or above lo: bin d0 and above, about k + eq0 of them; above hi
-    // only when bin d0 is too crowded for cb) are staged as (position, score
-    // bits) pairs in a ring in the row histogram (free once d0 is known);
-    // whole 64-entry blocks of it are then sent, all lanes busy, to the
-    // output (above hi, or all when taking all) or to cb.  A crowded bin's
-    // keys are counted into the wide digit histogram where they are met.
-    const int wshift = top - kPfWide;
+    // Level 0, one pass over the list.  The survivors to emit or to collect
+    // (at or above lo; above hi only when bin d0 is crowded) are staged as
+    // (position, score bits) pairs in a ring in the row histogram (free once
+    // d0 is known); whole 64-entry blocks of it are then sent, all lanes busy,
+    // to the output (above hi, or all when taking all) or to cb.  A crowded
+    // bin's keys are counted into the wide digit histogram where they are met.
     uint2* ring = reinterpret_cast<uint2*>(h);
     constexpr int kRing = kPfBins / 2;
     int staged = 0, done = 0;
@@ -216,35 +227,36 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
     // The pass, instantiated for a crowded bin d0 (WIDE) and for the rest.
     auto level0 = [&](auto wide_tag) __attribute__((always_inline)) {
         constexpr bool WIDE = decltype(wide_tag)::value;
-        const float4* sr4 = reinterpret_cast<const float4*>(sr);
-        const int last4 = (cnt - 1) >> 2;
-        constexpr int kStep = 256 * kPfSweep;
-        float4 cur[kPfSweep], nxt[kPfSweep];
+        const uint4* s4 = reinterpret_cast<const uint4*>(sl);
+        const int last = (cnt - 1) >> 1;
+        constexpr int kStep = 128 * kPfSweep;
+        uint4 cur[kPfSweep], nxt[kPfSweep];
 #pragma unroll
-        for (int j = 0; j < kPfSweep; ++j) cur[j] = sr4[min(j * 64 + lane, last4)];
+        for (int j = 0; j < kPfSweep; ++j) cur[j] = s4[min(j * 64 + lane, last)];
         for (int ub = 0; ub < cnt; ub += kStep) {
             // The next block is in flight while this one is sorted out
-            // (clamped: past the end it re-reads the last float4).
+            // (clamped: past the end it re-reads the last entries).
 #pragma unroll
             for (int j = 0; j < kPfSweep; ++j)
-                nxt[j] = sr4[min(((ub + kStep) >> 2) + j * 64 + lane, last4)];
+                nxt[j] = s4[min(((ub + kStep) >> 1) + j * 64 + lane, last)];
 #pragma unroll
             for (int j = 0; j < kPfSweep; ++j) {
-                const int u = ub + 4 * (j * 64 + lane);
-                const float e4[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+                const int u = ub + 2 * (j * 64 + lane);
+                const uint2 e2[2] = {make_uint2(cur[j].x, cur[j].y), make_uint2(cur[j].z, cur[j].w)};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < 2; ++i) {
                     const bool in = u + i < cnt;
-                    if (WIDE && in && e4[i] >= lo && e4[i] < hi)
-                        lds_add_u32(&hw[(uint32_t)(pf_key(e4[i], u + i) >> wshift) & ((1u << kPfWide) - 1)], 1u);
-                    const bool keep = in & (e4[i] >= (WIDE ? hi : lo));
+                    const float sc = __uint_as_float(e2[i].y);
+                    if (WIDE && in && sc >= lo && sc < hi)
+                        lds_add_u32(&hw[(uint32_t)(pf_key(sc, (int)e2[i].x) >> wshift) &
+                                        ((1u << kPfWide) - 1)],
+                                    1u);
+                    const bool keep = in & (sc >= (WIDE ? hi : lo));
                     const unsigned long long m = __ballot(keep);
-                    if (keep)
-                        ring[(staged + __popcll(m & lt)) & (kRing - 1)] =
-                            make_uint2((uint32_t)(u + i), __float_as_uint(e4[i]));
+                    if (keep) ring[(staged + __popcll(m & lt)) & (kRing - 1)] = e2[i];
                     staged += __popcll(m);
                     // At most 63 + 2 x 64 entries pending: the ring holds 256.
-                    if (i & 1) drain(false);
+                    if (i == 1) drain(false);
                 }
             }
 #pragma unroll
@@ -255,15 +267,14 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
         level0(std::true_type{});
     else
         level0(std::false_type{});
-    {
-        drain(true);
-    }
+    drain(true);
     if (take_all) return;
 
     int need_rem = need - gt0;
-    unsigned long long pval = clamped ? 0ull : (unsigned long long)(d0 + kPfBase);
+    const bool fixed = top < 64;
+    unsigned long long pval = fixed ? (unsigned long long)(pf_lo_ord(d0) >> (top - 32)) : 0ull;
     int pshift = top;
-    bool inlds = fits;  // candidates in cb, else re-read the row
+    bool inlds = fits;  // candidates in cb, else re-read the list
     int nsrc = fits ? nc : cnt;
     bool first = wide;  // the wide digit's histogram is already in cb
     while (top > 0) {
@@ -282,8 +293,8 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
                 for (int u = lane; u < nsrc; u += 64)
                     lds_add_u32(&h[(uint32_t)((cb[u] >> shift) & mask)], 1u);
             } else {
-                row_sweep(sr, cnt, [&](int u, float sc, bool in) {
-                    const unsigned long long key = pf_key(sc, u);
+                list_sweep(sl, cnt, [&](int s, float sc, bool in) {
+                    const unsigned long long key = pf_key(sc, s);
                     if (in && live(key, sc)) lds_add_u32(&h[(uint32_t)((key >> shift) & mask)], 1u);
                 });
             }
@@ -310,8 +321,8 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
                 visit(ok ? cb[u] : 0ull, ok);
             }
         } else {
-            row_sweep(sr, cnt, [&](int u, float sc, bool in) {
-                const unsigned long long key = pf_key(sc, u);
+            list_sweep(sl, cnt, [&](int s, float sc, bool in) {
+                const unsigned long long key = pf_key(sc, s);
                 visit(key, in && live(key, sc));
             });
         }
@@ -327,7 +338,8 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
 }
 
 template <int NHT>
-__global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_kernel(PrefillArgs a) {
     // The stages are four distinct LDS objects: the compiler then tracks the
     // direct-to-LDS loads per object and places no wait of its own for the
     // pair in flight before reads of the other pair.
@@ -338,16 +350,18 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     const int i0 = blockIdx.x * kPfRows;
     const int tid = threadIdx.x;
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+    const unsigned long long lt = (1ull << lane) - 1ull;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tmax = a.offset + min(i0 + kPfRows, a.T) - 1;
     const int ntiles = tmax / kPfTile + 1;
 
     // Per-row state of this wave's two rows.
     QFrag<NHT> f[kPfQpw];
-    int tq[kPfQpw];
+    int tq[kPfQpw], tau[kPfQpw], cnt[kPfQpw], cnt_ge[kPfQpw], htau[kPfQpw];
+    float tau_f[kPfQpw];
     bool act[kPfQpw];
     long long rowq[kPfQpw];
-    float* srow[kPfQpw];
+    uint2* sl[kPfQpw];
     uint32_t* h[kPfQpw];
 #pragma unroll
     for (int qq = 0; qq < kPfQpw; ++qq) {
@@ -355,7 +369,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         act[qq] = i < a.T;
         rowq[qq] = (long long)seq * a.T + min(i, a.T - 1);
         tq[qq] = act[qq] ? a.offset + i : -1;
-        srow[qq] = a.scores + rowq[qq] * a.stride;
+        tau[qq] = 0;
+        tau_f[qq] = -INFINITY;
+        cnt[qq] = 0;
+        cnt_ge[qq] = 0;
+        htau[qq] = 0;
+        sl[qq] = a.surv + rowq[qq] * a.cap;
         h[qq] = hist[wid * kPfQpw + qq];
         for (int x = lane; x < kPfBins; x += 64) h[qq][x] = 0u;
         load_qfrag<NHT>(f[qq], a.q + rowq[qq] * a.H * kD, a.w + rowq[qq] * a.H, a.H, nullptr, 0,
@@ -389,14 +408,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     };
 
     // Scores of tile j of a pair: lane (g, c) keeps, for the row and tile of
-    // its lane group (row g & 1, tile g >> 1), the scores of keys 4c .. 4c+3
-    // (st, stored at the next pair), and adds the score of key 4c + g of each
-    // row to that row's histogram.
+    // its lane group (row g & 1, tile g >> 1), the scores of keys 4c .. 4c+3.
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
-    auto tile_scores = [&](const uint4* ktile, int kbase, int j) __attribute__((always_inline)) {
-        float hv[kPfQpw];
-#pragma unroll
-        for (int qq = 0; qq < kPfQpw; ++qq) hv[qq] = 0.f;
+    auto tile_scores = [&](const uint4* ktile, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int gi = 0; gi < kPfTile / 16; ++gi) {
             uint4 kb[4];
@@ -414,31 +428,106 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sc = fmaf(f[qq].wv[ht][e], fmaxf(acc[ht][e], 0.f), sc);
                 sc = sum_lane_groups(sc);
-                hv[qq] = g == gi ? sc : hv[qq];
                 st[gi] = g == 2 * j + qq ? sc : st[gi];
             }
         }
-        const int s = kbase + 4 * c + g;
+    };
+
+    // Raise tau of row r while the bins at and above tau + 1 still hold k
+    // kept scores (the histogram adds of this wave are in LDS order before
+    // these reads).
+    auto raise = [&](int r) {
+        uint32_t* hr = r ? h[1] : h[0];
+        int t = r ? tau[1] : tau[0];
+        int ge = r ? cnt_ge[1] : cnt_ge[0];
+        int ht;
+        for (;;) {
+            const int bb = t + lane;
+            const int hv = bb < kPfBins ? (int)hr[bb] : 0;
+            int incl = hv;
 #pragma unroll
-        for (int qq = 0; qq < kPfQpw; ++qq) {
-            // Positive scores only: bin = (float bits >> 20) - 760 there.
-            const int v = (int)(__float_as_uint(hv[qq]) >> kPfBinShift) - (kPfBase - 2048);
-            if (s <= tq[qq] && hv[qq] > 0.f && v > 0) lds_add_u32(&h[qq][min(v, kPfBins - 1)], 1u);
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off);
+                if (lane >= off) incl += y;
+            }
+            const int excl = incl - hv;
+            const bool ok = bb < kPfBins && ge - excl >= a.k;
+            const int lstar = __popcll(__ballot(ok)) - 1;
+            t += lstar;
+            ge -= __shfl(excl, lstar);
+            if (lstar < 63 || t >= kPfBins - 1) {
+                ht = __shfl(hv, lstar);
+                break;
+            }
+        }
+        // Wave-uniform: keep them in scalar registers.
+        t = __builtin_amdgcn_readfirstlane(t);
+        ge = __builtin_amdgcn_readfirstlane(ge);
+        ht = __builtin_amdgcn_readfirstlane(ht);
+        const float tf = pf_lo(t);
+        if (r) {
+            tau[1] = t;
+            cnt_ge[1] = ge;
+            htau[1] = ht;
+            tau_f[1] = tf;
+        } else {
+            tau[0] = t;
+            cnt_ge[0] = ge;
+            htau[0] = ht;
+            tau_f[0] = tf;
         }
     };
 
-    // A pair's scores are stored at the top of the next pair, right after its
-    // stage wait, so the stores have two tiles of compute to complete before
-    // the next wait (which counts them too) comes round.  Keys past the row's
-    // last legal one inside its last tile are stored too (the line has room
-    // up to the next multiple of 64) and never read.
+    // A pair's scores are settled at the top of the next pair, right after its
+    // stage wait: each lane tests its 4 scores against its row's threshold,
+    // appends the survivors to the row's list (positions from a row-local
+    // prefix count over the lanes of the row) and to its histogram, and tau
+    // moves when it can.  The list stores then have two tiles of compute to
+    // complete before the next wait (which counts them too) comes round.
+    constexpr unsigned long long kRow0 = 0x0000FFFF0000FFFFull;  // lane groups 0 and 2
     int pend_base = -1;
-    auto put = [&]() __attribute__((always_inline)) {
+    auto settle = [&]() __attribute__((always_inline)) {
         if (pend_base < 0) return;
         const int qs = g & 1;
-        const int kb0 = pend_base + (g >> 1) * kPfTile;
-        if (kb0 <= (qs ? tq[1] : tq[0]))
-            __builtin_nontemporal_store(st, reinterpret_cast<f32x4*>((qs ? srow[1] : srow[0]) + kb0 + 4 * c));
+        const int key0 = pend_base + (g >> 1) * kPfTile + 4 * c;
+        const int tqs = qs ? tq[1] : tq[0];
+        const float thr = qs ? tau_f[1] : tau_f[0];
+        const int taus = qs ? tau[1] : tau[0];
+        bool sv[4];
+        int bn[4];
+        int n = 0, nt = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = key0 + e <= tqs && st[e] >= thr;
+            bn[e] = pf_bin(st[e]);
+            n += sv[e];
+            nt += sv[e] && bn[e] == taus;
+        }
+        const unsigned long long b0 = __ballot(n & 1), b1 = __ballot(n & 2), b2 = __ballot(n & 4);
+        const unsigned long long mrow = (qs ? ~kRow0 : kRow0) & lt;
+        int p = (qs ? cnt[1] : cnt[0]) + __popcll(b0 & mrow) + 2 * __popcll(b1 & mrow) +
+                4 * __popcll(b2 & mrow);
+        uint2* dst = qs ? sl[1] : sl[0];
+        uint32_t* hq = qs ? h[1] : h[0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (sv[e]) {
+                dst[p] = make_uint2((uint32_t)(key0 + e), __float_as_uint(st[e]));
+                lds_add_u32(&hq[bn[e]], 1u);
+            }
+            p += sv[e];
+        }
+        const unsigned long long t0 = __ballot(nt & 1), t1 = __ballot(nt & 2), t2 = __ballot(nt & 4);
+#pragma unroll
+        for (int r = 0; r < kPfQpw; ++r) {
+            const unsigned long long m = r ? ~kRow0 : kRow0;
+            const int tot = __popcll(b0 & m) + 2 * __popcll(b1 & m) + 4 * __popcll(b2 & m);
+            const int tt = __popcll(t0 & m) + 2 * __popcll(t1 & m) + 4 * __popcll(t2 & m);
+            cnt[r] += tot;
+            cnt_ge[r] += tot;
+            htau[r] += tt;
+            if (cnt_ge[r] - htau[r] >= a.k) raise(r);
+        }
         pend_base = -1;
     };
 
@@ -451,12 +540,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         __builtin_amdgcn_s_barrier();
         issue(na, tile + 2);
         issue(nb, tile + 3);
-        put();
+        settle();
         const int kbase = tile * kPfTile;
         if (kbase <= tw) {
-            tile_scores(ka, kbase, 0);
-            if (kbase + kPfTile <= tw) tile_scores(kb, kbase + kPfTile, 1);
-            pend_base = kbase;  // keys past tw are never stored
+            tile_scores(ka, 0);
+            if (kbase + kPfTile <= tw) tile_scores(kb, 1);
+            pend_base = kbase;  // keys past a row's last legal one are never kept
         }
     };
 
@@ -467,12 +556,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         if (tile + 2 >= ntiles) break;
         pair(kt2, kt3, kt0, kt1, tile + 2);
     }
-    put();
+    settle();
 
     // The key stages are free once every wave is past its last tile and the
     // last (clamped) fills have landed: they hold the candidate buffers, two
-    // rows per stage.  Each wave finishes its own rows from the score lines
-    // it wrote.
+    // rows per stage.  Each wave finishes its own rows from the survivor
+    // lists it wrote.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll 1
@@ -492,12 +581,12 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         }
         uint4* stage = wid == 0 ? kt0 : (wid == 1 ? kt1 : (wid == 2 ? kt2 : kt3));
         unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + qq * kPfCand;
-        pf_finish(qq ? h[1] : h[0], cb, qq ? srow[1] : srow[0], tqq + 1, need, oidx, osc);
+        pf_finish(qq ? h[1] : h[0], cb, qq ? sl[1] : sl[0], qq ? cnt[1] : cnt[0], need, oidx, osc);
     }
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
-    if (a.stride % 64 != 0 || a.stride < (long long)a.offset + a.T) return hipErrorInvalidValue;
+    if (a.cap % 2 != 0 || a.cap < (long long)a.offset + a.T) return hipErrorInvalidValue;
     const int batch = rows / a.T;
     const dim3 grid((unsigned)((a.T + kPfRows - 1) / kPfRows), (unsigned)batch);
     const int nht = (a.H + 15) / 16;

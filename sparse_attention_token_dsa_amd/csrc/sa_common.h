@@ -184,8 +184,8 @@ struct PrefillArgs {
     const float* w;
     const uint16_t* keys;
     int T, H, L, offset, k;
-    float* scores;              // [rows, stride] scores of the legal keys (workspace)
-    long long stride;           // >= offset + T, a multiple of 64
+    uint2* surv;                // [rows, cap] (position, score bits) survivor lists (workspace)
+    long long cap;              // >= offset + T, even
     int32_t* out_idx;           // [rows, out_stride]
     float* out_score;           // nullable
     long long out_stride;
