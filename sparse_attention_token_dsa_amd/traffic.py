@@ -1,0 +1,123 @@
+"""Measured HBM traffic of the decode scan, from rocprofv3 counters.
+
+Two counter runs of the same program, then a summary:
+
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/fetch -o p -- \
+      python3 -m sparse_attention_token_dsa_amd.traffic run
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/write -o p -- \
+      python3 -m sparse_attention_token_dsa_amd.traffic run
+  python3 -m sparse_attention_token_dsa_amd.traffic summarize OUT
+
+`run` launches the DSA decode selector on the L = 131072, batch-8, 64-head
+workload a few times, then a plain copy kernel (torch's elementwise add of a
+zero into a second 256 MiB fp32 tensor: 256 MiB read, 256 MiB written).
+`summarize` reads both runs, calibrates each counter on the copy kernel
+(counter bytes / known bytes) and writes, per launch of the scan kernel, the
+HBM bytes fetched and written divided by those factors to traffic.json
+(keyed by a digest of the scan's sources, which bench.py checks before it
+reports the figure).
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "traffic.json")
+SCAN_SOURCES = ["scan.hip", "sa_frag.h", "sa_common.h"]
+SCAN_KERNEL = "scan_kernel<4, 4, 4, 4, true, false>"
+COPY_BYTES = 256 << 20
+COPY_KERNEL = "CUDAFunctorOnSelf_add<float>"  # torch.add(src, 0.0, out=dst)
+
+
+def source_digest(names=SCAN_SOURCES):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(HERE, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def run():
+    import numpy as np
+    import torch
+
+    from sparse_attention_token_dsa_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    p = synth.make_config("misa_128k_h64")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(p["w"]).to(dev)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
+    for _ in range(4):
+        api.indexer_score_topk(q, w, K, p["offset"], 2048)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.add(src, 0.0, out=dst)
+    torch.cuda.synchronize()
+    print("traffic run done", flush=True)
+
+
+def _per_dispatch(run_dir, counter):
+    """{kernel name: [counter value per dispatch]} from one --pmc run."""
+    out = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def _pick(d, needle):
+    hits = [v for k, v in d.items() if needle in k]
+    if not hits:
+        raise SystemExit("no dispatch of %r in the counter run" % needle)
+    return statistics.median(hits[0])
+
+
+def summarize(out_dir):
+    fetch = _per_dispatch(os.path.join(out_dir, "fetch"), "FETCH_SIZE")
+    write = _per_dispatch(os.path.join(out_dir, "write"), "WRITE_SIZE")
+    scan_f, scan_w = _pick(fetch, SCAN_KERNEL), _pick(write, SCAN_KERNEL)
+    copy_f, copy_w = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
+    f_fetch = copy_f * 1024.0 / COPY_BYTES
+    f_write = copy_w * 1024.0 / COPY_BYTES
+    rec = {
+        "kernel": "scan_dsa",
+        "source_digest": source_digest(),
+        "fetch_kib_per_launch": scan_f,
+        "write_kib_per_launch": scan_w,
+        "copy_kernel_bytes_each_way": COPY_BYTES,
+        "copy_fetch_kib": copy_f,
+        "copy_write_kib": copy_w,
+        "factor_fetch": f_fetch,
+        "factor_write": f_write,
+        "bytes_per_launch": scan_f * 1024.0 / f_fetch + scan_w * 1024.0 / f_write,
+    }
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec["scan_dsa"] = rec
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 2 and sys.argv[1] == "run":
+        run()
+    elif len(sys.argv) >= 3 and sys.argv[1] == "summarize":
+        summarize(sys.argv[2])
+    else:
+        raise SystemExit(__doc__)
