@@ -4,16 +4,17 @@
 // MISA, LISA and ResMiSA", section 2.2: score, causal mask and top-k fused
 // into one pass, no n^2 score matrix written back).
 //
-// Layout: a workgroup of 4 waves owns 8 consecutive query rows of one
-// sequence (two rows per wave, their heads held as MFMA A fragments in
-// registers: each B fragment read from LDS feeds both rows) and sweeps the
-// legal keys [0, max t] in tiles of 64 keys.  Each tile (16 KiB of bf16 keys)
-// is staged once in LDS for all 8 rows by direct global-to-LDS loads, with a
-// 16-byte XOR swizzle so the B-fragment reads are free of bank conflicts.
-// Column c of MFMA group gi is key 4c + gi, so that after the head sum every
-// lane holds the scores of 4 consecutive keys.  Four stages are used in
-// pairs: one wait and one barrier per two tiles, and the next pair's loads
-// have two tiles of compute to arrive.
+// Layout: a workgroup of 16 waves owns 16 consecutive query rows of one
+// sequence, one row per wave (the row's heads held as MFMA A fragments in
+// registers; 1024 threads keep each wave within 128 registers, so every SIMD
+// runs 4 waves and their epilogue VALU work interleaves with the others'
+// MFMAs), and sweeps the legal keys [0, max t] in tiles of 64 keys.  Each
+// tile (16 KiB of bf16 keys) is staged once in LDS for all 16 rows by direct
+// global-to-LDS loads, with a 16-byte XOR swizzle so the B-fragment reads are
+// free of bank conflicts.  Column c of MFMA group gi is key 4c + gi, so that
+// after the head sum every lane holds the scores of consecutive keys.  Four
+// stages are used in pairs: one wait and one barrier per two tiles, and the
+// next pair's loads have two tiles of compute to arrive.
 //
 // Streaming threshold: each row keeps an LDS histogram of the scores it has
 // kept, over the bins below (monotone in the score).  tau is the highest bin
@@ -30,7 +31,7 @@
 // the list emits the scores above it (staged in LDS, written out 64 at a time)
 // and collects the ones in it, as 64-bit keys ord(score) << 32 | ~position
 // (ties -> lower position), into LDS; a radix select on those keys settles the
-// rest.  A bin too crowded for the LDS buffer has its next 11-bit digit counted
+// rest.  A bin too crowded for the LDS buffer has its next 10-bit digit counted
 // in the same pass, so one more pass over the list settles it or shrinks it to
 // LDS size.
 #include <type_traits>
@@ -39,38 +40,39 @@
 
 namespace sa {
 
-constexpr int kPfWaves = 4;
-constexpr int kPfQpw = 2;  // query rows per wave
-constexpr int kPfRows = kPfWaves * kPfQpw;
+constexpr int kPfWaves = 16;
+constexpr int kPfRows = kPfWaves;       // one query row per wave
 constexpr int kPfTile = 64;
 constexpr int kPfStage = kPfTile * 16;  // uint4 per stage (16 KiB)
-constexpr int kPfBins = 512;            // histogram size (bins 507 .. 511 stay empty)
-constexpr int kPfDigit = 9;             // radix digit of the finish over LDS candidates
-constexpr int kPfWide = 11;             // digit counted in the level-0 pass for crowded bins
-constexpr int kPfCand = 1024;           // LDS candidate keys per row: two rows per stage
+constexpr int kPfBins = 1024;           // histogram size (bins 947 .. 1023 stay empty)
+constexpr int kPfDigit = 10;            // radix digit of the finish over LDS candidates
+constexpr int kPfWide = 10;             // digit counted in the level-0 pass for crowded bins
+constexpr int kPfCand = 512;            // LDS candidate keys per row: four rows per stage
 constexpr int kPfSweep = 4;             // uint4 per lane per block of the level-0 pass
-static_assert(2 * kPfCand * 8 == kPfStage * 16, "two rows' candidate buffers fill one stage");
+static_assert(4 * kPfCand * 8 == kPfStage * 16, "four rows' candidate buffers fill one stage");
 static_assert((1 << kPfDigit) == kPfBins, "digit histograms reuse the row histogram");
 static_assert((1 << kPfWide) * 4 == kPfCand * 8, "the wide digit histogram fills cb");
-static_assert(kPfQpw == 2 && kPfTile == 64, "the 4 lane groups hold 2 rows x 2 tiles of a pair");
+static_assert(kPfStage == 64 * kPfWaves, "one 16-byte load per thread fills a stage");
 
 // Score bins, monotone in the score:
 //   0           x <= -2^32
 //   1 .. 64     negative x, one octave each: |x| in [2^(32-b), 2^(33-b))
 //   65          -2^-32 < x < 2^-23 (zero and the smallest magnitudes)
-//   66 .. 505   positive x in [2^-23, 2^32), 1/8 octave each
-//   506         x >= 2^32
+//   66 .. 945   positive x in [2^-23, 2^32), 1/16 octave each
+//   946         x >= 2^32
 constexpr int kPfNegOct = 64;
 constexpr int kPfMid = 65;
 constexpr int kPfPos0 = 66;
-constexpr int kPfTop = 506;
+constexpr int kPfPosShift = 19;  // float bits >> 19: exponent and 4 mantissa bits
+constexpr int kPfTop = kPfPos0 + 55 * 16;
 constexpr int kPfPosE = 104;  // biased exponent of 2^-23
 constexpr int kPfNegE = 95;   // biased exponent of 2^-32
+static_assert(kPfTop < kPfBins, "bins fit the histogram");
 
 __device__ __forceinline__ int pf_bin(float x) {
     const uint32_t u = __float_as_uint(x);
     const int e = (int)((u >> 23) & 255u);
-    const int pos = min(kPfPos0 + (int)(u >> 20) - (kPfPosE << 3), kPfTop);
+    const int pos = min(kPfPos0 + (int)(u >> kPfPosShift) - (kPfPosE << 4), kPfTop);
     const int neg = max(kPfNegOct - (e - kPfNegE), 0);
     return (u >> 31) ? (e >= kPfNegE ? neg : kPfMid) : (e >= kPfPosE ? pos : kPfMid);
 }
@@ -78,7 +80,7 @@ __device__ __forceinline__ int pf_bin(float x) {
 // Smallest order key ord(x) of bin b, 1 <= b <= kPfTop.
 __device__ __forceinline__ uint32_t pf_lo_ord(int b) {
     return b <= kPfMid ? 0x80000000u - ((uint32_t)(kPfNegE + 1 + kPfNegOct - b) << 23)
-                       : 0x80000000u | ((uint32_t)(b - kPfPos0 + (kPfPosE << 3)) << 20);
+                       : 0x80000000u | ((uint32_t)(b - kPfPos0 + (kPfPosE << 4)) << kPfPosShift);
 }
 
 // Bin b as the score interval [lo, hi).
@@ -89,7 +91,7 @@ __device__ __forceinline__ float pf_hi(int b) {
 
 // Key bits a bin fixes: 63 .. top (top = 64: none).
 __device__ __forceinline__ int pf_top(int b) {
-    return (b >= kPfPos0 && b < kPfTop) ? 52 : ((b >= 1 && b <= kPfNegOct) ? 55 : 64);
+    return (b >= kPfPos0 && b < kPfTop) ? 32 + kPfPosShift : ((b >= 1 && b <= kPfNegOct) ? 55 : 64);
 }
 
 __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
@@ -255,7 +257,7 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
                     const unsigned long long m = __ballot(keep);
                     if (keep) ring[(staged + __popcll(m & lt)) & (kRing - 1)] = e2[i];
                     staged += __popcll(m);
-                    // At most 63 + 2 x 64 entries pending: the ring holds 256.
+                    // At most 63 + 2 x 64 entries pending: the ring holds 512.
                     if (i == 1) drain(false);
                 }
             }
@@ -338,13 +340,13 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
 }
 
 template <int NHT>
-__global__ __launch_bounds__(64 * kPfWaves) __attribute__((amdgpu_waves_per_eu(2)))
-void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     // The stages are four distinct LDS objects: the compiler then tracks the
     // direct-to-LDS loads per object and places no wait of its own for the
     // pair in flight before reads of the other pair.
     __shared__ uint4 kt0[kPfStage], kt1[kPfStage], kt2[kPfStage], kt3[kPfStage];
     __shared__ uint32_t hist[kPfRows][kPfBins];
+    __shared__ float4 wts[kPfRows][kMaxH / 4];  // each row's w (zero past H)
 
     const int seq = blockIdx.y;
     const int i0 = blockIdx.x * kPfRows;
@@ -355,95 +357,73 @@ void prefill_kernel(PrefillArgs a) {
     const int tmax = a.offset + min(i0 + kPfRows, a.T) - 1;
     const int ntiles = tmax / kPfTile + 1;
 
-    // Per-row state of this wave's two rows.
-    QFrag<NHT> f[kPfQpw];
-    int tq[kPfQpw], tau[kPfQpw], cnt[kPfQpw], cnt_ge[kPfQpw], htau[kPfQpw];
-    float tau_f[kPfQpw];
-    bool act[kPfQpw];
-    long long rowq[kPfQpw];
-    uint2* sl[kPfQpw];
-    uint32_t* h[kPfQpw];
-#pragma unroll
-    for (int qq = 0; qq < kPfQpw; ++qq) {
-        const int i = i0 + wid * kPfQpw + qq;
-        act[qq] = i < a.T;
-        rowq[qq] = (long long)seq * a.T + min(i, a.T - 1);
-        tq[qq] = act[qq] ? a.offset + i : -1;
-        tau[qq] = 0;
-        tau_f[qq] = -INFINITY;
-        cnt[qq] = 0;
-        cnt_ge[qq] = 0;
-        htau[qq] = 0;
-        sl[qq] = a.surv + rowq[qq] * a.cap;
-        h[qq] = hist[wid * kPfQpw + qq];
-        for (int x = lane; x < kPfBins; x += 64) h[qq][x] = 0u;
-        load_qfrag<NHT>(f[qq], a.q + rowq[qq] * a.H * kD, a.w + rowq[qq] * a.H, a.H, nullptr, 0,
-                        g, c);
-        if (!act[qq]) {
-#pragma unroll
-            for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) f[qq].wv[ht][e] = 0.f;
-        }
-    }
-    const int tw = max(tq[0], tq[kPfQpw - 1]);  // last legal key of this wave
+    // This wave's row.
+    const int i = i0 + wid;
+    const bool act = i < a.T;
+    const long long rowq = (long long)seq * a.T + min(i, a.T - 1);
+    const int tq = act ? a.offset + i : -1;  // last legal key (-1: no row)
+    uint2* const sl = a.surv + rowq * a.cap;
+    uint32_t* const h = hist[wid];
+    for (int x = lane; x < kPfBins; x += 64) h[x] = 0u;
+    QFrag<NHT> f;  // A fragments only: the epilogue reads w from LDS, which
+                   // keeps the wave within 128 registers
+    load_qfrag<NHT>(f, a.q + rowq * a.H * kD, a.w + rowq * a.H, a.H, nullptr, 0, g, c);
+    reinterpret_cast<float*>(wts[wid])[lane] = act && lane < a.H ? a.w[rowq * a.H + lane] : 0.f;
+    int tau = 0, cnt = 0, cnt_ge = 0, htau = 0;
+    float tau_f = -INFINITY;
 
     const uint16_t* kseq = a.keys + (long long)seq * a.L * kD;
-    // Stage fill: a wave's load instruction writes 1 KiB of LDS (64 lanes x
-    // 16 bytes at consecutive addresses) = 4 key rows, block blk = 4j + wave.
-    // Lane l lands at key 4*blk + l/16, slot l%16 of the row, and fetches the
-    // chunk that belongs in that slot under the swizzle slot ^ (key/4 % 16),
-    // i.e. slot ^ blk.  Tiles past the last are clamped re-reads.
-    constexpr int kPfLoads = kPfStage / (64 * kPfWaves);
+    // Stage fill: each wave's load instruction writes 1 KiB of LDS (64 lanes x
+    // 16 bytes at consecutive addresses) = 4 key rows, block = wave.  Lane l
+    // lands at key 4*wave + l/16, slot l%16 of the row, and fetches the chunk
+    // that belongs in that slot under the swizzle slot ^ (key/4 % 16), i.e.
+    // slot ^ wave.  Tiles past the last are clamped re-reads.
     auto issue = [&](uint4* stage, int tile) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < kPfLoads; ++j) {
-            const int blk = kPfWaves * j + wid;
-            const int key = 4 * blk + (lane >> 4);
-            const int s = min(tile * kPfTile + key, tmax);
-            const int chunk = (lane & 15) ^ blk;
-            __builtin_amdgcn_global_load_lds(kseq + (long long)s * kD + chunk * 8,
-                                             stage + blk * 64, 16, 0, 0);
-        }
+        const int key = 4 * wid + (lane >> 4);
+        const int s = min(tile * kPfTile + key, tmax);
+        const int chunk = (lane & 15) ^ wid;
+        __builtin_amdgcn_global_load_lds(kseq + (long long)s * kD + chunk * 8, stage + wid * 64,
+                                         16, 0, 0);
     };
 
-    // Scores of tile j of a pair: lane (g, c) keeps, for the row and tile of
-    // its lane group (row g & 1, tile g >> 1), the scores of keys 4c .. 4c+3.
-    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+    // Scores of tile j of a pair.  After the head sum every lane holds the
+    // score of key 4c + gi of group gi; lane group g keeps those of tile
+    // g >> 1, keys 4c + 2 (g & 1) and 4c + 2 (g & 1) + 1, in st.
+    float st[2] = {0.f, 0.f};
     auto tile_scores = [&](const uint4* ktile, int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int gi = 0; gi < kPfTile / 16; ++gi) {
             uint4 kb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) kb[kk] = ktile[(4 * c + gi) * 16 + ((kk * 4 + g) ^ c)];
+            f32x4 acc[NHT];
+            group_dots<NHT, 4>(f, kb, acc);
+            // Compiler-only barrier: w is read again from LDS for each group
+            // instead of being kept live in 16 registers across the tiles.
+            asm volatile("" ::: "memory");
+            float sc = 0.f;
 #pragma unroll
-            for (int qq = 0; qq < kPfQpw; ++qq) {
-                // One row at a time keeps 16 accumulator registers live; the
-                // other wave on the SIMD fills the MFMA pipe meanwhile.
-                f32x4 acc[NHT];
-                group_dots<NHT, 4>(f[qq], kb, acc);
-                float sc = 0.f;
-#pragma unroll
-                for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sc = fmaf(f[qq].wv[ht][e], fmaxf(acc[ht][e], 0.f), sc);
-                sc = sum_lane_groups(sc);
-                st[gi] = g == 2 * j + qq ? sc : st[gi];
+            for (int ht = 0; ht < NHT; ++ht) {
+                // Heads 16 ht + 4 g + e of accumulator element e (one 16-byte
+                // LDS read, shared by the 16 lanes of the group).
+                const float4 w4 = wts[wid][4 * ht + g];
+                sc = fmaf(w4.x, fmaxf(acc[ht][0], 0.f), sc);
+                sc = fmaf(w4.y, fmaxf(acc[ht][1], 0.f), sc);
+                sc = fmaf(w4.z, fmaxf(acc[ht][2], 0.f), sc);
+                sc = fmaf(w4.w, fmaxf(acc[ht][3], 0.f), sc);
             }
+            sc = sum_lane_groups(sc);
+            st[gi & 1] = g == 2 * j + (gi >> 1) ? sc : st[gi & 1];
         }
     };
 
-    // Raise tau of row r while the bins at and above tau + 1 still hold k
-    // kept scores (the histogram adds of this wave are in LDS order before
-    // these reads).
-    auto raise = [&](int r) {
-        uint32_t* hr = r ? h[1] : h[0];
-        int t = r ? tau[1] : tau[0];
-        int ge = r ? cnt_ge[1] : cnt_ge[0];
-        int ht;
+    // Raise tau while the bins at and above tau + 1 still hold k kept scores
+    // (this wave's histogram adds are in LDS order before these reads).
+    auto raise = [&]() {
+        int t = tau, ge = cnt_ge, ht;
         for (;;) {
             const int bb = t + lane;
-            const int hv = bb < kPfBins ? (int)hr[bb] : 0;
+            const int hv = bb < kPfBins ? (int)h[bb] : 0;
             int incl = hv;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -461,73 +441,48 @@ void prefill_kernel(PrefillArgs a) {
             }
         }
         // Wave-uniform: keep them in scalar registers.
-        t = __builtin_amdgcn_readfirstlane(t);
-        ge = __builtin_amdgcn_readfirstlane(ge);
-        ht = __builtin_amdgcn_readfirstlane(ht);
-        const float tf = pf_lo(t);
-        if (r) {
-            tau[1] = t;
-            cnt_ge[1] = ge;
-            htau[1] = ht;
-            tau_f[1] = tf;
-        } else {
-            tau[0] = t;
-            cnt_ge[0] = ge;
-            htau[0] = ht;
-            tau_f[0] = tf;
-        }
+        tau = __builtin_amdgcn_readfirstlane(t);
+        cnt_ge = __builtin_amdgcn_readfirstlane(ge);
+        htau = __builtin_amdgcn_readfirstlane(ht);
+        tau_f = pf_lo(tau);
     };
 
     // A pair's scores are settled at the top of the next pair, right after its
-    // stage wait: each lane tests its 4 scores against its row's threshold,
-    // appends the survivors to the row's list (positions from a row-local
-    // prefix count over the lanes of the row) and to its histogram, and tau
-    // moves when it can.  The list stores then have two tiles of compute to
-    // complete before the next wait (which counts them too) comes round.
-    constexpr unsigned long long kRow0 = 0x0000FFFF0000FFFFull;  // lane groups 0 and 2
+    // stage wait: each lane tests its 2 scores against the row's threshold,
+    // appends the survivors to the row's list (positions from a prefix count
+    // over the wave) and to its histogram, and tau moves when it can.  The
+    // list stores then have two tiles of compute to complete before the next
+    // wait (which counts them too) comes round.
     int pend_base = -1;
     auto settle = [&]() __attribute__((always_inline)) {
         if (pend_base < 0) return;
-        const int qs = g & 1;
-        const int key0 = pend_base + (g >> 1) * kPfTile + 4 * c;
-        const int tqs = qs ? tq[1] : tq[0];
-        const float thr = qs ? tau_f[1] : tau_f[0];
-        const int taus = qs ? tau[1] : tau[0];
-        bool sv[4];
-        int bn[4];
+        const int key0 = pend_base + (g >> 1) * kPfTile + 4 * c + 2 * (g & 1);
+        bool sv[2];
+        int bn[2];
         int n = 0, nt = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            sv[e] = key0 + e <= tqs && st[e] >= thr;
+        for (int e = 0; e < 2; ++e) {
+            sv[e] = key0 + e <= tq && st[e] >= tau_f;
             bn[e] = pf_bin(st[e]);
             n += sv[e];
-            nt += sv[e] && bn[e] == taus;
+            nt += sv[e] && bn[e] == tau;
         }
-        const unsigned long long b0 = __ballot(n & 1), b1 = __ballot(n & 2), b2 = __ballot(n & 4);
-        const unsigned long long mrow = (qs ? ~kRow0 : kRow0) & lt;
-        int p = (qs ? cnt[1] : cnt[0]) + __popcll(b0 & mrow) + 2 * __popcll(b1 & mrow) +
-                4 * __popcll(b2 & mrow);
-        uint2* dst = qs ? sl[1] : sl[0];
-        uint32_t* hq = qs ? h[1] : h[0];
+        const unsigned long long b0 = __ballot(n & 1), b1 = __ballot(n & 2);
+        int p = cnt + __popcll(b0 & lt) + 2 * __popcll(b1 & lt);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < 2; ++e) {
             if (sv[e]) {
-                dst[p] = make_uint2((uint32_t)(key0 + e), __float_as_uint(st[e]));
-                lds_add_u32(&hq[bn[e]], 1u);
+                sl[p] = make_uint2((uint32_t)(key0 + e), __float_as_uint(st[e]));
+                lds_add_u32(&h[bn[e]], 1u);
             }
             p += sv[e];
         }
-        const unsigned long long t0 = __ballot(nt & 1), t1 = __ballot(nt & 2), t2 = __ballot(nt & 4);
-#pragma unroll
-        for (int r = 0; r < kPfQpw; ++r) {
-            const unsigned long long m = r ? ~kRow0 : kRow0;
-            const int tot = __popcll(b0 & m) + 2 * __popcll(b1 & m) + 4 * __popcll(b2 & m);
-            const int tt = __popcll(t0 & m) + 2 * __popcll(t1 & m) + 4 * __popcll(t2 & m);
-            cnt[r] += tot;
-            cnt_ge[r] += tot;
-            htau[r] += tt;
-            if (cnt_ge[r] - htau[r] >= a.k) raise(r);
-        }
+        const unsigned long long t0 = __ballot(nt & 1), t1 = __ballot(nt & 2);
+        const int tot = __popcll(b0) + 2 * __popcll(b1);
+        cnt += tot;
+        cnt_ge += tot;
+        htau += __popcll(t0) + 2 * __popcll(t1);
+        if (cnt_ge - htau >= a.k) raise();
         pend_base = -1;
     };
 
@@ -542,10 +497,10 @@ void prefill_kernel(PrefillArgs a) {
         issue(nb, tile + 3);
         settle();
         const int kbase = tile * kPfTile;
-        if (kbase <= tw) {
+        if (kbase <= tq) {
             tile_scores(ka, 0);
-            if (kbase + kPfTile <= tw) tile_scores(kb, 1);
-            pend_base = kbase;  // keys past a row's last legal one are never kept
+            if (kbase + kPfTile <= tq) tile_scores(kb, 1);
+            pend_base = kbase;  // keys past the row's last legal one are never kept
         }
     };
 
@@ -559,30 +514,23 @@ void prefill_kernel(PrefillArgs a) {
     settle();
 
     // The key stages are free once every wave is past its last tile and the
-    // last (clamped) fills have landed: they hold the candidate buffers, two
-    // rows per stage.  Each wave finishes its own rows from the survivor
-    // lists it wrote.
+    // last (clamped) fills have landed: they hold the candidate buffers, four
+    // rows per stage.  Each wave finishes its own row from the survivor list
+    // it wrote.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll 1
-    for (int qq = 0; qq < kPfQpw; ++qq) {
-        // One copy of the finish for both rows (selects, not array indexing,
-        // keep the per-row values in registers).
-        const bool aq = qq ? act[1] : act[0];
-        if (!aq) continue;
-        const int tqq = qq ? tq[1] : tq[0];
-        const long long rq = qq ? rowq[1] : rowq[0];
-        const int need = min(a.k, tqq + 1);
-        int32_t* oidx = a.out_idx + rq * a.out_stride;
-        float* osc = a.out_score ? a.out_score + rq * a.out_stride : nullptr;
-        for (int u = need + lane; u < a.k; u += 64) {
-            oidx[u] = -1;
-            if (osc) osc[u] = -INFINITY;
-        }
-        uint4* stage = wid == 0 ? kt0 : (wid == 1 ? kt1 : (wid == 2 ? kt2 : kt3));
-        unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + qq * kPfCand;
-        pf_finish(qq ? h[1] : h[0], cb, qq ? sl[1] : sl[0], qq ? cnt[1] : cnt[0], need, oidx, osc);
+    if (!act) return;
+    const int need = min(a.k, tq + 1);
+    int32_t* oidx = a.out_idx + rowq * a.out_stride;
+    float* osc = a.out_score ? a.out_score + rowq * a.out_stride : nullptr;
+    for (int u = need + lane; u < a.k; u += 64) {
+        oidx[u] = -1;
+        if (osc) osc[u] = -INFINITY;
     }
+    const int sq = wid >> 2;
+    uint4* stage = sq == 0 ? kt0 : (sq == 1 ? kt1 : (sq == 2 ? kt2 : kt3));
+    unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + (wid & 3) * kPfCand;
+    pf_finish(h, cb, sl, cnt, need, oidx, osc);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
