@@ -4,17 +4,30 @@
 // MISA, LISA and ResMiSA", section 2.2: score, causal mask and top-k fused
 // into one pass, no n^2 score matrix written back).
 //
-// Layout: a workgroup of 16 waves owns 16 consecutive query rows of one
-// sequence, one row per wave (the row's heads held as MFMA A fragments in
-// registers; 1024 threads keep each wave within 128 registers, so every SIMD
-// runs 4 waves and their epilogue VALU work interleaves with the others'
-// MFMAs), and sweeps the legal keys [0, max t] in tiles of 64 keys.  Each
-// tile (16 KiB of bf16 keys) is staged once in LDS for all 16 rows by direct
-// global-to-LDS loads, with a 16-byte XOR swizzle so the B-fragment reads are
-// free of bank conflicts.  Column c of MFMA group gi is key 4c + gi, so that
-// after the head sum every lane holds the scores of consecutive keys.  Four
-// stages are used in pairs: one wait and one barrier per two tiles, and the
-// next pair's loads have two tiles of compute to arrive.
+// Layout: a workgroup of 8 waves owns 16 consecutive query rows of one
+// sequence, two rows per wave (their heads and weights held in registers as
+// MFMA A fragments; each B fragment read from LDS feeds both rows, which keeps
+// the LDS read traffic at about half of what the MFMAs can absorb), and sweeps
+// the legal keys [0, max t] in tiles of 64 keys.  Each tile (16 KiB of bf16
+// keys) is staged once in LDS for all 16 rows by direct global-to-LDS loads,
+// in blocks of 4 keys padded by 16 bytes: the lanes that read one B-fragment
+// chunk (keys 4c + gi, c = 0..15) hit distinct bank groups, and every chunk's
+// address is one per-lane base plus an immediate offset.  Column c of MFMA
+// group gi is key 4c + gi, so that after the head sum every lane holds the
+// scores of 4 consecutive keys.  Four stages are used in pairs: one wait and
+// one barrier per two tiles, and the next pair's loads have two tiles of
+// compute to arrive.
+//
+// Epilogue: with ReLU(z) = (z + |z|) / 2,
+//     I = sum_j w_j ReLU(z_j) = g . k + sum_j (w_j / 2) |z_j|,   g = sum_j (w_j / 2) q_j,
+// the linear part being the one shared keys let the heads merge into
+// (PaperTrace, "2.2.2 MISA, LISA and ResMiSA", section 3.1).  The per-head
+// part is then one fused multiply-add per (head, key), |z| being a free
+// operand modifier, instead of a max and a multiply-add.  g . k is one more
+// MFMA tile per 16 keys for all 16 rows of the workgroup (g split into bf16
+// hi + lo, so g . k keeps about 16 bits more than bf16): the pair's 8 groups
+// are computed by 8 of the waves and pass through LDS to the row's wave when
+// the pair's scores are settled.
 //
 // Streaming threshold: each row keeps an LDS histogram of the scores it has
 // kept, over the bins below (monotone in the score).  tau is the highest bin
@@ -40,19 +53,22 @@
 
 namespace sa {
 
-constexpr int kPfWaves = 16;
-constexpr int kPfRows = kPfWaves;       // one query row per wave
+constexpr int kPfWaves = 8;
+constexpr int kPfQpw = 2;               // query rows per wave
+constexpr int kPfRows = kPfWaves * kPfQpw;
 constexpr int kPfTile = 64;
-constexpr int kPfStage = kPfTile * 16;  // uint4 per stage (16 KiB)
+constexpr int kPfBlk = 65;              // uint4 per 4-key block: 1 KiB + 16 B pad
+constexpr int kPfStage = 16 * kPfBlk;   // uint4 per stage (16 blocks, 16.25 KiB)
 constexpr int kPfBins = 1024;           // histogram size (bins 947 .. 1023 stay empty)
 constexpr int kPfDigit = 10;            // radix digit of the finish over LDS candidates
 constexpr int kPfWide = 10;             // digit counted in the level-0 pass for crowded bins
 constexpr int kPfCand = 512;            // LDS candidate keys per row: four rows per stage
 constexpr int kPfSweep = 4;             // uint4 per lane per block of the level-0 pass
-static_assert(4 * kPfCand * 8 == kPfStage * 16, "four rows' candidate buffers fill one stage");
+static_assert(4 * kPfCand * 8 <= kPfStage * 16, "four rows' candidate buffers fit one stage");
 static_assert((1 << kPfDigit) == kPfBins, "digit histograms reuse the row histogram");
 static_assert((1 << kPfWide) * 4 == kPfCand * 8, "the wide digit histogram fills cb");
-static_assert(kPfStage == 64 * kPfWaves, "one 16-byte load per thread fills a stage");
+static_assert(kPfRows == 16 && kPfWaves == 8, "16 rows: one g tile; 2 blocks per wave fill a stage");
+static_assert(kPfQpw == 2, "the 4 lane groups hold 2 rows x 2 tiles of a pair");
 
 // Score bins, monotone in the score:
 //   0           x <= -2^32
@@ -94,6 +110,12 @@ __device__ __forceinline__ int pf_top(int b) {
     return (b >= kPfPos0 && b < kPfTop) ? 32 + kPfPosShift : ((b >= 1 && b <= kPfNegOct) ? 55 : 64);
 }
 
+// Number of set bits of m below this lane (no 64-bit lane mask kept live).
+__device__ __forceinline__ int below(unsigned long long m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
     return ((unsigned long long)ord_key(sc) << 32) | (unsigned long long)(~(uint32_t)idx);
 }
@@ -104,6 +126,21 @@ __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
 // wave's own later reads of the histogram see it.
 __device__ __forceinline__ void lds_add_u32(uint32_t* p, uint32_t v) {
     asm volatile("ds_add_u32 %0, %1" : : "v"((uint32_t)(uintptr_t)p), "v"(v) : "memory");
+}
+
+
+// Scheduling of one pipelined block: M MFMAs, V VALU instructions spread
+// evenly between them and, with RELOAD, one LDS read after each k-step's
+// NHT MFMAs.
+template <int I, int M, int V, int NHT, bool RELOAD>
+__device__ __forceinline__ void pf_interleave() {
+    if constexpr (I < M) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        constexpr int nv = V * (I + 1) / M - V * I / M;
+        if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+        if constexpr (RELOAD && I % NHT == NHT - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        pf_interleave<I + 1, M, V, NHT, RELOAD>();
+    }
 }
 
 // One pass of a wave over a survivor list sl[0, cnt) of (position, score
@@ -346,84 +383,193 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     // pair in flight before reads of the other pair.
     __shared__ uint4 kt0[kPfStage], kt1[kPfStage], kt2[kPfStage], kt3[kPfStage];
     __shared__ uint32_t hist[kPfRows][kPfBins];
-    __shared__ float4 wts[kPfRows][kMaxH / 4];  // each row's w (zero past H)
+    // A fragments of the rows' g (hi, lo: tile row = workgroup row) and the
+    // g . k values of the last two pairs (pair parity, tile, row, 4 keys).
+    __shared__ uint4 gfrag[2][4][64];
+    __shared__ float4 gk[2][2][kPfRows][kPfTile / 4];
 
     const int seq = blockIdx.y;
     const int i0 = blockIdx.x * kPfRows;
     const int tid = threadIdx.x;
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
-    const unsigned long long lt = (1ull << lane) - 1ull;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int tmax = a.offset + min(i0 + kPfRows, a.T) - 1;
     const int ntiles = tmax / kPfTile + 1;
 
-    // This wave's row.
-    const int i = i0 + wid;
-    const bool act = i < a.T;
-    const long long rowq = (long long)seq * a.T + min(i, a.T - 1);
-    const int tq = act ? a.offset + i : -1;  // last legal key (-1: no row)
-    uint2* const sl = a.surv + rowq * a.cap;
-    uint32_t* const h = hist[wid];
-    for (int x = lane; x < kPfBins; x += 64) h[x] = 0u;
-    QFrag<NHT> f;  // A fragments only: the epilogue reads w from LDS, which
-                   // keeps the wave within 128 registers
-    load_qfrag<NHT>(f, a.q + rowq * a.H * kD, a.w + rowq * a.H, a.H, nullptr, 0, g, c);
-    reinterpret_cast<float*>(wts[wid])[lane] = act && lane < a.H ? a.w[rowq * a.H + lane] : 0.f;
-    int tau = 0, cnt = 0, cnt_ge = 0, htau = 0;
-    float tau_f = -INFINITY;
+    // Per-row state of this wave's two rows (workgroup rows 2 wid + qq).
+    QFrag<NHT> f[kPfQpw];
+    int tq[kPfQpw], tau[kPfQpw], cnt[kPfQpw], cnt_ge[kPfQpw], htau[kPfQpw];
+    float tau_f[kPfQpw];
+    bool act[kPfQpw];
+    long long rowq[kPfQpw];
+    uint2* sl[kPfQpw];
+    uint32_t* h[kPfQpw];
+#pragma unroll
+    for (int qq = 0; qq < kPfQpw; ++qq) {
+        const int r = wid * kPfQpw + qq;
+        const int i = i0 + r;
+        act[qq] = i < a.T;
+        rowq[qq] = (long long)seq * a.T + min(i, a.T - 1);
+        tq[qq] = act[qq] ? a.offset + i : -1;
+        tau[qq] = 0;
+        tau_f[qq] = -INFINITY;
+        cnt[qq] = 0;
+        cnt_ge[qq] = 0;
+        htau[qq] = 0;
+        sl[qq] = a.surv + rowq[qq] * a.cap;
+        h[qq] = hist[r];
+        for (int x = lane; x < kPfBins; x += 64) h[qq][x] = 0u;
+        const float* wrow = a.w + rowq[qq] * a.H;
+        load_qfrag<NHT>(f[qq], a.q + rowq[qq] * a.H * kD, wrow, a.H, nullptr, 0, g, c);
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[qq].wv[ht][e] = act[qq] ? 0.5f * f[qq].wv[ht][e] : 0.f;
+        // g = sum_j (w_j / 2) q_j of the row, two dims per lane, heads in
+        // order, staged in gk (free until the sweep starts); lanes 0..15 then
+        // pack the row's A-fragment entries: lane t holds dims
+        // (kk*4 + grp)*8 .. +8 with kk = t / 4, grp = t % 4, for tile row r.
+        const float wl = act[qq] && lane < a.H ? 0.5f * wrow[lane] : 0.f;
+        const uint16_t* qr = a.q + rowq[qq] * a.H * kD;
+        float g0 = 0.f, g1 = 0.f;
+        for (int j = 0; j < a.H; ++j) {
+            const float wj = __shfl(wl, j);
+            const uint32_t two = *reinterpret_cast<const uint32_t*>(qr + j * kD + 2 * lane);
+            g0 = fmaf(wj, bf16_bits_to_f32(two & 0xffffu), g0);
+            g1 = fmaf(wj, bf16_bits_to_f32(two >> 16), g1);
+        }
+        float* gt = reinterpret_cast<float*>(&gk[0][0][0][0]) + r * kD;
+        gt[2 * lane] = g0;
+        gt[2 * lane + 1] = g1;
+        if (lane < 16) {
+            const int kk = lane >> 2, grp = lane & 3;
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float v0 = gt[(kk * 4 + grp) * 8 + 2 * e];
+                const float v1 = gt[(kk * 4 + grp) * 8 + 2 * e + 1];
+                const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+                hi[e] = h0 | (h1 << 16);
+                lo[e] = f32_to_bf16_bits(v0 - bf16_bits_to_f32(h0)) |
+                        (f32_to_bf16_bits(v1 - bf16_bits_to_f32(h1)) << 16);
+            }
+            gfrag[0][kk][16 * grp + r] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            gfrag[1][kk][16 * grp + r] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+    }
+    __syncthreads();  // fragments visible; the staging area is free again
+    const int tw = max(tq[0], tq[kPfQpw - 1]);  // last legal key of this wave
 
     const uint16_t* kseq = a.keys + (long long)seq * a.L * kD;
-    // Stage fill: each wave's load instruction writes 1 KiB of LDS (64 lanes x
-    // 16 bytes at consecutive addresses) = 4 key rows, block = wave.  Lane l
-    // lands at key 4*wave + l/16, slot l%16 of the row, and fetches the chunk
-    // that belongs in that slot under the swizzle slot ^ (key/4 % 16), i.e.
-    // slot ^ wave.  Tiles past the last are clamped re-reads.
+    // Stage fill: each load instruction of a wave writes one 4-key block (64
+    // lanes x 16 bytes at consecutive addresses); wave w fills blocks w and
+    // w + 8: lane l brings chunk l%16 of key 4*block + l/16.  Tiles past the
+    // last are clamped re-reads.  The fills are buffer loads over the tile's
+    // 16 KiB (base key k0): unlike the global form, they leave the compiler's
+    // LDS wait counts exact, so the B-fragment reads of the sweep are waited
+    // for one by one.
     auto issue = [&](uint4* stage, int tile) __attribute__((always_inline)) {
-        const int key = 4 * wid + (lane >> 4);
-        const int s = min(tile * kPfTile + key, tmax);
-        const int chunk = (lane & 15) ^ wid;
-        __builtin_amdgcn_global_load_lds(kseq + (long long)s * kD + chunk * 8, stage + wid * 64,
-                                         16, 0, 0);
+        const int k0 = min(tile * kPfTile, tmax);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(kseq + (long long)k0 * kD), 0, kPfTile * kD * 2, 0x00020000);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int blk = wid + kPfWaves * jb;
+            const int key = 4 * blk + (lane >> 4);
+            const int s = min(tile * kPfTile + key, tmax);  // k0 <= s < k0 + 64
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(stage + blk * kPfBlk), 16,
+                (uint32_t)((s - k0) * kD * 2 + (lane & 15) * 16), 0, 0, 0);
+        }
     };
+    // B fragment of step kk for key 4c + gi: block c, row gi, chunk kk*4 + g.
+    const int bbase = c * kPfBlk + g;
 
-    // Scores of tile j of a pair.  After the head sum every lane holds the
-    // score of key 4c + gi of group gi; lane group g keeps those of tile
-    // g >> 1, keys 4c + 2 (g & 1) and 4c + 2 (g & 1) + 1, in st.
-    float st[2] = {0.f, 0.f};
-    auto tile_scores = [&](const uint4* ktile, int j) __attribute__((always_inline)) {
+    // Scores of tile j of a pair: lane (g, c) keeps, for the row and tile of
+    // its lane group (row g & 1, tile g >> 1), the per-head part of the
+    // scores of keys 4c .. 4c+3 in st.
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
+    // The pair's 16 blocks (group G = 4 j + gi of its two tiles, row qq) run
+    // as a software pipeline: block n issues its MFMAs into acc[qq] while
+    // the epilogue of block n - 1 (the other accumulator set) is interleaved
+    // between them, so that the wave keeps the MFMA pipe fed by itself.  The
+    // B fragments of group G + 1 are re-read into the registers of group G
+    // right after the second row's last use of each k-step; only the pair's
+    // first read waits in full.  The second tile's stage always holds a
+    // (possibly clamped) fill, so reading it ahead is harmless.
+    uint4 bf[4];
+    f32x4 acc[kPfQpw][NHT];
+    auto load_b = [&](const uint4* ktile, int gi) __attribute__((always_inline)) {
 #pragma unroll
-        for (int gi = 0; gi < kPfTile / 16; ++gi) {
-            uint4 kb[4];
+        for (int kk = 0; kk < 4; ++kk) bf[kk] = ktile[bbase + gi * 16 + kk * 4];
+    };
+    auto epilogue = [&](int qq, int j, int gi) __attribute__((always_inline)) {
+        float sc = 0.f;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) kb[kk] = ktile[(4 * c + gi) * 16 + ((kk * 4 + g) ^ c)];
-            f32x4 acc[NHT];
-            group_dots<NHT, 4>(f, kb, acc);
-            // Compiler-only barrier: w is read again from LDS for each group
-            // instead of being kept live in 16 registers across the tiles.
-            asm volatile("" ::: "memory");
-            float sc = 0.f;
+        for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-            for (int ht = 0; ht < NHT; ++ht) {
-                // Heads 16 ht + 4 g + e of accumulator element e (one 16-byte
-                // LDS read, shared by the 16 lanes of the group).
-                const float4 w4 = wts[wid][4 * ht + g];
-                sc = fmaf(w4.x, fmaxf(acc[ht][0], 0.f), sc);
-                sc = fmaf(w4.y, fmaxf(acc[ht][1], 0.f), sc);
-                sc = fmaf(w4.z, fmaxf(acc[ht][2], 0.f), sc);
-                sc = fmaf(w4.w, fmaxf(acc[ht][3], 0.f), sc);
-            }
-            sc = sum_lane_groups(sc);
-            st[gi & 1] = g == 2 * j + (gi >> 1) ? sc : st[gi & 1];
+            for (int e = 0; e < 4; ++e) sc = fmaf(f[qq].wv[ht][e], fabsf(acc[qq][ht][e]), sc);
+        sc = sum_lane_groups(sc);
+        st[gi] = g == 2 * j + qq ? sc : st[gi];
+    };
+    // Block (G, qq); RELOAD: re-read group G + 1 (at ntile, group ngi) behind
+    // the MFMAs; PREV: run the epilogue of the block before, (pj, pgi, 1 - qq).
+    auto block = [&](auto reload_c, auto prev_c, int qq, const uint4* ntile, int ngi, int pj,
+                     int pgi) __attribute__((always_inline)) {
+        constexpr bool kReload = decltype(reload_c)::value;
+        constexpr bool kPrev = decltype(prev_c)::value;
+        // Each block is scheduled on its own.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht)
+                acc[qq][ht] = mfma16x16x32(f[qq].a[ht][kk], bf[kk],
+                                           kk ? acc[qq][ht] : f32x4{0.f, 0.f, 0.f, 0.f});
+            if (kReload) bf[kk] = ntile[bbase + ngi * 16 + kk * 4];
+        }
+        if (kPrev) epilogue(1 - qq, pj, pgi);
+        pf_interleave<0, 4 * NHT, (kPrev ? 4 * NHT + 7 : 0), NHT, kReload>();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pair_scores = [&](const uint4* ka, const uint4* kb, bool two) __attribute__((always_inline)) {
+        const std::true_type y;
+        const std::false_type n;
+        load_b(ka, 0);
+        block(n, n, 0, ka, 0, 0, 0);
+        block(y, y, 1, ka, 1, 0, 0);
+        block(n, y, 0, ka, 0, 0, 0);
+        block(y, y, 1, ka, 2, 0, 1);
+        block(n, y, 0, ka, 0, 0, 1);
+        block(y, y, 1, ka, 3, 0, 2);
+        block(n, y, 0, ka, 0, 0, 2);
+        block(y, y, 1, kb, 0, 0, 3);
+        if (two) {
+            block(n, y, 0, kb, 0, 0, 3);
+            block(y, y, 1, kb, 1, 1, 0);
+            block(n, y, 0, kb, 0, 1, 0);
+            block(y, y, 1, kb, 2, 1, 1);
+            block(n, y, 0, kb, 0, 1, 1);
+            block(y, y, 1, kb, 3, 1, 2);
+            block(n, y, 0, kb, 0, 1, 2);
+            block(n, y, 1, kb, 0, 1, 3);
+            epilogue(1, 1, 3);
+        } else {
+            epilogue(1, 0, 3);
         }
     };
 
-    // Raise tau while the bins at and above tau + 1 still hold k kept scores
-    // (this wave's histogram adds are in LDS order before these reads).
-    auto raise = [&]() {
-        int t = tau, ge = cnt_ge, ht;
+    // Raise tau of row r while the bins at and above tau + 1 still hold k
+    // kept scores (the histogram adds of this wave are in LDS order before
+    // these reads).
+    auto raise = [&](int r) {
+        uint32_t* hr = r ? h[1] : h[0];
+        int t = r ? tau[1] : tau[0];
+        int ge = r ? cnt_ge[1] : cnt_ge[0];
+        int ht;
         for (;;) {
             const int bb = t + lane;
-            const int hv = bb < kPfBins ? (int)h[bb] : 0;
+            const int hv = bb < kPfBins ? (int)hr[bb] : 0;
             int incl = hv;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -441,66 +587,126 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
             }
         }
         // Wave-uniform: keep them in scalar registers.
-        tau = __builtin_amdgcn_readfirstlane(t);
-        cnt_ge = __builtin_amdgcn_readfirstlane(ge);
-        htau = __builtin_amdgcn_readfirstlane(ht);
-        tau_f = pf_lo(tau);
+        t = __builtin_amdgcn_readfirstlane(t);
+        ge = __builtin_amdgcn_readfirstlane(ge);
+        ht = __builtin_amdgcn_readfirstlane(ht);
+        const float tf = pf_lo(t);
+        if (r) {
+            tau[1] = t;
+            cnt_ge[1] = ge;
+            htau[1] = ht;
+            tau_f[1] = tf;
+        } else {
+            tau[0] = t;
+            cnt_ge[0] = ge;
+            htau[0] = ht;
+            tau_f[0] = tf;
+        }
     };
 
     // A pair's scores are settled at the top of the next pair, right after its
-    // stage wait: each lane tests its 2 scores against the row's threshold,
-    // appends the survivors to the row's list (positions from a prefix count
-    // over the wave) and to its histogram, and tau moves when it can.  The
-    // list stores then have two tiles of compute to complete before the next
-    // wait (which counts them too) comes round.
-    int pend_base = -1;
+    // stage wait: each lane completes its 4 scores with the pair's g . k,
+    // tests them against its row's threshold, appends the survivors to the
+    // row's list (positions from a row-local prefix count over the lanes of
+    // the row) and to its histogram, and tau moves when it can.
+    constexpr unsigned long long kRow0 = 0x0000FFFF0000FFFFull;  // lane groups 0 and 2
+    int pend_base = -1, pend_buf = 0;
     auto settle = [&]() __attribute__((always_inline)) {
         if (pend_base < 0) return;
-        const int key0 = pend_base + (g >> 1) * kPfTile + 4 * c + 2 * (g & 1);
-        bool sv[2];
-        int bn[2];
+        const int qs = g & 1;
+        const int key0 = pend_base + (g >> 1) * kPfTile + 4 * c;
+        // g . k of the pair is complete: every wave passed the pair's end
+        // barrier after its LDS stores (slots of tiles past the workgroup's
+        // last key are never written and only meet masked keys).
+        const float4 gv = gk[pend_buf][g >> 1][wid * kPfQpw + qs][c];
+        st[0] += gv.x;
+        st[1] += gv.y;
+        st[2] += gv.z;
+        st[3] += gv.w;
+        const int tqs = qs ? tq[1] : tq[0];
+        const float thr = qs ? tau_f[1] : tau_f[0];
+        const int taus = qs ? tau[1] : tau[0];
+        bool sv[4];
+        int bn[4];
         int n = 0, nt = 0;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            sv[e] = key0 + e <= tq && st[e] >= tau_f;
+        for (int e = 0; e < 4; ++e) {
+            sv[e] = key0 + e <= tqs && st[e] >= thr;
             bn[e] = pf_bin(st[e]);
             n += sv[e];
-            nt += sv[e] && bn[e] == tau;
+            nt += sv[e] && bn[e] == taus;
         }
-        const unsigned long long b0 = __ballot(n & 1), b1 = __ballot(n & 2);
-        int p = cnt + __popcll(b0 & lt) + 2 * __popcll(b1 & lt);
+        const unsigned long long b0 = __ballot(n & 1), b1 = __ballot(n & 2), b2 = __ballot(n & 4);
+        const unsigned long long mrow = qs ? ~kRow0 : kRow0;
+        int p = (qs ? cnt[1] : cnt[0]) + below(b0 & mrow) + 2 * below(b1 & mrow) +
+                4 * below(b2 & mrow);
+        uint2* dst = qs ? sl[1] : sl[0];
+        uint32_t* hq = qs ? h[1] : h[0];
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
+        for (int e = 0; e < 4; ++e) {
             if (sv[e]) {
-                sl[p] = make_uint2((uint32_t)(key0 + e), __float_as_uint(st[e]));
-                lds_add_u32(&h[bn[e]], 1u);
+                dst[p] = make_uint2((uint32_t)(key0 + e), __float_as_uint(st[e]));
+                lds_add_u32(&hq[bn[e]], 1u);
             }
             p += sv[e];
         }
-        const unsigned long long t0 = __ballot(nt & 1), t1 = __ballot(nt & 2);
-        const int tot = __popcll(b0) + 2 * __popcll(b1);
-        cnt += tot;
-        cnt_ge += tot;
-        htau += __popcll(t0) + 2 * __popcll(t1);
-        if (cnt_ge - htau >= a.k) raise();
+        const unsigned long long t0 = __ballot(nt & 1), t1 = __ballot(nt & 2), t2 = __ballot(nt & 4);
+#pragma unroll
+        for (int r = 0; r < kPfQpw; ++r) {
+            const unsigned long long m = r ? ~kRow0 : kRow0;
+            const int tot = __popcll(b0 & m) + 2 * __popcll(b1 & m) + 4 * __popcll(b2 & m);
+            const int tt = __popcll(t0 & m) + 2 * __popcll(t1 & m) + 4 * __popcll(t2 & m);
+            cnt[r] += tot;
+            cnt_ge[r] += tot;
+            htau[r] += tt;
+            if (cnt_ge[r] - htau[r] >= a.k) raise(r);
+        }
         pend_base = -1;
+    };
+
+    // g . k for one group of the pair per wave (group wave % 4 of tile
+    // wave / 4): 4 k-steps x (hi, lo) into one accumulator.  D row 4g+e is
+    // workgroup row 4g+e, column c is key 4c + gi of the tile.
+    auto gk_unit = [&](const uint4* ka, const uint4* kb, int tile, int buf)
+                       __attribute__((always_inline)) {
+        const int j = wid >> 2, gi = wid & 3;
+        if ((tile + j) * kPfTile > tmax) return;
+        const uint4* ktile = j ? kb : ka;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            // One k-step's fragments at a time (12 registers, not 48).
+            asm volatile("" ::: "memory");
+            const uint4 bq = ktile[bbase + gi * 16 + kk * 4];
+            d = mfma16x16x32(gfrag[0][kk][lane], bq, d);
+            d = mfma16x16x32(gfrag[1][kk][lane], bq, d);
+        }
+        float* dst = reinterpret_cast<float*>(&gk[buf][j][0][0]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(4 * g + e) * kPfTile + 4 * c + gi] = d[e];
     };
 
     // One barrier per pair: after it, the pair's data is visible to all and
     // every wave is done with the other pair's stages, which are refilled
-    // right away.
+    // for the pair after next.
     auto pair = [&](const uint4* ka, const uint4* kb, uint4* na, uint4* nb, int tile)
                     __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __builtin_amdgcn_s_barrier();
+        // Settle and the g . k unit read LDS locations the compiler cannot
+        // tell apart from the stage fills, so they run before the fills are
+        // issued (nothing in flight, no wait); the fills still have the
+        // pair's two tiles of compute to land.
+        settle();
+        const int buf = (tile >> 1) & 1;
+        gk_unit(ka, kb, tile, buf);
         issue(na, tile + 2);
         issue(nb, tile + 3);
-        settle();
         const int kbase = tile * kPfTile;
-        if (kbase <= tq) {
-            tile_scores(ka, 0);
-            if (kbase + kPfTile <= tq) tile_scores(kb, 1);
-            pend_base = kbase;  // keys past the row's last legal one are never kept
+        if (kbase <= tw) {
+            pair_scores(ka, kb, kbase + kPfTile <= tw);
+            pend_base = kbase;  // keys past a row's last legal one are never kept
+            pend_buf = buf;
         }
     };
 
@@ -511,26 +717,38 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         if (tile + 2 >= ntiles) break;
         pair(kt2, kt3, kt0, kt1, tile + 2);
     }
+    // The last pair's g . k stores of all waves complete before it is settled.
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
     settle();
 
     // The key stages are free once every wave is past its last tile and the
     // last (clamped) fills have landed: they hold the candidate buffers, four
-    // rows per stage.  Each wave finishes its own row from the survivor list
-    // it wrote.
+    // rows per stage.  Each wave finishes its own rows from the survivor
+    // lists it wrote.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (!act) return;
-    const int need = min(a.k, tq + 1);
-    int32_t* oidx = a.out_idx + rowq * a.out_stride;
-    float* osc = a.out_score ? a.out_score + rowq * a.out_stride : nullptr;
-    for (int u = need + lane; u < a.k; u += 64) {
-        oidx[u] = -1;
-        if (osc) osc[u] = -INFINITY;
+#pragma unroll 1
+    for (int qq = 0; qq < kPfQpw; ++qq) {
+        // One copy of the finish for both rows (selects, not array indexing,
+        // keep the per-row values in registers).
+        const bool aq = qq ? act[1] : act[0];
+        if (!aq) continue;
+        const int tqq = qq ? tq[1] : tq[0];
+        const long long rq = qq ? rowq[1] : rowq[0];
+        const int need = min(a.k, tqq + 1);
+        int32_t* oidx = a.out_idx + rq * a.out_stride;
+        float* osc = a.out_score ? a.out_score + rq * a.out_stride : nullptr;
+        for (int u = need + lane; u < a.k; u += 64) {
+            oidx[u] = -1;
+            if (osc) osc[u] = -INFINITY;
+        }
+        const int r = wid * kPfQpw + qq;
+        const int sq = r >> 2;
+        uint4* stage = sq == 0 ? kt0 : (sq == 1 ? kt1 : (sq == 2 ? kt2 : kt3));
+        unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + (r & 3) * kPfCand;
+        pf_finish(qq ? h[1] : h[0], cb, qq ? sl[1] : sl[0], qq ? cnt[1] : cnt[0], need, oidx, osc);
     }
-    const int sq = wid >> 2;
-    uint4* stage = sq == 0 ? kt0 : (sq == 1 ? kt1 : (sq == 2 ? kt2 : kt3));
-    unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + (wid & 3) * kPfCand;
-    pf_finish(h, cb, sl, cnt, need, oidx, osc);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
