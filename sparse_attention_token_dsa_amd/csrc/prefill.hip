@@ -62,11 +62,11 @@ constexpr int kPfStage = 16 * kPfBlk;   // uint4 per stage (16 blocks, 16.25 KiB
 constexpr int kPfBins = 1024;           // histogram size (bins 947 .. 1023 stay empty)
 constexpr int kPfDigit = 10;            // radix digit of the finish over LDS candidates
 constexpr int kPfWide = 10;             // digit counted in the level-0 pass for crowded bins
-constexpr int kPfCand = 512;            // LDS candidate keys per row: four rows per stage
-constexpr int kPfSweep = 4;             // uint4 per lane per block of the level-0 pass
-static_assert(4 * kPfCand * 8 <= kPfStage * 16, "four rows' candidate buffers fit one stage");
+constexpr int kPfCand = 1024;           // LDS candidate keys of a wave (its rows in turn)
+constexpr int kPfSweep = 8;             // uint4 per lane per block of the level-0 pass
+static_assert(2 * kPfCand * 8 <= kPfStage * 16, "two waves' candidate buffers fit one stage");
 static_assert((1 << kPfDigit) == kPfBins, "digit histograms reuse the row histogram");
-static_assert((1 << kPfWide) * 4 == kPfCand * 8, "the wide digit histogram fills cb");
+static_assert((1 << kPfWide) * 4 <= kPfCand * 8, "the wide digit histogram fits cb");
 static_assert(kPfRows == 16 && kPfWaves == 8, "16 rows: one g tile; 2 blocks per wave fill a stage");
 static_assert(kPfQpw == 2, "the 4 lane groups hold 2 rows x 2 tiles of a pair");
 
@@ -114,6 +114,18 @@ __device__ __forceinline__ int pf_top(int b) {
 __device__ __forceinline__ int below(unsigned long long m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: four row shifts within
+// each 16-lane row, then the row totals carried with the two row broadcasts.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return v;
 }
 
 __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
@@ -177,13 +189,7 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int&
     int local = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) local += (int)h[NB - 1 - (lane * kPer + j)];
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    int cum = incl - local;
+    int cum = wave_incl_scan(local) - local;
     int fd = -1, fg = 0, fe = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -198,9 +204,9 @@ __device__ __forceinline__ void wave_threshold(const uint32_t* h, int need, int&
     }
     const unsigned long long m = __ballot(fd >= 0);
     const int src = m ? __ffsll((long long)m) - 1 : 0;
-    d = __shfl(fd, src);
-    gt = __shfl(fg, src);
-    eq = __shfl(fe, src);
+    d = __builtin_amdgcn_readlane(fd, src);
+    gt = __builtin_amdgcn_readlane(fg, src);
+    eq = __builtin_amdgcn_readlane(fe, src);
 }
 
 // Exact top-`need` of one row by one wave (see the file header): h holds the
@@ -570,19 +576,13 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         for (;;) {
             const int bb = t + lane;
             const int hv = bb < kPfBins ? (int)hr[bb] : 0;
-            int incl = hv;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off);
-                if (lane >= off) incl += y;
-            }
-            const int excl = incl - hv;
+            const int excl = wave_incl_scan(hv) - hv;
             const bool ok = bb < kPfBins && ge - excl >= a.k;
             const int lstar = __popcll(__ballot(ok)) - 1;
             t += lstar;
-            ge -= __shfl(excl, lstar);
+            ge -= __builtin_amdgcn_readlane(excl, lstar);
             if (lstar < 63 || t >= kPfBins - 1) {
-                ht = __shfl(hv, lstar);
+                ht = __builtin_amdgcn_readlane(hv, lstar);
                 break;
             }
         }
@@ -723,9 +723,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     settle();
 
     // The key stages are free once every wave is past its last tile and the
-    // last (clamped) fills have landed: they hold the candidate buffers, four
-    // rows per stage.  Each wave finishes its own rows from the survivor
-    // lists it wrote.
+    // last (clamped) fills have landed: they hold the candidate buffers, one
+    // per wave (two per stage), used by the wave's rows in turn.  Each wave
+    // finishes its own rows from the survivor lists it wrote.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll 1
@@ -743,10 +743,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
-        const int r = wid * kPfQpw + qq;
-        const int sq = r >> 2;
+        const int sq = wid >> 1;
         uint4* stage = sq == 0 ? kt0 : (sq == 1 ? kt1 : (sq == 2 ? kt2 : kt3));
-        unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + (r & 3) * kPfCand;
+        unsigned long long* cb = reinterpret_cast<unsigned long long*>(stage) + (wid & 1) * kPfCand;
         pf_finish(qq ? h[1] : h[0], cb, qq ? sl[1] : sl[0], qq ? cnt[1] : cnt[0], need, oidx, osc);
     }
 }
