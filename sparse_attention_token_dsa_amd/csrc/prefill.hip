@@ -4,11 +4,13 @@
 // MISA, LISA and ResMiSA", section 2.2: score, causal mask and top-k fused
 // into one pass, no n^2 score matrix written back).
 //
-// Layout: a workgroup of 8 waves owns 16 consecutive query rows of one
-// sequence, two rows per wave (their heads and weights held in registers as
-// MFMA A fragments; each B fragment read from LDS feeds both rows, which keeps
-// the LDS read traffic at about half of what the MFMAs can absorb), and sweeps
-// the legal keys [0, max t] in tiles of 64 keys.  Each tile (16 KiB of bf16
+// Layout: a workgroup of 8 waves owns 16 query rows of one sequence, 8
+// consecutive ones near the start of the chunk and 8 near its end (so that
+// the causal work is about the same for every workgroup), two rows per wave
+// (their heads and weights held in registers as MFMA A fragments; each B
+// fragment read from LDS feeds both rows, which keeps the LDS read traffic at
+// about half of what the MFMAs can absorb), and sweeps the legal keys
+// [0, max t] in tiles of 64 keys.  Each tile (16 KiB of bf16
 // keys) is staged once in LDS for all 16 rows by direct global-to-LDS loads,
 // in blocks of 4 keys padded by 16 bytes: the lanes that read one B-fragment
 // chunk (keys 4c + gi, c = 0..15) hit distinct bank groups, and every chunk's
@@ -394,12 +396,18 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     __shared__ uint4 gfrag[2][4][64];
     __shared__ float4 gk[2][2][kPfRows][kPfTile / 4];
 
+    // Rows in groups of 8: workgroup x takes group x (waves 0-3) and group
+    // G-1-x (waves 4-7), a short and a long causal row range.  Waves w and
+    // w + 4 share a SIMD, so once the short rows are done the long ones have
+    // its MFMA pipe to themselves, and every workgroup carries about the same
+    // work.
     const int seq = blockIdx.y;
-    const int i0 = blockIdx.x * kPfRows;
+    const int G = (a.T + 7) >> 3;
+    const int gA = blockIdx.x, gB = G - 1 - blockIdx.x;  // gA <= gB
     const int tid = threadIdx.x;
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tmax = a.offset + min(i0 + kPfRows, a.T) - 1;
+    const int tmax = a.offset + min(gB * 8 + 7, a.T - 1);
     const int ntiles = tmax / kPfTile + 1;
 
     // Per-row state of this wave's two rows (workgroup rows 2 wid + qq).
@@ -413,8 +421,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int qq = 0; qq < kPfQpw; ++qq) {
         const int r = wid * kPfQpw + qq;
-        const int i = i0 + r;
-        act[qq] = i < a.T;
+        const int i = (r < 8 ? gA : gB) * 8 + (r & 7);
+        act[qq] = i < a.T && (r < 8 || gB != gA);
         rowq[qq] = (long long)seq * a.T + min(i, a.T - 1);
         tq[qq] = act[qq] ? a.offset + i : -1;
         tau[qq] = 0;
@@ -753,7 +761,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
     if (a.cap % 2 != 0 || a.cap < (long long)a.offset + a.T) return hipErrorInvalidValue;
     const int batch = rows / a.T;
-    const dim3 grid((unsigned)((a.T + kPfRows - 1) / kPfRows), (unsigned)batch);
+    const dim3 grid((unsigned)(((a.T + 7) / 8 + 1) / 2), (unsigned)batch);
     const int nht = (a.H + 15) / 16;
     prof_begin(K_PREFILL, s);
     switch (nht) {
