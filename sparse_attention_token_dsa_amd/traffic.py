@@ -1,4 +1,5 @@
-"""Measured HBM traffic of the decode scan, from rocprofv3 counters.
+"""Measured HBM traffic of the decode scan and the fused prefill, from
+rocprofv3 counters.
 
 Two counter runs of the same program, then a summary:
 
@@ -9,12 +10,13 @@ Two counter runs of the same program, then a summary:
   python3 -m sparse_attention_token_dsa_amd.traffic summarize OUT
 
 `run` launches the DSA decode selector on the L = 131072, batch-8, 64-head
-workload a few times, then a plain copy kernel (torch's elementwise add of a
-zero into a second 256 MiB fp32 tensor: 256 MiB read, 256 MiB written).
+workload a few times, the fused prefill (T = 4096 over 28672 cached keys,
+k = 2048) twice, then a plain copy kernel (torch's elementwise add of a zero
+into a second 256 MiB fp32 tensor: 256 MiB read, 256 MiB written).
 `summarize` reads both runs, calibrates each counter on the copy kernel
-(counter bytes / known bytes) and writes, per launch of the scan kernel, the
-HBM bytes fetched and written divided by those factors to traffic.json
-(keyed by a digest of the scan's sources, which bench.py checks before it
+(counter bytes / known bytes) and writes, per launch of each measured kernel,
+the HBM bytes fetched and written divided by those factors to traffic.json
+(keyed by a digest of the kernel's sources, which bench.py checks before it
 reports the figure).
 """
 from __future__ import annotations
@@ -31,6 +33,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "traffic.json")
 SCAN_SOURCES = ["scan.hip", "sa_frag.h", "sa_common.h"]
 SCAN_KERNEL = "scan_kernel<4, 4, 4, 4, true, false>"
+PREFILL_SOURCES = ["prefill.hip", "sa_frag.h", "sa_common.h"]
+PREFILL_KERNEL = "prefill_kernel<4>"
 COPY_BYTES = 256 << 20
 COPY_KERNEL = "CUDAFunctorOnSelf_add<float>"  # torch.add(src, 0.0, out=dst)
 
@@ -56,6 +60,13 @@ def run():
     K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
     for _ in range(4):
         api.indexer_score_topk(q, w, K, p["offset"], 2048)
+    torch.cuda.synchronize()
+    pp = synth.make_config("prefill_chunked")
+    q = torch.from_numpy(pp["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(pp["w"]).to(dev)
+    K = torch.from_numpy(pp["K"].view(np.int16)).to(dev)
+    for _ in range(2):
+        api.indexer_score_topk(q, w, K, pp["offset"], 2048)
     torch.cuda.synchronize()
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -86,32 +97,34 @@ def _pick(d, needle):
 def summarize(out_dir):
     fetch = _per_dispatch(os.path.join(out_dir, "fetch"), "FETCH_SIZE")
     write = _per_dispatch(os.path.join(out_dir, "write"), "WRITE_SIZE")
-    scan_f, scan_w = _pick(fetch, SCAN_KERNEL), _pick(write, SCAN_KERNEL)
     copy_f, copy_w = _pick(fetch, COPY_KERNEL), _pick(write, COPY_KERNEL)
     f_fetch = copy_f * 1024.0 / COPY_BYTES
     f_write = copy_w * 1024.0 / COPY_BYTES
-    rec = {
-        "kernel": "scan_dsa",
-        "source_digest": source_digest(),
-        "fetch_kib_per_launch": scan_f,
-        "write_kib_per_launch": scan_w,
-        "copy_kernel_bytes_each_way": COPY_BYTES,
-        "copy_fetch_kib": copy_f,
-        "copy_write_kib": copy_w,
-        "factor_fetch": f_fetch,
-        "factor_write": f_write,
-        "bytes_per_launch": scan_f * 1024.0 / f_fetch + scan_w * 1024.0 / f_write,
-    }
     try:
         with open(TRAFFIC_FILE) as f:
             allrec = json.load(f)
     except (OSError, ValueError):
         allrec = {}
-    allrec["scan_dsa"] = rec
+    for name, needle, sources in (("scan_dsa", SCAN_KERNEL, SCAN_SOURCES),
+                                  ("prefill_fused", PREFILL_KERNEL, PREFILL_SOURCES)):
+        kf, kw = _pick(fetch, needle), _pick(write, needle)
+        rec = {
+            "kernel": name,
+            "source_digest": source_digest(sources),
+            "fetch_kib_per_launch": kf,
+            "write_kib_per_launch": kw,
+            "copy_kernel_bytes_each_way": COPY_BYTES,
+            "copy_fetch_kib": copy_f,
+            "copy_write_kib": copy_w,
+            "factor_fetch": f_fetch,
+            "factor_write": f_write,
+            "bytes_per_launch": kf * 1024.0 / f_fetch + kw * 1024.0 / f_write,
+        }
+        allrec[name] = rec
+        print(json.dumps(rec, indent=1))
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(allrec, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps(rec, indent=1))
 
 
 if __name__ == "__main__":
