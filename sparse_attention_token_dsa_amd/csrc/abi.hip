@@ -166,7 +166,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.offset = s->causal_offset;
     a.len_div = 1;
     a.len_cap = s->L;
-    a.chunk = sa::scan_chunk(4);
+    a.chunk = sa::scan_chunk(4, rows, s->L);
     a.scores = scores;
     a.score_stride = score_stride(s->L);
     a.state = state;
@@ -575,7 +575,7 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
     a.offset = s->causal_offset;
     a.len_div = block_b;
     a.len_cap = nblk;
-    a.chunk = sa::scan_chunk(8);
+    a.chunk = sa::scan_chunk(8, rows, nblk);
     a.scores = p.bscores;
     a.score_stride = nblk;
     e = sa::launch_scan(a, rows, (s->H + 15) / 16, 8, false, st);

@@ -16,7 +16,7 @@ __device__ __forceinline__ void block_sum_partial(const uint16_t* kseq, int lo, 
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll 4
     for (int s = lo + kl; s < hi; s += 16) {
-        const uint4 v = ldg16(kseq + (long long)s * kD + c16 * 8);
+        const uint4 v = ldg16_stream(kseq + (long long)s * kD + c16 * 8);
         const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {

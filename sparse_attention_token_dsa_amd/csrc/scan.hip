@@ -15,16 +15,16 @@ namespace sa {
 // ------------------------------------------------------------ scan
 
 // One workgroup = 4 waves scans keys [cs, ce) of one query row (ce - cs <=
-// 4*G*16*NSTEP).  Each wave takes G*16 consecutive keys per step and the
-// workgroup advances 4*G*16 keys per step; the next step's key loads are in
-// flight while the current step is computed (two register buffers).  Scores
-// are staged in LDS and written out coalesced at the end, so the loop issues
-// no global stores.
+// kScanMaxChunk).  Each wave takes G*16 consecutive keys per step and the
+// workgroup advances 4*G*16 keys per step; NBUF register buffers rotate, so
+// the key loads of the next NBUF - 1 steps are in flight while one step is
+// computed.  Scores are staged in LDS and written out coalesced at the end,
+// so the loop issues no global stores.
 //
 // With a row state (HIST), the scores' first radix digit is histogrammed in
 // LDS and added to the row's global histogram for the top-k filter, which
 // runs after this kernel and so sees every workgroup's counts.
-template <int NHT, int KSTEPS, int G, int NSTEP, bool HIST, bool ROUTED>
+template <int NHT, int KSTEPS, int G, int NBUF, int NSTEP, bool HIST, bool ROUTED>
 __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     constexpr int KROW = KSTEPS * 32;
     constexpr int WKEYS = G * 16;
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int s = min(base + gi * 16 + 4 * j + (lane >> 4), ce - 1);
-                    buf[gi][j] = ldg16(kseq + (long long)s * kD + (lane & 15) * 8);
+                    buf[gi][j] = ldg16_stream(kseq + (long long)s * kD + (lane & 15) * 8);
                 }
             } else {
                 const int s = min(base + gi * 16 + c, ce - 1);
@@ -111,19 +111,32 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
         }
     };
 
-    // NSTEP steps per wave, fully unrolled and unconditional: steps past
-    // the end re-read the last key and store nothing, which keeps every load
-    // at its place in the pipeline (the compiler does not sink loads into
-    // guarded computes and its waits stay exact).
+    // Loads are unconditional: past the end they re-read the last key, so
+    // every load keeps its place in the pipeline and the compiler's waits
+    // stay exact.  With NSTEP > 0 (full chunks) the loop is unrolled
+    // completely and every step is computed (past the end nothing is
+    // stored); otherwise steps past the end (at most NBUF - 1) are skipped.
     const int base = cs + wid * WKEYS;
-    uint4 bufA[G][KSTEPS], bufB[G][KSTEPS];
-    loadG(bufA, base);
+    uint4 buf[NBUF][G][KSTEPS];
 #pragma unroll
-    for (int it = 0; it < NSTEP; it += 2) {
-        if (it + 1 < NSTEP) loadG(bufB, base + (it + 1) * STEP);
-        computeG(bufA, base + it * STEP);
-        if (it + 2 < NSTEP) loadG(bufA, base + (it + 2) * STEP);
-        if (it + 1 < NSTEP) computeG(bufB, base + (it + 1) * STEP);
+    for (int u = 0; u < NBUF - 1; ++u) loadG(buf[u], base + u * STEP);
+    if constexpr (NSTEP > 0) {
+#pragma unroll
+        for (int it = 0; it < NSTEP; ++it) {
+            if (it + NBUF - 1 < NSTEP)
+                loadG(buf[(it + NBUF - 1) % NBUF], base + (it + NBUF - 1) * STEP);
+            computeG(buf[it % NBUF], base + it * STEP);
+        }
+    } else {
+        const int nsteps = (ce - cs + STEP - 1) / STEP;
+#pragma unroll 4
+        for (int it0 = 0; it0 < nsteps; it0 += NBUF) {
+#pragma unroll
+            for (int u = 0; u < NBUF; ++u) {
+                loadG(buf[(u + NBUF - 1) % NBUF], base + (it0 + u + NBUF - 1) * STEP);
+                if (it0 + u < nsteps) computeG(buf[u], base + (it0 + u) * STEP);
+            }
+        }
     }
     __syncthreads();
     float* srow = a.scores + (long long)row * a.score_stride;
@@ -334,34 +347,68 @@ hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s) 
     return hipGetLastError();
 }
 
-// Keys (KSTEPS = 4): 4 groups x 4 steps per wave, 1024 keys per workgroup.
+// Keys (KSTEPS = 4): one 16-key group per wave and step, 4 register buffers
+// (three steps of loads in flight), nontemporal loads, and about one
+// workgroup per CU: long contiguous streams per workgroup read fastest (the
+// L = 131072, batch-8 scan takes 45.7 us right after a cache flush with 4096
+// keys per workgroup, 55.5 us with 1024 keys and 4 groups x 2 buffers).
 // Block representatives (KSTEPS = 8, a few thousand per row at most): 2
-// groups x 1 step, 128 per workgroup, so the grid still covers the chip.
+// groups, one step of 128 per workgroup, so the grid still covers the chip.
 template <int KS>
-constexpr int scan_groups() { return KS == 4 ? 4 : 2; }
+constexpr int scan_groups() { return KS == 4 ? 1 : 2; }
 template <int KS>
-constexpr int scan_steps() { return KS == 4 ? 4 : 1; }
+constexpr int scan_bufs() { return KS == 4 ? 4 : 1; }
 
-template <int NHT, int KS>
+template <int NHT, int KS, int NSTEP>
 static void scan_dispatch_hist(const ScanArgs& a, dim3 grid, hipStream_t s) {
     constexpr int G = scan_groups<KS>();
-    constexpr int NS = scan_steps<KS>();
+    constexpr int NB = scan_bufs<KS>();
     if (a.heads) {
         if (a.state)
-            scan_kernel<NHT, KS, G, NS, true, true><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, true, true><<<grid, dim3(256), 0, s>>>(a);
         else
-            scan_kernel<NHT, KS, G, NS, false, true><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, false, true><<<grid, dim3(256), 0, s>>>(a);
     } else {
         if (a.state)
-            scan_kernel<NHT, KS, G, NS, true, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, true, false><<<grid, dim3(256), 0, s>>>(a);
         else
-            scan_kernel<NHT, KS, G, NS, false, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, false, false><<<grid, dim3(256), 0, s>>>(a);
     }
 }
 
-int scan_chunk(int ksteps) {
-    return ksteps == 4 ? 4 * 16 * scan_groups<4>() * scan_steps<4>()
-                       : 4 * 16 * scan_groups<8>() * scan_steps<8>();
+// Full chunks of keys take the completely unrolled loop (about 2% faster).
+template <int NHT>
+static void scan_dispatch_keys(const ScanArgs& a, dim3 grid, hipStream_t s) {
+    constexpr int kFull = kScanMaxChunk / (4 * 16 * scan_groups<4>());
+    if (a.chunk == kScanMaxChunk)
+        scan_dispatch_hist<NHT, 4, kFull>(a, grid, s);
+    else
+        scan_dispatch_hist<NHT, 4, 0>(a, grid, s);
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int scan_chunk(int ksteps, long long rows, int maxn) {
+    if (ksteps != 4) return 4 * 16 * scan_groups<8>();
+    constexpr int step = 4 * 16 * scan_groups<4>();
+    const long long wgs = cu_count();
+    long long c = (rows * (long long)maxn + wgs - 1) / wgs;
+    c = (c + step - 1) / step * step;
+    c = c < (long long)step * scan_bufs<4>() ? (long long)step * scan_bufs<4>() : c;
+    c = c > kScanMaxChunk ? kScanMaxChunk : c;
+    return (int)c;
 }
 
 hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,
@@ -372,17 +419,17 @@ hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool ro
     prof_begin(kid, s);
     if (ksteps == 4) {
         switch (nht) {
-            case 1: scan_dispatch_hist<1, 4>(a, grid, s); break;
-            case 2: scan_dispatch_hist<2, 4>(a, grid, s); break;
-            case 3: scan_dispatch_hist<3, 4>(a, grid, s); break;
-            default: scan_dispatch_hist<4, 4>(a, grid, s); break;
+            case 1: scan_dispatch_keys<1>(a, grid, s); break;
+            case 2: scan_dispatch_keys<2>(a, grid, s); break;
+            case 3: scan_dispatch_keys<3>(a, grid, s); break;
+            default: scan_dispatch_keys<4>(a, grid, s); break;
         }
     } else {
         switch (nht) {
-            case 1: scan_dispatch_hist<1, 8>(a, grid, s); break;
-            case 2: scan_dispatch_hist<2, 8>(a, grid, s); break;
-            case 3: scan_dispatch_hist<3, 8>(a, grid, s); break;
-            default: scan_dispatch_hist<4, 8>(a, grid, s); break;
+            case 1: scan_dispatch_hist<1, 8, 1>(a, grid, s); break;
+            case 2: scan_dispatch_hist<2, 8, 1>(a, grid, s); break;
+            case 3: scan_dispatch_hist<3, 8, 1>(a, grid, s); break;
+            default: scan_dispatch_hist<4, 8, 1>(a, grid, s); break;
         }
     }
     prof_end(kid, s);
