@@ -32,7 +32,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "traffic.json")
 SCAN_SOURCES = ["scan.hip", "sa_frag.h", "sa_common.h"]
-SCAN_KERNEL = "scan_kernel<4, 4, 4, 4, true, false>"
+SCAN_KERNEL = "scan_kernel<4, 4, 1, 4, 64, true, false>"
 PREFILL_SOURCES = ["prefill.hip", "sa_frag.h", "sa_common.h"]
 PREFILL_KERNEL = "prefill_kernel<4>"
 COPY_BYTES = 256 << 20
