@@ -78,6 +78,23 @@ def test_dsa_prefill_path(api, Bt, T, L, offset, H, k):
     check_dsa(p, k, idx, sc, rows_of(p))
 
 
+def test_dsa_decode_winners_packed_in_few_chunks(api):
+    # Every winner sits in one 600-key stretch of each row, i.e. in the
+    # slices of a few scan and filter workgroups; the top-k must still be the
+    # exact one.
+    say("dsa packed winners")
+    p = synth.make_problem(7, Bt=2, T=1, L=20000, H=64)
+    rng = np.random.default_rng(7)
+    for b in range(2):
+        j = int(np.argmax(p["w"][b, 0]))
+        qj = synth.bf16_bits_to_f32(p["q"][b, 0, j])
+        noise = rng.standard_normal((600, 128)).astype(np.float32) * np.float32(0.3 / np.sqrt(128))
+        p["K"][b, 5000:5600] = synth.to_bf16_bits(qj[None, :] * np.float32(4.0) + noise)
+    idx, sc = run_dsa(api, p, 512)
+    check_dsa(p, 512, idx, sc, rows_of(p))
+    assert np.all((idx[:, 0] >= 5000) & (idx[:, 0] < 5600)), "winners outside the packed stretch"
+
+
 def test_dsa_all_equal_keys_take_lowest_positions(api):
     say("dsa ties")
     p = synth.make_problem(5, Bt=1, T=1, L=2000, H=64)
