@@ -53,7 +53,14 @@ def _load():
         _lib.oracle_misa.argtypes = [P, i, i, i, i, P, i, P, P, P, P, P, P, P, P, i]
         _lib.oracle_hisa.argtypes = [P, i, i, i, P, i, P, P, P, P, P, i]
         _lib.oracle_pool.argtypes = [P, i, i, i, i, P]
-        for f in (_lib.oracle_dsa, _lib.oracle_misa, _lib.oracle_hisa, _lib.oracle_pool):
+        _lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_long, i, P, P]
+        _lib.oracle_dsa_fp8.argtypes = [P, P, P, i, P, i, P, P, P, i]
+        _lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
+        _lib.oracle_fp8_e4m3_decode.restype = ctypes.c_double
+        _lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
+        _lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
+        for f in (_lib.oracle_dsa, _lib.oracle_misa, _lib.oracle_hisa, _lib.oracle_pool,
+                  _lib.oracle_quantize_keys_fp8, _lib.oracle_dsa_fp8):
             f.restype = ctypes.c_int
     return _lib
 
@@ -168,3 +175,51 @@ def pool(K, block: int):
     out = np.empty((Bt, nb, d), np.float64)
     _check(lib.oracle_pool(_ptr(K), Bt, L, d, block, _ptr(out)), "oracle_pool")
     return out
+
+
+def fp8_decode(codes):
+    """OCP E4M3 values (float64) of uint8 codes (any shape)."""
+    lib = _load()
+    c = np.asarray(codes, np.uint8)
+    table = np.array([lib.oracle_fp8_e4m3_decode(v) for v in range(256)], np.float64)
+    return table[c]
+
+
+def fp8_encode(x):
+    """Nearest OCP E4M3 codes (ties to even, saturating) of float32 values."""
+    lib = _load()
+    x = np.asarray(x, np.float32)
+    return np.array([lib.oracle_fp8_e4m3_encode(float(v)) for v in x.ravel()],
+                    np.uint8).reshape(x.shape)
+
+
+def quantize_keys_fp8(K):
+    """Per-key FP8 quantization of K [..., L, d] (bf16 bits) -> (codes uint8
+    [..., L, d], scales float32 [..., L])."""
+    lib = _load()
+    K = np.ascontiguousarray(K, np.uint16)
+    d = K.shape[-1]
+    n = K.size // d
+    codes = np.empty(K.shape, np.uint8)
+    scales = np.empty(K.shape[:-1], np.float32)
+    _check(lib.oracle_quantize_keys_fp8(_ptr(K), n, d, _ptr(codes), _ptr(scales)),
+           "oracle_quantize_keys_fp8")
+    return codes, scales
+
+
+def dsa_fp8(prob: Problem, codes, scales, topk: int, rows=None, want_rowscore=False,
+            nthreads=0):
+    """DSA on FP8 keys (codes [Bt, L, d], scales [Bt, L]); prob.K is not used.
+    Returns (idx, score[, rowscore])."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    assert codes.shape == (prob.Bt, prob.L, prob.d) and scales.shape == (prob.Bt, prob.L)
+    r, n = prob.rows(rows)
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    rs = np.empty((n, prob.L), np.float64) if want_rowscore else None
+    _check(lib.oracle_dsa_fp8(ctypes.byref(prob._c), _ptr(codes), _ptr(scales), topk, _ptr(r),
+                              n, _ptr(idx), _ptr(sc), _ptr(rs), _threads(nthreads)),
+           "oracle_dsa_fp8")
+    return (idx, sc, rs) if want_rowscore else (idx, sc)

@@ -23,6 +23,12 @@
  *  [BLOG] "The new bottleneck of sparse attention: from DSA to indexer
  *         acceleration and KV offload", sections "Route 1: HISA" and
  *         "Route 2: MISA".
+ *  [PT] section 2.3, "from the formula to the FP8 cache": indexer keys are
+ *         quantized in blocks to FP8 with one scale per block; the query
+ *         stays at the compute precision; the key error bound and the 2E < m
+ *         set-stability condition.  The FP8 format is OCP E4M3 (sign, 4
+ *         exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the
+ *         subnormals m * 2^-9; 0x7F / 0xFF are NaN; largest finite 448).
  *
  * Readings where the pages are silent (each listed in the design notes):
  *  - causal legality is s <= t, t = causal_offset + row;
@@ -517,6 +523,125 @@ int oracle_hisa(const oracle_problem* p, int topk, int b, int r, const int32_t* 
     if (!rows) nrows = p->Bt * p->T;
     hisa_ctx c = {p, topk, b, r, rows, override_blocks, out_blocks, out_J, out_idx, out_score};
     return run_rows(hisa_row, &c, nrows, nthreads);
+}
+
+/* ---------------------------------------------------------------- FP8 */
+
+/* Value of an OCP E4M3 code. */
+double oracle_fp8_e4m3_decode(uint8_t c)
+{
+    double sign = (c & 0x80) ? -1.0 : 1.0;
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) return sign * ldexp((double)m, -9);
+    return sign * ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/* Nearest E4M3 code to x: round to nearest, ties to the even code (mantissa
+ * bit 0 clear), magnitudes above 448 saturate to 448; the sign is kept
+ * (a value that rounds to zero keeps it, -0 -> 0x80).  Plain search over the
+ * 127 finite magnitudes. */
+uint8_t oracle_fp8_e4m3_encode(float x)
+{
+    double a = fabs((double)x);
+    uint8_t s = signbit(x) ? 0x80 : 0x00;
+    int best = 0;
+    double bd = a;  /* distance to code 0 */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(oracle_fp8_e4m3_decode((uint8_t)c) - a);
+        if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+            bd = d;
+            best = c;
+        }
+    }
+    if (a >= 448.0) best = 0x7E;
+    return (uint8_t)(s | best);
+}
+
+/* [PT] section 2.3: one scale per key (the block is the key's d = 128
+ * values): a = max_x |k_x| / 448 in fp32 (1 for an all-zero key), codes
+ * c_x = E4M3(k_x / a) with the division in fp32. */
+int oracle_quantize_keys_fp8(const uint16_t* K, long n_keys, int d, uint8_t* codes,
+                             float* scales)
+{
+    if (!K || !codes || !scales || n_keys < 0 || d < 1) return ORACLE_EINVAL;
+    for (long s = 0; s < n_keys; ++s) {
+        const uint16_t* k = K + (size_t)s * d;
+        float amax = 0.0f;
+        for (int x = 0; x < d; ++x) {
+            float v = (float)fabs(bf16_to_f64(k[x]));
+            if (v > amax) amax = v;
+        }
+        float a = amax > 0.0f ? amax / 448.0f : 1.0f;
+        scales[s] = a;
+        for (int x = 0; x < d; ++x) {
+            float v = (float)bf16_to_f64(k[x]) / a;
+            codes[(size_t)s * d + x] = oracle_fp8_e4m3_encode(v);
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    const oracle_problem* p;
+    const uint8_t* codes;
+    const float* scales;
+    int topk;
+    const int32_t* rows;
+    int32_t* out_idx;
+    double* out_score;
+    double* out_rowscore;
+} dsa8_ctx;
+
+/* DSA (as dsa_row) on the dequantized keys a_s * decode(c_s), exact in fp64. */
+static int dsa8_row(void* vctx, int r)
+{
+    dsa8_ctx* c = (dsa8_ctx*)vctx;
+    const oracle_problem* p = c->p;
+    int row = c->rows ? c->rows[r] : r;
+    int t = t_of(p, row);
+    int n = t + 1;
+    int b = row / p->T;
+    const uint16_t* qrow = qrow_of(p, row);
+    const float* wrow = wrow_of(p, row);
+    scored_t* cand = (scored_t*)malloc(sizeof(scored_t) * (size_t)n);
+    double* key = (double*)malloc(sizeof(double) * (size_t)p->d);
+    if (!cand || !key) {
+        free(cand);
+        free(key);
+        return ORACLE_ENOMEM;
+    }
+    double* rs = c->out_rowscore ? c->out_rowscore + (size_t)r * p->L : NULL;
+    for (int s = 0; s < n; ++s) {
+        size_t ks = (size_t)b * p->L + s;
+        for (int x = 0; x < p->d; ++x)
+            key[x] = (double)c->scales[ks] * oracle_fp8_e4m3_decode(c->codes[ks * p->d + x]);
+        cand[s].score = indexer_score(qrow, wrow, key, p->H, p->d, NULL, 0);
+        cand[s].idx = s;
+        if (rs) rs[s] = cand[s].score;
+    }
+    if (rs)
+        for (int s = n; s < p->L; ++s) rs[s] = NAN;
+    int kept = select_top(cand, n, c->topk);
+    write_topk(cand, kept, c->topk, c->out_idx + (size_t)r * c->topk,
+               c->out_score + (size_t)r * c->topk);
+    free(cand);
+    free(key);
+    return 0;
+}
+
+int oracle_dsa_fp8(const oracle_problem* p, const uint8_t* codes, const float* scales, int topk,
+                   const int32_t* rows, int nrows, int32_t* out_idx, double* out_score,
+                   double* out_rowscore, int nthreads)
+{
+    if (!p || !p->q || !p->w || !codes || !scales) return ORACLE_EINVAL;
+    if (p->Bt < 1 || p->T < 1 || p->H < 1 || p->d < 1 || p->L < 1) return ORACLE_EINVAL;
+    if (p->causal_offset < 0 || (long)p->causal_offset + p->T > p->L) return ORACLE_EINVAL;
+    if (topk < 1 || !out_idx || !out_score) return ORACLE_EINVAL;
+    if (!rows) nrows = p->Bt * p->T;
+    dsa8_ctx c = {p, codes, scales, topk, rows, out_idx, out_score, out_rowscore};
+    return run_rows(dsa8_row, &c, nrows, nthreads);
 }
 
 /* --------------------------------------------------------------- pool */

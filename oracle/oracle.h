@@ -60,6 +60,21 @@ int oracle_hisa(const oracle_problem* p, int topk, int b, int r, const int32_t* 
  * out [Bt, ceil(L/block), d]. */
 int oracle_pool(const uint16_t* K, int Bt, int L, int d, int block, double* out);
 
+/* OCP E4M3: value of a code; nearest code (ties to even, saturating at 448). */
+double oracle_fp8_e4m3_decode(uint8_t c);
+uint8_t oracle_fp8_e4m3_encode(float x);
+
+/* Per-key FP8 quantization of n_keys bf16 keys of d values: scales [n_keys]
+ * (max |k| / 448 in fp32, 1 for all-zero keys), codes [n_keys, d]. */
+int oracle_quantize_keys_fp8(const uint16_t* K, long n_keys, int d, uint8_t* codes,
+                             float* scales);
+
+/* DSA on FP8 keys (codes [Bt, L, d], scales [Bt, L]); p->K is not used.
+ * Scores are sum_j w_j max(q_j . (a_s decode(c_s)), 0) in fp64. */
+int oracle_dsa_fp8(const oracle_problem* p, const uint8_t* codes, const float* scales, int topk,
+                   const int32_t* rows, int nrows, int32_t* out_idx, double* out_score,
+                   double* out_rowscore, int nthreads);
+
 #ifdef __cplusplus
 }
 #endif
