@@ -86,6 +86,36 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------- FP8 keys */
+
+/* FP8 key cache (PaperTrace section 2.3, "from the formula to the FP8
+ * cache": indexer keys are quantized in blocks to FP8 with one scale per
+ * block; the query stays at the compute precision).  The block is one key
+ * (its d = 128 values):
+ *   scales[s] = max_x |k_{s,x}| / 448 in fp32 (1 for an all-zero key),
+ *   codes[s, x] = OCP E4M3 code nearest to k_{s,x} / scales[s] (fp32
+ *                 division; ties to the even code; |.| > 448 saturates).
+ * keys: [batch, L, d] bf16 bit patterns (device); codes: [batch, L, d]
+ * bytes; scales: [batch, L] fp32 (device, caller-owned).  d must be 128.
+ * Errors: SA_EINVAL (NULL pointer, batch or L < 1), SA_EUNSUPPORTED
+ * (d != 128), SA_EHIP. */
+int sa_quantize_keys_fp8(const uint16_t* keys, int32_t batch, int32_t L, int32_t d,
+                         uint8_t* codes, float* scales, void* stream);
+
+/* Workspace bytes for indexer_score_topk_fp8 on this shape. */
+int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes);
+
+/* DSA lightning indexer on an FP8 key cache (codes and scales as written by
+ * sa_quantize_keys_fp8): the scores are those of the dequantized keys,
+ *   I = sum_j w_j * ReLU(q_j . (scales[s] * e4m3(codes[s]))),
+ * and the selection is as in indexer_score_topk.  The key stream is 132
+ * bytes per key instead of 256.  Decode-style rows only: T must be < 16
+ * (SA_EUNSUPPORTED otherwise).  Other arguments, ownership and errors as in
+ * indexer_score_topk. */
+int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
+                           const float* scales, const sa_shape* s, int32_t* out_idx,
+                           float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* ----------------------------------------------------------- pooling */
 
 /* Block means of the keys, the cache-side state MISA (B = 1024) and HISA

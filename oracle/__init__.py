@@ -53,7 +53,7 @@ def _load():
         _lib.oracle_misa.argtypes = [P, i, i, i, i, P, i, P, P, P, P, P, P, P, P, i]
         _lib.oracle_hisa.argtypes = [P, i, i, i, P, i, P, P, P, P, P, i]
         _lib.oracle_pool.argtypes = [P, i, i, i, i, P]
-        _lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_long, i, P, P]
+        _lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_long, i, P, P, i]
         _lib.oracle_dsa_fp8.argtypes = [P, P, P, i, P, i, P, P, P, i]
         _lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
         _lib.oracle_fp8_e4m3_decode.restype = ctypes.c_double
@@ -193,7 +193,7 @@ def fp8_encode(x):
                     np.uint8).reshape(x.shape)
 
 
-def quantize_keys_fp8(K):
+def quantize_keys_fp8(K, nthreads=0):
     """Per-key FP8 quantization of K [..., L, d] (bf16 bits) -> (codes uint8
     [..., L, d], scales float32 [..., L])."""
     lib = _load()
@@ -202,7 +202,8 @@ def quantize_keys_fp8(K):
     n = K.size // d
     codes = np.empty(K.shape, np.uint8)
     scales = np.empty(K.shape[:-1], np.float32)
-    _check(lib.oracle_quantize_keys_fp8(_ptr(K), n, d, _ptr(codes), _ptr(scales)),
+    _check(lib.oracle_quantize_keys_fp8(_ptr(K), n, d, _ptr(codes), _ptr(scales),
+                                        _threads(nthreads)),
            "oracle_quantize_keys_fp8")
     return codes, scales
 

@@ -562,25 +562,50 @@ uint8_t oracle_fp8_e4m3_encode(float x)
 /* [PT] section 2.3: one scale per key (the block is the key's d = 128
  * values): a = max_x |k_x| / 448 in fp32 (1 for an all-zero key), codes
  * c_x = E4M3(k_x / a) with the division in fp32. */
+static void quantize_one_key(const uint16_t* k, int d, uint8_t* codes, float* scale)
+{
+    float amax = 0.0f;
+    for (int x = 0; x < d; ++x) {
+        float v = (float)fabs(bf16_to_f64(k[x]));
+        if (v > amax) amax = v;
+    }
+    float a = amax > 0.0f ? amax / 448.0f : 1.0f;
+    *scale = a;
+    for (int x = 0; x < d; ++x) {
+        float v = (float)bf16_to_f64(k[x]) / a;
+        codes[x] = oracle_fp8_e4m3_encode(v);
+    }
+}
+
+typedef struct {
+    const uint16_t* K;
+    long n_keys;
+    int d;
+    uint8_t* codes;
+    float* scales;
+} quant_ctx;
+
+enum { QUANT_KEYS_PER_TASK = 1024 };
+
+static int quant_task(void* vctx, int r)
+{
+    const quant_ctx* c = (const quant_ctx*)vctx;
+    long lo = (long)r * QUANT_KEYS_PER_TASK;
+    long hi = lo + QUANT_KEYS_PER_TASK < c->n_keys ? lo + QUANT_KEYS_PER_TASK : c->n_keys;
+    for (long s = lo; s < hi; ++s)
+        quantize_one_key(c->K + (size_t)s * c->d, c->d, c->codes + (size_t)s * c->d,
+                         c->scales + s);
+    return 0;
+}
+
 int oracle_quantize_keys_fp8(const uint16_t* K, long n_keys, int d, uint8_t* codes,
-                             float* scales)
+                             float* scales, int nthreads)
 {
     if (!K || !codes || !scales || n_keys < 0 || d < 1) return ORACLE_EINVAL;
-    for (long s = 0; s < n_keys; ++s) {
-        const uint16_t* k = K + (size_t)s * d;
-        float amax = 0.0f;
-        for (int x = 0; x < d; ++x) {
-            float v = (float)fabs(bf16_to_f64(k[x]));
-            if (v > amax) amax = v;
-        }
-        float a = amax > 0.0f ? amax / 448.0f : 1.0f;
-        scales[s] = a;
-        for (int x = 0; x < d; ++x) {
-            float v = (float)bf16_to_f64(k[x]) / a;
-            codes[(size_t)s * d + x] = oracle_fp8_e4m3_encode(v);
-        }
-    }
-    return 0;
+    quant_ctx c = {K, n_keys, d, codes, scales};
+    long ntask = (n_keys + QUANT_KEYS_PER_TASK - 1) / QUANT_KEYS_PER_TASK;
+    if (ntask > 0x7fffffffL) return ORACLE_EINVAL;
+    return run_rows(quant_task, &c, (int)ntask, nthreads);
 }
 
 typedef struct {

@@ -67,7 +67,7 @@ uint8_t oracle_fp8_e4m3_encode(float x);
 /* Per-key FP8 quantization of n_keys bf16 keys of d values: scales [n_keys]
  * (max |k| / 448 in fp32, 1 for all-zero keys), codes [n_keys, d]. */
 int oracle_quantize_keys_fp8(const uint16_t* K, long n_keys, int d, uint8_t* codes,
-                             float* scales);
+                             float* scales, int nthreads);
 
 /* DSA on FP8 keys (codes [Bt, L, d], scales [Bt, L]); p->K is not used.
  * Scores are sum_j w_j max(q_j . (a_s decode(c_s)), 0) in fp64. */

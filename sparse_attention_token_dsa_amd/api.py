@@ -32,7 +32,8 @@ EXPORTS = (
     "indexer_score_topk_ws", "indexer_score_topk", "sa_pool_blocks", "sa_pool_blocks2",
     "misa_route_ws", "misa_route", "hisa_coarse_fine_ws", "hisa_coarse_fine",
     "sa_last_error", "sa_profile_enable", "sa_profile_read", "sa_kernel_count",
-    "sa_kernel_name",
+    "sa_kernel_name", "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws",
+    "indexer_score_topk_fp8",
 )
 
 
@@ -68,6 +69,9 @@ def load():
     lib.misa_route.argtypes = [P, P, P, SP, I, I, I, P, P, P, P, P, P, S, P]
     lib.hisa_coarse_fine_ws.argtypes = [SP, I, I, I, ctypes.POINTER(S)]
     lib.hisa_coarse_fine.argtypes = [P, P, P, SP, I, I, P, P, P, P, P, S, P]
+    lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
+    lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
+    lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
     lib.sa_last_error.restype = ctypes.c_char_p
     lib.sa_profile_enable.argtypes = [I]
     lib.sa_profile_read.argtypes = [I, ctypes.POINTER(ctypes.c_double),
@@ -77,7 +81,8 @@ def load():
     lib.sa_kernel_name.restype = ctypes.c_char_p
     for name in ("indexer_score_topk_ws", "indexer_score_topk", "sa_pool_blocks",
                  "sa_pool_blocks2", "misa_route_ws", "misa_route", "hisa_coarse_fine_ws",
-                 "hisa_coarse_fine", "sa_profile_enable", "sa_profile_read"):
+                 "hisa_coarse_fine", "sa_profile_enable", "sa_profile_read",
+                 "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws", "indexer_score_topk_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -229,6 +234,61 @@ def hisa_coarse_fine(q, w, keys, causal_offset, topk, block_b, r, reps=None,
                                    int(r), _p(reps), _p(blocks), _p(out_idx), _p(out_score),
                                    _p(ws), ws.numel(), _stream(q.device)), "hisa_coarse_fine")
     return out_idx, out_score, blocks
+
+
+# ------------------------------------------------------------- FP8 keys
+
+def quantize_keys_fp8(keys, out_codes=None, out_scales=None):
+    """Per-key E4M3 codes and fp32 scales: codes uint8 [batch, L, 128],
+    scales fp32 [batch, L] with key = scale * decode(codes)."""
+    _bf16(keys, "keys", 3)
+    B, L, d = keys.shape
+    if out_codes is None:
+        out_codes = torch.empty((B, L, d), dtype=torch.uint8, device=keys.device)
+    if out_scales is None:
+        out_scales = torch.empty((B, L), dtype=torch.float32, device=keys.device)
+    _check(load().sa_quantize_keys_fp8(_p(keys), B, L, d, _p(out_codes), _p(out_scales),
+                                       _stream(keys.device)), "sa_quantize_keys_fp8")
+    return out_codes, out_scales
+
+
+def _fp8_shape(q, w, codes, scales, causal_offset, topk):
+    _bf16(q, "q", 4)
+    if codes.dtype != torch.uint8 or codes.dim() != 3 or not codes.is_cuda \
+            or not codes.is_contiguous():
+        raise TypeError("codes must be a contiguous uint8 [batch, L, 128] GPU tensor")
+    if scales.dtype != torch.float32 or not scales.is_cuda or not scales.is_contiguous():
+        raise TypeError("scales must be a contiguous float32 GPU tensor")
+    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
+        raise TypeError("w must be a contiguous float32 GPU tensor")
+    B, T, H, d = q.shape
+    if tuple(w.shape) != (B, T, H) or codes.shape[0] != B or codes.shape[2] != d \
+            or tuple(scales.shape) != tuple(codes.shape[:2]):
+        raise ValueError("shapes disagree: q %s w %s codes %s scales %s"
+                         % (tuple(q.shape), tuple(w.shape), tuple(codes.shape),
+                            tuple(scales.shape)))
+    if not (q.device == w.device == codes.device == scales.device):
+        raise ValueError("q, w, codes and scales must be on one device")
+    return Shape(B, T, H, d, codes.shape[1], int(causal_offset), int(topk))
+
+
+def indexer_score_topk_fp8_ws(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    _check(load().indexer_score_topk_fp8_ws(ctypes.byref(shape), ctypes.byref(n)),
+           "indexer_score_topk_fp8_ws")
+    return n.value
+
+
+def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=None,
+                           out_score=None, want_score=True, ws=None):
+    """DSA indexer over E4M3 keys with per-key scales (rows T < 16)."""
+    s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    ws = _workspace(indexer_score_topk_fp8_ws(s), q.device, ws)
+    _check(load().indexer_score_topk_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
+                                         _p(out_idx), _p(out_score), _p(ws), ws.numel(),
+                                         _stream(q.device)), "indexer_score_topk_fp8")
+    return out_idx, out_score
 
 
 # ------------------------------------------------------------ diagnostics

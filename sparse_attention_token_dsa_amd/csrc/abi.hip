@@ -64,7 +64,8 @@ void drain_records() {
 
 const char* kKernelNames[sa::K_COUNT] = {
     "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
-    "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused"};
+    "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused",
+    "quantize_fp8", "scan_dsa_fp8"};
 
 // ------------------------------------------------------------ workspace
 
@@ -149,7 +150,8 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
 hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                           const sa_shape* s, const int32_t* heads, int hsel, float* scores,
                           uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
-                          float* out_score, hipStream_t st) {
+                          float* out_score, hipStream_t st, const uint8_t* codes = nullptr,
+                          const float* kscale = nullptr) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
     hipError_t e = sa::launch_fill_u32(state, rows * sa::kRowState, 0u, st);
@@ -171,6 +173,8 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.score_stride = score_stride(s->L);
     a.state = state;
     a.k = k;
+    a.codes = codes;
+    a.kscale = kscale;
     const int nht = ((heads ? hsel : s->H) + 15) / 16;
     e = sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
     if (e != hipSuccess) return e;
@@ -404,6 +408,53 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                            out_idx, out_score, st);
         if (e != hipSuccess) return hip_fail(e, "decode scan");
     }
+    return SA_OK;
+}
+
+// ------------------------------------------------------------- FP8 keys
+
+int sa_quantize_keys_fp8(const uint16_t* keys, int32_t batch, int32_t L, int32_t d,
+                         uint8_t* codes, float* scales, void* stream) {
+    if (!keys || !codes || !scales) return fail(SA_EINVAL, "keys, codes and scales must be non-NULL");
+    if (batch < 1 || L < 1) return fail(SA_EINVAL, "batch and L must be >= 1");
+    if (d != sa::kD) return fail(SA_EUNSUPPORTED, "d must be 128");
+    hipError_t e = sa::launch_quantize_fp8(keys, (long long)batch * L, codes, scales,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "quantize fp8");
+    return SA_OK;
+}
+
+static int check_fp8_shape(const sa_shape* s) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->T >= kPrefillMinT)
+        return fail(SA_EUNSUPPORTED, "FP8 keys: decode-style rows only (T < 16)");
+    return SA_OK;
+}
+
+int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes) {
+    int rc = check_fp8_shape(s);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_dsa(s, nullptr).bytes;
+    return SA_OK;
+}
+
+int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
+                           const float* scales, const sa_shape* s, int32_t* out_idx,
+                           float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_fp8_shape(s);
+    if (rc) return rc;
+    if (!q || !w || !codes || !scales || !out_idx)
+        return fail(SA_EINVAL, "q, w, codes, scales and out_idx must be non-NULL");
+    const size_t need = plan_dsa(s, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    DsaPlan p = plan_dsa(s, base);
+    hipError_t e = run_dense_topk(q, w, nullptr, s, nullptr, 0, p.scores, p.state, p.cand,
+                                  s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
+                                  codes, scales);
+    if (e != hipSuccess) return hip_fail(e, "fp8 decode scan");
     return SA_OK;
 }
 

@@ -1,11 +1,46 @@
+// Key-cache-side kernels.
+//
 // Block mean-pooling of the indexer keys: MISA's pooled keys (summary page
 // "MISA", method step 1, B = 1024) and HISA's block representatives
 // (PaperTrace section 2.1 / blog "Route 1: HISA", b = 128).  HBM-bound: every
 // key is read once with 16-byte loads; sums are fp32; the mean is stored as a
 // hi/lo bf16 pair so the bf16 MFMA score kernels can use it at fp32 accuracy.
+//
+// FP8 quantization of the keys (PaperTrace section 2.3, the FP8 cache: one
+// scale per block, here per key): a = max |k| / 448, codes = E4M3(k / a).
 #include "sa_common.h"
 
 namespace sa {
+
+// One wave per key, 2 values per lane: the max-abs reduction over the wave,
+// the fp32 scale and divisions, then the hardware E4M3 conversion (round to
+// nearest even) of values clamped to +-448, which is the saturating rounding.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* keys, long long n,
+                                                           uint8_t* codes, float* scales) {
+    const long long s = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (s >= n) return;
+    const int lane = lane_id();
+    const uint32_t two = *reinterpret_cast<const uint32_t*>(keys + s * kD + 2 * lane);
+    const float v0 = bf16_bits_to_f32(two & 0xffffu), v1 = bf16_bits_to_f32(two >> 16);
+    float m = fmaxf(fabsf(v0), fabsf(v1));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float a = m > 0.f ? m / 448.0f : 1.0f;
+    const float x0 = fminf(fmaxf(v0 / a, -448.0f), 448.0f);
+    const float x1 = fminf(fmaxf(v1 / a, -448.0f), 448.0f);
+    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+    reinterpret_cast<uint16_t*>(codes + s * kD)[lane] = (uint16_t)((uint32_t)pk & 0xffffu);
+    if (lane == 0) scales[s] = a;
+}
+
+hipError_t launch_quantize_fp8(const uint16_t* keys, long long n, uint8_t* codes, float* scales,
+                               hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    prof_begin(K_QUANT8, s);
+    quantize_fp8_kernel<<<dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s>>>(keys, n, codes, scales);
+    prof_end(K_QUANT8, s);
+    return hipGetLastError();
+}
 
 // 256 threads: thread (kl = tid >> 4, c16 = tid & 15) sums dims c16*8..+8 of
 // keys lo+kl, lo+kl+16, ...; the 16 partial sums per dim are reduced in LDS.

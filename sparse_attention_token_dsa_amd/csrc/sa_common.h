@@ -70,6 +70,15 @@ __device__ __forceinline__ uint4 ldg16(const uint16_t* p) {
     return *reinterpret_cast<const uint4*>(p);
 }
 
+// Two OCP E4M3 codes (bytes 0-1 of w, or 2-3 with HI) widened to two bf16
+// values, exactly (every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // 16-byte load of streamed data (keys read once per kernel), marked
 // nontemporal: it streams past the caches instead of displacing lines that
 // are reused.  On this chip it also raises the cold read rate (about 6.2
@@ -114,6 +123,8 @@ enum KernelId {
     K_ROUTER,
     K_GATHER,
     K_PREFILL,
+    K_QUANT8,
+    K_SCAN8,
     K_COUNT
 };
 
@@ -141,6 +152,11 @@ struct ScanArgs {
     uint32_t* state;        // [rows, kRowState] (zeroed) or null: build the first-digit
                             // histogram and the k-th-score digit for the dense top-k
     int k;                  // top-k size for the state
+    // FP8 keys instead of `keys` (decode keys only): E4M3 codes, 128 bytes per
+    // key, sequences seq_stride bytes apart, and one fp32 scale per key
+    // (sequences seq_stride / 128 apart).
+    const uint8_t* codes;
+    const float* kscale;
 };
 
 struct GatherArgs {
@@ -223,5 +239,8 @@ hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16
 hipError_t launch_pool2(const uint16_t* keys, int batch, int L, int small, int large,
                         uint16_t* out_small, uint16_t* out_large, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s);
+// Per-key FP8 quantization of n keys of 128 bf16 values.
+hipError_t launch_quantize_fp8(const uint16_t* keys, long long n, uint8_t* codes, float* scales,
+                               hipStream_t s);
 
 }  // namespace sa

@@ -127,6 +127,23 @@ def check_dsa(p, k, gidx, gsc, rows):
     return swaps
 
 
+def check_dsa_fp8(p, codes, scales, k, gidx, gsc, rows):
+    """As check_dsa, against the oracle's scores on the dequantized FP8 keys."""
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    oidx, osc, rs = oracle.dsa_fp8(prob, codes, scales, k, rows=rows, want_rowscore=True)
+    gi = gidx.reshape(-1, k)
+    gs = None if gsc is None else gsc.reshape(-1, k)
+    swaps = 0
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        srow = rs[u, : t + 1]
+        tol = TOL_REL * np.max(np.abs(srow))
+        swaps += check_set(gi[row], None if gs is None else gs[row], oidx[u], osc[u],
+                           lambda s, srow=srow: srow[s], t + 1, k, tol, t=t,
+                           what="dsa-fp8 row %d" % row)
+    return swaps
+
+
 def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows):
     prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
     base = oracle.misa(prob, k, B, h, kprime=0, rows=rows)

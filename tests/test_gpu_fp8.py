@@ -1,0 +1,149 @@
+"""GPU parity of the FP8 key path (PaperTrace section 2.3: the indexer's keys
+held as E4M3 codes with one fp32 scale per key).
+
+* sa_quantize_keys_fp8 is byte work: its codes and scales must equal the
+  oracle's bit for bit, including subnormal codes, signed zeros, exact
+  midpoints between codes and all-zero keys.
+* indexer_score_topk_fp8 is compared with the oracle's DSA on the dequantized
+  keys under the rule of tests/parity.py, on the oracle's own codes, so the two
+  stages are checked independently.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import _np, check_dsa_fp8, rows_of, to_device
+from sparse_attention_token_dsa_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_token_dsa_amd import api as a
+    a.load()
+    return a
+
+
+def gpu_quantize(api, K):
+    Kd = torch.from_numpy(np.ascontiguousarray(K).view(np.int16)).to(DEV)
+    codes, scales = api.quantize_keys_fp8(Kd)
+    torch.cuda.synchronize()
+    return _np(codes), _np(scales)
+
+
+def assert_quantize_exact(api, K):
+    gc, gs = gpu_quantize(api, K)
+    oc, os_ = oracle.quantize_keys_fp8(K)
+    assert np.array_equal(gs.view(np.uint32), os_.view(np.uint32)), "scales differ"
+    bad = np.argwhere(gc != oc)
+    assert bad.size == 0, "codes differ at %s: gpu %s oracle %s" % (
+        bad[:4].tolist(), gc[tuple(bad[:4].T)].tolist(), oc[tuple(bad[:4].T)].tolist())
+
+
+@pytest.mark.parametrize("Bt,L,seed", [(1, 1, 1), (3, 1000, 2), (2, 4099, 3)])
+def test_quantize_random_keys(api, Bt, L, seed):
+    say("quantize random Bt=%d L=%d" % (Bt, L))
+    p = synth.make_problem(300 + seed, Bt=Bt, T=1, L=L, H=4)
+    assert_quantize_exact(api, p["K"])
+
+
+def test_quantize_edge_values(api):
+    # Keys built so that k_x / a lands on chosen values: every E4M3 magnitude,
+    # the midpoints between neighbouring codes (ties to even), values just off
+    # them, subnormals, values that round to zero, signed zeros and all-zero keys.
+    say("quantize edge values")
+    v = oracle.fp8_decode(np.arange(0x7F))
+    mids = (v[:-1] + v[1:]) / 2
+    vals = np.concatenate([v, mids, mids * (1 + 2.0 ** -7), mids * (1 - 2.0 ** -7),
+                           [2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11, 0.0]])
+    rng = np.random.default_rng(5)
+    rows = []
+    for e in (-20, -3, 0, 5):
+        for start in range(0, len(vals), 127):
+            row = np.zeros(128)
+            chunk = vals[start:start + 127]
+            row[:len(chunk)] = chunk * rng.choice([-1.0, 1.0], size=len(chunk))
+            row[127] = 448.0              # a = 2^e exactly
+            rows.append(row * 2.0 ** e)
+    K = synth.to_bf16_bits(np.array(rows, np.float32))[None]
+    K[0, 1, 5] = 0x8000                   # -0
+    zero = np.zeros((1, 3, 128), np.uint16)
+    zero[0, 1, :] = 0x8000                # a key of -0 only
+    K = np.concatenate([K, zero], axis=1)
+    assert_quantize_exact(api, K)
+
+
+@pytest.mark.parametrize("Bt,T,L,H,k", [
+    (3, 1, 5000, 64, 100),        # decode, ragged L
+    (2, 3, 9001, 64, 257),        # several decode rows per sequence
+    (1, 15, 3000, 64, 300),       # the most rows the FP8 path takes
+    (2, 1, 300, 64, 512),         # k > t+1: the whole prefix
+    (1, 2, 20000, 32, 2048),      # H = 32
+    (2, 1, 4100, 40, 64),         # H not a multiple of 16
+    (1, 1, 1, 64, 8),             # a single key
+])
+def test_dsa_fp8(api, Bt, T, L, H, k):
+    say("dsa fp8 Bt=%d T=%d L=%d H=%d k=%d" % (Bt, T, L, H, k))
+    p = synth.make_problem(400 + L % 89, Bt=Bt, T=T, L=L, H=H, needles=8,
+                           needle_mode="decode" if T == 1 else "rows")
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    idx, sc = api.indexer_score_topk_fp8(q, w, torch.from_numpy(codes).to(DEV),
+                                         torch.from_numpy(scales).to(DEV), p["offset"], k)
+    torch.cuda.synchronize()
+    check_dsa_fp8(p, codes, scales, k, _np(idx), _np(sc), rows_of(p))
+
+
+def test_dsa_fp8_zero_keys(api):
+    # All-zero keys (scale 1, codes 0) score exactly 0 next to real keys.
+    say("dsa fp8 zero keys")
+    p = synth.make_problem(410, Bt=1, T=1, L=3000, H=64)
+    p["K"][0, ::3] = 0
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    assert np.all(scales[0, ::3] == 1.0)
+    q, w, _ = to_device(p, DEV)
+    idx, sc = api.indexer_score_topk_fp8(q, w, torch.from_numpy(codes).to(DEV),
+                                         torch.from_numpy(scales).to(DEV), p["offset"], 1500)
+    torch.cuda.synchronize()
+    check_dsa_fp8(p, codes, scales, 1500, _np(idx), _np(sc), rows_of(p))
+
+
+def test_dsa_fp8_128k_quantized_on_gpu(api):
+    # The 128k decode workload (8 sequences, 64 heads, k = 2048): GPU-quantized
+    # keys (checked bit-exact first), then every row against the oracle.
+    say("dsa fp8 128k b8 h64")
+    p = synth.make_config("misa_128k_h64")
+    q, w, K = to_device(p, DEV)
+    codes, scales = api.quantize_keys_fp8(K)
+    torch.cuda.synchronize()
+    oc, os_ = oracle.quantize_keys_fp8(p["K"])
+    assert np.array_equal(_np(codes), oc) and np.array_equal(_np(scales), os_)
+    idx, sc = api.indexer_score_topk_fp8(q, w, codes, scales, p["offset"], 2048)
+    torch.cuda.synchronize()
+    check_dsa_fp8(p, oc, os_, 2048, _np(idx), _np(sc), rows_of(p))
+
+
+def test_dsa_fp8_rejects_prefill_rows(api):
+    say("dsa fp8 T=16 rejected")
+    p = synth.make_problem(420, Bt=1, T=16, L=100, H=16)
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    with pytest.raises(api.SaError) as e:
+        api.indexer_score_topk_fp8(q, w, torch.from_numpy(codes).to(DEV),
+                                   torch.from_numpy(scales).to(DEV), p["offset"], 8)
+    assert e.value.code == api.SA_EUNSUPPORTED
