@@ -274,6 +274,8 @@ def main():
         "hbm_kernels": other_hbm,
     }
 
+    result["fp8"] = bench_fp8(api, torch, dev, q, w, K, shape, flush, args.steps)
+
     if not args.no_prefill:
         result["prefill"] = bench_prefill(api, synth, torch, np, dev, args.prefill_iters)
 
@@ -296,6 +298,59 @@ def settle(fn, torch, dev):
         if n % 16 == 0:
             torch.cuda.synchronize(dev)
     torch.cuda.synchronize(dev)
+
+
+def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
+    """The DSA selector on the same decode batch with the keys held as E4M3
+    codes plus one fp32 scale per key (132 B per key instead of 256 B)."""
+    Bt, L, H, d, off, k = shape.batch, shape.L, shape.H, shape.d, shape.causal_offset, shape.topk
+    codes = torch.empty((Bt, L, d), dtype=torch.uint8, device=dev)
+    scales = torch.empty((Bt, L), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.indexer_score_topk_fp8_ws(shape), dtype=torch.uint8, device=dev)
+    oi = torch.empty((Bt, 1, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, 1, k), dtype=torch.float32, device=dev)
+
+    def call():
+        api.indexer_score_topk_fp8(q, w, codes, scales, off, k, oi, osc, ws=ws)
+
+    api.quantize_keys_fp8(K, codes, scales)
+    settle(call, torch, dev)
+    api.profile_enable(True)
+    for _ in range(steps):
+        flush()
+        api.quantize_keys_fp8(K, codes, scales)
+    torch.cuda.synchronize(dev)
+    kq = api.profile_read()
+    api.profile_enable(False)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    api.profile_enable(True)
+    for e0, e1 in evs:
+        flush()
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize(dev)
+    kern = api.profile_read()
+    api.profile_enable(False)
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    scan_bytes = Bt * L * (d + 4) + Bt * H * d * 2 + Bt * H * 4 + Bt * L * 4
+    us = 1e3 * kern["scan_dsa_fp8"][0] / kern["scan_dsa_fp8"][1]
+    gbs = scan_bytes / (us * 1e-6) / 1e9
+    q_us = 1e3 * kq["quantize_fp8"][0] / kq["quantize_fp8"][1]
+    q_bytes = Bt * L * (2 * d + d + 4)
+    return {"workload": "decode_128k_b8_h64_fp8keys", "cache": "cold: a 1 GiB read before "
+            "each call", "ms_per_call": ms, "scores_per_s": Bt * L / (ms * 1e-3),
+            "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()},
+            "roofline": {"kernel": "scan_dsa_fp8", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(
+                             "scan_dsa_fp8", source_digest(["scan8.hip", "sa_frag.h",
+                                                            "sa_common.h"])),
+                         "algorithmic_bytes_per_launch": scan_bytes, "avg_us": round(us, 2)},
+            "quantize": {"avg_us": round(q_us, 2), "algorithmic_bytes_per_launch": q_bytes,
+                         "GB/s": round(q_bytes / (q_us * 1e-6) / 1e9, 1)}}
 
 
 def bench_prefill(api, synth, torch, np, dev, iters):

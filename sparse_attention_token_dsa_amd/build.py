@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libsaindexer.so")
-SOURCES = ["abi.hip", "scan.hip", "topk.hip", "pool.hip", "prefill.hip"]
+SOURCES = ["abi.hip", "scan.hip", "scan8.hip", "topk.hip", "pool.hip", "prefill.hip"]
 
 # Packed fp32 ops are switched off for device code: hipcc -O3 would otherwise
 # form v_pk_* fp32 instructions on its own.  -fno-honor-nans: inputs are
@@ -19,10 +19,11 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# The prefill kernel's epilogue reads every MFMA result with VALU: results in
-# VGPRs save one accumulator-to-VGPR move per element.  (The scan kernels keep
-# the default: there it would cost occupancy.)
-FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The prefill kernel's and the FP8 scan's epilogues read every MFMA result with
+# VALU: results in VGPRs save one accumulator-to-VGPR move per element.  (The
+# bf16 scan kernels keep the default: there it would cost occupancy.)
+FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "scan8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 _NOISE = "is not a recognized feature for this target"
 
 

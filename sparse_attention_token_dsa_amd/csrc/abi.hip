@@ -168,7 +168,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.offset = s->causal_offset;
     a.len_div = 1;
     a.len_cap = s->L;
-    a.chunk = sa::scan_chunk(4, rows, s->L);
+    a.chunk = codes ? sa::scan8_chunk(rows, s->L) : sa::scan_chunk(4, rows, s->L);
     a.scores = scores;
     a.score_stride = score_stride(s->L);
     a.state = state;
@@ -176,7 +176,8 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.codes = codes;
     a.kscale = kscale;
     const int nht = ((heads ? hsel : s->H) + 15) / 16;
-    e = sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
+    e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
+              : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
     if (e != hipSuccess) return e;
     sa::TopkArgs t{};
     t.dense = scores;

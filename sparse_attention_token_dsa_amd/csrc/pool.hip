@@ -12,32 +12,51 @@
 
 namespace sa {
 
-// One wave per key, 2 values per lane: the max-abs reduction over the wave,
-// the fp32 scale and divisions, then the hardware E4M3 conversion (round to
-// nearest even) of values clamped to +-448, which is the saturating rounding.
+// 16 lanes per key, 8 values per lane (16-byte loads, 8-byte code stores):
+// the max-abs reduction over the 16 lanes, the fp32 scale and divisions, then
+// the hardware E4M3 conversion (round to nearest even) of values clamped to
+// +-448, which is the saturating rounding.
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* keys, long long n,
                                                            uint8_t* codes, float* scales) {
-    const long long s = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (s >= n) return;
-    const int lane = lane_id();
-    const uint32_t two = *reinterpret_cast<const uint32_t*>(keys + s * kD + 2 * lane);
-    const float v0 = bf16_bits_to_f32(two & 0xffffu), v1 = bf16_bits_to_f32(two >> 16);
-    float m = fmaxf(fabsf(v0), fabsf(v1));
+    // 16 lanes per key (lane part p: dims 8p .. 8p+7), 16 keys per workgroup.
+    const long long s = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4;
+    if (s >= n) return;  // whole 16-lane groups leave together
+    const int part = threadIdx.x & 15;
+    const uint4 v = ldg16_stream(keys + s * kD + part * 8);
+    const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = bf16_bits_to_f32(wds[e] & 0xffffu);
+        x[2 * e + 1] = bf16_bits_to_f32(wds[e] >> 16);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
     const float a = m > 0.f ? m / 448.0f : 1.0f;
-    const float x0 = fminf(fmaxf(v0 / a, -448.0f), 448.0f);
-    const float x1 = fminf(fmaxf(v1 / a, -448.0f), 448.0f);
-    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-    reinterpret_cast<uint16_t*>(codes + s * kD)[lane] = (uint16_t)((uint32_t)pk & 0xffffu);
-    if (lane == 0) scales[s] = a;
+    // x / a is at most 448 up to the rounding of a; the clamp keeps the
+    // conversion on the saturating side (beyond 448 it would give NaN).
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * h + e] / a, -448.0f), 448.0f);
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+        out[h] = (uint32_t)pk;
+    }
+    *reinterpret_cast<uint2*>(codes + s * kD + part * 8) = make_uint2(out[0], out[1]);
+    if (part == 0) scales[s] = a;
 }
 
 hipError_t launch_quantize_fp8(const uint16_t* keys, long long n, uint8_t* codes, float* scales,
                                hipStream_t s) {
     if (n <= 0) return hipSuccess;
     prof_begin(K_QUANT8, s);
-    quantize_fp8_kernel<<<dim3((unsigned)((n + 3) / 4)), dim3(256), 0, s>>>(keys, n, codes, scales);
+    quantize_fp8_kernel<<<dim3((unsigned)((n + 15) / 16)), dim3(256), 0, s>>>(keys, n, codes, scales);
     prof_end(K_QUANT8, s);
     return hipGetLastError();
 }

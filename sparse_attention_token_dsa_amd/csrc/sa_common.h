@@ -223,6 +223,9 @@ hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool ro
                        hipStream_t s);
 // Keys per scan workgroup for 4 (keys) or 8 (block reps) k-steps, rows x maxn keys.
 int scan_chunk(int ksteps, long long rows, int maxn);
+// FP8 key scan (DSA decode rows): scores of codes/kscale keys, chunk from scan8_chunk.
+hipError_t launch_scan8(const ScanArgs& a, int rows, int nht, hipStream_t s);
+int scan8_chunk(long long rows, int maxn);
 int cu_count();  // compute units of the current device (cached per device)
 hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
                          hipStream_t s);

@@ -24,17 +24,16 @@ namespace sa {
 // With a row state (HIST), the scores' first radix digit is histogrammed in
 // LDS and added to the row's global histogram for the top-k filter, which
 // runs after this kernel and so sees every workgroup's counts.
-// With F8, the keys are E4M3 codes with one scale per key: each load
-// instruction brings 8 whole 128-byte keys (lane l: key l/8, codes of dims
-// 16*(l%8) .. +16), the codes are widened to bf16 exactly (every E4M3 value
-// is a bf16 value) on their way into the transpose tile, and the score of
-// the widened key is multiplied by the key's scale (ReLU commutes with the
-// positive scale).
-template <int NHT, int KSTEPS, int G, int NBUF, int NSTEP, bool HIST, bool ROUTED, bool F8>
-__global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
+template <int KS>
+constexpr int scan_waves() { return 4; }
+
+template <int NHT, int KSTEPS, int G, int NBUF, int NSTEP, bool HIST, bool ROUTED>
+__global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArgs a) {
+    constexpr int NW = scan_waves<KSTEPS>();
+    constexpr int NT = 64 * NW;
     constexpr int KROW = KSTEPS * 32;
     constexpr int WKEYS = G * 16;
-    constexpr int STEP = 4 * WKEYS;
+    constexpr int STEP = NW * WKEYS;
     const int row = blockIdx.y;
     const int b = row / a.T;
     const int t = a.offset + (row - b * a.T);
@@ -47,7 +46,7 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     __shared__ uint32_t lhist[HIST ? kHist0Bins : 1];
     __shared__ float sbuf[kScanMaxChunk];
     if (HIST) {
-        for (int x = threadIdx.x; x < kHist0Bins; x += 256) lhist[x] = 0u;
+        for (int x = threadIdx.x; x < kHist0Bins; x += NT) lhist[x] = 0u;
         __syncthreads();
     }
 
@@ -59,8 +58,6 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
                             heads, a.hsel, g, c);
 
     const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
-    const uint8_t* cseq = F8 ? a.codes + (long long)b * a.seq_stride : nullptr;
-    const float* sseq = F8 ? a.kscale + (long long)b * (a.seq_stride / kD) : nullptr;
     const uint16_t* tailp =
         (KSTEPS == 8 && a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
 
@@ -75,24 +72,13 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     // instruction with 64 bytes each, which costs about a third of the HBM
     // rate.  The transpose tile is XOR-swizzled (chunk ^ key) so both the
     // row writes and the column reads are free of bank conflicts.
-    __shared__ uint4 tbuf[KSTEPS == 4 ? 4 : 1][KSTEPS == 4 ? 256 : 1];
+    __shared__ uint4 tbuf[KSTEPS == 4 ? NW : 1][KSTEPS == 4 ? 256 : 1];
     // Loads past the end re-read the last key, so they can be unconditional:
     // the wait before each compute then covers exactly the older buffer.
     auto loadG = [&](uint4 (&buf)[G][KSTEPS], int base) {
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
-            if (F8) {
-                // buf[gi][0..1]: the codes; buf[gi][2].x: the scale of key
-                // base + gi*16 + (lane & 15).
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int s = min(base + gi * 16 + 8 * j + (lane >> 3), ce - 1);
-                    buf[gi][j] = ldg16_stream(reinterpret_cast<const uint16_t*>(
-                        cseq + (long long)s * kD + (lane & 7) * 16));
-                }
-                const int s = min(base + gi * 16 + (lane & 15), ce - 1);
-                buf[gi][2].x = __float_as_uint(sseq[s]);
-            } else if (KSTEPS == 4) {
+            if (KSTEPS == 4) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int s = min(base + gi * 16 + 4 * j + (lane >> 4), ce - 1);
@@ -111,31 +97,15 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
             float sc;
             if (KSTEPS == 4) {
                 uint4* tp = tbuf[wid];
-                if (F8) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int key = 8 * j + (lane >> 3);
-                        const int ch = 2 * (lane & 7);
-                        const uint4 cw = buf[gi][j];
-                        tp[key * 16 + (ch ^ key)] = make_uint4(
-                            fp8x2_to_bf16x2<false>(cw.x), fp8x2_to_bf16x2<true>(cw.x),
-                            fp8x2_to_bf16x2<false>(cw.y), fp8x2_to_bf16x2<true>(cw.y));
-                        tp[key * 16 + ((ch + 1) ^ key)] = make_uint4(
-                            fp8x2_to_bf16x2<false>(cw.z), fp8x2_to_bf16x2<true>(cw.z),
-                            fp8x2_to_bf16x2<false>(cw.w), fp8x2_to_bf16x2<true>(cw.w));
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int key = 4 * j + (lane >> 4);
-                        tp[key * 16 + ((lane & 15) ^ key)] = buf[gi][j];
-                    }
+                for (int j = 0; j < 4; ++j) {
+                    const int key = 4 * j + (lane >> 4);
+                    tp[key * 16 + ((lane & 15) ^ key)] = buf[gi][j];
                 }
                 uint4 kb[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) kb[kk] = tp[c * 16 + ((kk * 4 + g) ^ c)];
                 sc = group_score<NHT, 4>(f, kb);
-                if (F8) sc *= __uint_as_float(buf[gi][2].x);
             } else {
                 sc = group_score<NHT, KSTEPS>(f, buf[gi]);
             }
@@ -175,10 +145,10 @@ __global__ __launch_bounds__(256) void scan_kernel(ScanArgs a) {
     }
     __syncthreads();
     float* srow = a.scores + (long long)row * a.score_stride;
-    for (int x = threadIdx.x; x < ce - cs; x += 256) srow[cs + x] = sbuf[x];
+    for (int x = threadIdx.x; x < ce - cs; x += NT) srow[cs + x] = sbuf[x];
     if (HIST) {
         uint32_t* grow = a.state + (long long)row * kRowState;
-        for (int x = threadIdx.x; x < kHist0Bins; x += 256) {
+        for (int x = threadIdx.x; x < kHist0Bins; x += NT) {
             const uint32_t v = lhist[x];
             if (v) atomicAdd(&grow[x], v);
         }
@@ -394,40 +364,28 @@ constexpr int scan_groups() { return KS == 4 ? 1 : 2; }
 template <int KS>
 constexpr int scan_bufs() { return KS == 4 ? 4 : 1; }
 
-template <int NHT, int KS, int NSTEP, bool F8 = false>
+template <int NHT, int KS, int NSTEP>
 static void scan_dispatch_hist(const ScanArgs& a, dim3 grid, hipStream_t s) {
     constexpr int G = scan_groups<KS>();
     constexpr int NB = scan_bufs<KS>();
-    if constexpr (F8) {  // DSA keys only (not routed)
-        if (a.state)
-            scan_kernel<NHT, KS, G, NB, NSTEP, true, false, true><<<grid, dim3(256), 0, s>>>(a);
-        else
-            scan_kernel<NHT, KS, G, NB, NSTEP, false, false, true><<<grid, dim3(256), 0, s>>>(a);
-        return;
-    }
     if (a.heads) {
         if (a.state)
-            scan_kernel<NHT, KS, G, NB, NSTEP, true, true, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, true, true><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
         else
-            scan_kernel<NHT, KS, G, NB, NSTEP, false, true, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, false, true><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
     } else {
         if (a.state)
-            scan_kernel<NHT, KS, G, NB, NSTEP, true, false, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, true, false><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
         else
-            scan_kernel<NHT, KS, G, NB, NSTEP, false, false, false><<<grid, dim3(256), 0, s>>>(a);
+            scan_kernel<NHT, KS, G, NB, NSTEP, false, false><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
     }
 }
 
 // Full chunks of keys take the completely unrolled loop (about 2% faster).
 template <int NHT>
 static void scan_dispatch_keys(const ScanArgs& a, dim3 grid, hipStream_t s) {
-    constexpr int kFull = kScanMaxChunk / (4 * 16 * scan_groups<4>());
-    if (a.codes) {
-        if (a.chunk == kScanMaxChunk)
-            scan_dispatch_hist<NHT, 4, kFull, true>(a, grid, s);
-        else
-            scan_dispatch_hist<NHT, 4, 0, true>(a, grid, s);
-    } else if (a.chunk == kScanMaxChunk) {
+    constexpr int kFull = kScanMaxChunk / (scan_waves<4>() * 16 * scan_groups<4>());
+    if (a.chunk == kScanMaxChunk) {
         scan_dispatch_hist<NHT, 4, kFull>(a, grid, s);
     } else {
         scan_dispatch_hist<NHT, 4, 0>(a, grid, s);
@@ -449,8 +407,8 @@ int cu_count() {
 }
 
 int scan_chunk(int ksteps, long long rows, int maxn) {
-    if (ksteps != 4) return 4 * 16 * scan_groups<8>();
-    constexpr int step = 4 * 16 * scan_groups<4>();
+    if (ksteps != 4) return scan_waves<8>() * 16 * scan_groups<8>();
+    constexpr int step = scan_waves<4>() * 16 * scan_groups<4>();
     const long long wgs = cu_count();
     long long c = (rows * (long long)maxn + wgs - 1) / wgs;
     c = (c + step - 1) / step * step;
@@ -464,7 +422,7 @@ hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool ro
     const int maxn = a.len_cap;
     const dim3 grid((unsigned)((maxn + a.chunk - 1) / a.chunk), (unsigned)rows);
     const int kid = ksteps == 8 ? K_BLOCK_SCORE
-                  : (routed ? K_SCAN_ROUTED : (a.codes ? K_SCAN8 : K_SCAN));
+                  : (routed ? K_SCAN_ROUTED : K_SCAN);
     prof_begin(kid, s);
     if (ksteps == 4) {
         switch (nht) {

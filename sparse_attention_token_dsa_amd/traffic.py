@@ -10,7 +10,8 @@ Two counter runs of the same program, then a summary:
   python3 -m sparse_attention_token_dsa_amd.traffic summarize OUT
 
 `run` launches the DSA decode selector on the L = 131072, batch-8, 64-head
-workload a few times, the fused prefill (T = 4096 over 28672 cached keys,
+workload a few times, then the same selector on the keys quantized to E4M3,
+the fused prefill (T = 4096 over 28672 cached keys,
 k = 2048) twice, then a plain copy kernel (torch's elementwise add of a zero
 into a second 256 MiB fp32 tensor: 256 MiB read, 256 MiB written).
 `summarize` reads both runs, calibrates each counter on the copy kernel
@@ -33,6 +34,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "traffic.json")
 SCAN_SOURCES = ["scan.hip", "sa_frag.h", "sa_common.h"]
 SCAN_KERNEL = "scan_kernel<4, 4, 1, 4, 64, true, false>"
+SCAN8_KERNEL = "scan8_kernel<4, true>"
+SCAN8_SOURCES = ["scan8.hip", "sa_frag.h", "sa_common.h"]
 PREFILL_SOURCES = ["prefill.hip", "sa_frag.h", "sa_common.h"]
 PREFILL_KERNEL = "prefill_kernel<4>"
 COPY_BYTES = 256 << 20
@@ -61,6 +64,11 @@ def run():
     for _ in range(4):
         api.indexer_score_topk(q, w, K, p["offset"], 2048)
     torch.cuda.synchronize()
+    codes, scales = api.quantize_keys_fp8(K)
+    for _ in range(4):
+        api.indexer_score_topk_fp8(q, w, codes, scales, p["offset"], 2048)
+    torch.cuda.synchronize()
+    del codes, scales
     pp = synth.make_config("prefill_chunked")
     q = torch.from_numpy(pp["q"].view(np.int16)).to(dev)
     w = torch.from_numpy(pp["w"]).to(dev)
@@ -106,6 +114,7 @@ def summarize(out_dir):
     except (OSError, ValueError):
         allrec = {}
     for name, needle, sources in (("scan_dsa", SCAN_KERNEL, SCAN_SOURCES),
+                                  ("scan_dsa_fp8", SCAN8_KERNEL, SCAN8_SOURCES),
                                   ("prefill_fused", PREFILL_KERNEL, PREFILL_SOURCES)):
         kf, kw = _pick(fetch, needle), _pick(write, needle)
         rec = {
