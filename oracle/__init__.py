@@ -55,12 +55,17 @@ def _load():
         _lib.oracle_pool.argtypes = [P, i, i, i, i, P]
         _lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_long, i, P, P, i]
         _lib.oracle_dsa_fp8.argtypes = [P, P, P, i, P, i, P, P, P, i]
+        _lib.oracle_lisa.argtypes = [P, i, P, i, P, P, P, i]
+        _lib.oracle_resmisa.argtypes = [P, i, i, i, P, i, P, P, P, P, P, P, i]
+        _lib.oracle_box_bound.argtypes = [P, P, P, i]
+        _lib.oracle_box_bound.restype = ctypes.c_double
         _lib.oracle_fp8_e4m3_decode.argtypes = [ctypes.c_uint8]
         _lib.oracle_fp8_e4m3_decode.restype = ctypes.c_double
         _lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
         _lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
         for f in (_lib.oracle_dsa, _lib.oracle_misa, _lib.oracle_hisa, _lib.oracle_pool,
-                  _lib.oracle_quantize_keys_fp8, _lib.oracle_dsa_fp8):
+                  _lib.oracle_quantize_keys_fp8, _lib.oracle_dsa_fp8, _lib.oracle_lisa,
+                  _lib.oracle_resmisa):
             f.restype = ctypes.c_int
     return _lib
 
@@ -224,3 +229,48 @@ def dsa_fp8(prob: Problem, codes, scales, topk: int, rows=None, want_rowscore=Fa
                               n, _ptr(idx), _ptr(sc), _ptr(rs), _threads(nthreads)),
            "oracle_dsa_fp8")
     return (idx, sc, rs) if want_rowscore else (idx, sc)
+
+
+def lisa(prob: Problem, topk: int, rows=None, want_rowscore=False, nthreads=0):
+    """LISA: top-k by the linear score g . k.  Returns (idx, score[, rowscore])."""
+    lib = _load()
+    r, n = prob.rows(rows)
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    rs = np.empty((n, prob.L), np.float64) if want_rowscore else None
+    _check(lib.oracle_lisa(ctypes.byref(prob._c), topk, _ptr(r), n, _ptr(idx), _ptr(sc), _ptr(rs),
+                           _threads(nthreads)), "oracle_lisa")
+    return (idx, sc, rs) if want_rowscore else (idx, sc)
+
+
+def resmisa(prob: Problem, topk: int, block: int, r: int, rows=None, override_heads=None,
+            want_rowscore=False, nthreads=0):
+    """ResMiSA: shared linear score + r routed residual heads.  Returns a dict
+    with idx, score, heads [n, r] (ascending), S [n, H], rowscore."""
+    lib = _load()
+    rw, n = prob.rows(rows)
+    oh = None if override_heads is None else np.ascontiguousarray(override_heads, np.int32)
+    if oh is not None:
+        assert oh.shape == (n, r)
+    out = {
+        "idx": np.empty((n, topk), np.int32),
+        "score": np.empty((n, topk), np.float64),
+        "heads": np.empty((n, r), np.int32) if r else None,
+        "S": np.empty((n, prob.H), np.float64) if r else None,
+        "rowscore": np.empty((n, prob.L), np.float64) if want_rowscore else None,
+    }
+    _check(lib.oracle_resmisa(ctypes.byref(prob._c), topk, block, r, _ptr(rw), n, _ptr(oh),
+                              _ptr(out["heads"]), _ptr(out["S"]), _ptr(out["rowscore"]),
+                              _ptr(out["idx"]), _ptr(out["score"]), _threads(nthreads)),
+           "oracle_resmisa")
+    return out
+
+
+def box_bound(q, kmin, kmax):
+    """U- = sum_d (max(-q,0) kmax - max(q,0) kmin) for one head and one box."""
+    lib = _load()
+    q = np.ascontiguousarray(q, np.float64)
+    kmin = np.ascontiguousarray(kmin, np.float64)
+    kmax = np.ascontiguousarray(kmax, np.float64)
+    assert q.shape == kmin.shape == kmax.shape and q.ndim == 1
+    return lib.oracle_box_bound(_ptr(q), _ptr(kmin), _ptr(kmax), q.shape[0])

@@ -16,7 +16,10 @@
  *  [PT]   PaperTrace, "2.2.2 MISA, LISA and ResMiSA: when the indexer becomes
  *         the new bottleneck" -- section 1 (DSA score), 2.1 (HISA / MISA),
  *         2.3 (acceptance procedure, budgets r*b >= k, min(k, t)),
- *         3.1 (two-head worked example, score 6).
+ *         3.1 (two-head worked example, score 6; the fused query and
+ *         LISA's linear score), 3.2 (ResMiSA: the shared linear expert, r
+ *         residual heads routed by the coordinate-box bound; the box example
+ *         U- = 9).
  *  [MISA] "MISA: Mixture of Indexer Sparse Attention for Long-Context LLM
  *         Inference" (structured paper summary), section "method steps"
  *         (steps 1-6 and the two-stage MISA-dagger variant).
@@ -38,7 +41,10 @@
  *  - a block's pooled key is the mean of its *legal* keys (s <= t and s < L);
  *  - MISA and HISA keys are shared across heads (one key head), so the head
  *    subscript some formulas attach to the key is dropped;
- *  - MISA routes by |A| but scores with the sign of w kept.
+ *  - MISA routes by |A| but scores with the sign of w kept;
+ *  - ResMiSA's blocks have a caller-given size; a block cut by the causal
+ *    bound takes the extrema of its legal keys only; routed heads are the r
+ *    largest S_h, ties to the lower head.
  */
 #include "oracle.h"
 
@@ -685,4 +691,183 @@ int oracle_pool(const uint16_t* K, int Bt, int L, int d, int block, double* out)
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------ LISA / ResMiSA */
+
+/* [PT] section 3.1: with one key shared by every head,
+ * ReLU(x) = x + ReLU(-x) splits the score into a linear term and a
+ * nonlinear correction, I = l + c with
+ *   l = sum_j w_j (q_j . k) = g . k,   g = sum_j w_j q_j   (the fused query),
+ *   c = sum_j w_j ReLU(-(q_j . k)).
+ * LISA ranks by l alone.  [PT] section 3.2 (ResMiSA / MISA-2) keeps l for
+ * every key and adds the corrections of r routed residual heads A:
+ *   R = l + sum_{h in A} w_h ReLU(-(q_h . k)).
+ * Routing bounds each head's possible correction over the legal history: for
+ * a block of keys with per-dimension extrema [kmin_d, kmax_d] and
+ * q+ = max(q, 0), q- = max(-q, 0),
+ *   U-_h = sum_d (q-_{h,d} kmax_d - q+_{h,d} kmin_d) >= -(q_h . k)
+ * for every key of the block, and S_h = |w_h| max_b ReLU(U-_{h,b}) over the
+ * blocks that intersect [0, t], a cut block taking the extrema of its legal
+ * keys only.  A = the r heads with the largest S_h (ties -> lower head). */
+
+double oracle_box_bound(const double* q, const double* kmin, const double* kmax, int d);
+
+/* g = sum_j w_j q_j in fp64, heads in order. */
+static void fused_query(const uint16_t* qrow, const float* wrow, int H, int d, double* g)
+{
+    for (int x = 0; x < d; ++x) g[x] = 0.0;
+    for (int j = 0; j < H; ++j)
+        for (int x = 0; x < d; ++x) g[x] += (double)wrow[j] * bf16_to_f64(qrow[(size_t)j * d + x]);
+}
+
+static double dot_f64(const double* a, const double* b, int d)
+{
+    double z = 0.0;
+    for (int x = 0; x < d; ++x) z += a[x] * b[x];
+    return z;
+}
+
+typedef struct {
+    const oracle_problem* p;
+    int topk, block, r;
+    const int32_t* rows;
+    const int32_t* override_heads;
+    int32_t* out_heads;
+    double* out_S;
+    double* out_rowscore;
+    int32_t* out_idx;
+    double* out_score;
+} resmisa_ctx;
+
+static int resmisa_row(void* vctx, int rr)
+{
+    resmisa_ctx* c = (resmisa_ctx*)vctx;
+    const oracle_problem* p = c->p;
+    const int H = p->H, d = p->d, r = c->r;
+    int row = c->rows ? c->rows[rr] : rr;
+    int t = t_of(p, row);
+    int n = t + 1;
+    const uint16_t* qrow = qrow_of(p, row);
+    const float* wrow = wrow_of(p, row);
+    const uint16_t* Kseq = kseq_of(p, row);
+
+    double* g = (double*)malloc(sizeof(double) * (size_t)d);
+    double* key = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kmax = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kmin = (double*)malloc(sizeof(double) * (size_t)d);
+    double* S = (double*)malloc(sizeof(double) * (size_t)H);
+    scored_t* hc = (scored_t*)malloc(sizeof(scored_t) * (size_t)H);
+    int32_t* heads = (int32_t*)malloc(sizeof(int32_t) * (size_t)(r > 0 ? r : 1));
+    scored_t* cand = (scored_t*)malloc(sizeof(scored_t) * (size_t)n);
+    if (!g || !key || !kmax || !kmin || !S || !hc || !heads || !cand) {
+        free(g); free(key); free(kmax); free(kmin); free(S); free(hc); free(heads); free(cand);
+        return ORACLE_ENOMEM;
+    }
+    fused_query(qrow, wrow, H, d, g);
+
+    if (r > 0) {
+        /* Routing statistic S_h over the blocks intersecting [0, t]. */
+        for (int j = 0; j < H; ++j) S[j] = 0.0;  /* max of ReLU(.) >= 0 */
+        int nb = t / c->block + 1;
+        for (int m = 0; m < nb; ++m) {
+            int lo = m * c->block;
+            int hi = lo + c->block;
+            if (hi > n) hi = n;
+            for (int x = 0; x < d; ++x) {
+                kmax[x] = -INFINITY;
+                kmin[x] = INFINITY;
+            }
+            for (int s = lo; s < hi; ++s)
+                for (int x = 0; x < d; ++x) {
+                    double v = bf16_to_f64(Kseq[(size_t)s * d + x]);
+                    if (v > kmax[x]) kmax[x] = v;
+                    if (v < kmin[x]) kmin[x] = v;
+                }
+            for (int j = 0; j < H; ++j) {
+                widen_key(qrow + (size_t)j * d, d, key);
+                double U = oracle_box_bound(key, kmin, kmax, d);
+                double bound = fabs((double)wrow[j]) * (U > 0.0 ? U : 0.0);
+                if (bound > S[j]) S[j] = bound;
+            }
+        }
+        for (int j = 0; j < H; ++j) {
+            hc[j].score = S[j];
+            hc[j].idx = j;
+        }
+        if (c->override_heads) {
+            for (int u = 0; u < r; ++u) heads[u] = c->override_heads[(size_t)rr * r + u];
+        } else {
+            select_top(hc, H, r);
+            for (int u = 0; u < r; ++u) heads[u] = hc[u].idx;
+        }
+        /* ascending head order for the residual sum */
+        for (int a = 1; a < r; ++a)
+            for (int b2 = a; b2 > 0 && heads[b2 - 1] > heads[b2]; --b2) {
+                int32_t tmp = heads[b2];
+                heads[b2] = heads[b2 - 1];
+                heads[b2 - 1] = tmp;
+            }
+        if (c->out_heads)
+            for (int u = 0; u < r; ++u) c->out_heads[(size_t)rr * r + u] = heads[u];
+        if (c->out_S)
+            for (int j = 0; j < H; ++j) c->out_S[(size_t)rr * H + j] = S[j];
+    }
+
+    double* rs = c->out_rowscore ? c->out_rowscore + (size_t)rr * p->L : NULL;
+    for (int s = 0; s < n; ++s) {
+        widen_key(Kseq + (size_t)s * d, d, key);
+        double R = dot_f64(g, key, d);  /* l = g . k */
+        for (int u = 0; u < r; ++u) {
+            int j = heads[u];
+            double z = dot_q_key(qrow + (size_t)j * d, key, d);
+            double neg = -z;
+            R += (double)wrow[j] * (neg > 0.0 ? neg : 0.0);
+        }
+        cand[s].score = R;
+        cand[s].idx = s;
+        if (rs) rs[s] = R;
+    }
+    if (rs)
+        for (int s = n; s < p->L; ++s) rs[s] = NAN;
+    int kept = select_top(cand, n, c->topk);
+    write_topk(cand, kept, c->topk, c->out_idx + (size_t)rr * c->topk,
+               c->out_score + (size_t)rr * c->topk);
+    free(g); free(key); free(kmax); free(kmin); free(S); free(hc); free(heads); free(cand);
+    return 0;
+}
+
+int oracle_resmisa(const oracle_problem* p, int topk, int block, int r, const int32_t* rows,
+                   int nrows, const int32_t* override_heads, int32_t* out_heads, double* out_S,
+                   double* out_rowscore, int32_t* out_idx, double* out_score, int nthreads)
+{
+    int e = check_problem(p);
+    if (e) return e;
+    if (topk < 1 || r < 0 || r > p->H || (r > 0 && block < 1) || !out_idx || !out_score)
+        return ORACLE_EINVAL;
+    if (!rows) nrows = p->Bt * p->T;
+    resmisa_ctx c = {p, topk, block, r, rows, override_heads, out_heads, out_S, out_rowscore,
+                     out_idx, out_score};
+    return run_rows(resmisa_row, &c, nrows, nthreads);
+}
+
+/* LISA: the linear score alone (ResMiSA with no residual head). */
+int oracle_lisa(const oracle_problem* p, int topk, const int32_t* rows, int nrows,
+                int32_t* out_idx, double* out_score, double* out_rowscore, int nthreads)
+{
+    return oracle_resmisa(p, topk, 0, 0, rows, nrows, NULL, NULL, NULL, out_rowscore, out_idx,
+                          out_score, nthreads);
+}
+
+/* The routing bound of one head over one box: U- = sum_d (q-_d kmax_d -
+ * q+_d kmin_d), fp64 inputs (exposed for the worked example of [PT] 3.2). */
+double oracle_box_bound(const double* q, const double* kmin, const double* kmax, int d)
+{
+    double U = 0.0;
+    for (int x = 0; x < d; ++x) {
+        double qpos = q[x] > 0.0 ? q[x] : 0.0;
+        double qneg = q[x] < 0.0 ? -q[x] : 0.0;
+        U += qneg * kmax[x] - qpos * kmin[x];
+    }
+    return U;
 }

@@ -75,6 +75,22 @@ int oracle_dsa_fp8(const oracle_problem* p, const uint8_t* codes, const float* s
                    const int32_t* rows, int nrows, int32_t* out_idx, double* out_score,
                    double* out_rowscore, int nthreads);
 
+/* LISA ([PT] 3.1): top-k by the linear score l = g . k, g = sum_j w_j q_j. */
+int oracle_lisa(const oracle_problem* p, int topk, const int32_t* rows, int nrows,
+                int32_t* out_idx, double* out_score, double* out_rowscore, int nthreads);
+
+/* ResMiSA ([PT] 3.2): r residual heads routed by S_h = |w_h| max_b ReLU(U-),
+ * extrema over blocks of `block` legal keys; score R = l + sum_{h in A}
+ * w_h ReLU(-(q_h . k)).  r = 0 is LISA.  out_heads [nrows, r] ascending,
+ * out_S [nrows, H], out_rowscore [nrows, L] (NaN past t); each may be NULL.
+ * override_heads [nrows, r] replaces the routing (staged checks). */
+int oracle_resmisa(const oracle_problem* p, int topk, int block, int r, const int32_t* rows,
+                   int nrows, const int32_t* override_heads, int32_t* out_heads, double* out_S,
+                   double* out_rowscore, int32_t* out_idx, double* out_score, int nthreads);
+
+/* U- = sum_d (max(-q_d,0) kmax_d - max(q_d,0) kmin_d) for one head and box. */
+double oracle_box_bound(const double* q, const double* kmin, const double* kmax, int d);
+
 #ifdef __cplusplus
 }
 #endif

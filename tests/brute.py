@@ -105,3 +105,50 @@ def hisa_row(qe, we, ke, i, t, k, b, r):
     cand = [s for m in sorted(blocks) for s in range(m * b, min((m + 1) * b, t + 1))]
     full = {s: score(qe[i], we[i], ke[s]) for s in cand}
     return dict(blocks=blocks, J=J, sel=best_subset(full, cand, k), full=full)
+
+
+def lisa_row(qe, we, ke, i, t, k):
+    """LISA: the per-head linear sum sum_j w_j (q_j . k), exact."""
+    H = len(qe[i])
+    lin = {s: sum((we[i][j] * dot(qe[i][j], ke[s]) for j in range(H)), Fraction(0))
+           for s in range(t + 1)}
+    return best_subset(lin, list(range(t + 1)), k), lin
+
+
+def box_max_negdot(q, lo, hi):
+    """max of -(q . k) over the box lo <= k <= hi, coordinate by coordinate:
+    -q_d k_d is largest at k_d = lo_d when q_d > 0 and at hi_d when q_d < 0."""
+    tot = Fraction(0)
+    for qd, a, b in zip(q, lo, hi):
+        if qd > 0:
+            tot += -qd * a
+        elif qd < 0:
+            tot += -qd * b
+    return tot
+
+
+def resmisa_row(qe, we, ke, i, t, k, block, r):
+    """ResMiSA, exact: route by |w_h| * max over legal blocks of the box
+    maximum of -(q_h . k); score the routed heads through ReLU and the other
+    heads linearly (sum_{h not in A} w_h z_h + sum_{h in A} w_h ReLU(z_h),
+    which equals l + sum_{h in A} w_h ReLU(-z_h))."""
+    H = len(qe[i])
+    nb = t // block + 1
+    S = {}
+    for j in range(H):
+        best = Fraction(0)
+        for m in range(nb):
+            keys = ke[m * block:min((m + 1) * block, t + 1)]
+            lo = [min(v[x] for v in keys) for x in range(len(keys[0]))]
+            hi = [max(v[x] for v in keys) for x in range(len(keys[0]))]
+            best = max(best, abs(we[i][j]) * relu(box_max_negdot(qe[i][j], lo, hi)))
+        S[j] = best
+    heads = best_subset(S, list(range(H)), r) if r else frozenset()
+    R = {}
+    for s in range(t + 1):
+        tot = Fraction(0)
+        for j in range(H):
+            z = dot(qe[i][j], ke[s])
+            tot += we[i][j] * (relu(z) if j in heads else z)
+        R[s] = tot
+    return dict(heads=heads, S=S, sel=best_subset(R, list(range(t + 1)), k), R=R)
