@@ -180,6 +180,55 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
                      int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------- LISA / ResMiSA */
+
+/* Workspace bytes for lisa_score_topk. */
+int lisa_score_topk_ws(const sa_shape* s, size_t* ws_bytes);
+
+/* LISA linear score (PaperTrace "2.2.2 MISA, LISA and ResMiSA", section 3.1):
+ * with the fused query g_t = sum_j w_j q_j (one key shared by every head),
+ *   l[t,s] = g_t . k_s
+ * for every legal key s <= t, then the top-k by l with the selection rules of
+ * indexer_score_topk; out_score = l.  g is formed in fp32 and carried as a
+ * bf16 hi/lo pair (~2^-16 relative).  Any T; arguments, ownership and errors
+ * as in indexer_score_topk. */
+int lisa_score_topk(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+                    int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* Per-block key extrema, the cache-side state of ResMiSA's routing bound.
+ * Block m covers keys [m*block, min((m+1)*block, L)).  out: [batch,
+ * ceil(L/block), 2, d] bf16 bit patterns: per block the per-dimension maximum,
+ * then the minimum (exact: extrema of bf16 values). */
+int sa_block_extrema(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, int32_t block,
+                     uint16_t* out, void* stream);
+
+/* Workspace bytes for resmisa_route.  extrema_given: whether `extrema` will
+ * be passed (non-NULL) to resmisa_route. */
+int resmisa_route_ws(const sa_shape* s, int32_t block, int32_t r, int32_t extrema_given,
+                     size_t* ws_bytes);
+
+/* ResMiSA / MISA-2 (same page, section 3.2): the shared linear score plus r
+ * routed residual heads,
+ *   R[t,s] = l[t,s] + sum_{h in A_t} w_h * ReLU(-(q_h . k_s)),
+ * then the top-k by R (selection rules of indexer_score_topk; out_score = R).
+ *   block    size of the blocks whose key extrema bound the residuals.
+ *   r        residual heads per query, 0 <= r <= H; 4 + r must be <= 64
+ *            unless r == H (SA_EUNSUPPORTED otherwise).  r = 0 is LISA,
+ *            r = H the DSA score.  Routing: for every block b that
+ *            intersects [0, t] (a block cut by the causal bound uses the
+ *            extrema of its legal keys) and head h,
+ *              U-[h,b] = sum_d (max(-q_hd,0) kmax_bd - max(q_hd,0) kmin_bd),
+ *            S_h = |w_h| max_b ReLU(U-[h,b]); A_t = the r largest S_h
+ *            (ties -> lower head).
+ *   extrema  NULL (computed inside the call) or sa_block_extrema(keys, ...,
+ *            block) output for these keys.
+ *   out_heads [batch, T, r] routed heads, ascending (nullable).
+ * Other arguments, ownership and errors as in indexer_score_topk. */
+int resmisa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+                  int32_t block, int32_t r, const uint16_t* extrema, int32_t* out_heads,
+                  int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------ diagnostics */
 
 /* Message for the last non-zero return on the calling thread ("" if none). */

@@ -33,7 +33,8 @@ EXPORTS = (
     "misa_route_ws", "misa_route", "hisa_coarse_fine_ws", "hisa_coarse_fine",
     "sa_last_error", "sa_profile_enable", "sa_profile_read", "sa_kernel_count",
     "sa_kernel_name", "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws",
-    "indexer_score_topk_fp8",
+    "indexer_score_topk_fp8", "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema",
+    "resmisa_route_ws", "resmisa_route",
 )
 
 
@@ -72,6 +73,11 @@ def load():
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
     lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
+    lib.lisa_score_topk_ws.argtypes = [SP, ctypes.POINTER(S)]
+    lib.lisa_score_topk.argtypes = [P, P, P, SP, P, P, P, S, P]
+    lib.sa_block_extrema.argtypes = [P, I, I, I, I, P, P]
+    lib.resmisa_route_ws.argtypes = [SP, I, I, I, ctypes.POINTER(S)]
+    lib.resmisa_route.argtypes = [P, P, P, SP, I, I, P, P, P, P, P, S, P]
     lib.sa_last_error.restype = ctypes.c_char_p
     lib.sa_profile_enable.argtypes = [I]
     lib.sa_profile_read.argtypes = [I, ctypes.POINTER(ctypes.c_double),
@@ -82,7 +88,9 @@ def load():
     for name in ("indexer_score_topk_ws", "indexer_score_topk", "sa_pool_blocks",
                  "sa_pool_blocks2", "misa_route_ws", "misa_route", "hisa_coarse_fine_ws",
                  "hisa_coarse_fine", "sa_profile_enable", "sa_profile_read",
-                 "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws", "indexer_score_topk_fp8"):
+                 "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws", "indexer_score_topk_fp8",
+                 "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema", "resmisa_route_ws",
+                 "resmisa_route"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -289,6 +297,61 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
                                          _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                          _stream(q.device)), "indexer_score_topk_fp8")
     return out_idx, out_score
+
+
+# ------------------------------------------------------- LISA / ResMiSA
+
+def lisa_score_topk_ws(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    _check(load().lisa_score_topk_ws(ctypes.byref(shape), ctypes.byref(n)), "lisa_score_topk_ws")
+    return n.value
+
+
+def lisa_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=None,
+                    want_score=True, ws=None):
+    """LISA: top-k by the linear score g . k, g = sum_j w_j q_j."""
+    s = _shape(q, w, keys, causal_offset, topk)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    ws = _workspace(lisa_score_topk_ws(s), q.device, ws)
+    _check(load().lisa_score_topk(_p(q), _p(w), _p(keys), ctypes.byref(s), _p(out_idx),
+                                  _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
+           "lisa_score_topk")
+    return out_idx, out_score
+
+
+def block_extrema(keys, block, out=None):
+    """Per-block key max then min -> [batch, ceil(L/block), 2, 128] bf16 bits."""
+    _bf16(keys, "keys", 3)
+    B, L, d = keys.shape
+    nb = (L + block - 1) // block
+    if out is None:
+        out = torch.empty((B, nb, 2, d), dtype=torch.int16, device=keys.device)
+    _check(load().sa_block_extrema(_p(keys), B, L, d, int(block), _p(out), _stream(keys.device)),
+           "sa_block_extrema")
+    return out
+
+
+def resmisa_route_ws(shape: Shape, block, r, extrema_given) -> int:
+    n = ctypes.c_size_t()
+    _check(load().resmisa_route_ws(ctypes.byref(shape), int(block), int(r),
+                                   int(bool(extrema_given)), ctypes.byref(n)), "resmisa_route_ws")
+    return n.value
+
+
+def resmisa_route(q, w, keys, causal_offset, topk, block, r, extrema=None, want_heads=True,
+                  out_idx=None, out_score=None, want_score=True, ws=None):
+    """ResMiSA: shared linear score + r routed residual heads.  Returns
+    (idx, score, heads)."""
+    s = _shape(q, w, keys, causal_offset, topk)
+    B, T = q.shape[0], q.shape[1]
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    heads = (torch.empty((B, T, r), dtype=torch.int32, device=q.device)
+             if (want_heads and r > 0) else None)
+    ws = _workspace(resmisa_route_ws(s, block, r, extrema is not None), q.device, ws)
+    _check(load().resmisa_route(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block), int(r),
+                                _p(extrema), _p(heads), _p(out_idx), _p(out_score), _p(ws),
+                                ws.numel(), _stream(q.device)), "resmisa_route")
+    return out_idx, out_score, heads
 
 
 # ------------------------------------------------------------ diagnostics

@@ -65,7 +65,7 @@ void drain_records() {
 const char* kKernelNames[sa::K_COUNT] = {
     "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
     "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused",
-    "quantize_fp8", "scan_dsa_fp8"};
+    "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows"};
 
 // ------------------------------------------------------------ workspace
 
@@ -456,6 +456,184 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
                                   s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
                                   codes, scales);
     if (e != hipSuccess) return hip_fail(e, "fp8 decode scan");
+    return SA_OK;
+}
+
+// ------------------------------------------------------- LISA / ResMiSA
+
+// Head rows per query row: the four linear heads (g' hi/lo, both signs) plus
+// the r routed heads; with r == H, g' is zero and only the H heads remain.
+static int resmisa_heads(int H, int r) { return r == H ? H : 4 + r; }
+
+struct ResPlan {
+    uint16_t* qp;
+    float* wp;
+    uint32_t* smax;
+    uint16_t* ext;
+    uint16_t* tail;
+    uint8_t* flag;
+    DsaPlan dsa;
+    size_t bytes;
+};
+
+static ResPlan plan_resmisa(const sa_shape* s, int block, int r, bool ext_given, bool partial,
+                            void* ws) {
+    ResPlan p{};
+    Carve cv(ws);
+    const long long rows = (long long)s->batch * s->T;
+    const int Hp = resmisa_heads(s->H, r);
+    p.qp = cv.take<uint16_t>(rows * Hp * sa::kD);
+    p.wp = cv.take<float>(rows * Hp);
+    if (r > 0) {
+        const long long nblk = ((long long)s->L + block - 1) / block;
+        p.smax = cv.take<uint32_t>(rows * s->H);
+        if (!ext_given) p.ext = cv.take<uint16_t>((long long)s->batch * nblk * 2 * sa::kD);
+        if (partial) {
+            p.tail = cv.take<uint16_t>(rows * 2 * sa::kD);
+            p.flag = cv.take<uint8_t>(rows);
+        }
+    }
+    const size_t off = (cv.off + 255) & ~size_t(255);
+    sa_shape s2 = *s;
+    s2.H = Hp;
+    p.dsa = plan_dsa(&s2, ws ? static_cast<char*>(ws) + off : nullptr);
+    p.bytes = off + p.dsa.bytes;
+    return p;
+}
+
+static int check_resmisa(const sa_shape* s, int block, int r) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (r < 0 || r > s->H) return fail(SA_EINVAL, "need 0 <= r <= H");
+    if (r > 0 && block < 1) return fail(SA_EINVAL, "block must be >= 1");
+    if (resmisa_heads(s->H, r) > sa::kMaxH)
+        return fail(SA_EUNSUPPORTED, "4 + r head rows must fit in 64 (r <= 60, or r == H)");
+    return SA_OK;
+}
+
+// LISA (r = 0) and ResMiSA: head rows, then the DSA score path on them.
+static int run_resmisa(const uint16_t* q, const float* w, const uint16_t* keys,
+                       const sa_shape* s, int block, int r, const uint16_t* extrema,
+                       int32_t* out_heads, int32_t* out_idx, float* out_score, void* ws,
+                       size_t ws_bytes, void* stream) {
+    const bool partial = r > 0 && any_partial(s, block);
+    const size_t need = plan_resmisa(s, block, r, extrema != nullptr, partial, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    ResPlan p = plan_resmisa(s, block, r, extrema != nullptr, partial, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int rows = s->batch * s->T;
+    const int Hp = resmisa_heads(s->H, r);
+    sa::ResmisaArgs a{};
+    a.q = q;
+    a.w = w;
+    a.T = s->T;
+    a.H = s->H;
+    a.offset = s->causal_offset;
+    a.block = block;
+    a.nblk = r > 0 ? (s->L + block - 1) / block : 0;
+    a.r = r;
+    a.Hp = Hp;
+    a.smax = p.smax;
+    a.heads_out = out_heads;
+    a.qp = p.qp;
+    a.wp = p.wp;
+    hipError_t e;
+    if (r > 0) {
+        e = sa::launch_fill_u32(p.smax, (long long)rows * s->H, 0u, st);
+        if (e != hipSuccess) return hip_fail(e, "fill");
+        if (!extrema) {
+            e = sa::launch_extrema(keys, s->batch, s->L, block, p.ext, st);
+            if (e != hipSuccess) return hip_fail(e, "block extrema");
+        }
+        a.ext = extrema ? extrema : p.ext;
+        if (partial) {
+            e = sa::launch_extrema_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset,
+                                        s->L, block, rows, p.tail, p.flag, st);
+            if (e != hipSuccess) return hip_fail(e, "cut-block extrema");
+            a.tail = p.tail;
+            a.tail_flag = p.flag;
+        }
+        e = sa::launch_resmisa_router(a, rows, st);
+        if (e != hipSuccess) return hip_fail(e, "residual routing");
+    }
+    e = sa::launch_head_rows(a, rows, st);
+    if (e != hipSuccess) return hip_fail(e, "head rows");
+    sa_shape s2 = *s;
+    s2.H = Hp;
+    if (p.dsa.prefill) {
+        sa::PrefillArgs pa{};
+        pa.q = p.qp;
+        pa.w = p.wp;
+        pa.keys = keys;
+        pa.T = s->T;
+        pa.H = Hp;
+        pa.L = s->L;
+        pa.offset = s->causal_offset;
+        pa.k = s->topk;
+        pa.surv = p.dsa.surv;
+        pa.cap = score_stride(s->causal_offset + s->T);
+        pa.out_idx = out_idx;
+        pa.out_score = out_score;
+        pa.out_stride = s->topk;
+        e = sa::launch_prefill(pa, rows, st);
+        if (e != hipSuccess) return hip_fail(e, "prefill");
+    } else {
+        e = run_dense_topk(p.qp, p.wp, keys, &s2, nullptr, 0, p.dsa.scores, p.dsa.state,
+                           p.dsa.cand, s->topk, out_idx, out_score, st);
+        if (e != hipSuccess) return hip_fail(e, "decode scan");
+    }
+    return SA_OK;
+}
+
+int lisa_score_topk_ws(const sa_shape* s, size_t* ws_bytes) {
+    int rc = check_resmisa(s, 1, 0);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_resmisa(s, 1, 0, false, false, nullptr).bytes;
+    return SA_OK;
+}
+
+int lisa_score_topk(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+                    int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                    void* stream) {
+    int rc = check_resmisa(s, 1, 0);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    return run_resmisa(q, w, keys, s, 1, 0, nullptr, nullptr, out_idx, out_score, ws, ws_bytes,
+                       stream);
+}
+
+int resmisa_route_ws(const sa_shape* s, int32_t block, int32_t r, int32_t extrema_given,
+                     size_t* ws_bytes) {
+    int rc = check_resmisa(s, block, r);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_resmisa(s, block, r, extrema_given != 0, r > 0 && any_partial(s, block),
+                             nullptr)
+                    .bytes;
+    return SA_OK;
+}
+
+int resmisa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+                  int32_t block, int32_t r, const uint16_t* extrema, int32_t* out_heads,
+                  int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_resmisa(s, block, r);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    return run_resmisa(q, w, keys, s, block, r, extrema, r > 0 ? out_heads : nullptr, out_idx,
+                       out_score, ws, ws_bytes, stream);
+}
+
+int sa_block_extrema(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, int32_t block,
+                     uint16_t* out, void* stream) {
+    if (!keys || !out) return fail(SA_EINVAL, "keys and out must be non-NULL");
+    if (batch < 1 || L < 1 || block < 1) return fail(SA_EINVAL, "batch, L and block must be >= 1");
+    if (d != sa::kD) return fail(SA_EUNSUPPORTED, "d must be 128");
+    hipError_t e = sa::launch_extrema(keys, batch, L, block, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "block extrema");
     return SA_OK;
 }
 

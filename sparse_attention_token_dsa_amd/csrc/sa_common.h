@@ -125,6 +125,9 @@ enum KernelId {
     K_PREFILL,
     K_QUANT8,
     K_SCAN8,
+    K_EXTREMA,
+    K_RES_ROUTER,
+    K_HEAD_ROWS,
     K_COUNT
 };
 
@@ -185,6 +188,22 @@ struct RouterArgs {
     float* E_out;           // [rows, H] or null
 };
 
+// LISA / ResMiSA head rows and routing.
+struct ResmisaArgs {
+    const uint16_t* q;      // [rows, H, 128]
+    const float* w;         // [rows, H]
+    const uint16_t* ext;    // [batch, nblk, 2, 128]: per-block key max, then min
+    const uint16_t* tail;   // [rows, 2, 128] extrema of a cut last block, or null
+    const uint8_t* tail_flag;
+    int T, H, offset, block, nblk;
+    int r;                  // routed residual heads (0: LISA)
+    int Hp;                 // output heads per row: 4 + r, or H when r == H
+    uint32_t* smax;         // [rows, H] zeroed: max_b ReLU(U-) as float bits
+    int32_t* heads_out;     // [rows, r] ascending, or null
+    uint16_t* qp;           // [rows, Hp, 128] output head rows
+    float* wp;              // [rows, Hp] output weights
+};
+
 struct TopkArgs {
     // dense source: scores[row * dense_stride + s], s < n(row)
     const float* dense;
@@ -242,6 +261,14 @@ hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16
 hipError_t launch_pool2(const uint16_t* keys, int batch, int L, int small, int large,
                         uint16_t* out_small, uint16_t* out_large, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s);
+// LISA / ResMiSA: block extrema, cut-block extrema, routing, head rows.
+hipError_t launch_extrema(const uint16_t* keys, int batch, int L, int block, uint16_t* out,
+                          hipStream_t s);
+hipError_t launch_extrema_tail(const uint16_t* keys, long long seq_stride, int T, int offset,
+                               int L, int block, int rows, uint16_t* tail, uint8_t* flag,
+                               hipStream_t s);
+hipError_t launch_resmisa_router(const ResmisaArgs& a, int rows, hipStream_t s);
+hipError_t launch_head_rows(const ResmisaArgs& a, int rows, hipStream_t s);
 // Per-key FP8 quantization of n keys of 128 bf16 values.
 hipError_t launch_quantize_fp8(const uint16_t* keys, long long n, uint8_t* codes, float* scales,
                                hipStream_t s);

@@ -144,6 +144,44 @@ def check_dsa_fp8(p, codes, scales, k, gidx, gsc, rows):
     return swaps
 
 
+def _check_rows(p, k, gidx, gsc, rows, ref_idx, ref_sc, rowscore, what):
+    gi = gidx.reshape(-1, k)
+    gs = None if gsc is None else gsc.reshape(-1, k)
+    swaps = 0
+    for u, row in enumerate(rows):
+        t = t_of_row(p, row)
+        srow = rowscore[u, : t + 1]
+        tol = TOL_REL * np.max(np.abs(srow))
+        swaps += check_set(gi[row], None if gs is None else gs[row], ref_idx[u], ref_sc[u],
+                           lambda s, srow=srow: srow[s], t + 1, k, tol, t=t,
+                           what="%s row %d" % (what, row))
+    return swaps
+
+
+def check_lisa(p, k, gidx, gsc, rows):
+    """LISA: against the oracle's linear score g . k."""
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    oidx, osc, rs = oracle.lisa(prob, k, rows=rows, want_rowscore=True)
+    return _check_rows(p, k, gidx, gsc, rows, oidx, osc, rs, "lisa")
+
+
+def check_resmisa(p, k, block, r, gidx, gsc, gheads, rows):
+    """ResMiSA: the routed heads by the near-tie rule on S, then the tokens
+    against the oracle run with the GPU's heads."""
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    over = None
+    if r > 0:
+        base = oracle.resmisa(prob, k, block, r, rows=rows)
+        gh = gheads.reshape(-1, r)
+        for u, row in enumerate(rows):
+            assert np.all(np.diff(gh[row]) > 0), "resmisa heads row %d not ascending" % row
+            check_choice(gh[row], base["S"][u], p["H"], r, "resmisa heads row %d" % row)
+        over = np.ascontiguousarray(gh[rows])
+    staged = oracle.resmisa(prob, k, block, r, rows=rows, override_heads=over, want_rowscore=True)
+    return _check_rows(p, k, gidx, gsc, rows, staged["idx"], staged["score"], staged["rowscore"],
+                       "resmisa")
+
+
 def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows):
     prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
     base = oracle.misa(prob, k, B, h, kprime=0, rows=rows)
