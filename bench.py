@@ -275,6 +275,8 @@ def main():
     }
 
     result["fp8"] = bench_fp8(api, torch, dev, q, w, K, shape, flush, args.steps)
+    result["lisa"], result["resmisa"] = bench_lisa_resmisa(api, torch, dev, q, w, K, shape, flush,
+                                                           args.steps)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(api, synth, torch, np, dev, args.prefill_iters)
@@ -351,6 +353,73 @@ def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
                          "algorithmic_bytes_per_launch": scan_bytes, "avg_us": round(us, 2)},
             "quantize": {"avg_us": round(q_us, 2), "algorithmic_bytes_per_launch": q_bytes,
                          "GB/s": round(q_bytes / (q_us * 1e-6) / 1e9, 1)}}
+
+
+def flushed_calls(api, torch, call, flush, steps):
+    """Per-call time (events around each call, after a cache flush) and the
+    library's per-kernel event averages over the same calls."""
+    settle(call, torch, torch.device("cuda:0"))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    api.profile_enable(True)
+    for e0, e1 in evs:
+        flush()
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    kern = api.profile_read()
+    api.profile_enable(False)
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+    return ms, {n: 1e3 * tt / c for n, (tt, c) in kern.items()}
+
+
+def bench_lisa_resmisa(api, torch, dev, q, w, K, shape, flush, steps):
+    """LISA (linear score g . k) and ResMiSA (block 128, r = 7 residual heads,
+    extrema given as cache-side state) on the same decode batch."""
+    Bt, L, H, d, off, k = shape.batch, shape.L, shape.H, shape.d, shape.causal_offset, shape.topk
+    block, r = 128, 7
+    oi = torch.empty((Bt, 1, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, 1, k), dtype=torch.float32, device=dev)
+    ws_l = torch.empty(api.lisa_score_topk_ws(shape), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(api.resmisa_route_ws(shape, block, r, True), dtype=torch.uint8, device=dev)
+    ext = api.block_extrema(K, block)
+    heads = torch.empty((Bt, 1, r), dtype=torch.int32, device=dev)
+
+    def lisa():
+        api.lisa_score_topk(q, w, K, off, k, oi, osc, ws=ws_l)
+
+    def resmisa():
+        api.resmisa_route(q, w, K, off, k, block, r, extrema=ext, out_heads=heads, out_idx=oi,
+                          out_score=osc, ws=ws_r)
+
+    def ext_pass():
+        api.block_extrema(K, block, out=ext)
+
+    scan_nbytes = lambda hp: Bt * L * d * 2 + Bt * hp * d * 2 + Bt * hp * 4 + Bt * L * 4
+    out = []
+    for name, call, hp in (("lisa", lisa, 4), ("resmisa", resmisa, 4 + r)):
+        ms, kus = flushed_calls(api, torch, call, flush, steps)
+        nb = scan_nbytes(hp)
+        gbs = nb / (kus["scan_dsa"] * 1e-6) / 1e9
+        o = {"workload": "decode_128k_b8_h64_" + name, "cache": "cold: a 1 GiB read before each call",
+             "ms_per_call": ms, "scores_per_s": Bt * L / (ms * 1e-3),
+             "kernels_us": {n: round(v, 2) for n, v in kus.items()},
+             "head_rows": hp,
+             "roofline": {"kernel": "scan_dsa", "bound": "hbm", "achieved": round(gbs, 1),
+                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                          "algorithmic_bytes_per_launch": nb,
+                          "avg_us": round(kus["scan_dsa"], 2)}}
+        if name == "resmisa":
+            o["config"] = {"block": block, "r": r, "extrema": "given (cache-side state)"}
+            ems, ekus = flushed_calls(api, torch, ext_pass, flush, steps)
+            eb = Bt * L * d * 2 + Bt * (L // block) * 2 * d * 2
+            o["extrema_pass"] = {"avg_us": round(ekus["block_extrema"], 2),
+                                 "algorithmic_bytes_per_launch": eb,
+                                 "GB/s": round(eb / (ekus["block_extrema"] * 1e-6) / 1e9, 1)}
+        out.append(o)
+    return out[0], out[1]
 
 
 def bench_prefill(api, synth, torch, np, dev, iters):

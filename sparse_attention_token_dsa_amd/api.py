@@ -339,14 +339,15 @@ def resmisa_route_ws(shape: Shape, block, r, extrema_given) -> int:
 
 
 def resmisa_route(q, w, keys, causal_offset, topk, block, r, extrema=None, want_heads=True,
-                  out_idx=None, out_score=None, want_score=True, ws=None):
+                  out_heads=None, out_idx=None, out_score=None, want_score=True, ws=None):
     """ResMiSA: shared linear score + r routed residual heads.  Returns
     (idx, score, heads)."""
     s = _shape(q, w, keys, causal_offset, topk)
     B, T = q.shape[0], q.shape[1]
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    heads = (torch.empty((B, T, r), dtype=torch.int32, device=q.device)
-             if (want_heads and r > 0) else None)
+    heads = out_heads
+    if heads is None and want_heads and r > 0:
+        heads = torch.empty((B, T, r), dtype=torch.int32, device=q.device)
     ws = _workspace(resmisa_route_ws(s, block, r, extrema is not None), q.device, ws)
     _check(load().resmisa_route(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block), int(r),
                                 _p(extrema), _p(heads), _p(out_idx), _p(out_score), _p(ws),

@@ -147,15 +147,20 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
 }
 
 // Decode-style path: score rows (+ row state), filter, finish.
+// state_zeroed: the caller's previous kernel on the stream already cleared
+// the row state.
 hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                           const sa_shape* s, const int32_t* heads, int hsel, float* scores,
                           uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
                           float* out_score, hipStream_t st, const uint8_t* codes = nullptr,
-                          const float* kscale = nullptr) {
+                          const float* kscale = nullptr, bool state_zeroed = false) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
-    hipError_t e = sa::launch_fill_u32(state, rows * sa::kRowState, 0u, st);
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (!state_zeroed) {
+        e = sa::launch_fill_u32(state, rows * sa::kRowState, 0u, st);
+        if (e != hipSuccess) return e;
+    }
     sa::ScanArgs a{};
     a.q = q;
     a.w = w;
@@ -465,10 +470,16 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
 // the r routed heads; with r == H, g' is zero and only the H heads remain.
 static int resmisa_heads(int H, int r) { return r == H ? H : 4 + r; }
 
+// Router workgroups per row: 64 blocks each over the widest row's legal blocks.
+static int resmisa_chunks(const sa_shape* s, int block) {
+    const long long maxnb = ((long long)s->causal_offset + s->T - 1) / block + 1;
+    return (int)((maxnb + 63) / 64);
+}
+
 struct ResPlan {
     uint16_t* qp;
     float* wp;
-    uint32_t* smax;
+    float* part;
     uint16_t* ext;
     uint16_t* tail;
     uint8_t* flag;
@@ -486,7 +497,7 @@ static ResPlan plan_resmisa(const sa_shape* s, int block, int r, bool ext_given,
     p.wp = cv.take<float>(rows * Hp);
     if (r > 0) {
         const long long nblk = ((long long)s->L + block - 1) / block;
-        p.smax = cv.take<uint32_t>(rows * s->H);
+        p.part = cv.take<float>(rows * resmisa_chunks(s, block) * s->H);
         if (!ext_given) p.ext = cv.take<uint16_t>((long long)s->batch * nblk * 2 * sa::kD);
         if (partial) {
             p.tail = cv.take<uint16_t>(rows * 2 * sa::kD);
@@ -534,14 +545,14 @@ static int run_resmisa(const uint16_t* q, const float* w, const uint16_t* keys,
     a.nblk = r > 0 ? (s->L + block - 1) / block : 0;
     a.r = r;
     a.Hp = Hp;
-    a.smax = p.smax;
+    a.part = p.part;
+    a.nchunk = r > 0 ? resmisa_chunks(s, block) : 0;
     a.heads_out = out_heads;
     a.qp = p.qp;
     a.wp = p.wp;
+    a.zero_state = p.dsa.prefill ? nullptr : p.dsa.state;
     hipError_t e;
     if (r > 0) {
-        e = sa::launch_fill_u32(p.smax, (long long)rows * s->H, 0u, st);
-        if (e != hipSuccess) return hip_fail(e, "fill");
         if (!extrema) {
             e = sa::launch_extrema(keys, s->batch, s->L, block, p.ext, st);
             if (e != hipSuccess) return hip_fail(e, "block extrema");
@@ -580,7 +591,8 @@ static int run_resmisa(const uint16_t* q, const float* w, const uint16_t* keys,
         if (e != hipSuccess) return hip_fail(e, "prefill");
     } else {
         e = run_dense_topk(p.qp, p.wp, keys, &s2, nullptr, 0, p.dsa.scores, p.dsa.state,
-                           p.dsa.cand, s->topk, out_idx, out_score, st);
+                           p.dsa.cand, s->topk, out_idx, out_score, st, nullptr, nullptr,
+                           /*state_zeroed=*/true);
         if (e != hipSuccess) return hip_fail(e, "decode scan");
     }
     return SA_OK;

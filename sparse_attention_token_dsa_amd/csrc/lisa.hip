@@ -98,11 +98,21 @@ __global__ __launch_bounds__(256) void extrema_tail_kernel(const uint16_t* keys,
 
 // ---------------------------------------------------------- router
 
-// Grid (ceil(nblk / 64), rows); 4 waves x 16 blocks.  For every head h and
-// legal block m of the workgroup: U = [q-_h | -q+_h] . [kmax_m | kmin_m] on
-// the MFMA (8 k-steps of 32), ReLU, max over the blocks; the row maximum per
-// head is merged into Smax[row][h] with an atomic max on the float bits
-// (non-negative floats order like their bits).
+// Max over the 16 lanes of a DPP row (lanes 16g .. 16g+15), in every lane:
+// row rotations by 8, 4, 2, 1.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false)));
+    return v;
+}
+
+// Grid (nchunk, rows); 4 waves x 16 blocks.  For every head h and legal
+// block m of the workgroup: U = [q-_h | -q+_h] . [kmax_m | kmin_m] on the
+// MFMA (8 k-steps of 32), ReLU, max over the blocks; the workgroup's maximum
+// per head goes to part[row][chunk][h].  Workgroups past the row's legal
+// blocks write nothing: the reader takes only the row's own chunks.
 template <int NHT>
 __global__ __launch_bounds__(256) void resmisa_router_kernel(ResmisaArgs a) {
     const int row = blockIdx.y;
@@ -173,9 +183,7 @@ __global__ __launch_bounds__(256) void resmisa_router_kernel(ResmisaArgs a) {
     for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float v = legal ? fmaxf(acc[ht][i], 0.f) : 0.f;
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 16));
+            const float v = row16_max(legal ? fmaxf(acc[ht][i], 0.f) : 0.f);
             if (c == 0) wmax[wid][ht * 16 + 4 * g + i] = v;
         }
     __syncthreads();
@@ -183,29 +191,55 @@ __global__ __launch_bounds__(256) void resmisa_router_kernel(ResmisaArgs a) {
         const int h = threadIdx.x;
         float v = wmax[0][h];
         for (int u = 1; u < 4; ++u) v = fmaxf(v, wmax[u][h]);
-        if (v > 0.f) atomicMax(a.smax + (long long)row * a.H + h, __float_as_uint(v));
+        a.part[((long long)row * a.nchunk + blockIdx.x) * a.H + h] = v;
     }
 }
 
 // ----------------------------------------------------- head rows
 
-// One workgroup of 128 threads per query row.  Routed heads (r > 0): the r
-// largest S_h = |w_h| Smax_h, ties to the lower head, listed in ascending
-// order.  Thread x then forms g'_x = sum over the other heads (ascending) of
-// w_h q_{h,x} in fp32 and writes dim x of every output head row.
+// One workgroup of 128 threads per query row.  The row's q (H x 128 bf16,
+// 16 KiB at H = 64) and w go to LDS first, every 16-byte load issued before
+// any is used.  Routed heads (r > 0): the r largest S_h = |w_h| max_b
+// ReLU(U-) (the max over the router workgroups that cover the row's legal
+// blocks), ties to the lower head, listed in ascending order.  Thread x then forms
+// g'_x = sum over the other heads (ascending) of w_h q_{h,x} in fp32 and
+// writes dim x of every output head row.  With zero_state it also clears the
+// row's state for the decode scan (one launch fewer on the decode path).
 __global__ __launch_bounds__(128) void head_rows_kernel(ResmisaArgs a) {
     const int row = blockIdx.x;
     const int H = a.H, r = a.r;
-    __shared__ float sS[64];
-    __shared__ int inA[64];
-    __shared__ int list[64];
+    __shared__ uint4 sq4[kMaxH * kD / 8];
+    __shared__ float sw[kMaxH], sS[kMaxH];
+    __shared__ int inA[kMaxH];
+    __shared__ int list[kMaxH];
+    const uint16_t* sq = reinterpret_cast<const uint16_t*>(sq4);
     const float* wrow = a.w + (long long)row * H;
-    const uint16_t* qrow = a.q + (long long)row * H * kD;
+    const uint4* q4 = reinterpret_cast<const uint4*>(a.q + (long long)row * H * kD);
+    const int n4 = H * kD / 8;
+    uint4 tmp[kMaxH * kD / 8 / 128];
+#pragma unroll
+    for (int i = 0; i < kMaxH * kD / 8 / 128; ++i) {
+        const int idx = threadIdx.x + i * 128;
+        tmp[i] = idx < n4 ? q4[idx] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float wv = 0.f, sv = 0.f;
     if (threadIdx.x < H) {
-        const int h = threadIdx.x;
-        float sv = 0.f;  // smax is null for LISA (r = 0)
-        if (r > 0) sv = __uint_as_float(a.smax[(long long)row * H + h]) * fabsf(wrow[h]);
-        sS[h] = sv;
+        wv = wrow[threadIdx.x];
+        if (r > 0) {  // part is null for LISA (r = 0)
+            const int t = a.offset + row % a.T;
+            const int nc = (t / a.block + 1 + 63) / 64;
+            const float* pr = a.part + (long long)row * a.nchunk * H + threadIdx.x;
+            float m = 0.f;
+#pragma unroll 8
+            for (int c2 = 0; c2 < nc; ++c2) m = fmaxf(m, pr[(long long)c2 * H]);
+            sv = m * fabsf(wv);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxH * kD / 8 / 128; ++i) sq4[threadIdx.x + i * 128] = tmp[i];
+    if (threadIdx.x < kMaxH) {
+        sw[threadIdx.x] = wv;
+        sS[threadIdx.x] = sv;
     }
     __syncthreads();
     if (threadIdx.x < H) {
@@ -232,8 +266,11 @@ __global__ __launch_bounds__(128) void head_rows_kernel(ResmisaArgs a) {
     float* wo = a.wp + (long long)row * a.Hp;
     if (linear) {
         float gx = 0.f;
-        for (int h = 0; h < H; ++h)
-            if (!inA[h]) gx = fmaf(wrow[h], bf16_bits_to_f32(qrow[(long long)h * kD + x]), gx);
+#pragma unroll 8
+        for (int h = 0; h < H; ++h) {
+            const float wh = inA[h] ? 0.f : sw[h];  // routed heads leave the linear term
+            gx = fmaf(wh, bf16_bits_to_f32(sq[h * kD + x]), gx);
+        }
         const uint32_t hi = f32_to_bf16_bits(gx);
         const uint32_t lo = f32_to_bf16_bits(gx - bf16_bits_to_f32(hi));
         qo[0 * kD + x] = (uint16_t)hi;
@@ -242,11 +279,15 @@ __global__ __launch_bounds__(128) void head_rows_kernel(ResmisaArgs a) {
         qo[3 * kD + x] = (uint16_t)(lo ^ 0x8000u);
         if (x < 4) wo[x] = x < 2 ? 1.f : -1.f;
     }
+#pragma unroll 4
     for (int u = 0; u < r; ++u) {
         const int h = list[u];
-        qo[(long long)(nlin + u) * kD + x] = qrow[(long long)h * kD + x];
-        if (x == 0) wo[nlin + u] = wrow[h];
+        qo[(long long)(nlin + u) * kD + x] = sq[h * kD + x];
+        if (x == 0) wo[nlin + u] = sw[h];
     }
+    // The decode scan that follows adds its histogram into a zeroed row state.
+    if (a.zero_state)
+        for (int u = x; u < kRowState; u += 128) a.zero_state[(long long)row * kRowState + u] = 0u;
 }
 
 }  // namespace
@@ -272,8 +313,7 @@ hipError_t launch_extrema_tail(const uint16_t* keys, long long seq_stride, int T
 }
 
 hipError_t launch_resmisa_router(const ResmisaArgs& a, int rows, hipStream_t s) {
-    const int maxnb = (a.offset + a.T - 1) / a.block + 1;
-    const dim3 grid((unsigned)((maxnb + 63) / 64), (unsigned)rows);
+    const dim3 grid((unsigned)a.nchunk, (unsigned)rows);
     const int nht = (a.H + 15) / 16;
     prof_begin(K_RES_ROUTER, s);
     switch (nht) {

@@ -198,10 +198,12 @@ struct ResmisaArgs {
     int T, H, offset, block, nblk;
     int r;                  // routed residual heads (0: LISA)
     int Hp;                 // output heads per row: 4 + r, or H when r == H
-    uint32_t* smax;         // [rows, H] zeroed: max_b ReLU(U-) as float bits
+    float* part;            // [rows, nchunk, H]: max_b ReLU(U-) per router workgroup
+    int nchunk;             // router workgroups per row (64 blocks each)
     int32_t* heads_out;     // [rows, r] ascending, or null
     uint16_t* qp;           // [rows, Hp, 128] output head rows
     float* wp;              // [rows, Hp] output weights
+    uint32_t* zero_state;   // [rows, kRowState] to clear for the decode scan, or null
 };
 
 struct TopkArgs {
