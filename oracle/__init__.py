@@ -51,7 +51,7 @@ def _load():
         i = ctypes.c_int
         _lib.oracle_dsa.argtypes = [P, i, P, i, P, P, P, i]
         _lib.oracle_misa.argtypes = [P, i, i, i, i, P, i, P, P, P, P, P, P, P, P, i]
-        _lib.oracle_hisa.argtypes = [P, i, i, i, P, i, P, P, P, P, P, i]
+        _lib.oracle_hisa.argtypes = [P, i, i, i, P, i, P, P, i, P, P, P, P, i]
         _lib.oracle_pool.argtypes = [P, i, i, i, i, P]
         _lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_long, i, P, P, i]
         _lib.oracle_dsa_fp8.argtypes = [P, P, P, i, P, i, P, P, P, i]
@@ -151,13 +151,18 @@ def misa(prob: Problem, topk: int, B: int, h: int, kprime: int = 0, rows=None,
 
 
 def hisa(prob: Problem, topk: int, b: int, r: int, rows=None, override_blocks=None,
-         nthreads=0):
-    """HISA coarse (blocks) + fine (tokens).  Returns a dict with idx, score, blocks, J."""
+         coarse_heads=None, nthreads=0):
+    """HISA coarse (blocks) + fine (tokens).  Returns a dict with idx, score, blocks, J.
+    coarse_heads [n, h] (ascending): score the blocks with those heads only."""
     lib = _load()
     rr, n = prob.rows(rows)
     ob = None if override_blocks is None else np.ascontiguousarray(override_blocks, np.int32)
     if ob is not None:
         assert ob.shape == (n, r)
+    ch = None if coarse_heads is None else np.ascontiguousarray(coarse_heads, np.int32)
+    hsel = 0 if ch is None else ch.shape[1]
+    if ch is not None:
+        assert ch.shape == (n, hsel) and np.all(np.diff(ch, axis=1) > 0)
     nbmax = (prob.L + b - 1) // b
     out = {
         "idx": np.empty((n, topk), np.int32),
@@ -165,8 +170,8 @@ def hisa(prob: Problem, topk: int, b: int, r: int, rows=None, override_blocks=No
         "blocks": np.empty((n, r), np.int32),
         "J": np.empty((n, nbmax), np.float64),
     }
-    _check(lib.oracle_hisa(ctypes.byref(prob._c), topk, b, r, _ptr(rr), n, _ptr(ob),
-                           _ptr(out["blocks"]), _ptr(out["J"]), _ptr(out["idx"]),
+    _check(lib.oracle_hisa(ctypes.byref(prob._c), topk, b, r, _ptr(rr), n, _ptr(ob), _ptr(ch),
+                           hsel, _ptr(out["blocks"]), _ptr(out["J"]), _ptr(out["idx"]),
                            _ptr(out["score"]), _threads(nthreads)), "oracle_hisa")
     return out
 
@@ -274,3 +279,18 @@ def box_bound(q, kmin, kmax):
     kmax = np.ascontiguousarray(kmax, np.float64)
     assert q.shape == kmin.shape == kmax.shape and q.ndim == 1
     return lib.oracle_box_bound(_ptr(q), _ptr(kmin), _ptr(kmax), q.shape[0])
+
+
+def misa_hisa(prob: Problem, topk: int, B: int, h: int, b: int, r: int, rows=None,
+              override_heads=None, override_blocks=None, nthreads=0):
+    """MISA x HISA: the MISA router picks h heads (pooled blocks of B), HISA's
+    block scores use only those heads (blocks of b), the legal tokens of the r
+    best blocks are rescored with every head, top-k.  Returns a dict with
+    heads, E, blocks, J, idx, score."""
+    m = misa(prob, 1, B, h, rows=rows, nthreads=nthreads)
+    heads = m["heads"] if override_heads is None else np.ascontiguousarray(override_heads, np.int32)
+    out = hisa(prob, topk, b, r, rows=rows, override_blocks=override_blocks, coarse_heads=heads,
+               nthreads=nthreads)
+    out["heads"] = heads
+    out["E"] = m["E"]
+    return out

@@ -434,6 +434,8 @@ typedef struct {
     int topk, b, r;
     const int32_t* rows;
     const int32_t* override_blocks;
+    const int32_t* coarse_heads;
+    int hsel;
     int32_t* out_blocks;
     double* out_J;
     int32_t* out_idx;
@@ -442,7 +444,11 @@ typedef struct {
 
 /* [PT] section 2.1 and [BLOG] "Route 1: HISA": block representatives are the
  * mean of b keys; blocks are scored with the indexer formula; the r best
- * blocks are kept and their tokens are rescored exactly; token top-k. */
+ * blocks are kept and their tokens are rescored exactly; token top-k.
+ * With coarse_heads (per row, hsel heads in ascending order) the block scores
+ * sum only those heads: the MISA x HISA composition ([MISA] "core method",
+ * point (1): head routing and HISA's token hierarchy are orthogonal and can
+ * run in series), whose fine stage still rescores with every head. */
 static int hisa_row(void* vctx, int rr)
 {
     hisa_ctx* c = (hisa_ctx*)vctx;
@@ -471,7 +477,8 @@ static int hisa_row(void* vctx, int rr)
         int hi = lo + c->b;
         if (hi > n) hi = n;
         pool_mean(Kseq, d, lo, hi, rep);
-        bc[m].score = indexer_score(qrow, wrow, rep, H, d, NULL, 0);
+        const int32_t* ch = c->coarse_heads ? c->coarse_heads + (size_t)rr * c->hsel : NULL;
+        bc[m].score = indexer_score(qrow, wrow, rep, H, d, ch, c->hsel);
         bc[m].idx = m;
         if (J) J[m] = bc[m].score;
     }
@@ -519,15 +526,18 @@ static int hisa_row(void* vctx, int rr)
 }
 
 int oracle_hisa(const oracle_problem* p, int topk, int b, int r, const int32_t* rows,
-                int nrows, const int32_t* override_blocks, int32_t* out_blocks, double* out_J,
-                int32_t* out_idx, double* out_score, int nthreads)
+                int nrows, const int32_t* override_blocks, const int32_t* coarse_heads,
+                int hsel, int32_t* out_blocks, double* out_J, int32_t* out_idx,
+                double* out_score, int nthreads)
 {
     int e = check_problem(p);
     if (e) return e;
     if (topk < 1 || b < 1 || r < 1 || !out_idx || !out_score) return ORACLE_EINVAL;
     if ((long)r * b < topk) return ORACLE_EINVAL; /* [PT] 2.3: r*b >= k */
+    if (coarse_heads && (hsel < 1 || hsel > p->H)) return ORACLE_EINVAL;
     if (!rows) nrows = p->Bt * p->T;
-    hisa_ctx c = {p, topk, b, r, rows, override_blocks, out_blocks, out_J, out_idx, out_score};
+    hisa_ctx c = {p, topk, b, r, rows, override_blocks, coarse_heads, coarse_heads ? hsel : 0,
+                  out_blocks, out_J, out_idx, out_score};
     return run_rows(hisa_row, &c, nrows, nthreads);
 }
 

@@ -49,12 +49,15 @@ int oracle_misa(const oracle_problem* p, int topk, int B, int h, int kprime,
                 int32_t* out_pool, double* out_hatrow, int32_t* out_idx, double* out_score,
                 int nthreads);
 
-/* HISA.  override_blocks [nrows, r] (nullable, -1 skipped); out_blocks
+/* HISA.  override_blocks [nrows, r] (nullable, -1 skipped); coarse_heads
+ * [nrows, hsel] (nullable, ascending): block scores over those heads only
+ * (the MISA x HISA composition; the fine stage keeps every head); out_blocks
  * [nrows, r] in selection order, -1 padded; out_J [nrows, ceil(L/b)] block
  * scores, NaN for blocks past t.  Rejects r*b < topk. */
 int oracle_hisa(const oracle_problem* p, int topk, int b, int r, const int32_t* rows,
-                int nrows, const int32_t* override_blocks, int32_t* out_blocks, double* out_J,
-                int32_t* out_idx, double* out_score, int nthreads);
+                int nrows, const int32_t* override_blocks, const int32_t* coarse_heads,
+                int hsel, int32_t* out_blocks, double* out_J, int32_t* out_idx,
+                double* out_score, int nthreads);
 
 /* Means of consecutive blocks of `block` keys (last block truncated at L):
  * out [Bt, ceil(L/block), d]. */

@@ -152,3 +152,18 @@ def resmisa_row(qe, we, ke, i, t, k, block, r):
             tot += we[i][j] * (relu(z) if j in heads else z)
         R[s] = tot
     return dict(heads=heads, S=S, sel=best_subset(R, list(range(t + 1)), k), R=R)
+
+
+def misa_hisa_row(qe, we, ke, i, t, k, B, h, b, r):
+    """MISA x HISA, exact: the MISA router's h heads score the b-blocks, the r
+    best blocks' legal tokens are scored with every head."""
+    routed = misa_row(qe, we, ke, i, t, 1, B, h)
+    heads = sorted(routed["heads"])
+    nb = t // b + 1
+    J = {m: score(qe[i], we[i], mean(ke[m * b:min((m + 1) * b, t + 1)]), heads)
+         for m in range(nb)}
+    blocks = best_subset(J, list(range(nb)), r)
+    cand = [s for m in sorted(blocks) for s in range(m * b, min((m + 1) * b, t + 1))]
+    full = {s: score(qe[i], we[i], ke[s]) for s in cand}
+    return dict(heads=routed["heads"], E=routed["E"], blocks=blocks, J=J,
+                sel=best_subset(full, cand, k), full=full)
