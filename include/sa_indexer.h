@@ -180,6 +180,31 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
                      int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* -------------------------------------------------------- MISA x HISA */
+
+/* Workspace bytes for misa_hisa. */
+int misa_hisa_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t block_b, int32_t r,
+                 int32_t pooled_given, int32_t reps_given, size_t* ws_bytes);
+
+/* MISA x HISA: the head axis and the token axis in series ("MISA" summary
+ * page, core method point (1): routing heads is orthogonal to HISA's
+ * block-to-token hierarchy and the two can be chained).
+ *   1. MISA router on the pooled keys (blocks of block_B): the h heads with
+ *      the largest E_j = mean_m |w_j ReLU(q_j . pooled_m)| (misa_route).
+ *   2. HISA coarse stage with those heads only: block scores
+ *      J_m = sum_{j routed} w_j ReLU(q_j . rep_m) over blocks of block_b
+ *      (reps: block means), the r best blocks (ties -> lower block).
+ *   3. Fine stage: every legal token of the kept blocks scored with all H
+ *      heads, token top-k; out_score = I.
+ * pooled / reps: NULL (pooled inside the call) or sa_pool_blocks output for
+ * block_B / block_b.  out_heads [batch, T, h] ascending, out_blocks [batch,
+ * T, r] (both nullable).  Requires 1 <= h <= H and r * block_b >= topk.
+ * Other arguments, ownership and errors as in indexer_score_topk. */
+int misa_hisa(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+              int32_t block_B, int32_t h, int32_t block_b, int32_t r, const uint16_t* pooled,
+              const uint16_t* reps, int32_t* out_heads, int32_t* out_blocks, int32_t* out_idx,
+              float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------- LISA / ResMiSA */
 
 /* Workspace bytes for lisa_score_topk. */

@@ -34,7 +34,7 @@ EXPORTS = (
     "sa_last_error", "sa_profile_enable", "sa_profile_read", "sa_kernel_count",
     "sa_kernel_name", "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws",
     "indexer_score_topk_fp8", "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema",
-    "resmisa_route_ws", "resmisa_route",
+    "resmisa_route_ws", "resmisa_route", "misa_hisa_ws", "misa_hisa",
 )
 
 
@@ -73,6 +73,8 @@ def load():
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
     lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
+    lib.misa_hisa_ws.argtypes = [SP, I, I, I, I, I, I, ctypes.POINTER(S)]
+    lib.misa_hisa.argtypes = [P, P, P, SP, I, I, I, I, P, P, P, P, P, P, P, S, P]
     lib.lisa_score_topk_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.lisa_score_topk.argtypes = [P, P, P, SP, P, P, P, S, P]
     lib.sa_block_extrema.argtypes = [P, I, I, I, I, P, P]
@@ -90,7 +92,7 @@ def load():
                  "hisa_coarse_fine", "sa_profile_enable", "sa_profile_read",
                  "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws", "indexer_score_topk_fp8",
                  "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema", "resmisa_route_ws",
-                 "resmisa_route"):
+                 "resmisa_route", "misa_hisa_ws", "misa_hisa"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -297,6 +299,39 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
                                          _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                          _stream(q.device)), "indexer_score_topk_fp8")
     return out_idx, out_score
+
+
+# ---------------------------------------------------------- MISA x HISA
+
+def misa_hisa_ws(shape: Shape, block_B, h, block_b, r, pooled_given, reps_given) -> int:
+    n = ctypes.c_size_t()
+    _check(load().misa_hisa_ws(ctypes.byref(shape), int(block_B), int(h), int(block_b), int(r),
+                               int(bool(pooled_given)), int(bool(reps_given)), ctypes.byref(n)),
+           "misa_hisa_ws")
+    return n.value
+
+
+def misa_hisa(q, w, keys, causal_offset, topk, block_B, h, block_b, r, pooled=None, reps=None,
+              want_heads=True, want_blocks=True, out_heads=None, out_blocks=None, out_idx=None,
+              out_score=None, want_score=True, ws=None):
+    """MISA router heads -> HISA block scores over those heads -> every-head
+    rescoring of the r best blocks' tokens.  Returns (idx, score, heads, blocks)."""
+    s = _shape(q, w, keys, causal_offset, topk)
+    B, T = q.shape[0], q.shape[1]
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    heads = out_heads
+    if heads is None and want_heads:
+        heads = torch.empty((B, T, h), dtype=torch.int32, device=q.device)
+    blocks = out_blocks
+    if blocks is None and want_blocks:
+        blocks = torch.empty((B, T, r), dtype=torch.int32, device=q.device)
+    ws = _workspace(misa_hisa_ws(s, block_B, h, block_b, r, pooled is not None, reps is not None),
+                    q.device, ws)
+    _check(load().misa_hisa(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_B), int(h),
+                            int(block_b), int(r), _p(pooled), _p(reps), _p(heads), _p(blocks),
+                            _p(out_idx), _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
+           "misa_hisa")
+    return out_idx, out_score, heads, blocks
 
 
 # ------------------------------------------------------- LISA / ResMiSA

@@ -675,6 +675,47 @@ int sa_pool_blocks2(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, i
 
 // ----------------------------------------------------------------- MISA
 
+// MISA router stage: pooled keys (given, or pooled into pooled_ws), the
+// pooled means of cut last blocks (tail != null), the router -> heads
+// [rows, h] ascending.
+static int route_heads(const uint16_t* q, const float* w, const uint16_t* keys,
+                       const sa_shape* s, int block_B, int h, const uint16_t* pooled,
+                       uint16_t* pooled_ws, uint16_t* tail, uint8_t* flag, int32_t* heads,
+                       hipStream_t st) {
+    const int rows = s->batch * s->T;
+    const int nblk = (s->L + block_B - 1) / block_B;
+    hipError_t e;
+    const uint16_t* reps = pooled;
+    if (!reps) {
+        e = sa::launch_pool(keys, s->batch, s->L, block_B, pooled_ws, st);
+        if (e != hipSuccess) return hip_fail(e, "pool");
+        reps = pooled_ws;
+    }
+    if (tail) {
+        e = sa::launch_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset, s->L,
+                            block_B, rows, tail, flag, st);
+        if (e != hipSuccess) return hip_fail(e, "tail pool");
+    }
+    sa::RouterArgs ra{};
+    ra.q = q;
+    ra.w = w;
+    ra.reps = reps;
+    ra.seq_stride = (long long)nblk * 2 * sa::kD;
+    ra.tail = tail;
+    ra.tail_flag = tail ? flag : nullptr;
+    ra.T = s->T;
+    ra.H = s->H;
+    ra.offset = s->causal_offset;
+    ra.B = block_B;
+    ra.nblk = nblk;
+    ra.h = h;
+    ra.heads_out = heads;
+    ra.E_out = nullptr;
+    e = sa::launch_router(ra, rows, st);
+    if (e != hipSuccess) return hip_fail(e, "router");
+    return SA_OK;
+}
+
 int misa_route_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
                   int32_t pooled_given, size_t* ws_bytes) {
     int rc = check_misa(s, block_B, h, k_prime);
@@ -701,37 +742,11 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     MisaPlan p = plan_misa(s, block_B, h, k_prime, pooled != nullptr, partial, base);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int rows = s->batch * s->T;
-    const int nblk = (s->L + block_B - 1) / block_B;
     hipError_t e;
-    const uint16_t* reps = pooled;
-    if (!reps) {
-        e = sa::launch_pool(keys, s->batch, s->L, block_B, p.pooled, st);
-        if (e != hipSuccess) return hip_fail(e, "pool");
-        reps = p.pooled;
-    }
-    if (partial) {
-        e = sa::launch_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset, s->L,
-                            block_B, rows, p.tail, p.flag, st);
-        if (e != hipSuccess) return hip_fail(e, "tail pool");
-    }
     int32_t* heads = out_heads ? out_heads : p.heads;
-    sa::RouterArgs ra{};
-    ra.q = q;
-    ra.w = w;
-    ra.reps = reps;
-    ra.seq_stride = (long long)nblk * 2 * sa::kD;
-    ra.tail = p.tail;
-    ra.tail_flag = p.flag;
-    ra.T = s->T;
-    ra.H = s->H;
-    ra.offset = s->causal_offset;
-    ra.B = block_B;
-    ra.nblk = nblk;
-    ra.h = h;
-    ra.heads_out = heads;
-    ra.E_out = nullptr;
-    e = sa::launch_router(ra, rows, st);
-    if (e != hipSuccess) return hip_fail(e, "router");
+    rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
+                     p.flag, heads, st);
+    if (rc) return rc;
     if (k_prime == 0) {
         e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, s->topk,
                            out_idx, out_score, st);
@@ -776,20 +791,14 @@ int hisa_coarse_fine_ws(const sa_shape* s, int32_t block_b, int32_t r, int32_t r
     return SA_OK;
 }
 
-int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
-                     const sa_shape* s, int32_t block_b, int32_t r, const uint16_t* reps,
-                     int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
-                     size_t ws_bytes, void* stream) {
-    int rc = check_hisa(s, block_b, r);
-    if (rc) return rc;
-    rc = check_ptrs(q, w, keys, out_idx);
-    if (rc) return rc;
-    const bool partial = any_partial(s, block_b);
-    const size_t need = plan_hisa(s, block_b, r, reps != nullptr, partial, nullptr).bytes;
-    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
-    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
-    HisaPlan p = plan_hisa(s, block_b, r, reps != nullptr, partial, base);
-    hipStream_t st = static_cast<hipStream_t>(stream);
+// HISA stages: block reps (given, or pooled into the plan), the means of cut
+// last blocks, block scores (over `heads` [rows, hsel] when given: the MISA x
+// HISA composition, else every head), top-r blocks, every-head rescoring of
+// their legal tokens, token top-k.
+static int hisa_stages(const uint16_t* q, const float* w, const uint16_t* keys,
+                       const sa_shape* s, int block_b, int r, const uint16_t* reps,
+                       const HisaPlan& p, bool partial, const int32_t* heads, int hsel,
+                       int32_t* out_blocks, int32_t* out_idx, float* out_score, hipStream_t st) {
     const int rows = s->batch * s->T;
     const int nblk = (s->L + block_b - 1) / block_b;
     hipError_t e;
@@ -804,7 +813,7 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
                             block_b, rows, p.tail, p.flag, st);
         if (e != hipSuccess) return hip_fail(e, "tail pool");
     }
-    // Coarse stage: block scores with the full indexer formula.
+    // Coarse stage: block scores with the indexer formula (routed heads or all).
     sa::ScanArgs a{};
     a.q = q;
     a.w = w;
@@ -820,7 +829,9 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
     a.chunk = sa::scan_chunk(8, rows, nblk);
     a.scores = p.bscores;
     a.score_stride = nblk;
-    e = sa::launch_scan(a, rows, (s->H + 15) / 16, 8, false, st);
+    a.heads = heads;
+    a.hsel = hsel;
+    e = sa::launch_scan(a, rows, ((heads ? hsel : s->H) + 15) / 16, 8, heads != nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "block scores");
     int32_t* blocks = out_blocks ? out_blocks : p.blocks;
     sa::TopkArgs t{};
@@ -858,6 +869,90 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
                       rows, s->topk, out_idx, out_score, st);
     if (e != hipSuccess) return hip_fail(e, "fine top-k");
     return SA_OK;
+}
+
+int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
+                     const sa_shape* s, int32_t block_b, int32_t r, const uint16_t* reps,
+                     int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
+                     size_t ws_bytes, void* stream) {
+    int rc = check_hisa(s, block_b, r);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    const bool partial = any_partial(s, block_b);
+    const size_t need = plan_hisa(s, block_b, r, reps != nullptr, partial, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    HisaPlan p = plan_hisa(s, block_b, r, reps != nullptr, partial, base);
+    return hisa_stages(q, w, keys, s, block_b, r, reps, p, partial, nullptr, 0, out_blocks,
+                       out_idx, out_score, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------ MISA x HISA
+
+struct MisaHisaPlan {
+    uint16_t* pooled;
+    uint16_t* tail;
+    uint8_t* flag;
+    int32_t* heads;
+    HisaPlan hisa;
+    size_t bytes;
+};
+
+static MisaHisaPlan plan_misa_hisa(const sa_shape* s, int B, int h, int b, int r,
+                                   bool pooled_given, bool reps_given, void* ws) {
+    MisaHisaPlan p{};
+    Carve cv(ws);
+    const long long rows = (long long)s->batch * s->T;
+    const long long nblk = (s->L + B - 1) / B;
+    if (!pooled_given) p.pooled = cv.take<uint16_t>(s->batch * nblk * 2 * sa::kD);
+    if (any_partial(s, B)) {
+        p.tail = cv.take<uint16_t>(rows * 2 * sa::kD);
+        p.flag = cv.take<uint8_t>(rows);
+    }
+    p.heads = cv.take<int32_t>(rows * h);
+    const size_t off = (cv.off + 255) & ~size_t(255);
+    p.hisa = plan_hisa(s, b, r, reps_given, any_partial(s, b),
+                       ws ? static_cast<char*>(ws) + off : nullptr);
+    p.bytes = off + p.hisa.bytes;
+    return p;
+}
+
+int misa_hisa_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t block_b, int32_t r,
+                 int32_t pooled_given, int32_t reps_given, size_t* ws_bytes) {
+    int rc = check_misa(s, block_B, h, 0);
+    if (rc) return rc;
+    rc = check_hisa(s, block_b, r);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_misa_hisa(s, block_B, h, block_b, r, pooled_given != 0, reps_given != 0,
+                               nullptr)
+                    .bytes;
+    return SA_OK;
+}
+
+int misa_hisa(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+              int32_t block_B, int32_t h, int32_t block_b, int32_t r, const uint16_t* pooled,
+              const uint16_t* reps, int32_t* out_heads, int32_t* out_blocks, int32_t* out_idx,
+              float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_misa(s, block_B, h, 0);
+    if (rc) return rc;
+    rc = check_hisa(s, block_b, r);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    const size_t need =
+        plan_misa_hisa(s, block_B, h, block_b, r, pooled != nullptr, reps != nullptr, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    MisaHisaPlan p =
+        plan_misa_hisa(s, block_B, h, block_b, r, pooled != nullptr, reps != nullptr, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* heads = out_heads ? out_heads : p.heads;
+    rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, p.tail, p.flag, heads, st);
+    if (rc) return rc;
+    return hisa_stages(q, w, keys, s, block_b, r, reps, p.hisa, any_partial(s, block_b), heads, h,
+                       out_blocks, out_idx, out_score, st);
 }
 
 }  // extern "C"

@@ -231,15 +231,18 @@ def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows):
     return swaps
 
 
-def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows):
+def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows, coarse_heads=None):
+    """coarse_heads [len(rows), h]: block scores over those heads (MISA x HISA,
+    staged with the GPU's routed heads)."""
     prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
-    base = oracle.hisa(prob, k, b, r, rows=rows)
+    base = oracle.hisa(prob, k, b, r, rows=rows, coarse_heads=coarse_heads)
     gb = gblocks.reshape(-1, r)
     for u, row in enumerate(rows):
         t = t_of_row(p, row)
         check_choice(gb[row], base["J"][u], t // b + 1, r, "hisa blocks row %d" % row)
     over = np.ascontiguousarray(gb[rows])
-    staged = oracle.hisa(prob, k, b, r, rows=rows, override_blocks=over)
+    staged = oracle.hisa(prob, k, b, r, rows=rows, override_blocks=over,
+                         coarse_heads=coarse_heads)
     gi = gidx.reshape(-1, k)
     gs = None if gsc is None else gsc.reshape(-1, k)
     swaps = 0
@@ -250,7 +253,8 @@ def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows):
         # exact scores of the candidates: from the staged oracle top-k over
         # exactly these candidates (k = #candidates gives every score)
         allc = oracle.hisa(prob, len(cand), b, r, rows=np.array([row], np.int32),
-                           override_blocks=over[u: u + 1])
+                           override_blocks=over[u: u + 1],
+                           coarse_heads=None if coarse_heads is None else coarse_heads[u: u + 1])
         sc_of = dict(zip(allc["idx"][0].tolist(), allc["score"][0].tolist()))
         tol = TOL_REL * max(abs(v) for v in sc_of.values())
         swaps += check_set(gi[row], None if gs is None else gs[row], staged["idx"][u],
@@ -258,6 +262,20 @@ def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows):
                            len(cand), k, tol, t=t, cand_set=set(cand.tolist()),
                            what="hisa row %d" % row)
     return swaps
+
+
+def check_misa_hisa(p, k, B, h, b, r, gidx, gsc, gheads, gblocks, rows):
+    """MISA x HISA, staged: the routed heads by the near-tie rule on E, the
+    blocks on the block scores over the GPU's heads, then the tokens over the
+    GPU's blocks."""
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    base = oracle.misa(prob, 1, B, h, rows=rows)
+    gh = gheads.reshape(-1, h)
+    for u, row in enumerate(rows):
+        assert np.all(np.diff(gh[row]) > 0), "misa-hisa heads row %d not ascending" % row
+        check_choice(gh[row], base["E"][u], p["H"], h, "misa-hisa heads row %d" % row)
+    return check_hisa(p, k, b, r, gidx, gsc, gblocks, rows,
+                      coarse_heads=np.ascontiguousarray(gh[rows]))
 
 
 # ------------------------------------------------------------------ smoke
