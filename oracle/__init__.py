@@ -294,3 +294,51 @@ def misa_hisa(prob: Problem, topk: int, B: int, h: int, b: int, r: int, rows=Non
     out["heads"] = heads
     out["E"] = m["E"]
     return out
+
+
+def dsa_ragged(q, w, K, seq_lens, topk, nthreads=0):
+    """DSA over sequences of different lengths: sequence b's history is
+    K[b, :seq_lens[b]] and its T query rows sit at seq_lens[b] - T + i; each
+    sequence is the plain DSA problem on its own keys.  Returns (idx, score,
+    rowscore) with rows b*T + i; rowscore [rows, L] is NaN past the row."""
+    Bt, T = q.shape[0], q.shape[1]
+    L = K.shape[1]
+    idx = np.empty((Bt * T, topk), np.int32)
+    sc = np.empty((Bt * T, topk), np.float64)
+    rs = np.full((Bt * T, L), np.nan)
+    for b in range(Bt):
+        n = int(seq_lens[b])
+        assert T <= n <= L
+        pb = Problem(q[b:b + 1], w[b:b + 1], np.ascontiguousarray(K[b:b + 1, :n]), n - T)
+        i, s, r = dsa(pb, topk, want_rowscore=True, nthreads=nthreads)
+        idx[b * T:(b + 1) * T] = i
+        sc[b * T:(b + 1) * T] = s
+        rs[b * T:(b + 1) * T, :n] = r
+    return idx, sc, rs
+
+
+def tidy(idx, T, block_table=None, page_size=1):
+    """Index tidy-up ([PT] 2.2; counts of [PT] 2.3): per row of idx [rows, k]
+    (-1 empty), the physical slots table[b][s // page] * page + s % page (s
+    itself without a table; positions past the table or on a negative entry
+    dropped), distinct, ascending, -1 padded; stats [rows, 3] = (distinct
+    slots, distinct pages, maximal runs of consecutive slots)."""
+    idx = np.asarray(idx).reshape(-1, np.asarray(idx).shape[-1])
+    rows, k = idx.shape
+    slots = np.full((rows, k), -1, np.int32)
+    stats = np.zeros((rows, 3), np.int32)
+    for row in range(rows):
+        b = row // T
+        v = idx[row][idx[row] >= 0].astype(np.int64)
+        if block_table is not None:
+            pg = v // page_size
+            keep = pg < block_table.shape[1]
+            v, pg = v[keep], pg[keep]
+            phys = block_table[b][pg].astype(np.int64)
+            keep = phys >= 0
+            v = phys[keep] * page_size + v[keep] % page_size
+        u = np.unique(v)
+        slots[row, :len(u)] = u
+        runs = 0 if len(u) == 0 else 1 + int(np.count_nonzero(np.diff(u) != 1))
+        stats[row] = (len(u), len(np.unique(u // page_size)), runs)
+    return slots, stats
