@@ -86,6 +86,51 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ----------------------------------------------------------- tidy-up */
+
+/* Index tidy-up after any selector (PaperTrace "2.2.2 MISA, LISA and
+ * ResMiSA", section 2.2: put the selected tokens in physical page / offset
+ * order for a coalesced gather, keep the set free of duplicates and its valid
+ * length; section 2.3: count the distinct pages and contiguous runs).
+ *   idx          device int32 [rows, k] selected positions per row, -1 empty
+ *                (any order, duplicates allowed); rows = batch * T, row r
+ *                belongs to sequence r / T.
+ *   block_table  device int32 [batch, pages_per_seq]: physical page of each
+ *                logical page of the sequence, or NULL (slot = position).
+ *                Positions past the table, or on a page mapped to a negative
+ *                entry, are dropped.  Slots must fit in int32.
+ *   page_size    tokens per page (>= 1): slot = table[b][s / page_size] *
+ *                page_size + s % page_size.
+ *   out_slots    device int32 [rows, k]: the row's distinct slots in
+ *                ascending order, then -1.
+ *   out_stats    device int32 [rows, 3] (nullable): distinct slots, distinct
+ *                pages (slot / page_size), maximal runs of consecutive slots.
+ * k <= 4096 (SA_EUNSUPPORTED otherwise); errors as in indexer_score_topk. */
+int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
+                    const int32_t* block_table, int32_t pages_per_seq, int32_t page_size,
+                    int32_t* out_slots, int32_t* out_stats, void* stream);
+
+/* ------------------------------------------------------- ragged rows */
+
+/* Workspace bytes for indexer_score_topk_ragged. */
+int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes);
+
+/* DSA indexer over a batch of sequences of different lengths (PaperTrace
+ * "2.2.2 MISA, LISA and ResMiSA", section 2.3, load and tail latency: each
+ * row selects among its own min(k, t+1) positions; per-row lengths instead of
+ * padding every row to the longest one).
+ *   seq_lens  device int32 [batch]: keys [0, seq_lens[b]) of sequence b are
+ *             its history; its T query rows sit at positions
+ *             seq_lens[b] - T + i (causal within the sequence).  Lengths are
+ *             clamped to [T, L].  Work beyond a row's length is skipped.
+ *   s         L is the per-sequence capacity (the keys' row stride);
+ *             causal_offset must be L - T; T < 16 (decode-style rows).
+ * Selection and outputs as in indexer_score_topk; other arguments,
+ * ownership and errors likewise. */
+int indexer_score_topk_ragged(const uint16_t* q, const float* w, const uint16_t* keys,
+                              const int32_t* seq_lens, const sa_shape* s, int32_t* out_idx,
+                              float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------- FP8 keys */
 
 /* FP8 key cache (PaperTrace section 2.3, "from the formula to the FP8

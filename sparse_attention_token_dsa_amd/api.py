@@ -34,7 +34,8 @@ EXPORTS = (
     "sa_last_error", "sa_profile_enable", "sa_profile_read", "sa_kernel_count",
     "sa_kernel_name", "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws",
     "indexer_score_topk_fp8", "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema",
-    "resmisa_route_ws", "resmisa_route", "misa_hisa_ws", "misa_hisa",
+    "resmisa_route_ws", "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
+    "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged",
 )
 
 
@@ -73,6 +74,9 @@ def load():
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
     lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
+    lib.sa_tidy_indices.argtypes = [P, I, I, I, P, I, I, P, P, P]
+    lib.indexer_score_topk_ragged_ws.argtypes = [SP, ctypes.POINTER(S)]
+    lib.indexer_score_topk_ragged.argtypes = [P, P, P, P, SP, P, P, P, S, P]
     lib.misa_hisa_ws.argtypes = [SP, I, I, I, I, I, I, ctypes.POINTER(S)]
     lib.misa_hisa.argtypes = [P, P, P, SP, I, I, I, I, P, P, P, P, P, P, P, S, P]
     lib.lisa_score_topk_ws.argtypes = [SP, ctypes.POINTER(S)]
@@ -92,7 +96,8 @@ def load():
                  "hisa_coarse_fine", "sa_profile_enable", "sa_profile_read",
                  "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws", "indexer_score_topk_fp8",
                  "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema", "resmisa_route_ws",
-                 "resmisa_route", "misa_hisa_ws", "misa_hisa"):
+                 "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
+                 "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -298,6 +303,58 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
     _check(load().indexer_score_topk_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                          _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                          _stream(q.device)), "indexer_score_topk_fp8")
+    return out_idx, out_score
+
+
+# ------------------------------------------------- tidy-up, ragged rows
+
+def tidy_indices(idx, T, block_table=None, page_size=1, out_slots=None, out_stats=None,
+                 want_stats=True):
+    """Selected positions [batch, T, k] (or [rows, k]) -> distinct physical
+    slots in ascending order, -1 padded, and per-row (slots, pages, runs)."""
+    if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous():
+        raise TypeError("idx must be a contiguous int32 GPU tensor")
+    k = idx.shape[-1]
+    rows = idx.numel() // k
+    if block_table is not None:
+        if (block_table.dtype != torch.int32 or not block_table.is_cuda
+                or not block_table.is_contiguous() or block_table.dim() != 2):
+            raise TypeError("block_table must be a contiguous int32 [batch, pages] GPU tensor")
+        if block_table.shape[0] * int(T) != rows:
+            raise ValueError("block_table needs one row per sequence (rows / T = %d), has %d"
+                             % (rows // int(T), block_table.shape[0]))
+    if out_slots is None:
+        out_slots = torch.empty_like(idx)
+    if out_stats is None and want_stats:
+        out_stats = torch.empty(idx.shape[:-1] + (3,), dtype=torch.int32, device=idx.device)
+    _check(load().sa_tidy_indices(_p(idx), rows, int(T), k, _p(block_table),
+                                  0 if block_table is None else block_table.shape[1],
+                                  int(page_size), _p(out_slots), _p(out_stats),
+                                  _stream(idx.device)), "sa_tidy_indices")
+    return out_slots, out_stats
+
+
+def indexer_score_topk_ragged_ws(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    _check(load().indexer_score_topk_ragged_ws(ctypes.byref(shape), ctypes.byref(n)),
+           "indexer_score_topk_ragged_ws")
+    return n.value
+
+
+def indexer_score_topk_ragged(q, w, keys, seq_lens, topk, out_idx=None, out_score=None,
+                              want_score=True, ws=None):
+    """DSA over sequences of different lengths: keys [batch, L_cap, 128],
+    seq_lens int32 [batch] on the GPU; row i of sequence b sits at
+    seq_lens[b] - T + i."""
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != q.shape[0]:
+        raise TypeError("seq_lens must be an int32 GPU tensor with one entry per sequence")
+    s = _shape(q, w, keys, keys.shape[1] - q.shape[1], topk)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    ws = _workspace(indexer_score_topk_ragged_ws(s), q.device, ws)
+    _check(load().indexer_score_topk_ragged(_p(q), _p(w), _p(keys), _p(seq_lens.contiguous()),
+                                            ctypes.byref(s), _p(out_idx), _p(out_score), _p(ws),
+                                            ws.numel(), _stream(q.device)),
+           "indexer_score_topk_ragged")
     return out_idx, out_score
 
 

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libsaindexer.so")
 SOURCES = ["abi.hip", "scan.hip", "scan8.hip", "topk.hip", "pool.hip", "prefill.hip",
-           "lisa.hip"]
+           "lisa.hip", "tidy.hip"]
 
 # Packed fp32 ops are switched off for device code: hipcc -O3 would otherwise
 # form v_pk_* fp32 instructions on its own.  -fno-honor-nans: inputs are

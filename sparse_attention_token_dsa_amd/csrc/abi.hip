@@ -65,7 +65,7 @@ void drain_records() {
 const char* kKernelNames[sa::K_COUNT] = {
     "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
     "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused",
-    "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows"};
+    "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows", "tidy"};
 
 // ------------------------------------------------------------ workspace
 
@@ -153,7 +153,8 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
                           const sa_shape* s, const int32_t* heads, int hsel, float* scores,
                           uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
                           float* out_score, hipStream_t st, const uint8_t* codes = nullptr,
-                          const float* kscale = nullptr, bool state_zeroed = false) {
+                          const float* kscale = nullptr, bool state_zeroed = false,
+                          const int32_t* seq_lens = nullptr) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
     hipError_t e;
@@ -180,6 +181,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.k = k;
     a.codes = codes;
     a.kscale = kscale;
+    a.seq_lens = seq_lens;
     const int nht = ((heads ? hsel : s->H) + 15) / 16;
     e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
               : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
@@ -197,6 +199,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     t.out_score = out_score;
     t.out_stride = k;
     t.cand_cap = maxn;
+    t.seq_lens = seq_lens;
     return sa::launch_topk_dense_filtered(t, (int)rows, maxn, cand, st);
 }
 
@@ -414,6 +417,73 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                            out_idx, out_score, st);
         if (e != hipSuccess) return hip_fail(e, "decode scan");
     }
+    return SA_OK;
+}
+
+// ------------------------------------------------------------ tidy-up
+
+int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
+                    const int32_t* block_table, int32_t pages_per_seq, int32_t page_size,
+                    int32_t* out_slots, int32_t* out_stats, void* stream) {
+    if (!idx || !out_slots) return fail(SA_EINVAL, "idx and out_slots must be non-NULL");
+    if (rows < 1 || T < 1 || rows % T != 0) return fail(SA_EINVAL, "need rows >= 1, T >= 1, T | rows");
+    if (k < 1) return fail(SA_EINVAL, "k must be >= 1");
+    if (k > sa::kTidyMax) return fail(SA_EUNSUPPORTED, "k must be <= 4096");
+    if (page_size < 1) return fail(SA_EINVAL, "page_size must be >= 1");
+    if (block_table && pages_per_seq < 1) return fail(SA_EINVAL, "pages_per_seq must be >= 1");
+    sa::TidyArgs a{};
+    a.idx = idx;
+    a.k = k;
+    a.T = T;
+    int n2 = 256;
+    while (n2 < k) n2 <<= 1;
+    a.n2 = n2;
+    a.table = block_table;
+    a.pages_per_seq = block_table ? pages_per_seq : 0;
+    a.page = page_size;
+    a.out_slots = out_slots;
+    a.out_stats = out_stats;
+    hipError_t e = sa::launch_tidy(a, rows, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "tidy");
+    return SA_OK;
+}
+
+// ----------------------------------------------------------- ragged rows
+
+static int check_ragged(const sa_shape* s) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->T >= kPrefillMinT)
+        return fail(SA_EUNSUPPORTED, "ragged batches: decode-style rows only (T < 16)");
+    if (s->causal_offset != s->L - s->T)
+        return fail(SA_EINVAL, "ragged batches: causal_offset must be L - T (the capacity)");
+    return SA_OK;
+}
+
+int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes) {
+    int rc = check_ragged(s);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_dsa(s, nullptr).bytes;
+    return SA_OK;
+}
+
+int indexer_score_topk_ragged(const uint16_t* q, const float* w, const uint16_t* keys,
+                              const int32_t* seq_lens, const sa_shape* s, int32_t* out_idx,
+                              float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_ragged(s);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    if (!seq_lens) return fail(SA_EINVAL, "seq_lens is NULL");
+    const size_t need = plan_dsa(s, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    DsaPlan p = plan_dsa(s, base);
+    hipError_t e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand,
+                                  s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
+                                  nullptr, nullptr, false, seq_lens);
+    if (e != hipSuccess) return hip_fail(e, "ragged decode scan");
     return SA_OK;
 }
 

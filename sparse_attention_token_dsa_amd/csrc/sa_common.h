@@ -43,6 +43,17 @@ __device__ __forceinline__ float ord_to_f32(uint32_t o) {
     return __uint_as_float(u);
 }
 
+// Absolute position of query row `row`: offset + i, or with per-sequence
+// lengths (ragged batches) len_b - T + i, len_b clamped to [T, cap].
+__device__ __forceinline__ int row_pos(int row, int T, int offset, const int32_t* seq_lens,
+                                       int cap) {
+    const int b = row / T;
+    const int i = row - b * T;
+    if (!seq_lens) return offset + i;
+    const int len = min(max(seq_lens[b], T), cap);
+    return len - T + i;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
 }
@@ -128,6 +139,7 @@ enum KernelId {
     K_EXTREMA,
     K_RES_ROUTER,
     K_HEAD_ROWS,
+    K_TIDY,
     K_COUNT
 };
 
@@ -160,6 +172,9 @@ struct ScanArgs {
     // (sequences seq_stride / 128 apart).
     const uint8_t* codes;
     const float* kscale;
+    // Ragged batches: per-sequence lengths [batch] (row positions from
+    // row_pos with cap = len_cap), or null.
+    const int32_t* seq_lens;
 };
 
 struct GatherArgs {
@@ -206,6 +221,18 @@ struct ResmisaArgs {
     uint32_t* zero_state;   // [rows, kRowState] to clear for the decode scan, or null
 };
 
+// Index tidy-up: per row, physical slots sorted ascending, unique, -1 padded.
+constexpr int kTidyMax = 4096;  // selected indices per row
+struct TidyArgs {
+    const int32_t* idx;     // [rows, k], -1 = empty
+    int k, T;
+    int n2;                 // sort width: power of two >= max(k, 256)
+    const int32_t* table;   // [batch, pages_per_seq] physical page of each logical page, or null
+    int pages_per_seq, page;
+    int32_t* out_slots;     // [rows, k]
+    int32_t* out_stats;     // [rows, 3]: unique slots, distinct pages, contiguous runs; or null
+};
+
 struct TopkArgs {
     // dense source: scores[row * dense_stride + s], s < n(row)
     const float* dense;
@@ -224,6 +251,7 @@ struct TopkArgs {
     float* out_score;           // nullable
     long long out_stride;
     long long cand_cap;         // candidate keys per row (filter path)
+    const int32_t* seq_lens;    // ragged batches (dense source): as in ScanArgs, or null
 };
 
 struct PrefillArgs {
@@ -271,6 +299,7 @@ hipError_t launch_extrema_tail(const uint16_t* keys, long long seq_stride, int T
                                hipStream_t s);
 hipError_t launch_resmisa_router(const ResmisaArgs& a, int rows, hipStream_t s);
 hipError_t launch_head_rows(const ResmisaArgs& a, int rows, hipStream_t s);
+hipError_t launch_tidy(const TidyArgs& a, int rows, hipStream_t s);
 // Per-key FP8 quantization of n keys of 128 bf16 values.
 hipError_t launch_quantize_fp8(const uint16_t* keys, long long n, uint8_t* codes, float* scales,
                                hipStream_t s);

@@ -80,7 +80,7 @@ template <int NHT, bool HIST>
 __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     const int row = blockIdx.y;
     const int b = row / a.T;
-    const int t = a.offset + (row - b * a.T);
+    const int t = row_pos(row, a.T, a.offset, a.seq_lens, a.len_cap);
     int n = t / a.len_div + 1;
     if (n > a.len_cap) n = a.len_cap;
     const int cs = blockIdx.x * a.chunk;

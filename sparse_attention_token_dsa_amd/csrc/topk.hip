@@ -41,11 +41,10 @@ __device__ __forceinline__ float key_score(unsigned long long k) {
 __constant__ int kShift[6] = {52, 42, 32, 20, 10, 0};
 __constant__ int kWidth[6] = {12, 10, 10, 12, 10, 10};
 
-__device__ __forceinline__ int dense_len(int row, int T, int offset, int len_div, int len_cap) {
-    const int b = row / T;
-    const int t = offset + (row - b * T);
-    const int n = t / len_div + 1;
-    return n < len_cap ? n : len_cap;
+__device__ __forceinline__ int dense_len(const TopkArgs& a, int row) {
+    const int t = row_pos(row, a.T, a.offset, a.seq_lens, a.len_cap);
+    const int n = t / a.len_div + 1;
+    return n < a.len_cap ? n : a.len_cap;
 }
 
 // ------------------------------------------------------------ filter
@@ -67,7 +66,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     __shared__ Thresh th;
     const int row = blockIdx.y;
     const int tid = threadIdx.x;
-    const int n = dense_len(row, a.T, a.offset, a.len_div, a.len_cap);
+    const int n = dense_len(a, row);
     const int lo = blockIdx.x * kFilterChunk;
     if (lo >= n) return;
     const int hi = min(lo + kFilterChunk, n);
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         lsc = a.list_score + (long long)row * a.list_stride;
         lid = a.list_idx + (long long)row * a.list_stride;
     } else {
-        const int n = dense_len(row, a.T, a.offset, a.len_div, a.len_cap);
+        const int n = dense_len(a, row);
         dsrc = a.dense + (long long)row * a.dense_stride;
         nsrc0 = n;
     }

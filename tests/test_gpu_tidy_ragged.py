@@ -1,0 +1,111 @@
+"""GPU parity of the index tidy-up (bit-exact: integer work) and of the
+ragged-batch DSA indexer (parity rule of tests/parity.py against the oracle's
+per-sequence DSA)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity import TOL_REL, _np, check_set
+from sparse_attention_token_dsa_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from sparse_attention_token_dsa_amd import api as a
+    a.load()
+    return a
+
+
+def _tidy_both(api, idx, T, table, page):
+    gi = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    gt = None if table is None else torch.from_numpy(table.astype(np.int32)).to(DEV)
+    slots, stats = api.tidy_indices(gi, T, block_table=gt, page_size=page)
+    torch.cuda.synchronize()
+    os_, ost = oracle.tidy(idx, T, block_table=table, page_size=page)
+    assert np.array_equal(_np(slots).reshape(os_.shape), os_)
+    assert np.array_equal(_np(stats).reshape(ost.shape), ost)
+
+
+@pytest.mark.parametrize("rows,T,k,page,span,tabled", [
+    (4, 1, 2048, 64, 131072, False),   # decode top-k sets over a 128K cache
+    (6, 3, 257, 16, 5000, True),       # page table, ragged k, several rows per sequence
+    (2, 1, 1, 1, 10, False),           # k = 1
+    (3, 1, 4096, 32, 6000, True),      # the largest k, many duplicates
+    (2, 2, 100, 7, 300, True),         # page size not a power of two
+])
+def test_tidy(api, rows, T, k, page, span, tabled):
+    say("tidy rows=%d T=%d k=%d page=%d tabled=%s" % (rows, T, k, page, tabled))
+    rng = np.random.default_rng(k + page)
+    idx = rng.integers(-1, span, size=(rows, k))
+    idx[:, 1::2] = idx[:, ::2][:, : idx[:, 1::2].shape[1]]   # every value twice
+    table = None
+    if tabled:
+        npages = (span + page - 1) // page
+        table = rng.permutation(3 * npages)[: (rows // T) * npages].reshape(rows // T, npages)
+        table[rng.random(table.shape) < 0.05] = -1
+        table = table[:, : npages - 1]      # the last logical page has no entry
+    _tidy_both(api, idx, T, table, page)
+
+
+def test_tidy_of_a_selector_output(api):
+    # the top-k of the 32K decode batch, tidied with 64-token pages
+    say("tidy of decode top-k")
+    p = synth.make_problem(75, Bt=4, T=1, L=32768, H=64, needles=32, needle_mode="decode")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(DEV)
+    w = torch.from_numpy(p["w"]).to(DEV)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
+    idx, _ = api.indexer_score_topk(q, w, K, p["offset"], 2048)
+    torch.cuda.synchronize()
+    _tidy_both(api, _np(idx).reshape(4, 2048), 1, None, 64)
+
+
+@pytest.mark.parametrize("Bt,T,L,H,k,lens", [
+    (4, 1, 20000, 64, 512, [20000, 9001, 37, 1]),      # one row per sequence, very uneven
+    (3, 3, 5000, 32, 100, [5000, 1200, 3]),            # several rows; a sequence of exactly T
+    (2, 1, 131072, 64, 2048, [131072, 65537]),         # 128K capacity
+])
+def test_ragged(api, Bt, T, L, H, k, lens):
+    say("ragged Bt=%d T=%d L=%d lens=%s" % (Bt, T, L, lens))
+    p = synth.make_problem(80 + Bt, Bt=Bt, T=T, L=L, H=H, offset=L - T, needles=8)
+    lens = np.array(lens, np.int32)
+    q = torch.from_numpy(p["q"].view(np.int16)).to(DEV)
+    w = torch.from_numpy(p["w"]).to(DEV)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
+    gl = torch.from_numpy(lens).to(DEV)
+    idx, sc = api.indexer_score_topk_ragged(q, w, K, gl, k)
+    torch.cuda.synchronize()
+    oi, osc, rs = oracle.dsa_ragged(p["q"], p["w"], p["K"], lens, k)
+    gi, gs = _np(idx).reshape(-1, k), _np(sc).reshape(-1, k)
+    for row in range(Bt * T):
+        t = int(lens[row // T]) - T + row % T
+        srow = rs[row, : t + 1]
+        tol = TOL_REL * np.max(np.abs(srow))
+        check_set(gi[row], gs[row], oi[row], osc[row], lambda s, srow=srow: srow[s], t + 1, k,
+                  tol, t=t, what="ragged row %d" % row)
+
+
+def test_ragged_rejects_prefill_rows_and_bad_offset(api):
+    say("ragged rejects")
+    p = synth.make_problem(85, Bt=1, T=16, L=100, H=16)
+    q = torch.from_numpy(p["q"].view(np.int16)).to(DEV)
+    w = torch.from_numpy(p["w"]).to(DEV)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
+    with pytest.raises(api.SaError) as e:
+        api.indexer_score_topk_ragged(q, w, K, torch.tensor([50], dtype=torch.int32, device=DEV), 8)
+    assert e.value.code == api.SA_EUNSUPPORTED
