@@ -277,6 +277,10 @@ def main():
     result["fp8"] = bench_fp8(api, torch, dev, q, w, K, shape, flush, args.steps)
     result["lisa"], result["resmisa"] = bench_lisa_resmisa(api, torch, dev, q, w, K, shape, flush,
                                                            args.steps)
+    result["misa_hisa"] = bench_misa_hisa(api, torch, dev, q, w, K, shape, reps_b, reps_B, flush,
+                                          args.steps)
+    result["tidy"], result["ragged"] = bench_tidy_ragged(api, torch, dev, q, w, K, shape, outs,
+                                                         flush, args.steps)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(api, synth, torch, np, dev, args.prefill_iters)
@@ -420,6 +424,74 @@ def bench_lisa_resmisa(api, torch, dev, q, w, K, shape, flush, steps):
                                  "GB/s": round(eb / (ekus["block_extrema"] * 1e-6) / 1e9, 1)}
         out.append(o)
     return out[0], out[1]
+
+
+def bench_misa_hisa(api, torch, dev, q, w, K, shape, reps_b, reps_B, flush, steps):
+    """MISA x HISA on the same decode batch: h = 8 routed heads (B = 1024)
+    score the b = 128 blocks, r = 64 blocks kept, every head rescores their
+    8192 tokens; the pools are given (cache-side state, as in the step)."""
+    Bt, k = shape.batch, shape.topk
+    B, h, b, r = 1024, 8, 128, 64
+    oi = torch.empty((Bt, 1, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, 1, k), dtype=torch.float32, device=dev)
+    heads = torch.empty((Bt, 1, h), dtype=torch.int32, device=dev)
+    blocks = torch.empty((Bt, 1, r), dtype=torch.int32, device=dev)
+    ws = torch.empty(api.misa_hisa_ws(shape, B, h, b, r, True, True), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        api.misa_hisa(q, w, K, shape.causal_offset, k, B, h, b, r, pooled=reps_B, reps=reps_b,
+                      out_heads=heads, out_blocks=blocks, out_idx=oi, out_score=osc, ws=ws)
+
+    ms, kus = flushed_calls(api, torch, call, flush, steps)
+    return {"workload": "decode_128k_b8_h64_misa_hisa", "cache": "cold: a 1 GiB read before "
+            "each call", "config": {"B": B, "h": h, "b": b, "r": r, "pools": "given"},
+            "ms_per_call": ms, "scores_per_s": Bt * shape.L / (ms * 1e-3),
+            "kernels_us": {n: round(v, 2) for n, v in kus.items()}}
+
+
+def bench_tidy_ragged(api, torch, dev, q, w, K, shape, outs, flush, steps):
+    """The tidy-up of the DSA selector's 8 x 2048 indices (64-token pages), and
+    the DSA selector on a ragged batch of the same capacity: lengths 128K,
+    96K, 64K, 32K, 16K, 8K, 4K and 1K against the same batch padded to 128K."""
+    Bt, L, k = shape.batch, shape.L, shape.topk
+    idx = outs["dsa"][0]
+    slots = torch.empty_like(idx)
+    stats = torch.empty((Bt, 1, 3), dtype=torch.int32, device=dev)
+
+    def tidy():
+        api.tidy_indices(idx, 1, page_size=64, max_slots=L, out_slots=slots, out_stats=stats)
+
+    ms_t, kus_t = flushed_calls(api, torch, tidy, flush, steps)
+    st = stats.view(Bt, 3).cpu()
+    tidy_o = {"workload": "decode_128k_b8_h64_tidy", "page_size": 64, "k": k, "max_slots": L,
+              "avg_us": round(kus_t["tidy"], 2), "ms_per_call": ms_t,
+              "mean_pages_per_row": float(st[:, 1].float().mean()),
+              "mean_runs_per_row": float(st[:, 2].float().mean())}
+    lens = [L, L * 3 // 4, L // 2, L // 4, L // 8, L // 16, L // 32, L // 128][:Bt]
+    gl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    oi = torch.empty((Bt, 1, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, 1, k), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.indexer_score_topk_ragged_ws(shape), dtype=torch.uint8, device=dev)
+
+    def ragged():
+        api.indexer_score_topk_ragged(q, w, K, gl, k, total_len=sum(lens), out_idx=oi,
+                                      out_score=osc, ws=ws)
+
+    ms_r, kus_r = flushed_calls(api, torch, ragged, flush, steps)
+    full = torch.full((Bt,), L, dtype=torch.int32, device=dev)
+
+    def padded():
+        api.indexer_score_topk_ragged(q, w, K, full, k, total_len=Bt * L, out_idx=oi,
+                                      out_score=osc, ws=ws)
+
+    ms_p, kus_p = flushed_calls(api, torch, padded, flush, steps)
+    ragged_o = {"workload": "decode_b8_h64_ragged", "seq_lens": lens,
+                "ms_per_call": ms_r, "scores_per_s": sum(lens) / (ms_r * 1e-3),
+                "kernels_us": {n: round(v, 2) for n, v in kus_r.items()},
+                "padded_ms_per_call": ms_p,
+                "padded_kernels_us": {n: round(v, 2) for n, v in kus_p.items()}}
+    return tidy_o, ragged_o
 
 
 def bench_prefill(api, synth, torch, np, dev, iters):

@@ -101,14 +101,17 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
  *                entry, are dropped.  Slots must fit in int32.
  *   page_size    tokens per page (>= 1): slot = table[b][s / page_size] *
  *                page_size + s % page_size.
+ *   max_slots    number of physical slots (slots >= max_slots are dropped),
+ *                or 0 if unbounded.  With 0 < max_slots <= 2^18 the kernel
+ *                uses a bitmap in LDS (any k); otherwise it sorts (k <= 4096).
  *   out_slots    device int32 [rows, k]: the row's distinct slots in
  *                ascending order, then -1.
  *   out_stats    device int32 [rows, 3] (nullable): distinct slots, distinct
  *                pages (slot / page_size), maximal runs of consecutive slots.
- * k <= 4096 (SA_EUNSUPPORTED otherwise); errors as in indexer_score_topk. */
+ * Errors as in indexer_score_topk. */
 int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
                     const int32_t* block_table, int32_t pages_per_seq, int32_t page_size,
-                    int32_t* out_slots, int32_t* out_stats, void* stream);
+                    int32_t max_slots, int32_t* out_slots, int32_t* out_stats, void* stream);
 
 /* ------------------------------------------------------- ragged rows */
 
@@ -123,13 +126,17 @@ int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes);
  *             its history; its T query rows sit at positions
  *             seq_lens[b] - T + i (causal within the sequence).  Lengths are
  *             clamped to [T, L].  Work beyond a row's length is skipped.
+ *   total_len host-side sum of the lengths, or 0 if unknown: it only sizes
+ *             the key chunks per workgroup (the result does not depend on it),
+ *             so that a batch with a few long rows still spreads over the CUs.
  *   s         L is the per-sequence capacity (the keys' row stride);
  *             causal_offset must be L - T; T < 16 (decode-style rows).
  * Selection and outputs as in indexer_score_topk; other arguments,
  * ownership and errors likewise. */
 int indexer_score_topk_ragged(const uint16_t* q, const float* w, const uint16_t* keys,
-                              const int32_t* seq_lens, const sa_shape* s, int32_t* out_idx,
-                              float* out_score, void* ws, size_t ws_bytes, void* stream);
+                              const int32_t* seq_lens, int64_t total_len, const sa_shape* s,
+                              int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* ------------------------------------------------------------- FP8 keys */
 

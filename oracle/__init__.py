@@ -317,12 +317,13 @@ def dsa_ragged(q, w, K, seq_lens, topk, nthreads=0):
     return idx, sc, rs
 
 
-def tidy(idx, T, block_table=None, page_size=1):
-    """Index tidy-up ([PT] 2.2; counts of [PT] 2.3): per row of idx [rows, k]
-    (-1 empty), the physical slots table[b][s // page] * page + s % page (s
-    itself without a table; positions past the table or on a negative entry
-    dropped), distinct, ascending, -1 padded; stats [rows, 3] = (distinct
-    slots, distinct pages, maximal runs of consecutive slots)."""
+def tidy(idx, T, block_table=None, page_size=1, max_slots=0):
+    """Index tidy-up ([PT] 2.2; counts of [PT] 2.3).  Per row of idx [rows, k]
+    (-1 empty): the physical slots table[b][s // page] * page + s % page (s
+    itself without a table), dropping positions past the table, on a negative
+    entry, or (max_slots > 0) at or after max_slots; distinct, ascending, -1
+    padded.  stats [rows, 3] = (distinct slots, distinct pages, maximal runs of
+    consecutive slots)."""
     idx = np.asarray(idx).reshape(-1, np.asarray(idx).shape[-1])
     rows, k = idx.shape
     slots = np.full((rows, k), -1, np.int32)
@@ -337,6 +338,8 @@ def tidy(idx, T, block_table=None, page_size=1):
             phys = block_table[b][pg].astype(np.int64)
             keep = phys >= 0
             v = phys[keep] * page_size + v[keep] % page_size
+        if max_slots > 0:
+            v = v[v < max_slots]
         u = np.unique(v)
         slots[row, :len(u)] = u
         runs = 0 if len(u) == 0 else 1 + int(np.count_nonzero(np.diff(u) != 1))

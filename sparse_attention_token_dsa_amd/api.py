@@ -74,9 +74,9 @@ def load():
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
     lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
-    lib.sa_tidy_indices.argtypes = [P, I, I, I, P, I, I, P, P, P]
+    lib.sa_tidy_indices.argtypes = [P, I, I, I, P, I, I, I, P, P, P]
     lib.indexer_score_topk_ragged_ws.argtypes = [SP, ctypes.POINTER(S)]
-    lib.indexer_score_topk_ragged.argtypes = [P, P, P, P, SP, P, P, P, S, P]
+    lib.indexer_score_topk_ragged.argtypes = [P, P, P, P, ctypes.c_int64, SP, P, P, P, S, P]
     lib.misa_hisa_ws.argtypes = [SP, I, I, I, I, I, I, ctypes.POINTER(S)]
     lib.misa_hisa.argtypes = [P, P, P, SP, I, I, I, I, P, P, P, P, P, P, P, S, P]
     lib.lisa_score_topk_ws.argtypes = [SP, ctypes.POINTER(S)]
@@ -308,8 +308,8 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
 
 # ------------------------------------------------- tidy-up, ragged rows
 
-def tidy_indices(idx, T, block_table=None, page_size=1, out_slots=None, out_stats=None,
-                 want_stats=True):
+def tidy_indices(idx, T, block_table=None, page_size=1, max_slots=0, out_slots=None,
+                 out_stats=None, want_stats=True):
     """Selected positions [batch, T, k] (or [rows, k]) -> distinct physical
     slots in ascending order, -1 padded, and per-row (slots, pages, runs)."""
     if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous():
@@ -329,7 +329,7 @@ def tidy_indices(idx, T, block_table=None, page_size=1, out_slots=None, out_stat
         out_stats = torch.empty(idx.shape[:-1] + (3,), dtype=torch.int32, device=idx.device)
     _check(load().sa_tidy_indices(_p(idx), rows, int(T), k, _p(block_table),
                                   0 if block_table is None else block_table.shape[1],
-                                  int(page_size), _p(out_slots), _p(out_stats),
+                                  int(page_size), int(max_slots), _p(out_slots), _p(out_stats),
                                   _stream(idx.device)), "sa_tidy_indices")
     return out_slots, out_stats
 
@@ -341,18 +341,19 @@ def indexer_score_topk_ragged_ws(shape: Shape) -> int:
     return n.value
 
 
-def indexer_score_topk_ragged(q, w, keys, seq_lens, topk, out_idx=None, out_score=None,
-                              want_score=True, ws=None):
+def indexer_score_topk_ragged(q, w, keys, seq_lens, topk, total_len=0, out_idx=None,
+                              out_score=None, want_score=True, ws=None):
     """DSA over sequences of different lengths: keys [batch, L_cap, 128],
     seq_lens int32 [batch] on the GPU; row i of sequence b sits at
-    seq_lens[b] - T + i."""
+    seq_lens[b] - T + i.  total_len: the host's sum of the lengths (0 if
+    unknown), used only to size the work per workgroup."""
     if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != q.shape[0]:
         raise TypeError("seq_lens must be an int32 GPU tensor with one entry per sequence")
     s = _shape(q, w, keys, keys.shape[1] - q.shape[1], topk)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(indexer_score_topk_ragged_ws(s), q.device, ws)
     _check(load().indexer_score_topk_ragged(_p(q), _p(w), _p(keys), _p(seq_lens.contiguous()),
-                                            ctypes.byref(s), _p(out_idx), _p(out_score), _p(ws),
+                                            int(total_len), ctypes.byref(s), _p(out_idx), _p(out_score), _p(ws),
                                             ws.numel(), _stream(q.device)),
            "indexer_score_topk_ragged")
     return out_idx, out_score

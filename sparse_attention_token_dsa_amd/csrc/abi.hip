@@ -154,7 +154,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
                           uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
                           float* out_score, hipStream_t st, const uint8_t* codes = nullptr,
                           const float* kscale = nullptr, bool state_zeroed = false,
-                          const int32_t* seq_lens = nullptr) {
+                          const int32_t* seq_lens = nullptr, long long total_keys = 0) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
     hipError_t e;
@@ -174,7 +174,11 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.offset = s->causal_offset;
     a.len_div = 1;
     a.len_cap = s->L;
-    a.chunk = codes ? sa::scan8_chunk(rows, s->L) : sa::scan_chunk(4, rows, s->L);
+    // Keys per workgroup from the work there is: rows x L, or for ragged
+    // batches the caller's total of the sequence lengths when given.
+    const long long work = total_keys > 0 ? total_keys : rows * (long long)s->L;
+    const int wrk = (int)std::min<long long>(work, 1LL << 30);
+    a.chunk = codes ? sa::scan8_chunk(1, wrk) : sa::scan_chunk(4, 1, wrk);
     a.scores = scores;
     a.score_stride = score_stride(s->L);
     a.state = state;
@@ -424,11 +428,14 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
 
 int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
                     const int32_t* block_table, int32_t pages_per_seq, int32_t page_size,
-                    int32_t* out_slots, int32_t* out_stats, void* stream) {
+                    int32_t max_slots, int32_t* out_slots, int32_t* out_stats, void* stream) {
     if (!idx || !out_slots) return fail(SA_EINVAL, "idx and out_slots must be non-NULL");
     if (rows < 1 || T < 1 || rows % T != 0) return fail(SA_EINVAL, "need rows >= 1, T >= 1, T | rows");
     if (k < 1) return fail(SA_EINVAL, "k must be >= 1");
-    if (k > sa::kTidyMax) return fail(SA_EUNSUPPORTED, "k must be <= 4096");
+    if (max_slots < 0) return fail(SA_EINVAL, "max_slots must be >= 0");
+    const bool bitmap = max_slots > 0 && max_slots <= sa::kTidyBitmapMax;
+    if (!bitmap && k > sa::kTidyMax)
+        return fail(SA_EUNSUPPORTED, "k > 4096 needs a slot bound max_slots <= 2^18");
     if (page_size < 1) return fail(SA_EINVAL, "page_size must be >= 1");
     if (block_table && pages_per_seq < 1) return fail(SA_EINVAL, "pages_per_seq must be >= 1");
     sa::TidyArgs a{};
@@ -441,6 +448,7 @@ int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
     a.table = block_table;
     a.pages_per_seq = block_table ? pages_per_seq : 0;
     a.page = page_size;
+    a.max_slots = max_slots;
     a.out_slots = out_slots;
     a.out_stats = out_stats;
     hipError_t e = sa::launch_tidy(a, rows, static_cast<hipStream_t>(stream));
@@ -469,20 +477,22 @@ int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes) {
 }
 
 int indexer_score_topk_ragged(const uint16_t* q, const float* w, const uint16_t* keys,
-                              const int32_t* seq_lens, const sa_shape* s, int32_t* out_idx,
-                              float* out_score, void* ws, size_t ws_bytes, void* stream) {
+                              const int32_t* seq_lens, int64_t total_len, const sa_shape* s,
+                              int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes,
+                              void* stream) {
     int rc = check_ragged(s);
     if (rc) return rc;
     rc = check_ptrs(q, w, keys, out_idx);
     if (rc) return rc;
     if (!seq_lens) return fail(SA_EINVAL, "seq_lens is NULL");
+    if (total_len < 0) return fail(SA_EINVAL, "total_len must be >= 0");
     const size_t need = plan_dsa(s, nullptr).bytes;
     if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
     void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     DsaPlan p = plan_dsa(s, base);
     hipError_t e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand,
                                   s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
-                                  nullptr, nullptr, false, seq_lens);
+                                  nullptr, nullptr, false, seq_lens, total_len);
     if (e != hipSuccess) return hip_fail(e, "ragged decode scan");
     return SA_OK;
 }

@@ -222,11 +222,13 @@ struct ResmisaArgs {
 };
 
 // Index tidy-up: per row, physical slots sorted ascending, unique, -1 padded.
-constexpr int kTidyMax = 4096;  // selected indices per row
+constexpr int kTidyMax = 4096;          // selected indices per row (sorting form)
+constexpr int kTidyBitmapMax = 1 << 18;  // slot bound of the bitmap form (32 KiB of LDS)
 struct TidyArgs {
     const int32_t* idx;     // [rows, k], -1 = empty
     int k, T;
     int n2;                 // sort width: power of two >= max(k, 256)
+    int max_slots;          // slots >= max_slots are dropped (0: no bound)
     const int32_t* table;   // [batch, pages_per_seq] physical page of each logical page, or null
     int pages_per_seq, page;
     int32_t* out_slots;     // [rows, k]

@@ -7,10 +7,13 @@
 //
 // One workgroup per query row: each selected position s (>= 0) becomes its
 // physical slot table[b][s / page] * page + s % page (or s itself without a
-// table), the slots are sorted in LDS (bitonic, ascending), duplicates are
-// dropped, and the row's unique slots are written in order, -1 padded, with
-// three counts: unique slots, distinct pages, maximal runs of consecutive
-// slots.
+// table), duplicates are dropped, and the row's unique slots are written in
+// ascending order, -1 padded, with three counts: unique slots, distinct pages,
+// maximal runs of consecutive slots.  Two forms:
+//  - bitmap (slot bound known and <= 2^18): one bit per slot in LDS, set
+//    with LDS atomics, then each thread walks its words with a popcount
+//    prefix sum for its output position;
+//  - sort (any slot range, k <= 4096): bitonic sort of the slots in LDS.
 #include "sa_common.h"
 
 namespace sa {
@@ -18,6 +21,105 @@ namespace sa {
 namespace {
 
 constexpr int kTidyThreads = 256;
+
+// Physical slot of selected position s of sequence b, or -1 (empty, past the
+// table, an unmapped page, or at/after the slot bound).
+__device__ __forceinline__ int tidy_slot(const TidyArgs& a, const int32_t* tab, int s) {
+    if (s < 0) return -1;
+    int v = s;
+    if (tab) {
+        const int pg = s / a.page;
+        if (pg >= a.pages_per_seq) return -1;
+        const int phys = tab[pg];
+        if (phys < 0) return -1;
+        v = phys * a.page + (s - pg * a.page);
+    }
+    if (a.max_slots > 0 && v >= a.max_slots) return -1;
+    return v;
+}
+
+// Block-wide sums of two per-thread counts (part: kTidyThreads ints of LDS).
+__device__ __forceinline__ void tidy_write_stats(const TidyArgs& a, int row, int total, int np,
+                                                 int ns, int* part) {
+    const int tid = threadIdx.x;
+    __syncthreads();
+    part[tid] = np;
+    __syncthreads();
+    for (int off = kTidyThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) part[tid] += part[tid + off];
+        __syncthreads();
+    }
+    const int pages = part[0];
+    __syncthreads();
+    part[tid] = ns;
+    __syncthreads();
+    for (int off = kTidyThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) part[tid] += part[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) {
+        int32_t* st = a.out_stats + (long long)row * 3;
+        st[0] = total;
+        st[1] = pages;
+        st[2] = part[0];
+    }
+}
+
+__global__ __launch_bounds__(kTidyThreads) void tidy_bitmap_kernel(TidyArgs a) {
+    extern __shared__ uint32_t bits[];  // ceil(max_slots / 32) words
+    __shared__ int part[kTidyThreads];
+    __shared__ int lastv[kTidyThreads];
+    const int row = blockIdx.x;
+    const int b = row / a.T;
+    const int tid = threadIdx.x;
+    const int nw = (a.max_slots + 31) >> 5;
+    for (int x = tid; x < nw; x += kTidyThreads) bits[x] = 0u;
+    __syncthreads();
+    const int32_t* in = a.idx + (long long)row * a.k;
+    const int32_t* tab = a.table ? a.table + (long long)b * a.pages_per_seq : nullptr;
+    for (int x = tid; x < a.k; x += kTidyThreads) {
+        const int v = tidy_slot(a, tab, in[x]);
+        if (v >= 0) atomicOr(&bits[v >> 5], 1u << (v & 31));
+    }
+    __syncthreads();
+    const int wpt = (nw + kTidyThreads - 1) / kTidyThreads;
+    const int w0 = min(tid * wpt, nw), w1 = min(w0 + wpt, nw);
+    int cnt = 0, last = -1;
+    for (int x = w0; x < w1; ++x) {
+        const uint32_t m = bits[x];
+        cnt += __popc(m);
+        if (m) last = x * 32 + 31 - __clz(m);
+    }
+    part[tid] = cnt;
+    lastv[tid] = last;
+    __syncthreads();
+    for (int off = 1; off < kTidyThreads; off <<= 1) {  // inclusive sum and max scans
+        const int add = tid >= off ? part[tid - off] : 0;
+        const int mx = tid >= off ? lastv[tid - off] : -1;
+        __syncthreads();
+        part[tid] += add;
+        lastv[tid] = max(lastv[tid], mx);
+        __syncthreads();
+    }
+    int pos = part[tid] - cnt;
+    const int total = part[kTidyThreads - 1];
+    int prev = tid > 0 ? lastv[tid - 1] : -1;  // the largest slot before my words
+    int np = 0, ns = 0;
+    int32_t* out = a.out_slots + (long long)row * a.k;
+    for (int x = w0; x < w1; ++x) {
+        uint32_t m = bits[x];
+        while (m) {
+            const int v = x * 32 + __ffs(m) - 1;
+            m &= m - 1u;
+            out[pos++] = v;
+            if (prev < 0 || prev / a.page != v / a.page) ++np;
+            if (prev < 0 || prev + 1 != v) ++ns;
+            prev = v;
+        }
+    }
+    for (int x = total + tid; x < a.k; x += kTidyThreads) out[x] = -1;
+    if (a.out_stats) tidy_write_stats(a, row, total, np, ns, part);
+}
 
 __global__ __launch_bounds__(kTidyThreads) void tidy_kernel(TidyArgs a) {
     const int row = blockIdx.x;
@@ -31,18 +133,8 @@ __global__ __launch_bounds__(kTidyThreads) void tidy_kernel(TidyArgs a) {
     for (int x = tid; x < n2; x += kTidyThreads) {
         uint32_t v = 0xffffffffu;  // empty / invalid: sorts last
         if (x < a.k) {
-            const int s = in[x];
-            if (s >= 0) {
-                if (!tab) {
-                    v = (uint32_t)s;
-                } else {
-                    const int pg = s / a.page;
-                    if (pg < a.pages_per_seq) {
-                        const int phys = tab[pg];
-                        if (phys >= 0) v = (uint32_t)phys * (uint32_t)a.page + (uint32_t)(s - pg * a.page);
-                    }
-                }
-            }
+            const int s = tidy_slot(a, tab, in[x]);
+            if (s >= 0) v = (uint32_t)s;
         }
         key[x] = v;
     }
@@ -97,36 +189,18 @@ __global__ __launch_bounds__(kTidyThreads) void tidy_kernel(TidyArgs a) {
         out[pos++] = (int32_t)v;
     }
     for (int x = total + tid; x < a.k; x += kTidyThreads) out[x] = -1;
-    if (a.out_stats) {
-        __syncthreads();
-        part[tid] = np;
-        __syncthreads();
-        for (int off = kTidyThreads / 2; off > 0; off >>= 1) {
-            if (tid < off) part[tid] += part[tid + off];
-            __syncthreads();
-        }
-        const int pages = part[0];
-        __syncthreads();
-        part[tid] = ns;
-        __syncthreads();
-        for (int off = kTidyThreads / 2; off > 0; off >>= 1) {
-            if (tid < off) part[tid] += part[tid + off];
-            __syncthreads();
-        }
-        if (tid == 0) {
-            int32_t* st = a.out_stats + (long long)row * 3;
-            st[0] = total;
-            st[1] = pages;
-            st[2] = part[0];
-        }
-    }
+    if (a.out_stats) tidy_write_stats(a, row, total, np, ns, part);
 }
 
 }  // namespace
 
 hipError_t launch_tidy(const TidyArgs& a, int rows, hipStream_t s) {
     prof_begin(K_TIDY, s);
-    tidy_kernel<<<dim3((unsigned)rows), dim3(kTidyThreads), 0, s>>>(a);
+    if (a.max_slots > 0 && a.max_slots <= kTidyBitmapMax)
+        tidy_bitmap_kernel<<<dim3((unsigned)rows), dim3(kTidyThreads),
+                             (size_t)((a.max_slots + 31) >> 5) * 4, s>>>(a);
+    else
+        tidy_kernel<<<dim3((unsigned)rows), dim3(kTidyThreads), 0, s>>>(a);
     prof_end(K_TIDY, s);
     return hipGetLastError();
 }

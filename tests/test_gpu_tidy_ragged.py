@@ -32,12 +32,12 @@ def api():
     return a
 
 
-def _tidy_both(api, idx, T, table, page):
+def _tidy_both(api, idx, T, table, page, max_slots=0):
     gi = torch.from_numpy(idx.astype(np.int32)).to(DEV)
     gt = None if table is None else torch.from_numpy(table.astype(np.int32)).to(DEV)
-    slots, stats = api.tidy_indices(gi, T, block_table=gt, page_size=page)
+    slots, stats = api.tidy_indices(gi, T, block_table=gt, page_size=page, max_slots=max_slots)
     torch.cuda.synchronize()
-    os_, ost = oracle.tidy(idx, T, block_table=table, page_size=page)
+    os_, ost = oracle.tidy(idx, T, block_table=table, page_size=page, max_slots=max_slots)
     assert np.array_equal(_np(slots).reshape(os_.shape), os_)
     assert np.array_equal(_np(stats).reshape(ost.shape), ost)
 
@@ -60,7 +60,17 @@ def test_tidy(api, rows, T, k, page, span, tabled):
         table = rng.permutation(3 * npages)[: (rows // T) * npages].reshape(rows // T, npages)
         table[rng.random(table.shape) < 0.05] = -1
         table = table[:, : npages - 1]      # the last logical page has no entry
-    _tidy_both(api, idx, T, table, page)
+    bound = 3 * ((span + page - 1) // page) * page if tabled else span
+    _tidy_both(api, idx, T, table, page)                  # sorting form
+    _tidy_both(api, idx, T, table, page, bound)           # bitmap form
+    _tidy_both(api, idx, T, table, page, bound // 2 + 1)  # bitmap, part of the slots dropped
+
+
+def test_tidy_bitmap_beyond_the_sort_limit(api):
+    say("tidy k=6000 bitmap")
+    rng = np.random.default_rng(9)
+    idx = rng.integers(-1, 200000, size=(3, 6000))
+    _tidy_both(api, idx, 1, None, 64, 200000)
 
 
 def test_tidy_of_a_selector_output(api):
@@ -73,6 +83,7 @@ def test_tidy_of_a_selector_output(api):
     idx, _ = api.indexer_score_topk(q, w, K, p["offset"], 2048)
     torch.cuda.synchronize()
     _tidy_both(api, _np(idx).reshape(4, 2048), 1, None, 64)
+    _tidy_both(api, _np(idx).reshape(4, 2048), 1, None, 64, 32768)
 
 
 @pytest.mark.parametrize("Bt,T,L,H,k,lens", [
@@ -88,7 +99,9 @@ def test_ragged(api, Bt, T, L, H, k, lens):
     w = torch.from_numpy(p["w"]).to(DEV)
     K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
     gl = torch.from_numpy(lens).to(DEV)
-    idx, sc = api.indexer_score_topk_ragged(q, w, K, gl, k)
+    # the total length only sizes the work per workgroup: give it on odd batch sizes
+    idx, sc = api.indexer_score_topk_ragged(q, w, K, gl, k,
+                                            total_len=int(lens.sum()) if Bt % 2 else 0)
     torch.cuda.synchronize()
     oi, osc, rs = oracle.dsa_ragged(p["q"], p["w"], p["K"], lens, k)
     gi, gs = _np(idx).reshape(-1, k), _np(sc).reshape(-1, k)

@@ -27,6 +27,10 @@ def test_tidy_hand_example():
     # 5 -> 453, 3 -> 451, 64 -> 128, 65 -> 129, 200 -> 8
     assert slots[0].tolist() == [8, 128, 129, 451, 453, -1, -1, -1]
     assert stats[0].tolist() == [5, 3, 4]
+    # a pool of 200 slots: 451 and 453 are dropped
+    slots, stats = oracle.tidy(idx, 1, block_table=table, page_size=64, max_slots=200)
+    assert slots[0].tolist() == [8, 128, 129, -1, -1, -1, -1, -1]
+    assert stats[0].tolist() == [3, 2, 2]
 
 
 def test_tidy_against_loops_and_invariances():
