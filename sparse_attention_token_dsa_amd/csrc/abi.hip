@@ -761,7 +761,7 @@ int sa_pool_blocks2(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, i
 static int route_heads(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int block_B, int h, const uint16_t* pooled,
                        uint16_t* pooled_ws, uint16_t* tail, uint8_t* flag, int32_t* heads,
-                       hipStream_t st) {
+                       hipStream_t st, uint32_t* zero_state = nullptr) {
     const int rows = s->batch * s->T;
     const int nblk = (s->L + block_B - 1) / block_B;
     hipError_t e;
@@ -791,6 +791,7 @@ static int route_heads(const uint16_t* q, const float* w, const uint16_t* keys,
     ra.h = h;
     ra.heads_out = heads;
     ra.E_out = nullptr;
+    ra.zero_state = zero_state;
     e = sa::launch_router(ra, rows, st);
     if (e != hipSuccess) return hip_fail(e, "router");
     return SA_OK;
@@ -825,17 +826,17 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     hipError_t e;
     int32_t* heads = out_heads ? out_heads : p.heads;
     rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
-                     p.flag, heads, st);
+                     p.flag, heads, st, p.state);
     if (rc) return rc;
     if (k_prime == 0) {
         e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, s->topk,
-                           out_idx, out_score, st);
+                           out_idx, out_score, st, nullptr, nullptr, /*state_zeroed=*/true);
         if (e != hipSuccess) return hip_fail(e, "routed scan");
         return SA_OK;
     }
     int32_t* pool_idx = out_pool ? out_pool : p.pool_idx;
     e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, k_prime, pool_idx,
-                       nullptr, st);
+                       nullptr, st, nullptr, nullptr, /*state_zeroed=*/true);
     if (e != hipSuccess) return hip_fail(e, "routed scan");
     sa::GatherArgs ga{};
     ga.q = q;

@@ -201,6 +201,7 @@ struct RouterArgs {
     int T, H, offset, B, nblk, h;
     int32_t* heads_out;     // [rows, h]
     float* E_out;           // [rows, H] or null
+    uint32_t* zero_state;   // [rows, kRowState] cleared for the routed scan that follows, or null
 };
 
 // LISA / ResMiSA head rows and routing.

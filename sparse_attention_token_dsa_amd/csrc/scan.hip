@@ -286,6 +286,11 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
         const int pos = __popcll(msk & ((1ull << lane) - 1ull));
         if (sel) a.heads_out[(long long)row * a.h + pos] = j;
     }
+    // The routed scan that follows adds its histogram into a zeroed row state
+    // (one launch fewer on the MISA path).
+    if (a.zero_state)
+        for (int x = threadIdx.x; x < kRowState; x += 256)
+            a.zero_state[(long long)row * kRowState + x] = 0u;
 }
 
 // ------------------------------------------------------------- tail
