@@ -90,25 +90,59 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
         s_nc = 0;
     }
     __syncthreads();
+    // Each thread classifies its 16 scores (4 float4 loads, all issued first),
+    // then one wave-level prefix sum of its (emit, candidate) counts and one
+    // LDS atomic per wave and kind give it its staging slots.
     const float* src = a.dense + (long long)row * a.dense_stride;
-    for (int u0 = lo + tid * 4; u0 < hi; u0 += kFilterThreads * 4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(src + u0);
-        const float vs[4] = {v4.x, v4.y, v4.z, v4.w};
+    constexpr int kPer = kFilterChunk / kFilterThreads;  // 16 scores per thread
+    float vs[kPer];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int u = u0 + j;
-            const bool in = u < hi;
-            const uint32_t dig = ord_key(vs[j]) >> (32 - kHist0Bits);
-            const bool emit = in && (dig > d || (take_all && dig == d));
-            const bool app = in && !take_all && dig == d;
-            const int slot = wave_append(emit, &s_ne);
-            if (emit) {
-                s_idx[slot] = u;
-                s_sc[slot] = vs[j];
-            }
-            const int cslot = wave_append(app, &s_nc);
-            if (app) s_cand[cslot] = make_key(vs[j], u);
+    for (int i = 0; i < kPer / 4; ++i) {
+        const int u0 = lo + (tid + i * kFilterThreads) * 4;
+        float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u0 < hi) v4 = *reinterpret_cast<const float4*>(src + u0);
+        vs[4 * i] = v4.x;
+        vs[4 * i + 1] = v4.y;
+        vs[4 * i + 2] = v4.z;
+        vs[4 * i + 3] = v4.w;
+    }
+    uint32_t emask = 0u, cmask = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int u = lo + (tid + (j >> 2) * kFilterThreads) * 4 + (j & 3);
+        const bool in = u < hi;
+        const uint32_t dig = ord_key(vs[j]) >> (32 - kHist0Bits);
+        if (in && (dig > d || (take_all && dig == d))) emask |= 1u << j;
+        if (in && !take_all && dig == d) cmask |= 1u << j;
+    }
+    const int lane = lane_id();
+    const int mine = __popc(emask) | (__popc(cmask) << 16);
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    int wbase = 0;
+    if (lane == 63) {
+        const int te = incl & 0xffff, tc = incl >> 16;
+        const int be = te ? atomicAdd(&s_ne, te) : 0;
+        const int bc = tc ? atomicAdd(&s_nc, tc) : 0;
+        wbase = be | (bc << 16);
+    }
+    wbase = __shfl(wbase, 63);
+    const int excl = incl - mine;
+    int se = (wbase & 0xffff) + (excl & 0xffff);
+    int sc2 = (wbase >> 16) + (excl >> 16);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int u = lo + (tid + (j >> 2) * kFilterThreads) * 4 + (j & 3);
+        if (emask & (1u << j)) {
+            s_idx[se] = u;
+            s_sc[se] = vs[j];
+            ++se;
         }
+        if (cmask & (1u << j)) s_cand[sc2++] = make_key(vs[j], u);
     }
     __syncthreads();
     if (tid == 0) {
