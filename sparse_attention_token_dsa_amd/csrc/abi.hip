@@ -34,7 +34,6 @@ std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_free_events;
 double g_ms[sa::K_COUNT];
 long long g_launches[sa::K_COUNT];
-int g_open = -1;  // index of the record awaiting its stop event
 
 hipEvent_t take_event() {
     if (!g_free_events.empty()) {
@@ -319,23 +318,49 @@ int check_hisa(const sa_shape* s, int b, int r) {
 
 namespace sa {
 
+// The open record of this host thread: its index in g_recs, or -1.
+static thread_local int t_open = -1;
+static thread_local bool t_taken = false;
+
+void prof_reset_thread() {
+    t_open = -1;
+    t_taken = false;
+}
+
 void prof_begin(int kid, hipStream_t s) {
+    (void)s;
     if (!g_prof_on) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) return;
     hipEvent_t a = take_event(), b = take_event();
     if (!a || !b) return;
-    (void)hipEventRecord(a, s);
     g_recs.push_back(ProfRec{kid, a, b});
-    g_open = (int)g_recs.size() - 1;
+    t_open = (int)g_recs.size() - 1;
+    t_taken = false;
+}
+
+bool prof_pending(hipEvent_t* start, hipEvent_t* stop) {
+    if (t_open < 0 || t_taken) return false;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (t_open < 0 || t_open >= (int)g_recs.size()) return false;
+    *start = g_recs[t_open].start;
+    *stop = g_recs[t_open].stop;
+    t_taken = true;
+    return true;
 }
 
 void prof_end(int kid, hipStream_t s) {
-    if (!g_prof_on) return;
+    (void)s;
+    if (t_open < 0) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (g_open < 0 || g_recs[g_open].kid != kid) return;
-    (void)hipEventRecord(g_recs[g_open].stop, s);
-    g_open = -1;
+    if (t_open < (int)g_recs.size() && g_recs[t_open].kid == kid && !t_taken) {
+        // no kernel was launched: drop the record
+        g_free_events.push_back(g_recs[t_open].start);
+        g_free_events.push_back(g_recs[t_open].stop);
+        g_recs.erase(g_recs.begin() + t_open);
+    }
+    t_open = -1;
+    t_taken = false;
 }
 
 }  // namespace sa
@@ -354,7 +379,7 @@ int sa_profile_enable(int32_t on) {
         }
     }
     g_prof_on = on != 0;
-    g_open = -1;
+    sa::prof_reset_thread();
     return SA_OK;
 }
 

@@ -296,7 +296,7 @@ hipError_t launch_extrema(const uint16_t* keys, int batch, int L, int block, uin
                           hipStream_t s) {
     const int nblk = (L + block - 1) / block;
     prof_begin(K_EXTREMA, s);
-    extrema_kernel<<<dim3((unsigned)nblk, (unsigned)batch), dim3(256), 0, s>>>(keys, L, block,
+    sa_launch(extrema_kernel, dim3((unsigned)nblk, (unsigned)batch), dim3(256), 0, s, keys, L, block,
                                                                               nblk, out);
     prof_end(K_EXTREMA, s);
     return hipGetLastError();
@@ -306,7 +306,7 @@ hipError_t launch_extrema_tail(const uint16_t* keys, long long seq_stride, int T
                                int L, int block, int rows, uint16_t* tail, uint8_t* flag,
                                hipStream_t s) {
     prof_begin(K_EXTREMA, s);
-    extrema_tail_kernel<<<dim3((unsigned)rows), dim3(256), 0, s>>>(keys, seq_stride, T, offset,
+    sa_launch(extrema_tail_kernel, dim3((unsigned)rows), dim3(256), 0, s, keys, seq_stride, T, offset,
                                                                    L, block, tail, flag);
     prof_end(K_EXTREMA, s);
     return hipGetLastError();
@@ -317,10 +317,10 @@ hipError_t launch_resmisa_router(const ResmisaArgs& a, int rows, hipStream_t s) 
     const int nht = (a.H + 15) / 16;
     prof_begin(K_RES_ROUTER, s);
     switch (nht) {
-        case 1: resmisa_router_kernel<1><<<grid, dim3(256), 0, s>>>(a); break;
-        case 2: resmisa_router_kernel<2><<<grid, dim3(256), 0, s>>>(a); break;
-        case 3: resmisa_router_kernel<3><<<grid, dim3(256), 0, s>>>(a); break;
-        default: resmisa_router_kernel<4><<<grid, dim3(256), 0, s>>>(a); break;
+        case 1: sa_launch(resmisa_router_kernel<1>, grid, dim3(256), 0, s, a); break;
+        case 2: sa_launch(resmisa_router_kernel<2>, grid, dim3(256), 0, s, a); break;
+        case 3: sa_launch(resmisa_router_kernel<3>, grid, dim3(256), 0, s, a); break;
+        default: sa_launch(resmisa_router_kernel<4>, grid, dim3(256), 0, s, a); break;
     }
     prof_end(K_RES_ROUTER, s);
     return hipGetLastError();
@@ -328,7 +328,7 @@ hipError_t launch_resmisa_router(const ResmisaArgs& a, int rows, hipStream_t s) 
 
 hipError_t launch_head_rows(const ResmisaArgs& a, int rows, hipStream_t s) {
     prof_begin(K_HEAD_ROWS, s);
-    head_rows_kernel<<<dim3((unsigned)rows), dim3(128), 0, s>>>(a);
+    sa_launch(head_rows_kernel, dim3((unsigned)rows), dim3(128), 0, s, a);
     prof_end(K_HEAD_ROWS, s);
     return hipGetLastError();
 }

@@ -56,7 +56,7 @@ hipError_t launch_quantize_fp8(const uint16_t* keys, long long n, uint8_t* codes
                                hipStream_t s) {
     if (n <= 0) return hipSuccess;
     prof_begin(K_QUANT8, s);
-    quantize_fp8_kernel<<<dim3((unsigned)((n + 15) / 16)), dim3(256), 0, s>>>(keys, n, codes, scales);
+    sa_launch(quantize_fp8_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), 0, s, keys, n, codes, scales);
     prof_end(K_QUANT8, s);
     return hipGetLastError();
 }
@@ -143,7 +143,7 @@ hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16
                        hipStream_t s) {
     const int nblk = (L + block - 1) / block;
     prof_begin(K_POOL, s);
-    pool_kernel<<<dim3(nblk, batch), dim3(256), 0, s>>>(keys, L, block, nblk, out);
+    sa_launch(pool_kernel, dim3(nblk, batch), dim3(256), 0, s, keys, L, block, nblk, out);
     prof_end(K_POOL, s);
     return hipGetLastError();
 }
@@ -153,7 +153,7 @@ hipError_t launch_pool2(const uint16_t* keys, int batch, int L, int small, int l
     const int nsmall = (L + small - 1) / small;
     const int nlarge = (L + large - 1) / large;
     prof_begin(K_POOL2, s);
-    pool2_kernel<<<dim3(nlarge, batch), dim3(256), 0, s>>>(keys, L, small, large, nsmall,
+    sa_launch(pool2_kernel, dim3(nlarge, batch), dim3(256), 0, s, keys, L, small, large, nsmall,
                                                            nlarge, out_small, out_large);
     prof_end(K_POOL2, s);
     return hipGetLastError();

@@ -765,10 +765,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
     const int nht = (a.H + 15) / 16;
     prof_begin(K_PREFILL, s);
     switch (nht) {
-        case 1: prefill_kernel<1><<<grid, dim3(64 * kPfWaves), 0, s>>>(a); break;
-        case 2: prefill_kernel<2><<<grid, dim3(64 * kPfWaves), 0, s>>>(a); break;
-        case 3: prefill_kernel<3><<<grid, dim3(64 * kPfWaves), 0, s>>>(a); break;
-        default: prefill_kernel<4><<<grid, dim3(64 * kPfWaves), 0, s>>>(a); break;
+        case 1: sa_launch(prefill_kernel<1>, grid, dim3(64 * kPfWaves), 0, s, a); break;
+        case 2: sa_launch(prefill_kernel<2>, grid, dim3(64 * kPfWaves), 0, s, a); break;
+        case 3: sa_launch(prefill_kernel<3>, grid, dim3(64 * kPfWaves), 0, s, a); break;
+        default: sa_launch(prefill_kernel<4>, grid, dim3(64 * kPfWaves), 0, s, a); break;
     }
     prof_end(K_PREFILL, s);
     return hipGetLastError();

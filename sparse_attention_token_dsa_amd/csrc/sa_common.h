@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace sa {
@@ -144,8 +145,26 @@ enum KernelId {
 };
 
 // Host side: bracket a launch with profiling events when enabled.
+// Per-kernel timing (sa_profile_enable).  prof_begin(kid, s) opens a record
+// whose events the next sa_launch on this host thread attaches to its own
+// dispatch (hipExtLaunchKernelGGL), so they time the kernel and not the
+// dispatch gap before it; prof_end closes the record (dropped if no kernel
+// was launched in between).
 void prof_begin(int kid, hipStream_t s);
 void prof_end(int kid, hipStream_t s);
+bool prof_pending(hipEvent_t* start, hipEvent_t* stop);  // takes the open record's events
+void prof_reset_thread();
+
+// Every kernel launch of the library goes through here.
+template <typename... KArgs, typename... Args>
+inline void sa_launch(void (*kern)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                      Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (prof_pending(&e0, &e1))
+        hipExtLaunchKernelGGL(kern, grid, block, lds, s, e0, e1, 0u, static_cast<KArgs>(args)...);
+    else
+        kern<<<grid, block, lds, s>>>(static_cast<KArgs>(args)...);
+}
 
 // ---------------------------------------------------- launch records
 

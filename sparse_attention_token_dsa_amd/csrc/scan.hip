@@ -352,7 +352,7 @@ hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s) 
     long long blocks = (n + 255) / 256;
     if (blocks > 2048) blocks = 2048;
     prof_begin(K_FILL, s);
-    fill_u32_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(p, n, v);
+    sa_launch(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
     prof_end(K_FILL, s);
     return hipGetLastError();
 }
@@ -375,14 +375,14 @@ static void scan_dispatch_hist(const ScanArgs& a, dim3 grid, hipStream_t s) {
     constexpr int NB = scan_bufs<KS>();
     if (a.heads) {
         if (a.state)
-            scan_kernel<NHT, KS, G, NB, NSTEP, true, true><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
+            sa_launch(scan_kernel<NHT, KS, G, NB, NSTEP, true, true>, grid, dim3(64 * scan_waves<KS>()), 0, s, a);
         else
-            scan_kernel<NHT, KS, G, NB, NSTEP, false, true><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
+            sa_launch(scan_kernel<NHT, KS, G, NB, NSTEP, false, true>, grid, dim3(64 * scan_waves<KS>()), 0, s, a);
     } else {
         if (a.state)
-            scan_kernel<NHT, KS, G, NB, NSTEP, true, false><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
+            sa_launch(scan_kernel<NHT, KS, G, NB, NSTEP, true, false>, grid, dim3(64 * scan_waves<KS>()), 0, s, a);
         else
-            scan_kernel<NHT, KS, G, NB, NSTEP, false, false><<<grid, dim3(64 * scan_waves<KS>()), 0, s>>>(a);
+            sa_launch(scan_kernel<NHT, KS, G, NB, NSTEP, false, false>, grid, dim3(64 * scan_waves<KS>()), 0, s, a);
     }
 }
 
@@ -454,9 +454,9 @@ hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode
     prof_begin(K_GATHER, s);
 #define SA_GATHER(N)                                                            \
     if (block_mode)                                                             \
-        gather_kernel<N, true><<<grid, dim3(256), 0, s>>>(a);                   \
+        sa_launch(gather_kernel<N, true>, grid, dim3(256), 0, s, a);                   \
     else                                                                        \
-        gather_kernel<N, false><<<grid, dim3(256), 0, s>>>(a);
+        sa_launch(gather_kernel<N, false>, grid, dim3(256), 0, s, a);
     switch (nht) {
         case 1: SA_GATHER(1) break;
         case 2: SA_GATHER(2) break;
@@ -472,10 +472,10 @@ hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s) {
     const int nht = (a.H + 15) / 16;
     prof_begin(K_ROUTER, s);
     switch (nht) {
-        case 1: router_kernel<1><<<dim3(rows), dim3(256), 0, s>>>(a); break;
-        case 2: router_kernel<2><<<dim3(rows), dim3(256), 0, s>>>(a); break;
-        case 3: router_kernel<3><<<dim3(rows), dim3(256), 0, s>>>(a); break;
-        default: router_kernel<4><<<dim3(rows), dim3(256), 0, s>>>(a); break;
+        case 1: sa_launch(router_kernel<1>, dim3(rows), dim3(256), 0, s, a); break;
+        case 2: sa_launch(router_kernel<2>, dim3(rows), dim3(256), 0, s, a); break;
+        case 3: sa_launch(router_kernel<3>, dim3(rows), dim3(256), 0, s, a); break;
+        default: sa_launch(router_kernel<4>, dim3(rows), dim3(256), 0, s, a); break;
     }
     prof_end(K_ROUTER, s);
     return hipGetLastError();
@@ -484,7 +484,7 @@ hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s) {
 hipError_t launch_tail(const uint16_t* keys, long long seq_stride, int T, int offset, int L,
                        int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s) {
     prof_begin(K_TAIL, s);
-    tail_kernel<<<dim3(rows), dim3(256), 0, s>>>(keys, seq_stride, T, offset, L, block, tail,
+    sa_launch(tail_kernel, dim3(rows), dim3(256), 0, s, keys, seq_stride, T, offset, L, block, tail,
                                                  flag);
     prof_end(K_TAIL, s);
     return hipGetLastError();

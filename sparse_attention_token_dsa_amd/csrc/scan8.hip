@@ -224,9 +224,9 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
 template <int NHT>
 void scan8_dispatch(const ScanArgs& a, dim3 grid, hipStream_t s) {
     if (a.state)
-        scan8_kernel<NHT, true><<<grid, dim3(64 * kS8Waves), 0, s>>>(a);
+        sa_launch(scan8_kernel<NHT, true>, grid, dim3(64 * kS8Waves), 0, s, a);
     else
-        scan8_kernel<NHT, false><<<grid, dim3(64 * kS8Waves), 0, s>>>(a);
+        sa_launch(scan8_kernel<NHT, false>, grid, dim3(64 * kS8Waves), 0, s, a);
 }
 
 }  // namespace

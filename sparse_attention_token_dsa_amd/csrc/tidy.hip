@@ -197,10 +197,10 @@ __global__ __launch_bounds__(kTidyThreads) void tidy_kernel(TidyArgs a) {
 hipError_t launch_tidy(const TidyArgs& a, int rows, hipStream_t s) {
     prof_begin(K_TIDY, s);
     if (a.max_slots > 0 && a.max_slots <= kTidyBitmapMax)
-        tidy_bitmap_kernel<<<dim3((unsigned)rows), dim3(kTidyThreads),
-                             (size_t)((a.max_slots + 31) >> 5) * 4, s>>>(a);
+        sa_launch(tidy_bitmap_kernel, dim3((unsigned)rows), dim3(kTidyThreads),
+                  (uint32_t)((a.max_slots + 31) >> 5) * 4u, s, a);
     else
-        tidy_kernel<<<dim3((unsigned)rows), dim3(kTidyThreads), 0, s>>>(a);
+        sa_launch(tidy_kernel, dim3((unsigned)rows), dim3(kTidyThreads), 0, s, a);
     prof_end(K_TIDY, s);
     return hipGetLastError();
 }

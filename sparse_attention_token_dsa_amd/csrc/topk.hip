@@ -336,13 +336,13 @@ hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn,
                                       unsigned long long* cand, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     prof_begin(K_TOPK_FILTER, s);
-    topk_filter_kernel<<<dim3((maxn + kFilterChunk - 1) / kFilterChunk, rows),
-                         dim3(kFilterThreads), 0, s>>>(a, cand);
+    sa_launch(topk_filter_kernel, dim3((maxn + kFilterChunk - 1) / kFilterChunk, rows),
+                         dim3(kFilterThreads), 0, s, a, cand);
     prof_end(K_TOPK_FILTER, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_begin(K_TOPK, s);
-    topk_select_kernel<<<dim3(rows), dim3(kTopkThreads), 0, s>>>(a, SRC_KEYS, cand);
+    sa_launch(topk_select_kernel, dim3(rows), dim3(kTopkThreads), 0, s, a, SRC_KEYS, cand);
     prof_end(K_TOPK, s);
     return hipGetLastError();
 }
@@ -351,7 +351,7 @@ hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     const int kind = a.dense ? SRC_DENSE : SRC_LIST;
     prof_begin(K_TOPK, s);
-    topk_select_kernel<<<dim3(rows), dim3(kTopkThreads), 0, s>>>(a, kind, nullptr);
+    sa_launch(topk_select_kernel, dim3(rows), dim3(kTopkThreads), 0, s, a, kind, nullptr);
     prof_end(K_TOPK, s);
     return hipGetLastError();
 }
