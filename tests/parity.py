@@ -301,9 +301,45 @@ def smoke_run(device):
     torch.cuda.synchronize(device)
     check_hisa(p, 64, 64, 8, _np(idx), _np(sc), _np(blocks), rows)
 
+    codes, scales = api.quantize_keys_fp8(K)
+    torch.cuda.synchronize(device)
+    oc, os_ = oracle.quantize_keys_fp8(p["K"])
+    assert np.array_equal(_np(codes), oc) and np.array_equal(_np(scales), os_), "fp8 codes"
+    idx, sc = api.indexer_score_topk_fp8(q, w, codes, scales, p["offset"], 64)
+    torch.cuda.synchronize(device)
+    check_dsa_fp8(p, oc, os_, 64, _np(idx), _np(sc), rows)
+
+    idx, sc = api.lisa_score_topk(q, w, K, p["offset"], 64)
+    torch.cuda.synchronize(device)
+    check_lisa(p, 64, _np(idx), _np(sc), rows)
+    idx, sc, heads = api.resmisa_route(q, w, K, p["offset"], 64, 128, 7)
+    torch.cuda.synchronize(device)
+    check_resmisa(p, 64, 128, 7, _np(idx), _np(sc), _np(heads), rows)
+    idx, sc, heads, blocks = api.misa_hisa(q, w, K, p["offset"], 64, 256, 8, 64, 8)
+    torch.cuda.synchronize(device)
+    check_misa_hisa(p, 64, 256, 8, 64, 8, _np(idx), _np(sc), _np(heads), _np(blocks), rows)
+
+    slots, stats = api.tidy_indices(idx, 1, page_size=16, max_slots=p["L"])
+    torch.cuda.synchronize(device)
+    os2, ost = oracle.tidy(_np(idx).reshape(-1, 64), 1, page_size=16, max_slots=p["L"])
+    assert np.array_equal(_np(slots).reshape(os2.shape), os2), "tidy slots"
+    assert np.array_equal(_np(stats).reshape(ost.shape), ost), "tidy counts"
+    lens = np.array([3000, 1234], np.int32)
+    idx, sc = api.indexer_score_topk_ragged(q, w, K, torch.from_numpy(lens).to(device), 64,
+                                            total_len=int(lens.sum()))
+    torch.cuda.synchronize(device)
+    oi, osc, rs = oracle.dsa_ragged(p["q"], p["w"], p["K"], lens, 64)
+    gi, gs = _np(idx).reshape(-1, 64), _np(sc).reshape(-1, 64)
+    for row in range(2):
+        t = int(lens[row]) - 1
+        srow = rs[row, : t + 1]
+        check_set(gi[row], gs[row], oi[row], osc[row], lambda s, srow=srow: srow[s], t + 1, 64,
+                  TOL_REL * np.max(np.abs(srow)), t=t, what="ragged row %d" % row)
+
     pp = synth.make_problem(8, Bt=1, T=64, L=700, H=64, needles=8, needle_mode="rows")
     q, w, K = to_device(pp, device)
     idx, sc = api.indexer_score_topk(q, w, K, pp["offset"], 48)
     torch.cuda.synchronize(device)
     check_dsa(pp, 48, _np(idx), _np(sc), rows_of(pp))
-    print("smoke ok: DSA decode, MISA-dagger, HISA and fused prefill match the oracle")
+    print("smoke ok: DSA, FP8 keys, MISA-dagger, HISA, LISA, ResMiSA, MISA x HISA, tidy-up, "
+          "ragged batches and the fused prefill match the oracle")
