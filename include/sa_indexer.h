@@ -39,6 +39,10 @@
  *     `ws` of at least the size its *_ws function reports (any alignment is
  *     accepted; 256 B is recommended).  Workspace contents need no
  *     initialisation and are clobbered.
+ *   - Query rows per call: batch * T <= 65535 (rows are a grid dimension of
+ *     the scan kernels), except the fused prefill path of indexer_score_topk
+ *     and lisa_score_topk (T >= 16), which takes batch <= 65535 sequences of
+ *     any T; SA_EUNSUPPORTED otherwise.
  *   - Inputs must be finite; NaN / inf scores give unspecified selections.
  *   - Return value: SA_OK or a negative SA_E* code; sa_last_error() then
  *     returns a message for the calling thread.  On error nothing has been

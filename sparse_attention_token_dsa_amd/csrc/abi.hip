@@ -96,6 +96,21 @@ int check_shape(const sa_shape* s) {
     return SA_OK;
 }
 
+// Kernels that index query rows (or sequences) on the grid's y axis: at most
+// 65535 of them per call.
+constexpr long long kMaxGridY = 65535;
+
+int check_grid_rows(const sa_shape* s) {
+    if ((long long)s->batch * s->T > kMaxGridY)
+        return fail(SA_EUNSUPPORTED, "batch * T must be <= 65535 per call on this path");
+    return SA_OK;
+}
+
+int check_grid_batch(const sa_shape* s) {
+    if ((long long)s->batch > kMaxGridY) return fail(SA_EUNSUPPORTED, "batch must be <= 65535");
+    return SA_OK;
+}
+
 int check_ptrs(const void* q, const void* w, const void* k, const void* out_idx) {
     if (!q || !w || !k || !out_idx) return fail(SA_EINVAL, "q, w, keys and out_idx must be non-NULL");
     return SA_OK;
@@ -269,7 +284,7 @@ int check_misa(const sa_shape* s, int B, int h, int kp) {
     if (B < 1) return fail(SA_EINVAL, "block_B must be >= 1");
     if (h < 1 || h > s->H) return fail(SA_EINVAL, "need 1 <= h <= H");
     if (kp != 0 && kp < s->topk) return fail(SA_EINVAL, "k_prime must be 0 or >= topk");
-    return SA_OK;
+    return check_grid_rows(s);
 }
 
 // ---------------------------------------------------------------- HISA
@@ -309,7 +324,7 @@ int check_hisa(const sa_shape* s, int b, int r) {
     if (b < 1 || r < 1) return fail(SA_EINVAL, "block_b and r must be >= 1");
     if ((long long)r * b < s->topk) return fail(SA_EINVAL, "need r * block_b >= topk");
     if ((long long)r * b > (1LL << 30)) return fail(SA_EUNSUPPORTED, "r * block_b too large");
-    return SA_OK;
+    return check_grid_rows(s);
 }
 
 }  // namespace
@@ -402,8 +417,14 @@ const char* sa_kernel_name(int32_t id) {
 
 // ------------------------------------------------------------------ DSA
 
-int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes) {
+static int check_dsa(const sa_shape* s) {
     int rc = check_shape(s);
+    if (rc) return rc;
+    return s->T >= kPrefillMinT ? check_grid_batch(s) : check_grid_rows(s);
+}
+
+int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes) {
+    int rc = check_dsa(s);
     if (rc) return rc;
     if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
     *ws_bytes = plan_dsa(s, nullptr).bytes;
@@ -413,7 +434,7 @@ int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes) {
 int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
                        size_t ws_bytes, void* stream) {
-    int rc = check_shape(s);
+    int rc = check_dsa(s);
     if (rc) return rc;
     rc = check_ptrs(q, w, keys, out_idx);
     if (rc) return rc;
@@ -490,7 +511,7 @@ static int check_ragged(const sa_shape* s) {
         return fail(SA_EUNSUPPORTED, "ragged batches: decode-style rows only (T < 16)");
     if (s->causal_offset != s->L - s->T)
         return fail(SA_EINVAL, "ragged batches: causal_offset must be L - T (the capacity)");
-    return SA_OK;
+    return check_grid_rows(s);
 }
 
 int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes) {
@@ -540,7 +561,7 @@ static int check_fp8_shape(const sa_shape* s) {
     if (rc) return rc;
     if (s->T >= kPrefillMinT)
         return fail(SA_EUNSUPPORTED, "FP8 keys: decode-style rows only (T < 16)");
-    return SA_OK;
+    return check_grid_rows(s);
 }
 
 int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes) {
@@ -624,7 +645,9 @@ static int check_resmisa(const sa_shape* s, int block, int r) {
     if (r > 0 && block < 1) return fail(SA_EINVAL, "block must be >= 1");
     if (resmisa_heads(s->H, r) > sa::kMaxH)
         return fail(SA_EUNSUPPORTED, "4 + r head rows must fit in 64 (r <= 60, or r == H)");
-    return SA_OK;
+    // the router and the decode scan put rows on the grid's y axis; the fused
+    // prefill puts sequences there
+    return (r > 0 || s->T < kPrefillMinT) ? check_grid_rows(s) : check_grid_batch(s);
 }
 
 // LISA (r = 0) and ResMiSA: head rows, then the DSA score path on them.

@@ -125,3 +125,66 @@ def test_kernel_names(api):
     names = api.kernel_names()
     assert "scan_dsa" in names and "prefill_fused" in names and "topk_select" in names
     assert len(set(names)) == len(names)
+
+
+def test_grid_row_limits(api):
+    """Paths that put query rows on the grid's y axis take at most 65535 rows per call; the
+    fused prefill puts sequences there instead."""
+    lib = api.load()
+    n = ctypes.c_size_t()
+    big_decode = shape(api, batch=65536, T=1, L=64, causal_offset=63)
+    assert ws_rc(api, big_decode)[0] == api.SA_EUNSUPPORTED
+    assert "65535" in api.last_error()
+    assert ws_rc(api, shape(api, batch=65535, T=1, L=64, causal_offset=63))[0] == api.SA_OK
+    prefill_rows = shape(api, batch=5, T=16384, L=16384, causal_offset=0)   # 81920 rows
+    assert ws_rc(api, prefill_rows)[0] == api.SA_OK
+    assert lib.hisa_coarse_fine_ws(ctypes.byref(prefill_rows), 128, 64, 0,
+                                   ctypes.byref(n)) == api.SA_EUNSUPPORTED
+    assert lib.misa_route_ws(ctypes.byref(prefill_rows), 1024, 8, 0, 0,
+                             ctypes.byref(n)) == api.SA_EUNSUPPORTED
+    assert lib.lisa_score_topk_ws(ctypes.byref(prefill_rows), ctypes.byref(n)) == api.SA_OK
+    assert lib.resmisa_route_ws(ctypes.byref(prefill_rows), 128, 7, 0,
+                                ctypes.byref(n)) == api.SA_EUNSUPPORTED
+
+
+def test_new_entry_points_validate(api):
+    lib = api.load()
+    n = ctypes.c_size_t()
+    buf = ctypes.create_string_buffer(16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    s = shape(api)
+    # FP8 keys: decode-style rows only
+    assert lib.indexer_score_topk_fp8_ws(ctypes.byref(s), ctypes.byref(n)) == api.SA_OK
+    s16 = shape(api, T=16, causal_offset=4080)
+    assert lib.indexer_score_topk_fp8_ws(ctypes.byref(s16), ctypes.byref(n)) == api.SA_EUNSUPPORTED
+    assert lib.sa_quantize_keys_fp8(p, 1, 10, 64, p, p, None) == api.SA_EUNSUPPORTED
+    assert lib.sa_quantize_keys_fp8(None, 1, 10, 128, p, p, None) == api.SA_EINVAL
+    # ResMiSA: 0 <= r <= H and 4 + r <= 64 unless r == H
+    assert lib.resmisa_route_ws(ctypes.byref(s), 128, 60, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.resmisa_route_ws(ctypes.byref(s), 128, 64, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.resmisa_route_ws(ctypes.byref(s), 128, 61, 0, ctypes.byref(n)) == \
+        api.SA_EUNSUPPORTED
+    assert lib.resmisa_route_ws(ctypes.byref(s), 128, 65, 0, ctypes.byref(n)) == api.SA_EINVAL
+    assert lib.resmisa_route_ws(ctypes.byref(s), 0, 7, 0, ctypes.byref(n)) == api.SA_EINVAL
+    assert lib.sa_block_extrema(p, 1, 100, 128, 0, p, None) == api.SA_EINVAL
+    # MISA x HISA: both budgets
+    s2 = shape(api, topk=2048, L=131072, causal_offset=131071)
+    assert lib.misa_hisa_ws(ctypes.byref(s2), 1024, 8, 128, 64, 0, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.misa_hisa_ws(ctypes.byref(s2), 1024, 8, 128, 15, 0, 0, ctypes.byref(n)) == \
+        api.SA_EINVAL
+    assert lib.misa_hisa_ws(ctypes.byref(s2), 1024, 0, 128, 64, 0, 0, ctypes.byref(n)) == \
+        api.SA_EINVAL
+    # ragged: decode rows, causal_offset = L - T, seq_lens required, total_len >= 0
+    assert lib.indexer_score_topk_ragged_ws(ctypes.byref(s), ctypes.byref(n)) == api.SA_OK
+    s3 = shape(api, causal_offset=100)
+    assert lib.indexer_score_topk_ragged_ws(ctypes.byref(s3), ctypes.byref(n)) == api.SA_EINVAL
+    assert lib.indexer_score_topk_ragged(p, p, p, None, 0, ctypes.byref(s), p, None, p, 16,
+                                         None) == api.SA_EINVAL
+    assert lib.indexer_score_topk_ragged(p, p, p, p, -1, ctypes.byref(s), p, None, p, 16,
+                                         None) == api.SA_EINVAL
+    # tidy-up: k <= 4096 unless a slot bound <= 2^18 is given
+    assert lib.sa_tidy_indices(p, 4, 1, 5000, None, 0, 64, 0, p, None, None) == \
+        api.SA_EUNSUPPORTED
+    assert lib.sa_tidy_indices(p, 4, 3, 64, None, 0, 64, 0, p, None, None) == api.SA_EINVAL
+    assert lib.sa_tidy_indices(p, 4, 1, 64, None, 0, 0, 0, p, None, None) == api.SA_EINVAL
+    assert lib.sa_tidy_indices(p, 4, 1, 64, p, 0, 64, 0, p, None, None) == api.SA_EINVAL
