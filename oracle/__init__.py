@@ -236,6 +236,31 @@ def dsa_fp8(prob: Problem, codes, scales, topk: int, rows=None, want_rowscore=Fa
     return (idx, sc, rs) if want_rowscore else (idx, sc)
 
 
+def dsa_fp8q(prob: Problem, codes, scales, topk: int, rows=None, want_rowscore=False,
+             nthreads=0):
+    """DSA on FP8 keys with the query converted to E4M3 as well, the compute
+    type of the fp8 matrix product (PaperTrace section 2.3: the query is
+    converted to the compute type in registers; its error counts on top of
+    the key error).
+
+    Each head vector q_{t,j} is quantized by the key-cache rule: b = max|q|/448
+    (1 for a zero vector) and the E4M3 codes of q/b.  b > 0 commutes with ReLU,
+    so the score is a_s * sum_j (w_j b_j) ReLU(decode(qc_j) . decode(c_s)),
+    with the folded weight w_j b_j rounded to fp32, the weight the kernel
+    carries.  Decoded E4M3 values are bf16 values, so this is dsa_fp8 on the
+    decoded query and the folded weights.  Returns (idx, score[, rowscore]).
+    """
+    qc, qs = quantize_keys_fp8(prob.q, nthreads)
+    qf = fp8_decode(qc).astype(np.float32)
+    qbits = qf.view(np.uint32)
+    assert not np.any(qbits & 0xFFFF), "an E4M3 value must be a bf16 value"
+    qb = (qbits >> 16).astype(np.uint16)
+    wb = (prob.w * qs).astype(np.float32)  # one fp32 rounding per weight
+    folded = Problem(qb, wb, prob.K, prob.offset)
+    return dsa_fp8(folded, codes, scales, topk, rows=rows, want_rowscore=want_rowscore,
+                   nthreads=nthreads)
+
+
 def lisa(prob: Problem, topk: int, rows=None, want_rowscore=False, nthreads=0):
     """LISA: top-k by the linear score g . k.  Returns (idx, score[, rowscore])."""
     lib = _load()

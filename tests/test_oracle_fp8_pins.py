@@ -14,6 +14,13 @@ What fixes the FP8 functions, other than the functions themselves:
   between the k-th and (k+1)-th score, the FP8 top-k set is the bf16 one;
 * a key quantized without error (values already on the FP8 grid times a
   power of two) gives exactly the bf16 oracle's scores.
+
+The query converted to E4M3 too (dsa_fp8q) is pinned by: a pure-Python
+brute force (format table built from the definition, nearest-code search,
+Python-float scores) on a tiny case; query heads already on the grid with
+448 as their largest element giving exactly the dsa_fp8 scores; exact 2^e
+scaling of every score under q -> 2^e q; and the Lipschitz bound on the
+query's quantization error against dsa_fp8.
 """
 from __future__ import annotations
 
@@ -168,3 +175,128 @@ def test_fp8_exact_keys_give_the_bf16_scores():
     i8, s8 = oracle.dsa_fp8(prob, codes, scales, k)
     ib, sb = oracle.dsa(prob, k)
     assert np.array_equal(i8, ib) and np.array_equal(s8, sb)
+
+
+# ---------------------------------------------------------------- FP8 query
+# The query converted to E4M3 as well (dsa_fp8q): each head vector by the
+# key-cache rule, its scale folded into the fp32 weight.
+
+def _e4m3_values():
+    """The 127 non-negative finite E4M3 values, code order, from the format's
+    definition (bias 7, 3 mantissa bits, subnormals below 2^-6)."""
+    out = []
+    for c in range(0x7F):
+        e, m = c >> 3, c & 7
+        out.append(2.0 ** (e - 7) * (1 + m / 8) if e else 2.0 ** -6 * m / 8)
+    return out
+
+
+def _encode_py(x, vals):
+    """Nearest E4M3 code of x (ties to the even code, saturating), by search."""
+    s = 0x80 if x < 0 or (x == 0 and math.copysign(1.0, x) < 0) else 0
+    a = min(abs(x), 448.0)
+    best = min(range(len(vals)), key=lambda c: (abs(vals[c] - a), c & 1))
+    return s | best, (-1 if s else 1) * vals[best]
+
+
+def test_fp8q_brute_force_tiny():
+    # Pure-Python quantization of q and k (fp32 divisions by fp32 scales) and
+    # the score in Python floats, against the oracle.
+    vals = _e4m3_values()
+    T, L, H, d, k = 2, 12, 3, 128, 4
+    p = synth.make_problem(91, Bt=1, T=T, L=L, H=H, d=d, offset=L - T)
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    idx, sc, rs = oracle.dsa_fp8q(prob, codes, scales, k, want_rowscore=True)
+    f32 = np.float32
+
+    def quant(vec):
+        m = max(abs(float(v)) for v in vec)
+        a = f32(f32(m) / f32(448.0)) if m > 0 else f32(1.0)
+        return a, [_encode_py(float(f32(v) / a), vals)[1] for v in vec]
+
+    K = synth.bf16_bits_to_f32(p["K"][0])
+    keys = [quant(K[s]) for s in range(L)]
+    q = synth.bf16_bits_to_f32(p["q"][0])
+    for i in range(T):
+        t = p["offset"] + i
+        heads = [quant(q[i, j]) for j in range(H)]
+        wf = [float(f32(p["w"][0, i, j]) * heads[j][0]) for j in range(H)]
+        for s in range(t + 1):
+            a, kv = keys[s]
+            tot = 0.0
+            for j in range(H):
+                dot = sum(x * y for x, y in zip(heads[j][1], kv))
+                tot += wf[j] * max(dot, 0.0)
+            ref = float(a) * tot
+            assert abs(rs[i, s] - ref) <= 1e-12 * max(1.0, abs(ref)), (i, s, rs[i, s], ref)
+        order = sorted(range(t + 1), key=lambda s: (-rs[i, s], s))[:k]
+        assert idx[i].tolist() == order
+
+
+def test_fp8q_exact_queries_give_the_fp8_scores():
+    # Query heads whose values are E4M3 values with one element at 448: the
+    # scale is 1, nothing is lost, and the scores are those of dsa_fp8.
+    rng = np.random.default_rng(92)
+    Bt, T, L, H, d, k = 1, 3, 60, 5, 128, 8
+    v = oracle.fp8_decode(np.arange(0x7F))
+    p = synth.make_problem(92, Bt=Bt, T=T, L=L, H=H, d=d, offset=L - T)
+    q = np.empty((Bt, T, H, d), np.float32)
+    for i in range(T):
+        for j in range(H):
+            row = rng.choice(v, size=d) * rng.choice([-1.0, 1.0], size=d)
+            row[int(rng.integers(0, d))] = 448.0
+            q[0, i, j] = row
+    qb = synth.to_bf16_bits(q)
+    prob = oracle.Problem(qb, p["w"], p["K"], p["offset"])
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    iq, sq, rq = oracle.dsa_fp8q(prob, codes, scales, k, want_rowscore=True)
+    i8, s8, r8 = oracle.dsa_fp8(prob, codes, scales, k, want_rowscore=True)
+    assert np.array_equal(iq, i8) and np.array_equal(sq, s8)
+
+
+@pytest.mark.parametrize("e", [-3, 2])
+def test_fp8q_power_of_two_query_scaling(e):
+    # q -> 2^e q leaves every code alone and scales every b by 2^e exactly, so
+    # every score scales by 2^e exactly.
+    T, L, H, d, k = 2, 90, 6, 128, 9
+    p = synth.make_problem(93, Bt=1, T=T, L=L, H=H, d=d, offset=L - T)
+    q2 = synth.to_bf16_bits(synth.bf16_bits_to_f32(p["q"]) * np.float32(2.0 ** e))
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    a = oracle.dsa_fp8q(oracle.Problem(p["q"], p["w"], p["K"], p["offset"]), codes, scales, k,
+                        want_rowscore=True)
+    b = oracle.dsa_fp8q(oracle.Problem(q2, p["w"], p["K"], p["offset"]), codes, scales, k,
+                        want_rowscore=True)
+    assert np.array_equal(a[0], b[0])
+    for i in range(T):
+        t = p["offset"] + i
+        assert np.array_equal(a[2][i, : t + 1] * 2.0 ** e, b[2][i, : t + 1])
+
+
+@pytest.mark.parametrize("seed", [94, 95])
+def test_fp8q_error_bound_against_fp8(seed):
+    # ReLU is 1-Lipschitz: against the bf16 query on the same FP8 keys, a
+    # score moves by at most a_s sum_j |w_j| |b_j qhat_j - q_j|_2 |khat_s|_2,
+    # plus the fp32 rounding of the folded weights.
+    T, L, H, d, k = 3, 200, 8, 128, 16
+    p = synth.make_problem(seed, Bt=1, T=T, L=L, H=H, d=d, offset=L - T)
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    _, _, rq = oracle.dsa_fp8q(prob, codes, scales, k, want_rowscore=True)
+    _, _, r8 = oracle.dsa_fp8(prob, codes, scales, k, want_rowscore=True)
+    qc, qs = oracle.quantize_keys_fp8(p["q"])
+    q = synth.bf16_bits_to_f32(p["q"][0]).astype(np.float64)
+    eq = np.linalg.norm(oracle.fp8_decode(qc[0]) * qs[0][..., None] - q, axis=2)  # [T, H]
+    qhat = oracle.fp8_decode(qc[0]) * qs[0][..., None]
+    khat = oracle.fp8_decode(codes[0])                                            # [L, d]
+    kn = np.linalg.norm(khat, axis=1)
+    a = scales[0].astype(np.float64)
+    w = np.abs(p["w"][0].astype(np.float64))
+    for i in range(T):
+        t = p["offset"] + i
+        dots = np.abs(qhat[i] @ khat[: t + 1].T)                                 # [H, t+1]
+        bound = a[: t + 1] * ((w[i] * eq[i])[:, None] * kn[None, : t + 1]
+                              + 2.0 ** -23 * w[i][:, None] * dots).sum(0)
+        diff = np.abs(rq[i, : t + 1] - r8[i, : t + 1])
+        assert np.all(diff <= bound * (1 + 1e-9) + 1e-15)
+        assert np.any(diff > 0), "quantizing q should perturb some score"
