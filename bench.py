@@ -375,18 +375,36 @@ def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
     gbs = scan_bytes / (us * 1e-6) / 1e9
     q_us = 1e3 * kq["quantize_fp8"][0] / kq["quantize_fp8"][1]
     q_bytes = Bt * L * (2 * d + d + 4)
+    scan8_digest = source_digest(["scan8.hip", "sa_frag.h", "sa_common.h"])
+
+    # The same selector with the query converted to E4M3 in the kernel and the
+    # dot products on the fp8 MFMA (same bytes, a quarter of the MFMAs).
+    def call_q():
+        api.indexer_score_topk_fp8q(q, w, codes, scales, off, k, oi, osc, ws=ws)
+
+    ms_q, kern_q = flushed_calls(api, torch, call_q, flush, steps)
+    us_q = kern_q["scan_dsa_fp8q"]
+    gbs_q = scan_bytes / (us_q * 1e-6) / 1e9
     return {"workload": "decode_128k_b8_h64_fp8keys", "cache": "cold: a 1 GiB read before "
             "each call", "ms_per_call": ms, "scores_per_s": Bt * L / (ms * 1e-3),
             "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()},
             "roofline": {"kernel": "scan_dsa_fp8", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(
-                             "scan_dsa_fp8", source_digest(["scan8.hip", "sa_frag.h",
-                                                            "sa_common.h"])),
+                         "traffic": measured_traffic("scan_dsa_fp8", scan8_digest),
                          "algorithmic_bytes_per_launch": scan_bytes, "avg_us": round(us, 2)},
             "quantize": {"avg_us": round(q_us, 2), "algorithmic_bytes_per_launch": q_bytes,
-                         "GB/s": round(q_bytes / (q_us * 1e-6) / 1e9, 1)}}
+                         "GB/s": round(q_bytes / (q_us * 1e-6) / 1e9, 1)},
+            "fp8q": {"workload": "decode_128k_b8_h64_fp8keys_fp8q",
+                     "what": "query converted to E4M3 in the kernel, 16x16x128 fp8 MFMA",
+                     "ms_per_call": ms_q, "scores_per_s": Bt * L / (ms_q * 1e-3),
+                     "kernels_us": {n: round(v, 2) for n, v in kern_q.items()},
+                     "roofline": {"kernel": "scan_dsa_fp8q", "bound": "hbm",
+                                  "achieved": round(gbs_q, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs_q / HBM_PEAK_GBS, 4),
+                                  "traffic": measured_traffic("scan_dsa_fp8q", scan8_digest),
+                                  "algorithmic_bytes_per_launch": scan_bytes,
+                                  "avg_us": round(us_q, 2)}}}
 
 
 def flushed_calls(api, torch, call, flush, steps):

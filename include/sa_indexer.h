@@ -172,6 +172,24 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
                            const float* scales, const sa_shape* s, int32_t* out_idx,
                            float* out_score, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for indexer_score_topk_fp8q on this shape (the same as for
+ * indexer_score_topk_fp8). */
+int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes);
+
+/* As indexer_score_topk_fp8, with the query converted to E4M3 as well, the
+ * compute type of the fp8 matrix product (PaperTrace section 2.3: the query
+ * is converted to the compute type in registers; its quantization error
+ * adds to the key's).  Each head vector q_{t,j} is quantized by the rule of
+ * sa_quantize_keys_fp8 (b_j = max|q_{t,j}| / 448, codes of q / b_j) inside
+ * the kernel, and since b_j > 0 commutes with ReLU,
+ *   I = scales[s] * sum_j fp32(w_j * b_j) * ReLU(e4m3(qc_j) . e4m3(codes[s])),
+ * the dot product on the 16x16x128 fp8 MFMA with fp32 accumulation.  Same
+ * arguments, shapes, ownership and errors as indexer_score_topk_fp8; q stays
+ * bf16 in memory. */
+int indexer_score_topk_fp8q(const uint16_t* q, const float* w, const uint8_t* codes,
+                            const float* scales, const sa_shape* s, int32_t* out_idx,
+                            float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* ----------------------------------------------------------- pooling */
 
 /* Block means of the keys, the cache-side state MISA (B = 1024) and HISA

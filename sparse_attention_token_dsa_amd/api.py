@@ -35,7 +35,8 @@ EXPORTS = (
     "sa_kernel_name", "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws",
     "indexer_score_topk_fp8", "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema",
     "resmisa_route_ws", "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
-    "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged",
+    "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged", "indexer_score_topk_fp8q_ws",
+    "indexer_score_topk_fp8q",
 )
 
 
@@ -74,6 +75,8 @@ def load():
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
     lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
+    lib.indexer_score_topk_fp8q_ws.argtypes = [SP, ctypes.POINTER(S)]
+    lib.indexer_score_topk_fp8q.argtypes = [P, P, P, P, SP, P, P, P, S, P]
     lib.sa_tidy_indices.argtypes = [P, I, I, I, P, I, I, I, P, P, P]
     lib.indexer_score_topk_ragged_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_ragged.argtypes = [P, P, P, P, ctypes.c_int64, SP, P, P, P, S, P]
@@ -97,7 +100,8 @@ def load():
                  "sa_quantize_keys_fp8", "indexer_score_topk_fp8_ws", "indexer_score_topk_fp8",
                  "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema", "resmisa_route_ws",
                  "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
-                 "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged"):
+                 "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged",
+                 "indexer_score_topk_fp8q_ws", "indexer_score_topk_fp8q"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -303,6 +307,26 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
     _check(load().indexer_score_topk_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                          _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                          _stream(q.device)), "indexer_score_topk_fp8")
+    return out_idx, out_score
+
+
+def indexer_score_topk_fp8q_ws(shape: Shape) -> int:
+    n = ctypes.c_size_t()
+    _check(load().indexer_score_topk_fp8q_ws(ctypes.byref(shape), ctypes.byref(n)),
+           "indexer_score_topk_fp8q_ws")
+    return n.value
+
+
+def indexer_score_topk_fp8q(q, w, codes, scales, causal_offset, topk, out_idx=None,
+                            out_score=None, want_score=True, ws=None):
+    """As indexer_score_topk_fp8 with the query converted to E4M3 in the
+    kernel (per-head scale) and the dot products on the fp8 MFMA."""
+    s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    ws = _workspace(indexer_score_topk_fp8q_ws(s), q.device, ws)
+    _check(load().indexer_score_topk_fp8q(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
+                                          _p(out_idx), _p(out_score), _p(ws), ws.numel(),
+                                          _stream(q.device)), "indexer_score_topk_fp8q")
     return out_idx, out_score
 
 

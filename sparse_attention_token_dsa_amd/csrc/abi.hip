@@ -64,7 +64,8 @@ void drain_records() {
 const char* kKernelNames[sa::K_COUNT] = {
     "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
     "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused",
-    "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows", "tidy"};
+    "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows", "tidy",
+    "scan_dsa_fp8q"};
 
 // ------------------------------------------------------------ workspace
 
@@ -168,7 +169,8 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
                           uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
                           float* out_score, hipStream_t st, const uint8_t* codes = nullptr,
                           const float* kscale = nullptr, bool state_zeroed = false,
-                          const int32_t* seq_lens = nullptr, long long total_keys = 0) {
+                          const int32_t* seq_lens = nullptr, long long total_keys = 0,
+                          bool q_fp8 = false) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
     hipError_t e;
@@ -200,6 +202,7 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.codes = codes;
     a.kscale = kscale;
     a.seq_lens = seq_lens;
+    a.q_fp8 = q_fp8 ? 1 : 0;
     const int nht = ((heads ? hsel : s->H) + 15) / 16;
     e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
               : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
@@ -572,9 +575,9 @@ int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes) {
     return SA_OK;
 }
 
-int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
-                           const float* scales, const sa_shape* s, int32_t* out_idx,
-                           float* out_score, void* ws, size_t ws_bytes, void* stream) {
+static int run_fp8(const uint16_t* q, const float* w, const uint8_t* codes, const float* scales,
+                   const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
+                   size_t ws_bytes, void* stream, bool q_fp8) {
     int rc = check_fp8_shape(s);
     if (rc) return rc;
     if (!q || !w || !codes || !scales || !out_idx)
@@ -585,9 +588,25 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
     DsaPlan p = plan_dsa(s, base);
     hipError_t e = run_dense_topk(q, w, nullptr, s, nullptr, 0, p.scores, p.state, p.cand,
                                   s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
-                                  codes, scales);
+                                  codes, scales, false, nullptr, 0, q_fp8);
     if (e != hipSuccess) return hip_fail(e, "fp8 decode scan");
     return SA_OK;
+}
+
+int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
+                           const float* scales, const sa_shape* s, int32_t* out_idx,
+                           float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    return run_fp8(q, w, codes, scales, s, out_idx, out_score, ws, ws_bytes, stream, false);
+}
+
+int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes) {
+    return indexer_score_topk_fp8_ws(s, ws_bytes);
+}
+
+int indexer_score_topk_fp8q(const uint16_t* q, const float* w, const uint8_t* codes,
+                            const float* scales, const sa_shape* s, int32_t* out_idx,
+                            float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    return run_fp8(q, w, codes, scales, s, out_idx, out_score, ws, ws_bytes, stream, true);
 }
 
 // ------------------------------------------------------- LISA / ResMiSA

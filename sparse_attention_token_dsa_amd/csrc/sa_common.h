@@ -141,6 +141,7 @@ enum KernelId {
     K_RES_ROUTER,
     K_HEAD_ROWS,
     K_TIDY,
+    K_SCAN8Q,
     K_COUNT
 };
 
@@ -194,6 +195,9 @@ struct ScanArgs {
     // Ragged batches: per-sequence lengths [batch] (row positions from
     // row_pos with cap = len_cap), or null.
     const int32_t* seq_lens;
+    // FP8 keys only: the query converted to E4M3 as well (per-head scale
+    // folded into the weight) and the contraction on the fp8 MFMA.
+    int q_fp8;
 };
 
 struct GatherArgs {

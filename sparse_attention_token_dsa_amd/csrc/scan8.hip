@@ -17,6 +17,14 @@
 // MFMAs of a step are interleaved with the head sum of the step before, and
 // buffer loads past the end of the chunk return zeros, so no address needs
 // clamping and every step of the unrolled loop is uniform.
+//
+// With the query converted to E4M3 as well (the section's "query converted to
+// the compute type"): each head vector is quantized by the key-cache rule
+// (b = max|q|/448, codes of q/b in fp32, round to nearest even, saturating) by
+// the whole workgroup into LDS, b is folded into the fp32 weight, and the
+// contraction of 16 keys x 16 heads x all 128 dims is one 16x16x128 fp8 MFMA
+// fed by the codes as they sit in LDS: a quarter of the matrix instructions
+// of the widened path and no widening.
 #include "sa_frag.h"
 
 namespace sa {
@@ -30,10 +38,90 @@ constexpr int kS8Ahead = kS8Ring - 1;       // steps of loads in flight
 // Step i stages step i+1 before it issues the load of step i + kS8Ahead, so
 // the load of step i+1 must have been issued in an earlier step.
 static_assert(kS8Ring >= 3, "the register ring must hold at least three steps");
+static_assert(64 * kS8Waves == kMaxH * 8, "the query quantizer takes 8 threads per head");
 constexpr int kBufFlags = 0x00020000;       // raw buffer, 32-bit elements
 constexpr int kNontemporal = 2;             // cache policy bit of a streaming load
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// q codes for the fp8 MFMA: per head tile, lane (c, g) holds 32 codes of head
+// ht*16 + c, dims 32g .. 32g+31, the same dims as the key operand of lane g.
+template <int NHT>
+struct QFrag8 {
+    i32x8 a[NHT];
+    float wv[NHT][4];
+};
+
+// Codes of a head vector in LDS: [head][8 chunks of 16 codes], chunk m of
+// head h in slot h*8 + (m ^ (h & 7)).
+__device__ __forceinline__ int qslot(int h, int m) { return h * 8 + (m ^ (h & 7)); }
+
+// The workgroup (512 threads: 8 per head, 16 dims each) quantizes the query
+// row's head vectors into LDS: scale b = max|q| / 448 (1 for a zero vector),
+// codes of q / b clamped to +-448 and rounded to nearest even.  Heads at or
+// past H get zero codes and scale 1.
+__device__ __forceinline__ void quantize_q8(const uint16_t* qrow, int H, uint4* qcode,
+                                            float* qscale) {
+    const int h = threadIdx.x >> 3, part = threadIdx.x & 7;
+    float x[16];
+    if (h < H) {
+        const uint4 v0 = ldg16(qrow + h * kD + part * 16);
+        const uint4 v1 = ldg16(qrow + h * kD + part * 16 + 8);
+        const uint32_t wds[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[2 * e] = bf16_bits_to_f32(wds[e] & 0xffffu);
+            x[2 * e + 1] = bf16_bits_to_f32(wds[e] >> 16);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) x[e] = 0.f;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf(x[e]));
+#pragma unroll
+    for (int off = 4; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 8));
+    const float b = m > 0.f ? m / 448.0f : 1.0f;
+    uint32_t out[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(x[4 * u + e] / b, -448.0f), 448.0f);
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+        out[u] = (uint32_t)pk;
+    }
+    qcode[qslot(h, part)] = make_uint4(out[0], out[1], out[2], out[3]);
+    if (part == 0) qscale[h] = b;
+}
+
+// A fragments from the LDS codes, and the weights folded with the scales.
+template <int NHT>
+__device__ __forceinline__ void load_qfrag_fp8(QFrag8<NHT>& f, const uint4* qcode,
+                                               const float* qscale, const float* wrow, int H,
+                                               int g, int c) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        const int h = ht * 16 + c;
+        const uint4 lo = qcode[qslot(h, 2 * g)], hi = qcode[qslot(h, 2 * g + 1)];
+        f.a[ht] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hw = ht * 16 + 4 * g + i;
+            f.wv[ht][i] = hw < H ? wrow[hw] * qscale[hw] : 0.f;
+        }
+    }
+}
+
+// 16 keys x 16 heads x 128 dims in E4M3, fp32 accumulate (no block scales).
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(const i32x8& a, const i32x8& b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0, 0, 0, 0);
+}
 
 // Two E4M3 codes per 16-bit half of x and y -> 8 bf16 values in dim order.
 __device__ __forceinline__ uint4 widen8(uint32_t x, uint32_t y) {
@@ -76,7 +164,7 @@ __device__ __forceinline__ void s8_interleave() {
     }
 }
 
-template <int NHT, bool HIST>
+template <int NHT, bool HIST, bool QF8>
 __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     const int row = blockIdx.y;
     const int b = row / a.T;
@@ -94,11 +182,20 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     // sits in slot r*8 + (m ^ (r & 7)), so both the row writes and the
     // per-key reads of 8 consecutive lanes hit 8 different bank groups.
     __shared__ uint4 tile[kS8Waves][2][128];
+    __shared__ uint4 qcode[QF8 ? kMaxH * 8 : 1];
+    __shared__ float qscale[QF8 ? kMaxH : 1];
 
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     QFrag<NHT> f;
-    load_qfrag8<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H, g, c);
+    QFrag8<NHT> f8;
+    const uint16_t* qrow = a.q + (long long)row * a.H * kD;
+    const float* wrow = a.w + (long long)row * a.H;
+    if constexpr (QF8)
+        quantize_q8(qrow, a.H, qcode, qscale);
+    else
+        load_qfrag8<NHT>(f, qrow, wrow, a.H, g, c);
+    float (&wv)[NHT][4] = QF8 ? f8.wv : f.wv;
 
     const uint8_t* cbase = a.codes + (long long)b * a.seq_stride + (long long)cs * kD;
     const float* sbase = a.kscale + (long long)b * (a.seq_stride / kD) + cs;
@@ -146,9 +243,9 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
         float part[NHT];
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht) {
-            part[ht] = f.wv[ht][0] * fmaxf(acc[p][ht][0], 0.f);
+            part[ht] = wv[ht][0] * fmaxf(acc[p][ht][0], 0.f);
 #pragma unroll
-            for (int e = 1; e < 4; ++e) part[ht] = fmaf(f.wv[ht][e], fmaxf(acc[p][ht][e], 0.f), part[ht]);
+            for (int e = 1; e < 4; ++e) part[ht] = fmaf(wv[ht][e], fmaxf(acc[p][ht][e], 0.f), part[ht]);
         }
         float sc = part[0];
 #pragma unroll
@@ -169,10 +266,10 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     // histogram is cleared), step 0 staged and fetched.
 #pragma unroll
     for (int u = 0; u < kS8Ahead; ++u) load(u, u);
-    if (HIST) {
+    if (HIST)
         for (int x = threadIdx.x; x < kHist0Bins; x += 64 * kS8Waves) lhist[x] = 0u;
-        __syncthreads();
-    }
+    if (HIST || QF8) __syncthreads();
+    if constexpr (QF8) load_qfrag_fp8<NHT>(f8, qcode, qscale, wrow, a.H, g, c);
     stage(0, 0);
     fetch(0);
 #pragma unroll
@@ -186,23 +283,32 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
         for (int u = 0; u < kS8Ring; ++u) {
             const int i = i0 + u;
             const int p = u & 1;
-            uint4 kb[4];
-            kb[0] = widen8(r0.x, r0.y);
-            kb[1] = widen8(r0.z, r0.w);
-            kb[2] = widen8(r1.x, r1.y);
-            kb[3] = widen8(r1.z, r1.w);
             scl[p] = __uint_as_float(ls[u]);
+            if constexpr (QF8) {
+                const i32x8 kb = {(int)r0.x, (int)r0.y, (int)r0.z, (int)r0.w,
+                                  (int)r1.x, (int)r1.y, (int)r1.z, (int)r1.w};
 #pragma unroll
-            for (int ht = 0; ht < NHT; ++ht) acc[p][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ht = 0; ht < NHT; ++ht) acc[p][ht] = mfma16x16x128_fp8(f8.a[ht], kb);
+            } else {
+                uint4 kb[4];
+                kb[0] = widen8(r0.x, r0.y);
+                kb[1] = widen8(r0.z, r0.w);
+                kb[2] = widen8(r1.x, r1.y);
+                kb[3] = widen8(r1.z, r1.w);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+                for (int ht = 0; ht < NHT; ++ht) acc[p][ht] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ht = 0; ht < NHT; ++ht) acc[p][ht] = mfma16x16x32(f.a[ht][kk], kb[kk], acc[p][ht]);
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int ht = 0; ht < NHT; ++ht)
+                        acc[p][ht] = mfma16x16x32(f.a[ht][kk], kb[kk], acc[p][ht]);
+            }
             const float sc = head_sum(1 - p);
             stage(1 - p, (u + 1) % kS8Ring);
             fetch(1 - p);
             load(i + kS8Ahead, (u + kS8Ahead) % kS8Ring);
-            s8_interleave<0, 4 * NHT, 8 * NHT + 8>();
+            // (With four MFMAs a step the compiler's own order is as fast.)
+            if constexpr (!QF8) s8_interleave<0, 4 * NHT, 8 * NHT + 8>();
             store(sc, i - 1);
         }
     }
@@ -221,12 +327,22 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     }
 }
 
-template <int NHT>
+template <int NHT, bool QF8>
 void scan8_dispatch(const ScanArgs& a, dim3 grid, hipStream_t s) {
     if (a.state)
-        sa_launch(scan8_kernel<NHT, true>, grid, dim3(64 * kS8Waves), 0, s, a);
+        sa_launch(scan8_kernel<NHT, true, QF8>, grid, dim3(64 * kS8Waves), 0, s, a);
     else
-        sa_launch(scan8_kernel<NHT, false>, grid, dim3(64 * kS8Waves), 0, s, a);
+        sa_launch(scan8_kernel<NHT, false, QF8>, grid, dim3(64 * kS8Waves), 0, s, a);
+}
+
+template <bool QF8>
+void scan8_heads(const ScanArgs& a, dim3 grid, int nht, hipStream_t s) {
+    switch (nht) {
+        case 1: scan8_dispatch<1, QF8>(a, grid, s); break;
+        case 2: scan8_dispatch<2, QF8>(a, grid, s); break;
+        case 3: scan8_dispatch<3, QF8>(a, grid, s); break;
+        default: scan8_dispatch<4, QF8>(a, grid, s); break;
+    }
 }
 
 }  // namespace
@@ -244,14 +360,13 @@ int scan8_chunk(long long rows, int maxn) {
 
 hipError_t launch_scan8(const ScanArgs& a, int rows, int nht, hipStream_t s) {
     const dim3 grid((unsigned)((a.len_cap + a.chunk - 1) / a.chunk), (unsigned)rows);
-    prof_begin(K_SCAN8, s);
-    switch (nht) {
-        case 1: scan8_dispatch<1>(a, grid, s); break;
-        case 2: scan8_dispatch<2>(a, grid, s); break;
-        case 3: scan8_dispatch<3>(a, grid, s); break;
-        default: scan8_dispatch<4>(a, grid, s); break;
-    }
-    prof_end(K_SCAN8, s);
+    const int id = a.q_fp8 ? K_SCAN8Q : K_SCAN8;
+    prof_begin(id, s);
+    if (a.q_fp8)
+        scan8_heads<true>(a, grid, nht, s);
+    else
+        scan8_heads<false>(a, grid, nht, s);
+    prof_end(id, s);
     return hipGetLastError();
 }
 

@@ -34,7 +34,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(HERE, "traffic.json")
 SCAN_SOURCES = ["scan.hip", "sa_frag.h", "sa_common.h"]
 SCAN_KERNEL = "scan_kernel<4, 4, 1, 4, 64, true, false>"
-SCAN8_KERNEL = "scan8_kernel<4, true>"
+SCAN8_KERNEL = "scan8_kernel<4, true, false>"
+SCAN8Q_KERNEL = "scan8_kernel<4, true, true>"
 SCAN8_SOURCES = ["scan8.hip", "sa_frag.h", "sa_common.h"]
 PREFILL_SOURCES = ["prefill.hip", "sa_frag.h", "sa_common.h"]
 PREFILL_KERNEL = "prefill_kernel<4>"
@@ -67,6 +68,8 @@ def run():
     codes, scales = api.quantize_keys_fp8(K)
     for _ in range(4):
         api.indexer_score_topk_fp8(q, w, codes, scales, p["offset"], 2048)
+    for _ in range(4):
+        api.indexer_score_topk_fp8q(q, w, codes, scales, p["offset"], 2048)
     torch.cuda.synchronize()
     del codes, scales
     pp = synth.make_config("prefill_chunked")
@@ -115,6 +118,7 @@ def summarize(out_dir):
         allrec = {}
     for name, needle, sources in (("scan_dsa", SCAN_KERNEL, SCAN_SOURCES),
                                   ("scan_dsa_fp8", SCAN8_KERNEL, SCAN8_SOURCES),
+                                  ("scan_dsa_fp8q", SCAN8Q_KERNEL, SCAN8_SOURCES),
                                   ("prefill_fused", PREFILL_KERNEL, PREFILL_SOURCES)):
         kf, kw = _pick(fetch, needle), _pick(write, needle)
         rec = {

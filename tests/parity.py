@@ -144,6 +144,13 @@ def check_dsa_fp8(p, codes, scales, k, gidx, gsc, rows):
     return swaps
 
 
+def check_dsa_fp8q(p, codes, scales, k, gidx, gsc, rows):
+    """As check_dsa_fp8, with the query converted to E4M3 too (dsa_fp8q)."""
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    oidx, osc, rs = oracle.dsa_fp8q(prob, codes, scales, k, rows=rows, want_rowscore=True)
+    return _check_rows(p, k, gidx, gsc, rows, oidx, osc, rs, "dsa-fp8q")
+
+
 def _check_rows(p, k, gidx, gsc, rows, ref_idx, ref_sc, rowscore, what):
     gi = gidx.reshape(-1, k)
     gs = None if gsc is None else gsc.reshape(-1, k)
@@ -308,6 +315,9 @@ def smoke_run(device):
     idx, sc = api.indexer_score_topk_fp8(q, w, codes, scales, p["offset"], 64)
     torch.cuda.synchronize(device)
     check_dsa_fp8(p, oc, os_, 64, _np(idx), _np(sc), rows)
+    idx, sc = api.indexer_score_topk_fp8q(q, w, codes, scales, p["offset"], 64)
+    torch.cuda.synchronize(device)
+    check_dsa_fp8q(p, oc, os_, 64, _np(idx), _np(sc), rows)
 
     idx, sc = api.lisa_score_topk(q, w, K, p["offset"], 64)
     torch.cuda.synchronize(device)

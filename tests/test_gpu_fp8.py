@@ -7,6 +7,10 @@ held as E4M3 codes with one fp32 scale per key).
 * indexer_score_topk_fp8 is compared with the oracle's DSA on the dequantized
   keys under the rule of tests/parity.py, on the oracle's own codes, so the two
   stages are checked independently.
+* indexer_score_topk_fp8q (the query converted to E4M3 in the kernel, fp8
+  MFMA) is compared with the oracle's dsa_fp8q the same way; its query codes,
+  a decision taken in fp32 on both sides, are checked exactly through unit
+  keys that read one code each.
 """
 from __future__ import annotations
 
@@ -16,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import _np, check_dsa_fp8, rows_of, to_device
+from parity import _np, check_dsa_fp8, check_dsa_fp8q, rows_of, to_device
 from sparse_attention_token_dsa_amd import synth
 
 torch = pytest.importorskip("torch")
@@ -146,4 +150,95 @@ def test_dsa_fp8_rejects_prefill_rows(api):
     with pytest.raises(api.SaError) as e:
         api.indexer_score_topk_fp8(q, w, torch.from_numpy(codes).to(DEV),
                                    torch.from_numpy(scales).to(DEV), p["offset"], 8)
+    assert e.value.code == api.SA_EUNSUPPORTED
+
+
+# ------------------------------------------------------------ FP8 query
+
+@pytest.mark.parametrize("Bt,T,L,H,k", [
+    (3, 1, 5000, 64, 100),
+    (2, 3, 9001, 64, 257),
+    (1, 15, 3000, 64, 300),
+    (2, 1, 300, 64, 512),
+    (1, 2, 20000, 32, 2048),
+    (2, 1, 4100, 40, 64),
+    (1, 1, 1, 64, 8),
+    (1, 4, 700, 1, 50),           # a single head
+])
+def test_dsa_fp8q(api, Bt, T, L, H, k):
+    say("dsa fp8q Bt=%d T=%d L=%d H=%d k=%d" % (Bt, T, L, H, k))
+    p = synth.make_problem(430 + L % 89, Bt=Bt, T=T, L=L, H=H, needles=8,
+                           needle_mode="decode" if T == 1 else "rows")
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    idx, sc = api.indexer_score_topk_fp8q(q, w, torch.from_numpy(codes).to(DEV),
+                                          torch.from_numpy(scales).to(DEV), p["offset"], k)
+    torch.cuda.synchronize()
+    check_dsa_fp8q(p, codes, scales, k, _np(idx), _np(sc), rows_of(p))
+
+
+def test_dsa_fp8q_query_codes_exact(api):
+    # Keys +-448 e_x (scale 1) read one query code each: with a single head of
+    # weight 1, key x scores b * 448 * max(qhat_x, 0) and key 128 + x scores
+    # b * 448 * max(-qhat_x, 0).  Rows put q / b on E4M3 values, midpoints
+    # between codes (ties to even), points just off them, subnormals and
+    # values that round to zero; one row is all zero (b = 1).  Every score
+    # must match the oracle's to fp32 rounding, which no wrong code does.
+    say("dsa fp8q query codes")
+    v = oracle.fp8_decode(np.arange(0x7F))
+    mids = (v[:-1] + v[1:]) / 2
+    pool = np.concatenate([v, mids, mids * (1 + 2.0 ** -7), mids * (1 - 2.0 ** -7),
+                           [2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11]])
+    rng = np.random.default_rng(11)
+    T, L = 8, 256
+    q = np.zeros((1, T, 1, 128), np.float32)
+    for i in range(T - 1):
+        row = rng.choice(pool, size=128) * rng.choice([-1.0, 1.0], size=128)
+        row[int(rng.integers(0, 128))] = 448.0 * (1 if i % 2 else -1)
+        q[0, i, 0] = row * 2.0 ** (-12 + 3 * i)
+    qb = synth.to_bf16_bits(q)
+    K = np.zeros((1, L, 128), np.float32)
+    for x in range(128):
+        K[0, x, x] = 448.0
+        K[0, 128 + x, x] = -448.0
+    p = {"q": qb, "w": np.ones((1, T, 1), np.float32), "K": synth.to_bf16_bits(K),
+         "offset": L - T, "Bt": 1, "T": T, "H": 1, "L": L}
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    assert np.all(scales == 1.0)
+    qd = torch.from_numpy(qb.view(np.int16)).to(DEV)
+    wd = torch.from_numpy(p["w"]).to(DEV)
+    idx, sc = api.indexer_score_topk_fp8q(qd, wd, torch.from_numpy(codes).to(DEV),
+                                          torch.from_numpy(scales).to(DEV), p["offset"], L)
+    torch.cuda.synchronize()
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    _, _, rs = oracle.dsa_fp8q(prob, codes, scales, L, want_rowscore=True)
+    gi, gs = _np(idx).reshape(T, L), _np(sc).reshape(T, L)
+    for i in range(T):
+        n = p["offset"] + i + 1      # k >= n: the whole prefix, in no set order
+        assert np.array_equal(np.sort(gi[i, :n]), np.arange(n)), "row %d set" % i
+        assert np.all(gi[i, n:] == -1)
+        ref = rs[i, gi[i, :n]]
+        assert np.allclose(gs[i, :n], ref, rtol=2e-7, atol=0), "row %d scores" % i
+    assert np.any(rs[:, :128] > 0) and np.any(rs[:, 128:] > 0)
+
+
+def test_dsa_fp8q_128k(api):
+    # The 128k decode workload with GPU-quantized keys, every row.
+    say("dsa fp8q 128k b8 h64")
+    p = synth.make_config("misa_128k_h64")
+    q, w, K = to_device(p, DEV)
+    codes, scales = api.quantize_keys_fp8(K)
+    idx, sc = api.indexer_score_topk_fp8q(q, w, codes, scales, p["offset"], 2048)
+    torch.cuda.synchronize()
+    check_dsa_fp8q(p, _np(codes), _np(scales), 2048, _np(idx), _np(sc), rows_of(p))
+
+
+def test_dsa_fp8q_rejects_prefill_rows(api):
+    say("dsa fp8q T=16 rejected")
+    p = synth.make_problem(421, Bt=1, T=16, L=100, H=16)
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    with pytest.raises(api.SaError) as e:
+        api.indexer_score_topk_fp8q(q, w, torch.from_numpy(codes).to(DEV),
+                                    torch.from_numpy(scales).to(DEV), p["offset"], 8)
     assert e.value.code == api.SA_EUNSUPPORTED
