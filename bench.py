@@ -576,7 +576,44 @@ def bench_prefill(api, synth, torch, np, dev, iters):
                          "traffic": measured_traffic(
                              "prefill_fused",
                              source_digest(["prefill.hip", "sa_frag.h", "sa_common.h"])),
-                         "algorithmic_flops_per_launch": flops}}
+                         "algorithmic_flops_per_launch": flops},
+            "ragged": bench_prefill_ragged(api, synth, torch, np, dev, iters)}
+
+
+def bench_prefill_ragged(api, synth, torch, np, dev, iters):
+    """Chunked prefill of sequences with different cached prefixes: 4 sequences
+    of 1024 new queries each at lengths 32K, 24K, 12K and 4K (capacity 32K),
+    one ragged call, next to the same batch padded to the capacity."""
+    Bt, T, L, H, d, k = 4, 1024, 32768, 64, 128, 2048
+    lens = [32768, 24576, 12288, 4096]
+    p = synth.make_problem(611, Bt=Bt, T=T, L=L, H=H, d=d, offset=L - T, needles=16,
+                           needle_mode="rows")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(p["w"]).to(dev)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
+    gl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    full = torch.full((Bt,), L, dtype=torch.int32, device=dev)
+    shape = api.Shape(Bt, T, H, d, L, L - T, k)
+    ws = torch.empty(api.indexer_score_topk_ragged_ws(shape), dtype=torch.uint8, device=dev)
+    oi = torch.empty((Bt, T, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, T, k), dtype=torch.float32, device=dev)
+    res = {}
+    for name, sl, ls in (("ragged", gl, lens), ("padded", full, [L] * Bt)):
+        def call(sl=sl):
+            api.indexer_score_topk_ragged(q, w, K, sl, k, out_idx=oi, out_score=osc, ws=ws)
+        settle(call, torch, dev)
+        api.profile_enable(True)
+        for _ in range(iters):
+            call()
+        torch.cuda.synchronize(dev)
+        kern = api.profile_read()
+        api.profile_enable(False)
+        us = 1e3 * kern["prefill_fused"][0] / kern["prefill_fused"][1]
+        pairs = sum(n - T + i + 1 for n in ls for i in range(T))
+        res[name] = {"prefill_us": round(us, 1), "legal_pairs": pairs,
+                     "TFLOP/s": round(2.0 * pairs * H * d / (us * 1e-6) / 1e12, 1)}
+    return {"workload": "prefill_ragged_b4_T1024_cap32k_h64", "seq_lens": lens, "T": T,
+            "k": k, **res}
 
 
 def cpu_baseline(p, k, B, h, kp, b, r):

@@ -125,16 +125,20 @@ int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes);
 /* DSA indexer over a batch of sequences of different lengths (PaperTrace
  * "2.2.2 MISA, LISA and ResMiSA", section 2.3, load and tail latency: each
  * row selects among its own min(k, t+1) positions; per-row lengths instead of
- * padding every row to the longest one).
+ * padding every row to the longest one).  Decode-style rows (T < 16) take
+ * the decode scan; T >= 16 takes the fused prefill, each sequence's query
+ * block placed at the end of its own history (chunked prefill of sequences
+ * with different cached prefixes).
  *   seq_lens  device int32 [batch]: keys [0, seq_lens[b]) of sequence b are
  *             its history; its T query rows sit at positions
  *             seq_lens[b] - T + i (causal within the sequence).  Lengths are
  *             clamped to [T, L].  Work beyond a row's length is skipped.
  *   total_len host-side sum of the lengths, or 0 if unknown: it only sizes
- *             the key chunks per workgroup (the result does not depend on it),
- *             so that a batch with a few long rows still spreads over the CUs.
+ *             the decode scan's key chunks per workgroup (the result does not
+ *             depend on it), so that a batch with a few long rows still
+ *             spreads over the CUs; the prefill ignores it.
  *   s         L is the per-sequence capacity (the keys' row stride);
- *             causal_offset must be L - T; T < 16 (decode-style rows).
+ *             causal_offset must be L - T.
  * Selection and outputs as in indexer_score_topk; other arguments,
  * ownership and errors likewise. */
 int indexer_score_topk_ragged(const uint16_t* q, const float* w, const uint16_t* keys,

@@ -426,6 +426,28 @@ static int check_dsa(const sa_shape* s) {
     return s->T >= kPrefillMinT ? check_grid_batch(s) : check_grid_rows(s);
 }
 
+// Fused prefill rows (T >= 16) of a DSA call; seq_lens for ragged batches.
+static hipError_t run_prefill(const uint16_t* q, const float* w, const uint16_t* keys,
+                              const sa_shape* s, const DsaPlan& p, int32_t* out_idx,
+                              float* out_score, hipStream_t st, const int32_t* seq_lens) {
+    sa::PrefillArgs a{};
+    a.q = q;
+    a.w = w;
+    a.keys = keys;
+    a.T = s->T;
+    a.H = s->H;
+    a.L = s->L;
+    a.offset = s->causal_offset;
+    a.k = s->topk;
+    a.surv = p.surv;
+    a.cap = score_stride(s->causal_offset + s->T);
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    a.out_stride = s->topk;
+    a.seq_lens = seq_lens;
+    return sa::launch_prefill(a, s->batch * s->T, st);
+}
+
 int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes) {
     int rc = check_dsa(s);
     if (rc) return rc;
@@ -446,24 +468,9 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
     void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     DsaPlan p = plan_dsa(s, base);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const int rows = s->batch * s->T;
     hipError_t e;
     if (p.prefill) {
-        sa::PrefillArgs a{};
-        a.q = q;
-        a.w = w;
-        a.keys = keys;
-        a.T = s->T;
-        a.H = s->H;
-        a.L = s->L;
-        a.offset = s->causal_offset;
-        a.k = s->topk;
-        a.surv = p.surv;
-        a.cap = score_stride(s->causal_offset + s->T);
-        a.out_idx = out_idx;
-        a.out_score = out_score;
-        a.out_stride = s->topk;
-        e = sa::launch_prefill(a, rows, st);
+        e = run_prefill(q, w, keys, s, p, out_idx, out_score, st, nullptr);
         if (e != hipSuccess) return hip_fail(e, "prefill");
     } else {
         e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand, s->topk,
@@ -510,11 +517,9 @@ int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
 static int check_ragged(const sa_shape* s) {
     int rc = check_shape(s);
     if (rc) return rc;
-    if (s->T >= kPrefillMinT)
-        return fail(SA_EUNSUPPORTED, "ragged batches: decode-style rows only (T < 16)");
     if (s->causal_offset != s->L - s->T)
         return fail(SA_EINVAL, "ragged batches: causal_offset must be L - T (the capacity)");
-    return check_grid_rows(s);
+    return s->T >= kPrefillMinT ? check_grid_batch(s) : check_grid_rows(s);
 }
 
 int indexer_score_topk_ragged_ws(const sa_shape* s, size_t* ws_bytes) {
@@ -539,9 +544,15 @@ int indexer_score_topk_ragged(const uint16_t* q, const float* w, const uint16_t*
     if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
     void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     DsaPlan p = plan_dsa(s, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.prefill) {
+        hipError_t e = run_prefill(q, w, keys, s, p, out_idx, out_score, st, seq_lens);
+        if (e != hipSuccess) return hip_fail(e, "ragged prefill");
+        return SA_OK;
+    }
     hipError_t e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand,
-                                  s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
-                                  nullptr, nullptr, false, seq_lens, total_len);
+                                  s->topk, out_idx, out_score, st, nullptr, nullptr, false,
+                                  seq_lens, total_len);
     if (e != hipSuccess) return hip_fail(e, "ragged decode scan");
     return SA_OK;
 }

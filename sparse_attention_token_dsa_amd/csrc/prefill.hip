@@ -407,7 +407,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int tmax = a.offset + min(gB * 8 + 7, a.T - 1);
+    // Position of the sequence's first row: the common offset, or for a
+    // ragged batch its own length less T.
+    const int offset =
+        a.seq_lens ? min(max(a.seq_lens[seq], a.T), a.L) - a.T : a.offset;
+    const int tmax = offset + min(gB * 8 + 7, a.T - 1);
     const int ntiles = tmax / kPfTile + 1;
 
     // Per-row state of this wave's two rows (workgroup rows 2 wid + qq).
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         const int i = (r < 8 ? gA : gB) * 8 + (r & 7);
         act[qq] = i < a.T && (r < 8 || gB != gA);
         rowq[qq] = (long long)seq * a.T + min(i, a.T - 1);
-        tq[qq] = act[qq] ? a.offset + i : -1;
+        tq[qq] = act[qq] ? offset + i : -1;
         tau[qq] = 0;
         tau_f[qq] = -INFINITY;
         cnt[qq] = 0;

@@ -290,6 +290,9 @@ struct PrefillArgs {
     int32_t* out_idx;           // [rows, out_stride]
     float* out_score;           // nullable
     long long out_stride;
+    // Ragged batches: per-sequence key counts [batch] (clamped to [T, L]); the
+    // rows of sequence b sit at seq_lens[b] - T + i instead of offset + i.
+    const int32_t* seq_lens;
 };
 
 // Launchers (defined next to their kernels).

@@ -174,8 +174,11 @@ def test_new_entry_points_validate(api):
         api.SA_EINVAL
     assert lib.misa_hisa_ws(ctypes.byref(s2), 1024, 0, 128, 64, 0, 0, ctypes.byref(n)) == \
         api.SA_EINVAL
-    # ragged: decode rows, causal_offset = L - T, seq_lens required, total_len >= 0
+    # ragged: causal_offset = L - T, seq_lens required, total_len >= 0; decode
+    # rows and prefill rows (T >= 16) both taken
     assert lib.indexer_score_topk_ragged_ws(ctypes.byref(s), ctypes.byref(n)) == api.SA_OK
+    s16r = shape(api, T=16, causal_offset=4096 - 16)
+    assert lib.indexer_score_topk_ragged_ws(ctypes.byref(s16r), ctypes.byref(n)) == api.SA_OK
     s3 = shape(api, causal_offset=100)
     assert lib.indexer_score_topk_ragged_ws(ctypes.byref(s3), ctypes.byref(n)) == api.SA_EINVAL
     assert lib.indexer_score_topk_ragged(p, p, p, None, 0, ctypes.byref(s), p, None, p, 16,

@@ -1,6 +1,6 @@
 """GPU parity of the index tidy-up (bit-exact: integer work) and of the
-ragged-batch DSA indexer (parity rule of tests/parity.py against the oracle's
-per-sequence DSA)."""
+ragged-batch DSA indexer, decode rows and fused prefill (parity rule of
+tests/parity.py against the oracle's per-sequence DSA)."""
 from __future__ import annotations
 
 import sys
@@ -113,12 +113,47 @@ def test_ragged(api, Bt, T, L, H, k, lens):
                   tol, t=t, what="ragged row %d" % row)
 
 
-def test_ragged_rejects_prefill_rows_and_bad_offset(api):
-    say("ragged rejects")
-    p = synth.make_problem(85, Bt=1, T=16, L=100, H=16)
+@pytest.mark.parametrize("Bt,T,L,H,k,lens", [
+    (3, 64, 3000, 64, 200, [3000, 1500, 64]),          # a sequence of exactly T (offset 0)
+    (2, 40, 5000, 32, 300, [5000, 2345]),              # T not a multiple of 16, H = 32
+    (4, 16, 1024, 64, 2048, [1024, 700, 16, 300]),     # k past every row: whole prefixes
+    (2, 128, 16384, 64, 2048, [16384, 5000]),          # several key tiles, long and short
+])
+def test_ragged_prefill(api, Bt, T, L, H, k, lens):
+    # T >= 16: the fused prefill with each sequence's query block at the end
+    # of its own history, against the oracle's per-sequence DSA.
+    say("ragged prefill Bt=%d T=%d L=%d lens=%s" % (Bt, T, L, lens))
+    p = synth.make_problem(90 + Bt, Bt=Bt, T=T, L=L, H=H, offset=L - T, needles=8,
+                           needle_mode="rows")
+    lens = np.array(lens, np.int32)
     q = torch.from_numpy(p["q"].view(np.int16)).to(DEV)
     w = torch.from_numpy(p["w"]).to(DEV)
     K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
-    with pytest.raises(api.SaError) as e:
-        api.indexer_score_topk_ragged(q, w, K, torch.tensor([50], dtype=torch.int32, device=DEV), 8)
-    assert e.value.code == api.SA_EUNSUPPORTED
+    idx, sc = api.indexer_score_topk_ragged(q, w, K, torch.from_numpy(lens).to(DEV), k)
+    torch.cuda.synchronize()
+    oi, osc, rs = oracle.dsa_ragged(p["q"], p["w"], p["K"], lens, k)
+    gi, gs = _np(idx).reshape(-1, k), _np(sc).reshape(-1, k)
+    for row in range(Bt * T):
+        t = int(lens[row // T]) - T + row % T
+        srow = rs[row, : t + 1]
+        tol = TOL_REL * np.max(np.abs(srow))
+        check_set(gi[row], gs[row], oi[row], osc[row], lambda s, srow=srow: srow[s], t + 1, k,
+                  tol, t=t, what="ragged prefill row %d" % row)
+
+
+def test_ragged_prefill_equals_dsa_at_full_length(api):
+    # Every sequence at full length: the ragged prefill is the plain prefill.
+    say("ragged prefill at full length")
+    Bt, T, L, k = 2, 48, 2000, 100
+    p = synth.make_problem(97, Bt=Bt, T=T, L=L, H=64, offset=L - T, needles=8,
+                           needle_mode="rows")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(DEV)
+    w = torch.from_numpy(p["w"]).to(DEV)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
+    full = torch.full((Bt,), L, dtype=torch.int32, device=DEV)
+    ri, rsc = api.indexer_score_topk_ragged(q, w, K, full, k)
+    di, dsc = api.indexer_score_topk(q, w, K, L - T, k)
+    torch.cuda.synchronize()
+    a = np.sort(_np(ri).reshape(-1, k), axis=1)
+    b = np.sort(_np(di).reshape(-1, k), axis=1)
+    assert np.array_equal(a, b)
