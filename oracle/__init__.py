@@ -40,7 +40,8 @@ class _Problem(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("w", ctypes.c_void_p), ("K", ctypes.c_void_p),
                 ("Bt", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("L", ctypes.c_int32),
-                ("causal_offset", ctypes.c_int32)]
+                ("causal_offset", ctypes.c_int32), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
 
 
 def _load():
@@ -75,20 +76,28 @@ def _ptr(a):
 
 
 class Problem:
-    """Holds contiguous copies of (q, w, K) and the causal offset."""
+    """Holds contiguous copies of (q, w, K) and the causal offset.  With
+    codes/scales (an FP8 key cache, K = None) DSA, MISA and HISA read key s of
+    sequence b as scales[b, s] * e4m3(codes[b, s])."""
 
-    def __init__(self, q, w, K, causal_offset):
+    def __init__(self, q, w, K, causal_offset, codes=None, scales=None):
         self.q = np.ascontiguousarray(q, dtype=np.uint16)
         self.w = np.ascontiguousarray(w, dtype=np.float32)
-        self.K = np.ascontiguousarray(K, dtype=np.uint16)
+        self.K = None if K is None else np.ascontiguousarray(K, dtype=np.uint16)
+        self.codes = None if codes is None else np.ascontiguousarray(codes, dtype=np.uint8)
+        self.scales = None if scales is None else np.ascontiguousarray(scales, dtype=np.float32)
         Bt, T, H, d = self.q.shape
         assert self.w.shape == (Bt, T, H), self.w.shape
-        assert self.K.shape[0] == Bt and self.K.shape[2] == d, self.K.shape
+        assert (self.K is None) != (self.codes is None), "K or (codes, scales)"
+        kk = self.K if self.K is not None else self.codes
+        assert kk.shape[0] == Bt and kk.shape[2] == d, kk.shape
+        if self.codes is not None:
+            assert self.scales is not None and self.scales.shape == kk.shape[:2]
         self.Bt, self.T, self.H, self.d = Bt, T, H, d
-        self.L = self.K.shape[1]
+        self.L = kk.shape[1]
         self.offset = int(causal_offset)
         self._c = _Problem(_ptr(self.q), _ptr(self.w), _ptr(self.K), Bt, T, H, d, self.L,
-                           self.offset)
+                           self.offset, _ptr(self.codes), _ptr(self.scales))
 
     def rows(self, rows):
         if rows is None:

@@ -188,7 +188,8 @@ static int run_rows(int (*fn)(void*, int), void* ctx, int nrows, int nthreads)
 
 static int check_problem(const oracle_problem* p)
 {
-    if (!p || !p->q || !p->w || !p->K) return ORACLE_EINVAL;
+    if (!p || !p->q || !p->w) return ORACLE_EINVAL;
+    if (!p->K && !(p->codes && p->scales)) return ORACLE_EINVAL;
     if (p->Bt < 1 || p->T < 1 || p->H < 1 || p->d < 1 || p->L < 1) return ORACLE_EINVAL;
     if (p->causal_offset < 0 || (long)p->causal_offset + p->T > p->L) return ORACLE_EINVAL;
     return 0;
@@ -210,6 +211,34 @@ static const uint16_t* kseq_of(const oracle_problem* p, int row)
 static int t_of(const oracle_problem* p, int row)
 {
     return p->causal_offset + row % p->T;
+}
+
+/* Key s of row's sequence in fp64: the bf16 key, or with an FP8 cache its
+ * dequantized value scale * e4m3(code) (exact in fp64). */
+static void key_of(const oracle_problem* p, int row, int s, double* out)
+{
+    const int b = row / p->T;
+    const size_t at = (size_t)b * p->L + (size_t)s;
+    if (p->codes) {
+        const double a = (double)p->scales[at];
+        const uint8_t* c = p->codes + at * p->d;
+        for (int x = 0; x < p->d; ++x) out[x] = a * oracle_fp8_e4m3_decode(c[x]);
+    } else {
+        widen_key(p->K + at * p->d, p->d, out);
+    }
+}
+
+/* Mean of keys [lo, hi) of row's sequence, fp64, summed in index order. */
+static void pool_mean_of(const oracle_problem* p, int row, int lo, int hi, double* key,
+                         double* out)
+{
+    for (int x = 0; x < p->d; ++x) out[x] = 0.0;
+    for (int s = lo; s < hi; ++s) {
+        key_of(p, row, s, key);
+        for (int x = 0; x < p->d; ++x) out[x] += key[x];
+    }
+    double c = (double)(hi - lo);
+    for (int x = 0; x < p->d; ++x) out[x] /= c;
 }
 
 static void write_topk(const scored_t* c, int kept, int topk, int32_t* idx, double* score)
@@ -247,7 +276,6 @@ static int dsa_row(void* vctx, int r)
     int n = t + 1;
     const uint16_t* qrow = qrow_of(p, row);
     const float* wrow = wrow_of(p, row);
-    const uint16_t* Kseq = kseq_of(p, row);
     scored_t* cand = (scored_t*)malloc(sizeof(scored_t) * (size_t)n);
     double* key = (double*)malloc(sizeof(double) * (size_t)p->d);
     if (!cand || !key) {
@@ -257,7 +285,7 @@ static int dsa_row(void* vctx, int r)
     }
     double* rs = c->out_rowscore ? c->out_rowscore + (size_t)r * p->L : NULL;
     for (int s = 0; s < n; ++s) {
-        widen_key(Kseq + (size_t)s * p->d, p->d, key);
+        key_of(p, row, s, key);
         cand[s].score = indexer_score(qrow, wrow, key, p->H, p->d, NULL, 0);
         cand[s].idx = s;
         if (rs) rs[s] = cand[s].score;
@@ -309,7 +337,6 @@ static int misa_row(void* vctx, int r)
     int n = t + 1;
     const uint16_t* qrow = qrow_of(p, row);
     const float* wrow = wrow_of(p, row);
-    const uint16_t* Kseq = kseq_of(p, row);
 
     int Mt = t / c->B + 1; /* blocks that intersect the legal prefix [0, t] */
     double* pooled = (double*)malloc(sizeof(double) * (size_t)Mt * d);
@@ -330,7 +357,7 @@ static int misa_row(void* vctx, int r)
         int lo = m * c->B;
         int hi = lo + c->B;
         if (hi > n) hi = n;
-        pool_mean(Kseq, d, lo, hi, pooled + (size_t)m * d);
+        pool_mean_of(p, row, lo, hi, key, pooled + (size_t)m * d);
     }
     /* Step 2 [MISA]: A_{j,m} = w_j * ReLU(q_j . pooled_m);
      * E_j = (1/M) * sum_m |A_{j,m}|. */
@@ -367,7 +394,7 @@ static int misa_row(void* vctx, int r)
     /* Step 4 [MISA]: routed score over the selected heads only. */
     double* hr = c->out_hatrow ? c->out_hatrow + (size_t)r * p->L : NULL;
     for (int s = 0; s < n; ++s) {
-        widen_key(Kseq + (size_t)s * d, d, key);
+        key_of(p, row, s, key);
         cand[s].score = indexer_score(qrow, wrow, key, H, d, heads, c->h);
         cand[s].idx = s;
         if (hr) hr[s] = cand[s].score;
@@ -400,7 +427,7 @@ static int misa_row(void* vctx, int r)
         }
         for (int u = 0; u < np; ++u) {
             int32_t s = pool[u];
-            widen_key(Kseq + (size_t)s * d, d, key);
+            key_of(p, row, s, key);
             cand[u].score = indexer_score(qrow, wrow, key, H, d, NULL, 0);
             cand[u].idx = s;
         }
@@ -459,7 +486,6 @@ static int hisa_row(void* vctx, int rr)
     int n = t + 1;
     const uint16_t* qrow = qrow_of(p, row);
     const float* wrow = wrow_of(p, row);
-    const uint16_t* Kseq = kseq_of(p, row);
     int nb = t / c->b + 1; /* blocks that intersect [0, t] */
     int nbmax = (p->L + c->b - 1) / c->b;
 
@@ -476,7 +502,7 @@ static int hisa_row(void* vctx, int rr)
         int lo = m * c->b;
         int hi = lo + c->b;
         if (hi > n) hi = n;
-        pool_mean(Kseq, d, lo, hi, rep);
+        pool_mean_of(p, row, lo, hi, key, rep);
         const int32_t* ch = c->coarse_heads ? c->coarse_heads + (size_t)rr * c->hsel : NULL;
         bc[m].score = indexer_score(qrow, wrow, rep, H, d, ch, c->hsel);
         bc[m].idx = m;
@@ -512,7 +538,7 @@ static int hisa_row(void* vctx, int rr)
         int hi = lo + c->b;
         if (hi > n) hi = n;
         for (int s = lo; s < hi; ++s) {
-            widen_key(Kseq + (size_t)s * d, d, key);
+            key_of(p, row, s, key);
             cand[ncand].score = indexer_score(qrow, wrow, key, H, d, NULL, 0);
             cand[ncand].idx = s;
             ++ncand;
@@ -853,6 +879,7 @@ int oracle_resmisa(const oracle_problem* p, int topk, int block, int r, const in
 {
     int e = check_problem(p);
     if (e) return e;
+    if (!p->K) return ORACLE_EINVAL; /* bf16 keys only */
     if (topk < 1 || r < 0 || r > p->H || (r > 0 && block < 1) || !out_idx || !out_score)
         return ORACLE_EINVAL;
     if (!rows) nrows = p->Bt * p->T;

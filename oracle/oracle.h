@@ -29,6 +29,11 @@ typedef struct {
     const uint16_t* K;  /* [Bt, L, d] bf16 bit patterns, one shared key head */
     int32_t Bt, T, H, d, L;
     int32_t causal_offset; /* absolute position of row 0 of each sequence */
+    /* Optional FP8 key cache in place of K (DSA, MISA, HISA): key s of
+     * sequence b is scales[b, s] * e4m3(codes[b, s, :]) (PaperTrace section
+     * 2.3).  K may then be NULL. */
+    const uint8_t* codes; /* [Bt, L, d] or NULL */
+    const float* scales;  /* [Bt, L] */
 } oracle_problem;
 
 /* rows: flat row ids to evaluate (NULL = every row, nrows ignored).

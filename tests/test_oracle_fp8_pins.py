@@ -300,3 +300,66 @@ def test_fp8q_error_bound_against_fp8(seed):
         diff = np.abs(rq[i, : t + 1] - r8[i, : t + 1])
         assert np.all(diff <= bound * (1 + 1e-9) + 1e-15)
         assert np.any(diff > 0), "quantizing q should perturb some score"
+
+
+# ------------------------------------------------- FP8 keys in MISA and HISA
+# oracle.Problem with codes/scales: DSA, MISA and HISA read the dequantized
+# keys.  Pinned by the reductions that hold for any keys (h = H is DSA; r = all
+# blocks is DSA; the generic DSA equals dsa_fp8) and by keys already on the
+# E4M3 grid, where the FP8 problem is the bf16 problem.
+
+def _fp8_problem(seed, T, L, H, d=128):
+    p = synth.make_problem(seed, Bt=1, T=T, L=L, H=H, d=d, offset=L - T)
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    prob8 = oracle.Problem(p["q"], p["w"], None, p["offset"], codes=codes, scales=scales)
+    return p, codes, scales, prob8
+
+
+def test_fp8_problem_dsa_equals_dsa_fp8():
+    T, L, H, k = 3, 400, 8, 25
+    p, codes, scales, prob8 = _fp8_problem(101, T, L, H)
+    i1, s1, r1 = oracle.dsa(prob8, k, want_rowscore=True)
+    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    i2, s2, r2 = oracle.dsa_fp8(prob, codes, scales, k, want_rowscore=True)
+    for i in range(T):
+        n = p["offset"] + i + 1
+        assert np.allclose(r1[i, :n], r2[i, :n], rtol=1e-12, atol=1e-300)
+    assert np.array_equal(i1, i2)
+
+
+def test_fp8_misa_all_heads_and_hisa_all_blocks_are_dsa():
+    T, L, H, k = 2, 700, 8, 30
+    p, codes, scales, prob8 = _fp8_problem(102, T, L, H)
+    di, ds = oracle.dsa(prob8, k)
+    m = oracle.misa(prob8, k, 128, H, 0)
+    assert np.array_equal(m["idx"], di)
+    md = oracle.misa(prob8, k, 128, 2, kprime=L)      # k' >= t+1: the full-head DSA
+    assert np.array_equal(md["idx"], di)
+    h = oracle.hisa(prob8, k, 64, (L + 63) // 64)
+    assert np.array_equal(h["idx"], di)
+
+
+def test_fp8_misa_hisa_on_grid_keys_equal_bf16():
+    # Keys already on the E4M3 grid with 448 * 2^e as their largest element:
+    # the FP8 cache holds them exactly, so every stage sees the bf16 keys.
+    rng = np.random.default_rng(103)
+    T, L, H, k = 2, 300, 8, 20
+    v = oracle.fp8_decode(np.arange(0x7F))
+    K = np.empty((1, L, 128), np.float32)
+    for s in range(L):
+        e = int(rng.integers(-8, -3))
+        row = rng.choice(v, size=128) * rng.choice([-1.0, 1.0], size=128)
+        row[int(rng.integers(0, 128))] = 448.0
+        K[0, s] = row * 2.0 ** e
+    Kb = synth.to_bf16_bits(K)
+    p = synth.make_problem(103, Bt=1, T=T, L=L, H=H, offset=L - T)
+    codes, scales = oracle.quantize_keys_fp8(Kb)
+    prob = oracle.Problem(p["q"], p["w"], Kb, p["offset"])
+    prob8 = oracle.Problem(p["q"], p["w"], None, p["offset"], codes=codes, scales=scales)
+    for kp in (0, 64):
+        a, b = oracle.misa(prob, k, 64, 3, kp), oracle.misa(prob8, k, 64, 3, kp)
+        assert np.array_equal(a["heads"], b["heads"]) and np.array_equal(a["idx"], b["idx"])
+        assert np.array_equal(a["score"], b["score"])
+    a, b = oracle.hisa(prob, k, 32, 4), oracle.hisa(prob8, k, 32, 4)
+    assert np.array_equal(a["blocks"], b["blocks"]) and np.array_equal(a["idx"], b["idx"])
+    assert np.array_equal(a["score"], b["score"])
