@@ -237,6 +237,23 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
                int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
                void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for misa_route_fp8 (the same as for misa_route). */
+int misa_route_fp8_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
+                      int32_t pooled_given, size_t* ws_bytes);
+
+/* misa_route over an FP8 key cache (PaperTrace section 2.3; codes and scales
+ * as written by sa_quantize_keys_fp8): every stage reads key s as
+ * scales[s] * e4m3(codes[s]) -- the pooled keys (when `pooled` is NULL; the
+ * means in fp32), the routed scan (codes widened exactly to bf16, the scale
+ * applied after the head sum) and MISA-dagger's rerank.  q stays bf16.
+ * `pooled`, if given, holds the block means of the dequantized keys in the
+ * sa_pool_blocks layout.  Other arguments, shapes, ownership and errors as in
+ * misa_route. */
+int misa_route_fp8(const uint16_t* q, const float* w, const uint8_t* codes, const float* scales,
+                   const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
+                   const uint16_t* pooled, int32_t* out_heads, int32_t* out_pool,
+                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* --------------------------------------------------------------- HISA */
 
 /* Workspace bytes for hisa_coarse_fine.  reps_given: whether `reps` will be
@@ -257,6 +274,20 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
                      const sa_shape* s, int32_t block_b, int32_t r, const uint16_t* reps,
                      int32_t* out_blocks, int32_t* out_idx, float* out_score, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* Workspace bytes for hisa_coarse_fine_fp8 (the same as for hisa_coarse_fine). */
+int hisa_coarse_fine_fp8_ws(const sa_shape* s, int32_t block_b, int32_t r, int32_t reps_given,
+                            size_t* ws_bytes);
+
+/* hisa_coarse_fine over an FP8 key cache: block representatives (when `reps`
+ * is NULL) are the fp32 means of the dequantized keys, and the fine stage
+ * rescores the kept blocks' tokens from the codes (widened exactly, the key's
+ * scale applied after the head sum).  Other arguments, shapes, ownership and
+ * errors as in hisa_coarse_fine. */
+int hisa_coarse_fine_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
+                         const float* scales, const sa_shape* s, int32_t block_b, int32_t r,
+                         const uint16_t* reps, int32_t* out_blocks, int32_t* out_idx,
+                         float* out_score, void* ws, size_t ws_bytes, void* stream);
 
 /* -------------------------------------------------------- MISA x HISA */
 

@@ -36,7 +36,8 @@ EXPORTS = (
     "indexer_score_topk_fp8", "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema",
     "resmisa_route_ws", "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
     "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged", "indexer_score_topk_fp8q_ws",
-    "indexer_score_topk_fp8q",
+    "indexer_score_topk_fp8q", "misa_route_fp8_ws", "misa_route_fp8", "hisa_coarse_fine_fp8_ws",
+    "hisa_coarse_fine_fp8",
 )
 
 
@@ -75,6 +76,10 @@ def load():
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
     lib.indexer_score_topk_fp8_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8.argtypes = [P, P, P, P, SP, P, P, P, S, P]
+    lib.misa_route_fp8_ws.argtypes = lib.misa_route_ws.argtypes
+    lib.misa_route_fp8.argtypes = [P, P, P, P, SP, I, I, I, P, P, P, P, P, P, S, P]
+    lib.hisa_coarse_fine_fp8_ws.argtypes = lib.hisa_coarse_fine_ws.argtypes
+    lib.hisa_coarse_fine_fp8.argtypes = [P, P, P, P, SP, I, I, P, P, P, P, P, S, P]
     lib.indexer_score_topk_fp8q_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8q.argtypes = [P, P, P, P, SP, P, P, P, S, P]
     lib.sa_tidy_indices.argtypes = [P, I, I, I, P, I, I, I, P, P, P]
@@ -101,7 +106,8 @@ def load():
                  "lisa_score_topk_ws", "lisa_score_topk", "sa_block_extrema", "resmisa_route_ws",
                  "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
                  "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged",
-                 "indexer_score_topk_fp8q_ws", "indexer_score_topk_fp8q"):
+                 "indexer_score_topk_fp8q_ws", "indexer_score_topk_fp8q", "misa_route_fp8_ws",
+                 "misa_route_fp8", "hisa_coarse_fine_fp8_ws", "hisa_coarse_fine_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -328,6 +334,47 @@ def indexer_score_topk_fp8q(q, w, codes, scales, causal_offset, topk, out_idx=No
                                           _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                           _stream(q.device)), "indexer_score_topk_fp8q")
     return out_idx, out_score
+
+
+def misa_route_fp8(q, w, codes, scales, causal_offset, topk, block_B, h, k_prime=0, pooled=None,
+                   want_heads=True, want_pool=False, out_idx=None, out_score=None,
+                   want_score=True, ws=None):
+    """misa_route over an FP8 key cache.  Returns (idx, score, heads, pool)."""
+    s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
+    B, T = q.shape[0], q.shape[1]
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    heads = torch.empty((B, T, h), dtype=torch.int32, device=q.device) if want_heads else None
+    pool = (torch.empty((B, T, k_prime), dtype=torch.int32, device=q.device)
+            if (want_pool and k_prime) else None)
+    n = ctypes.c_size_t()
+    _check(load().misa_route_fp8_ws(ctypes.byref(s), int(block_B), int(h), int(k_prime),
+                                    int(pooled is not None), ctypes.byref(n)), "misa_route_fp8_ws")
+    ws = _workspace(n.value, q.device, ws)
+    _check(load().misa_route_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
+                                 int(block_B), int(h), int(k_prime), _p(pooled), _p(heads),
+                                 _p(pool), _p(out_idx), _p(out_score), _p(ws), ws.numel(),
+                                 _stream(q.device)), "misa_route_fp8")
+    return out_idx, out_score, heads, pool
+
+
+def hisa_coarse_fine_fp8(q, w, codes, scales, causal_offset, topk, block_b, r, reps=None,
+                         want_blocks=True, out_idx=None, out_score=None, want_score=True,
+                         ws=None):
+    """hisa_coarse_fine over an FP8 key cache.  Returns (idx, score, blocks)."""
+    s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
+    B, T = q.shape[0], q.shape[1]
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    blocks = torch.empty((B, T, r), dtype=torch.int32, device=q.device) if want_blocks else None
+    n = ctypes.c_size_t()
+    _check(load().hisa_coarse_fine_fp8_ws(ctypes.byref(s), int(block_b), int(r),
+                                          int(reps is not None), ctypes.byref(n)),
+           "hisa_coarse_fine_fp8_ws")
+    ws = _workspace(n.value, q.device, ws)
+    _check(load().hisa_coarse_fine_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
+                                       int(block_b), int(r), _p(reps), _p(blocks), _p(out_idx),
+                                       _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
+           "hisa_coarse_fine_fp8")
+    return out_idx, out_score, blocks
 
 
 # ------------------------------------------------- tidy-up, ragged rows

@@ -839,19 +839,20 @@ int sa_pool_blocks2(const uint16_t* keys, int32_t batch, int32_t L, int32_t d, i
 static int route_heads(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int block_B, int h, const uint16_t* pooled,
                        uint16_t* pooled_ws, uint16_t* tail, uint8_t* flag, int32_t* heads,
-                       hipStream_t st, uint32_t* zero_state = nullptr) {
+                       hipStream_t st, uint32_t* zero_state = nullptr,
+                       const uint8_t* codes = nullptr, const float* kscale = nullptr) {
     const int rows = s->batch * s->T;
     const int nblk = (s->L + block_B - 1) / block_B;
     hipError_t e;
     const uint16_t* reps = pooled;
     if (!reps) {
-        e = sa::launch_pool(keys, s->batch, s->L, block_B, pooled_ws, st);
+        e = sa::launch_pool(keys, s->batch, s->L, block_B, pooled_ws, st, codes, kscale);
         if (e != hipSuccess) return hip_fail(e, "pool");
         reps = pooled_ws;
     }
     if (tail) {
         e = sa::launch_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset, s->L,
-                            block_B, rows, tail, flag, st);
+                            block_B, rows, tail, flag, st, codes, kscale);
         if (e != hipSuccess) return hip_fail(e, "tail pool");
     }
     sa::RouterArgs ra{};
@@ -886,13 +887,13 @@ int misa_route_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime
     return SA_OK;
 }
 
-int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
-               int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
-               int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
-               void* ws, size_t ws_bytes, void* stream) {
+// MISA over bf16 keys, or over an FP8 cache (codes, kscale; keys null).
+static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, const uint8_t* codes,
+                    const float* kscale, const sa_shape* s, int32_t block_B, int32_t h,
+                    int32_t k_prime, const uint16_t* pooled, int32_t* out_heads,
+                    int32_t* out_pool, int32_t* out_idx, float* out_score, void* ws,
+                    size_t ws_bytes, void* stream) {
     int rc = check_misa(s, block_B, h, k_prime);
-    if (rc) return rc;
-    rc = check_ptrs(q, w, keys, out_idx);
     if (rc) return rc;
     const bool partial = any_partial(s, block_B);
     const size_t need = plan_misa(s, block_B, h, k_prime, pooled != nullptr, partial, nullptr).bytes;
@@ -904,17 +905,17 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     hipError_t e;
     int32_t* heads = out_heads ? out_heads : p.heads;
     rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
-                     p.flag, heads, st, p.state);
+                     p.flag, heads, st, p.state, codes, kscale);
     if (rc) return rc;
     if (k_prime == 0) {
         e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, s->topk,
-                           out_idx, out_score, st, nullptr, nullptr, /*state_zeroed=*/true);
+                           out_idx, out_score, st, codes, kscale, /*state_zeroed=*/true);
         if (e != hipSuccess) return hip_fail(e, "routed scan");
         return SA_OK;
     }
     int32_t* pool_idx = out_pool ? out_pool : p.pool_idx;
     e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, k_prime, pool_idx,
-                       nullptr, st, nullptr, nullptr, /*state_zeroed=*/true);
+                       nullptr, st, codes, kscale, /*state_zeroed=*/true);
     if (e != hipSuccess) return hip_fail(e, "routed scan");
     sa::GatherArgs ga{};
     ga.q = q;
@@ -931,12 +932,43 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     ga.offset = s->causal_offset;
     ga.out_score = p.list_score;
     ga.out_idx = p.list_idx;
+    ga.codes = codes;
+    ga.kscale = kscale;
     e = sa::launch_gather(ga, rows, (s->H + 15) / 16, false, st);
     if (e != hipSuccess) return hip_fail(e, "rerank");
     e = run_list_topk(p.list_score, p.list_idx, k_prime, nullptr, k_prime, rows, s->topk,
                       out_idx, out_score, st);
     if (e != hipSuccess) return hip_fail(e, "rerank top-k");
     return SA_OK;
+}
+
+int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+               int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
+               int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
+               void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_misa(s, block_B, h, k_prime);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    return run_misa(q, w, keys, nullptr, nullptr, s, block_B, h, k_prime, pooled, out_heads,
+                    out_pool, out_idx, out_score, ws, ws_bytes, stream);
+}
+
+int misa_route_fp8_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
+                      int32_t pooled_given, size_t* ws_bytes) {
+    return misa_route_ws(s, block_B, h, k_prime, pooled_given, ws_bytes);
+}
+
+int misa_route_fp8(const uint16_t* q, const float* w, const uint8_t* codes, const float* scales,
+                   const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
+                   const uint16_t* pooled, int32_t* out_heads, int32_t* out_pool,
+                   int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_misa(s, block_B, h, k_prime);
+    if (rc) return rc;
+    if (!q || !w || !codes || !scales || !out_idx)
+        return fail(SA_EINVAL, "q, w, codes, scales and out_idx must be non-NULL");
+    return run_misa(q, w, nullptr, codes, scales, s, block_B, h, k_prime, pooled, out_heads,
+                    out_pool, out_idx, out_score, ws, ws_bytes, stream);
 }
 
 // ----------------------------------------------------------------- HISA
@@ -957,19 +989,20 @@ int hisa_coarse_fine_ws(const sa_shape* s, int32_t block_b, int32_t r, int32_t r
 static int hisa_stages(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int block_b, int r, const uint16_t* reps,
                        const HisaPlan& p, bool partial, const int32_t* heads, int hsel,
-                       int32_t* out_blocks, int32_t* out_idx, float* out_score, hipStream_t st) {
+                       int32_t* out_blocks, int32_t* out_idx, float* out_score, hipStream_t st,
+                       const uint8_t* codes = nullptr, const float* kscale = nullptr) {
     const int rows = s->batch * s->T;
     const int nblk = (s->L + block_b - 1) / block_b;
     hipError_t e;
     const uint16_t* rp = reps;
     if (!rp) {
-        e = sa::launch_pool(keys, s->batch, s->L, block_b, p.reps, st);
+        e = sa::launch_pool(keys, s->batch, s->L, block_b, p.reps, st, codes, kscale);
         if (e != hipSuccess) return hip_fail(e, "pool");
         rp = p.reps;
     }
     if (partial) {
         e = sa::launch_tail(keys, (long long)s->L * sa::kD, s->T, s->causal_offset, s->L,
-                            block_b, rows, p.tail, p.flag, st);
+                            block_b, rows, p.tail, p.flag, st, codes, kscale);
         if (e != hipSuccess) return hip_fail(e, "tail pool");
     }
     // Coarse stage: block scores with the indexer formula (routed heads or all).
@@ -1022,6 +1055,8 @@ static int hisa_stages(const uint16_t* q, const float* w, const uint16_t* keys,
     ga.offset = s->causal_offset;
     ga.out_score = p.list_score;
     ga.out_idx = p.list_idx;
+    ga.codes = codes;
+    ga.kscale = kscale;
     e = sa::launch_gather(ga, rows, (s->H + 15) / 16, true, st);
     if (e != hipSuccess) return hip_fail(e, "fine rescore");
     e = run_list_topk(p.list_score, p.list_idx, (long long)r * block_b, nullptr, r * block_b,
@@ -1045,6 +1080,28 @@ int hisa_coarse_fine(const uint16_t* q, const float* w, const uint16_t* keys,
     HisaPlan p = plan_hisa(s, block_b, r, reps != nullptr, partial, base);
     return hisa_stages(q, w, keys, s, block_b, r, reps, p, partial, nullptr, 0, out_blocks,
                        out_idx, out_score, static_cast<hipStream_t>(stream));
+}
+
+int hisa_coarse_fine_fp8_ws(const sa_shape* s, int32_t block_b, int32_t r, int32_t reps_given,
+                            size_t* ws_bytes) {
+    return hisa_coarse_fine_ws(s, block_b, r, reps_given, ws_bytes);
+}
+
+int hisa_coarse_fine_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
+                         const float* scales, const sa_shape* s, int32_t block_b, int32_t r,
+                         const uint16_t* reps, int32_t* out_blocks, int32_t* out_idx,
+                         float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_hisa(s, block_b, r);
+    if (rc) return rc;
+    if (!q || !w || !codes || !scales || !out_idx)
+        return fail(SA_EINVAL, "q, w, codes, scales and out_idx must be non-NULL");
+    const bool partial = any_partial(s, block_b);
+    const size_t need = plan_hisa(s, block_b, r, reps != nullptr, partial, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    HisaPlan p = plan_hisa(s, block_b, r, reps != nullptr, partial, base);
+    return hisa_stages(q, w, nullptr, s, block_b, r, reps, p, partial, nullptr, 0, out_blocks,
+                       out_idx, out_score, static_cast<hipStream_t>(stream), codes, scales);
 }
 
 // ------------------------------------------------------------ MISA x HISA

@@ -87,15 +87,30 @@ __device__ __forceinline__ void write_rep(uint16_t* out, float mean, int dim) {
     out[kD + dim] = (uint16_t)lo;
 }
 
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* keys, int L, int block,
+// Block means of bf16 keys, or of an FP8 cache's dequantized keys (codes
+// non-null: code times the key's scale, in fp32).
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* keys, const uint8_t* codes,
+                                                   const float* scales, int L, int block,
                                                    int nblk, uint16_t* out) {
     const int b = blockIdx.y, m = blockIdx.x;
     const int lo = m * block, hi = min(lo + block, L);
-    const uint16_t* kseq = keys + (long long)b * L * kD;
-    float acc[8];
-    block_sum_partial(kseq, lo, hi, acc);
-    __shared__ float red[16][kD];
     const int c16 = threadIdx.x & 15, kl = threadIdx.x >> 4;
+    float acc[8];
+    if (codes) {
+        const uint8_t* cseq = codes + (long long)b * L * kD;
+        const float* sseq = scales + (long long)b * L;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        for (int s = lo + kl; s < hi; s += 16) {
+            float x[8];
+            key8_f32(nullptr, cseq, sseq, s, c16, x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += x[e];
+        }
+    } else {
+        block_sum_partial(keys + (long long)b * L * kD, lo, hi, acc);
+    }
+    __shared__ float red[16][kD];
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[kl][c16 * 8 + e] = acc[e];
     __syncthreads();
@@ -140,10 +155,11 @@ __global__ __launch_bounds__(256) void pool2_kernel(const uint16_t* keys, int L,
 }
 
 hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16_t* out,
-                       hipStream_t s) {
+                       hipStream_t s, const uint8_t* codes, const float* scales) {
     const int nblk = (L + block - 1) / block;
     prof_begin(K_POOL, s);
-    sa_launch(pool_kernel, dim3(nblk, batch), dim3(256), 0, s, keys, L, block, nblk, out);
+    sa_launch(pool_kernel, dim3(nblk, batch), dim3(256), 0, s, keys, codes, scales, L, block,
+              nblk, out);
     prof_end(K_POOL, s);
     return hipGetLastError();
 }

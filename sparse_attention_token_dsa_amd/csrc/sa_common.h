@@ -91,6 +91,34 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight E4M3 codes (two per 16-bit half of x and y) -> 8 bf16 values in dim
+// order.
+__device__ __forceinline__ uint4 widen8(uint32_t x, uint32_t y) {
+    return make_uint4(fp8x2_to_bf16x2<false>(x), fp8x2_to_bf16x2<true>(x),
+                      fp8x2_to_bf16x2<false>(y), fp8x2_to_bf16x2<true>(y));
+}
+
+// Dims 8p .. 8p+7 of key s of one sequence in fp32: the bf16 key (kseq), or
+// with an FP8 cache (cseq != null) the codes times the key's scale sseq[s].
+__device__ __forceinline__ void key8_f32(const uint16_t* kseq, const uint8_t* cseq,
+                                         const float* sseq, long long s, int p, float (&x)[8]) {
+    uint4 v;
+    float a = 1.f;
+    if (cseq) {
+        const uint2 c = *reinterpret_cast<const uint2*>(cseq + s * 128 + p * 8);
+        v = widen8(c.x, c.y);
+        a = sseq[s];
+    } else {
+        v = ldg16(kseq + s * 128 + p * 8);
+    }
+    const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(wds[e] << 16) * a;
+        x[2 * e + 1] = __uint_as_float(wds[e] & 0xffff0000u) * a;
+    }
+}
+
 // 16-byte load of streamed data (keys read once per kernel), marked
 // nontemporal: it streams past the caches instead of displacing lines that
 // are reused.  On this chip it also raises the cold read rate (about 6.2
@@ -212,6 +240,10 @@ struct GatherArgs {
     int T, H, L, offset;
     float* out_score;       // [rows, ncand]
     int32_t* out_idx;       // [rows, ncand]
+    // FP8 key cache instead of `keys` (codes [batch, L, 128] with the same
+    // seq_stride, one fp32 scale per key), or null.
+    const uint8_t* codes;
+    const float* kscale;
 };
 
 struct RouterArgs {
@@ -308,15 +340,18 @@ int cu_count();  // compute units of the current device (cached per device)
 hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
                          hipStream_t s);
 hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s);
+// keys, or codes + scales (FP8 cache) when codes is not null.
 hipError_t launch_tail(const uint16_t* keys, long long seq_stride, int T, int offset, int L,
-                       int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s);
+                       int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s,
+                       const uint8_t* codes = nullptr, const float* scales = nullptr);
 hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s);
 // Dense rows scanned with a row state: multi-workgroup filter + per-row finish.
 // cand: [rows, a.cand_cap] keys.
 hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn,
                                       unsigned long long* cand, hipStream_t s);
 hipError_t launch_pool(const uint16_t* keys, int batch, int L, int block, uint16_t* out,
-                       hipStream_t s);
+                       hipStream_t s, const uint8_t* codes = nullptr,
+                       const float* scales = nullptr);
 hipError_t launch_pool2(const uint16_t* keys, int batch, int L, int small, int large,
                         uint16_t* out_small, uint16_t* out_large, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s);

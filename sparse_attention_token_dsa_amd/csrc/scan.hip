@@ -163,7 +163,7 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
 // get score -inf and index -1.  A workgroup takes kGatherChunk candidates;
 // each wave resolves its kGatherGroups x 16 candidate ids, issues every key
 // load (16 KiB in flight per wave), then runs the MFMA groups.
-template <int NHT, bool BLOCKS>
+template <int NHT, bool BLOCKS, bool F8>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     constexpr int NG = kGatherGroups;
     const int row = blockIdx.y;
@@ -194,17 +194,39 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     QFrag<NHT> f;
     load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
                     nullptr, 0, g, c);
-    const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
     uint4 kb[NG][4];
+    float ks[NG];
+    if (F8) {
+        // FP8 cache: the same dims as load_key (k-step kk, lane group g:
+        // dims 32kk + 8g .. +8), widened exactly; the key's scale multiplies
+        // the head sum.
+        const uint8_t* cseq = a.codes + (long long)b * a.seq_stride;
+        const float* sseq = a.kscale + (long long)b * (a.seq_stride / kD);
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi)
-        load_key<4>(kb[gi], kseq + (long long)(sid[gi] >= 0 ? sid[gi] : 0) * kD, g);
+        for (int gi = 0; gi < NG; ++gi) {
+            const long long s = sid[gi] >= 0 ? sid[gi] : 0;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint2 v = *reinterpret_cast<const uint2*>(cseq + s * kD + 32 * kk + 8 * g);
+                kb[gi][kk] = widen8(v.x, v.y);
+            }
+            ks[gi] = sseq[s];
+        }
+    } else {
+        const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            load_key<4>(kb[gi], kseq + (long long)(sid[gi] >= 0 ? sid[gi] : 0) * kD, g);
+            ks[gi] = 1.f;
+        }
+    }
     float* osc = a.out_score + (long long)row * a.ncand;
     int32_t* oid = a.out_idx + (long long)row * a.ncand;
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         const int u = cs + (gi * 4 + wid) * 16 + c;
-        const float sc = group_score<NHT, 4>(f, kb[gi]);
+        float sc = group_score<NHT, 4>(f, kb[gi]);
+        if (F8) sc *= ks[gi];
         if (g == 0 && u < ce) {
             osc[u] = sid[gi] >= 0 ? sc : -INFINITY;
             oid[u] = sid[gi];
@@ -299,7 +321,8 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
 // by the causal bound (t is not the block's last key), the representative is
 // the mean of keys [m*block, t]; written as a hi/lo bf16 pair like the cached
 // representatives.  flag[row] tells the score kernels whether to use it.
-__global__ __launch_bounds__(256) void tail_kernel(const uint16_t* keys, long long seq_stride,
+__global__ __launch_bounds__(256) void tail_kernel(const uint16_t* keys, const uint8_t* codes,
+                                                   const float* scales, long long seq_stride,
                                                    int T, int offset, int L, int block,
                                                    uint16_t* tail, uint8_t* flag) {
     const int row = blockIdx.x;
@@ -314,15 +337,16 @@ __global__ __launch_bounds__(256) void tail_kernel(const uint16_t* keys, long lo
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    const uint16_t* kseq = keys + (long long)b * seq_stride;
+    // (FP8 cache: codes seq_stride bytes apart per sequence, scales
+    // seq_stride / 128 apart.)
+    const uint16_t* kseq = codes ? nullptr : keys + (long long)b * seq_stride;
+    const uint8_t* cseq = codes ? codes + (long long)b * seq_stride : nullptr;
+    const float* sseq = codes ? scales + (long long)b * (seq_stride / kD) : nullptr;
     for (int s = lo + kl; s <= t; s += 16) {
-        const uint4 v = ldg16(kseq + (long long)s * kD + c16 * 8);
-        const uint32_t wds[4] = {v.x, v.y, v.z, v.w};
+        float x[8];
+        key8_f32(kseq, cseq, sseq, s, c16, x);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            acc[2 * e] += bf16_bits_to_f32(wds[e] & 0xffffu);
-            acc[2 * e + 1] += bf16_bits_to_f32(wds[e] >> 16);
-        }
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
     }
     __shared__ float red[16][kD];
 #pragma unroll
@@ -453,10 +477,16 @@ hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode
     const dim3 grid((unsigned)((a.ncand + kGatherChunk - 1) / kGatherChunk), (unsigned)rows);
     prof_begin(K_GATHER, s);
 #define SA_GATHER(N)                                                            \
-    if (block_mode)                                                             \
-        sa_launch(gather_kernel<N, true>, grid, dim3(256), 0, s, a);                   \
-    else                                                                        \
-        sa_launch(gather_kernel<N, false>, grid, dim3(256), 0, s, a);
+    if (a.codes) {                                                              \
+        if (block_mode)                                                         \
+            sa_launch(gather_kernel<N, true, true>, grid, dim3(256), 0, s, a);  \
+        else                                                                    \
+            sa_launch(gather_kernel<N, false, true>, grid, dim3(256), 0, s, a); \
+    } else if (block_mode) {                                                    \
+        sa_launch(gather_kernel<N, true, false>, grid, dim3(256), 0, s, a);     \
+    } else {                                                                    \
+        sa_launch(gather_kernel<N, false, false>, grid, dim3(256), 0, s, a);    \
+    }
     switch (nht) {
         case 1: SA_GATHER(1) break;
         case 2: SA_GATHER(2) break;
@@ -482,10 +512,11 @@ hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s) {
 }
 
 hipError_t launch_tail(const uint16_t* keys, long long seq_stride, int T, int offset, int L,
-                       int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s) {
+                       int block, int rows, uint16_t* tail, uint8_t* flag, hipStream_t s,
+                       const uint8_t* codes, const float* scales) {
     prof_begin(K_TAIL, s);
-    sa_launch(tail_kernel, dim3(rows), dim3(256), 0, s, keys, seq_stride, T, offset, L, block, tail,
-                                                 flag);
+    sa_launch(tail_kernel, dim3(rows), dim3(256), 0, s, keys, codes, scales, seq_stride, T, offset,
+              L, block, tail, flag);
     prof_end(K_TAIL, s);
     return hipGetLastError();
 }

@@ -123,31 +123,29 @@ __device__ __forceinline__ f32x4 mfma16x16x128_fp8(const i32x8& a, const i32x8& 
                                                             0, 0, 0, 0, 0, 0);
 }
 
-// Two E4M3 codes per 16-bit half of x and y -> 8 bf16 values in dim order.
-__device__ __forceinline__ uint4 widen8(uint32_t x, uint32_t y) {
-    return make_uint4(fp8x2_to_bf16x2<false>(x), fp8x2_to_bf16x2<true>(x),
-                      fp8x2_to_bf16x2<false>(y), fp8x2_to_bf16x2<true>(y));
-}
-
-// q fragments in the permuted dim order: head tile ht, row c = head
-// ht*16 + c; lane group g of k-step kk holds dims 32g + 8kk .. +8.  Absent
-// heads (H not a multiple of 16) get zero q and zero weight.
+// q fragments in the permuted dim order: head tile ht, row c = head slot
+// ht*16 + c; lane group g of k-step kk holds dims 32g + 8kk .. +8.  A slot is
+// head u itself, or with a routed head list (heads, hsel: MISA's routed
+// scan) the u-th listed head.  Absent slots (past H or hsel) get zero q and
+// zero weight.
 template <int NHT>
 __device__ __forceinline__ void load_qfrag8(QFrag<NHT>& f, const uint16_t* qrow,
-                                            const float* wrow, int H, int g, int c) {
+                                            const float* wrow, int H, const int32_t* heads,
+                                            int hsel, int g, int c) {
+    const int nh = heads ? hsel : H;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-        const int h = ht * 16 + c;
-        const uint16_t* qp = qrow + (h < H ? h : 0) * kD + 32 * g;
+        const int u = ht * 16 + c;
+        const int h = u < nh ? (heads ? heads[u] : u) : 0;
+        const uint16_t* qp = qrow + h * kD + 32 * g;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = ldg16(qp + 8 * kk);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int hw = ht * 16 + 4 * g + i;
-            f.wv[ht][i] = wrow[hw < H ? hw : 0];
-            if (hw >= H) f.wv[ht][i] = 0.f;
+            const int uw = ht * 16 + 4 * g + i;
+            f.wv[ht][i] = uw < nh ? wrow[heads ? heads[uw] : uw] : 0.f;
         }
-        if (h >= H)
+        if (u >= nh)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -194,7 +192,8 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     if constexpr (QF8)
         quantize_q8(qrow, a.H, qcode, qscale);
     else
-        load_qfrag8<NHT>(f, qrow, wrow, a.H, g, c);
+        load_qfrag8<NHT>(f, qrow, wrow, a.H, a.heads ? a.heads + (long long)row * a.hsel : nullptr,
+                         a.hsel, g, c);
     float (&wv)[NHT][4] = QF8 ? f8.wv : f.wv;
 
     const uint8_t* cbase = a.codes + (long long)b * a.seq_stride + (long long)cs * kD;

@@ -189,8 +189,16 @@ def check_resmisa(p, k, block, r, gidx, gsc, gheads, rows):
                        "resmisa")
 
 
-def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows):
-    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+def _problem(p, fp8):
+    """The oracle's problem: bf16 keys, or with fp8 = (codes, scales) the FP8
+    key cache."""
+    if fp8 is None:
+        return oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    return oracle.Problem(p["q"], p["w"], None, p["offset"], codes=fp8[0], scales=fp8[1])
+
+
+def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows, fp8=None):
+    prob = _problem(p, fp8)
     base = oracle.misa(prob, k, B, h, kprime=0, rows=rows)
     gh = gheads.reshape(-1, h)
     for u, row in enumerate(rows):
@@ -238,10 +246,10 @@ def check_misa(p, k, B, h, kprime, gidx, gsc, gheads, gpool, rows):
     return swaps
 
 
-def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows, coarse_heads=None):
+def check_hisa(p, k, b, r, gidx, gsc, gblocks, rows, coarse_heads=None, fp8=None):
     """coarse_heads [len(rows), h]: block scores over those heads (MISA x HISA,
     staged with the GPU's routed heads)."""
-    prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
+    prob = _problem(p, fp8)
     base = oracle.hisa(prob, k, b, r, rows=rows, coarse_heads=coarse_heads)
     gb = gblocks.reshape(-1, r)
     for u, row in enumerate(rows):

@@ -11,6 +11,9 @@ held as E4M3 codes with one fp32 scale per key).
   MFMA) is compared with the oracle's dsa_fp8q the same way; its query codes,
   a decision taken in fp32 on both sides, are checked exactly through unit
   keys that read one code each.
+* misa_route_fp8 and hisa_coarse_fine_fp8 are staged against the oracle's
+  MISA and HISA over the same FP8 cache (heads, pool and blocks by the
+  near-tie rule, then tokens on the GPU's choices).
 """
 from __future__ import annotations
 
@@ -20,7 +23,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import _np, check_dsa_fp8, check_dsa_fp8q, rows_of, to_device
+from parity import _np, check_dsa_fp8, check_dsa_fp8q, check_hisa, check_misa, rows_of, to_device
 from sparse_attention_token_dsa_amd import synth
 
 torch = pytest.importorskip("torch")
@@ -242,3 +245,74 @@ def test_dsa_fp8q_rejects_prefill_rows(api):
         api.indexer_score_topk_fp8q(q, w, torch.from_numpy(codes).to(DEV),
                                     torch.from_numpy(scales).to(DEV), p["offset"], 8)
     assert e.value.code == api.SA_EUNSUPPORTED
+
+
+# --------------------------------------------------- MISA / HISA on FP8 keys
+
+def _fp8_case(p):
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    return q, w, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV), (codes, scales)
+
+
+@pytest.mark.parametrize("Bt,T,L,H,B,h,k,kp", [
+    (2, 1, 5000, 64, 256, 8, 64, 0),
+    (2, 1, 5000, 64, 256, 8, 64, 320),       # MISA-dagger
+    (1, 3, 7000, 32, 1024, 8, 100, 0),       # cut last block, H = 32
+    (1, 4, 4000, 64, 300, 4, 50, 200),       # block not a power of two
+    (1, 20, 900, 64, 128, 8, 40, 100),       # many rows
+])
+def test_misa_fp8(api, Bt, T, L, H, B, h, k, kp):
+    say("misa fp8 Bt=%d T=%d L=%d H=%d B=%d h=%d k=%d kp=%d" % (Bt, T, L, H, B, h, k, kp))
+    p = synth.make_problem(450 + L % 97 + kp, Bt=Bt, T=T, L=L, H=H, needles=8,
+                           needle_mode="decode" if T == 1 else "rows")
+    q, w, cd, sd, fp8 = _fp8_case(p)
+    idx, sc, heads, pool = api.misa_route_fp8(q, w, cd, sd, p["offset"], k, B, h, k_prime=kp,
+                                              want_pool=True)
+    torch.cuda.synchronize()
+    check_misa(p, k, B, h, kp, _np(idx), _np(sc), _np(heads), None if pool is None else _np(pool),
+               rows_of(p), fp8=fp8)
+
+
+def test_misa_fp8_all_heads_equals_dsa_fp8(api):
+    say("misa fp8 h = H")
+    p = synth.make_problem(460, Bt=2, T=1, L=6000, H=32, needles=8, needle_mode="decode")
+    q, w, cd, sd, fp8 = _fp8_case(p)
+    mi, _, _, _ = api.misa_route_fp8(q, w, cd, sd, p["offset"], 128, 512, 32)
+    di, _ = api.indexer_score_topk_fp8(q, w, cd, sd, p["offset"], 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.sort(_np(mi).reshape(-1, 128), 1), np.sort(_np(di).reshape(-1, 128), 1))
+
+
+@pytest.mark.parametrize("Bt,T,L,H,b,r,k", [
+    (2, 1, 5000, 64, 64, 8, 64),
+    (1, 3, 9000, 64, 128, 16, 300),           # cut last block
+    (1, 20, 1000, 32, 32, 6, 100),
+])
+def test_hisa_fp8(api, Bt, T, L, H, b, r, k):
+    say("hisa fp8 Bt=%d T=%d L=%d H=%d b=%d r=%d k=%d" % (Bt, T, L, H, b, r, k))
+    p = synth.make_problem(470 + L % 89, Bt=Bt, T=T, L=L, H=H, needles=8,
+                           needle_mode="decode" if T == 1 else "rows")
+    q, w, cd, sd, fp8 = _fp8_case(p)
+    idx, sc, blocks = api.hisa_coarse_fine_fp8(q, w, cd, sd, p["offset"], k, b, r)
+    torch.cuda.synchronize()
+    check_hisa(p, k, b, r, _np(idx), _np(sc), _np(blocks), rows_of(p), fp8=fp8)
+
+
+def test_misa_hisa_fp8_128k(api):
+    # The 128k decode workload's MISA (B 1024, h 8, k' 8192) and HISA (b 128,
+    # r 64) on GPU-quantized keys, every row.
+    say("misa-dagger / hisa fp8 128k b8 h64")
+    p = synth.make_config("misa_128k_h64")
+    q, w, K = to_device(p, DEV)
+    cd, sd = api.quantize_keys_fp8(K)
+    torch.cuda.synchronize()
+    fp8 = (_np(cd), _np(sd))
+    idx, sc, heads, pool = api.misa_route_fp8(q, w, cd, sd, p["offset"], 2048, 1024, 8,
+                                              k_prime=8192, want_pool=True)
+    torch.cuda.synchronize()
+    check_misa(p, 2048, 1024, 8, 8192, _np(idx), _np(sc), _np(heads), _np(pool), rows_of(p),
+               fp8=fp8)
+    idx, sc, blocks = api.hisa_coarse_fine_fp8(q, w, cd, sd, p["offset"], 2048, 128, 64)
+    torch.cuda.synchronize()
+    check_hisa(p, 2048, 128, 64, _np(idx), _np(sc), _np(blocks), rows_of(p), fp8=fp8)
