@@ -385,6 +385,29 @@ def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
     ms_q, kern_q = flushed_calls(api, torch, call_q, flush, steps)
     us_q = kern_q["scan_dsa_fp8q"]
     gbs_q = scan_bytes / (us_q * 1e-6) / 1e9
+
+    # MISA (B 1024, h 8), MISA-dagger (k' 8192) and HISA (b 128, r 64) on the
+    # same FP8 cache, block means given as cache-side state like the bf16 step.
+    B, h, kp, b, r = 1024, 8, 8192, 128, 64
+    deq = (codes.view(torch.float8_e4m3fn).float() * scales[..., None]).to(torch.bfloat16)
+    pooled = api.pool_blocks(deq.view(torch.int16), B)
+    reps = api.pool_blocks(deq.view(torch.int16), b)
+    del deq
+    ws_m = torch.empty(api.misa_route_ws(shape, B, h, kp, True), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(api.hisa_coarse_fine_ws(shape, b, r, True), dtype=torch.uint8, device=dev)
+    sel = {}
+    for name, fn in (
+            ("misa", lambda: api.misa_route_fp8(q, w, codes, scales, off, k, B, h, 0, pooled=pooled,
+                                                want_heads=False, out_idx=oi, out_score=osc,
+                                                ws=ws_m)),
+            ("misa_dagger", lambda: api.misa_route_fp8(q, w, codes, scales, off, k, B, h, kp,
+                                                       pooled=pooled, want_heads=False,
+                                                       out_idx=oi, out_score=osc, ws=ws_m)),
+            ("hisa", lambda: api.hisa_coarse_fine_fp8(q, w, codes, scales, off, k, b, r,
+                                                      reps=reps, want_blocks=False, out_idx=oi,
+                                                      out_score=osc, ws=ws_h))):
+        ms_s, kern_s = flushed_calls(api, torch, fn, flush, steps)
+        sel[name] = {"ms_per_call": ms_s, "kernels_us": {n: round(v, 2) for n, v in kern_s.items()}}
     return {"workload": "decode_128k_b8_h64_fp8keys", "cache": "cold: a 1 GiB read before "
             "each call", "ms_per_call": ms, "scores_per_s": Bt * L / (ms * 1e-3),
             "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()},
@@ -404,7 +427,10 @@ def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
                                   "unit": "GB/s", "frac": round(gbs_q / HBM_PEAK_GBS, 4),
                                   "traffic": measured_traffic("scan_dsa_fp8q", scan8_digest),
                                   "algorithmic_bytes_per_launch": scan_bytes,
-                                  "avg_us": round(us_q, 2)}}}
+                                  "avg_us": round(us_q, 2)}},
+            "selectors": {"config": {"B": B, "h": h, "k_prime": kp, "b": b, "r": r,
+                                     "pools": "given: block means of the dequantized keys"},
+                          **sel}}
 
 
 def flushed_calls(api, torch, call, flush, steps):
