@@ -326,6 +326,14 @@ def smoke_run(device):
     idx, sc = api.indexer_score_topk_fp8q(q, w, codes, scales, p["offset"], 64)
     torch.cuda.synchronize(device)
     check_dsa_fp8q(p, oc, os_, 64, _np(idx), _np(sc), rows)
+    idx, sc, heads, pool = api.misa_route_fp8(q, w, codes, scales, p["offset"], 64, 256, 8,
+                                              k_prime=256, want_pool=True)
+    torch.cuda.synchronize(device)
+    check_misa(p, 64, 256, 8, 256, _np(idx), _np(sc), _np(heads), _np(pool), rows,
+               fp8=(oc, os_))
+    idx, sc, blocks = api.hisa_coarse_fine_fp8(q, w, codes, scales, p["offset"], 64, 64, 8)
+    torch.cuda.synchronize(device)
+    check_hisa(p, 64, 64, 8, _np(idx), _np(sc), _np(blocks), rows, fp8=(oc, os_))
 
     idx, sc = api.lisa_score_topk(q, w, K, p["offset"], 64)
     torch.cuda.synchronize(device)
@@ -359,5 +367,6 @@ def smoke_run(device):
     idx, sc = api.indexer_score_topk(q, w, K, pp["offset"], 48)
     torch.cuda.synchronize(device)
     check_dsa(pp, 48, _np(idx), _np(sc), rows_of(pp))
-    print("smoke ok: DSA, FP8 keys, MISA-dagger, HISA, LISA, ResMiSA, MISA x HISA, tidy-up, "
+    print("smoke ok: DSA, FP8 keys (q bf16 and E4M3; MISA-dagger and HISA too), MISA-dagger, "
+          "HISA, LISA, ResMiSA, MISA x HISA, tidy-up, "
           "ragged batches and the fused prefill match the oracle")

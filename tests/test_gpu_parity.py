@@ -260,3 +260,10 @@ def test_profile_counters(api):
     api.profile_enable(False)
     assert prof["scan_dsa"][1] == 1 and prof["scan_dsa"][0] > 0
     assert "topk_select" in prof and "topk_filter" in prof
+
+
+def test_smoke_run_every_entry_point(api):
+    # The smoke check's sequence: one small call of every entry point, each
+    # checked against the oracle.
+    say("smoke run")
+    parity.smoke_run(torch.device(DEV))
