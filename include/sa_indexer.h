@@ -176,6 +176,19 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
                            const float* scales, const sa_shape* s, int32_t* out_idx,
                            float* out_score, void* ws, size_t ws_bytes, void* stream);
 
+/* Workspace bytes for indexer_score_topk_fp8_ragged. */
+int indexer_score_topk_fp8_ragged_ws(const sa_shape* s, size_t* ws_bytes);
+
+/* Ragged batches (as indexer_score_topk_ragged: seq_lens, total_len, the
+ * capacity L with causal_offset = L - T) over an FP8 key cache, decode-style
+ * rows (T < 16).  q_fp8 = 0: the scores of indexer_score_topk_fp8 (q bf16);
+ * q_fp8 != 0: those of indexer_score_topk_fp8q (q converted to E4M3, fp8
+ * MFMA).  Other arguments, ownership and errors as in indexer_score_topk_fp8. */
+int indexer_score_topk_fp8_ragged(const uint16_t* q, const float* w, const uint8_t* codes,
+                                  const float* scales, const int32_t* seq_lens, int64_t total_len,
+                                  int32_t q_fp8, const sa_shape* s, int32_t* out_idx,
+                                  float* out_score, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes for indexer_score_topk_fp8q on this shape (the same as for
  * indexer_score_topk_fp8). */
 int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes);

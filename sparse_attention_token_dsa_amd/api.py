@@ -37,7 +37,7 @@ EXPORTS = (
     "resmisa_route_ws", "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
     "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged", "indexer_score_topk_fp8q_ws",
     "indexer_score_topk_fp8q", "misa_route_fp8_ws", "misa_route_fp8", "hisa_coarse_fine_fp8_ws",
-    "hisa_coarse_fine_fp8",
+    "hisa_coarse_fine_fp8", "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged",
 )
 
 
@@ -80,6 +80,9 @@ def load():
     lib.misa_route_fp8.argtypes = [P, P, P, P, SP, I, I, I, P, P, P, P, P, P, S, P]
     lib.hisa_coarse_fine_fp8_ws.argtypes = lib.hisa_coarse_fine_ws.argtypes
     lib.hisa_coarse_fine_fp8.argtypes = [P, P, P, P, SP, I, I, P, P, P, P, P, S, P]
+    lib.indexer_score_topk_fp8_ragged_ws.argtypes = [SP, ctypes.POINTER(S)]
+    lib.indexer_score_topk_fp8_ragged.argtypes = [P, P, P, P, P, ctypes.c_int64, I, SP, P, P, P,
+                                                  S, P]
     lib.indexer_score_topk_fp8q_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk_fp8q.argtypes = [P, P, P, P, SP, P, P, P, S, P]
     lib.sa_tidy_indices.argtypes = [P, I, I, I, P, I, I, I, P, P, P]
@@ -107,7 +110,8 @@ def load():
                  "resmisa_route", "misa_hisa_ws", "misa_hisa", "sa_tidy_indices",
                  "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged",
                  "indexer_score_topk_fp8q_ws", "indexer_score_topk_fp8q", "misa_route_fp8_ws",
-                 "misa_route_fp8", "hisa_coarse_fine_fp8_ws", "hisa_coarse_fine_fp8"):
+                 "misa_route_fp8", "hisa_coarse_fine_fp8_ws", "hisa_coarse_fine_fp8",
+                 "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -333,6 +337,27 @@ def indexer_score_topk_fp8q(q, w, codes, scales, causal_offset, topk, out_idx=No
     _check(load().indexer_score_topk_fp8q(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                           _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                           _stream(q.device)), "indexer_score_topk_fp8q")
+    return out_idx, out_score
+
+
+def indexer_score_topk_fp8_ragged(q, w, codes, scales, seq_lens, topk, total_len=0, q_fp8=False,
+                                  out_idx=None, out_score=None, want_score=True, ws=None):
+    """Ragged batches over an FP8 key cache (capacity codes.shape[1]); q_fp8
+    picks the E4M3-query scores of indexer_score_topk_fp8q."""
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != q.shape[0]:
+        raise TypeError("seq_lens must be an int32 GPU tensor with one entry per sequence")
+    s = _fp8_shape(q, w, codes, scales, codes.shape[1] - q.shape[1], topk)
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    n = ctypes.c_size_t()
+    _check(load().indexer_score_topk_fp8_ragged_ws(ctypes.byref(s), ctypes.byref(n)),
+           "indexer_score_topk_fp8_ragged_ws")
+    ws = _workspace(n.value, q.device, ws)
+    _check(load().indexer_score_topk_fp8_ragged(_p(q), _p(w), _p(codes), _p(scales),
+                                                _p(seq_lens.contiguous()), int(total_len),
+                                                int(bool(q_fp8)), ctypes.byref(s), _p(out_idx),
+                                                _p(out_score), _p(ws), ws.numel(),
+                                                _stream(q.device)),
+           "indexer_score_topk_fp8_ragged")
     return out_idx, out_score
 
 

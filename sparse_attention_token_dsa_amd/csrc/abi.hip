@@ -610,6 +610,36 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
     return run_fp8(q, w, codes, scales, s, out_idx, out_score, ws, ws_bytes, stream, false);
 }
 
+int indexer_score_topk_fp8_ragged_ws(const sa_shape* s, size_t* ws_bytes) {
+    int rc = check_fp8_shape(s);
+    if (rc) return rc;
+    if (s->causal_offset != s->L - s->T)
+        return fail(SA_EINVAL, "ragged batches: causal_offset must be L - T (the capacity)");
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_dsa(s, nullptr).bytes;
+    return SA_OK;
+}
+
+int indexer_score_topk_fp8_ragged(const uint16_t* q, const float* w, const uint8_t* codes,
+                                  const float* scales, const int32_t* seq_lens, int64_t total_len,
+                                  int32_t q_fp8, const sa_shape* s, int32_t* out_idx,
+                                  float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    size_t need = 0;
+    int rc = indexer_score_topk_fp8_ragged_ws(s, &need);
+    if (rc) return rc;
+    if (!q || !w || !codes || !scales || !seq_lens || !out_idx)
+        return fail(SA_EINVAL, "q, w, codes, scales, seq_lens and out_idx must be non-NULL");
+    if (total_len < 0) return fail(SA_EINVAL, "total_len must be >= 0");
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    DsaPlan p = plan_dsa(s, base);
+    hipError_t e = run_dense_topk(q, w, nullptr, s, nullptr, 0, p.scores, p.state, p.cand,
+                                  s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
+                                  codes, scales, false, seq_lens, total_len, q_fp8 != 0);
+    if (e != hipSuccess) return hip_fail(e, "ragged fp8 decode scan");
+    return SA_OK;
+}
+
 int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes) {
     return indexer_score_topk_fp8_ws(s, ws_bytes);
 }

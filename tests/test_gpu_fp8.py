@@ -316,3 +316,37 @@ def test_misa_hisa_fp8_128k(api):
     idx, sc, blocks = api.hisa_coarse_fine_fp8(q, w, cd, sd, p["offset"], 2048, 128, 64)
     torch.cuda.synchronize()
     check_hisa(p, 2048, 128, 64, _np(idx), _np(sc), _np(blocks), rows_of(p), fp8=fp8)
+
+
+@pytest.mark.parametrize("q_fp8", [False, True])
+@pytest.mark.parametrize("Bt,T,L,H,k,lens", [
+    (4, 1, 20000, 64, 512, [20000, 9001, 37, 1]),
+    (3, 3, 5000, 32, 100, [5000, 1200, 3]),
+])
+def test_dsa_fp8_ragged(api, Bt, T, L, H, k, lens, q_fp8):
+    # Each sequence against the oracle's FP8 DSA on its own prefix.
+    from parity import TOL_REL, check_set
+    say("dsa fp8 ragged Bt=%d T=%d L=%d lens=%s q_fp8=%s" % (Bt, T, L, lens, q_fp8))
+    p = synth.make_problem(480 + Bt, Bt=Bt, T=T, L=L, H=H, offset=L - T, needles=8)
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    lens = np.array(lens, np.int32)
+    idx, sc = api.indexer_score_topk_fp8_ragged(q, w, torch.from_numpy(codes).to(DEV),
+                                                torch.from_numpy(scales).to(DEV),
+                                                torch.from_numpy(lens).to(DEV), k,
+                                                total_len=int(lens.sum()), q_fp8=q_fp8)
+    torch.cuda.synchronize()
+    gi, gs = _np(idx).reshape(-1, k), _np(sc).reshape(-1, k)
+    fn = oracle.dsa_fp8q if q_fp8 else oracle.dsa_fp8
+    for b in range(Bt):
+        n = max(int(lens[b]), T)
+        pb = oracle.Problem(p["q"][b:b + 1], p["w"][b:b + 1],
+                            np.ascontiguousarray(p["K"][b:b + 1, :n]), n - T)
+        oi, osc, rs = fn(pb, np.ascontiguousarray(codes[b:b + 1, :n]),
+                         np.ascontiguousarray(scales[b:b + 1, :n]), k, want_rowscore=True)
+        for i in range(T):
+            row, t = b * T + i, n - T + i
+            srow = rs[i, : t + 1]
+            tol = TOL_REL * np.max(np.abs(srow))
+            check_set(gi[row], gs[row], oi[i], osc[i], lambda s, srow=srow: srow[s], t + 1, k,
+                      tol, t=t, what="fp8 ragged row %d" % row)
