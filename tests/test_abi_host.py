@@ -185,6 +185,27 @@ def test_new_entry_points_validate(api):
                                          None) == api.SA_EINVAL
     assert lib.indexer_score_topk_ragged(p, p, p, p, -1, ctypes.byref(s), p, None, p, 16,
                                          None) == api.SA_EINVAL
+    # FP8 MISA / HISA / ragged: same shape rules as their bf16 forms; the FP8
+    # cache pointers are required; ragged FP8 takes decode-style rows with
+    # causal_offset = L - T
+    s4 = shape(api, topk=64, L=4096, causal_offset=4095)
+    assert lib.misa_route_fp8_ws(ctypes.byref(s4), 256, 8, 0, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.misa_route_fp8_ws(ctypes.byref(s4), 256, 65, 0, 0, ctypes.byref(n)) == \
+        api.SA_EINVAL
+    assert lib.misa_route_fp8(p, p, None, p, ctypes.byref(s4), 256, 8, 0, None, None, None, p,
+                              None, p, 16, None) == api.SA_EINVAL
+    assert lib.hisa_coarse_fine_fp8_ws(ctypes.byref(s4), 64, 8, 0, ctypes.byref(n)) == api.SA_OK
+    assert lib.hisa_coarse_fine_fp8(p, p, p, None, ctypes.byref(s4), 64, 8, None, None, p, None,
+                                    p, 16, None) == api.SA_EINVAL
+    assert lib.indexer_score_topk_fp8_ragged_ws(ctypes.byref(s), ctypes.byref(n)) == api.SA_OK
+    assert lib.indexer_score_topk_fp8_ragged_ws(ctypes.byref(s3), ctypes.byref(n)) == \
+        api.SA_EINVAL
+    assert lib.indexer_score_topk_fp8_ragged_ws(ctypes.byref(s16r), ctypes.byref(n)) == \
+        api.SA_EUNSUPPORTED
+    assert lib.indexer_score_topk_fp8_ragged(p, p, p, p, None, 0, 0, ctypes.byref(s), p, None, p,
+                                             16, None) == api.SA_EINVAL
+    assert lib.indexer_score_topk_fp8q_ws(ctypes.byref(s16), ctypes.byref(n)) == \
+        api.SA_EUNSUPPORTED
     # tidy-up: k <= 4096 unless a slot bound <= 2^18 is given
     assert lib.sa_tidy_indices(p, 4, 1, 5000, None, 0, 64, 0, p, None, None) == \
         api.SA_EUNSUPPORTED
