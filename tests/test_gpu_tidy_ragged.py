@@ -157,3 +157,34 @@ def test_ragged_prefill_equals_dsa_at_full_length(api):
     a = np.sort(_np(ri).reshape(-1, k), axis=1)
     b = np.sort(_np(di).reshape(-1, k), axis=1)
     assert np.array_equal(a, b)
+
+
+def test_ragged_prefill_bench_batch_sampled(api):
+    # The ragged-prefill leg of bench.py (4 sequences x 1024 queries at 32K, 24K,
+    # 12K and 4K keys, capacity 32K, k = 2048), in the same launch, with 6
+    # sampled rows per sequence (its first, last and 4 random) against the
+    # oracle's DSA on that sequence alone.
+    Bt, T, L, k = 4, 1024, 32768, 2048
+    lens = np.array([32768, 24576, 12288, 4096], np.int32)
+    say("ragged prefill bench batch, sampled rows")
+    p = synth.make_problem(611, Bt=Bt, T=T, L=L, H=64, d=128, offset=L - T, needles=16,
+                           needle_mode="rows")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(DEV)
+    w = torch.from_numpy(p["w"]).to(DEV)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(DEV)
+    idx, sc = api.indexer_score_topk_ragged(q, w, K, torch.from_numpy(lens).to(DEV), k)
+    torch.cuda.synchronize()
+    gi, gs = _np(idx).reshape(-1, k), _np(sc).reshape(-1, k)
+    rng = np.random.default_rng(5)
+    for b in range(Bt):
+        n = int(lens[b])
+        rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 4, replace=False)])).astype(np.int32)
+        pb = oracle.Problem(p["q"][b:b + 1], p["w"][b:b + 1],
+                            np.ascontiguousarray(p["K"][b:b + 1, :n]), n - T)
+        oi, osc, rs = oracle.dsa(pb, k, rows=rows, want_rowscore=True)
+        for u, i in enumerate(rows):
+            row, t = b * T + int(i), n - T + int(i)
+            srow = rs[u, : t + 1]
+            tol = TOL_REL * np.max(np.abs(srow))
+            check_set(gi[row], gs[row], oi[u], osc[u], lambda s, srow=srow: srow[s], t + 1, k,
+                      tol, t=t, what="ragged prefill bench row %d" % row)
