@@ -17,6 +17,11 @@
  *   - HISA (PaperTrace section 2.1; blog "Route 1: HISA"): block
  *     representatives are scored, r blocks are kept, their tokens are
  *     rescored exactly, token top-k.
+ * Further entry points: MISA x HISA in series, LISA's linear score and
+ * ResMiSA (PaperTrace sections 3.1-3.2), an FP8 (E4M3) key cache for DSA,
+ * MISA and HISA with the query in bf16 or in E4M3 (section 2.3), ragged
+ * batches with per-sequence lengths, and the index tidy-up after the top-k
+ * (section 2.2).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE memory owned by the caller, row-major
@@ -40,9 +45,9 @@
  *     accepted; 256 B is recommended).  Workspace contents need no
  *     initialisation and are clobbered.
  *   - Query rows per call: batch * T <= 65535 (rows are a grid dimension of
- *     the scan kernels), except the fused prefill path of indexer_score_topk
- *     and lisa_score_topk (T >= 16), which takes batch <= 65535 sequences of
- *     any T; SA_EUNSUPPORTED otherwise.
+ *     the scan kernels), except the fused prefill path of indexer_score_topk,
+ *     indexer_score_topk_ragged and lisa_score_topk (T >= 16), which takes
+ *     batch <= 65535 sequences of any T; SA_EUNSUPPORTED otherwise.
  *   - Inputs must be finite; NaN / inf scores give unspecified selections.
  *   - Return value: SA_OK or a negative SA_E* code; sa_last_error() then
  *     returns a message for the calling thread.  On error nothing has been
