@@ -212,3 +212,14 @@ def test_new_entry_points_validate(api):
     assert lib.sa_tidy_indices(p, 4, 3, 64, None, 0, 64, 0, p, None, None) == api.SA_EINVAL
     assert lib.sa_tidy_indices(p, 4, 1, 64, None, 0, 0, 0, p, None, None) == api.SA_EINVAL
     assert lib.sa_tidy_indices(p, 4, 1, 64, p, 0, 64, 0, p, None, None) == api.SA_EINVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # bench.py measures one GPU; asking for more exits with a message before
+    # any device work.
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
