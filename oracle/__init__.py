@@ -56,6 +56,7 @@ def _load():
         _lib.oracle_pool.argtypes = [P, i, i, i, i, P]
         _lib.oracle_quantize_keys_fp8.argtypes = [P, ctypes.c_long, i, P, P, i]
         _lib.oracle_dsa_fp8.argtypes = [P, P, P, i, P, i, P, P, P, i]
+        _lib.oracle_dsa_fp8q.argtypes = [P, P, P, i, P, i, P, P, P, i]
         _lib.oracle_lisa.argtypes = [P, i, P, i, P, P, P, i]
         _lib.oracle_resmisa.argtypes = [P, i, i, i, P, i, P, P, P, P, P, P, i]
         _lib.oracle_box_bound.argtypes = [P, P, P, i]
@@ -65,7 +66,8 @@ def _load():
         _lib.oracle_fp8_e4m3_encode.argtypes = [ctypes.c_float]
         _lib.oracle_fp8_e4m3_encode.restype = ctypes.c_uint8
         for f in (_lib.oracle_dsa, _lib.oracle_misa, _lib.oracle_hisa, _lib.oracle_pool,
-                  _lib.oracle_quantize_keys_fp8, _lib.oracle_dsa_fp8, _lib.oracle_lisa,
+                  _lib.oracle_quantize_keys_fp8, _lib.oracle_dsa_fp8, _lib.oracle_dsa_fp8q,
+                  _lib.oracle_lisa,
                   _lib.oracle_resmisa):
             f.restype = ctypes.c_int
     return _lib
@@ -252,22 +254,24 @@ def dsa_fp8q(prob: Problem, codes, scales, topk: int, rows=None, want_rowscore=F
     converted to the compute type in registers; its error counts on top of
     the key error).
 
-    Each head vector q_{t,j} is quantized by the key-cache rule: b = max|q|/448
-    (1 for a zero vector) and the E4M3 codes of q/b.  b > 0 commutes with ReLU,
-    so the score is a_s * sum_j (w_j b_j) ReLU(decode(qc_j) . decode(c_s)),
-    with the folded weight w_j b_j rounded to fp32, the weight the kernel
-    carries.  Decoded E4M3 values are bf16 values, so this is dsa_fp8 on the
-    decoded query and the folded weights.  Returns (idx, score[, rowscore]).
+    Each head vector q_{t,j} is quantized by the key-cache rule (b_j =
+    max|q|/448 in fp32, 1 for a zero vector; codes of q/b_j), and the score is
+    the indexer formula on the dequantized vectors, in fp64:
+    I = sum_j w_j max((b_j decode(qc_j)) . (a_s decode(c_s)), 0).
+    Returns (idx, score[, rowscore]).
     """
-    qc, qs = quantize_keys_fp8(prob.q, nthreads)
-    qf = fp8_decode(qc).astype(np.float32)
-    qbits = qf.view(np.uint32)
-    assert not np.any(qbits & 0xFFFF), "an E4M3 value must be a bf16 value"
-    qb = (qbits >> 16).astype(np.uint16)
-    wb = (prob.w * qs).astype(np.float32)  # one fp32 rounding per weight
-    folded = Problem(qb, wb, prob.K, prob.offset)
-    return dsa_fp8(folded, codes, scales, topk, rows=rows, want_rowscore=want_rowscore,
-                   nthreads=nthreads)
+    lib = _load()
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    assert codes.shape == (prob.Bt, prob.L, prob.d) and scales.shape == (prob.Bt, prob.L)
+    r, n = prob.rows(rows)
+    idx = np.empty((n, topk), np.int32)
+    sc = np.empty((n, topk), np.float64)
+    rs = np.empty((n, prob.L), np.float64) if want_rowscore else None
+    _check(lib.oracle_dsa_fp8q(ctypes.byref(prob._c), _ptr(codes), _ptr(scales), topk, _ptr(r),
+                               n, _ptr(idx), _ptr(sc), _ptr(rs), _threads(nthreads)),
+           "oracle_dsa_fp8q")
+    return (idx, sc, rs) if want_rowscore else (idx, sc)
 
 
 def lisa(prob: Problem, topk: int, rows=None, want_rowscore=False, nthreads=0):

@@ -711,6 +711,81 @@ int oracle_dsa_fp8(const oracle_problem* p, const uint8_t* codes, const float* s
     return run_rows(dsa8_row, &c, nrows, nthreads);
 }
 
+/* DSA on FP8 keys with the query converted to E4M3 as well ([PT] section
+ * 2.3: the query is converted to the compute type of the fp8 product; its
+ * quantization error adds to the key's).  Each head vector q_{t,j} is
+ * quantized by the key rule of quantize_one_key (scale b_j = max|q|/448 in
+ * fp32, codes of q/b_j), so the row's query is the dequantized
+ * qhat_j = b_j * e4m3(qc_j); key s is khat_s = a_s * e4m3(c_s).  The score is
+ * the plain indexer formula on those vectors, in fp64:
+ *   I = sum_j w_j * max(qhat_j . khat_s, 0). */
+static int dsa8q_row(void* vctx, int r)
+{
+    dsa8_ctx* c = (dsa8_ctx*)vctx;
+    const oracle_problem* p = c->p;
+    int row = c->rows ? c->rows[r] : r;
+    int t = t_of(p, row);
+    int n = t + 1;
+    int b = row / p->T;
+    const uint16_t* qrow = qrow_of(p, row);
+    const float* wrow = wrow_of(p, row);
+    scored_t* cand = (scored_t*)malloc(sizeof(scored_t) * (size_t)n);
+    double* key = (double*)malloc(sizeof(double) * (size_t)p->d);
+    double* qhat = (double*)malloc(sizeof(double) * (size_t)p->H * p->d);
+    uint8_t* qc = (uint8_t*)malloc((size_t)p->d);
+    if (!cand || !key || !qhat || !qc) {
+        free(cand);
+        free(key);
+        free(qhat);
+        free(qc);
+        return ORACLE_ENOMEM;
+    }
+    for (int j = 0; j < p->H; ++j) {
+        float bj;
+        quantize_one_key(qrow + (size_t)j * p->d, p->d, qc, &bj);
+        for (int x = 0; x < p->d; ++x)
+            qhat[(size_t)j * p->d + x] = (double)bj * oracle_fp8_e4m3_decode(qc[x]);
+    }
+    double* rs = c->out_rowscore ? c->out_rowscore + (size_t)r * p->L : NULL;
+    for (int s = 0; s < n; ++s) {
+        size_t ks = (size_t)b * p->L + s;
+        for (int x = 0; x < p->d; ++x)
+            key[x] = (double)c->scales[ks] * oracle_fp8_e4m3_decode(c->codes[ks * p->d + x]);
+        double acc = 0.0;
+        for (int j = 0; j < p->H; ++j) {
+            double z = 0.0;
+            for (int x = 0; x < p->d; ++x) z += qhat[(size_t)j * p->d + x] * key[x];
+            acc += (double)wrow[j] * (z > 0.0 ? z : 0.0);
+        }
+        cand[s].score = acc;
+        cand[s].idx = s;
+        if (rs) rs[s] = acc;
+    }
+    if (rs)
+        for (int s = n; s < p->L; ++s) rs[s] = NAN;
+    int kept = select_top(cand, n, c->topk);
+    write_topk(cand, kept, c->topk, c->out_idx + (size_t)r * c->topk,
+               c->out_score + (size_t)r * c->topk);
+    free(cand);
+    free(key);
+    free(qhat);
+    free(qc);
+    return 0;
+}
+
+int oracle_dsa_fp8q(const oracle_problem* p, const uint8_t* codes, const float* scales, int topk,
+                    const int32_t* rows, int nrows, int32_t* out_idx, double* out_score,
+                    double* out_rowscore, int nthreads)
+{
+    if (!p || !p->q || !p->w || !codes || !scales) return ORACLE_EINVAL;
+    if (p->Bt < 1 || p->T < 1 || p->H < 1 || p->d < 1 || p->L < 1) return ORACLE_EINVAL;
+    if (p->causal_offset < 0 || (long)p->causal_offset + p->T > p->L) return ORACLE_EINVAL;
+    if (topk < 1 || !out_idx || !out_score) return ORACLE_EINVAL;
+    if (!rows) nrows = p->Bt * p->T;
+    dsa8_ctx c = {p, codes, scales, topk, rows, out_idx, out_score, out_rowscore};
+    return run_rows(dsa8q_row, &c, nrows, nthreads);
+}
+
 /* --------------------------------------------------------------- pool */
 
 int oracle_pool(const uint16_t* K, int Bt, int L, int d, int block, double* out)

@@ -83,6 +83,12 @@ int oracle_dsa_fp8(const oracle_problem* p, const uint8_t* codes, const float* s
                    const int32_t* rows, int nrows, int32_t* out_idx, double* out_score,
                    double* out_rowscore, int nthreads);
 
+/* DSA on FP8 keys with the query quantized per head by the key rule as well:
+ * I = sum_j w_j max((b_j e4m3(qc_j)) . (a_s e4m3(c_s)), 0) in fp64. */
+int oracle_dsa_fp8q(const oracle_problem* p, const uint8_t* codes, const float* scales, int topk,
+                    const int32_t* rows, int nrows, int32_t* out_idx, double* out_score,
+                    double* out_rowscore, int nthreads);
+
 /* LISA ([PT] 3.1): top-k by the linear score l = g . k, g = sum_j w_j q_j. */
 int oracle_lisa(const oracle_problem* p, int topk, const int32_t* rows, int nrows,
                 int32_t* out_idx, double* out_score, double* out_rowscore, int nthreads);

@@ -131,24 +131,59 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
 def _bf16(t, name, ndim):
-    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype not in BF16:
         raise TypeError("%s must hold bf16 bits (bfloat16/int16/uint16), got %s" % (name, t.dtype))
-    if t.dim() != ndim or not t.is_cuda or not t.is_contiguous():
-        raise ValueError("%s must be a contiguous %d-d GPU tensor" % (name, ndim))
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %d-d tensor" % (name, ndim))
     return t
+
+
+def _tensor(t, name, dtypes, shape, device):
+    """Check a caller-supplied tensor the library will read or write through a
+    raw pointer: dtype, exact shape, contiguity and device."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a tensor" % name)
+    if t.dtype not in dtypes:
+        raise TypeError("%s must be %s, got %s" % (name, "/".join(str(d) for d in dtypes),
+                                                   t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    return t
+
+
+def _opt(t, name, dtypes, shape, device):
+    return None if t is None else _tensor(t, name, dtypes, shape, device)
+
+
+def _gpu(t):
+    """Every pointer handed to the library must be device memory."""
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a GPU (got %s)" % t.device)
+
+
+def _blocks(L, blk):
+    return (L + int(blk) - 1) // int(blk)
 
 
 def _shape(q, w, keys, causal_offset, topk):
     _bf16(q, "q", 4)
     _bf16(keys, "keys", 3)
-    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
-        raise TypeError("w must be a contiguous float32 GPU tensor")
     B, T, H, d = q.shape
-    if tuple(w.shape) != (B, T, H) or keys.shape[0] != B or keys.shape[2] != d:
+    _tensor(w, "w", (torch.float32,), (B, T, H), q.device)
+    if keys.shape[0] != B or keys.shape[2] != d:
         raise ValueError("shapes disagree: q %s w %s keys %s" % (tuple(q.shape), tuple(w.shape),
                                                                   tuple(keys.shape)))
-    if not (q.device == w.device == keys.device):
+    if keys.device != q.device:
         raise ValueError("q, w and keys must be on one device")
     return Shape(B, T, H, d, keys.shape[1], int(causal_offset), int(topk))
 
@@ -157,25 +192,39 @@ def _outputs(q, topk, out_idx, out_score, want_score):
     B, T = q.shape[0], q.shape[1]
     if out_idx is None:
         out_idx = torch.empty((B, T, topk), dtype=torch.int32, device=q.device)
+    else:
+        _tensor(out_idx, "out_idx", (torch.int32,), (B, T, topk), q.device)
     if out_score is None and want_score:
         out_score = torch.empty((B, T, topk), dtype=torch.float32, device=q.device)
+    elif out_score is not None:
+        _tensor(out_score, "out_score", (torch.float32,), (B, T, topk), q.device)
     return out_idx, out_score
 
 
 def _workspace(nbytes, device, ws):
     if ws is not None:
-        if ws.numel() * ws.element_size() < nbytes:
-            raise ValueError("workspace too small: %d < %d" % (ws.numel() * ws.element_size(),
-                                                              nbytes))
+        if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8:
+            raise TypeError("ws must be a uint8 tensor")
+        if not ws.is_contiguous() or ws.device != device:
+            raise ValueError("ws must be contiguous and on %s" % device)
+        if ws.numel() < nbytes:
+            raise ValueError("workspace too small: %d < %d" % (ws.numel(), nbytes))
         return ws
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def indexer_score_topk_ws(shape: Shape) -> int:
+def _seq_lens(seq_lens, B, device):
+    return _tensor(seq_lens, "seq_lens", (torch.int32,), (B,), device)
+
+
+def _ws_query(fn, name, *args):
     n = ctypes.c_size_t()
-    _check(load().indexer_score_topk_ws(ctypes.byref(shape), ctypes.byref(n)),
-           "indexer_score_topk_ws")
+    _check(fn(*args, ctypes.byref(n)), name)
     return n.value
+
+
+def indexer_score_topk_ws(shape: Shape) -> int:
+    return _ws_query(load().indexer_score_topk_ws, "indexer_score_topk_ws", ctypes.byref(shape))
 
 
 def indexer_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=None,
@@ -184,19 +233,29 @@ def indexer_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=
     s = _shape(q, w, keys, causal_offset, topk)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(indexer_score_topk_ws(s), q.device, ws)
+    _gpu(q)
     _check(load().indexer_score_topk(_p(q), _p(w), _p(keys), ctypes.byref(s), _p(out_idx),
                                      _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
            "indexer_score_topk")
     return out_idx, out_score
 
 
+def _reps_out(keys, block, out, name):
+    B, L, d = keys.shape
+    shape = (B, _blocks(L, block), 2, d)
+    if out is None:
+        return torch.empty(shape, dtype=torch.int16, device=keys.device)
+    return _tensor(out, name, BF16, shape, keys.device)
+
+
 def pool_blocks(keys, block, out=None):
     """Block means of keys -> [batch, ceil(L/block), 2, 128] bf16 hi/lo pairs."""
     _bf16(keys, "keys", 3)
+    if int(block) < 1:
+        raise ValueError("block must be >= 1")
     B, L, d = keys.shape
-    nb = (L + block - 1) // block
-    if out is None:
-        out = torch.empty((B, nb, 2, d), dtype=torch.int16, device=keys.device)
+    out = _reps_out(keys, block, out, "out")
+    _gpu(keys)
     _check(load().sa_pool_blocks(_p(keys), B, L, d, int(block), _p(out), _stream(keys.device)),
            "sa_pool_blocks")
     return out
@@ -205,37 +264,52 @@ def pool_blocks(keys, block, out=None):
 def pool_blocks2(keys, small, large, out_small=None, out_large=None):
     """Both block pools in one pass over the keys."""
     _bf16(keys, "keys", 3)
+    if int(small) < 1 or int(large) < 1:
+        raise ValueError("block sizes must be >= 1")
     B, L, d = keys.shape
-    if out_small is None:
-        out_small = torch.empty((B, (L + small - 1) // small, 2, d), dtype=torch.int16,
-                                device=keys.device)
-    if out_large is None:
-        out_large = torch.empty((B, (L + large - 1) // large, 2, d), dtype=torch.int16,
-                                device=keys.device)
+    out_small = _reps_out(keys, small, out_small, "out_small")
+    out_large = _reps_out(keys, large, out_large, "out_large")
+    _gpu(keys)
     _check(load().sa_pool_blocks2(_p(keys), B, L, d, int(small), int(large), _p(out_small),
                                   _p(out_large), _stream(keys.device)), "sa_pool_blocks2")
     return out_small, out_large
 
 
+def _reps_in(t, name, q, L, block):
+    """Block representatives given by the caller: [batch, ceil(L/block), 2, 128]."""
+    if t is None:
+        return None
+    if int(block) < 1:
+        raise ValueError("block size must be >= 1")
+    return _tensor(t, name, BF16, (q.shape[0], _blocks(L, block), 2, q.shape[3]), q.device)
+
+
+def _rows_out(t, name, q, n, want):
+    """int32 [batch, T, n] per-row output (heads, blocks, pool), or None."""
+    if t is not None:
+        return _tensor(t, name, (torch.int32,), (q.shape[0], q.shape[1], n), q.device)
+    if want and n > 0:
+        return torch.empty((q.shape[0], q.shape[1], n), dtype=torch.int32, device=q.device)
+    return None
+
+
 def misa_route_ws(shape: Shape, block_B, h, k_prime, pooled_given) -> int:
-    n = ctypes.c_size_t()
-    _check(load().misa_route_ws(ctypes.byref(shape), int(block_B), int(h), int(k_prime),
-                                int(bool(pooled_given)), ctypes.byref(n)), "misa_route_ws")
-    return n.value
+    return _ws_query(load().misa_route_ws, "misa_route_ws", ctypes.byref(shape), int(block_B),
+                     int(h), int(k_prime), int(bool(pooled_given)))
 
 
 def misa_route(q, w, keys, causal_offset, topk, block_B, h, k_prime=0, pooled=None,
                want_heads=True, want_pool=False, out_idx=None, out_score=None,
-               want_score=True, ws=None):
+               want_score=True, ws=None, out_heads=None, out_pool=None):
     """MISA routed indexer (k_prime=0) or MISA-dagger (k_prime >= topk).
     Returns (idx, score, heads, pool)."""
     s = _shape(q, w, keys, causal_offset, topk)
-    B, T = q.shape[0], q.shape[1]
+    pooled = _reps_in(pooled, "pooled", q, s.L, block_B)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    heads = torch.empty((B, T, h), dtype=torch.int32, device=q.device) if want_heads else None
-    pool = (torch.empty((B, T, k_prime), dtype=torch.int32, device=q.device)
-            if (want_pool and k_prime) else None)
+    heads = _rows_out(out_heads, "out_heads", q, int(h), want_heads)
+    pool = _rows_out(out_pool, "out_pool", q, int(k_prime), want_pool) if k_prime else None
     ws = _workspace(misa_route_ws(s, block_B, h, k_prime, pooled is not None), q.device, ws)
+    _gpu(q)
     _check(load().misa_route(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_B), int(h),
                              int(k_prime), _p(pooled), _p(heads), _p(pool), _p(out_idx),
                              _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
@@ -244,21 +318,20 @@ def misa_route(q, w, keys, causal_offset, topk, block_B, h, k_prime=0, pooled=No
 
 
 def hisa_coarse_fine_ws(shape: Shape, block_b, r, reps_given) -> int:
-    n = ctypes.c_size_t()
-    _check(load().hisa_coarse_fine_ws(ctypes.byref(shape), int(block_b), int(r),
-                                      int(bool(reps_given)), ctypes.byref(n)),
-           "hisa_coarse_fine_ws")
-    return n.value
+    return _ws_query(load().hisa_coarse_fine_ws, "hisa_coarse_fine_ws", ctypes.byref(shape),
+                     int(block_b), int(r), int(bool(reps_given)))
 
 
 def hisa_coarse_fine(q, w, keys, causal_offset, topk, block_b, r, reps=None,
-                     want_blocks=True, out_idx=None, out_score=None, want_score=True, ws=None):
+                     want_blocks=True, out_idx=None, out_score=None, want_score=True, ws=None,
+                     out_blocks=None):
     """HISA block-then-token search.  Returns (idx, score, blocks)."""
     s = _shape(q, w, keys, causal_offset, topk)
-    B, T = q.shape[0], q.shape[1]
+    reps = _reps_in(reps, "reps", q, s.L, block_b)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    blocks = torch.empty((B, T, r), dtype=torch.int32, device=q.device) if want_blocks else None
+    blocks = _rows_out(out_blocks, "out_blocks", q, int(r), want_blocks)
     ws = _workspace(hisa_coarse_fine_ws(s, block_b, r, reps is not None), q.device, ws)
+    _gpu(q)
     _check(load().hisa_coarse_fine(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_b),
                                    int(r), _p(reps), _p(blocks), _p(out_idx), _p(out_score),
                                    _p(ws), ws.numel(), _stream(q.device)), "hisa_coarse_fine")
@@ -274,8 +347,13 @@ def quantize_keys_fp8(keys, out_codes=None, out_scales=None):
     B, L, d = keys.shape
     if out_codes is None:
         out_codes = torch.empty((B, L, d), dtype=torch.uint8, device=keys.device)
+    else:
+        _tensor(out_codes, "out_codes", (torch.uint8,), (B, L, d), keys.device)
     if out_scales is None:
         out_scales = torch.empty((B, L), dtype=torch.float32, device=keys.device)
+    else:
+        _tensor(out_scales, "out_scales", (torch.float32,), (B, L), keys.device)
+    _gpu(keys)
     _check(load().sa_quantize_keys_fp8(_p(keys), B, L, d, _p(out_codes), _p(out_scales),
                                        _stream(keys.device)), "sa_quantize_keys_fp8")
     return out_codes, out_scales
@@ -283,29 +361,19 @@ def quantize_keys_fp8(keys, out_codes=None, out_scales=None):
 
 def _fp8_shape(q, w, codes, scales, causal_offset, topk):
     _bf16(q, "q", 4)
-    if codes.dtype != torch.uint8 or codes.dim() != 3 or not codes.is_cuda \
-            or not codes.is_contiguous():
-        raise TypeError("codes must be a contiguous uint8 [batch, L, 128] GPU tensor")
-    if scales.dtype != torch.float32 or not scales.is_cuda or not scales.is_contiguous():
-        raise TypeError("scales must be a contiguous float32 GPU tensor")
-    if w.dtype != torch.float32 or not w.is_cuda or not w.is_contiguous():
-        raise TypeError("w must be a contiguous float32 GPU tensor")
     B, T, H, d = q.shape
-    if tuple(w.shape) != (B, T, H) or codes.shape[0] != B or codes.shape[2] != d \
-            or tuple(scales.shape) != tuple(codes.shape[:2]):
-        raise ValueError("shapes disagree: q %s w %s codes %s scales %s"
-                         % (tuple(q.shape), tuple(w.shape), tuple(codes.shape),
-                            tuple(scales.shape)))
-    if not (q.device == w.device == codes.device == scales.device):
-        raise ValueError("q, w, codes and scales must be on one device")
-    return Shape(B, T, H, d, codes.shape[1], int(causal_offset), int(topk))
+    if not isinstance(codes, torch.Tensor) or codes.dtype != torch.uint8 or codes.dim() != 3:
+        raise TypeError("codes must be a uint8 [batch, L, 128] tensor")
+    L = codes.shape[1]
+    _tensor(codes, "codes", (torch.uint8,), (B, L, d), q.device)
+    _tensor(scales, "scales", (torch.float32,), (B, L), q.device)
+    _tensor(w, "w", (torch.float32,), (B, T, H), q.device)
+    return Shape(B, T, H, d, L, int(causal_offset), int(topk))
 
 
 def indexer_score_topk_fp8_ws(shape: Shape) -> int:
-    n = ctypes.c_size_t()
-    _check(load().indexer_score_topk_fp8_ws(ctypes.byref(shape), ctypes.byref(n)),
-           "indexer_score_topk_fp8_ws")
-    return n.value
+    return _ws_query(load().indexer_score_topk_fp8_ws, "indexer_score_topk_fp8_ws",
+                     ctypes.byref(shape))
 
 
 def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=None,
@@ -314,6 +382,7 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
     s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(indexer_score_topk_fp8_ws(s), q.device, ws)
+    _gpu(q)
     _check(load().indexer_score_topk_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                          _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                          _stream(q.device)), "indexer_score_topk_fp8")
@@ -321,10 +390,8 @@ def indexer_score_topk_fp8(q, w, codes, scales, causal_offset, topk, out_idx=Non
 
 
 def indexer_score_topk_fp8q_ws(shape: Shape) -> int:
-    n = ctypes.c_size_t()
-    _check(load().indexer_score_topk_fp8q_ws(ctypes.byref(shape), ctypes.byref(n)),
-           "indexer_score_topk_fp8q_ws")
-    return n.value
+    return _ws_query(load().indexer_score_topk_fp8q_ws, "indexer_score_topk_fp8q_ws",
+                     ctypes.byref(shape))
 
 
 def indexer_score_topk_fp8q(q, w, codes, scales, causal_offset, topk, out_idx=None,
@@ -334,6 +401,7 @@ def indexer_score_topk_fp8q(q, w, codes, scales, causal_offset, topk, out_idx=No
     s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(indexer_score_topk_fp8q_ws(s), q.device, ws)
+    _gpu(q)
     _check(load().indexer_score_topk_fp8q(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                           _p(out_idx), _p(out_score), _p(ws), ws.numel(),
                                           _stream(q.device)), "indexer_score_topk_fp8q")
@@ -344,16 +412,18 @@ def indexer_score_topk_fp8_ragged(q, w, codes, scales, seq_lens, topk, total_len
                                   out_idx=None, out_score=None, want_score=True, ws=None):
     """Ragged batches over an FP8 key cache (capacity codes.shape[1]); q_fp8
     picks the E4M3-query scores of indexer_score_topk_fp8q."""
-    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != q.shape[0]:
-        raise TypeError("seq_lens must be an int32 GPU tensor with one entry per sequence")
+    _bf16(q, "q", 4)
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 3:
+        raise TypeError("codes must be a uint8 [batch, L, 128] tensor")
     s = _fp8_shape(q, w, codes, scales, codes.shape[1] - q.shape[1], topk)
+    _seq_lens(seq_lens, q.shape[0], q.device)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    n = ctypes.c_size_t()
-    _check(load().indexer_score_topk_fp8_ragged_ws(ctypes.byref(s), ctypes.byref(n)),
-           "indexer_score_topk_fp8_ragged_ws")
-    ws = _workspace(n.value, q.device, ws)
+    n = _ws_query(load().indexer_score_topk_fp8_ragged_ws, "indexer_score_topk_fp8_ragged_ws",
+                  ctypes.byref(s))
+    ws = _workspace(n, q.device, ws)
+    _gpu(q)
     _check(load().indexer_score_topk_fp8_ragged(_p(q), _p(w), _p(codes), _p(scales),
-                                                _p(seq_lens.contiguous()), int(total_len),
+                                                _p(seq_lens), int(total_len),
                                                 int(bool(q_fp8)), ctypes.byref(s), _p(out_idx),
                                                 _p(out_score), _p(ws), ws.numel(),
                                                 _stream(q.device)),
@@ -363,18 +433,17 @@ def indexer_score_topk_fp8_ragged(q, w, codes, scales, seq_lens, topk, total_len
 
 def misa_route_fp8(q, w, codes, scales, causal_offset, topk, block_B, h, k_prime=0, pooled=None,
                    want_heads=True, want_pool=False, out_idx=None, out_score=None,
-                   want_score=True, ws=None):
+                   want_score=True, ws=None, out_heads=None, out_pool=None):
     """misa_route over an FP8 key cache.  Returns (idx, score, heads, pool)."""
     s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
-    B, T = q.shape[0], q.shape[1]
+    pooled = _reps_in(pooled, "pooled", q, s.L, block_B)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    heads = torch.empty((B, T, h), dtype=torch.int32, device=q.device) if want_heads else None
-    pool = (torch.empty((B, T, k_prime), dtype=torch.int32, device=q.device)
-            if (want_pool and k_prime) else None)
-    n = ctypes.c_size_t()
-    _check(load().misa_route_fp8_ws(ctypes.byref(s), int(block_B), int(h), int(k_prime),
-                                    int(pooled is not None), ctypes.byref(n)), "misa_route_fp8_ws")
-    ws = _workspace(n.value, q.device, ws)
+    heads = _rows_out(out_heads, "out_heads", q, int(h), want_heads)
+    pool = _rows_out(out_pool, "out_pool", q, int(k_prime), want_pool) if k_prime else None
+    n = _ws_query(load().misa_route_fp8_ws, "misa_route_fp8_ws", ctypes.byref(s), int(block_B),
+                  int(h), int(k_prime), int(pooled is not None))
+    ws = _workspace(n, q.device, ws)
+    _gpu(q)
     _check(load().misa_route_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                  int(block_B), int(h), int(k_prime), _p(pooled), _p(heads),
                                  _p(pool), _p(out_idx), _p(out_score), _p(ws), ws.numel(),
@@ -384,17 +453,16 @@ def misa_route_fp8(q, w, codes, scales, causal_offset, topk, block_B, h, k_prime
 
 def hisa_coarse_fine_fp8(q, w, codes, scales, causal_offset, topk, block_b, r, reps=None,
                          want_blocks=True, out_idx=None, out_score=None, want_score=True,
-                         ws=None):
+                         ws=None, out_blocks=None):
     """hisa_coarse_fine over an FP8 key cache.  Returns (idx, score, blocks)."""
     s = _fp8_shape(q, w, codes, scales, causal_offset, topk)
-    B, T = q.shape[0], q.shape[1]
+    reps = _reps_in(reps, "reps", q, s.L, block_b)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    blocks = torch.empty((B, T, r), dtype=torch.int32, device=q.device) if want_blocks else None
-    n = ctypes.c_size_t()
-    _check(load().hisa_coarse_fine_fp8_ws(ctypes.byref(s), int(block_b), int(r),
-                                          int(reps is not None), ctypes.byref(n)),
-           "hisa_coarse_fine_fp8_ws")
-    ws = _workspace(n.value, q.device, ws)
+    blocks = _rows_out(out_blocks, "out_blocks", q, int(r), want_blocks)
+    n = _ws_query(load().hisa_coarse_fine_fp8_ws, "hisa_coarse_fine_fp8_ws", ctypes.byref(s),
+                  int(block_b), int(r), int(reps is not None))
+    ws = _workspace(n, q.device, ws)
+    _gpu(q)
     _check(load().hisa_coarse_fine_fp8(_p(q), _p(w), _p(codes), _p(scales), ctypes.byref(s),
                                        int(block_b), int(r), _p(reps), _p(blocks), _p(out_idx),
                                        _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
@@ -408,21 +476,29 @@ def tidy_indices(idx, T, block_table=None, page_size=1, max_slots=0, out_slots=N
                  out_stats=None, want_stats=True):
     """Selected positions [batch, T, k] (or [rows, k]) -> distinct physical
     slots in ascending order, -1 padded, and per-row (slots, pages, runs)."""
-    if idx.dtype != torch.int32 or not idx.is_cuda or not idx.is_contiguous():
-        raise TypeError("idx must be a contiguous int32 GPU tensor")
+    if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int32 or not idx.is_contiguous():
+        raise TypeError("idx must be a contiguous int32 tensor")
+    if idx.dim() < 1 or idx.numel() == 0:
+        raise ValueError("idx must have at least one row")
     k = idx.shape[-1]
     rows = idx.numel() // k
+    if int(T) < 1 or rows % int(T):
+        raise ValueError("T must divide the number of rows (%d)" % rows)
     if block_table is not None:
-        if (block_table.dtype != torch.int32 or not block_table.is_cuda
-                or not block_table.is_contiguous() or block_table.dim() != 2):
-            raise TypeError("block_table must be a contiguous int32 [batch, pages] GPU tensor")
-        if block_table.shape[0] * int(T) != rows:
-            raise ValueError("block_table needs one row per sequence (rows / T = %d), has %d"
-                             % (rows // int(T), block_table.shape[0]))
+        if (not isinstance(block_table, torch.Tensor) or block_table.dtype != torch.int32
+                or block_table.dim() != 2):
+            raise TypeError("block_table must be an int32 [batch, pages] tensor")
+        _tensor(block_table, "block_table", (torch.int32,), (rows // int(T), block_table.shape[1]),
+                idx.device)
     if out_slots is None:
         out_slots = torch.empty_like(idx)
+    else:
+        _tensor(out_slots, "out_slots", (torch.int32,), tuple(idx.shape), idx.device)
     if out_stats is None and want_stats:
         out_stats = torch.empty(idx.shape[:-1] + (3,), dtype=torch.int32, device=idx.device)
+    elif out_stats is not None:
+        _tensor(out_stats, "out_stats", (torch.int32,), tuple(idx.shape[:-1]) + (3,), idx.device)
+    _gpu(idx)
     _check(load().sa_tidy_indices(_p(idx), rows, int(T), k, _p(block_table),
                                   0 if block_table is None else block_table.shape[1],
                                   int(page_size), int(max_slots), _p(out_slots), _p(out_stats),
@@ -431,10 +507,8 @@ def tidy_indices(idx, T, block_table=None, page_size=1, max_slots=0, out_slots=N
 
 
 def indexer_score_topk_ragged_ws(shape: Shape) -> int:
-    n = ctypes.c_size_t()
-    _check(load().indexer_score_topk_ragged_ws(ctypes.byref(shape), ctypes.byref(n)),
-           "indexer_score_topk_ragged_ws")
-    return n.value
+    return _ws_query(load().indexer_score_topk_ragged_ws, "indexer_score_topk_ragged_ws",
+                     ctypes.byref(shape))
 
 
 def indexer_score_topk_ragged(q, w, keys, seq_lens, topk, total_len=0, out_idx=None,
@@ -443,14 +517,16 @@ def indexer_score_topk_ragged(q, w, keys, seq_lens, topk, total_len=0, out_idx=N
     seq_lens int32 [batch] on the GPU; row i of sequence b sits at
     seq_lens[b] - T + i.  total_len: the host's sum of the lengths (0 if
     unknown), used only to size the work per workgroup."""
-    if seq_lens.dtype != torch.int32 or not seq_lens.is_cuda or seq_lens.numel() != q.shape[0]:
-        raise TypeError("seq_lens must be an int32 GPU tensor with one entry per sequence")
+    _bf16(q, "q", 4)
+    _bf16(keys, "keys", 3)
     s = _shape(q, w, keys, keys.shape[1] - q.shape[1], topk)
+    _seq_lens(seq_lens, q.shape[0], q.device)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(indexer_score_topk_ragged_ws(s), q.device, ws)
-    _check(load().indexer_score_topk_ragged(_p(q), _p(w), _p(keys), _p(seq_lens.contiguous()),
-                                            int(total_len), ctypes.byref(s), _p(out_idx), _p(out_score), _p(ws),
-                                            ws.numel(), _stream(q.device)),
+    _gpu(q)
+    _check(load().indexer_score_topk_ragged(_p(q), _p(w), _p(keys), _p(seq_lens),
+                                            int(total_len), ctypes.byref(s), _p(out_idx),
+                                            _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
            "indexer_score_topk_ragged")
     return out_idx, out_score
 
@@ -458,11 +534,9 @@ def indexer_score_topk_ragged(q, w, keys, seq_lens, topk, total_len=0, out_idx=N
 # ---------------------------------------------------------- MISA x HISA
 
 def misa_hisa_ws(shape: Shape, block_B, h, block_b, r, pooled_given, reps_given) -> int:
-    n = ctypes.c_size_t()
-    _check(load().misa_hisa_ws(ctypes.byref(shape), int(block_B), int(h), int(block_b), int(r),
-                               int(bool(pooled_given)), int(bool(reps_given)), ctypes.byref(n)),
-           "misa_hisa_ws")
-    return n.value
+    return _ws_query(load().misa_hisa_ws, "misa_hisa_ws", ctypes.byref(shape), int(block_B),
+                     int(h), int(block_b), int(r), int(bool(pooled_given)),
+                     int(bool(reps_given)))
 
 
 def misa_hisa(q, w, keys, causal_offset, topk, block_B, h, block_b, r, pooled=None, reps=None,
@@ -471,16 +545,14 @@ def misa_hisa(q, w, keys, causal_offset, topk, block_B, h, block_b, r, pooled=No
     """MISA router heads -> HISA block scores over those heads -> every-head
     rescoring of the r best blocks' tokens.  Returns (idx, score, heads, blocks)."""
     s = _shape(q, w, keys, causal_offset, topk)
-    B, T = q.shape[0], q.shape[1]
+    pooled = _reps_in(pooled, "pooled", q, s.L, block_B)
+    reps = _reps_in(reps, "reps", q, s.L, block_b)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    heads = out_heads
-    if heads is None and want_heads:
-        heads = torch.empty((B, T, h), dtype=torch.int32, device=q.device)
-    blocks = out_blocks
-    if blocks is None and want_blocks:
-        blocks = torch.empty((B, T, r), dtype=torch.int32, device=q.device)
+    heads = _rows_out(out_heads, "out_heads", q, int(h), want_heads)
+    blocks = _rows_out(out_blocks, "out_blocks", q, int(r), want_blocks)
     ws = _workspace(misa_hisa_ws(s, block_B, h, block_b, r, pooled is not None, reps is not None),
                     q.device, ws)
+    _gpu(q)
     _check(load().misa_hisa(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_B), int(h),
                             int(block_b), int(r), _p(pooled), _p(reps), _p(heads), _p(blocks),
                             _p(out_idx), _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
@@ -491,9 +563,7 @@ def misa_hisa(q, w, keys, causal_offset, topk, block_B, h, block_b, r, pooled=No
 # ------------------------------------------------------- LISA / ResMiSA
 
 def lisa_score_topk_ws(shape: Shape) -> int:
-    n = ctypes.c_size_t()
-    _check(load().lisa_score_topk_ws(ctypes.byref(shape), ctypes.byref(n)), "lisa_score_topk_ws")
-    return n.value
+    return _ws_query(load().lisa_score_topk_ws, "lisa_score_topk_ws", ctypes.byref(shape))
 
 
 def lisa_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=None,
@@ -502,6 +572,7 @@ def lisa_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=Non
     s = _shape(q, w, keys, causal_offset, topk)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(lisa_score_topk_ws(s), q.device, ws)
+    _gpu(q)
     _check(load().lisa_score_topk(_p(q), _p(w), _p(keys), ctypes.byref(s), _p(out_idx),
                                   _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
            "lisa_score_topk")
@@ -511,20 +582,19 @@ def lisa_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=Non
 def block_extrema(keys, block, out=None):
     """Per-block key max then min -> [batch, ceil(L/block), 2, 128] bf16 bits."""
     _bf16(keys, "keys", 3)
+    if int(block) < 1:
+        raise ValueError("block must be >= 1")
     B, L, d = keys.shape
-    nb = (L + block - 1) // block
-    if out is None:
-        out = torch.empty((B, nb, 2, d), dtype=torch.int16, device=keys.device)
+    out = _reps_out(keys, block, out, "out")
+    _gpu(keys)
     _check(load().sa_block_extrema(_p(keys), B, L, d, int(block), _p(out), _stream(keys.device)),
            "sa_block_extrema")
     return out
 
 
 def resmisa_route_ws(shape: Shape, block, r, extrema_given) -> int:
-    n = ctypes.c_size_t()
-    _check(load().resmisa_route_ws(ctypes.byref(shape), int(block), int(r),
-                                   int(bool(extrema_given)), ctypes.byref(n)), "resmisa_route_ws")
-    return n.value
+    return _ws_query(load().resmisa_route_ws, "resmisa_route_ws", ctypes.byref(shape),
+                     int(block), int(r), int(bool(extrema_given)))
 
 
 def resmisa_route(q, w, keys, causal_offset, topk, block, r, extrema=None, want_heads=True,
@@ -532,12 +602,11 @@ def resmisa_route(q, w, keys, causal_offset, topk, block, r, extrema=None, want_
     """ResMiSA: shared linear score + r routed residual heads.  Returns
     (idx, score, heads)."""
     s = _shape(q, w, keys, causal_offset, topk)
-    B, T = q.shape[0], q.shape[1]
+    extrema = _reps_in(extrema, "extrema", q, s.L, block) if int(r) > 0 else None
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
-    heads = out_heads
-    if heads is None and want_heads and r > 0:
-        heads = torch.empty((B, T, r), dtype=torch.int32, device=q.device)
+    heads = _rows_out(out_heads, "out_heads", q, int(r), want_heads) if int(r) > 0 else None
     ws = _workspace(resmisa_route_ws(s, block, r, extrema is not None), q.device, ws)
+    _gpu(q)
     _check(load().resmisa_route(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block), int(r),
                                 _p(extrema), _p(heads), _p(out_idx), _p(out_score), _p(ws),
                                 ws.numel(), _stream(q.device)), "resmisa_route")

@@ -9,6 +9,7 @@ lengths equals the padded DSA call.
 from __future__ import annotations
 
 import numpy as np
+import pytest
 
 import oracle
 from sparse_attention_token_dsa_amd import synth
@@ -71,3 +72,40 @@ def test_ragged_equals_per_sequence_and_padded():
     i2, s2, _ = oracle.dsa_ragged(p["q"], p["w"], p["K"], full, 40)
     i3, s3 = oracle.dsa(oracle.Problem(p["q"], p["w"], p["K"], 898), 40)
     assert np.array_equal(i2, i3) and np.array_equal(s2, s3)
+
+
+def test_ragged_brute_force_with_needles_past_each_length():
+    # Exact rational brute force (tests/brute.py), written from the reading
+    # of seq_lens alone: sequence b's history is keys 0 .. n_b - 1 and its row
+    # i sits at t = n_b - T + i.  Keys at and after n_b are planted to beat
+    # every legal key of every row, so reading past a sequence's length (or
+    # placing the rows at the capacity) would select them.
+    import brute
+    Bt, T, L, H, d, k = 3, 2, 11, 3, 8, 3
+    p = synth.make_problem(72, Bt=Bt, T=T, L=L, H=H, d=d, offset=L - T)
+    w = np.abs(p["w"]).astype(np.float32)
+    K = p["K"].copy()
+    lens = np.array([11, 7, 3], np.int32)
+    qf = synth.bf16_bits_to_f32(p["q"])
+    for b in range(Bt):
+        for s in range(lens[b], L):
+            K[b, s] = synth.to_bf16_bits(8.0 * (qf[b, 0, 0] + qf[b, 1, 0]))
+    idx, sc, rs = oracle.dsa_ragged(p["q"], w, K, lens, k)
+    for b in range(Bt):
+        n = int(lens[b])
+        qe, we, ke = brute.exact_vectors(p["q"][b], w[b], K[b])
+        for i in range(T):
+            row, t = b * T + i, n - T + i
+            sel, scores = brute.dsa_row(qe, we, ke, i, t, k)
+            got = [int(s) for s in idx[row] if s >= 0]
+            assert len(got) == min(k, t + 1)
+            assert set(got) == set(sel), (b, i, got, sorted(sel))
+            assert all(s <= t for s in got)
+            for u, s in enumerate(idx[row]):
+                if s >= 0:
+                    assert sc[row, u] == pytest.approx(float(scores[int(s)]), rel=1e-12, abs=1e-300)
+            assert np.all(np.isnan(rs[row, t + 1:]))
+            # the planted keys would have won: their exact score beats the kept ones
+            if n < L:
+                planted = brute.score(qe[i], we[i], ke[n])
+                assert all(planted > scores[s] for s in got)
