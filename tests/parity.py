@@ -94,6 +94,46 @@ def _np(t):
     return None if t is None else t.cpu().numpy()
 
 
+class Guarded:
+    """A device buffer with guard bytes on both sides: `view` is what the
+    library gets, the guards hold a fixed byte pattern that check() confirms
+    is untouched after the call (a write past either end of an output or a
+    workspace would change it)."""
+
+    GUARD = 4096
+    PATTERN = 0xA5
+
+    def __init__(self, shape, dtype, device):
+        import torch
+        n = 1
+        for x in shape:
+            n *= int(x)
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        self.raw = torch.full((nbytes + 2 * self.GUARD,), self.PATTERN, dtype=torch.uint8,
+                              device=device)
+        self.nbytes = nbytes
+        self.view = self.raw[self.GUARD:self.GUARD + nbytes].view(dtype).view(*shape)
+
+    def check(self, what="buffer"):
+        g = self.raw.cpu().numpy()
+        lo, hi = g[:self.GUARD], g[self.GUARD + self.nbytes:]
+        assert np.all(lo == self.PATTERN), "%s: guard bytes before it were written" % what
+        assert np.all(hi == self.PATTERN), "%s: guard bytes after it were written" % what
+
+
+def guarded_outputs(q, k, device, ws_bytes):
+    """Guarded out_idx [B, T, k] int32, out_score fp32 and a uint8 workspace."""
+    import torch
+    B, T = q.shape[0], q.shape[1]
+    return (Guarded((B, T, k), torch.int32, device), Guarded((B, T, k), torch.float32, device),
+            Guarded((max(ws_bytes, 1),), torch.uint8, device))
+
+
+def check_guards(*bufs):
+    for i, b in enumerate(bufs):
+        b.check("buffer %d" % i)
+
+
 def rows_of(p, sample=None, seed=0):
     R = p["Bt"] * p["T"]
     if sample is None or sample >= R:

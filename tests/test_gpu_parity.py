@@ -1,9 +1,12 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
 Small cases span several key tiles and chunks with ragged tails (L not a
-multiple of 64 / 128 / 1024 / 8192); the named workloads run at full size with
-sampled rows.  Every comparison uses the rule in tests/parity.py
-(tolerance 2e-3 * max |score| per row, near-tie exchanges only).
+multiple of 64 / 128 / 1024 / 8192); the named workloads run at full size,
+every row of the decode-style ones and 512 rows of the chunked prefill (one
+of each workgroup's two 8-row groups).  Every comparison uses the rule in
+tests/parity.py (tolerance 2e-3 * max |score| per row, near-tie exchanges
+only).  Outputs and workspaces sit between guard bytes that must come back
+untouched.
 """
 from __future__ import annotations
 
@@ -14,7 +17,8 @@ import pytest
 
 import oracle
 import parity
-from parity import _np, check_dsa, check_hisa, check_misa, rows_of, to_device
+from parity import (_np, check_dsa, check_guards, check_hisa, check_misa, guarded_outputs,
+                    rows_of, to_device)
 from sparse_attention_token_dsa_amd import synth
 
 torch = pytest.importorskip("torch")
@@ -39,9 +43,37 @@ def api():
 
 def run_dsa(api, p, k):
     q, w, K = to_device(p, DEV)
-    idx, sc = api.indexer_score_topk(q, w, K, p["offset"], k)
+    shape = api.Shape(p["Bt"], p["T"], p["H"], p["d"], p["L"], p["offset"], k)
+    gi, gs, gw = guarded_outputs(q, k, DEV, api.indexer_score_topk_ws(shape))
+    idx, sc = api.indexer_score_topk(q, w, K, p["offset"], k, out_idx=gi.view,
+                                     out_score=gs.view, ws=gw.view)
     torch.cuda.synchronize()
+    check_guards(gi, gs, gw)
     return _np(idx), _np(sc)
+
+
+def run_misa(api, p, k, B, h, kp):
+    q, w, K = to_device(p, DEV)
+    shape = api.Shape(p["Bt"], p["T"], p["H"], p["d"], p["L"], p["offset"], k)
+    gi, gs, gw = guarded_outputs(q, k, DEV, api.misa_route_ws(shape, B, h, kp, False))
+    idx, sc, heads, pool = api.misa_route(q, w, K, p["offset"], k, B, h, k_prime=kp,
+                                          want_pool=kp > 0, out_idx=gi.view, out_score=gs.view,
+                                          ws=gw.view)
+    torch.cuda.synchronize()
+    check_guards(gi, gs, gw)
+    return _np(idx), _np(sc), _np(heads), _np(pool)
+
+
+def run_hisa(api, p, k, b, r, reps_given=False):
+    q, w, K = to_device(p, DEV)
+    reps = api.pool_blocks(K, b) if reps_given else None
+    shape = api.Shape(p["Bt"], p["T"], p["H"], p["d"], p["L"], p["offset"], k)
+    gi, gs, gw = guarded_outputs(q, k, DEV, api.hisa_coarse_fine_ws(shape, b, r, reps_given))
+    idx, sc, blocks = api.hisa_coarse_fine(q, w, K, p["offset"], k, b, r, reps=reps,
+                                           out_idx=gi.view, out_score=gs.view, ws=gw.view)
+    torch.cuda.synchronize()
+    check_guards(gi, gs, gw)
+    return _np(idx), _np(sc), _np(blocks)
 
 
 # ------------------------------------------------------------------ DSA
@@ -123,18 +155,30 @@ def test_prefill_tiny_full(api):
     check_dsa(p, 128, idx, sc, rows_of(p))
 
 
-def test_decode_32k_sampled(api):
-    say("decode_32k sampled")
+def test_decode_32k_all_rows(api):
+    say("decode_32k all rows")
     p = synth.make_config("decode_32k")
     idx, sc = run_dsa(api, p, 2048)
-    check_dsa(p, 2048, idx, sc, rows_of(p, sample=8, seed=1))
+    check_dsa(p, 2048, idx, sc, rows_of(p))
 
 
-def test_prefill_chunked_sampled(api):
-    say("prefill_chunked sampled")
+def prefill_group_rows(T, seed):
+    """One random row of each 8-row group: the fused prefill's workgroup x
+    runs group x (its short causal range) and group G - 1 - x (its long one),
+    so this covers both groups of every workgroup."""
+    rng = np.random.default_rng(seed)
+    G = (T + 7) // 8
+    return np.array(sorted(min(8 * g + int(rng.integers(0, 8)), T - 1) for g in range(G)),
+                    dtype=np.int32)
+
+
+def test_prefill_chunked_rows(api):
+    say("prefill_chunked 512 rows")
     p = synth.make_config("prefill_chunked")
     idx, sc = run_dsa(api, p, 2048)
-    check_dsa(p, 2048, idx, sc, rows_of(p, sample=32, seed=2))
+    rows = prefill_group_rows(p["T"], 2)
+    assert len(rows) == 512
+    check_dsa(p, 2048, idx, sc, rows)
 
 
 # ----------------------------------------------------------------- MISA
@@ -151,11 +195,8 @@ def test_misa(api, Bt, T, L, H, B, h, k, kp):
     say("misa Bt=%d T=%d L=%d H=%d B=%d h=%d k=%d k'=%d" % (Bt, T, L, H, B, h, k, kp))
     p = synth.make_problem(300 + L % 89, Bt=Bt, T=T, L=L, H=H, needles=8,
                            needle_mode="decode" if T == 1 else "rows")
-    q, w, K = to_device(p, DEV)
-    idx, sc, heads, pool = api.misa_route(q, w, K, p["offset"], k, B, h, k_prime=kp,
-                                          want_pool=kp > 0)
-    torch.cuda.synchronize()
-    check_misa(p, k, B, h, kp, _np(idx), _np(sc), _np(heads), _np(pool), rows_of(p))
+    idx, sc, heads, pool = run_misa(api, p, k, B, h, kp)
+    check_misa(p, k, B, h, kp, idx, sc, heads, pool, rows_of(p))
 
 
 def test_misa_all_heads_equals_dsa(api):
@@ -187,12 +228,8 @@ def test_misa_pooled_given_matches_internal(api):
 def test_misa_configs(api, name, kp):
     say("%s k'=%d" % (name, kp))
     p = synth.make_config(name)
-    q, w, K = to_device(p, DEV)
-    idx, sc, heads, pool = api.misa_route(q, w, K, p["offset"], 2048, 1024, 8, k_prime=kp,
-                                          want_pool=kp > 0)
-    torch.cuda.synchronize()
-    check_misa(p, 2048, 1024, 8, kp, _np(idx), _np(sc), _np(heads), _np(pool),
-               rows_of(p, sample=4, seed=3))
+    idx, sc, heads, pool = run_misa(api, p, 2048, 1024, 8, kp)
+    check_misa(p, 2048, 1024, 8, kp, idx, sc, heads, pool, rows_of(p))
 
 
 # ----------------------------------------------------------------- HISA
@@ -207,20 +244,15 @@ def test_hisa(api, Bt, T, L, H, b, r, k):
     say("hisa Bt=%d T=%d L=%d H=%d b=%d r=%d k=%d" % (Bt, T, L, H, b, r, k))
     p = synth.make_problem(400 + L % 83, Bt=Bt, T=T, L=L, H=H, needles=8,
                            needle_mode="hisa" if T == 1 else "rows", b=b)
-    q, w, K = to_device(p, DEV)
-    idx, sc, blocks = api.hisa_coarse_fine(q, w, K, p["offset"], k, b, r)
-    torch.cuda.synchronize()
-    check_hisa(p, k, b, r, _np(idx), _np(sc), _np(blocks), rows_of(p))
+    idx, sc, blocks = run_hisa(api, p, k, b, r)
+    check_hisa(p, k, b, r, idx, sc, blocks, rows_of(p))
 
 
 def test_hisa_config(api):
     say("hisa_128k")
     p = synth.make_config("hisa_128k")
-    q, w, K = to_device(p, DEV)
-    reps = api.pool_blocks(K, 128)
-    idx, sc, blocks = api.hisa_coarse_fine(q, w, K, p["offset"], 2048, 128, 64, reps=reps)
-    torch.cuda.synchronize()
-    check_hisa(p, 2048, 128, 64, _np(idx), _np(sc), _np(blocks), rows_of(p, sample=4, seed=4))
+    idx, sc, blocks = run_hisa(api, p, 2048, 128, 64, reps_given=True)
+    check_hisa(p, 2048, 128, 64, idx, sc, blocks, rows_of(p))
 
 
 # ----------------------------------------------------------------- pool
