@@ -95,6 +95,33 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------ allocation-free DSA */
+
+/* Size of the static device scratch behind indexer_score_topk_noalloc: 32 MiB
+ * per GPU, held by the library from the first call on that GPU until the
+ * process ends. */
+#define SA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* indexer_score_topk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and outputs, with the workspace
+ * taken from a static device array of SA_NOALLOC_SCRATCH_BYTES instead of a
+ * caller buffer.  The call allocates nothing (no hipMalloc / hipFree); the
+ * first call on a device looks up that device's array address once.
+ *   - Shapes whose indexer_score_topk_ws size exceeds
+ *     SA_NOALLOC_SCRATCH_BYTES are rejected with SA_EWORKSPACE (e.g. 8
+ *     decode rows at L = 131072 need about 12.2 MiB and fit; the 4096-row
+ *     chunked prefill at L = 32768 needs 1 GiB and does not).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     the same GPU (concurrent streams, or host threads, without ordering
+ *     between them) race and give undefined results.  Calls ordered on one
+ *     stream are safe; the array keeps the last call's contents, and each
+ *     call clears what it needs zeroed itself.
+ * Arguments, ownership and errors otherwise as in indexer_score_topk. */
+int indexer_score_topk_noalloc(const uint16_t* q, const float* w, const uint16_t* keys,
+                               const sa_shape* s, int32_t* out_idx, float* out_score,
+                               void* stream);
+
 /* ----------------------------------------------------------- tidy-up */
 
 /* Index tidy-up after any selector (PaperTrace "2.2.2 MISA, LISA and

@@ -38,7 +38,12 @@ EXPORTS = (
     "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged", "indexer_score_topk_fp8q_ws",
     "indexer_score_topk_fp8q", "misa_route_fp8_ws", "misa_route_fp8", "hisa_coarse_fine_fp8_ws",
     "hisa_coarse_fine_fp8", "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged",
+    "indexer_score_topk_noalloc",
 )
+
+# Bytes of the static device scratch behind indexer_score_topk_noalloc
+# (SA_NOALLOC_SCRATCH_BYTES in include/sa_indexer.h).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class SaError(RuntimeError):
@@ -67,6 +72,7 @@ def load():
     SP = ctypes.POINTER(Shape)
     lib.indexer_score_topk_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk.argtypes = [P, P, P, SP, P, P, P, S, P]
+    lib.indexer_score_topk_noalloc.argtypes = [P, P, P, SP, P, P, P]
     lib.sa_pool_blocks.argtypes = [P, I, I, I, I, P, P]
     lib.sa_pool_blocks2.argtypes = [P, I, I, I, I, I, P, P, P]
     lib.misa_route_ws.argtypes = [SP, I, I, I, I, ctypes.POINTER(S)]
@@ -111,7 +117,8 @@ def load():
                  "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged",
                  "indexer_score_topk_fp8q_ws", "indexer_score_topk_fp8q", "misa_route_fp8_ws",
                  "misa_route_fp8", "hisa_coarse_fine_fp8_ws", "hisa_coarse_fine_fp8",
-                 "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged"):
+                 "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged",
+                 "indexer_score_topk_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -237,6 +244,22 @@ def indexer_score_topk(q, w, keys, causal_offset, topk, out_idx=None, out_score=
     _check(load().indexer_score_topk(_p(q), _p(w), _p(keys), ctypes.byref(s), _p(out_idx),
                                      _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
            "indexer_score_topk")
+    return out_idx, out_score
+
+
+def indexer_score_topk_noalloc(q, w, keys, causal_offset, topk, out_idx, out_score=None):
+    """indexer_score_topk with the library's static device scratch in place of
+    a workspace: the call allocates nothing, so out_idx (and out_score, or
+    None) must be given.  Calls that overlap on one GPU race (they share the
+    scratch); shapes needing more than NOALLOC_SCRATCH_BYTES are rejected."""
+    s = _shape(q, w, keys, causal_offset, topk)
+    if out_idx is None:
+        raise ValueError("indexer_score_topk_noalloc allocates nothing: pass out_idx")
+    _outputs(q, topk, out_idx, out_score, False)
+    _gpu(q)
+    _check(load().indexer_score_topk_noalloc(_p(q), _p(w), _p(keys), ctypes.byref(s),
+                                             _p(out_idx), _p(out_score), _stream(q.device)),
+           "indexer_score_topk_noalloc")
     return out_idx, out_score
 
 

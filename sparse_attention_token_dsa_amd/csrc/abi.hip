@@ -480,6 +480,75 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
     return SA_OK;
 }
 
+// ------------------------------------------------- allocation-free DSA
+
+}  // extern "C"
+
+namespace {
+
+// The scratch of indexer_score_topk_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes its name
+// to a kernel (on the host the name is only a stand-in): the device address
+// of each GPU's copy comes from hipGetSymbolAddress with that device current.
+static __device__ __align__(256) unsigned char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// This GPU's scratch address, looked up once per device.
+int scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(SA_EUNSUPPORTED, "device ordinal >= 64");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(SA_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int indexer_score_topk_noalloc(const uint16_t* q, const float* w, const uint16_t* keys,
+                               const sa_shape* s, int32_t* out_idx, float* out_score,
+                               void* stream) {
+    int rc = check_dsa(s);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    const size_t need = plan_dsa(s, nullptr).bytes;
+    if (need > (size_t)SA_NOALLOC_SCRATCH_BYTES)
+        return fail(SA_EWORKSPACE, "this shape needs " + std::to_string(need) +
+                                       " bytes of scratch; the static scratch holds " +
+                                       std::to_string((size_t)SA_NOALLOC_SCRATCH_BYTES));
+    void* base = nullptr;
+    rc = scratch_address(&base);
+    if (rc) return rc;
+    // Same plan and kernels as indexer_score_topk on a workspace at the
+    // scratch's (256-byte aligned) address; the decode path clears its row
+    // state with a fill kernel before the scan.
+    DsaPlan p = plan_dsa(s, base);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (p.prefill) {
+        e = run_prefill(q, w, keys, s, p, out_idx, out_score, st, nullptr);
+        if (e != hipSuccess) return hip_fail(e, "prefill");
+    } else {
+        e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand, s->topk,
+                           out_idx, out_score, st);
+        if (e != hipSuccess) return hip_fail(e, "decode scan");
+    }
+    return SA_OK;
+}
+
 // ------------------------------------------------------------ tidy-up
 
 int sa_tidy_indices(const int32_t* idx, int32_t rows, int32_t T, int32_t k,
