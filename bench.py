@@ -70,6 +70,20 @@ def measured_traffic(kernel, digest):
     return e.get("bytes_per_launch")
 
 
+def measured_mfma(digest):
+    """Counter-derived MFMA figures of the fused prefill (rocprofv3 --pmc,
+    see traffic.py), or None if taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            e = json.load(f).get("prefill_fused_mfma")
+    except (OSError, ValueError):
+        return None
+    if not e or e.get("source_digest") != digest:
+        return None
+    return {k: e[k] for k in ("mfma_busy_frac", "valu_per_mfma", "lds_bank_conflict_frac",
+                              "active_cycles")}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -83,6 +97,7 @@ def main():
     import torch
 
     from sparse_attention_token_dsa_amd import api, synth
+    from sparse_attention_token_dsa_amd import workload as wl
 
     dev = torch.device("cuda:0")
     api.load()
@@ -249,17 +264,40 @@ def main():
         for i, n in enumerate(split):
             split[n] += ev[i].elapsed_time(ev[i + 1]) / nsplit
 
+    # Each selector alone, cache flushed before each call (pools given, as in
+    # the step): the per-selector times behind the ratios and computed rates.
+    sel_calls = {
+        "dsa": lambda: api.indexer_score_topk(q, w, K, off, k, *outs["dsa"], ws=ws_dsa),
+        "misa": lambda: api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
+                                       out_idx=outs["misa"][0], out_score=outs["misa"][1],
+                                       ws=ws_m1),
+        "misa_dagger": lambda: api.misa_route(q, w, K, off, k, B, h, kp, pooled=reps_B,
+                                              want_heads=False, out_idx=outs["misa_dagger"][0],
+                                              out_score=outs["misa_dagger"][1], ws=ws_m2),
+        "hisa": lambda: api.hisa_coarse_fine(q, w, K, off, k, b, r, reps=reps_b,
+                                             want_blocks=False, out_idx=outs["hisa"][0],
+                                             out_score=outs["hisa"][1], ws=ws_hi),
+    }
+    sel_ms, sel_kern = {}, {}
+    for n, fn in sel_calls.items():
+        sel_ms[n], kus = flushed_calls(api, torch, fn, flush, args.steps)
+        sel_kern[n] = {x: round(v, 2) for x, v in kus.items()}
+
     rows = Bt  # one query per sequence
-    logical_pairs = 4 * rows * L     # four selectors, every legal token of each row
+    pairs = wl.legal_pairs(1, off, batch=Bt)   # every legal token of each row
+    logical_pairs = 4 * pairs                  # four selectors
     value = logical_pairs / (ms_step * 1e-3)
     kernels = {n: {"avg_us": 1e3 * t / c, "launches_per_step": c / args.steps}
                for n, (t, c) in sorted(kern.items())}
+    computed = computed_work(rows, L, H, d, B, h, kp, b, r, pairs, sel_ms, ms_step)
 
-    # Roofline of the DSA decode scan: algorithmic bytes per launch over its
-    # average duration right after a cache flush (the warm figure, from the
-    # eager step pass, for context).
-    kbytes = Bt * L * d * 2
-    scan_bytes = kbytes + Bt * H * d * 2 + Bt * H * 4 + Bt * L * 4
+    # Roofline of the DSA decode scan: algorithmic bytes per launch (the keys
+    # once, q and w) over its average duration right after a cache flush (the
+    # warm figure, from the eager step pass, for context).  The score rows
+    # this design stages for its top-k are reported apart.
+    kbytes = wl.key_bytes(Bt, L, d)
+    scan_bytes = wl.scan_bytes(rows, Bt, L, H, d)
+    design_bytes = wl.score_row_bytes(rows, L)
     scan_us = 1e3 * kern_cold["scan_dsa"][0] / kern_cold["scan_dsa"][1]
     scan_gbs = scan_bytes / (scan_us * 1e-6) / 1e9
     scan_us_warm = kernels["scan_dsa"]["avg_us"]
@@ -267,13 +305,16 @@ def main():
     roofline = {"kernel": "scan_dsa", "bound": "hbm", "achieved": round(scan_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("scan_dsa", digest),
-                "algorithmic_bytes_per_launch": scan_bytes, "avg_us": round(scan_us, 2),
+                "algorithmic_bytes_per_launch": scan_bytes,
+                "design_bytes_per_launch": design_bytes,
+                "design_bytes": "fp32 score rows written for the top-k (not in achieved)",
+                "avg_us": round(scan_us, 2),
                 "cache": "cold: a 1 GiB read before each launch",
                 "avg_us_warm": round(scan_us_warm, 2),
                 "achieved_warm": round(scan_bytes / (scan_us_warm * 1e-6) / 1e9, 1)}
     other_hbm = {}
-    for name, nbytes in (("scan_routed", kbytes + Bt * h * d * 2 + Bt * H * 4 + Bt * L * 4),
-                         ("pool2", kbytes + Bt * (L // b + L // B) * 2 * d * 2)):
+    for name, nbytes in (("scan_routed", wl.scan_bytes(rows, Bt, L, h, d)),
+                         ("pool2", wl.pool_bytes(Bt, L, d, L // b + L // B))):
         if name in kernels:
             us = kernels[name]["avg_us"]
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -300,13 +341,27 @@ def main():
         "ms_per_step_warm": ms_step_warm,
         "ms_per_step_eager": ms_eager,
         "selector_ms": {n: round(v, 4) for n, v in split.items()},
-        "selector_scores_per_s": {n: rows * L / (split[n] * 1e-3)
+        "selector_ms_note": "selector_ms: eager step, one call after another, no flush "
+                            "between them",
+        "selector_ms_flushed": sel_ms,
+        "selector_kernels_us_flushed": sel_kern,
+        "selector_scores_per_s": {n: pairs / (sel_ms[n] * 1e-3)
                                   for n in ("dsa", "misa", "misa_dagger", "hisa")},
+        "computed": computed,
         "kernels": kernels,
         "roofline": roofline,
         "hbm_kernels": other_hbm,
     }
 
+    result["decode_32k"] = bench_decode_32k(api, synth, torch, np, dev, flush, args.steps)
+    result["h32"] = bench_h32(api, synth, torch, np, dev, flush, args.steps)
+    result["ratios"] = {
+        "what": "selector time ratios DSA / X on the same inputs, cache flushed before each "
+                "call (pages' context, other hardware: MISA 3.82x, MISA-dagger 1.76x, "
+                "HISA 4x at 128K)",
+        "h64": {n: sel_ms["dsa"] / sel_ms[n] for n in ("misa", "misa_dagger", "hisa")},
+        "h32": {n: result["h32"]["ms_per_call"]["dsa"] / v
+                for n, v in result["h32"]["ms_per_call"].items() if n != "dsa"}}
     result["fp8"] = bench_fp8(api, torch, dev, q, w, K, shape, flush, args.steps)
     result["lisa"], result["resmisa"] = bench_lisa_resmisa(api, torch, dev, q, w, K, shape, flush,
                                                            args.steps)
@@ -319,7 +374,9 @@ def main():
         result["prefill"] = bench_prefill(api, synth, torch, np, dev, args.prefill_iters)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(p, k, B, h, kp, b, r)
+        gpu_sets = {m: o[0].view(Bt, k).cpu().numpy() for m, o in outs.items()}
+        result["cpu_baseline"], result["selection_margins"] = cpu_baseline(p, k, B, h, kp, b, r,
+                                                                          gpu_sets)
 
     print(json.dumps(result))
 
@@ -337,6 +394,92 @@ def settle(fn, torch, dev):
         if n % 16 == 0:
             torch.cuda.synchronize(dev)
     torch.cuda.synchronize(dev)
+
+
+def computed_work(rows, L, H, d, B, h, kp, b, r, pairs, split, ms_step):
+    """(query, key) pairs each selector actually scores, and per-head dot
+    products, per call and per second of the selector alone (split, cache
+    flushed) and of the whole step."""
+    nB, nb = -(-L // B), -(-L // b)
+    sel = {
+        "dsa": (pairs, pairs * H),
+        "misa": (pairs + rows * nB, pairs * h + rows * nB * H),
+        "misa_dagger": (pairs + rows * nB + rows * kp, pairs * h + rows * nB * H + rows * kp * H),
+        "hisa": (rows * nb + rows * r * b, rows * nb * H + rows * r * b * H),
+    }
+    out = {"what": "pairs scored by each selector (any number of heads; MISA counts its "
+                   "router's pooled keys, MISA-dagger its rerank, HISA its block "
+                   "representatives and rescored tokens) and the per-head dot products "
+                   "behind them; per_s uses the selector's own flushed time"}
+    for n, (pc, dots) in sel.items():
+        out[n] = {"pairs": pc, "dots": dots, "pairs_per_s": pc / (split[n] * 1e-3),
+                  "dots_per_s": dots / (split[n] * 1e-3)}
+    out["step_pairs_per_s"] = sum(v[0] for v in sel.values()) / (ms_step * 1e-3)
+    out["step_dots_per_s"] = sum(v[1] for v in sel.values()) / (ms_step * 1e-3)
+    return out
+
+
+def bench_decode_32k(api, synth, torch, np, dev, flush, steps):
+    """The DSA selector on the 32 x 32768 decode batch (64 heads, k = 2048),
+    cache flushed before each call: scan time against the HBM roofline."""
+    from sparse_attention_token_dsa_amd import workload as wl
+    p = synth.make_config("decode_32k")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(p["w"]).to(dev)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
+    Bt, L, H, d, off, k = p["Bt"], p["L"], p["H"], p["d"], p["offset"], 2048
+    shape = api.Shape(Bt, 1, H, d, L, off, k)
+    ws = torch.empty(api.indexer_score_topk_ws(shape), dtype=torch.uint8, device=dev)
+    oi = torch.empty((Bt, 1, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, 1, k), dtype=torch.float32, device=dev)
+    ms, kus = flushed_calls(api, torch, lambda: api.indexer_score_topk(q, w, K, off, k, oi, osc,
+                                                                       ws=ws), flush, steps)
+    nb = wl.scan_bytes(Bt, Bt, L, H, d)
+    gbs = nb / (kus["scan_dsa"] * 1e-6) / 1e9
+    pairs = wl.legal_pairs(1, off, batch=Bt)
+    return {"workload": "decode_32k_b32_h64", "cache": "cold: a 1 GiB read before each call",
+            "ms_per_call": ms, "scores_per_s": pairs / (ms * 1e-3),
+            "topk_rows_per_s": Bt / (ms * 1e-3),
+            "kernels_us": {n: round(v, 2) for n, v in kus.items()},
+            "roofline": {"kernel": "scan_dsa", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": nb,
+                         "design_bytes_per_launch": wl.score_row_bytes(Bt, L),
+                         "avg_us": round(kus["scan_dsa"], 2),
+                         "target": "scan <= 48 us (70 % of 8 TB/s)"}}
+
+
+def bench_h32(api, synth, torch, np, dev, flush, steps):
+    """DSA, MISA (h = 8) and MISA-dagger (k' = 8192) on the 128K batch-8
+    decode with 32 indexer heads (the GLM-5 indexer width), pooled keys given:
+    per-call times after a cache flush."""
+    p = synth.make_config("misa_128k_h32")
+    q = torch.from_numpy(p["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(p["w"]).to(dev)
+    K = torch.from_numpy(p["K"].view(np.int16)).to(dev)
+    Bt, L, H, d, off, k = p["Bt"], p["L"], p["H"], p["d"], p["offset"], 2048
+    B, h, kp = 1024, 8, 8192
+    shape = api.Shape(Bt, 1, H, d, L, off, k)
+    pooled = api.pool_blocks(K, B)
+    ws = torch.empty(max(api.indexer_score_topk_ws(shape), api.misa_route_ws(shape, B, h, kp, True)),
+                     dtype=torch.uint8, device=dev)
+    oi = torch.empty((Bt, 1, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((Bt, 1, k), dtype=torch.float32, device=dev)
+    calls = {
+        "dsa": lambda: api.indexer_score_topk(q, w, K, off, k, oi, osc, ws=ws),
+        "misa": lambda: api.misa_route(q, w, K, off, k, B, h, 0, pooled=pooled, want_heads=False,
+                                       out_idx=oi, out_score=osc, ws=ws),
+        "misa_dagger": lambda: api.misa_route(q, w, K, off, k, B, h, kp, pooled=pooled,
+                                              want_heads=False, out_idx=oi, out_score=osc, ws=ws),
+    }
+    ms, kern = {}, {}
+    for n, fn in calls.items():
+        ms[n], kus = flushed_calls(api, torch, fn, flush, steps)
+        kern[n] = {x: round(v, 2) for x, v in kus.items()}
+    return {"workload": "misa_128k_b8_h32", "cache": "cold: a 1 GiB read before each call",
+            "config": {"B": B, "h": h, "k_prime": kp, "pooled": "given"},
+            "ms_per_call": ms, "kernels_us": kern}
 
 
 def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
@@ -605,7 +748,9 @@ def bench_prefill(api, synth, torch, np, dev, iters):
                          "traffic": measured_traffic(
                              "prefill_fused",
                              source_digest(["prefill.hip", "sa_frag.h", "sa_common.h"])),
-                         "algorithmic_flops_per_launch": flops},
+                         "algorithmic_flops_per_launch": flops,
+                         "counters": measured_mfma(
+                             source_digest(["prefill.hip", "sa_frag.h", "sa_common.h"]))},
             "ragged": bench_prefill_ragged(api, synth, torch, np, dev, iters)}
 
 
@@ -645,28 +790,67 @@ def bench_prefill_ragged(api, synth, torch, np, dev, iters):
             "k": k, **res}
 
 
-def cpu_baseline(p, k, B, h, kp, b, r):
-    """The fp64 CPU oracle on all 8 query rows of the same workload, through the
-    same four selectors (pooling included in its MISA / HISA calls)."""
-    import oracle
+def host_cpu():
+    """CPU model, logical CPUs of the host and the CPUs this process may use."""
+    model = "unknown"
     try:
-        cores = len(os.sched_getaffinity(0))
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, usable
+
+
+def cpu_baseline(p, k, B, h, kp, b, r, gpu_sets):
+    """The fp64 CPU oracle on all 8 query rows of the same workload, through the
+    same four selectors (pooling included in its MISA / HISA calls), one
+    thread per row.  It selects k + 1 per row, so the same run also gives the
+    cutoff margin S_k - S_(k+1) of each row and selector, and how many of the
+    oracle's top-k the GPU exchanged for near-tie positions."""
+    import numpy as np
+
+    import oracle
+    model, ncpu, usable = host_cpu()
     rows = p["Bt"] * p["T"]
-    threads = min(cores, rows)
+    threads = min(usable, rows)
     prob = oracle.Problem(p["q"], p["w"], p["K"], p["offset"])
     t0 = time.perf_counter()
-    oracle.dsa(prob, k, nthreads=threads)
-    oracle.misa(prob, k, B, h, 0, nthreads=threads)
-    oracle.misa(prob, k, B, h, kp, nthreads=threads)
-    oracle.hisa(prob, k, b, r, nthreads=threads)
+    res = {"dsa": oracle.dsa(prob, k + 1, nthreads=threads),
+           "misa": oracle.misa(prob, k + 1, B, h, 0, nthreads=threads),
+           "misa_dagger": oracle.misa(prob, k + 1, B, h, kp, nthreads=threads),
+           "hisa": oracle.hisa(prob, k + 1, b, r, nthreads=threads)}
     dt = time.perf_counter() - t0
     pairs = 4 * rows * p["L"]
-    return {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+    base = {"value": pairs / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
+            "host_cpu_model": model, "host_logical_cpus": ncpu, "usable_cpus": usable,
             "sample": "all %d query rows of the L=%d decode batch through DSA, MISA, "
-                      "MISA-dagger and HISA (fp64 C oracle, one thread per row); %.1f s wall"
-                      % (rows, p["L"], dt)}
+                      "MISA-dagger and HISA (fp64 C oracle, %d threads, one per row); "
+                      "%.1f s wall" % (rows, p["L"], threads, dt)}
+    margins = {}
+    for m, o in res.items():
+        idx, sc = (o[0], o[1]) if isinstance(o, tuple) else (o["idx"], o["score"])
+        rel, diff = [], []
+        for row in range(rows):
+            s_k, s_k1 = sc[row, k - 1], sc[row, k]
+            top = float(np.max(np.abs(sc[row][np.isfinite(sc[row])])))
+            rel.append((s_k - s_k1) / top if np.isfinite(s_k1) and top > 0 else float("inf"))
+            diff.append(len(set(idx[row, :k].tolist()) - set(gpu_sets[m][row].tolist())))
+        margins[m] = {"min_rel_margin": float(np.min(rel)),
+                      "median_rel_margin": float(np.median(rel)),
+                      "rows_margin_below_tol": int(np.sum(np.array(rel) < 2e-3)),
+                      "exchanged_positions": int(np.sum(diff)),
+                      "rows_with_exchanges": int(np.sum(np.array(diff) > 0))}
+    return base, {"what": "oracle cutoff margin (S_k - S_(k+1)) / max|S| per row, and oracle "
+                          "top-k positions the GPU set replaced (near ties; the parity tests "
+                          "bound them), 8 rows per selector",
+                  **margins}
 
 
 if __name__ == "__main__":

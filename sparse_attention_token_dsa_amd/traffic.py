@@ -19,6 +19,19 @@ into a second 256 MiB fp32 tensor: 256 MiB read, 256 MiB written).
 the HBM bytes fetched and written divided by those factors to traffic.json
 (keyed by a digest of the kernel's sources, which bench.py checks before it
 reports the figure).
+
+MFMA utilisation of the fused prefill, one more counter run:
+
+  rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES \
+      SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE \
+      GRBM_GUI_ACTIVE --output-format csv -d OUT/mfma -o p -- \
+      python3 -m sparse_attention_token_dsa_amd.traffic run_prefill
+  python3 -m sparse_attention_token_dsa_amd.traffic summarize_mfma OUT
+
+`summarize_mfma` stores, per prefill launch (median over the launches): the
+raw counters, MFMA-busy cycles per SIMD over the GPU's active cycles, VALU
+instructions per MFMA instruction and LDS bank-conflict cycles over LDS-active
+cycles, under "prefill_fused_mfma" in traffic.json.
 """
 from __future__ import annotations
 
@@ -87,6 +100,57 @@ def run():
     print("traffic run done", flush=True)
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU",
+                 "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4   # compute units x SIMDs
+XCDS = 8
+
+
+def run_prefill(launches=6):
+    """The fused prefill at T = 4096 over 28672 cached keys, k = 2048."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_token_dsa_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    pp = synth.make_config("prefill_chunked")
+    q = torch.from_numpy(pp["q"].view(np.int16)).to(dev)
+    w = torch.from_numpy(pp["w"]).to(dev)
+    K = torch.from_numpy(pp["K"].view(np.int16)).to(dev)
+    oi = torch.empty((1, pp["T"], 2048), dtype=torch.int32, device=dev)
+    for _ in range(launches):
+        api.indexer_score_topk(q, w, K, pp["offset"], 2048, out_idx=oi)
+    torch.cuda.synchronize()
+    print("prefill counter run done", flush=True)
+
+
+def summarize_mfma(out_dir):
+    vals = {c: _per_dispatch(os.path.join(out_dir, "mfma"), c) for c in MFMA_COUNTERS}
+    raw = {c: _pick(v, PREFILL_KERNEL) for c, v in vals.items()}
+    gui = raw["GRBM_GUI_ACTIVE"] / XCDS          # the counter sums the XCDs
+    rec = {
+        "kernel": "prefill_fused",
+        "source_digest": source_digest(PREFILL_SOURCES),
+        "counters_median_per_launch": raw,
+        "active_cycles": gui,
+        "mfma_busy_per_simd": raw["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS,
+        "mfma_busy_frac": raw["SQ_VALU_MFMA_BUSY_CYCLES"] / SIMDS / gui,
+        "valu_per_mfma": raw["SQ_INSTS_VALU"] / raw["SQ_INSTS_MFMA"],
+        "lds_bank_conflict_frac": raw["SQ_LDS_BANK_CONFLICT"] / raw["SQ_LDS_IDX_ACTIVE"],
+    }
+    try:
+        with open(TRAFFIC_FILE) as f:
+            allrec = json.load(f)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec["prefill_fused_mfma"] = rec
+    print(json.dumps(rec, indent=1))
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(allrec, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
 def _per_dispatch(run_dir, counter):
     """{kernel name: [counter value per dispatch]} from one --pmc run."""
     out = {}
@@ -143,6 +207,10 @@ def summarize(out_dir):
 if __name__ == "__main__":
     if len(sys.argv) >= 2 and sys.argv[1] == "run":
         run()
+    elif len(sys.argv) >= 2 and sys.argv[1] == "run_prefill":
+        run_prefill()
+    elif len(sys.argv) >= 3 and sys.argv[1] == "summarize_mfma":
+        summarize_mfma(sys.argv[2])
     elif len(sys.argv) >= 3 and sys.argv[1] == "summarize":
         summarize(sys.argv[2])
     else:
