@@ -276,7 +276,10 @@ int misa_route_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime
  *            output for these keys.
  *   out_heads [batch, T, h] routed heads, ascending (nullable).
  *   out_pool  [batch, T, k_prime] the k' pool, -1 padded (nullable; only for
- *             k_prime > 0). */
+ *             k_prime > 0).
+ * Rows with T >= 16 per sequence (prefill) take the fused prefill kernel on
+ * the routed heads' q rows: no score row is written; decode-style rows write
+ * one O(L) routed score row per query into the workspace. */
 int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
                int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
                int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
@@ -292,8 +295,9 @@ int misa_route_fp8_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_p
  * means in fp32), the routed scan (codes widened exactly to bf16, the scale
  * applied after the head sum) and MISA-dagger's rerank.  q stays bf16.
  * `pooled`, if given, holds the block means of the dequantized keys in the
- * sa_pool_blocks layout.  Other arguments, shapes, ownership and errors as in
- * misa_route. */
+ * sa_pool_blocks layout.  Decode-style rows only: T must be < 16
+ * (SA_EUNSUPPORTED otherwise).  Other arguments, shapes, ownership and errors
+ * as in misa_route. */
 int misa_route_fp8(const uint16_t* q, const float* w, const uint8_t* codes, const float* scales,
                    const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
                    const uint16_t* pooled, int32_t* out_heads, int32_t* out_pool,

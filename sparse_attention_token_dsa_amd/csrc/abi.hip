@@ -243,6 +243,7 @@ hipError_t run_list_topk(const float* ls, const int32_t* li, long long stride,
 // ---------------------------------------------------------------- MISA
 
 struct MisaPlan {
+    bool prefill;
     uint16_t* pooled;
     uint16_t* tail;
     uint8_t* flag;
@@ -250,12 +251,18 @@ struct MisaPlan {
     float* scores;
     uint32_t* state;
     unsigned long long* cand;
+    uint16_t* qp;
+    float* wp;
+    uint2* surv;
     int32_t* pool_idx;
     float* list_score;
     int32_t* list_idx;
     size_t bytes;
 };
 
+// Decode-style rows (T < 16) score the routed heads with the dense scan into
+// O(L) score rows; prefill rows (T >= 16) take the fused prefill on the
+// routed heads' q rows (written by the router), so no rows x L scores exist.
 MisaPlan plan_misa(const sa_shape* s, int B, int h, int kp, bool pooled_given, bool partial,
                    void* ws) {
     MisaPlan p{};
@@ -263,15 +270,22 @@ MisaPlan plan_misa(const sa_shape* s, int B, int h, int kp, bool pooled_given, b
     const long long rows = (long long)s->batch * s->T;
     const long long maxn = (long long)s->causal_offset + s->T;
     const long long nblk = (s->L + B - 1) / B;
+    p.prefill = s->T >= kPrefillMinT;
     if (!pooled_given) p.pooled = cv.take<uint16_t>(s->batch * nblk * 2 * sa::kD);
     if (partial) {
         p.tail = cv.take<uint16_t>(rows * 2 * sa::kD);
         p.flag = cv.take<uint8_t>(rows);
     }
     p.heads = cv.take<int32_t>(rows * h);
-    p.scores = cv.take<float>(rows * score_stride(s->L));
-    p.state = cv.take<uint32_t>(rows * sa::kRowState);
-    p.cand = cv.take<unsigned long long>(rows * maxn);
+    if (p.prefill) {
+        p.qp = cv.take<uint16_t>(rows * h * sa::kD);
+        p.wp = cv.take<float>(rows * h);
+        p.surv = cv.take<uint2>(rows * score_stride((int)maxn));
+    } else {
+        p.scores = cv.take<float>(rows * score_stride(s->L));
+        p.state = cv.take<uint32_t>(rows * sa::kRowState);
+        p.cand = cv.take<unsigned long long>(rows * maxn);
+    }
     if (kp > 0) {
         p.pool_idx = cv.take<int32_t>(rows * kp);
         p.list_score = cv.take<float>(rows * kp);
@@ -939,7 +953,8 @@ static int route_heads(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int block_B, int h, const uint16_t* pooled,
                        uint16_t* pooled_ws, uint16_t* tail, uint8_t* flag, int32_t* heads,
                        hipStream_t st, uint32_t* zero_state = nullptr,
-                       const uint8_t* codes = nullptr, const float* kscale = nullptr) {
+                       const uint8_t* codes = nullptr, const float* kscale = nullptr,
+                       uint16_t* qp = nullptr, float* wp = nullptr) {
     const int rows = s->batch * s->T;
     const int nblk = (s->L + block_B - 1) / block_B;
     hipError_t e;
@@ -970,6 +985,8 @@ static int route_heads(const uint16_t* q, const float* w, const uint16_t* keys,
     ra.heads_out = heads;
     ra.E_out = nullptr;
     ra.zero_state = zero_state;
+    ra.qp = qp;
+    ra.wp = wp;
     e = sa::launch_router(ra, rows, st);
     if (e != hipSuccess) return hip_fail(e, "router");
     return SA_OK;
@@ -1004,18 +1021,42 @@ static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, con
     hipError_t e;
     int32_t* heads = out_heads ? out_heads : p.heads;
     rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
-                     p.flag, heads, st, p.state, codes, kscale);
+                     p.flag, heads, st, p.state, codes, kscale, p.qp, p.wp);
     if (rc) return rc;
+    int32_t* pool_idx = k_prime ? (out_pool ? out_pool : p.pool_idx) : nullptr;
+    if (p.prefill) {
+        // The routed score of every legal key is the DSA score of the h
+        // routed heads: the fused prefill on their q rows keeps the top-k (or
+        // the k' pool) without writing any score row.
+        sa::PrefillArgs pa{};
+        pa.q = p.qp;
+        pa.w = p.wp;
+        pa.keys = keys;
+        pa.T = s->T;
+        pa.H = h;
+        pa.L = s->L;
+        pa.offset = s->causal_offset;
+        pa.k = k_prime ? k_prime : s->topk;
+        pa.surv = p.surv;
+        pa.cap = score_stride(s->causal_offset + s->T);
+        pa.out_idx = k_prime ? pool_idx : out_idx;
+        pa.out_score = k_prime ? nullptr : out_score;
+        pa.out_stride = k_prime ? k_prime : s->topk;
+        e = sa::launch_prefill(pa, rows, st);
+        if (e != hipSuccess) return hip_fail(e, "routed prefill");
+        if (k_prime == 0) return SA_OK;
+    }
     if (k_prime == 0) {
         e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, s->topk,
                            out_idx, out_score, st, codes, kscale, /*state_zeroed=*/true);
         if (e != hipSuccess) return hip_fail(e, "routed scan");
         return SA_OK;
     }
-    int32_t* pool_idx = out_pool ? out_pool : p.pool_idx;
-    e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, k_prime, pool_idx,
-                       nullptr, st, codes, kscale, /*state_zeroed=*/true);
-    if (e != hipSuccess) return hip_fail(e, "routed scan");
+    if (!p.prefill) {
+        e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, k_prime, pool_idx,
+                           nullptr, st, codes, kscale, /*state_zeroed=*/true);
+        if (e != hipSuccess) return hip_fail(e, "routed scan");
+    }
     sa::GatherArgs ga{};
     ga.q = q;
     ga.w = w;
@@ -1055,6 +1096,8 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
 
 int misa_route_fp8_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,
                       int32_t pooled_given, size_t* ws_bytes) {
+    if (s && s->T >= kPrefillMinT)
+        return fail(SA_EUNSUPPORTED, "FP8 keys: MISA takes decode-style rows only (T < 16)");
     return misa_route_ws(s, block_B, h, k_prime, pooled_given, ws_bytes);
 }
 
@@ -1064,6 +1107,8 @@ int misa_route_fp8(const uint16_t* q, const float* w, const uint8_t* codes, cons
                    int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream) {
     int rc = check_misa(s, block_B, h, k_prime);
     if (rc) return rc;
+    if (s->T >= kPrefillMinT)
+        return fail(SA_EUNSUPPORTED, "FP8 keys: MISA takes decode-style rows only (T < 16)");
     if (!q || !w || !codes || !scales || !out_idx)
         return fail(SA_EINVAL, "q, w, codes, scales and out_idx must be non-NULL");
     return run_misa(q, w, nullptr, codes, scales, s, block_B, h, k_prime, pooled, out_heads,

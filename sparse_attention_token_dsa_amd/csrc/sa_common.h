@@ -257,6 +257,10 @@ struct RouterArgs {
     int32_t* heads_out;     // [rows, h]
     float* E_out;           // [rows, H] or null
     uint32_t* zero_state;   // [rows, kRowState] cleared for the routed scan that follows, or null
+    // Routed head rows for the fused prefill, or null: qp [rows, h, 128] =
+    // q of the routed heads (ascending), wp [rows, h] their weights.
+    uint16_t* qp;
+    float* wp;
 };
 
 // LISA / ResMiSA head rows and routing.

@@ -285,6 +285,7 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
             if (c == 0) part[wid][ht * 16 + 4 * g + i] = v;
         }
     __syncthreads();
+    __shared__ int s_heads[kMaxH];
     if (wid == 0) {
         __shared__ float sE[kMaxH];
         const int j = lane;
@@ -306,7 +307,22 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
         const bool sel = j < a.H && rank < a.h;
         const unsigned long long msk = __ballot(sel);
         const int pos = __popcll(msk & ((1ull << lane) - 1ull));
-        if (sel) a.heads_out[(long long)row * a.h + pos] = j;
+        if (sel) {
+            a.heads_out[(long long)row * a.h + pos] = j;
+            s_heads[pos] = j;
+        }
+    }
+    // The routed heads' q rows and weights, for the fused prefill: 16 lanes
+    // per head, 16 bytes each.
+    if (a.qp) {
+        __syncthreads();
+        for (int x = threadIdx.x; x < a.h * 16; x += 256) {
+            const int u = x >> 4, part = x & 15;
+            const int j = s_heads[u];
+            const uint4 v = ldg16(a.q + ((long long)row * a.H + j) * kD + part * 8);
+            *reinterpret_cast<uint4*>(a.qp + ((long long)row * a.h + u) * kD + part * 8) = v;
+            if (part == 0) a.wp[(long long)row * a.h + u] = a.w[(long long)row * a.H + j];
+        }
     }
     // The routed scan that follows adds its histogram into a zeroed row state
     // (one launch fewer on the MISA path).

@@ -260,7 +260,7 @@ def _fp8_case(p):
     (2, 1, 5000, 64, 256, 8, 64, 320),       # MISA-dagger
     (1, 3, 7000, 32, 1024, 8, 100, 0),       # cut last block, H = 32
     (1, 4, 4000, 64, 300, 4, 50, 200),       # block not a power of two
-    (1, 20, 900, 64, 128, 8, 40, 100),       # many rows
+    (1, 15, 900, 64, 128, 8, 40, 100),       # many decode-style rows
 ])
 def test_misa_fp8(api, Bt, T, L, H, B, h, k, kp):
     say("misa fp8 Bt=%d T=%d L=%d H=%d B=%d h=%d k=%d kp=%d" % (Bt, T, L, H, B, h, k, kp))
@@ -272,6 +272,15 @@ def test_misa_fp8(api, Bt, T, L, H, B, h, k, kp):
     torch.cuda.synchronize()
     check_misa(p, k, B, h, kp, _np(idx), _np(sc), _np(heads), None if pool is None else _np(pool),
                rows_of(p), fp8=fp8)
+
+
+def test_misa_fp8_rejects_prefill_rows(api):
+    say("misa fp8 T=16 rejected")
+    p = synth.make_problem(461, Bt=1, T=16, L=300, H=16)
+    q, w, cd, sd, _ = _fp8_case(p)
+    with pytest.raises(api.SaError) as e:
+        api.misa_route_fp8(q, w, cd, sd, p["offset"], 8, 64, 4)
+    assert e.value.code == api.SA_EUNSUPPORTED
 
 
 def test_misa_fp8_all_heads_equals_dsa_fp8(api):

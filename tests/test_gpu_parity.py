@@ -189,7 +189,9 @@ def test_prefill_chunked_rows(api):
     (1, 3, 7000, 32, 1024, 8, 100, 0),     # partial last blocks (causal tail)
     (1, 4, 4000, 64, 300, 4, 50, 200),     # B not a power of two, dagger
     (1, 1, 2100, 64, 512, 64, 32, 0),      # h = H: equals DSA
-    (1, 20, 900, 64, 128, 8, 40, 100),     # T >= 16 rows per sequence
+    (1, 20, 900, 64, 128, 8, 40, 100),     # T >= 16 rows per sequence: the fused prefill
+    (1, 256, 4096, 64, 1024, 8, 256, 1024),  # prefill rows, MISA-dagger
+    (2, 64, 3000, 32, 512, 4, 100, 0),     # prefill rows, H = 32, partial blocks
 ])
 def test_misa(api, Bt, T, L, H, B, h, k, kp):
     say("misa Bt=%d T=%d L=%d H=%d B=%d h=%d k=%d k'=%d" % (Bt, T, L, H, B, h, k, kp))
