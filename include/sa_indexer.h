@@ -88,7 +88,9 @@ int indexer_score_topk_ws(const sa_shape* s, size_t* ws_bytes);
  * keep the top-k (PaperTrace section 1; section 2.2 asks for score, causal
  * mask and top-k fused so that no n^2 score matrix is written).
  * Rows with T >= 16 per sequence take the fused prefill kernel (scores never
- * leave the chip; survivors of a running per-row threshold are kept);
+ * leave the chip; survivors of a running per-row threshold are kept in a
+ * bounded per-row list of min(t + 1, max(6 topk, 8192)) entries, compacted in
+ * place when it fills, so the workspace is O(rows * topk));
  * smaller T take the decode scan, which writes one O(L) score row per query
  * into the workspace. */
 int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,

@@ -121,6 +121,17 @@ int check_ptrs(const void* q, const void* w, const void* k, const void* out_idx)
 // reads in the top-k filter).
 long long score_stride(int L) { return ((long long)L + 63) / 64 * 64; }
 
+// Survivor slots per row of the fused prefill: every legal key when that is
+// fewer, else max(6k, 8192).  About k (1 + ln(n / k)) entries survive a
+// running threshold over n keys in random order (5.2 k at n = 64 k), so
+// typical rows never fill the list; the kernel compacts one that does.  The
+// workspace is O(rows * k), not O(rows * n).
+long long surv_cap(long long maxn, int k) {
+    const long long all = score_stride((int)maxn);
+    const long long bounded = std::max<long long>(6LL * k, 8192);
+    return std::min(all, (bounded + 63) / 64 * 64);
+}
+
 constexpr int kPrefillMinT = 16;
 
 // Rows whose last legal block is cut by the causal bound need a tail rep.
@@ -151,7 +162,7 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
     const long long maxn = (long long)s->causal_offset + s->T;
     p.prefill = s->T >= kPrefillMinT;
     if (p.prefill) {
-        p.surv = cv.take<uint2>(rows * score_stride((int)maxn));
+        p.surv = cv.take<uint2>(rows * surv_cap(maxn, s->topk));
     } else {
         p.scores = cv.take<float>(rows * score_stride(s->L));
         p.state = cv.take<uint32_t>(rows * sa::kRowState);
@@ -280,7 +291,7 @@ MisaPlan plan_misa(const sa_shape* s, int B, int h, int kp, bool pooled_given, b
     if (p.prefill) {
         p.qp = cv.take<uint16_t>(rows * h * sa::kD);
         p.wp = cv.take<float>(rows * h);
-        p.surv = cv.take<uint2>(rows * score_stride((int)maxn));
+        p.surv = cv.take<uint2>(rows * surv_cap(maxn, kp ? kp : s->topk));
     } else {
         p.scores = cv.take<float>(rows * score_stride(s->L));
         p.state = cv.take<uint32_t>(rows * sa::kRowState);
@@ -454,7 +465,7 @@ static hipError_t run_prefill(const uint16_t* q, const float* w, const uint16_t*
     a.offset = s->causal_offset;
     a.k = s->topk;
     a.surv = p.surv;
-    a.cap = score_stride(s->causal_offset + s->T);
+    a.cap = surv_cap((long long)s->causal_offset + s->T, s->topk);
     a.out_idx = out_idx;
     a.out_score = out_score;
     a.out_stride = s->topk;
@@ -854,7 +865,7 @@ static int run_resmisa(const uint16_t* q, const float* w, const uint16_t* keys,
         pa.offset = s->causal_offset;
         pa.k = s->topk;
         pa.surv = p.dsa.surv;
-        pa.cap = score_stride(s->causal_offset + s->T);
+        pa.cap = surv_cap((long long)s->causal_offset + s->T, s->topk);
         pa.out_idx = out_idx;
         pa.out_score = out_score;
         pa.out_stride = s->topk;
@@ -1038,7 +1049,7 @@ static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, con
         pa.offset = s->causal_offset;
         pa.k = k_prime ? k_prime : s->topk;
         pa.surv = p.surv;
-        pa.cap = score_stride(s->causal_offset + s->T);
+        pa.cap = surv_cap((long long)s->causal_offset + s->T, pa.k);
         pa.out_idx = k_prime ? pool_idx : out_idx;
         pa.out_score = k_prime ? nullptr : out_score;
         pa.out_stride = k_prime ? k_prime : s->topk;

@@ -39,7 +39,11 @@
 // for n keys in random order) are appended as (position, score) pairs to the
 // row's survivor list in the workspace; the scores themselves never leave the
 // chip.  The count of bin tau is mirrored in a register, so tau is re-derived
-// from the histogram only when it can move.
+// from the histogram only when it can move.  A list has room for a bounded
+// number of entries (the host gives max(6 k, 8192) per row when a row has
+// more legal keys): a list that fills is compacted in place to the entries in
+// bins >= tau, or, when one bin is too crowded for that, to exactly the row's
+// current top-k (see pf_compact).
 //
 // Finish: after the sweep each wave selects its rows' exact top-k from their
 // survivors: the histogram gives the bin holding the k-th score; one pass over
@@ -384,6 +388,111 @@ __device__ __forceinline__ void pf_finish(uint32_t* h, unsigned long long* cb, c
     }
 }
 
+// Threshold state of one row: list entries, entries in bins >= tau, tau, the
+// count of bin tau, and the score a new key must reach.
+struct PfRow {
+    int cnt, ge, tau, htau;
+    float tau_f;
+};
+
+// Compaction of a full survivor list (the row holds at least k + kPfRoom
+// entries, at least k of them in bins >= tau).  It runs rarely, at the top
+// of a pair of tiles, as passes over the list in position order; the last
+// keeps, in place, the entries whose order key ord(score) is above xo, or
+// equal to xo with position <= pmax, and rebuilds the row histogram:
+//  - normally xo is just below bin tau: the entries in bins >= tau stay (at
+//    least k, so the row's top-k does);
+//  - if that leaves too little room (a crowded bin, e.g. equal scores),
+//    exactly the row's current top-k stays: earlier passes bisect the order
+//    keys of bin tau for its k-th score s (count of entries at or above a
+//    probe), then find pmax, the position of the last entry equal to s that
+//    is still in the top-k (ties go to the lower position, and the list is
+//    in position order).  The threshold then moves just above s: a later key
+//    with score s loses the tie to an earlier one.
+// All passes share one loop over the list.
+constexpr int kPfRoom = 3 * 2 * kPfTile;
+__device__ __forceinline__ PfRow pf_compact(uint2* L, uint32_t* hr, PfRow st, int k,
+                                            long long cap) {
+    const int lane = lane_id();
+    const int n = st.cnt;
+    const bool exact = st.ge + kPfRoom > cap;
+    // bisection bounds on the order key: at least k entries at or above lo,
+    // fewer than k at or above hi (tau is the highest such bin)
+    uint32_t lo = st.tau == 0 ? 0u : pf_lo_ord(st.tau);
+    uint32_t hi = st.tau >= kPfTop ? 0xffffffffu : pf_lo_ord(st.tau + 1);
+    // passes: 0 count at or above the probe, 1 count above s, 2 find pmax,
+    // 3 compact
+    int kind = exact ? (hi - lo > 1u ? 0 : 1) : 3;
+    uint32_t xo = exact ? lo : pf_lo_ord(st.tau) - 1u;
+    int pmax = -1, m = 0;
+#pragma unroll 1
+    for (;;) {
+        const uint32_t probe = kind == 0 ? lo + (hi - lo) / 2u : hi;
+        if (kind == 3)
+            for (int b = lane; b < kPfBins; b += 64) hr[b] = 0u;
+        int c = 0, out = 0;
+        // 256 entries per step, all four loads issued before any is used
+#pragma unroll 1
+        for (int ub = 0; ub < n; ub += 256) {
+            uint2 ev[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ev[j] = L[min(ub + 64 * j + lane, n - 1)];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint2 e = ev[j];
+                const int u = ub + 64 * j + lane;
+                const uint32_t o = ord_key(__uint_as_float(e.y));
+                const bool in = u < n;
+                if (kind <= 1) {
+                    c += __popcll(__ballot(in && o >= probe));
+                } else if (kind == 2) {
+                    const bool eqs = in && o == xo;
+                    const unsigned long long me = __ballot(eqs);
+                    const int ne = __popcll(me);
+                    if (m > 0 && ne >= m) {
+                        const unsigned long long ml = __ballot(eqs && below(me) == m - 1);
+                        pmax = __builtin_amdgcn_readlane((int)e.x, __ffsll((long long)ml) - 1);
+                    }
+                    m -= ne;
+                } else {
+                    // the step's entries are read before any is written; every
+                    // write lands at or below the slot it came from
+                    const bool kept = in && (o > xo || (o == xo && (int)e.x <= pmax));
+                    const unsigned long long mk = __ballot(kept);
+                    if (kept) {
+                        L[out + below(mk)] = e;
+                        lds_add_u32(&hr[pf_bin(__uint_as_float(e.y))], 1u);
+                    }
+                    out += __popcll(mk);
+                }
+            }
+        }
+        if (kind == 0) {
+            if (c >= k) lo = probe; else hi = probe;
+            if (hi - lo <= 1u) kind = 1;
+        } else if (kind == 1) {
+            xo = lo;       // the order key of the k-th score
+            m = k - c;     // entries equal to it that are in the top-k
+            kind = 2;
+        } else if (kind == 2) {
+            kind = 3;
+        } else {
+            st.cnt = out;
+            break;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the compacted list is stored
+    if (exact) {
+        // exactly k entries, all at or above s: tau is the bin of s
+        const float sk = ord_to_f32(xo);
+        st.ge = st.cnt;
+        st.tau = pf_bin(sk);
+        st.htau = __builtin_amdgcn_readfirstlane((int)hr[st.tau]);
+        st.tau_f = fmaxf(pf_lo(st.tau), ord_to_f32(xo + 1u));
+    }
+    return st;
+}
+
 template <int NHT>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     // The stages are four distinct LDS objects: the compiler then tracks the
@@ -724,7 +833,26 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 
     issue(kt0, 0);
     issue(kt1, 1);
+    // Bounded survivor lists: a row whose legal keys outnumber its list slots
+    // (a.cap) has its list compacted, out of line, when fewer than kPfRoom
+    // slots are left (three settles' worth: the check runs once per two
+    // pairs, and the last settle follows the loop).
+    auto maybe_compact = [&](int r) __attribute__((always_inline)) {
+        const bool aq = r ? act[1] : act[0];
+        const int tqr = r ? tq[1] : tq[0];
+        PfRow st{r ? cnt[1] : cnt[0], r ? cnt_ge[1] : cnt_ge[0], r ? tau[1] : tau[0],
+                 r ? htau[1] : htau[0], r ? tau_f[1] : tau_f[0]};
+        if (__builtin_expect(!aq || tqr < a.cap || st.cnt + kPfRoom <= a.cap, 1)) return;
+        st = pf_compact(r ? sl[1] : sl[0], r ? h[1] : h[0], st, a.k, a.cap);
+        if (r) {
+            cnt[1] = st.cnt; cnt_ge[1] = st.ge; tau[1] = st.tau; htau[1] = st.htau; tau_f[1] = st.tau_f;
+        } else {
+            cnt[0] = st.cnt; cnt_ge[0] = st.ge; tau[0] = st.tau; htau[0] = st.htau; tau_f[0] = st.tau_f;
+        }
+    };
     for (int tile = 0; tile < ntiles; tile += 4) {
+#pragma unroll 1
+        for (int r = 0; r < kPfQpw; ++r) maybe_compact(r);
         pair(kt0, kt1, kt2, kt3, tile);
         if (tile + 2 >= ntiles) break;
         pair(kt2, kt3, kt0, kt1, tile + 2);
@@ -763,7 +891,11 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
-    if (a.cap % 2 != 0 || a.cap < (long long)a.offset + a.T) return hipErrorInvalidValue;
+    // Even capacity (16-byte list reads); a list shorter than the longest row
+    // must leave room for the k kept entries and three settles.
+    if (a.cap % 2 != 0) return hipErrorInvalidValue;
+    if (a.cap < (long long)a.offset + a.T && a.cap < (long long)a.k + 3 * 2 * kPfTile)
+        return hipErrorInvalidValue;
     const int batch = rows / a.T;
     const dim3 grid((unsigned)(((a.T + 7) / 8 + 1) / 2), (unsigned)batch);
     const int nht = (a.H + 15) / 16;

@@ -322,7 +322,8 @@ struct PrefillArgs {
     const uint16_t* keys;
     int T, H, L, offset, k;
     uint2* surv;                // [rows, cap] (position, score bits) survivor lists (workspace)
-    long long cap;              // >= offset + T, even
+    long long cap;              // survivor slots per row, even: >= offset + T (every
+                                // legal key), or >= k + 384 (compacted when full)
     int32_t* out_idx;           // [rows, out_stride]
     float* out_score;           // nullable
     long long out_stride;

@@ -147,6 +147,56 @@ def test_dsa_all_equal_keys_take_lowest_positions(api):
         assert sorted(idx[0, i].tolist()) == list(range(50))
 
 
+def _bounded(api, T, L, offset, H, k):
+    # the survivor list of these rows is shorter than their legal keys, so the
+    # kernel compacts it while sweeping
+    shape = api.Shape(1, T, H, 128, L, offset, k)
+    return api.indexer_score_topk_ws(shape) < T * (offset + T) * 8
+
+
+def test_prefill_bounded_lists_ascending_scores(api):
+    # Scores grow with the position (every key survives the running threshold
+    # until the list fills), with runs of exactly equal keys from bf16
+    # rounding: the lists are compacted by the threshold bin and, where a bin
+    # is too crowded, by the exact k-th key.
+    say("prefill bounded lists, ascending scores")
+    T, L, H, k = 16, 20000, 64, 100
+    assert _bounded(api, T, L, L - T, H, k)
+    p = synth.make_problem(61, Bt=1, T=T, L=L, H=H, offset=L - T)
+    p["w"] = np.abs(p["w"])
+    j = int(np.argmax(p["w"][0, 0]))
+    u = synth.bf16_bits_to_f32(p["q"][0, 0, j])
+    c = (0.5 + np.arange(L, dtype=np.float32) / np.float32(L))[:, None]
+    p["K"][0] = synth.to_bf16_bits(c * u[None, :])
+    idx, sc = run_dsa(api, p, k)
+    check_dsa(p, k, idx, sc, rows_of(p))
+
+
+def test_prefill_bounded_lists_all_equal(api):
+    # 20000 equal scores per row: no threshold bin can be dropped, so the
+    # exact compaction keeps positions 0..k-1 and refuses every later key.
+    say("prefill bounded lists, all equal")
+    T, L, H, k = 16, 20000, 64, 50
+    assert _bounded(api, T, L, L - T, H, k)
+    p = synth.make_problem(62, Bt=1, T=T, L=L, H=H, offset=L - T)
+    p["K"][:] = p["K"][0, 0]
+    idx, sc = run_dsa(api, p, k)
+    for i in range(T):
+        assert sorted(idx[0, i].tolist()) == list(range(k))
+
+
+def test_prefill_bounded_lists_negative_scores(api):
+    # Every weight negative: the scores are negative, their k-th in a crowded
+    # one-octave bin.
+    say("prefill bounded lists, negative scores")
+    T, L, H, k = 32, 24000, 64, 64
+    assert _bounded(api, T, L, L - T, H, k)
+    p = synth.make_problem(63, Bt=1, T=T, L=L, H=H, offset=L - T, needles=8, needle_mode="rows")
+    p["w"] = -np.abs(p["w"])
+    idx, sc = run_dsa(api, p, k)
+    check_dsa(p, k, idx, sc, rows_of(p))
+
+
 def test_prefill_tiny_full(api):
     """Causal prefill, T = L = 1024, k = 128: every row against the oracle."""
     say("prefill_tiny full")

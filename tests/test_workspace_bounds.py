@@ -1,0 +1,35 @@
+"""Workspace sizes on the host: the prefill paths keep O(rows * k) survivor
+entries per call, never an O(rows * n) score matrix (PaperTrace, "2.2.2 MISA,
+LISA and ResMiSA", section 2.2: the score matrix is not written back)."""
+import pytest
+
+from sparse_attention_token_dsa_amd import api
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    try:
+        return api.load()
+    except RuntimeError as e:
+        pytest.skip(str(e))
+
+
+@pytest.mark.parametrize("T,L,k", [(4096, 32768, 2048), (16384, 131072, 2048), (1024, 131072, 64)])
+def test_prefill_workspace_is_below_the_score_matrix(T, L, k):
+    s = api.Shape(1, T, 64, 128, L, L - T, k)
+    n2 = T * L * 4  # fp32 scores of every (row, key) pair
+    dsa = api.indexer_score_topk_ws(s)
+    assert dsa < n2 and dsa <= T * max(6 * k, 8192) * 8 + (1 << 20)
+    misa = api.misa_route_ws(s, 1024, 8, 0, True)
+    assert misa < n2
+    # MISA-dagger keeps a pool of k' = 4k per row: O(rows * k') survivors and
+    # pool lists (here k' may reach a quarter of the row)
+    kp = 4 * k
+    dagger = api.misa_route_ws(s, 1024, 8, kp, True)
+    assert dagger <= T * min(L, max(6 * kp, 8192)) * 8 + T * kp * 12 + (1 << 20)
+
+
+def test_short_rows_keep_every_key():
+    # rows with fewer legal keys than the bound: one slot per legal key
+    s = api.Shape(1, 1024, 64, 128, 1024, 0, 128)
+    assert api.indexer_score_topk_ws(s) <= 1024 * 1024 * 8 + (1 << 20)
