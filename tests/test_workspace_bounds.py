@@ -27,7 +27,7 @@ def test_prefill_workspace_is_below_the_score_matrix(T, L, k):
     kp = 4 * k
     dagger = api.misa_route_ws(s, 1024, 8, kp, True)
     heads = T * 8 * (2 * 128 + 4 + 4)   # routed q rows, weights, head ids
-    assert dagger <= T * min(L, max(6 * kp, 8192)) * 8 + T * kp * 12 + heads + (1 << 20)
+    assert dagger <= T * min(L, max(6 * kp, 8192)) * 8 + T * kp * 12 + heads + (2 << 20)
 
 
 def test_short_rows_keep_every_key():
