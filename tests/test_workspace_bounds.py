@@ -26,7 +26,7 @@ def test_prefill_workspace_is_below_the_score_matrix(T, L, k):
     # pool lists (here k' may reach a quarter of the row)
     kp = 4 * k
     dagger = api.misa_route_ws(s, 1024, 8, kp, True)
-    heads = T * 8 * (2 * 128 + 4 + 4)   # routed q rows, weights, head ids
+    heads = T * 8 * (2 * 128 + 4 + 4) + T * (4 * 128 + 1)  # routed q rows, weights, ids; cut-block means
     assert dagger <= T * min(L, max(6 * kp, 8192)) * 8 + T * kp * 12 + heads + (2 << 20)
 
 
