@@ -4,11 +4,12 @@
 Workload (one "step"): one decode batch at L = 131072 -- 8 sequences, one query
 each, H_I = 64 heads, d = 128, bf16 q / keys, fp32 w, k = 2048 -- pushed through
 every selector of the library, with all inputs resident in HBM:
-  1. block pooling of the keys (HISA b = 128 and MISA B = 1024, one pass),
-  2. DSA: score every causal prefix token with all heads, top-k,
-  3. MISA: router over the pooled keys, top-8 heads, routed scan, top-k,
-  4. MISA-dagger: routed top-k' (8192), rerank with all heads, top-k,
-  5. HISA: block scores, top-64 blocks, exact rescoring of their 8192 tokens,
+  1. DSA: score every causal prefix token with all heads, top-k; its key scan
+     also writes the block means of the keys (HISA b = 128 and MISA B =
+     1024), the pooling being done in the same pass over the key cache,
+  2. MISA: router over the pooled keys, top-8 heads, routed scan, top-k,
+  3. MISA-dagger: routed top-k' (8192), rerank with all heads, top-k,
+  4. HISA: block scores, top-64 blocks, exact rescoring of their 8192 tokens,
      top-k.
 value = logical indexer scores per second = (query, legal token) pairs that the
 four selectors rank per step / step time.
@@ -128,47 +129,48 @@ def main():
             if ev is not None:
                 ev[i].record()
         mark(0)
-        api.pool_blocks2(K, b, B, out_small=reps_b, out_large=reps_B)
+        # DSA, pooling the keys it streams into the b and B block means that
+        # MISA and HISA read (one pass over the key cache for both)
+        api.indexer_score_topk_pooled(q, w, K, off, k, b, B, out_small=reps_b, out_large=reps_B,
+                                      out_idx=outs["dsa"][0], out_score=outs["dsa"][1],
+                                      ws=ws_dsa)
         mark(1)
-        api.indexer_score_topk(q, w, K, off, k, *outs["dsa"], ws=ws_dsa)
-        mark(2)
         api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
                        out_idx=outs["misa"][0], out_score=outs["misa"][1], ws=ws_m1)
-        mark(3)
+        mark(2)
         api.misa_route(q, w, K, off, k, B, h, kp, pooled=reps_B, want_heads=False,
                        out_idx=outs["misa_dagger"][0], out_score=outs["misa_dagger"][1],
                        ws=ws_m2)
-        mark(4)
+        mark(3)
         api.hisa_coarse_fine(q, w, K, off, k, b, r, reps=reps_b, want_blocks=False,
                              out_idx=outs["hisa"][0], out_score=outs["hisa"][1], ws=ws_hi)
-        mark(5)
+        mark(4)
 
-    # The same step with the selectors on their own streams (default priority)
-    # after the pooling: the latency-bound top-k, router and gather kernels of
-    # one selector overlap the HBM-bound scans of another.  (Running DSA's scan
-    # beside the pooling instead delays the pools, and with them the longest
-    # chain, MISA-dagger: 0.298 against 0.278 ms per step.)
-    streams = [torch.cuda.Stream(device=dev) for _ in range(4)]
-    pools_done = torch.cuda.Event()
+    # The same step with MISA, MISA-dagger and HISA on their own streams
+    # (default priority), started by an event the pooled DSA scan records as
+    # soon as the block means are written: DSA's top-k kernels and the other
+    # selectors' latency-bound kernels overlap the two routed scans.
+    streams = [torch.cuda.Stream(device=dev) for _ in range(3)]
+    pools_ready = torch.cuda.Event()
+    pools_ready.record()  # created outside any capture
 
     def step_concurrent():
         main = torch.cuda.current_stream(dev)
-        api.pool_blocks2(K, b, B, out_small=reps_b, out_large=reps_B)
+        api.indexer_score_topk_pooled(q, w, K, off, k, b, B, out_small=reps_b, out_large=reps_B,
+                                      out_idx=outs["dsa"][0], out_score=outs["dsa"][1],
+                                      ws=ws_dsa, pools_ready=pools_ready)
         for st_ in streams:
-            st_.wait_stream(main)
+            st_.wait_event(pools_ready)
         # The longest chain (MISA-dagger: router, routed scan, k' select,
-        # rerank, select) is enqueued first so its scan takes the CUs first
-        # (0.273 -> 0.265 ms per step on one box).
-        with torch.cuda.stream(streams[2]):
+        # rerank, select) is enqueued first, so its scan takes the CUs first.
+        with torch.cuda.stream(streams[0]):
             api.misa_route(q, w, K, off, k, B, h, kp, pooled=reps_B, want_heads=False,
                            out_idx=outs["misa_dagger"][0], out_score=outs["misa_dagger"][1],
                            ws=ws_m2)
         with torch.cuda.stream(streams[1]):
             api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
                            out_idx=outs["misa"][0], out_score=outs["misa"][1], ws=ws_m1)
-        with torch.cuda.stream(streams[0]):
-            api.indexer_score_topk(q, w, K, off, k, *outs["dsa"], ws=ws_dsa)
-        with torch.cuda.stream(streams[3]):
+        with torch.cuda.stream(streams[2]):
             api.hisa_coarse_fine(q, w, K, off, k, b, r, reps=reps_b, want_blocks=False,
                                  out_idx=outs["hisa"][0], out_score=outs["hisa"][1], ws=ws_hi)
         for st_ in streams:
@@ -255,8 +257,8 @@ def main():
     api.profile_enable(False)
 
     # Per-selector split (separate pass, torch events between the calls).
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    split = {n: 0.0 for n in ("pool", "dsa", "misa", "misa_dagger", "hisa")}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    split = {n: 0.0 for n in ("dsa_pool", "misa", "misa_dagger", "hisa")}
     nsplit = max(5, args.steps // 5)
     for _ in range(nsplit):
         step(ev)
@@ -268,6 +270,10 @@ def main():
     # the step): the per-selector times behind the ratios and computed rates.
     sel_calls = {
         "dsa": lambda: api.indexer_score_topk(q, w, K, off, k, *outs["dsa"], ws=ws_dsa),
+        "dsa_pool": lambda: api.indexer_score_topk_pooled(q, w, K, off, k, b, B, out_small=reps_b,
+                                                          out_large=reps_B,
+                                                          out_idx=outs["dsa"][0],
+                                                          out_score=outs["dsa"][1], ws=ws_dsa),
         "misa": lambda: api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
                                        out_idx=outs["misa"][0], out_score=outs["misa"][1],
                                        ws=ws_m1),
@@ -278,10 +284,11 @@ def main():
                                              want_blocks=False, out_idx=outs["hisa"][0],
                                              out_score=outs["hisa"][1], ws=ws_hi),
     }
-    sel_ms, sel_kern = {}, {}
+    sel_ms, sel_kern, sel_graph = {}, {}, {}
     for n, fn in sel_calls.items():
         sel_ms[n], kus = flushed_calls(api, torch, fn, flush, args.steps)
         sel_kern[n] = {x: round(v, 2) for x, v in kus.items()}
+        sel_graph[n] = round(flushed_graph_ms(torch, fn, flush, args.steps), 4)
 
     rows = Bt  # one query per sequence
     pairs = wl.legal_pairs(1, off, batch=Bt)   # every legal token of each row
@@ -300,7 +307,8 @@ def main():
     design_bytes = wl.score_row_bytes(rows, L)
     scan_us = 1e3 * kern_cold["scan_dsa"][0] / kern_cold["scan_dsa"][1]
     scan_gbs = scan_bytes / (scan_us * 1e-6) / 1e9
-    scan_us_warm = kernels["scan_dsa"]["avg_us"]
+    # (in the eager step the DSA scan is the pooled one)
+    scan_us_warm = kernels["scan_dsa_pool"]["avg_us"]
     digest = source_digest(["scan.hip", "sa_frag.h", "sa_common.h"])
     roofline = {"kernel": "scan_dsa", "bound": "hbm", "achieved": round(scan_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(scan_gbs / HBM_PEAK_GBS, 4),
@@ -311,10 +319,18 @@ def main():
                 "avg_us": round(scan_us, 2),
                 "cache": "cold: a 1 GiB read before each launch",
                 "avg_us_warm": round(scan_us_warm, 2),
+                "warm_kernel": "scan_dsa_pool (the step's DSA scan, pooling the keys too)",
                 "achieved_warm": round(scan_bytes / (scan_us_warm * 1e-6) / 1e9, 1)}
+    pus = sel_kern["dsa_pool"]["scan_dsa_pool"]
+    roofline["pooled_scan"] = {
+        "kernel": "scan_dsa_pool", "cache": "cold", "avg_us": pus,
+        "algorithmic_bytes_per_launch": scan_bytes + Bt * (L // b + L // B) * 4 * d,
+        "frac": round((scan_bytes + Bt * (L // b + L // B) * 4 * d) / (pus * 1e-6) / 1e9
+                      / HBM_PEAK_GBS, 4)}
     other_hbm = {}
     for name, nbytes in (("scan_routed", wl.scan_bytes(rows, Bt, L, h, d)),
-                         ("pool2", wl.pool_bytes(Bt, L, d, L // b + L // B))):
+                         ("scan_dsa_pool", wl.scan_bytes(rows, Bt, L, H, d)
+                          + Bt * (L // b + L // B) * 4 * d)):
         if name in kernels:
             us = kernels[name]["avg_us"]
             gbs = nbytes / (us * 1e-6) / 1e9
@@ -329,10 +345,12 @@ def main():
         "config": {"workload": "decode_128k_b8_h64", "batch": Bt, "L": L, "H_I": H, "d": d,
                    "topk": k, "misa": {"B": B, "h": h, "k_prime": kp},
                    "hisa": {"b": b, "r": r},
-                   "step": "pool(b=128,B=1024) + DSA + MISA + MISA-dagger + HISA"},
+                   "step": "DSA with pooling (b=128, B=1024) in its key scan + MISA + "
+                           "MISA-dagger + HISA"},
         "topk_rows_per_s": 4 * rows / (ms_step * 1e-3),
-        "timing": "value and ms_per_step: the step replayed as one HIP graph: the pooling, "
-                  "then the four selectors on four streams, each step after a 1 GiB read "
+        "timing": "value and ms_per_step: the step replayed as one HIP graph: the pooled DSA "
+                  "scan, then MISA, MISA-dagger and HISA on three streams beside DSA's "
+                  "top-k, each step after a 1 GiB read "
                   "that evicts the keys from the "
                   "256 MB infinity cache, timed with its own events; ms_per_step_warm: "
                   "back-to-back replays; ms_per_step_eager, the kernel table and "
@@ -344,6 +362,9 @@ def main():
         "selector_ms_note": "selector_ms: eager step, one call after another, no flush "
                             "between them",
         "selector_ms_flushed": sel_ms,
+        "selector_ms_flushed_graph": sel_graph,
+        "selector_ms_flushed_note": "each call alone after a 1 GiB read: eager (the library's "
+                                    "kernel events off), and captured alone into a HIP graph",
         "selector_kernels_us_flushed": sel_kern,
         "selector_scores_per_s": {n: pairs / (sel_ms[n] * 1e-3)
                                   for n in ("dsa", "misa", "misa_dagger", "hisa")},
@@ -579,23 +600,47 @@ def bench_fp8(api, torch, dev, q, w, K, shape, flush, steps):
                           **sel}}
 
 
-def flushed_calls(api, torch, call, flush, steps):
-    """Per-call time (events around each call, after a cache flush) and the
-    library's per-kernel event averages over the same calls."""
-    settle(call, torch, torch.device("cuda:0"))
+def _flushed_ms(torch, call, flush, steps):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    api.profile_enable(True)
     for e0, e1 in evs:
         flush()
         e0.record()
         call()
         e1.record()
     torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
+
+
+def flushed_calls(api, torch, call, flush, steps):
+    """Per-call time (events around each call, after a cache flush; the
+    library's own kernel events off) and, from a second pass with them on,
+    the library's per-kernel averages.  The flush kernel runs long enough for
+    the host to enqueue the whole call behind it, so the call's host-side
+    work is not in the time."""
+    settle(call, torch, torch.device("cuda:0"))
+    ms = _flushed_ms(torch, call, flush, steps)
+    api.profile_enable(True)
+    for _ in range(steps):
+        flush()
+        call()
+    torch.cuda.synchronize()
     kern = api.profile_read()
     api.profile_enable(False)
-    ms = sum(e0.elapsed_time(e1) for e0, e1 in evs) / steps
     return ms, {n: 1e3 * tt / c for n, (tt, c) in kern.items()}
+
+
+def flushed_graph_ms(torch, call, flush, steps):
+    """Per-call time of the call captured alone into a HIP graph, replayed
+    after a cache flush."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(3):
+        flush()
+        g.replay()
+    torch.cuda.synchronize()
+    return _flushed_ms(torch, g.replay, flush, steps)
 
 
 def bench_lisa_resmisa(api, torch, dev, q, w, K, shape, flush, steps):

@@ -97,6 +97,38 @@ int indexer_score_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                        const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- DSA + block pooling */
+
+/* Workspace bytes for indexer_score_topk_pooled (the same as for
+ * indexer_score_topk on this shape). */
+int indexer_score_topk_pooled_ws(const sa_shape* s, int32_t small, int32_t large,
+                                 size_t* ws_bytes);
+
+/* indexer_score_topk for decode rows that also writes the block means of the
+ * keys it streams: the outputs of sa_pool_blocks2(keys, ..., small, large),
+ * the cache-side state MISA ("MISA" summary page, method step 1: blocks of B)
+ * and HISA (PaperTrace section 2.1: blocks of b) score against, without a
+ * second pass over the key cache.
+ *   s          T must be 1 and causal_offset L - 1 (each sequence's one query
+ *              row reads every key), else SA_EUNSUPPORTED.
+ *   small      block of out_small: a power of two >= 128.
+ *   large      block of out_large: a multiple of small that divides 2048
+ *              (SA_EUNSUPPORTED otherwise).
+ *   out_small  [batch, ceil(L/small), 2, d], out_large [batch, ceil(L/large),
+ *              2, d]: per block the fp32 mean as hi = bf16(mean), lo =
+ *              bf16(mean - hi), as sa_pool_blocks (sums in another order:
+ *              equal to its output up to fp32 rounding).
+ *   pools_ready  a hipEvent_t recorded on `stream` as soon as the block means
+ *              are written (before the top-k kernels of the call), so that
+ *              work on other streams can start on them; or NULL.
+ * Selection, outputs, ownership and errors otherwise as in
+ * indexer_score_topk. */
+int indexer_score_topk_pooled(const uint16_t* q, const float* w, const uint16_t* keys,
+                              const sa_shape* s, int32_t small, int32_t large,
+                              uint16_t* out_small, uint16_t* out_large, int32_t* out_idx,
+                              float* out_score, void* ws, size_t ws_bytes, void* pools_ready,
+                              void* stream);
+
 /* ------------------------------------------------ allocation-free DSA */
 
 /* Size of the static device scratch behind indexer_score_topk_noalloc: 32 MiB

@@ -38,7 +38,7 @@ EXPORTS = (
     "indexer_score_topk_ragged_ws", "indexer_score_topk_ragged", "indexer_score_topk_fp8q_ws",
     "indexer_score_topk_fp8q", "misa_route_fp8_ws", "misa_route_fp8", "hisa_coarse_fine_fp8_ws",
     "hisa_coarse_fine_fp8", "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged",
-    "indexer_score_topk_noalloc",
+    "indexer_score_topk_noalloc", "indexer_score_topk_pooled_ws", "indexer_score_topk_pooled",
 )
 
 # Bytes of the static device scratch behind indexer_score_topk_noalloc
@@ -73,6 +73,8 @@ def load():
     lib.indexer_score_topk_ws.argtypes = [SP, ctypes.POINTER(S)]
     lib.indexer_score_topk.argtypes = [P, P, P, SP, P, P, P, S, P]
     lib.indexer_score_topk_noalloc.argtypes = [P, P, P, SP, P, P, P]
+    lib.indexer_score_topk_pooled_ws.argtypes = [SP, I, I, ctypes.POINTER(S)]
+    lib.indexer_score_topk_pooled.argtypes = [P, P, P, SP, I, I, P, P, P, P, P, S, P, P]
     lib.sa_pool_blocks.argtypes = [P, I, I, I, I, P, P]
     lib.sa_pool_blocks2.argtypes = [P, I, I, I, I, I, P, P, P]
     lib.misa_route_ws.argtypes = [SP, I, I, I, I, ctypes.POINTER(S)]
@@ -118,7 +120,8 @@ def load():
                  "indexer_score_topk_fp8q_ws", "indexer_score_topk_fp8q", "misa_route_fp8_ws",
                  "misa_route_fp8", "hisa_coarse_fine_fp8_ws", "hisa_coarse_fine_fp8",
                  "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged",
-                 "indexer_score_topk_noalloc"):
+                 "indexer_score_topk_noalloc", "indexer_score_topk_pooled_ws",
+                 "indexer_score_topk_pooled"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -136,6 +139,17 @@ def _p(t):
 
 def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _event(ev, dev):
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use), or None."""
+    if ev is None:
+        return None
+    if not isinstance(ev, torch.cuda.Event):
+        raise TypeError("pools_ready must be a torch.cuda.Event")
+    if not ev.cuda_event:
+        ev.record(torch.cuda.current_stream(dev))  # creates the event
+    return ctypes.c_void_p(ev.cuda_event)
 
 
 BF16 = (torch.bfloat16, torch.int16, torch.uint16)
@@ -261,6 +275,33 @@ def indexer_score_topk_noalloc(q, w, keys, causal_offset, topk, out_idx, out_sco
                                              _p(out_idx), _p(out_score), _stream(q.device)),
            "indexer_score_topk_noalloc")
     return out_idx, out_score
+
+
+def indexer_score_topk_pooled_ws(shape: Shape, small, large) -> int:
+    return _ws_query(load().indexer_score_topk_pooled_ws, "indexer_score_topk_pooled_ws",
+                     ctypes.byref(shape), int(small), int(large))
+
+
+def indexer_score_topk_pooled(q, w, keys, causal_offset, topk, small, large, out_small=None,
+                              out_large=None, out_idx=None, out_score=None, want_score=True,
+                              ws=None, pools_ready=None):
+    """DSA decode selector that also writes the block means of the keys
+    (sa_pool_blocks2 layout) in the same pass.  pools_ready: a
+    torch.cuda.Event recorded on the current stream once the means are
+    written (before the call's top-k kernels).  Returns (idx, score, small
+    pools, large pools)."""
+    s = _shape(q, w, keys, causal_offset, topk)
+    out_small = _reps_out(keys, small, out_small, "out_small")
+    out_large = _reps_out(keys, large, out_large, "out_large")
+    out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
+    ws = _workspace(indexer_score_topk_pooled_ws(s, small, large), q.device, ws)
+    _gpu(q)
+    _check(load().indexer_score_topk_pooled(_p(q), _p(w), _p(keys), ctypes.byref(s), int(small),
+                                            int(large), _p(out_small), _p(out_large),
+                                            _p(out_idx), _p(out_score), _p(ws), ws.numel(),
+                                            _event(pools_ready, q.device), _stream(q.device)),
+           "indexer_score_topk_pooled")
+    return out_idx, out_score, out_small, out_large
 
 
 def _reps_out(keys, block, out, name):

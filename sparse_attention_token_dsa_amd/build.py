@@ -24,7 +24,10 @@ HIPCC_FLAGS = [
 # VALU: results in VGPRs save one accumulator-to-VGPR move per element.  (The
 # bf16 scan kernels keep the default: there it would cost occupancy.)
 FILE_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "scan8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "scan8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              # the key scans' 64-step loops unroll completely (waits stay
+              # exact), including the one that pools the keys as well
+              "scan.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
 _NOISE = "is not a recognized feature for this target"
 
 

@@ -65,7 +65,7 @@ const char* kKernelNames[sa::K_COUNT] = {
     "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
     "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused",
     "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows", "tidy",
-    "scan_dsa_fp8q"};
+    "scan_dsa_fp8q", "scan_dsa_pool"};
 
 // ------------------------------------------------------------ workspace
 
@@ -181,7 +181,10 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
                           float* out_score, hipStream_t st, const uint8_t* codes = nullptr,
                           const float* kscale = nullptr, bool state_zeroed = false,
                           const int32_t* seq_lens = nullptr, long long total_keys = 0,
-                          bool q_fp8 = false) {
+                          bool q_fp8 = false, uint16_t* pool_small_out = nullptr,
+                          uint16_t* pool_large_out = nullptr, int pool_small = 0,
+                          int pool_large = 0, hipEvent_t after_scan = nullptr,
+                          const uint16_t* route_reps = nullptr, int route_B = 0) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
     hipError_t e;
@@ -214,10 +217,35 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
     a.kscale = kscale;
     a.seq_lens = seq_lens;
     a.q_fp8 = q_fp8 ? 1 : 0;
+    if (route_reps) {
+        // the scan routes each row itself and writes the heads to `heads`
+        a.route_reps = route_reps;
+        a.route_B = route_B;
+        a.route_nblk = (s->L + route_B - 1) / route_B;
+        a.route_seq_stride = (long long)a.route_nblk * 2 * sa::kD;
+        a.route_heads_out = const_cast<int32_t*>(heads);
+    }
     const int nht = ((heads ? hsel : s->H) + 15) / 16;
-    e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
-              : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
+    if (pool_small_out) {
+        // chunks of whole large blocks (pool_large divides kScanPoolChunk)
+        const int c = (a.chunk + pool_large - 1) / pool_large * pool_large;
+        a.chunk = std::min(c, sa::kScanPoolChunk);
+        a.pool_out_small = pool_small_out;
+        a.pool_out_large = pool_large_out;
+        a.pool_small = pool_small;
+        a.pool_large = pool_large;
+        a.pool_shift = 0;
+        while ((64 << a.pool_shift) < pool_small) ++a.pool_shift;
+        e = sa::launch_scan_pooled(a, (int)rows, nht, st);
+    } else {
+        e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
+                  : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
+    }
     if (e != hipSuccess) return e;
+    if (after_scan) {
+        e = hipEventRecord(after_scan, st);
+        if (e != hipSuccess) return e;
+    }
     sa::TopkArgs t{};
     t.dense = scores;
     t.dense_stride = score_stride(s->L);
@@ -571,6 +599,52 @@ int indexer_score_topk_noalloc(const uint16_t* q, const float* w, const uint16_t
                            out_idx, out_score, st);
         if (e != hipSuccess) return hip_fail(e, "decode scan");
     }
+    return SA_OK;
+}
+
+// ------------------------------------------------- DSA + block pooling
+
+static int check_pooled(const sa_shape* s, int small, int large) {
+    int rc = check_shape(s);
+    if (rc) return rc;
+    if (s->T != 1 || s->causal_offset != s->L - 1)
+        return fail(SA_EUNSUPPORTED, "pooled DSA: decode rows only (T = 1, causal_offset = L - 1)");
+    if (small < 128 || (small & (small - 1)) != 0 || large < small || large % small != 0)
+        return fail(SA_EINVAL, "pooled DSA: need small a power of two >= 128 and large a "
+                               "multiple of small");
+    if (large > sa::kScanPoolChunk || sa::kScanPoolChunk % large != 0)
+        return fail(SA_EUNSUPPORTED, "pooled DSA: large must divide 2048");
+    return check_grid_rows(s);
+}
+
+int indexer_score_topk_pooled_ws(const sa_shape* s, int32_t small, int32_t large,
+                                 size_t* ws_bytes) {
+    int rc = check_pooled(s, small, large);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_dsa(s, nullptr).bytes;
+    return SA_OK;
+}
+
+int indexer_score_topk_pooled(const uint16_t* q, const float* w, const uint16_t* keys,
+                              const sa_shape* s, int32_t small, int32_t large,
+                              uint16_t* out_small, uint16_t* out_large, int32_t* out_idx,
+                              float* out_score, void* ws, size_t ws_bytes, void* pools_ready,
+                              void* stream) {
+    int rc = check_pooled(s, small, large);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    if (!out_small || !out_large) return fail(SA_EINVAL, "out_small and out_large must be non-NULL");
+    const size_t need = plan_dsa(s, nullptr).bytes;
+    if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
+    void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
+    DsaPlan p = plan_dsa(s, base);
+    hipError_t e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand, s->topk,
+                                  out_idx, out_score, static_cast<hipStream_t>(stream), nullptr,
+                                  nullptr, false, nullptr, 0, false, out_small, out_large, small,
+                                  large, static_cast<hipEvent_t>(pools_ready));
+    if (e != hipSuccess) return hip_fail(e, "pooled decode scan");
     return SA_OK;
 }
 
@@ -1031,10 +1105,29 @@ static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, con
     const int rows = s->batch * s->T;
     hipError_t e;
     int32_t* heads = out_heads ? out_heads : p.heads;
-    rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
-                     p.flag, heads, st, p.state, codes, kscale, p.qp, p.wp);
-    if (rc) return rc;
     int32_t* pool_idx = k_prime ? (out_pool ? out_pool : p.pool_idx) : nullptr;
+    if (!p.prefill && !codes && !partial) {
+        // Decode rows on bf16 keys, no block cut by the causal bound: the
+        // routed scan routes each row itself (no router launch).
+        const uint16_t* reps = pooled;
+        if (!reps) {
+            e = sa::launch_pool(keys, s->batch, s->L, block_B, p.pooled, st);
+            if (e != hipSuccess) return hip_fail(e, "pool");
+            reps = p.pooled;
+        }
+        const int kk = k_prime ? k_prime : s->topk;
+        e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, kk,
+                           k_prime ? pool_idx : out_idx, k_prime ? nullptr : out_score, st,
+                           nullptr, nullptr, /*state_zeroed=*/false, nullptr, 0, false, nullptr,
+                           nullptr, 0, 0, nullptr, reps, block_B);
+        if (e != hipSuccess) return hip_fail(e, "routed scan");
+        if (k_prime == 0) return SA_OK;
+    } else {
+        rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
+                         p.flag, heads, st, p.state, codes, kscale, p.qp, p.wp);
+        if (rc) return rc;
+    }
+    const bool routed_inline = !p.prefill && !codes && !partial;
     if (p.prefill) {
         // The routed score of every legal key is the DSA score of the h
         // routed heads: the fused prefill on their q rows keeps the top-k (or
@@ -1063,7 +1156,7 @@ static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, con
         if (e != hipSuccess) return hip_fail(e, "routed scan");
         return SA_OK;
     }
-    if (!p.prefill) {
+    if (!p.prefill && !routed_inline) {
         e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, k_prime, pool_idx,
                            nullptr, st, codes, kscale, /*state_zeroed=*/true);
         if (e != hipSuccess) return hip_fail(e, "routed scan");

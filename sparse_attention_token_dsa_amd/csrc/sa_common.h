@@ -16,6 +16,7 @@ constexpr int kMaxH = 64;        // heads supported
 constexpr int kHist0Bits = 12;   // first radix digit = top 12 bits of the ordered score
 constexpr int kHist0Bins = 1 << kHist0Bits;
 constexpr int kScanMaxChunk = 4096;  // keys per scan workgroup (LDS score staging)
+constexpr int kScanPoolChunk = 2048; // keys per workgroup of the scan that also pools
 constexpr int kGatherGroups = 4;     // 16-candidate groups per gather wave
 constexpr int kGatherChunk = 4 * 16 * kGatherGroups;
 // Per-row state of the dense top-k, zeroed before each scan: the first-digit
@@ -170,6 +171,7 @@ enum KernelId {
     K_HEAD_ROWS,
     K_TIDY,
     K_SCAN8Q,
+    K_SCAN_POOL,
     K_COUNT
 };
 
@@ -226,6 +228,26 @@ struct ScanArgs {
     // FP8 keys only: the query converted to E4M3 as well (per-head scale
     // folded into the weight) and the contraction on the fp8 MFMA.
     int q_fp8;
+    // Block means of the streamed keys (decode rows that read every key of
+    // their sequence once): [batch, ceil(L / pool_small), 2, 128] and the same
+    // for pool_large, hi/lo bf16 like sa_pool_blocks.  pool_small is a power
+    // of two >= 128, pool_large a multiple of it; the chunk is a multiple of
+    // pool_large.  Null: no pooling.
+    uint16_t* pool_out_small;
+    uint16_t* pool_out_large;
+    int pool_small, pool_large;
+    int pool_shift;         // log2(pool_small / 64): workgroup steps per small block
+    // Routed key scans (decode rows) that route their row themselves: every
+    // workgroup of the row runs the MISA router on the row's pooled blocks
+    // (route_reps: [batch, route_nblk, 256] hi/lo, route_seq_stride elements
+    // apart; blocks of route_B keys, none cut by the causal bound) before its
+    // keys, and the row's first workgroup writes the hsel routed heads,
+    // ascending, to route_heads_out [rows, hsel].  Null route_reps: the heads
+    // come from `heads`.
+    const uint16_t* route_reps;
+    long long route_seq_stride;
+    int route_B, route_nblk;
+    int32_t* route_heads_out;
 };
 
 struct GatherArgs {
@@ -336,6 +358,9 @@ struct PrefillArgs {
 hipError_t launch_fill_u32(uint32_t* p, long long n, uint32_t v, hipStream_t s);
 hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool routed,
                        hipStream_t s);
+// The DSA decode scan (keys, every row's whole history) that also writes the
+// block means of the keys it streams (a.pool_out_small / a.pool_out_large).
+hipError_t launch_scan_pooled(const ScanArgs& a, int rows, int nht, hipStream_t s);
 // Keys per scan workgroup for 4 (keys) or 8 (block reps) k-steps, rows x maxn keys.
 int scan_chunk(int ksteps, long long rows, int maxn);
 // FP8 key scan (DSA decode rows): scores of codes/kscale keys, chunk from scan8_chunk.

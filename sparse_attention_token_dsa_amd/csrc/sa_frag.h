@@ -67,6 +67,32 @@ __device__ __forceinline__ void load_qfrag(QFrag<NHT>& f, const uint16_t* qrow,
     }
 }
 
+// Workgroup barrier that orders LDS only: the waits before it cover LDS
+// operations, so global loads in flight stay in flight (a plain
+// __syncthreads() also waits for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Sum of a value over the 16 lanes of its row (lanes 16g .. 16g+15): four
+// DPP row rotations (8, 4, 2, 1) on the VALU, no LDS round trips.  Every
+// lane of the row ends with the row's sum (the rounding order depends on the
+// lane; callers read one fixed lane).
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xf, 0xf,
+                                                      false));
+}
+__device__ __forceinline__ float sum_row16(float v) {
+    v += row_ror<8>(v);
+    v += row_ror<4>(v);
+    v += row_ror<2>(v);
+    v += row_ror<1>(v);
+    return v;
+}
+
 // Sum of a value over the four 16-lane groups (lanes l, l^16, l^32, l^48),
 // returned in every lane: two gfx950 row swaps, no LDS traffic.
 __device__ __forceinline__ float sum_lane_groups(float v) {

@@ -12,6 +12,156 @@
 
 namespace sa {
 
+// MISA router for one query row (summary page "MISA", method steps 2-3):
+// E_j = |w_j| * mean_m ReLU(q_j . pooled_m) over the blocks that intersect
+// [0, t], then the h largest E (ties -> lower head).  A workgroup of 4 waves
+// computes it: each wave takes two groups of 16 blocks per pass on the MFMA
+// (all heads as M; both groups' loads in flight together), the ReLU sums meet
+// in LDS, and wave 0 ranks the heads.  On return (after a barrier) s_heads[0..h)
+// holds the routed heads in ascending order in every thread's view, and
+// s_w[0..H) the head weights; E_out (nullable) gets the row's E.  With s_q
+// (LDS, [kMaxH][16] uint4) the row's q is left there too: head j's 16-byte
+// chunk x at s_q[j * 16 + x].
+struct RouteIn {
+    const uint16_t* q;      // the row's [H, 128]
+    const float* w;         // the row's [H]
+    const uint16_t* reps;   // the row's sequence [nblk, 256] hi/lo
+    const uint16_t* tailp;  // mean of a cut last block [256], or null
+    int H, Mt, h;
+    float* E_out;           // the row's [H], or null
+};
+
+// The router's register operands: the row's q fragments (all heads) and the
+// first pass of representatives (two groups of 16 blocks per wave).
+template <int NHT>
+struct RouteRegs {
+    QFrag<NHT> f;
+    uint4 kb[2][8];
+    bool valid[2];
+};
+
+template <int NHT>
+__device__ __forceinline__ void route_load_reps(const RouteIn& r, int base, RouteRegs<NHT>& R,
+                                                int g, int c) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int m = base + 64 * u + c;
+        R.valid[u] = m < r.Mt;
+        const int ml = R.valid[u] ? m : r.Mt - 1;
+        const uint16_t* kp = (r.tailp && ml == r.Mt - 1) ? r.tailp : r.reps + (long long)ml * 256;
+        load_key<8>(R.kb[u], kp, g);
+    }
+}
+
+// Issue the router's first loads (q, w and the first pass of blocks); the
+// caller may issue other loads before route_finish consumes these.
+template <int NHT>
+__device__ __forceinline__ void route_issue(const RouteIn& r, RouteRegs<NHT>& R) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    load_qfrag<NHT>(R.f, r.q, r.w, r.H, nullptr, 0, g, c);
+    route_load_reps(r, wid * 16, R, g, c);
+}
+
+// The workgroup barriers here order LDS only: global loads the caller has in
+// flight stay in flight.
+template <int NHT>
+__device__ __forceinline__ void route_finish(const RouteIn& r, RouteRegs<NHT>& R, int* s_heads,
+                                             float* s_w, uint4* s_q = nullptr) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    float sum[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[ht][i] = 0.f;
+    for (int base = wid * 16;;) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 acc[NHT];
+            group_dots<NHT, 8>(R.f, R.kb[u], acc);
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sum[ht][i] += R.valid[u] ? fmaxf(acc[ht][i], 0.f) : 0.f;
+        }
+        base += 128;
+        if (base >= r.Mt) break;
+        route_load_reps(r, base, R, g, c);
+    }
+    __shared__ float part[4][kMaxH];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = sum_row16(sum[ht][i]);
+            if (c == 0) {
+                part[wid][ht * 16 + 4 * g + i] = v;
+                if (wid == 0) s_w[ht * 16 + 4 * g + i] = R.f.wv[ht][i];
+            }
+        }
+    if (s_q && wid == 0) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) s_q[(ht * 16 + c) * 16 + kk * 4 + g] = R.f.a[ht][kk];
+    }
+    lds_barrier();
+    if (wid == 0) {
+        __shared__ float sE[kMaxH];
+        const int j = lane;
+        float E = -1.f;  // absent heads rank below every real head (E >= 0)
+        if (j < r.H) {
+            const float S = part[0][j] + part[1][j] + part[2][j] + part[3][j];
+            E = fabsf(s_w[j]) * S / (float)r.Mt;
+            if (r.E_out) r.E_out[j] = E;
+        }
+        sE[j] = E;  // same wave writes then reads: LDS keeps the order
+        int rank = 0;
+#pragma unroll
+        for (int j4 = 0; j4 < kMaxH; j4 += 4) {
+            const float4 e4 = *reinterpret_cast<const float4*>(&sE[j4]);
+            const float es[4] = {e4.x, e4.y, e4.z, e4.w};
+            // branch-free: (larger E) or (equal E and lower head)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                rank += (int)(es[u] > E) + (int)((es[u] == E) & (j4 + u < j));
+        }
+        const bool sel = j < r.H && rank < r.h;
+        const unsigned long long msk = __ballot(sel);
+        const int pos = __popcll(msk & ((1ull << lane) - 1ull));
+        if (sel) s_heads[pos] = j;
+    }
+    lds_barrier();
+}
+
+template <int NHT>
+__device__ __forceinline__ void route_wg(const RouteIn& r, int* s_heads, float* s_w) {
+    RouteRegs<NHT> R;
+    route_issue<NHT>(r, R);
+    route_finish<NHT>(r, R, s_heads, s_w);
+}
+
+// The routed heads' q fragments (tile rows = s_heads[0..hsel), padded with
+// zero rows) from the copies route_wg left in LDS.
+template <int NHT>
+__device__ __forceinline__ void routed_qfrag_lds(QFrag<NHT>& f, const uint4* s_q,
+                                                 const float* s_w, const int* s_heads, int hsel,
+                                                 int g, int c) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        const int u = ht * 16 + c;
+        const int v = u < hsel ? s_heads[u] : -1;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            f.a[ht][kk] = v >= 0 ? s_q[v * 16 + kk * 4 + g] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int u2 = ht * 16 + 4 * g + i;
+            f.wv[ht][i] = u2 < hsel ? s_w[s_heads[u2]] : 0.f;
+        }
+    }
+}
+
 // ------------------------------------------------------------ scan
 
 // One workgroup = 4 waves scans keys [cs, ce) of one query row (ce - cs <=
@@ -27,7 +177,14 @@ namespace sa {
 template <int KS>
 constexpr int scan_waves() { return 4; }
 
-template <int NHT, int KSTEPS, int G, int NBUF, int NSTEP, bool HIST, bool ROUTED>
+// With POOL (keys, one decode row per sequence reading all of its keys), the
+// workgroup also sums the keys it streams into block means: each lane adds
+// the 8 dims it loaded of its 4 keys per step; at the end of every small
+// block the four lanes holding the same dims are summed (lane-group swaps)
+// into a per-wave LDS slot, and after the sweep the four waves' slots are
+// added in a fixed order into the small and large block means (hi/lo bf16).
+template <int NHT, int KSTEPS, int G, int NBUF, int NSTEP, bool HIST, bool ROUTED,
+          bool POOL = false>
 __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArgs a) {
     constexpr int NW = scan_waves<KSTEPS>();
     constexpr int NT = 64 * NW;
@@ -44,7 +201,10 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
     const int ce = min(cs + a.chunk, n);
 
     __shared__ uint32_t lhist[HIST ? kHist0Bins : 1];
-    __shared__ float sbuf[kScanMaxChunk];
+    // The pooling scan runs two workgroups per CU on half-size chunks (its
+    // extra arithmetic needs the second workgroup's waves to hide latency).
+    constexpr int kMaxChunk = POOL ? kScanPoolChunk : kScanMaxChunk;
+    __shared__ float sbuf[kMaxChunk];
     if (HIST) {
         for (int x = threadIdx.x; x < kHist0Bins; x += NT) lhist[x] = 0u;
         __syncthreads();
@@ -52,10 +212,15 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
 
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int32_t* heads = ROUTED ? a.heads + (long long)row * a.hsel : nullptr;
     QFrag<NHT> f;
-    load_qfrag<NHT, ROUTED>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
-                            heads, a.hsel, g, c);
+    // POOL: per-wave partial sums of each small block of the chunk
+    constexpr int kPoolSlots = kMaxChunk / 128;
+    __shared__ float pbuf[POOL ? NW : 1][POOL ? kPoolSlots : 1][POOL ? kD : 1];
+    float pacc[POOL ? 8 : 1];
+#pragma unroll
+    for (int e = 0; e < (POOL ? 8 : 1); ++e) pacc[e] = 0.f;
+    const int psteps = POOL ? a.pool_small / STEP : 1;  // workgroup steps per small block
+    const int nsteps_all = (ce - cs + STEP - 1) / STEP;
 
     const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
     const uint16_t* tailp =
@@ -90,7 +255,50 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
             }
         }
     };
-    auto computeG = [&](const uint4 (&buf)[G][KSTEPS], int base) {
+    auto computeG = [&](const uint4 (&buf)[G][KSTEPS], int base, int it) {
+        if constexpr (POOL) {
+            // This lane's dims 8c' .. 8c'+7 (c' = lane & 15) of keys
+            // base + 4j + (lane >> 4), two keys at a time: the same dim of
+            // keys j and j + 1 packed into one bf16 pair (a byte permute) and
+            // summed into the dim's fp32 accumulator by one dot product with
+            // (1, 1) -- or 0 for a key past the chunk (a re-read).
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const int k0 = base + (lane >> 4);
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                const uint32_t mw = (k0 + 4 * j < ce ? 0x3F80u : 0u) |
+                                    (k0 + 4 * j + 4 < ce ? 0x3F800000u : 0u);
+                const bf16x2_t m = __builtin_bit_cast(bf16x2_t, mw);
+                const uint32_t w0[4] = {buf[0][j].x, buf[0][j].y, buf[0][j].z, buf[0][j].w};
+                const uint32_t w1[4] = {buf[0][j + 1].x, buf[0][j + 1].y, buf[0][j + 1].z,
+                                        buf[0][j + 1].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t lo = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);
+                    const uint32_t hi = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);
+                    pacc[2 * e] = __builtin_amdgcn_fdot2_f32_bf16(
+                        __builtin_bit_cast(bf16x2_t, lo), m, pacc[2 * e], false);
+                    pacc[2 * e + 1] = __builtin_amdgcn_fdot2_f32_bf16(
+                        __builtin_bit_cast(bf16x2_t, hi), m, pacc[2 * e + 1], false);
+                }
+            }
+            // end of a small block (a power-of-two number of steps) or of the
+            // chunk: the four lanes holding the same dims are summed into this
+            // wave's slot of the block
+            if (it < nsteps_all && ((it & (psteps - 1)) == psteps - 1 || it + 1 == nsteps_all)) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[e] = sum_lane_groups(pacc[e]);
+                    pacc[e] = 0.f;
+                }
+                if (g == 0) {
+                    float4* dst = reinterpret_cast<float4*>(&pbuf[wid][it >> a.pool_shift][8 * c]);
+                    dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+                    dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+                }
+            }
+        }
 #pragma unroll
         for (int gi = 0; gi < G; ++gi) {
             const int s = base + gi * 16 + c;
@@ -123,14 +331,52 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
     // stored); otherwise steps past the end (at most NBUF - 1) are skipped.
     const int base = cs + wid * WKEYS;
     uint4 buf[NBUF][G][KSTEPS];
+    const int32_t* heads = ROUTED ? a.heads + (long long)row * a.hsel : nullptr;
+    // MISA routing inside the scan: every workgroup of the row computes the
+    // same heads (same inputs, same arithmetic), so the router costs no launch
+    // of its own.  Its loads go first, the first key loads behind them, and
+    // its barriers order LDS only, so the keys stay in flight while it runs.
+    constexpr bool kRoute = ROUTED && KSTEPS == 4;
+    __shared__ int s_rheads[kRoute ? kMaxH : 1];
+    __shared__ float s_rw[kRoute ? kMaxH : 1];
+    __shared__ uint4 s_rq[kRoute ? kMaxH * 16 : 1];
+    RouteIn rin;
+    RouteRegs<kRoute ? 4 : 1> rregs;
+    const bool route = kRoute && a.route_reps;
+    if constexpr (kRoute) {
+        if (route) {
+            rin.q = a.q + (long long)row * a.H * kD;
+            rin.w = a.w + (long long)row * a.H;
+            rin.reps = a.route_reps + (long long)b * a.route_seq_stride;
+            rin.tailp = nullptr;
+            rin.H = a.H;
+            rin.Mt = min(t / a.route_B + 1, a.route_nblk);
+            rin.h = a.hsel;
+            rin.E_out = nullptr;
+            route_issue(rin, rregs);
+        }
+    }
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u) loadG(buf[u], base + u * STEP);
+    if constexpr (kRoute) {
+        if (route) {
+            route_finish(rin, rregs, s_rheads, s_rw, s_rq);
+            if (blockIdx.x == 0 && a.route_heads_out)
+                for (int u = threadIdx.x; u < a.hsel; u += NT)
+                    a.route_heads_out[(long long)row * a.hsel + u] = s_rheads[u];
+            routed_qfrag_lds<NHT>(f, s_rq, s_rw, s_rheads, a.hsel, g, c);
+            heads = nullptr;
+        }
+    }
+    if (!ROUTED || heads)
+        load_qfrag<NHT, ROUTED>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H,
+                                a.H, heads, a.hsel, g, c);
     if constexpr (NSTEP > 0) {
 #pragma unroll
         for (int it = 0; it < NSTEP; ++it) {
             if (it + NBUF - 1 < NSTEP)
                 loadG(buf[(it + NBUF - 1) % NBUF], base + (it + NBUF - 1) * STEP);
-            computeG(buf[it % NBUF], base + it * STEP);
+            computeG(buf[it % NBUF], base + it * STEP, it);
         }
     } else {
         const int nsteps = (ce - cs + STEP - 1) / STEP;
@@ -139,13 +385,47 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
 #pragma unroll
             for (int u = 0; u < NBUF; ++u) {
                 loadG(buf[(u + NBUF - 1) % NBUF], base + (it0 + u + NBUF - 1) * STEP);
-                if (it0 + u < nsteps) computeG(buf[u], base + (it0 + u) * STEP);
+                if (it0 + u < nsteps) computeG(buf[u], base + (it0 + u) * STEP, it0 + u);
             }
         }
     }
     __syncthreads();
     float* srow = a.scores + (long long)row * a.score_stride;
     for (int x = threadIdx.x; x < ce - cs; x += NT) srow[cs + x] = sbuf[x];
+    if constexpr (POOL) {
+        // Block means of this chunk (cs is a multiple of the large block): the
+        // four waves' partials in a fixed order, so every call rounds alike.
+        const int sb = a.pool_small, lb = a.pool_large;
+        const int nsb = (ce - cs + sb - 1) / sb, per = lb / sb;
+        const int nsmall = (a.len_cap + sb - 1) / sb, nlarge = (a.len_cap + lb - 1) / lb;
+        auto blk_sum = [&](int k, int d) {
+            return ((pbuf[0][k][d] + pbuf[1][k][d]) + pbuf[2][k][d]) + pbuf[3][k][d];
+        };
+        for (int x = threadIdx.x; x < nsb * kD; x += NT) {
+            const int k = x >> 7, d = x & (kD - 1);
+            const int lo = cs + k * sb;
+            const float mean = blk_sum(k, d) / (float)(min(lo + sb, ce) - lo);
+            uint16_t* o = a.pool_out_small + ((long long)b * nsmall + lo / sb) * 2 * kD;
+            const uint32_t hi = f32_to_bf16_bits(mean);
+            o[d] = (uint16_t)hi;
+            o[kD + d] = (uint16_t)f32_to_bf16_bits(mean - bf16_bits_to_f32(hi));
+        }
+        const int nlb = (ce - cs + lb - 1) / lb;
+        for (int x = threadIdx.x; x < nlb * kD; x += NT) {
+            const int m = x >> 7, d = x & (kD - 1);
+            const int lo = cs + m * lb;
+            float S = 0.f;
+            for (int i = 0; i < per; ++i) {
+                const int k = m * per + i;
+                if (k < nsb) S += blk_sum(k, d);
+            }
+            const float mean = S / (float)(min(lo + lb, ce) - lo);
+            uint16_t* o = a.pool_out_large + ((long long)b * nlarge + lo / lb) * 2 * kD;
+            const uint32_t hi = f32_to_bf16_bits(mean);
+            o[d] = (uint16_t)hi;
+            o[kD + d] = (uint16_t)f32_to_bf16_bits(mean - bf16_bits_to_f32(hi));
+        }
+    }
     if (HIST) {
         uint32_t* grow = a.state + (long long)row * kRowState;
         for (int x = threadIdx.x; x < kHist0Bins; x += NT) {
@@ -236,86 +516,27 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 
 // ----------------------------------------------------------- router
 
-// MISA router for one query row (summary page "MISA", method steps 2-3):
-// E_j = |w_j| * mean_m ReLU(q_j . pooled_m) over the blocks that intersect
-// [0, t], then the h largest E (ties -> lower head), written ascending.
 template <int NHT>
 __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
     const int row = blockIdx.x;
     const int b = row / a.T;
     const int t = a.offset + (row - b * a.T);
-    const int Mt = min(t / a.B + 1, a.nblk);
-    const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    QFrag<NHT> f;
-    load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
-                    nullptr, 0, g, c);
-    const uint16_t* kseq = a.reps + (long long)b * a.seq_stride;
-    const uint16_t* tailp = (a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
-
-    float sum[NHT][4];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sum[ht][i] = 0.f;
-
-    for (int base = wid * 16; base < Mt; base += 64) {
-        const int m = base + c;
-        const bool valid = m < Mt;
-        const int ml = valid ? m : Mt - 1;
-        const uint16_t* kp = (tailp && ml == Mt - 1) ? tailp : kseq + (long long)ml * 256;
-        uint4 kb[8];
-        load_key<8>(kb, kp, g);
-        f32x4 acc[NHT];
-        group_dots<NHT, 8>(f, kb, acc);
-#pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sum[ht][i] += valid ? fmaxf(acc[ht][i], 0.f) : 0.f;
-    }
-    __shared__ float part[4][kMaxH];
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v = sum[ht][i];
-            v += __shfl_xor(v, 1);
-            v += __shfl_xor(v, 2);
-            v += __shfl_xor(v, 4);
-            v += __shfl_xor(v, 8);
-            if (c == 0) part[wid][ht * 16 + 4 * g + i] = v;
-        }
-    __syncthreads();
     __shared__ int s_heads[kMaxH];
-    if (wid == 0) {
-        __shared__ float sE[kMaxH];
-        const int j = lane;
-        float E = -1.f;  // absent heads rank below every real head (E >= 0)
-        if (j < a.H) {
-            const float S = part[0][j] + part[1][j] + part[2][j] + part[3][j];
-            E = fabsf(a.w[(long long)row * a.H + j]) * S / (float)Mt;
-            if (a.E_out) a.E_out[(long long)row * a.H + j] = E;
-        }
-        sE[j] = E;  // same wave writes then reads: LDS keeps the order
-        int rank = 0;
-#pragma unroll
-        for (int j4 = 0; j4 < kMaxH; j4 += 4) {
-            const float4 e4 = *reinterpret_cast<const float4*>(&sE[j4]);
-            const float es[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) rank += (es[u] > E) || (es[u] == E && j4 + u < j);
-        }
-        const bool sel = j < a.H && rank < a.h;
-        const unsigned long long msk = __ballot(sel);
-        const int pos = __popcll(msk & ((1ull << lane) - 1ull));
-        if (sel) {
-            a.heads_out[(long long)row * a.h + pos] = j;
-            s_heads[pos] = j;
-        }
-    }
+    __shared__ float s_w[kMaxH];
+    RouteIn r;
+    r.q = a.q + (long long)row * a.H * kD;
+    r.w = a.w + (long long)row * a.H;
+    r.reps = a.reps + (long long)b * a.seq_stride;
+    r.tailp = (a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
+    r.H = a.H;
+    r.Mt = min(t / a.B + 1, a.nblk);
+    r.h = a.h;
+    r.E_out = a.E_out ? a.E_out + (long long)row * a.H : nullptr;
+    route_wg<NHT>(r, s_heads, s_w);
+    for (int u = threadIdx.x; u < a.h; u += 256) a.heads_out[(long long)row * a.h + u] = s_heads[u];
     // The routed heads' q rows and weights, for the fused prefill: 16 lanes
     // per head, 16 bytes each.
     if (a.qp) {
-        __syncthreads();
         for (int x = threadIdx.x; x < a.h * 16; x += 256) {
             const int u = x >> 4, part = x & 15;
             const int j = s_heads[u];
@@ -435,6 +656,31 @@ static void scan_dispatch_keys(const ScanArgs& a, dim3 grid, hipStream_t s) {
     } else {
         scan_dispatch_hist<NHT, 4, 0>(a, grid, s);
     }
+}
+
+template <int NHT>
+static void scan_dispatch_pooled(const ScanArgs& a, dim3 grid, hipStream_t s) {
+    constexpr int kFull = kScanPoolChunk / (scan_waves<4>() * 16 * scan_groups<4>());
+    constexpr int G = scan_groups<4>();
+    constexpr int NB = scan_bufs<4>();
+    if (a.chunk == kScanPoolChunk)
+        sa_launch(scan_kernel<NHT, 4, G, NB, kFull, true, false, true>, grid, dim3(64 * scan_waves<4>()), 0, s, a);
+    else
+        sa_launch(scan_kernel<NHT, 4, G, NB, 0, true, false, true>, grid, dim3(64 * scan_waves<4>()), 0, s, a);
+}
+
+hipError_t launch_scan_pooled(const ScanArgs& a, int rows, int nht, hipStream_t s) {
+    const int maxn = a.len_cap;
+    const dim3 grid((unsigned)((maxn + a.chunk - 1) / a.chunk), (unsigned)rows);
+    prof_begin(K_SCAN_POOL, s);
+    switch (nht) {
+        case 1: scan_dispatch_pooled<1>(a, grid, s); break;
+        case 2: scan_dispatch_pooled<2>(a, grid, s); break;
+        case 3: scan_dispatch_pooled<3>(a, grid, s); break;
+        default: scan_dispatch_pooled<4>(a, grid, s); break;
+    }
+    prof_end(K_SCAN_POOL, s);
+    return hipGetLastError();
 }
 
 int cu_count() {

@@ -91,6 +91,18 @@ int main() {
     EXPECT(indexer_score_topk_noalloc(q, w, k, &pre, oi, os, nullptr), SA_EWORKSPACE);
     EXPECT(indexer_score_topk_noalloc(q, w, nullptr, &dec, oi, os, nullptr), SA_EINVAL);
 
+    // DSA with block pooling
+    EXPECT(indexer_score_topk_pooled_ws(&dec, 128, 1024, &n), SA_OK);
+    EXPECT(indexer_score_topk_pooled_ws(&pre, 128, 1024, &n), SA_EUNSUPPORTED);
+    EXPECT(indexer_score_topk_pooled_ws(&dec, 64, 1024, &n), SA_EINVAL);
+    EXPECT(indexer_score_topk_pooled_ws(&dec, 128, 1000, &n), SA_EINVAL);
+    EXPECT(indexer_score_topk_pooled_ws(&dec, 1024, 8192, &n), SA_EUNSUPPORTED);
+    EXPECT(indexer_score_topk_pooled(q, w, k, &dec, 128, 1024, nullptr, nullptr, oi, os, ws,
+                                     1 << 30, nullptr, nullptr), SA_EINVAL);
+    EXPECT(indexer_score_topk_pooled(q, w, k, &dec, 128, 1024, reinterpret_cast<uint16_t*>(oi),
+                                     reinterpret_cast<uint16_t*>(oi), oi, os, ws, 1, nullptr,
+                                     nullptr), SA_EWORKSPACE);
+
     // MISA / HISA arguments
     EXPECT(misa_route_ws(&dec, 0, 8, 0, 0, &n), SA_EINVAL);
     EXPECT(misa_route_ws(&dec, 1024, 0, 0, 0, &n), SA_EINVAL);

@@ -321,6 +321,48 @@ def test_pool_blocks(api, L, block):
     np.testing.assert_allclose(val, ref, rtol=1e-4, atol=2e-6)
 
 
+@pytest.mark.parametrize("Bt,L,small,large,k", [
+    (8, 131072, 128, 1024, 2048),   # the 128K decode batch: full 4096-key chunks
+    (3, 5000, 128, 1024, 100),      # partial last chunk and blocks
+    (2, 300, 128, 1024, 64),        # one chunk shorter than a large block
+    (2, 20000, 256, 2048, 500),     # other block sizes
+])
+def test_pooled_dsa(api, Bt, L, small, large, k):
+    # The DSA decode selector that also pools the keys it streams: the same
+    # selection as indexer_score_topk (same scores, so the same set), and the
+    # block means of the oracle (as sa_pool_blocks2, up to fp32 rounding).
+    say("pooled dsa Bt=%d L=%d small=%d large=%d" % (Bt, L, small, large))
+    p = synth.make_problem(70 + L % 61, Bt=Bt, T=1, L=L, H=64, needles=8, needle_mode="decode")
+    q, w, K = to_device(p, DEV)
+    shape = api.Shape(Bt, 1, 64, 128, L, L - 1, k)
+    gi, gs, gw = guarded_outputs(q, k, DEV, api.indexer_score_topk_pooled_ws(shape, small, large))
+    ev = torch.cuda.Event()
+    idx, sc, ps, pl = api.indexer_score_topk_pooled(q, w, K, L - 1, k, small, large,
+                                                    out_idx=gi.view, out_score=gs.view,
+                                                    ws=gw.view, pools_ready=ev)
+    ridx, rsc = api.indexer_score_topk(q, w, K, L - 1, k)
+    torch.cuda.synchronize()
+    check_guards(gi, gs, gw)
+    a, r = _np(idx).reshape(Bt, k), _np(ridx).reshape(Bt, k)
+    for row in range(Bt):
+        assert set(a[row].tolist()) == set(r[row].tolist())
+    check_dsa(p, k, _np(idx), _np(sc), rows_of(p))
+    for got, block in ((ps, small), (pl, large)):
+        g = _np(got).view(np.uint16)
+        val = synth.bf16_bits_to_f32(g[:, :, 0]).astype(np.float64) + \
+            synth.bf16_bits_to_f32(g[:, :, 1]).astype(np.float64)
+        np.testing.assert_allclose(val, oracle.pool(p["K"], block), rtol=1e-4, atol=2e-6)
+
+
+def test_pooled_dsa_rejects_prefill_rows(api):
+    say("pooled dsa rejects T > 1")
+    p = synth.make_problem(79, Bt=1, T=2, L=500, H=16)
+    q, w, K = to_device(p, DEV)
+    with pytest.raises(api.SaError) as e:
+        api.indexer_score_topk_pooled(q, w, K, 498, 8, 128, 1024)
+    assert e.value.code == api.SA_EUNSUPPORTED
+
+
 def test_pool_blocks2_matches_single(api):
     say("pool2")
     p = synth.make_problem(51, Bt=2, T=1, L=10000, H=4)
