@@ -122,18 +122,6 @@ __device__ __forceinline__ int below(unsigned long long m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave: four row shifts within
-// each 16-lane row, then the row totals carried with the two row broadcasts.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
-    return v;
-}
-
 __device__ __forceinline__ unsigned long long pf_key(float sc, int idx) {
     return ((unsigned long long)ord_key(sc) << 32) | (unsigned long long)(~(uint32_t)idx);
 }

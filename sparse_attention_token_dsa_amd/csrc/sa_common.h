@@ -134,6 +134,28 @@ __device__ __forceinline__ uint4 ldg16_stream(const uint16_t* p) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Workgroup barrier that orders LDS only: the waits before it cover LDS
+// operations, so global loads in flight stay in flight (a plain
+// __syncthreads() also waits for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave on the VALU: row shifts
+// 1, 2, 4, 8 inside each 16-lane row (lanes past the row start add 0), then
+// lane 15 broadcast into rows 1 and 3 and lane 31 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return x;
+}
+
 // Wave-aggregated append: every lane of the wave must call it.  Lanes with
 // pred get consecutive slots starting at an atomically reserved base.
 __device__ __forceinline__ int wave_append(bool pred, int* counter) {
@@ -144,7 +166,7 @@ __device__ __forceinline__ int wave_append(bool pred, int* counter) {
     if (m) {
         int leader = __ffsll((long long)m) - 1;
         if (lane == leader) base = atomicAdd(counter, __popcll(m));
-        base = __shfl(base, leader);
+        base = __builtin_amdgcn_readlane(base, leader);
     }
     return base + rank;
 }

@@ -67,15 +67,6 @@ __device__ __forceinline__ void load_qfrag(QFrag<NHT>& f, const uint16_t* qrow,
     }
 }
 
-// Workgroup barrier that orders LDS only: the waits before it cover LDS
-// operations, so global loads in flight stay in flight (a plain
-// __syncthreads() also waits for every outstanding global load).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Sum of a value over the 16 lanes of its row (lanes 16g .. 16g+15): four
 // DPP row rotations (8, 4, 2, 1) on the VALU, no LDS round trips.  Every
 // lane of the row ends with the row's sum (the rounding order depends on the

@@ -12,14 +12,9 @@ namespace sa {
 template <int NT>
 __device__ int block_excl_scan(int v, int* s_wave, int* total) {
     const int lane = lane_id(), wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_incl_scan(v);
     if (lane == 63) s_wave[wid] = x;
-    __syncthreads();
+    lds_barrier();
     int base = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) {
@@ -27,7 +22,7 @@ __device__ int block_excl_scan(int v, int* s_wave, int* total) {
         if (w < wid) base += sw;
         tot += sw;
     }
-    __syncthreads();
+    lds_barrier();
     *total = tot;
     return base + x - v;
 }
@@ -57,7 +52,7 @@ __device__ void find_threshold(const uint32_t* hist, int nbins, int need, int* s
         }
         cum += h;
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 }  // namespace sa

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     uint32_t* hist = reinterpret_cast<uint32_t*>(s_cand);  // 16 KiB, reused below
     const uint32_t* grow = a.state + (long long)row * kRowState;
     for (int x = tid; x < kHist0Bins; x += kFilterThreads) hist[x] = grow[x];
-    __syncthreads();
+    lds_barrier();
     const int need = min(a.k, n);
     find_threshold<kFilterThreads>(hist, kHist0Bins, need, s_wave, &th);
     int* ctl = reinterpret_cast<int*>(a.state + (long long)row * kRowState + kHist0Bins);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
         s_ne = 0;
         s_nc = 0;
     }
-    __syncthreads();
+    lds_barrier();
     // Each thread classifies its kPer scores (float4 loads, all issued first),
     // then one wave-level prefix sum of its (emit, candidate) counts and one
     // LDS atomic per wave and kind give it its staging slots.
@@ -121,12 +121,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     }
     const int lane = lane_id();
     const int mine = __popc(emask) | (__popc(cmask) << 16);
-    int incl = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
+    const int incl = wave_incl_scan(mine);
     int wbase = 0;
     if (lane == 63) {
         const int te = incl & 0xffff, tc = incl >> 16;
@@ -134,7 +129,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
         const int bc = tc ? atomicAdd(&s_nc, tc) : 0;
         wbase = be | (bc << 16);
     }
-    wbase = __shfl(wbase, 63);
+    wbase = __builtin_amdgcn_readlane(wbase, 63);
     const int excl = incl - mine;
     int se = (wbase & 0xffff) + (excl & 0xffff);
     int sc2 = (wbase >> 16) + (excl >> 16);
@@ -148,12 +143,12 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
         }
         if (cmask & (1u << j)) s_cand[sc2++] = make_key(vs[j], u);
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == 0) {
         s_base[0] = s_ne ? atomicAdd(&ctl[CTL_EMITTED], s_ne) : 0;
         s_base[1] = s_nc ? atomicAdd(&ctl[CTL_CANDS], s_nc) : 0;
     }
-    __syncthreads();
+    lds_barrier();
     int32_t* oidx = a.out_idx + (long long)row * a.out_stride;
     float* osc = a.out_score ? a.out_score + (long long)row * a.out_stride : nullptr;
     for (int x = tid; x < s_ne; x += kFilterThreads) {
@@ -178,6 +173,7 @@ struct SelShared {
     uint32_t hist[kHist0Bins];
     unsigned long long lbuf[2][kLdsCand];
     int wave[kTopkThreads / 64];
+    uint32_t wmax[kTopkThreads / 64], wmin[kTopkThreads / 64];
     Thresh th;
     int out, cand;
 };
@@ -191,6 +187,206 @@ __device__ __forceinline__ unsigned long long src_key(int kind, const float* dsr
     const int id = lid[u];
     valid = valid && id >= 0;
     return make_key(lsc[u], id);
+}
+
+// Sources of at most kRegKeys keys per thread (rescored lists, block score
+// rows, the filter's candidates): every key is loaded once into registers,
+// all loads in flight together, and the selection runs on the registers.
+// The digits are taken from the key relative to the smallest score present:
+// with r = ord(score) - min ord, the 64-bit key (r << 32 | ~index) orders
+// like the plain key, and its top 12 significant bits split the actual score
+// range evenly (the plain key's top bits hold sign and exponent, which few
+// scores share out).  After a digit level, if at most kRankMax keys sit on
+// the threshold digit, each of them is placed by its exact rank among them.
+constexpr int kRegKeys = 8;
+constexpr int kRankMax = 1024;
+
+// Largest value over the wave, in every lane (identity 0).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    const auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
+                                                    const float* dsrc, const float* lsc,
+                                                    const int32_t* lid,
+                                                    const unsigned long long* ksrc, int nsrc,
+                                                    int32_t* oidx, float* osc, SelShared& S) {
+    const int tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
+    const int row = blockIdx.x;
+    unsigned long long kr[kRegKeys];
+    uint32_t alive = 0u;
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j) {
+        const int u = tid + j * kTopkThreads;
+        bool valid = u < nsrc;
+        kr[j] = valid ? src_key(kind, dsrc, lsc, lid, ksrc, u, valid) : 0ull;
+        if (valid) alive |= 1u << j;
+    }
+    int need = 0, need_rem = 0;
+    if (kind == SRC_KEYS) {
+        // continue after the filter: its winners are written, its
+        // candidates are the keys on the row's first-digit threshold
+        const int* ctl = reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
+                                                      kHist0Bins);
+        need = ctl[CTL_NEED];
+        const int gt = ctl[CTL_GT];
+        for (int u = need + tid; u < a.k; u += kTopkThreads) {
+            oidx[u] = -1;
+            if (osc) osc[u] = -INFINITY;
+        }
+        if (gt + ctl[CTL_EQ] == need) return;  // the filter emitted everything
+        need_rem = need - gt;
+        if (tid == 0) S.out = gt;
+    } else if (tid == 0) {
+        S.out = 0;
+    }
+    // Score range of the keys present, and their count.
+    uint32_t smax = 0u, sinv = 0u;  // max of ord, max of ~ord
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j)
+        if ((alive >> j) & 1u) {
+            const uint32_t o = (uint32_t)(kr[j] >> 32);
+            smax = o > smax ? o : smax;
+            sinv = ~o > sinv ? ~o : sinv;
+            ++cnt;
+        }
+    smax = wave_max_u32(smax);
+    sinv = wave_max_u32(sinv);
+    cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+    if (lane == 0) {
+        S.wmax[wid] = smax;
+        S.wmin[wid] = sinv;
+        S.wave[wid] = cnt;
+    }
+    lds_barrier();
+    uint32_t omax = 0u, oinv = 0u;
+    int nvalid = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+        omax = S.wmax[w] > omax ? S.wmax[w] : omax;
+        oinv = S.wmin[w] > oinv ? S.wmin[w] : oinv;
+        nvalid += S.wave[w];
+    }
+    if (kind != SRC_KEYS) {
+        need = min(a.k, nvalid);
+        for (int u = need + tid; u < a.k; u += kTopkThreads) {
+            oidx[u] = -1;
+            if (osc) osc[u] = -INFINITY;
+        }
+        if (need <= 0) return;
+        need_rem = need;
+    }
+    const uint32_t omin = ~oinv;
+    const uint32_t span = omax - omin;
+    // significant bits of the relative key: the score part's, then 32 index bits
+    int pos = 32 + (span ? 32 - __clz(span) : 0);
+    unsigned long long rk[kRegKeys];
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j)
+        rk[j] = ((unsigned long long)((uint32_t)(kr[j] >> 32) - omin) << 32) |
+                (kr[j] & 0xffffffffull);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int level = 0; pos > 0; ++level) {
+        const int width = level == 0 ? kHist0Bits : 10;
+        const int shift = pos > width ? pos - width : 0;
+        const int nbins = 1 << (pos - shift);
+        const unsigned long long mask = (unsigned long long)(nbins - 1);
+        const int hbins = nbins < kTopkThreads ? kTopkThreads : nbins;  // bins scanned
+        for (int x = tid; x < hbins; x += kTopkThreads) S.hist[x] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kRegKeys; ++j)
+            if ((alive >> j) & 1u) atomicAdd(&S.hist[(uint32_t)((rk[j] >> shift) & mask)], 1u);
+        lds_barrier();
+        find_threshold<kTopkThreads>(S.hist, hbins, need_rem, S.wave, &S.th);
+        const uint32_t d = (uint32_t)S.th.dstar;
+        const int gt = S.th.gt;
+        const int eq = S.th.eq;
+        const bool take_all = gt + eq == need_rem;
+        // winners of this level: one LDS atomic per wave for all its keys
+        unsigned long long m[kRegKeys];
+        int wtot = 0;
+#pragma unroll
+        for (int j = 0; j < kRegKeys; ++j) {
+            const uint32_t dig = (uint32_t)((rk[j] >> shift) & mask);
+            const bool in = (alive >> j) & 1u;
+            const bool emit = in && (dig > d || (take_all && dig == d));
+            m[j] = __ballot(emit);
+            wtot += __popcll(m[j]);
+            if (!(in && dig == d)) alive &= ~(1u << j);
+        }
+        int base = 0;
+        if (wtot) {
+            if (lane == 0) base = atomicAdd(&S.out, wtot);
+            base = __builtin_amdgcn_readlane(base, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < kRegKeys; ++j) {
+            if ((m[j] >> lane) & 1ull) {
+                const int slot = base + __popcll(m[j] & below);
+                if (slot < need) {
+                    oidx[slot] = key_idx(kr[j]);
+                    if (osc) osc[slot] = key_score(kr[j]);
+                }
+            }
+            base += __popcll(m[j]);
+        }
+        need_rem -= gt;
+        if (take_all) return;
+        if (eq <= kRankMax) {
+            // Few keys left on the threshold digits: compact them into LDS
+            // and place each by its rank among them (keys are distinct).
+            if (tid == 0) S.cand = 0;
+            lds_barrier();
+            unsigned long long cm[kRegKeys];
+            int ctot = 0;
+#pragma unroll
+            for (int j = 0; j < kRegKeys; ++j) {
+                cm[j] = __ballot((alive >> j) & 1u);
+                ctot += __popcll(cm[j]);
+            }
+            int cbase = 0;
+            if (ctot) {
+                if (lane == 0) cbase = atomicAdd(&S.cand, ctot);
+                cbase = __builtin_amdgcn_readlane(cbase, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < kRegKeys; ++j) {
+                if ((cm[j] >> lane) & 1ull) S.lbuf[0][cbase + __popcll(cm[j] & below)] = kr[j];
+                cbase += __popcll(cm[j]);
+            }
+            lds_barrier();
+            const int done = need - need_rem;  // winners already written
+            for (int c = tid; c < eq; c += kTopkThreads) {
+                const unsigned long long key = S.lbuf[0][c];
+                int rank = 0;
+                int o = 0;
+                for (; o + 8 <= eq; o += 8) {
+                    unsigned long long v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = S.lbuf[0][o + e];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) rank += v[e] > key;
+                }
+                for (; o < eq; ++o) rank += S.lbuf[0][o] > key;
+                if (rank < need_rem) {
+                    oidx[done + rank] = key_idx(key);
+                    if (osc) osc[done + rank] = key_score(key);
+                }
+            }
+            return;
+        }
+        pos = shift;
+        lds_barrier();
+    }
 }
 
 // mode: SRC_DENSE / SRC_LIST: full selection from level 0.
@@ -225,6 +421,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
     if (kind == SRC_KEYS) {
         const int* ctl = reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
                                                       kHist0Bins);
+        ksrc = cand + (long long)row * a.cand_cap;
+        nsrc0 = (int)min((long long)ctl[CTL_CANDS], a.cand_cap);
+    }
+    if (nsrc0 <= kRegKeys * kTopkThreads) {
+        select_in_registers(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S);
+        return;
+    }
+    if (kind == SRC_KEYS) {
+        const int* ctl = reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
+                                                      kHist0Bins);
         need = ctl[CTL_NEED];
         const int gt = ctl[CTL_GT];
         for (int u = need + tid; u < a.k; u += kTopkThreads) {
@@ -239,16 +445,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         ksrc = cand + (long long)row * a.cand_cap;
         nsrc0 = (int)min((long long)ctl[CTL_CANDS], a.cand_cap);
         if (tid == 0) S.out = gt;
-        __syncthreads();
+        lds_barrier();
     } else {
         for (int x = tid; x < kHist0Bins; x += kTopkThreads) S.hist[x] = 0u;
-        __syncthreads();
+        lds_barrier();
         for (int u = tid; u < nsrc0; u += kTopkThreads) {
             bool valid = true;
             const unsigned long long key = src_key(kind, dsrc, lsc, lid, nullptr, u, valid);
             if (valid) atomicAdd(&S.hist[(uint32_t)(key >> kShift[0])], 1u);
         }
-        __syncthreads();
+        lds_barrier();
         int local = 0;
         for (int j = 0; j < kHist0Bins / kTopkThreads; ++j)
             local += (int)S.hist[tid * (kHist0Bins / kTopkThreads) + j];
@@ -262,7 +468,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         if (need <= 0) return;
         need_rem = need;
         if (tid == 0) S.out = 0;
-        __syncthreads();
+        lds_barrier();
     }
 
     // Current source: the global source (with prefix filter) or an LDS buffer.
@@ -275,7 +481,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         const bool hist_ready = (level == 0);  // level-0 histogram built above
         if (!hist_ready) {
             for (int x = tid; x < nbins; x += kTopkThreads) S.hist[x] = 0u;
-            __syncthreads();
+            lds_barrier();
             for (int u = tid; u < nsrc; u += kTopkThreads) {
                 bool valid = true;
                 unsigned long long key;
@@ -287,7 +493,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
                 }
                 if (valid) atomicAdd(&S.hist[(uint32_t)((key >> shift) & mask)], 1u);
             }
-            __syncthreads();
+            lds_barrier();
         }
         find_threshold<kTopkThreads>(S.hist, nbins, need_rem, S.wave, &S.th);
         const uint32_t d = (uint32_t)S.th.dstar;
@@ -296,7 +502,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         const bool next_fits = !take_all && S.th.eq <= kLdsCand;
         const int dst = cur_lds == 0 ? 1 : 0;
         if (tid == 0) S.cand = 0;
-        __syncthreads();
+        lds_barrier();
         for (int ub = 0; ub < nsrc; ub += kTopkThreads) {
             const int u = ub + tid;
             bool valid = u < nsrc;
@@ -320,7 +526,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
             const int cslot = wave_append(app, &S.cand);
             if (app && cslot < kLdsCand) S.lbuf[dst][cslot] = key;
         }
-        __syncthreads();
+        lds_barrier();
         need_rem -= gt;
         if (take_all) break;
         pfx = (pfx_shift == 64) ? (unsigned long long)d : ((pfx << kWidth[level]) | d);
@@ -332,7 +538,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
             cur_lds = -1;
             nsrc = nsrc0;
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
