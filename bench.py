@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "indexer scores/s (query·token) + top-k rows/s at L=128K; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "sparse_attention_token_dsa_amd", "traffic.json")
 
 
@@ -792,7 +793,43 @@ def bench_prefill(api, synth, torch, np, dev, iters):
                          "algorithmic_flops_per_launch": flops,
                          "counters": measured_mfma(
                              source_digest(["prefill.hip", "sa_frag.h", "sa_common.h"]))},
-            "ragged": bench_prefill_ragged(api, synth, torch, np, dev, iters)}
+            "ragged": bench_prefill_ragged(api, synth, torch, np, dev, iters),
+            "fp8q": bench_prefill_fp8q(api, torch, dev, q, w, K, shape, oi, osc, iters, flops,
+                                       pairs)}
+
+
+def bench_prefill_fp8q(api, torch, dev, q, w, K, shape, oi, osc, iters, flops, pairs):
+    """The same chunked prefill on the FP8 key cache with the query converted
+    to E4M3 in the kernel (indexer_score_topk_fp8q): the contraction on the
+    16x16x128 fp8 MFMA, against the dense fp8 peak."""
+    T, off, k = shape.T, shape.causal_offset, shape.topk
+    codes, scales = api.quantize_keys_fp8(K)
+    ws = torch.empty(api.indexer_score_topk_fp8q_ws(shape), dtype=torch.uint8, device=dev)
+
+    def call():
+        api.indexer_score_topk_fp8q(q, w, codes, scales, off, k, oi, osc, ws=ws)
+    settle(call, torch, dev)
+    api.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(iters):
+        call()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    kern = api.profile_read()
+    api.profile_enable(False)
+    us = 1e3 * kern["prefill_fused_fp8q"][0] / kern["prefill_fused_fp8q"][1]
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"workload": "prefill_chunked_T4096_P28672_h64_fp8keys_fp8q",
+            "what": "keys as E4M3 codes + one fp32 scale per key, query quantized per head "
+                    "in the kernel, 16x16x128 fp8 MFMA",
+            "ms_per_call": (t1 - t0) * 1e3 / iters,
+            "logical_scores_per_s": pairs / ((t1 - t0) / iters),
+            "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()},
+            "roofline": {"kernel": "prefill_fused_fp8q", "bound": "mfma",
+                         "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4),
+                         "traffic": None, "algorithmic_flops_per_launch": flops,
+                         "vs_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}}
 
 
 def bench_prefill_ragged(api, synth, torch, np, dev, iters):

@@ -236,7 +236,8 @@ int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes);
  *   I = sum_j w_j * ReLU(q_j . (scales[s] * e4m3(codes[s]))),
  * and the selection is as in indexer_score_topk.  The key stream is 132
  * bytes per key instead of 256.  Decode-style rows only: T must be < 16
- * (SA_EUNSUPPORTED otherwise).  Other arguments, ownership and errors as in
+ * (SA_EUNSUPPORTED otherwise; prefill rows on the FP8 cache take
+ * indexer_score_topk_fp8q).  Other arguments, ownership and errors as in
  * indexer_score_topk. */
 int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
                            const float* scales, const sa_shape* s, int32_t* out_idx,
@@ -246,17 +247,20 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
 int indexer_score_topk_fp8_ragged_ws(const sa_shape* s, size_t* ws_bytes);
 
 /* Ragged batches (as indexer_score_topk_ragged: seq_lens, total_len, the
- * capacity L with causal_offset = L - T) over an FP8 key cache, decode-style
- * rows (T < 16).  q_fp8 = 0: the scores of indexer_score_topk_fp8 (q bf16);
- * q_fp8 != 0: those of indexer_score_topk_fp8q (q converted to E4M3, fp8
- * MFMA).  Other arguments, ownership and errors as in indexer_score_topk_fp8. */
+ * capacity L with causal_offset = L - T) over an FP8 key cache.  q_fp8 = 0:
+ * the scores of indexer_score_topk_fp8 (q bf16), decode-style rows (T < 16,
+ * SA_EUNSUPPORTED otherwise); q_fp8 != 0: those of indexer_score_topk_fp8q
+ * (q converted to E4M3, fp8 MFMA), any T (T >= 16: the fused prefill, each
+ * sequence's rows at its own end).  Other arguments, ownership and errors as
+ * in indexer_score_topk_fp8. */
 int indexer_score_topk_fp8_ragged(const uint16_t* q, const float* w, const uint8_t* codes,
                                   const float* scales, const int32_t* seq_lens, int64_t total_len,
                                   int32_t q_fp8, const sa_shape* s, int32_t* out_idx,
                                   float* out_score, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes for indexer_score_topk_fp8q on this shape (the same as for
- * indexer_score_topk_fp8). */
+/* Workspace bytes for indexer_score_topk_fp8q on this shape (for T < 16 the
+ * same as for indexer_score_topk_fp8; for T >= 16 the fused prefill's
+ * survivor lists, as indexer_score_topk). */
 int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes);
 
 /* As indexer_score_topk_fp8, with the query converted to E4M3 as well, the
@@ -266,9 +270,11 @@ int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes);
  * sa_quantize_keys_fp8 (b_j = max|q_{t,j}| / 448, codes of q / b_j) inside
  * the kernel, and since b_j > 0 commutes with ReLU,
  *   I = scales[s] * sum_j fp32(w_j * b_j) * ReLU(e4m3(qc_j) . e4m3(codes[s])),
- * the dot product on the 16x16x128 fp8 MFMA with fp32 accumulation.  Same
- * arguments, shapes, ownership and errors as indexer_score_topk_fp8; q stays
- * bf16 in memory. */
+ * the dot product on the 16x16x128 fp8 MFMA with fp32 accumulation.  Rows
+ * with T >= 16 per sequence take the fused prefill on the same arithmetic
+ * (the query quantized per head in the kernel, the keys' codes and scales
+ * staged in LDS, no score matrix written).  Same arguments, ownership and
+ * errors as indexer_score_topk_fp8 otherwise; q stays bf16 in memory. */
 int indexer_score_topk_fp8q(const uint16_t* q, const float* w, const uint8_t* codes,
                             const float* scales, const sa_shape* s, int32_t* out_idx,
                             float* out_score, void* ws, size_t ws_bytes, void* stream);

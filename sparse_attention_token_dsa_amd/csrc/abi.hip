@@ -65,7 +65,7 @@ const char* kKernelNames[sa::K_COUNT] = {
     "fill_u32", "scan_dsa", "scan_routed", "block_score", "topk_select", "topk_filter",
     "pool", "pool2", "tail_pool", "misa_router", "gather_rescore", "prefill_fused",
     "quantize_fp8", "scan_dsa_fp8", "block_extrema", "resmisa_router", "head_rows", "tidy",
-    "scan_dsa_fp8q", "scan_dsa_pool"};
+    "scan_dsa_fp8q", "scan_dsa_pool", "prefill_fused_fp8q"};
 
 // ------------------------------------------------------------ workspace
 
@@ -738,12 +738,43 @@ int sa_quantize_keys_fp8(const uint16_t* keys, int32_t batch, int32_t L, int32_t
     return SA_OK;
 }
 
-static int check_fp8_shape(const sa_shape* s) {
+// FP8 keys: decode-style rows (T < 16) with q in bf16 or E4M3; prefill rows
+// (T >= 16) with q in E4M3 only (the fused prefill on the fp8 MFMA).
+static int check_fp8_shape(const sa_shape* s, bool prefill_ok = false) {
     int rc = check_shape(s);
     if (rc) return rc;
-    if (s->T >= kPrefillMinT)
-        return fail(SA_EUNSUPPORTED, "FP8 keys: decode-style rows only (T < 16)");
+    if (s->T >= kPrefillMinT) {
+        if (!prefill_ok)
+            return fail(SA_EUNSUPPORTED,
+                        "FP8 keys with a bf16 query: decode-style rows only (T < 16); "
+                        "prefill rows take the E4M3 query (indexer_score_topk_fp8q)");
+        return check_grid_batch(s);
+    }
     return check_grid_rows(s);
+}
+
+// Fused prefill rows on the FP8 cache, the query quantized in the kernel.
+static hipError_t run_prefill_fp8(const uint16_t* q, const float* w, const uint8_t* codes,
+                                  const float* scales, const sa_shape* s, const DsaPlan& p,
+                                  int32_t* out_idx, float* out_score, hipStream_t st,
+                                  const int32_t* seq_lens) {
+    sa::PrefillArgs a{};
+    a.q = q;
+    a.w = w;
+    a.codes = codes;
+    a.kscale = scales;
+    a.T = s->T;
+    a.H = s->H;
+    a.L = s->L;
+    a.offset = s->causal_offset;
+    a.k = s->topk;
+    a.surv = p.surv;
+    a.cap = surv_cap((long long)s->causal_offset + s->T, s->topk);
+    a.out_idx = out_idx;
+    a.out_score = out_score;
+    a.out_stride = s->topk;
+    a.seq_lens = seq_lens;
+    return sa::launch_prefill(a, s->batch * s->T, st);
 }
 
 int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes) {
@@ -757,7 +788,7 @@ int indexer_score_topk_fp8_ws(const sa_shape* s, size_t* ws_bytes) {
 static int run_fp8(const uint16_t* q, const float* w, const uint8_t* codes, const float* scales,
                    const sa_shape* s, int32_t* out_idx, float* out_score, void* ws,
                    size_t ws_bytes, void* stream, bool q_fp8) {
-    int rc = check_fp8_shape(s);
+    int rc = check_fp8_shape(s, q_fp8);
     if (rc) return rc;
     if (!q || !w || !codes || !scales || !out_idx)
         return fail(SA_EINVAL, "q, w, codes, scales and out_idx must be non-NULL");
@@ -765,6 +796,12 @@ static int run_fp8(const uint16_t* q, const float* w, const uint8_t* codes, cons
     if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
     void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     DsaPlan p = plan_dsa(s, base);
+    if (p.prefill) {
+        hipError_t e = run_prefill_fp8(q, w, codes, scales, s, p, out_idx, out_score,
+                                       static_cast<hipStream_t>(stream), nullptr);
+        if (e != hipSuccess) return hip_fail(e, "fp8 prefill");
+        return SA_OK;
+    }
     hipError_t e = run_dense_topk(q, w, nullptr, s, nullptr, 0, p.scores, p.state, p.cand,
                                   s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
                                   codes, scales, false, nullptr, 0, q_fp8);
@@ -779,7 +816,7 @@ int indexer_score_topk_fp8(const uint16_t* q, const float* w, const uint8_t* cod
 }
 
 int indexer_score_topk_fp8_ragged_ws(const sa_shape* s, size_t* ws_bytes) {
-    int rc = check_fp8_shape(s);
+    int rc = check_fp8_shape(s, true);
     if (rc) return rc;
     if (s->causal_offset != s->L - s->T)
         return fail(SA_EINVAL, "ragged batches: causal_offset must be L - T (the capacity)");
@@ -798,18 +835,33 @@ int indexer_score_topk_fp8_ragged(const uint16_t* q, const float* w, const uint8
     if (!q || !w || !codes || !scales || !seq_lens || !out_idx)
         return fail(SA_EINVAL, "q, w, codes, scales, seq_lens and out_idx must be non-NULL");
     if (total_len < 0) return fail(SA_EINVAL, "total_len must be >= 0");
+    if (s->T >= kPrefillMinT && !q_fp8)
+        return fail(SA_EUNSUPPORTED,
+                    "FP8 keys with a bf16 query: decode-style rows only (T < 16); prefill "
+                    "rows take q_fp8 = 1");
     if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
     void* base = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(ws) + 255) & ~uintptr_t(255));
     DsaPlan p = plan_dsa(s, base);
-    hipError_t e = run_dense_topk(q, w, nullptr, s, nullptr, 0, p.scores, p.state, p.cand,
-                                  s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
-                                  codes, scales, false, seq_lens, total_len, q_fp8 != 0);
+    hipError_t e;
+    if (p.prefill) {
+        e = run_prefill_fp8(q, w, codes, scales, s, p, out_idx, out_score,
+                            static_cast<hipStream_t>(stream), seq_lens);
+        if (e != hipSuccess) return hip_fail(e, "ragged fp8 prefill");
+        return SA_OK;
+    }
+    e = run_dense_topk(q, w, nullptr, s, nullptr, 0, p.scores, p.state, p.cand,
+                       s->topk, out_idx, out_score, static_cast<hipStream_t>(stream),
+                       codes, scales, false, seq_lens, total_len, q_fp8 != 0);
     if (e != hipSuccess) return hip_fail(e, "ragged fp8 decode scan");
     return SA_OK;
 }
 
 int indexer_score_topk_fp8q_ws(const sa_shape* s, size_t* ws_bytes) {
-    return indexer_score_topk_fp8_ws(s, ws_bytes);
+    int rc = check_fp8_shape(s, true);
+    if (rc) return rc;
+    if (!ws_bytes) return fail(SA_EINVAL, "ws_bytes is NULL");
+    *ws_bytes = plan_dsa(s, nullptr).bytes;
+    return SA_OK;
 }
 
 int indexer_score_topk_fp8q(const uint16_t* q, const float* w, const uint8_t* codes,

@@ -149,6 +149,20 @@ __device__ __forceinline__ void pf_interleave() {
     }
 }
 
+// The same for an E4M3 block: M MFMAs (one per head tile, all 128 dims), V
+// VALU instructions spread between them and, with RELOAD, the two LDS reads
+// of the next group's key operand right after the first MFMA.
+template <int I, int M, int V, bool RELOAD>
+__device__ __forceinline__ void pf_interleave8() {
+    if constexpr (I < M) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (RELOAD && I == 0) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        constexpr int nv = V * (I + 1) / M - V * I / M;
+        if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+        pf_interleave8<I + 1, M, V, RELOAD>();
+    }
+}
+
 // One pass of a wave over a survivor list sl[0, cnt) of (position, score
 // bits) pairs: fn(position, score, valid) for every lane and element, 2
 // elements per 16-byte load, 4 loads in flight.  Lists have room for an even
@@ -481,7 +495,7 @@ __device__ __forceinline__ PfRow pf_compact(uint2* L, uint32_t* hr, PfRow st, in
     return st;
 }
 
-template <int NHT>
+template <int NHT, bool F8>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     // The stages are four distinct LDS objects: the compiler then tracks the
     // direct-to-LDS loads per object and places no wait of its own for the
@@ -512,7 +526,9 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     const int ntiles = tmax / kPfTile + 1;
 
     // Per-row state of this wave's two rows (workgroup rows 2 wid + qq).
-    QFrag<NHT> f[kPfQpw];
+    // With F8 the A fragments are the rows' E4M3 query codes, and the
+    // weights carry the query scales.
+    std::conditional_t<F8, QFrag8<NHT>, QFrag<NHT>> f[kPfQpw];
     int tq[kPfQpw], tau[kPfQpw], cnt[kPfQpw], cnt_ge[kPfQpw], htau[kPfQpw];
     float tau_f[kPfQpw];
     bool act[kPfQpw];
@@ -535,7 +551,17 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         h[qq] = hist[r];
         for (int x = lane; x < kPfBins; x += 64) h[qq][x] = 0u;
         const float* wrow = a.w + rowq[qq] * a.H;
-        load_qfrag<NHT>(f[qq], a.q + rowq[qq] * a.H * kD, wrow, a.H, nullptr, 0, g, c);
+        // F8: the wave quantizes the row's heads into its own slice of the
+        // key stages (free until the first fill) and the scales into gk.
+        uint4* qc = (wid >> 1 == 0 ? kt0 : wid >> 1 == 1 ? kt1 : wid >> 1 == 2 ? kt2 : kt3) +
+                    (wid & 1) * 512;
+        float* qs = reinterpret_cast<float*>(&gk[0][0][0][0]) + kPfRows * kD + wid * 64;
+        if constexpr (F8) {
+            quantize_q8_wave(a.q + rowq[qq] * a.H * kD, a.H, qc, qs);
+            load_qfrag_fp8<NHT>(f[qq], qc, qs, wrow, a.H, g, c);
+        } else {
+            load_qfrag<NHT>(f[qq], a.q + rowq[qq] * a.H * kD, wrow, a.H, nullptr, 0, g, c);
+        }
 #pragma unroll
         for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
@@ -544,14 +570,29 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         // order, staged in gk (free until the sweep starts); lanes 0..15 then
         // pack the row's A-fragment entries: lane t holds dims
         // (kk*4 + grp)*8 .. +8 with kk = t / 4, grp = t % 4, for tile row r.
-        const float wl = act[qq] && lane < a.H ? 0.5f * wrow[lane] : 0.f;
+        // (F8: g of the decoded query codes, with the weights w_j b_j.)
+        const float wl =
+            act[qq] && lane < a.H ? 0.5f * (F8 ? wrow[lane] * qs[lane] : wrow[lane]) : 0.f;
         const uint16_t* qr = a.q + rowq[qq] * a.H * kD;
         float g0 = 0.f, g1 = 0.f;
         for (int j = 0; j < a.H; ++j) {
             const float wj = __shfl(wl, j);
-            const uint32_t two = *reinterpret_cast<const uint32_t*>(qr + j * kD + 2 * lane);
-            g0 = fmaf(wj, bf16_bits_to_f32(two & 0xffffu), g0);
-            g1 = fmaf(wj, bf16_bits_to_f32(two >> 16), g1);
+            float x0, x1;
+            if constexpr (F8) {
+                // dims 2 lane, 2 lane + 1: chunk lane / 8, word (lane % 8) / 2
+                const uint32_t wd =
+                    reinterpret_cast<const uint32_t*>(qc + qslot(j, lane >> 3))[(lane & 7) >> 1];
+                const auto lo2 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, false);
+                const auto hi2 = __builtin_amdgcn_cvt_pk_f32_fp8(wd, true);
+                x0 = (lane & 1) ? hi2[0] : lo2[0];
+                x1 = (lane & 1) ? hi2[1] : lo2[1];
+            } else {
+                const uint32_t two = *reinterpret_cast<const uint32_t*>(qr + j * kD + 2 * lane);
+                x0 = bf16_bits_to_f32(two & 0xffffu);
+                x1 = bf16_bits_to_f32(two >> 16);
+            }
+            g0 = fmaf(wj, x0, g0);
+            g1 = fmaf(wj, x1, g1);
         }
         float* gt = reinterpret_cast<float*>(&gk[0][0][0][0]) + r * kD;
         gt[2 * lane] = g0;
@@ -583,8 +624,34 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     // 16 KiB (base key k0): unlike the global form, they leave the compiler's
     // LDS wait counts exact, so the B-fragment reads of the sweep are waited
     // for one by one.
+    // F8: a tile is 64 keys x 128 codes (8 KiB, one 1 KiB load per wave:
+    // key 8 wid + l / 8, LDS slot l % 8 holding the key's global 16-byte
+    // chunk (l % 8) ^ ((key / 4) % 8), so that the 8 lanes of a B-fragment
+    // read hit 8 different bank groups), then the tile's 64 scales (256 B,
+    // wave 0) at uint4 512 of the stage.
+    const uint8_t* cseq = F8 ? a.codes + (long long)seq * a.L * kD : nullptr;
+    const float* sseq = F8 ? a.kscale + (long long)seq * a.L : nullptr;
     auto issue = [&](uint4* stage, int tile) __attribute__((always_inline)) {
         const int k0 = min(tile * kPfTile, tmax);
+        if constexpr (F8) {
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(cseq + (long long)k0 * kD), 0, kPfTile * kD, 0x00020000);
+            const int kt = 8 * wid + (lane >> 3);
+            const int s = min(tile * kPfTile + kt, tmax);
+            const int m = (lane & 7) ^ ((kt >> 2) & 7);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rc, (__attribute__((address_space(3))) void*)(stage + wid * 64), 16,
+                (uint32_t)((s - k0) * kD + m * 16), 0, 0, 0);
+            if (wid == 0) {
+                const __amdgpu_buffer_rsrc_t rs8 = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<float*>(sseq + k0), 0, kPfTile * 4, 0x00020000);
+                const int s2 = min(tile * kPfTile + lane, tmax);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs8, (__attribute__((address_space(3))) void*)(stage + 512), 4,
+                    (uint32_t)((s2 - k0) * 4), 0, 0, 0);
+            }
+            return;
+        }
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(kseq + (long long)k0 * kD), 0, kPfTile * kD * 2, 0x00020000);
 #pragma unroll
@@ -599,6 +666,16 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
     };
     // B fragment of step kk for key 4c + gi: block c, row gi, chunk kk*4 + g.
     const int bbase = c * kPfBlk + g;
+    // F8 B operand of key 4c + gi: its chunks 2g and 2g + 1 (dims 32g ..
+    // 32g+31), at slots (4c + gi) * 8 + (chunk ^ (c % 8)).
+    const int b8lo = c * 32 + ((2 * g) ^ (c & 7)), b8hi = c * 32 + ((2 * g + 1) ^ (c & 7));
+    auto load_b8 = [&](const uint4* ktile, int gi) __attribute__((always_inline)) {
+        const uint4 lo = ktile[b8lo + gi * 8], hi = ktile[b8hi + gi * 8];
+        return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    // F8: scales of keys 4c .. 4c+3 of the pair's two tiles.
+    float ksr[2][4];
 
     // Scores of tile j of a pair: lane (g, c) keeps, for the row and tile of
     // its lane group (row g & 1, tile g >> 1), the per-head part of the
@@ -625,6 +702,7 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) sc = fmaf(f[qq].wv[ht][e], fabsf(acc[qq][ht][e]), sc);
         sc = sum_lane_groups(sc);
+        if constexpr (F8) sc *= ksr[j][gi];
         st[gi] = g == 2 * j + qq ? sc : st[gi];
     };
     // Block (G, qq); RELOAD: re-read group G + 1 (at ntile, group ngi) behind
@@ -635,17 +713,70 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         constexpr bool kPrev = decltype(prev_c)::value;
         // Each block is scheduled on its own.
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!F8) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+            for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-            for (int ht = 0; ht < NHT; ++ht)
-                acc[qq][ht] = mfma16x16x32(f[qq].a[ht][kk], bf[kk],
-                                           kk ? acc[qq][ht] : f32x4{0.f, 0.f, 0.f, 0.f});
-            if (kReload) bf[kk] = ntile[bbase + ngi * 16 + kk * 4];
+                for (int ht = 0; ht < NHT; ++ht)
+                    acc[qq][ht] = mfma16x16x32(f[qq].a[ht][kk], bf[kk],
+                                               kk ? acc[qq][ht] : f32x4{0.f, 0.f, 0.f, 0.f});
+                if (kReload) bf[kk] = ntile[bbase + ngi * 16 + kk * 4];
+            }
+            if (kPrev) epilogue(1 - qq, pj, pgi);
+            pf_interleave<0, 4 * NHT, (kPrev ? 4 * NHT + 7 : 0), NHT, kReload>();
         }
-        if (kPrev) epilogue(1 - qq, pj, pgi);
-        pf_interleave<0, 4 * NHT, (kPrev ? 4 * NHT + 7 : 0), NHT, kReload>();
         __builtin_amdgcn_sched_barrier(0);
+    };
+    // E4M3 blocks: B operands alternate between two register sets per group,
+    // so the next group's operand loads during the current group's first
+    // block (the other set's last reader is the block before).
+    i32x8 bfr[2];
+    auto block8 = [&](auto reload_c, auto prev_c, auto cur_c, int qq, const uint4* ntile, int ngi,
+                      int pj, int pgi) __attribute__((always_inline)) {
+        constexpr bool kReload = decltype(reload_c)::value;
+        constexpr bool kPrev = decltype(prev_c)::value;
+        constexpr int kCur = decltype(cur_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (F8) {
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht) acc[qq][ht] = mfma16x16x128_fp8(f[qq].a[ht], bfr[kCur]);
+            if (kReload) bfr[1 - kCur] = load_b8(ntile, ngi);
+            if (kPrev) epilogue(1 - qq, pj, pgi);
+            pf_interleave8<0, NHT, (kPrev ? 4 * NHT + 8 : 0), kReload>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pair_scores8 = [&](const uint4* ka, const uint4* kb, bool two) __attribute__((always_inline)) {
+        const std::true_type y;
+        const std::false_type n;
+        const std::integral_constant<int, 0> b0;
+        const std::integral_constant<int, 1> b1;
+        const float4 sa4 = reinterpret_cast<const float4*>(ka + 512)[c];
+        const float4 sb4 = reinterpret_cast<const float4*>(kb + 512)[c];
+        ksr[0][0] = sa4.x; ksr[0][1] = sa4.y; ksr[0][2] = sa4.z; ksr[0][3] = sa4.w;
+        ksr[1][0] = sb4.x; ksr[1][1] = sb4.y; ksr[1][2] = sb4.z; ksr[1][3] = sb4.w;
+        bfr[0] = load_b8(ka, 0);
+        block8(y, n, b0, 0, ka, 1, 0, 0);
+        block8(n, y, b0, 1, ka, 0, 0, 0);
+        block8(y, y, b1, 0, ka, 2, 0, 0);
+        block8(n, y, b1, 1, ka, 0, 0, 1);
+        block8(y, y, b0, 0, ka, 3, 0, 1);
+        block8(n, y, b0, 1, ka, 0, 0, 2);
+        block8(y, y, b1, 0, kb, 0, 0, 2);
+        block8(n, y, b1, 1, kb, 0, 0, 3);
+        if (two) {
+            block8(y, y, b0, 0, kb, 1, 0, 3);
+            block8(n, y, b0, 1, kb, 0, 1, 0);
+            block8(y, y, b1, 0, kb, 2, 1, 0);
+            block8(n, y, b1, 1, kb, 0, 1, 1);
+            block8(y, y, b0, 0, kb, 3, 1, 1);
+            block8(n, y, b0, 1, kb, 0, 1, 2);
+            block8(n, y, b1, 0, kb, 0, 1, 2);
+            block8(n, y, b1, 1, kb, 0, 1, 3);
+            epilogue(1, 1, 3);
+        } else {
+            epilogue(1, 0, 3);
+        }
     };
     auto pair_scores = [&](const uint4* ka, const uint4* kb, bool two) __attribute__((always_inline)) {
         const std::true_type y;
@@ -786,9 +917,24 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         for (int kk = 0; kk < 4; ++kk) {
             // One k-step's fragments at a time (12 registers, not 48).
             asm volatile("" ::: "memory");
-            const uint4 bq = ktile[bbase + gi * 16 + kk * 4];
+            uint4 bq;
+            if constexpr (F8) {
+                // dims (kk*4 + g)*8 .. +8 of key 4c + gi: half (kk*4 + g) % 2 of
+                // its 16-byte chunk (kk*4 + g) / 2, widened exactly to bf16
+                const int ch = (kk * 4 + g) >> 1;
+                const uint2 v = reinterpret_cast<const uint2*>(
+                    ktile + (4 * c + gi) * 8 + (ch ^ (c & 7)))[(kk * 4 + g) & 1];
+                bq = widen8(v.x, v.y);
+            } else {
+                bq = ktile[bbase + gi * 16 + kk * 4];
+            }
             d = mfma16x16x32(gfrag[0][kk][lane], bq, d);
             d = mfma16x16x32(gfrag[1][kk][lane], bq, d);
+        }
+        if constexpr (F8) {
+            const float ks = reinterpret_cast<const float*>(ktile + 512)[4 * c + gi];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[e] *= ks;
         }
         float* dst = reinterpret_cast<float*>(&gk[buf][j][0][0]);
 #pragma unroll
@@ -813,7 +959,10 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         issue(nb, tile + 3);
         const int kbase = tile * kPfTile;
         if (kbase <= tw) {
-            pair_scores(ka, kb, kbase + kPfTile <= tw);
+            if constexpr (F8)
+                pair_scores8(ka, kb, kbase + kPfTile <= tw);
+            else
+                pair_scores(ka, kb, kbase + kPfTile <= tw);
             pend_base = kbase;  // keys past a row's last legal one are never kept
             pend_buf = buf;
         }
@@ -887,12 +1036,25 @@ hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
     const int batch = rows / a.T;
     const dim3 grid((unsigned)(((a.T + 7) / 8 + 1) / 2), (unsigned)batch);
     const int nht = (a.H + 15) / 16;
+    const dim3 block(64 * kPfWaves);
+    if (a.codes) {
+        if (!a.kscale) return hipErrorInvalidValue;
+        prof_begin(K_PREFILL_FP8, s);
+        switch (nht) {
+            case 1: sa_launch(prefill_kernel<1, true>, grid, block, 0, s, a); break;
+            case 2: sa_launch(prefill_kernel<2, true>, grid, block, 0, s, a); break;
+            case 3: sa_launch(prefill_kernel<3, true>, grid, block, 0, s, a); break;
+            default: sa_launch(prefill_kernel<4, true>, grid, block, 0, s, a); break;
+        }
+        prof_end(K_PREFILL_FP8, s);
+        return hipGetLastError();
+    }
     prof_begin(K_PREFILL, s);
     switch (nht) {
-        case 1: sa_launch(prefill_kernel<1>, grid, dim3(64 * kPfWaves), 0, s, a); break;
-        case 2: sa_launch(prefill_kernel<2>, grid, dim3(64 * kPfWaves), 0, s, a); break;
-        case 3: sa_launch(prefill_kernel<3>, grid, dim3(64 * kPfWaves), 0, s, a); break;
-        default: sa_launch(prefill_kernel<4>, grid, dim3(64 * kPfWaves), 0, s, a); break;
+        case 1: sa_launch(prefill_kernel<1, false>, grid, block, 0, s, a); break;
+        case 2: sa_launch(prefill_kernel<2, false>, grid, block, 0, s, a); break;
+        case 3: sa_launch(prefill_kernel<3, false>, grid, block, 0, s, a); break;
+        default: sa_launch(prefill_kernel<4, false>, grid, block, 0, s, a); break;
     }
     prof_end(K_PREFILL, s);
     return hipGetLastError();

@@ -194,6 +194,7 @@ enum KernelId {
     K_TIDY,
     K_SCAN8Q,
     K_SCAN_POOL,
+    K_PREFILL_FP8,
     K_COUNT
 };
 
@@ -374,6 +375,11 @@ struct PrefillArgs {
     // Ragged batches: per-sequence key counts [batch] (clamped to [T, L]); the
     // rows of sequence b sit at seq_lens[b] - T + i instead of offset + i.
     const int32_t* seq_lens;
+    // FP8 key cache (keys unused): E4M3 codes [batch, L, 128] and one fp32
+    // scale per key [batch, L]; the query is quantized to E4M3 in the kernel
+    // (per head, the key rule) and the contraction runs on the fp8 MFMA.
+    const uint8_t* codes;
+    const float* kscale;
 };
 
 // Launchers (defined next to their kernels).

@@ -127,4 +127,91 @@ __device__ __forceinline__ void load_key(uint4 (&b)[KSTEPS], const uint16_t* kp,
     for (int kk = 0; kk < KSTEPS; ++kk) b[kk] = ldg16(kp + (kk * 4 + g) * 8);
 }
 
+// ------------------------------------------------------ E4M3 operands
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// q codes for the fp8 MFMA: per head tile, lane (c, g) holds 32 codes of head
+// ht*16 + c, dims 32g .. 32g+31, the same dims as the key operand of lane g.
+template <int NHT>
+struct QFrag8 {
+    i32x8 a[NHT];
+    float wv[NHT][4];
+};
+
+// Codes of a head vector in LDS: [head][8 chunks of 16 codes], chunk m of
+// head h in slot h*8 + (m ^ (h & 7)).
+__device__ __forceinline__ int qslot(int h, int m) { return h * 8 + (m ^ (h & 7)); }
+
+// A fragments from the LDS codes, and the weights folded with the scales.
+template <int NHT>
+__device__ __forceinline__ void load_qfrag_fp8(QFrag8<NHT>& f, const uint4* qcode,
+                                               const float* qscale, const float* wrow, int H,
+                                               int g, int c) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+        const int h = ht * 16 + c;
+        const uint4 lo = qcode[qslot(h, 2 * g)], hi = qcode[qslot(h, 2 * g + 1)];
+        f.a[ht] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hw = ht * 16 + 4 * g + i;
+            f.wv[ht][i] = hw < H ? wrow[hw] * qscale[hw] : 0.f;
+        }
+    }
+}
+
+// One wave quantizes a query row's head vectors by the key-cache rule: lane h
+// takes head h (all 128 dims), scale b = max|q| / 448 (1 for a zero vector),
+// codes of q / b (fp32 division) clamped to +-448 and rounded to nearest even,
+// into qcode (qslot layout) and b into qscale.  Heads at or past H get zero
+// codes and scale 1.
+__device__ __forceinline__ void quantize_q8_wave(const uint16_t* qrow, int H, uint4* qcode,
+                                                 float* qscale) {
+    const int h = lane_id();
+    uint4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        v[i] = h < H ? ldg16(qrow + h * kD + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t wds[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m = fmaxf(m, fmaxf(fabsf(bf16_bits_to_f32(wds[e] & 0xffffu)),
+                               fabsf(bf16_bits_to_f32(wds[e] >> 16))));
+    }
+    const float b = m > 0.f ? m / 448.0f : 1.0f;
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+        const uint32_t wds[8] = {v[2 * mm].x, v[2 * mm].y, v[2 * mm].z, v[2 * mm].w,
+                                 v[2 * mm + 1].x, v[2 * mm + 1].y, v[2 * mm + 1].z,
+                                 v[2 * mm + 1].w};
+        uint32_t out[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float y[4];
+            y[0] = bf16_bits_to_f32(wds[2 * u] & 0xffffu);
+            y[1] = bf16_bits_to_f32(wds[2 * u] >> 16);
+            y[2] = bf16_bits_to_f32(wds[2 * u + 1] & 0xffffu);
+            y[3] = bf16_bits_to_f32(wds[2 * u + 1] >> 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(y[e] / b, -448.0f), 448.0f);
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], pk, true);
+            out[u] = (uint32_t)pk;
+        }
+        qcode[qslot(h, mm)] = make_uint4(out[0], out[1], out[2], out[3]);
+    }
+    qscale[h] = b;
+}
+
+// 16 keys x 16 heads x 128 dims in E4M3, fp32 accumulate (no block scales).
+__device__ __forceinline__ f32x4 mfma16x16x128_fp8(const i32x8& a, const i32x8& b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                            0, 0, 0, 0, 0, 0);
+}
+
 }  // namespace sa

@@ -43,20 +43,6 @@ constexpr int kBufFlags = 0x00020000;       // raw buffer, 32-bit elements
 constexpr int kNontemporal = 2;             // cache policy bit of a streaming load
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-// q codes for the fp8 MFMA: per head tile, lane (c, g) holds 32 codes of head
-// ht*16 + c, dims 32g .. 32g+31, the same dims as the key operand of lane g.
-template <int NHT>
-struct QFrag8 {
-    i32x8 a[NHT];
-    float wv[NHT][4];
-};
-
-// Codes of a head vector in LDS: [head][8 chunks of 16 codes], chunk m of
-// head h in slot h*8 + (m ^ (h & 7)).
-__device__ __forceinline__ int qslot(int h, int m) { return h * 8 + (m ^ (h & 7)); }
-
 // The workgroup (512 threads: 8 per head, 16 dims each) quantizes the query
 // row's head vectors into LDS: scale b = max|q| / 448 (1 for a zero vector),
 // codes of q / b clamped to +-448 and rounded to nearest even.  Heads at or
@@ -96,31 +82,6 @@ __device__ __forceinline__ void quantize_q8(const uint16_t* qrow, int H, uint4* 
     }
     qcode[qslot(h, part)] = make_uint4(out[0], out[1], out[2], out[3]);
     if (part == 0) qscale[h] = b;
-}
-
-// A fragments from the LDS codes, and the weights folded with the scales.
-template <int NHT>
-__device__ __forceinline__ void load_qfrag_fp8(QFrag8<NHT>& f, const uint4* qcode,
-                                               const float* qscale, const float* wrow, int H,
-                                               int g, int c) {
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-        const int h = ht * 16 + c;
-        const uint4 lo = qcode[qslot(h, 2 * g)], hi = qcode[qslot(h, 2 * g + 1)];
-        f.a[ht] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hw = ht * 16 + 4 * g + i;
-            f.wv[ht][i] = hw < H ? wrow[hw] * qscale[hw] : 0.f;
-        }
-    }
-}
-
-// 16 keys x 16 heads x 128 dims in E4M3, fp32 accumulate (no block scales).
-__device__ __forceinline__ f32x4 mfma16x16x128_fp8(const i32x8& a, const i32x8& b) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, f32x4{0.f, 0.f, 0.f, 0.f},
-                                                            0, 0, 0, 0, 0, 0);
 }
 
 // q fragments in the permuted dim order: head tile ht, row c = head slot

@@ -410,3 +410,13 @@ def smoke_run(device):
     print("smoke ok: DSA, FP8 keys (q bf16 and E4M3; MISA-dagger and HISA too), MISA-dagger, "
           "HISA, LISA, ResMiSA, MISA x HISA, tidy-up, "
           "ragged batches and the fused prefill match the oracle")
+
+
+def prefill_group_rows(T, seed):
+    """One random row of each 8-row group: the fused prefill's workgroup x
+    runs group x (its short causal range) and group G - 1 - x (its long one),
+    so this covers both groups of every workgroup."""
+    rng = np.random.default_rng(seed)
+    G = (T + 7) // 8
+    return np.array(sorted(min(8 * g + int(rng.integers(0, 8)), T - 1) for g in range(G)),
+                    dtype=np.int32)

@@ -157,6 +157,11 @@ def test_new_entry_points_validate(api):
     assert lib.indexer_score_topk_fp8_ws(ctypes.byref(s), ctypes.byref(n)) == api.SA_OK
     s16 = shape(api, T=16, causal_offset=4080)
     assert lib.indexer_score_topk_fp8_ws(ctypes.byref(s16), ctypes.byref(n)) == api.SA_EUNSUPPORTED
+    # with the query in E4M3, prefill rows take the fused prefill
+    assert lib.indexer_score_topk_fp8q_ws(ctypes.byref(s16), ctypes.byref(n)) == api.SA_OK
+    n16 = n.value
+    assert lib.indexer_score_topk_ws(ctypes.byref(s16), ctypes.byref(n)) == api.SA_OK
+    assert n16 == n.value
     assert lib.sa_quantize_keys_fp8(p, 1, 10, 64, p, p, None) == api.SA_EUNSUPPORTED
     assert lib.sa_quantize_keys_fp8(None, 1, 10, 128, p, p, None) == api.SA_EINVAL
     # ResMiSA: 0 <= r <= H and 4 + r <= 64 unless r == H
@@ -200,12 +205,11 @@ def test_new_entry_points_validate(api):
     assert lib.indexer_score_topk_fp8_ragged_ws(ctypes.byref(s), ctypes.byref(n)) == api.SA_OK
     assert lib.indexer_score_topk_fp8_ragged_ws(ctypes.byref(s3), ctypes.byref(n)) == \
         api.SA_EINVAL
+    # prefill rows: sized for the fused prefill (a bf16 query is refused by the call)
     assert lib.indexer_score_topk_fp8_ragged_ws(ctypes.byref(s16r), ctypes.byref(n)) == \
-        api.SA_EUNSUPPORTED
+        api.SA_OK
     assert lib.indexer_score_topk_fp8_ragged(p, p, p, p, None, 0, 0, ctypes.byref(s), p, None, p,
                                              16, None) == api.SA_EINVAL
-    assert lib.indexer_score_topk_fp8q_ws(ctypes.byref(s16), ctypes.byref(n)) == \
-        api.SA_EUNSUPPORTED
     # tidy-up: k <= 4096 unless a slot bound <= 2^18 is given
     assert lib.sa_tidy_indices(p, 4, 1, 5000, None, 0, 64, 0, p, None, None) == \
         api.SA_EUNSUPPORTED

@@ -23,7 +23,8 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import _np, check_dsa_fp8, check_dsa_fp8q, check_hisa, check_misa, rows_of, to_device
+from parity import (_np, check_dsa_fp8, check_dsa_fp8q, check_hisa, check_misa,
+                    prefill_group_rows, rows_of, to_device)
 from sparse_attention_token_dsa_amd import synth
 
 torch = pytest.importorskip("torch")
@@ -236,14 +237,67 @@ def test_dsa_fp8q_128k(api):
     check_dsa_fp8q(p, _np(codes), _np(scales), 2048, _np(idx), _np(sc), rows_of(p))
 
 
-def test_dsa_fp8q_rejects_prefill_rows(api):
-    say("dsa fp8q T=16 rejected")
-    p = synth.make_problem(421, Bt=1, T=16, L=100, H=16)
+# ------------------------------------------- FP8 prefill (fused, fp8 MFMA)
+
+def _fp8q_prefill(api, p, k):
     codes, scales = oracle.quantize_keys_fp8(p["K"])
     q, w, _ = to_device(p, DEV)
+    idx, sc = api.indexer_score_topk_fp8q(q, w, torch.from_numpy(codes).to(DEV),
+                                          torch.from_numpy(scales).to(DEV), p["offset"], k)
+    torch.cuda.synchronize()
+    return codes, scales, _np(idx), _np(sc)
+
+
+@pytest.mark.parametrize("Bt,T,L,H,k", [
+    (1, 16, 100, 16, 8),           # the smallest prefill chunk
+    (1, 1024, 1024, 64, 128),      # the whole sequence as one chunk
+    (2, 200, 3000, 64, 257),       # ragged tail of 8-row groups and 64-key tiles
+    (1, 96, 20000, 32, 2048),      # H = 32, k above the LDS candidate buffer
+    (1, 120, 2500, 40, 100),       # H = 40: three head tiles, the last partial
+    (1, 40, 700, 1, 50),           # a single head
+])
+def test_dsa_fp8q_prefill(api, Bt, T, L, H, k):
+    say("dsa fp8q prefill Bt=%d T=%d L=%d H=%d k=%d" % (Bt, T, L, H, k))
+    p = synth.make_problem(440 + L % 83, Bt=Bt, T=T, L=L, H=H, needles=8, needle_mode="rows")
+    codes, scales, idx, sc = _fp8q_prefill(api, p, k)
+    check_dsa_fp8q(p, codes, scales, k, idx, sc, rows_of(p))
+
+
+def test_dsa_fp8q_prefill_bounded_lists(api):
+    # More legal keys than list slots: the lists are compacted while sweeping.
+    say("dsa fp8q prefill bounded lists")
+    T, L, H, k = 64, 40000, 16, 100
+    shape = api.Shape(1, T, H, 128, L, L - T, k)
+    assert api.indexer_score_topk_fp8q_ws(shape) < T * L * 8
+    p = synth.make_problem(447, Bt=1, T=T, L=L, H=H, offset=L - T, needles=8,
+                           needle_mode="rows")
+    codes, scales, idx, sc = _fp8q_prefill(api, p, k)
+    check_dsa_fp8q(p, codes, scales, k, idx, sc, rows_of(p))
+
+
+def test_dsa_fp8q_prefill_chunked_rows(api):
+    # The chunked-prefill workload (4096 queries over 28672 cached keys) on
+    # the FP8 cache; one row of every eighth 8-row group checked.
+    say("dsa fp8q prefill_chunked 64 rows")
+    p = synth.make_config("prefill_chunked")
+    q, w, K = to_device(p, DEV)
+    codes, scales = api.quantize_keys_fp8(K)
+    idx, sc = api.indexer_score_topk_fp8q(q, w, codes, scales, p["offset"], 2048)
+    torch.cuda.synchronize()
+    rows = prefill_group_rows(p["T"], 5)[::8]
+    check_dsa_fp8q(p, _np(codes), _np(scales), 2048, _np(idx), _np(sc), rows)
+
+
+def test_dsa_fp8_bf16_query_rejects_prefill_rows(api):
+    say("dsa fp8 ragged T=16 with a bf16 query rejected")
+    p = synth.make_problem(422, Bt=2, T=16, L=100, H=16, offset=84)
+    codes, scales = oracle.quantize_keys_fp8(p["K"])
+    q, w, _ = to_device(p, DEV)
+    lens = torch.tensor([100, 50], dtype=torch.int32, device=DEV)
     with pytest.raises(api.SaError) as e:
-        api.indexer_score_topk_fp8q(q, w, torch.from_numpy(codes).to(DEV),
-                                    torch.from_numpy(scales).to(DEV), p["offset"], 8)
+        api.indexer_score_topk_fp8_ragged(q, w, torch.from_numpy(codes).to(DEV),
+                                          torch.from_numpy(scales).to(DEV), lens, 8,
+                                          q_fp8=False)
     assert e.value.code == api.SA_EUNSUPPORTED
 
 
@@ -327,10 +381,12 @@ def test_misa_hisa_fp8_128k(api):
     check_hisa(p, 2048, 128, 64, _np(idx), _np(sc), _np(blocks), rows_of(p), fp8=fp8)
 
 
-@pytest.mark.parametrize("q_fp8", [False, True])
-@pytest.mark.parametrize("Bt,T,L,H,k,lens", [
-    (4, 1, 20000, 64, 512, [20000, 9001, 37, 1]),
-    (3, 3, 5000, 32, 100, [5000, 1200, 3]),
+@pytest.mark.parametrize("Bt,T,L,H,k,lens,q_fp8", [
+    (4, 1, 20000, 64, 512, [20000, 9001, 37, 1], False),
+    (4, 1, 20000, 64, 512, [20000, 9001, 37, 1], True),
+    (3, 3, 5000, 32, 100, [5000, 1200, 3], False),
+    (3, 3, 5000, 32, 100, [5000, 1200, 3], True),
+    (3, 32, 5000, 64, 100, [5000, 1200, 40], True),   # prefill rows: the fused prefill
 ])
 def test_dsa_fp8_ragged(api, Bt, T, L, H, k, lens, q_fp8):
     # Each sequence against the oracle's FP8 DSA on its own prefix.

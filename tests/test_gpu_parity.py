@@ -18,6 +18,7 @@ import pytest
 import oracle
 import parity
 from parity import (_np, check_dsa, check_guards, check_hisa, check_misa, guarded_outputs,
+                    prefill_group_rows,
                     rows_of, to_device)
 from sparse_attention_token_dsa_amd import synth
 
@@ -210,16 +211,6 @@ def test_decode_32k_all_rows(api):
     p = synth.make_config("decode_32k")
     idx, sc = run_dsa(api, p, 2048)
     check_dsa(p, 2048, idx, sc, rows_of(p))
-
-
-def prefill_group_rows(T, seed):
-    """One random row of each 8-row group: the fused prefill's workgroup x
-    runs group x (its short causal range) and group G - 1 - x (its long one),
-    so this covers both groups of every workgroup."""
-    rng = np.random.default_rng(seed)
-    G = (T + 7) // 8
-    return np.array(sorted(min(8 * g + int(rng.integers(0, 8)), T - 1) for g in range(G)),
-                    dtype=np.int32)
 
 
 def test_prefill_chunked_rows(api):
