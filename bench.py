@@ -73,12 +73,12 @@ def measured_traffic(kernel, digest):
     return e.get("bytes_per_launch")
 
 
-def measured_mfma(digest):
+def measured_mfma(digest, key="prefill_fused_mfma"):
     """Counter-derived MFMA figures of the fused prefill (rocprofv3 --pmc,
     see traffic.py), or None if taken on a different kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            e = json.load(f).get("prefill_fused_mfma")
+            e = json.load(f).get(key)
     except (OSError, ValueError):
         return None
     if not e or e.get("source_digest") != digest:
@@ -323,7 +323,8 @@ def main():
         "kernel": "scan_dsa_pool", "cache": "cold", "avg_us": pus,
         "algorithmic_bytes_per_launch": scan_bytes + Bt * (L // b + L // B) * 4 * d,
         "frac": round((scan_bytes + Bt * (L // b + L // B) * 4 * d) / (pus * 1e-6) / 1e9
-                      / HBM_PEAK_GBS, 4)}
+                      / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic("scan_dsa_pool", digest)}
     other_hbm = {}
     for name, nbytes in (("scan_routed", wl.scan_bytes(rows, Bt, L, h, d)),
                          ("scan_dsa_pool", wl.scan_bytes(rows, Bt, L, H, d)
@@ -332,7 +333,9 @@ def main():
             us = kernels[name]["avg_us"]
             gbs = nbytes / (us * 1e-6) / 1e9
             other_hbm[name] = {"cache": "warm", "avg_us": round(us, 2), "GB/s": round(gbs, 1),
-                               "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                               "frac": round(gbs / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes_per_launch": nbytes,
+                               "traffic": measured_traffic(name, digest)}
 
     result = {
         "metric": METRIC, "value": value, "unit": "scores/s", "n_gpus": 1,
@@ -803,6 +806,7 @@ def bench_prefill_fp8q(api, torch, dev, q, w, K, shape, oi, osc, iters, flops, p
     to E4M3 in the kernel (indexer_score_topk_fp8q): the contraction on the
     16x16x128 fp8 MFMA, against the dense fp8 peak."""
     T, off, k = shape.T, shape.causal_offset, shape.topk
+    digest = source_digest(["prefill.hip", "sa_frag.h", "sa_common.h"])
     codes, scales = api.quantize_keys_fp8(K)
     ws = torch.empty(api.indexer_score_topk_fp8q_ws(shape), dtype=torch.uint8, device=dev)
 
@@ -828,8 +832,10 @@ def bench_prefill_fp8q(api, torch, dev, q, w, K, shape, oi, osc, iters, flops, p
             "roofline": {"kernel": "prefill_fused_fp8q", "bound": "mfma",
                          "achieved": round(tflops, 1), "peak": FP8_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / FP8_PEAK_TFLOPS, 4),
-                         "traffic": None, "algorithmic_flops_per_launch": flops,
-                         "vs_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}}
+                         "traffic": measured_traffic("prefill_fused_fp8q", digest),
+                         "algorithmic_flops_per_launch": flops,
+                         "vs_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "counters": measured_mfma(digest, "prefill_fused_fp8q_mfma")}}
 
 
 def bench_prefill_ragged(api, synth, torch, np, dev, iters):
