@@ -32,6 +32,7 @@ constexpr int kFilterThreads = 512;
 // decode rows against 10.8 us at 4096).
 constexpr int kFilterChunk = 8192;
 constexpr int kLdsCand = 4096;           // keys per LDS candidate buffer
+constexpr int kBatch = 8;                // keys per thread in flight in a pass over a source
 
 __device__ __forceinline__ unsigned long long make_key(float sc, int idx) {
     return ((unsigned long long)ord_key(sc) << 32) | (unsigned long long)(~(uint32_t)idx);
@@ -61,9 +62,10 @@ __device__ __forceinline__ int dense_len(const TopkArgs& a, int row) {
 // the count above it and the count on it for the finishing kernel.
 __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
                                                                      unsigned long long* cand) {
-    __shared__ int s_idx[kFilterChunk];
-    __shared__ float s_sc[kFilterChunk];
-    __shared__ unsigned long long s_cand[kFilterChunk];
+    // Winners (from the front) and candidates (from the back) staged as keys
+    // in one buffer: each score is at most one of them.  64 KiB, so the
+    // filter fits beside a key scan's workgroup on the same CU.
+    __shared__ unsigned long long s_buf[kFilterChunk];
     __shared__ int s_ne, s_nc, s_base[2];
     __shared__ int s_wave[kFilterThreads / 64];
     __shared__ Thresh th;
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     const int lo = blockIdx.x * kFilterChunk;
     if (lo >= n) return;
     const int hi = min(lo + kFilterChunk, n);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(s_cand);  // 16 KiB, reused below
+    uint32_t* hist = reinterpret_cast<uint32_t*>(s_buf);  // 16 KiB, reused below
     const uint32_t* grow = a.state + (long long)row * kRowState;
     for (int x = tid; x < kHist0Bins; x += kFilterThreads) hist[x] = grow[x];
     lds_barrier();
@@ -136,12 +138,8 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
         const int u = lo + (tid + (j >> 2) * kFilterThreads) * 4 + (j & 3);
-        if (emask & (1u << j)) {
-            s_idx[se] = u;
-            s_sc[se] = vs[j];
-            ++se;
-        }
-        if (cmask & (1u << j)) s_cand[sc2++] = make_key(vs[j], u);
+        if (emask & (1u << j)) s_buf[se++] = make_key(vs[j], u);
+        if (cmask & (1u << j)) s_buf[kFilterChunk - 1 - sc2++] = make_key(vs[j], u);
     }
     lds_barrier();
     if (tid == 0) {
@@ -154,14 +152,15 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     for (int x = tid; x < s_ne; x += kFilterThreads) {
         const int slot = s_base[0] + x;
         if (slot < need) {
-            oidx[slot] = s_idx[x];
-            if (osc) osc[slot] = s_sc[x];
+            const unsigned long long key = s_buf[x];
+            oidx[slot] = key_idx(key);
+            if (osc) osc[slot] = key_score(key);
         }
     }
     unsigned long long* crow = cand + (long long)row * a.cand_cap;
     for (int x = tid; x < s_nc; x += kFilterThreads) {
         const long long cs = (long long)s_base[1] + x;
-        if (cs < a.cand_cap) crow[cs] = s_cand[x];
+        if (cs < a.cand_cap) crow[cs] = s_buf[kFilterChunk - 1 - x];
     }
 }
 
@@ -288,11 +287,14 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
     const uint32_t span = omax - omin;
     // significant bits of the relative key: the score part's, then 32 index bits
     int pos = 32 + (span ? 32 - __clz(span) : 0);
-    unsigned long long rk[kRegKeys];
+    // the keys become relative in place; okey() gives back the plain key
 #pragma unroll
     for (int j = 0; j < kRegKeys; ++j)
-        rk[j] = ((unsigned long long)((uint32_t)(kr[j] >> 32) - omin) << 32) |
+        kr[j] = ((unsigned long long)((uint32_t)(kr[j] >> 32) - omin) << 32) |
                 (kr[j] & 0xffffffffull);
+    auto okey = [&](unsigned long long r) {
+        return ((unsigned long long)((uint32_t)(r >> 32) + omin) << 32) | (r & 0xffffffffull);
+    };
     const unsigned long long below = (1ull << lane) - 1ull;
     for (int level = 0; pos > 0; ++level) {
         const int width = level == 0 ? kHist0Bits : 10;
@@ -304,7 +306,7 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < kRegKeys; ++j)
-            if ((alive >> j) & 1u) atomicAdd(&S.hist[(uint32_t)((rk[j] >> shift) & mask)], 1u);
+            if ((alive >> j) & 1u) atomicAdd(&S.hist[(uint32_t)((kr[j] >> shift) & mask)], 1u);
         lds_barrier();
         find_threshold<kTopkThreads>(S.hist, hbins, need_rem, S.wave, &S.th);
         const uint32_t d = (uint32_t)S.th.dstar;
@@ -312,17 +314,14 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         const int eq = S.th.eq;
         const bool take_all = gt + eq == need_rem;
         // winners of this level: one LDS atomic per wave for all its keys
-        unsigned long long m[kRegKeys];
+        // (the ballots are taken twice rather than held)
+        auto emits = [&](int j) {
+            const uint32_t dig = (uint32_t)((kr[j] >> shift) & mask);
+            return ((alive >> j) & 1u) && (dig > d || (take_all && dig == d));
+        };
         int wtot = 0;
 #pragma unroll
-        for (int j = 0; j < kRegKeys; ++j) {
-            const uint32_t dig = (uint32_t)((rk[j] >> shift) & mask);
-            const bool in = (alive >> j) & 1u;
-            const bool emit = in && (dig > d || (take_all && dig == d));
-            m[j] = __ballot(emit);
-            wtot += __popcll(m[j]);
-            if (!(in && dig == d)) alive &= ~(1u << j);
-        }
+        for (int j = 0; j < kRegKeys; ++j) wtot += __popcll(__ballot(emits(j)));
         int base = 0;
         if (wtot) {
             if (lane == 0) base = atomicAdd(&S.out, wtot);
@@ -330,15 +329,22 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         }
 #pragma unroll
         for (int j = 0; j < kRegKeys; ++j) {
-            if ((m[j] >> lane) & 1ull) {
-                const int slot = base + __popcll(m[j] & below);
+            const bool e = emits(j);
+            const unsigned long long m = __ballot(e);
+            if (e) {
+                const int slot = base + __popcll(m & below);
                 if (slot < need) {
-                    oidx[slot] = key_idx(kr[j]);
-                    if (osc) osc[slot] = key_score(kr[j]);
+                    const unsigned long long key = okey(kr[j]);
+                    oidx[slot] = key_idx(key);
+                    if (osc) osc[slot] = key_score(key);
                 }
             }
-            base += __popcll(m[j]);
+            base += __popcll(m);
         }
+        // keys on the threshold digit stay alive
+#pragma unroll
+        for (int j = 0; j < kRegKeys; ++j)
+            if ((uint32_t)((kr[j] >> shift) & mask) != d) alive &= ~(1u << j);
         need_rem -= gt;
         if (take_all) return;
         if (eq <= kRankMax) {
@@ -346,13 +352,9 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
             // and place each by its rank among them (keys are distinct).
             if (tid == 0) S.cand = 0;
             lds_barrier();
-            unsigned long long cm[kRegKeys];
             int ctot = 0;
 #pragma unroll
-            for (int j = 0; j < kRegKeys; ++j) {
-                cm[j] = __ballot((alive >> j) & 1u);
-                ctot += __popcll(cm[j]);
-            }
+            for (int j = 0; j < kRegKeys; ++j) ctot += __popcll(__ballot((alive >> j) & 1u));
             int cbase = 0;
             if (ctot) {
                 if (lane == 0) cbase = atomicAdd(&S.cand, ctot);
@@ -360,8 +362,10 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
             }
 #pragma unroll
             for (int j = 0; j < kRegKeys; ++j) {
-                if ((cm[j] >> lane) & 1ull) S.lbuf[0][cbase + __popcll(cm[j] & below)] = kr[j];
-                cbase += __popcll(cm[j]);
+                const bool al = (alive >> j) & 1u;
+                const unsigned long long cm = __ballot(al);
+                if (al) S.lbuf[0][cbase + __popcll(cm & below)] = kr[j];
+                cbase += __popcll(cm);
             }
             lds_barrier();
             const int done = need - need_rem;  // winners already written
@@ -378,8 +382,9 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
                 }
                 for (; o < eq; ++o) rank += S.lbuf[0][o] > key;
                 if (rank < need_rem) {
-                    oidx[done + rank] = key_idx(key);
-                    if (osc) osc[done + rank] = key_score(key);
+                    const unsigned long long ok = okey(key);
+                    oidx[done + rank] = key_idx(ok);
+                    if (osc) osc[done + rank] = key_score(ok);
                 }
             }
             return;
@@ -449,10 +454,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
     } else {
         for (int x = tid; x < kHist0Bins; x += kTopkThreads) S.hist[x] = 0u;
         lds_barrier();
-        for (int u = tid; u < nsrc0; u += kTopkThreads) {
-            bool valid = true;
-            const unsigned long long key = src_key(kind, dsrc, lsc, lid, nullptr, u, valid);
-            if (valid) atomicAdd(&S.hist[(uint32_t)(key >> kShift[0])], 1u);
+        for (int ub = 0; ub < nsrc0; ub += kTopkThreads * kBatch) {
+            unsigned long long kb[kBatch];
+            bool vb[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int u = ub + j * kTopkThreads + tid;
+                vb[j] = u < nsrc0;
+                kb[j] = vb[j] ? src_key(kind, dsrc, lsc, lid, nullptr, u, vb[j]) : 0ull;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j)
+                if (vb[j]) atomicAdd(&S.hist[(uint32_t)(kb[j] >> kShift[0])], 1u);
         }
         lds_barrier();
         int local = 0;
@@ -482,16 +495,28 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         if (!hist_ready) {
             for (int x = tid; x < nbins; x += kTopkThreads) S.hist[x] = 0u;
             lds_barrier();
-            for (int u = tid; u < nsrc; u += kTopkThreads) {
-                bool valid = true;
-                unsigned long long key;
-                if (cur_lds >= 0) {
-                    key = S.lbuf[cur_lds][u];
-                } else {
-                    key = src_key(kind, dsrc, lsc, lid, ksrc, u, valid);
-                    valid = valid && (pfx_shift == 64 || (key >> pfx_shift) == pfx);
+            // kBatch keys per thread loaded before any is used, so a pass over
+            // a global source costs a few memory round trips, not one per key
+            for (int ub = 0; ub < nsrc; ub += kTopkThreads * kBatch) {
+                unsigned long long kb[kBatch];
+                bool vb[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const int u = ub + j * kTopkThreads + tid;
+                    vb[j] = u < nsrc;
+                    kb[j] = 0ull;
+                    if (vb[j]) {
+                        if (cur_lds >= 0) {
+                            kb[j] = S.lbuf[cur_lds][u];
+                        } else {
+                            kb[j] = src_key(kind, dsrc, lsc, lid, ksrc, u, vb[j]);
+                            vb[j] = vb[j] && (pfx_shift == 64 || (kb[j] >> pfx_shift) == pfx);
+                        }
+                    }
                 }
-                if (valid) atomicAdd(&S.hist[(uint32_t)((key >> shift) & mask)], 1u);
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (vb[j]) atomicAdd(&S.hist[(uint32_t)((kb[j] >> shift) & mask)], 1u);
             }
             lds_barrier();
         }
@@ -503,28 +528,37 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         const int dst = cur_lds == 0 ? 1 : 0;
         if (tid == 0) S.cand = 0;
         lds_barrier();
-        for (int ub = 0; ub < nsrc; ub += kTopkThreads) {
-            const int u = ub + tid;
-            bool valid = u < nsrc;
-            unsigned long long key = 0ull;
-            if (valid) {
-                if (cur_lds >= 0) {
-                    key = S.lbuf[cur_lds][u];
-                } else {
-                    key = src_key(kind, dsrc, lsc, lid, ksrc, u, valid);
-                    valid = valid && (pfx_shift == 64 || (key >> pfx_shift) == pfx);
+        for (int ub = 0; ub < nsrc; ub += kTopkThreads * kBatch) {
+            unsigned long long kb[kBatch];
+            bool vb[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int u = ub + j * kTopkThreads + tid;
+                vb[j] = u < nsrc;
+                kb[j] = 0ull;
+                if (vb[j]) {
+                    if (cur_lds >= 0) {
+                        kb[j] = S.lbuf[cur_lds][u];
+                    } else {
+                        kb[j] = src_key(kind, dsrc, lsc, lid, ksrc, u, vb[j]);
+                        vb[j] = vb[j] && (pfx_shift == 64 || (kb[j] >> pfx_shift) == pfx);
+                    }
                 }
             }
-            const uint32_t dig = (uint32_t)((key >> shift) & mask);
-            const bool emit = valid && (dig > d || (take_all && dig == d));
-            const bool app = valid && next_fits && dig == d;
-            const int slot = wave_append(emit, &S.out);
-            if (emit && slot < need) {
-                oidx[slot] = key_idx(key);
-                if (osc) osc[slot] = key_score(key);
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const unsigned long long key = kb[j];
+                const uint32_t dig = (uint32_t)((key >> shift) & mask);
+                const bool emit = vb[j] && (dig > d || (take_all && dig == d));
+                const bool app = vb[j] && next_fits && dig == d;
+                const int slot = wave_append(emit, &S.out);
+                if (emit && slot < need) {
+                    oidx[slot] = key_idx(key);
+                    if (osc) osc[slot] = key_score(key);
+                }
+                const int cslot = wave_append(app, &S.cand);
+                if (app && cslot < kLdsCand) S.lbuf[dst][cslot] = key;
             }
-            const int cslot = wave_append(app, &S.cand);
-            if (app && cslot < kLdsCand) S.lbuf[dst][cslot] = key;
         }
         lds_barrier();
         need_rem -= gt;
