@@ -28,6 +28,15 @@ def test_prefill_workspace_is_below_the_score_matrix(T, L, k):
     dagger = api.misa_route_ws(s, 1024, 8, kp, True)
     heads = T * 8 * (2 * 128 + 4 + 4) + T * (4 * 128 + 1)  # routed q rows, weights, ids; cut-block means
     assert dagger <= T * min(L, max(6 * kp, 8192)) * 8 + T * kp * 12 + heads + (2 << 20)
+    # HISA and MISA x HISA: block scores and the r*b rescored tokens per row
+    b, r = 128, 64
+    lists = T * ((L + b - 1) // b * 4 + r * 4 + r * b * 8)
+    assert api.hisa_coarse_fine_ws(s, b, r, True) <= lists + T * 2 * 128 * 2 + (1 << 20)
+    # (plus the routed heads and the cut-block means of both block sizes)
+    assert api.misa_hisa_ws(s, 1024, 8, b, r, True, True) <= lists + T * (8 * 4 + 2 * 512 + 2) \
+        + (1 << 20)
+    # the fused prefill on the FP8 cache: the same survivor lists as bf16 keys
+    assert api.indexer_score_topk_fp8q_ws(s) == dsa
 
 
 def test_short_rows_keep_every_key():
