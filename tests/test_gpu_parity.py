@@ -233,6 +233,11 @@ def test_prefill_chunked_rows(api):
     (1, 20, 900, 64, 128, 8, 40, 100),     # T >= 16 rows per sequence: the fused prefill
     (1, 256, 4096, 64, 1024, 8, 256, 1024),  # prefill rows, MISA-dagger
     (2, 64, 3000, 32, 512, 4, 100, 0),     # prefill rows, H = 32, partial blocks
+    # decode rows whose blocks are whole (L a multiple of B): routed inside the scan
+    (2, 1, 4096, 64, 512, 24, 100, 0),     # h = 24: two routed head tiles
+    (1, 1, 8192, 40, 1024, 40, 64, 200),   # h = H = 40 (three tiles), MISA-dagger
+    (3, 1, 2048, 16, 256, 3, 50, 100),     # H = 16, h = 3
+    (2, 1, 4096, 64, 4096, 8, 64, 0),      # one block
 ])
 def test_misa(api, Bt, T, L, H, B, h, k, kp):
     say("misa Bt=%d T=%d L=%d H=%d B=%d h=%d k=%d k'=%d" % (Bt, T, L, H, B, h, k, kp))
