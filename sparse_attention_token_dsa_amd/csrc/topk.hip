@@ -19,8 +19,10 @@
 //  * topk_select_kernel -- one 1024-thread workgroup per row for everything
 //    else: candidate arrays left by the filter, short dense rows (block
 //    scores) and (score, index) lists (rescored pools, prefill survivors).
-//    Candidates of later digits are compacted into LDS when they fit; if not,
-//    the source is rescanned with a prefix filter.
+//    Sources of at most 8192 keys are held in registers, with bins fitted
+//    to the range of the keys in play (below); for larger ones, candidates
+//    of later digits are compacted into LDS when they fit, and if not, the
+//    source is rescanned with a prefix filter.
 #include "sa_select.h"
 
 namespace sa {
@@ -169,10 +171,10 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
 enum SrcKind { SRC_DENSE = 0, SRC_LIST = 1, SRC_KEYS = 2 };
 
 struct SelShared {
-    uint32_t hist[kHist0Bins];
+    alignas(16) uint32_t hist[kHist0Bins];
     unsigned long long lbuf[2][kLdsCand];
     int wave[kTopkThreads / 64];
-    uint32_t wmax[kTopkThreads / 64], wmin[kTopkThreads / 64];
+    uint32_t wr[4 * (kTopkThreads / 64)];  // per-wave ranges, by field then wave
     Thresh th;
     int out, cand;
 };
@@ -191,14 +193,58 @@ __device__ __forceinline__ unsigned long long src_key(int kind, const float* dsr
 // Sources of at most kRegKeys keys per thread (rescored lists, block score
 // rows, the filter's candidates): every key is loaded once into registers,
 // all loads in flight together, and the selection runs on the registers.
-// The digits are taken from the key relative to the smallest score present:
-// with r = ord(score) - min ord, the 64-bit key (r << 32 | ~index) orders
-// like the plain key, and its top 12 significant bits split the actual score
-// range evenly (the plain key's top bits hold sign and exponent, which few
-// scores share out).  After a digit level, if at most kRankMax keys sit on
-// the threshold digit, each of them is placed by its exact rank among them.
+// Each level sorts the keys still in play into at most kSelBins bins by a
+// map that never decreases along the key order, finds the bin that holds the
+// need-th largest key, emits the keys above it and keeps the keys in it.  The
+// map comes from the range of the keys in play: while their scores differ,
+// equal slices of the [min, max] score interval (a fixed radix digit of the
+// ordered bits follows the float exponent and puts most scores of a narrow
+// band into one bin); once a slicing level keeps more than half its keys, or
+// the interval is not a usable float range, radix digits of the ordered score
+// bits above the smallest; once the scores are all equal, radix digits of the
+// index part.  When at most kRankMax keys remain, each is placed by its exact
+// rank among them (a cost that grows with the square of their number).
 constexpr int kRegKeys = 8;
-constexpr int kRankMax = 1024;
+constexpr int kRankMax = 256;
+constexpr int kSelBins = 1024;
+
+// Wave 0 finds the bin of a kSelBins-bin histogram (16-byte aligned; bins
+// above the map's range hold zero) that holds the need-th largest key,
+// scanning from the top, into *out.  Each lane takes 16 adjacent bins in
+// four 16-byte reads, all in flight together.  One barrier, after which
+// every thread reads *out.
+__device__ __forceinline__ void wave0_threshold(const uint32_t* hist, int need, Thresh* out) {
+    static_assert(kSelBins == 64 * 16, "16 bins per lane of wave 0");
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        const int base = kSelBins - 16 - 16 * lane;  // lane 0 takes the top bins
+        const uint4* hp = reinterpret_cast<const uint4*>(hist + base);
+        uint32_t v[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 x = hp[c];
+            v[4 * c] = x.x;
+            v[4 * c + 1] = x.y;
+            v[4 * c + 2] = x.z;
+            v[4 * c + 3] = x.w;
+        }
+        int local = 0;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) local += (int)v[j];
+        int cum = wave_incl_scan(local) - local;
+#pragma unroll
+        for (int j = 15; j >= 0; --j) {
+            const int h = (int)v[j];
+            if (cum < need && need <= cum + h) {
+                out->dstar = base + j;
+                out->gt = cum;
+                out->eq = h;
+            }
+            cum += h;
+        }
+    }
+    lds_barrier();
+}
 
 // Largest value over the wave, in every lane (identity 0).
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
@@ -212,12 +258,63 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
+// Each wave publishes the range of its keys in play (score order bits and
+// index part, as maxima of the value and of its complement) and their count;
+// read_range takes them after the next barrier.
+__device__ __forceinline__ void publish_range(const unsigned long long* kr, uint32_t alive,
+                                              SelShared& S) {
+    uint32_t omax = 0u, oinv = 0u, lmax = 0u, linv = 0u;
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kRegKeys; ++j)
+        if ((alive >> j) & 1u) {
+            const uint32_t o = (uint32_t)(kr[j] >> 32), l = (uint32_t)kr[j];
+            omax = o > omax ? o : omax;
+            oinv = ~o > oinv ? ~o : oinv;
+            lmax = l > lmax ? l : lmax;
+            linv = ~l > linv ? ~l : linv;
+            ++cnt;
+        }
+    omax = wave_max_u32(omax);
+    oinv = wave_max_u32(oinv);
+    lmax = wave_max_u32(lmax);
+    linv = wave_max_u32(linv);
+    cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
+    if (lane_id() == 0) {
+        constexpr int NW = kTopkThreads / 64;
+        const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+        S.wr[w] = omax;
+        S.wr[NW + w] = oinv;
+        S.wr[2 * NW + w] = lmax;
+        S.wr[3 * NW + w] = linv;
+        S.wave[w] = cnt;
+    }
+}
+
+// Block-wide range of the keys in play, as wave-uniform values: lane l reads
+// field l / 16 of wave l % 16 (one 4-byte read per lane rather than every
+// thread reading all 64 words), each row of 16 lanes takes its maximum.
+__device__ __forceinline__ void read_range(const SelShared& S, uint32_t& omax, uint32_t& oinv,
+                                           uint32_t& lmax, uint32_t& linv) {
+    static_assert(kTopkThreads / 64 == 16, "one row of 16 lanes per field");
+    const auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    uint32_t x = S.wr[lane_id()];
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));
+    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
+    omax = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+    oinv = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+    lmax = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+    linv = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
                                                     const float* dsrc, const float* lsc,
                                                     const int32_t* lid,
                                                     const unsigned long long* ksrc, int nsrc,
                                                     int32_t* oidx, float* osc, SelShared& S) {
-    const int tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
+    const int tid = threadIdx.x, lane = lane_id();
     const int row = blockIdx.x;
     unsigned long long kr[kRegKeys];
     uint32_t alive = 0u;
@@ -246,36 +343,14 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
     } else if (tid == 0) {
         S.out = 0;
     }
-    // Score range of the keys present, and their count.
-    uint32_t smax = 0u, sinv = 0u;  // max of ord, max of ~ord
-    int cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kRegKeys; ++j)
-        if ((alive >> j) & 1u) {
-            const uint32_t o = (uint32_t)(kr[j] >> 32);
-            smax = o > smax ? o : smax;
-            sinv = ~o > sinv ? ~o : sinv;
-            ++cnt;
-        }
-    smax = wave_max_u32(smax);
-    sinv = wave_max_u32(sinv);
-    cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
-    if (lane == 0) {
-        S.wmax[wid] = smax;
-        S.wmin[wid] = sinv;
-        S.wave[wid] = cnt;
-    }
+    publish_range(kr, alive, S);
+    // the first level's bins (two kSelBins halves of S.hist alternate)
+    for (int x = tid; x < kSelBins; x += kTopkThreads) S.hist[x] = 0u;
     lds_barrier();
-    uint32_t omax = 0u, oinv = 0u;
-    int nvalid = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-        omax = S.wmax[w] > omax ? S.wmax[w] : omax;
-        oinv = S.wmin[w] > oinv ? S.wmin[w] : oinv;
-        nvalid += S.wave[w];
-    }
+    int nalive = lane < kTopkThreads / 64 ? S.wave[lane] : 0;
+    nalive = __builtin_amdgcn_readlane(wave_incl_scan(nalive), 63);
     if (kind != SRC_KEYS) {
-        need = min(a.k, nvalid);
+        need = min(a.k, nalive);
         for (int u = need + tid; u < a.k; u += kTopkThreads) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
@@ -283,73 +358,102 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         if (need <= 0) return;
         need_rem = need;
     }
-    const uint32_t omin = ~oinv;
-    const uint32_t span = omax - omin;
-    // significant bits of the relative key: the score part's, then 32 index bits
-    int pos = 32 + (span ? 32 - __clz(span) : 0);
-    // the keys become relative in place; okey() gives back the plain key
-#pragma unroll
-    for (int j = 0; j < kRegKeys; ++j)
-        kr[j] = ((unsigned long long)((uint32_t)(kr[j] >> 32) - omin) << 32) |
-                (kr[j] & 0xffffffffull);
-    auto okey = [&](unsigned long long r) {
-        return ((unsigned long long)((uint32_t)(r >> 32) + omin) << 32) | (r & 0xffffffffull);
-    };
     const unsigned long long below = (1ull << lane) - 1ull;
-    for (int level = 0; pos > 0; ++level) {
-        const int width = level == 0 ? kHist0Bits : 10;
-        const int shift = pos > width ? pos - width : 0;
-        const int nbins = 1 << (pos - shift);
-        const unsigned long long mask = (unsigned long long)(nbins - 1);
-        const int hbins = nbins < kTopkThreads ? kTopkThreads : nbins;  // bins scanned
-        for (int x = tid; x < hbins; x += kTopkThreads) S.hist[x] = 0u;
-        lds_barrier();
+    uint32_t* hcur = S.hist;
+    uint32_t* hnext = S.hist + kSelBins;
+    bool slice_ok = true;
+    for (;;) {
+        uint32_t omax, oinv, lmax, linv;
+        read_range(S, omax, oinv, lmax, linv);
+        const uint32_t omin = ~oinv, lmin = ~linv;
+        // this level's map (uniform over the block)
+        int mode;  // 0: score slices, 1: score-bit radix, 2: index-bit radix
+        float fmin = 0.f, inv = 0.f;
+        uint32_t base = 0u;
+        int shift = 0, nbins = kSelBins;
+        if (omax != omin) {
+            fmin = ord_to_f32(omin);
+            const float range = ord_to_f32(omax) - fmin;
+            const uint32_t rb = __float_as_uint(range);
+            // finite ends, and a range that is finite and not tiny (so that
+            // kSelBins / range is finite)
+            mode = (slice_ok && omin >= 0x00800000u && omax < 0xff800000u &&
+                    rb >= 0x0da24260u /* 1e-30f */ && rb < 0x7f800000u)
+                       ? 0
+                       : 1;
+            if (mode == 0) {
+                inv = (float)kSelBins / range;
+            } else {
+                base = omin;
+                const uint32_t span = omax - omin;
+                const int bits = 32 - __clz(span);
+                shift = bits > 10 ? bits - 10 : 0;
+                nbins = (int)(span >> shift) + 1;
+            }
+        } else {
+            mode = 2;
+            base = lmin;
+            const uint32_t span = lmax - lmin;
+            const int bits = span ? 32 - __clz(span) : 0;
+            shift = bits > 10 ? bits - 10 : 0;
+            nbins = (int)(span >> shift) + 1;
+        }
+        // (recomputed where used rather than held in registers)
+        auto digit = [&](int j) {
+            if (mode == 0) {
+                // monotone: a rounded difference, a rounded product, truncation
+                const int d = (int)((key_score(kr[j]) - fmin) * inv);
+                return (uint32_t)min(max(d, 0), kSelBins - 1);
+            }
+            const uint32_t v = mode == 1 ? (uint32_t)(kr[j] >> 32) : (uint32_t)kr[j];
+            return (v - base) >> shift;
+        };
 #pragma unroll
         for (int j = 0; j < kRegKeys; ++j)
-            if ((alive >> j) & 1u) atomicAdd(&S.hist[(uint32_t)((kr[j] >> shift) & mask)], 1u);
+            if ((alive >> j) & 1u) atomicAdd(&hcur[digit(j)], 1u);
         lds_barrier();
-        find_threshold<kTopkThreads>(S.hist, hbins, need_rem, S.wave, &S.th);
+        wave0_threshold(hcur, need_rem, &S.th);
         const uint32_t d = (uint32_t)S.th.dstar;
         const int gt = S.th.gt;
         const int eq = S.th.eq;
-        const bool take_all = gt + eq == need_rem;
+        // (one bin: every key in play is the same key, any of them will do)
+        const bool take_all = gt + eq == need_rem || nbins == 1;
         // winners of this level: one LDS atomic per wave for all its keys
         // (the ballots are taken twice rather than held)
         auto emits = [&](int j) {
-            const uint32_t dig = (uint32_t)((kr[j] >> shift) & mask);
-            return ((alive >> j) & 1u) && (dig > d || (take_all && dig == d));
+            const uint32_t g = digit(j);
+            return ((alive >> j) & 1u) && (g > d || (take_all && g == d));
         };
         int wtot = 0;
 #pragma unroll
         for (int j = 0; j < kRegKeys; ++j) wtot += __popcll(__ballot(emits(j)));
-        int base = 0;
+        int obase = 0;
         if (wtot) {
-            if (lane == 0) base = atomicAdd(&S.out, wtot);
-            base = __builtin_amdgcn_readlane(base, 0);
+            if (lane == 0) obase = atomicAdd(&S.out, wtot);
+            obase = __builtin_amdgcn_readlane(obase, 0);
         }
 #pragma unroll
         for (int j = 0; j < kRegKeys; ++j) {
             const bool e = emits(j);
             const unsigned long long m = __ballot(e);
             if (e) {
-                const int slot = base + __popcll(m & below);
+                const int slot = obase + __popcll(m & below);
                 if (slot < need) {
-                    const unsigned long long key = okey(kr[j]);
-                    oidx[slot] = key_idx(key);
-                    if (osc) osc[slot] = key_score(key);
+                    oidx[slot] = key_idx(kr[j]);
+                    if (osc) osc[slot] = key_score(kr[j]);
                 }
             }
-            base += __popcll(m);
+            obase += __popcll(m);
         }
-        // keys on the threshold digit stay alive
+        // keys on the threshold bin stay in play
 #pragma unroll
         for (int j = 0; j < kRegKeys; ++j)
-            if ((uint32_t)((kr[j] >> shift) & mask) != d) alive &= ~(1u << j);
+            if (digit(j) != d) alive &= ~(1u << j);
         need_rem -= gt;
         if (take_all) return;
         if (eq <= kRankMax) {
-            // Few keys left on the threshold digits: compact them into LDS
-            // and place each by its rank among them (keys are distinct).
+            // Few keys left: compact them into LDS and place each by its
+            // rank among them (keys are distinct).
             if (tid == 0) S.cand = 0;
             lds_barrier();
             int ctot = 0;
@@ -373,23 +477,30 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
                 const unsigned long long key = S.lbuf[0][c];
                 int rank = 0;
                 int o = 0;
-                for (; o + 8 <= eq; o += 8) {
-                    unsigned long long v[8];
+                for (; o + 4 <= eq; o += 4) {
+                    unsigned long long v[4];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = S.lbuf[0][o + e];
+                    for (int e = 0; e < 4; ++e) v[e] = S.lbuf[0][o + e];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) rank += v[e] > key;
+                    for (int e = 0; e < 4; ++e) rank += v[e] > key;
                 }
                 for (; o < eq; ++o) rank += S.lbuf[0][o] > key;
                 if (rank < need_rem) {
-                    const unsigned long long ok = okey(key);
-                    oidx[done + rank] = key_idx(ok);
-                    if (osc) osc[done + rank] = key_score(ok);
+                    oidx[done + rank] = key_idx(key);
+                    if (osc) osc[done + rank] = key_score(key);
                 }
             }
             return;
         }
-        pos = shift;
+        // a slicing level that kept most of its keys: radix digits from here
+        if (mode == 0 && 2 * eq > nalive) slice_ok = false;
+        nalive = eq;
+        // the next level's bins, free since the level before this one
+        for (int x = tid; x < kSelBins; x += kTopkThreads) hnext[x] = 0u;
+        uint32_t* t = hcur;
+        hcur = hnext;
+        hnext = t;
+        publish_range(kr, alive, S);
         lds_barrier();
     }
 }

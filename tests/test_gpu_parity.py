@@ -303,6 +303,51 @@ def test_hisa_config(api):
     check_hisa(p, 2048, 128, 64, idx, sc, blocks, rows_of(p))
 
 
+# ------------------------------------------------- score ranges of the select
+
+def _scaled_keys(p, q_scale, key_scale):
+    """q times q_scale, key row i times key_scale[i] (powers of two keep the
+    bf16 mantissas as they were)."""
+    q = synth.bf16_bits_to_f32(p["q"]) * np.float32(q_scale)
+    K = synth.bf16_bits_to_f32(p["K"]) * key_scale.astype(np.float32)[None, :, None]
+    p["q"], p["K"] = synth.to_bf16_bits(q), synth.to_bf16_bits(K)
+    return p
+
+
+def test_select_tiny_score_range(api):
+    # Scores below 1e-32: the span of a row's scores is too small for
+    # equal slices of the score interval, so the selects take radix digits
+    # of the ordered score bits from their first level.
+    say("tiny score range")
+    L = 20000
+    p = _scaled_keys(synth.make_problem(11, Bt=2, T=1, L=L, H=64, needles=8,
+                                        needle_mode="decode"), 2.0 ** -52, np.full(L, 2.0 ** -52))
+    idx, sc = run_dsa(api, p, 2048)
+    assert np.abs(sc).max() < 1e-30
+    check_dsa(p, 2048, idx, sc, rows_of(p))
+    idx, sc, heads, pool = run_misa(api, p, 512, 1024, 8, 2048)
+    check_misa(p, 512, 1024, 8, 2048, idx, sc, heads, pool, rows_of(p))
+    idx, sc, blocks = run_hisa(api, p, 512, 64, 32)
+    check_hisa(p, 512, 64, 32, idx, sc, blocks, rows_of(p))
+
+
+def test_select_scores_over_many_octaves(api):
+    # Key i scaled by 2^-(i mod 40): the scores spread over some 40 octaves,
+    # most of them near the bottom of the interval, so a slicing level keeps
+    # most of its keys and the selects go on with radix digits.
+    say("scores over many octaves")
+    L = 20000
+    p = _scaled_keys(synth.make_problem(12, Bt=2, T=1, L=L, H=64, needles=8,
+                                        needle_mode="decode"), 1.0,
+                     2.0 ** -(np.arange(L) % 40).astype(np.float64))
+    idx, sc = run_dsa(api, p, 2048)
+    check_dsa(p, 2048, idx, sc, rows_of(p))
+    idx, sc, heads, pool = run_misa(api, p, 512, 1024, 8, 2048)
+    check_misa(p, 512, 1024, 8, 2048, idx, sc, heads, pool, rows_of(p))
+    idx, sc, blocks = run_hisa(api, p, 512, 64, 32)
+    check_hisa(p, 512, 64, 32, idx, sc, blocks, rows_of(p))
+
+
 # ----------------------------------------------------------------- pool
 
 @pytest.mark.parametrize("L,block", [(5000, 128), (131072, 1024), (1000, 300)])
