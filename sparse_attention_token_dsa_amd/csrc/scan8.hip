@@ -46,23 +46,23 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // The workgroup (512 threads: 8 per head, 16 dims each) quantizes the query
 // row's head vectors into LDS: scale b = max|q| / 448 (1 for a zero vector),
 // codes of q / b clamped to +-448 and rounded to nearest even.  Heads at or
-// past H get zero codes and scale 1.
-__device__ __forceinline__ void quantize_q8(const uint16_t* qrow, int H, uint4* qcode,
-                                            float* qscale) {
+// past H get zero codes and scale 1.  q8_load issues the thread's two loads
+// (head 0 stands in for absent heads), q8_store quantizes once they landed.
+__device__ __forceinline__ void q8_load(const uint16_t* qrow, int H, uint4& v0, uint4& v1) {
     const int h = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const uint16_t* p = qrow + (h < H ? h : 0) * kD + part * 16;
+    v0 = ldg16(p);
+    v1 = ldg16(p + 8);
+}
+__device__ __forceinline__ void q8_store(const uint4& v0, const uint4& v1, int H, uint4* qcode,
+                                         float* qscale) {
+    const int h = threadIdx.x >> 3, part = threadIdx.x & 7;
+    const uint32_t wds[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     float x[16];
-    if (h < H) {
-        const uint4 v0 = ldg16(qrow + h * kD + part * 16);
-        const uint4 v1 = ldg16(qrow + h * kD + part * 16 + 8);
-        const uint32_t wds[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            x[2 * e] = bf16_bits_to_f32(wds[e] & 0xffffu);
-            x[2 * e + 1] = bf16_bits_to_f32(wds[e] >> 16);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) x[e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+        x[2 * e] = h < H ? bf16_bits_to_f32(wds[e] & 0xffffu) : 0.f;
+        x[2 * e + 1] = h < H ? bf16_bits_to_f32(wds[e] >> 16) : 0.f;
     }
     float m = 0.f;
 #pragma unroll
@@ -87,29 +87,57 @@ __device__ __forceinline__ void quantize_q8(const uint16_t* qrow, int H, uint4* 
 // q fragments in the permuted dim order: head tile ht, row c = head slot
 // ht*16 + c; lane group g of k-step kk holds dims 32g + 8kk .. +8.  A slot is
 // head u itself, or with a routed head list (heads, hsel: MISA's routed
-// scan) the u-th listed head.  Absent slots (past H or hsel) get zero q and
-// zero weight.
+// scan) the u-th listed head.  The head ids come first (the routed list in
+// one batch of loads), then every q / w load back to back with no wait in
+// between; absent slots (past H or hsel) load head 0 and are returned as
+// clear bits of the weight mask, for mask_qfrag8 to zero their weights once
+// the loads have landed (zero weight is enough: their dot products are
+// finite and are multiplied by it).
 template <int NHT>
-__device__ __forceinline__ void load_qfrag8(QFrag<NHT>& f, const uint16_t* qrow,
-                                            const float* wrow, int H, const int32_t* heads,
-                                            int hsel, int g, int c) {
-    const int nh = heads ? hsel : H;
+__device__ __forceinline__ uint32_t load_qfrag8(QFrag<NHT>& f, const uint16_t* qrow,
+                                                const float* wrow, int H,
+                                                const int32_t* heads, int hsel, int g, int c) {
+    int ha[NHT], hw[NHT][4];
+    bool va[NHT], vw[NHT][4];
+    if (heads) {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+            ha[ht] = head_at<true>(ht * 16 + c, H, heads, hsel, va[ht]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hw[ht][i] = head_at<true>(ht * 16 + 4 * g + i, H, heads, hsel, vw[ht][i]);
+        }
+    } else {
+#pragma unroll
+        for (int ht = 0; ht < NHT; ++ht) {
+            ha[ht] = head_at<false>(ht * 16 + c, H, heads, hsel, va[ht]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hw[ht][i] = head_at<false>(ht * 16 + 4 * g + i, H, heads, hsel, vw[ht][i]);
+        }
+    }
+    uint32_t wmask = 0u;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-        const int u = ht * 16 + c;
-        const int h = u < nh ? (heads ? heads[u] : u) : 0;
-        const uint16_t* qp = qrow + h * kD + 32 * g;
+        const uint16_t* qp = qrow + ha[ht] * kD + 32 * g;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = ldg16(qp + 8 * kk);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int uw = ht * 16 + 4 * g + i;
-            f.wv[ht][i] = uw < nh ? wrow[heads ? heads[uw] : uw] : 0.f;
+            f.wv[ht][i] = wrow[hw[ht][i]];
+            if (vw[ht][i]) wmask |= 1u << (4 * ht + i);
         }
-        if (u >= nh)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = make_uint4(0u, 0u, 0u, 0u);
     }
+    return wmask;
+}
+
+template <int NHT>
+__device__ __forceinline__ void mask_qfrag8(QFrag<NHT>& f, uint32_t wmask) {
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (!((wmask >> (4 * ht + i)) & 1u)) f.wv[ht][i] = 0.f;
 }
 
 // MFMA i of a step, then nv VALU instructions of the previous step's head sum.
@@ -150,11 +178,16 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     QFrag8<NHT> f8;
     const uint16_t* qrow = a.q + (long long)row * a.H * kD;
     const float* wrow = a.w + (long long)row * a.H;
+    // The query's loads are issued first and used only after the key
+    // prefetch below is in flight.
+    uint4 qv0, qv1;
+    uint32_t wmask = 0u;
     if constexpr (QF8)
-        quantize_q8(qrow, a.H, qcode, qscale);
+        q8_load(qrow, a.H, qv0, qv1);
     else
-        load_qfrag8<NHT>(f, qrow, wrow, a.H, a.heads ? a.heads + (long long)row * a.hsel : nullptr,
-                         a.hsel, g, c);
+        wmask = load_qfrag8<NHT>(f, qrow, wrow, a.H,
+                                 a.heads ? a.heads + (long long)row * a.hsel : nullptr, a.hsel,
+                                 g, c);
     float (&wv)[NHT][4] = QF8 ? f8.wv : f.wv;
 
     const uint8_t* cbase = a.codes + (long long)b * a.seq_stride + (long long)cs * kD;
@@ -223,12 +256,18 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     };
 
     // Prologue: loads of steps 0 .. kS8Ahead-1 (in flight while the
-    // histogram is cleared), step 0 staged and fetched.
+    // histogram is cleared and the query finished), step 0 staged and
+    // fetched.
 #pragma unroll
     for (int u = 0; u < kS8Ahead; ++u) load(u, u);
     if (HIST)
         for (int x = threadIdx.x; x < kHist0Bins; x += 64 * kS8Waves) lhist[x] = 0u;
-    if (HIST || QF8) __syncthreads();
+    if constexpr (QF8)
+        q8_store(qv0, qv1, a.H, qcode, qscale);
+    else
+        mask_qfrag8<NHT>(f, wmask);
+    // LDS only: a full barrier would also wait for the loads just issued
+    if (HIST || QF8) lds_barrier();
     if constexpr (QF8) load_qfrag_fp8<NHT>(f8, qcode, qscale, wrow, a.H, g, c);
     stage(0, 0);
     fetch(0);
@@ -275,7 +314,7 @@ __global__ __launch_bounds__(64 * kS8Waves) void scan8_kernel(ScanArgs a) {
     const int last = (nsteps + kS8Ring - 1) / kS8Ring * kS8Ring - 1;
     store(head_sum(1), last);
 
-    __syncthreads();
+    lds_barrier();
     float* srow = a.scores + (long long)row * a.score_stride;
     for (int x = threadIdx.x; x < len; x += 64 * kS8Waves) srow[cs + x] = sbuf[x];
     if (HIST) {
