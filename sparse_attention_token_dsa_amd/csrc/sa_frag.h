@@ -35,19 +35,28 @@ __device__ __forceinline__ int head_at(int u, int H, const int32_t* heads, int h
     return valid ? u : 0;
 }
 
-// All head ids first, then every q / w load back to back (no branches), then
-// the zero-masking of absent heads.
+// All head ids first, then every q / w load back to back (no branches).
+// Returns the slots' validity (bit ht: q row of tile ht; bit 8 + 4 ht + i:
+// weight i of tile ht) for mask_qfrag, which zeroes the absent slots once the
+// loads have landed: a caller can issue other loads in between.
 template <int NHT, bool ROUTED = false>
-__device__ __forceinline__ void load_qfrag(QFrag<NHT>& f, const uint16_t* qrow,
-                                           const float* wrow, int H, const int32_t* heads,
-                                           int hsel, int g, int c) {
+__device__ __forceinline__ uint32_t load_qfrag_issue(QFrag<NHT>& f, const uint16_t* qrow,
+                                                     const float* wrow, int H,
+                                                     const int32_t* heads, int hsel, int g,
+                                                     int c) {
     int ha[NHT], hw[NHT][4];
-    bool va[NHT], vw[NHT][4];
+    uint32_t valid = 0u;
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-        ha[ht] = head_at<ROUTED>(ht * 16 + c, H, heads, hsel, va[ht]);
+        bool va;
+        ha[ht] = head_at<ROUTED>(ht * 16 + c, H, heads, hsel, va);
+        if (va) valid |= 1u << ht;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) hw[ht][i] = head_at<ROUTED>(ht * 16 + 4 * g + i, H, heads, hsel, vw[ht][i]);
+        for (int i = 0; i < 4; ++i) {
+            bool vw;
+            hw[ht][i] = head_at<ROUTED>(ht * 16 + 4 * g + i, H, heads, hsel, vw);
+            if (vw) valid |= 1u << (8 + 4 * ht + i);
+        }
     }
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
@@ -56,15 +65,27 @@ __device__ __forceinline__ void load_qfrag(QFrag<NHT>& f, const uint16_t* qrow,
 #pragma unroll
         for (int i = 0; i < 4; ++i) f.wv[ht][i] = wrow[hw[ht][i]];
     }
+    return valid;
+}
+
+template <int NHT>
+__device__ __forceinline__ void mask_qfrag(QFrag<NHT>& f, uint32_t valid) {
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
-        if (!va[ht])
+        if (!((valid >> ht) & 1u))
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) f.a[ht][kk] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (!vw[ht][i]) f.wv[ht][i] = 0.f;
+            if (!((valid >> (8 + 4 * ht + i)) & 1u)) f.wv[ht][i] = 0.f;
     }
+}
+
+template <int NHT, bool ROUTED = false>
+__device__ __forceinline__ void load_qfrag(QFrag<NHT>& f, const uint16_t* qrow,
+                                           const float* wrow, int H, const int32_t* heads,
+                                           int hsel, int g, int c) {
+    mask_qfrag<NHT>(f, load_qfrag_issue<NHT, ROUTED>(f, qrow, wrow, H, heads, hsel, g, c));
 }
 
 // Sum of a value over the 16 lanes of its row (lanes 16g .. 16g+15): four

@@ -38,6 +38,7 @@ struct RouteRegs {
     QFrag<NHT> f;
     uint4 kb[2][8];
     bool valid[2];
+    uint32_t qvalid;  // slots of f, for mask_qfrag in route_finish
 };
 
 template <int NHT>
@@ -53,12 +54,13 @@ __device__ __forceinline__ void route_load_reps(const RouteIn& r, int base, Rout
     }
 }
 
-// Issue the router's first loads (q, w and the first pass of blocks); the
-// caller may issue other loads before route_finish consumes these.
+// Issue the router's first loads (q, w and the first pass of blocks), with
+// nothing that waits for them; the caller may issue other loads before
+// route_finish consumes these.
 template <int NHT>
 __device__ __forceinline__ void route_issue(const RouteIn& r, RouteRegs<NHT>& R) {
     const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
-    load_qfrag<NHT>(R.f, r.q, r.w, r.H, nullptr, 0, g, c);
+    R.qvalid = load_qfrag_issue<NHT>(R.f, r.q, r.w, r.H, nullptr, 0, g, c);
     route_load_reps(r, wid * 16, R, g, c);
 }
 
@@ -68,6 +70,7 @@ template <int NHT>
 __device__ __forceinline__ void route_finish(const RouteIn& r, RouteRegs<NHT>& R, int* s_heads,
                                              float* s_w, uint4* s_q = nullptr) {
     const int lane = lane_id(), wid = threadIdx.x >> 6, g = lane >> 4, c = lane & 15;
+    mask_qfrag<NHT>(R.f, R.qvalid);
     float sum[NHT][4];
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht)
@@ -205,10 +208,6 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
     // extra arithmetic needs the second workgroup's waves to hide latency).
     constexpr int kMaxChunk = POOL ? kScanPoolChunk : kScanMaxChunk;
     __shared__ float sbuf[kMaxChunk];
-    if (HIST) {
-        for (int x = threadIdx.x; x < kHist0Bins; x += NT) lhist[x] = 0u;
-        __syncthreads();
-    }
 
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -343,6 +342,12 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
     RouteIn rin;
     RouteRegs<kRoute ? 4 : 1> rregs;
     const bool route = kRoute && a.route_reps;
+    // Loads in this order: the query (or the router's inputs), the first
+    // key steps, and only then anything that waits for the query.
+    uint32_t qvalid = 0u;
+    if constexpr (!ROUTED)
+        qvalid = load_qfrag_issue<NHT>(f, a.q + (long long)row * a.H * kD,
+                                       a.w + (long long)row * a.H, a.H, nullptr, 0, g, c);
     if constexpr (kRoute) {
         if (route) {
             rin.q = a.q + (long long)row * a.H * kD;
@@ -358,6 +363,12 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
     }
 #pragma unroll
     for (int u = 0; u < NBUF - 1; ++u) loadG(buf[u], base + u * STEP);
+    if (HIST) {
+        // LDS only: the key loads just issued stay in flight
+        for (int x = threadIdx.x; x < kHist0Bins; x += NT) lhist[x] = 0u;
+        lds_barrier();
+    }
+    if constexpr (!ROUTED) mask_qfrag<NHT>(f, qvalid);
     if constexpr (kRoute) {
         if (route) {
             route_finish(rin, rregs, s_rheads, s_rw, s_rq);
@@ -368,7 +379,7 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
             heads = nullptr;
         }
     }
-    if (!ROUTED || heads)
+    if (ROUTED && heads)
         load_qfrag<NHT, ROUTED>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H,
                                 a.H, heads, a.hsel, g, c);
     if constexpr (NSTEP > 0) {
