@@ -314,6 +314,26 @@ def _scaled_keys(p, q_scale, key_scale):
     return p
 
 
+def test_select_sources_over_8192_keys(api):
+    # Sources of more than 8192 keys take the select's general path, not the
+    # register-resident one: every key of a 20000-key row on the filter's
+    # threshold bin (all keys equal), a MISA-dagger pool of k' = 12000, and
+    # HISA's 96 x 128 rescored tokens.
+    say("select over 8192 keys")
+    p = synth.make_problem(13, Bt=1, T=1, L=20000, H=64)
+    p["K"][:] = p["K"][0, 0]
+    idx, sc = run_dsa(api, p, 100)
+    assert sorted(idx[0, 0].tolist()) == list(range(100))
+    idx, sc = run_dsa(api, p, 9000)
+    assert sorted(idx[0, 0].tolist()) == list(range(9000))
+    p = synth.make_problem(14, Bt=2, T=1, L=20000, H=64, needles=8, needle_mode="decode")
+    idx, sc, heads, pool = run_misa(api, p, 2048, 1024, 8, 12000)
+    check_misa(p, 2048, 1024, 8, 12000, idx, sc, heads, pool, rows_of(p))
+    p = synth.make_problem(15, Bt=2, T=1, L=20000, H=64, needles=8, needle_mode="hisa", b=128)
+    idx, sc, blocks = run_hisa(api, p, 2048, 128, 96)
+    check_hisa(p, 2048, 128, 96, idx, sc, blocks, rows_of(p))
+
+
 def test_select_tiny_score_range(api):
     # Scores below 1e-32: the span of a row's scores is too small for
     # equal slices of the score interval, so the selects take radix digits
