@@ -77,6 +77,22 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     const int lo = blockIdx.x * kFilterChunk;
     if (lo >= n) return;
     const int hi = min(lo + kFilterChunk, n);
+    // The slice's scores are loaded first: they do not depend on the
+    // threshold, so their latency overlaps the histogram's.
+    const float* src = a.dense + (long long)row * a.dense_stride;
+    constexpr int kPer = kFilterChunk / kFilterThreads;  // scores per thread
+    static_assert(kPer % 4 == 0 && kPer <= 32, "float4 loads; one bit per score in a mask");
+    float vs[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer / 4; ++i) {
+        const int u0 = lo + (tid + i * kFilterThreads) * 4;
+        float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (u0 < hi) v4 = *reinterpret_cast<const float4*>(src + u0);
+        vs[4 * i] = v4.x;
+        vs[4 * i + 1] = v4.y;
+        vs[4 * i + 2] = v4.z;
+        vs[4 * i + 3] = v4.w;
+    }
     uint32_t* hist = reinterpret_cast<uint32_t*>(s_buf);  // 16 KiB, reused below
     const uint32_t* grow = a.state + (long long)row * kRowState;
     for (int x = tid; x < kHist0Bins; x += kFilterThreads) hist[x] = grow[x];
@@ -100,20 +116,6 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
     // Each thread classifies its kPer scores (float4 loads, all issued first),
     // then one wave-level prefix sum of its (emit, candidate) counts and one
     // LDS atomic per wave and kind give it its staging slots.
-    const float* src = a.dense + (long long)row * a.dense_stride;
-    constexpr int kPer = kFilterChunk / kFilterThreads;  // scores per thread
-    static_assert(kPer % 4 == 0 && kPer <= 32, "float4 loads; one bit per score in a mask");
-    float vs[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer / 4; ++i) {
-        const int u0 = lo + (tid + i * kFilterThreads) * 4;
-        float4 v4 = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (u0 < hi) v4 = *reinterpret_cast<const float4*>(src + u0);
-        vs[4 * i] = v4.x;
-        vs[4 * i + 1] = v4.y;
-        vs[4 * i + 2] = v4.z;
-        vs[4 * i + 3] = v4.w;
-    }
     uint32_t emask = 0u, cmask = 0u;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
