@@ -91,7 +91,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the indexer shards by sequence with no communication); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
