@@ -129,6 +129,39 @@ int indexer_score_topk_pooled(const uint16_t* q, const float* w, const uint16_t*
                               float* out_score, void* ws, size_t ws_bytes, void* pools_ready,
                               void* stream);
 
+/* ------------------------------------------- decode selectors in phases */
+
+/* Phases of indexer_score_topk_pooled_phase and misa_route_phase.
+ * SA_PHASE_SCAN streams the keys: the score row and first-digit histogram of
+ * every query row go into the workspace (and, for the pooled call, the block
+ * means into out_small / out_large).  SA_PHASE_SELECT takes the top-k from
+ * what the scan left in the workspace (for MISA-dagger, the k' pool, its
+ * rescoring with all heads and the final top-k).  Both bits together are the
+ * whole call.  Between the two phases a caller may run other work on the
+ * GPU, for example the scans of other selectors, so that the latency-bound
+ * selections of several selectors run side by side once every key stream is
+ * done (the top-k is a cost of its own next to the key scan, one that does
+ * not shrink with the head count: PaperTrace, "2.2.2 MISA, LISA and
+ * ResMiSA", section 2.2).  The operations are those of
+ * indexer_score_topk_pooled and misa_route. */
+#define SA_PHASE_SCAN 1
+#define SA_PHASE_SELECT 2
+
+/* indexer_score_topk_pooled in phases.
+ *   phases  SA_PHASE_SCAN, SA_PHASE_SELECT or both (SA_EINVAL otherwise).
+ * The SA_PHASE_SELECT call must follow the SA_PHASE_SCAN call on the same
+ * stream order, with the same arguments and the same workspace, which the
+ * caller does not touch in between; nothing checks this.  Each call launches
+ * only its phase's kernels; out_idx / out_score are written by the select
+ * phase, out_small / out_large by the scan phase.  Arguments, shapes and
+ * errors otherwise as in indexer_score_topk_pooled (no pools_ready event:
+ * the scan phase's end is the caller's own ordering point). */
+int indexer_score_topk_pooled_phase(const uint16_t* q, const float* w, const uint16_t* keys,
+                                    const sa_shape* s, int32_t small, int32_t large,
+                                    uint16_t* out_small, uint16_t* out_large, int32_t* out_idx,
+                                    float* out_score, void* ws, size_t ws_bytes, int32_t phases,
+                                    void* stream);
+
 /* ------------------------------------------------ allocation-free DSA */
 
 /* Size of the static device scratch behind indexer_score_topk_noalloc: 32 MiB
@@ -324,6 +357,22 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
                int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
                int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
                void* ws, size_t ws_bytes, void* stream);
+
+/* misa_route in phases (SA_PHASE_SCAN / SA_PHASE_SELECT, see
+ * indexer_score_topk_pooled_phase): the scan phase routes each row and
+ * streams the keys on the routed heads (out_heads written there; with
+ * pooled NULL it pools the keys first, into the workspace); the select phase
+ * takes the top-k, or for k_prime > 0 the k' pool (out_pool), its rescoring
+ * with all H heads and the top-k.  Only decode rows (T < 16) whose pooling
+ * blocks are all whole (the routed scan's own routing) can be split:
+ * SA_EUNSUPPORTED for other shapes unless phases is both bits.  The select
+ * call must follow the scan call on the same stream order, with the same
+ * arguments and workspace, untouched in between; nothing checks this.
+ * Arguments and errors otherwise as in misa_route. */
+int misa_route_phase(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+                     int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
+                     int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
+                     void* ws, size_t ws_bytes, int32_t phases, void* stream);
 
 /* Workspace bytes for misa_route_fp8 (the same as for misa_route). */
 int misa_route_fp8_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,

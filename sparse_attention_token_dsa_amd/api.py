@@ -39,6 +39,7 @@ EXPORTS = (
     "indexer_score_topk_fp8q", "misa_route_fp8_ws", "misa_route_fp8", "hisa_coarse_fine_fp8_ws",
     "hisa_coarse_fine_fp8", "indexer_score_topk_fp8_ragged_ws", "indexer_score_topk_fp8_ragged",
     "indexer_score_topk_noalloc", "indexer_score_topk_pooled_ws", "indexer_score_topk_pooled",
+    "indexer_score_topk_pooled_phase", "misa_route_phase",
 )
 
 # Bytes of the static device scratch behind indexer_score_topk_noalloc
@@ -75,10 +76,12 @@ def load():
     lib.indexer_score_topk_noalloc.argtypes = [P, P, P, SP, P, P, P]
     lib.indexer_score_topk_pooled_ws.argtypes = [SP, I, I, ctypes.POINTER(S)]
     lib.indexer_score_topk_pooled.argtypes = [P, P, P, SP, I, I, P, P, P, P, P, S, P, P]
+    lib.indexer_score_topk_pooled_phase.argtypes = [P, P, P, SP, I, I, P, P, P, P, P, S, I, P]
     lib.sa_pool_blocks.argtypes = [P, I, I, I, I, P, P]
     lib.sa_pool_blocks2.argtypes = [P, I, I, I, I, I, P, P, P]
     lib.misa_route_ws.argtypes = [SP, I, I, I, I, ctypes.POINTER(S)]
     lib.misa_route.argtypes = [P, P, P, SP, I, I, I, P, P, P, P, P, P, S, P]
+    lib.misa_route_phase.argtypes = [P, P, P, SP, I, I, I, P, P, P, P, P, P, S, I, P]
     lib.hisa_coarse_fine_ws.argtypes = [SP, I, I, I, ctypes.POINTER(S)]
     lib.hisa_coarse_fine.argtypes = [P, P, P, SP, I, I, P, P, P, P, P, S, P]
     lib.sa_quantize_keys_fp8.argtypes = [P, I, I, I, P, P, P]
@@ -282,25 +285,52 @@ def indexer_score_topk_pooled_ws(shape: Shape, small, large) -> int:
                      ctypes.byref(shape), int(small), int(large))
 
 
+# Phases of the decode selectors (SA_PHASE_SCAN, SA_PHASE_SELECT; both = the
+# whole call).  The select call repeats the scan call's arguments, outputs
+# and workspace.
+PHASE_SCAN, PHASE_SELECT, PHASE_ALL = 1, 2, 3
+
+
+def _phases(phases):
+    if phases not in (PHASE_SCAN, PHASE_SELECT, PHASE_ALL):
+        raise ValueError("phases must be PHASE_SCAN, PHASE_SELECT or PHASE_ALL")
+    return int(phases)
+
+
 def indexer_score_topk_pooled(q, w, keys, causal_offset, topk, small, large, out_small=None,
                               out_large=None, out_idx=None, out_score=None, want_score=True,
-                              ws=None, pools_ready=None):
+                              ws=None, pools_ready=None, phases=PHASE_ALL):
     """DSA decode selector that also writes the block means of the keys
     (sa_pool_blocks2 layout) in the same pass.  pools_ready: a
     torch.cuda.Event recorded on the current stream once the means are
-    written (before the call's top-k kernels).  Returns (idx, score, small
-    pools, large pools)."""
+    written (before the call's top-k kernels).  phases: PHASE_SCAN and then
+    PHASE_SELECT split the call in two (same arguments and workspace).
+    Returns (idx, score, small pools, large pools)."""
+    phases = _phases(phases)
+    if phases != PHASE_ALL and pools_ready is not None:
+        raise ValueError("pools_ready belongs to the whole call (phases=PHASE_ALL)")
+    if phases != PHASE_ALL and ws is None:
+        raise ValueError("a call in phases needs the caller's workspace (ws)")
     s = _shape(q, w, keys, causal_offset, topk)
     out_small = _reps_out(keys, small, out_small, "out_small")
     out_large = _reps_out(keys, large, out_large, "out_large")
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
     ws = _workspace(indexer_score_topk_pooled_ws(s, small, large), q.device, ws)
     _gpu(q)
-    _check(load().indexer_score_topk_pooled(_p(q), _p(w), _p(keys), ctypes.byref(s), int(small),
-                                            int(large), _p(out_small), _p(out_large),
-                                            _p(out_idx), _p(out_score), _p(ws), ws.numel(),
-                                            _event(pools_ready, q.device), _stream(q.device)),
-           "indexer_score_topk_pooled")
+    if phases == PHASE_ALL:
+        _check(load().indexer_score_topk_pooled(_p(q), _p(w), _p(keys), ctypes.byref(s),
+                                                int(small), int(large), _p(out_small),
+                                                _p(out_large), _p(out_idx), _p(out_score), _p(ws),
+                                                ws.numel(), _event(pools_ready, q.device),
+                                                _stream(q.device)),
+               "indexer_score_topk_pooled")
+    else:
+        _check(load().indexer_score_topk_pooled_phase(_p(q), _p(w), _p(keys), ctypes.byref(s),
+                                                      int(small), int(large), _p(out_small),
+                                                      _p(out_large), _p(out_idx),
+                                                      _p(out_score), _p(ws), ws.numel(), phases,
+                                                      _stream(q.device)),
+               "indexer_score_topk_pooled_phase")
     return out_idx, out_score, out_small, out_large
 
 
@@ -364,9 +394,14 @@ def misa_route_ws(shape: Shape, block_B, h, k_prime, pooled_given) -> int:
 
 def misa_route(q, w, keys, causal_offset, topk, block_B, h, k_prime=0, pooled=None,
                want_heads=True, want_pool=False, out_idx=None, out_score=None,
-               want_score=True, ws=None, out_heads=None, out_pool=None):
+               want_score=True, ws=None, out_heads=None, out_pool=None, phases=PHASE_ALL):
     """MISA routed indexer (k_prime=0) or MISA-dagger (k_prime >= topk).
+    phases: PHASE_SCAN and then PHASE_SELECT split the call in two (decode
+    rows with whole pooling blocks; same arguments, outputs and workspace).
     Returns (idx, score, heads, pool)."""
+    phases = _phases(phases)
+    if phases != PHASE_ALL and ws is None:
+        raise ValueError("a call in phases needs the caller's workspace (ws)")
     s = _shape(q, w, keys, causal_offset, topk)
     pooled = _reps_in(pooled, "pooled", q, s.L, block_B)
     out_idx, out_score = _outputs(q, topk, out_idx, out_score, want_score)
@@ -374,10 +409,17 @@ def misa_route(q, w, keys, causal_offset, topk, block_B, h, k_prime=0, pooled=No
     pool = _rows_out(out_pool, "out_pool", q, int(k_prime), want_pool) if k_prime else None
     ws = _workspace(misa_route_ws(s, block_B, h, k_prime, pooled is not None), q.device, ws)
     _gpu(q)
-    _check(load().misa_route(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_B), int(h),
-                             int(k_prime), _p(pooled), _p(heads), _p(pool), _p(out_idx),
-                             _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
-           "misa_route")
+    if phases == PHASE_ALL:
+        _check(load().misa_route(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_B), int(h),
+                                 int(k_prime), _p(pooled), _p(heads), _p(pool), _p(out_idx),
+                                 _p(out_score), _p(ws), ws.numel(), _stream(q.device)),
+               "misa_route")
+    else:
+        _check(load().misa_route_phase(_p(q), _p(w), _p(keys), ctypes.byref(s), int(block_B),
+                                       int(h), int(k_prime), _p(pooled), _p(heads), _p(pool),
+                                       _p(out_idx), _p(out_score), _p(ws), ws.numel(), phases,
+                                       _stream(q.device)),
+               "misa_route_phase")
     return out_idx, out_score, heads, pool
 
 

@@ -174,7 +174,8 @@ DsaPlan plan_dsa(const sa_shape* s, void* ws) {
 
 // Decode-style path: score rows (+ row state), filter, finish.
 // state_zeroed: the caller's previous kernel on the stream already cleared
-// the row state.
+// the row state.  phases: bit 1 the state clear and the scan, bit 2 the
+// top-k from what the scan left in the workspace.
 hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* keys,
                           const sa_shape* s, const int32_t* heads, int hsel, float* scores,
                           uint32_t* state, unsigned long long* cand, int k, int32_t* out_idx,
@@ -184,68 +185,72 @@ hipError_t run_dense_topk(const uint16_t* q, const float* w, const uint16_t* key
                           bool q_fp8 = false, uint16_t* pool_small_out = nullptr,
                           uint16_t* pool_large_out = nullptr, int pool_small = 0,
                           int pool_large = 0, hipEvent_t after_scan = nullptr,
-                          const uint16_t* route_reps = nullptr, int route_B = 0) {
+                          const uint16_t* route_reps = nullptr, int route_B = 0,
+                          int phases = 3) {
     const long long rows = (long long)s->batch * s->T;
     const int maxn = s->causal_offset + s->T;
     hipError_t e;
-    if (!state_zeroed) {
-        e = sa::launch_fill_u32(state, rows * sa::kRowState, 0u, st);
+    if (phases & 1) {
+        if (!state_zeroed) {
+            e = sa::launch_fill_u32(state, rows * sa::kRowState, 0u, st);
+            if (e != hipSuccess) return e;
+        }
+        sa::ScanArgs a{};
+        a.q = q;
+        a.w = w;
+        a.keys = keys;
+        a.seq_stride = (long long)s->L * sa::kD;
+        a.heads = heads;
+        a.hsel = hsel;
+        a.T = s->T;
+        a.H = s->H;
+        a.offset = s->causal_offset;
+        a.len_div = 1;
+        a.len_cap = s->L;
+        // Keys per workgroup from the work there is: rows x L, or for ragged
+        // batches the caller's total of the sequence lengths when given.
+        const long long work = total_keys > 0 ? total_keys : rows * (long long)s->L;
+        const int wrk = (int)std::min<long long>(work, 1LL << 30);
+        a.chunk = codes ? sa::scan8_chunk(1, wrk) : sa::scan_chunk(4, 1, wrk);
+        a.scores = scores;
+        a.score_stride = score_stride(s->L);
+        a.state = state;
+        a.k = k;
+        a.codes = codes;
+        a.kscale = kscale;
+        a.seq_lens = seq_lens;
+        a.q_fp8 = q_fp8 ? 1 : 0;
+        if (route_reps) {
+            // the scan routes each row itself and writes the heads to `heads`
+            a.route_reps = route_reps;
+            a.route_B = route_B;
+            a.route_nblk = (s->L + route_B - 1) / route_B;
+            a.route_seq_stride = (long long)a.route_nblk * 2 * sa::kD;
+            a.route_heads_out = const_cast<int32_t*>(heads);
+        }
+        const int nht = ((heads ? hsel : s->H) + 15) / 16;
+        if (pool_small_out) {
+            // chunks of whole large blocks (pool_large divides kScanPoolChunk)
+            const int c = (a.chunk + pool_large - 1) / pool_large * pool_large;
+            a.chunk = std::min(c, sa::kScanPoolChunk);
+            a.pool_out_small = pool_small_out;
+            a.pool_out_large = pool_large_out;
+            a.pool_small = pool_small;
+            a.pool_large = pool_large;
+            a.pool_shift = 0;
+            while ((64 << a.pool_shift) < pool_small) ++a.pool_shift;
+            e = sa::launch_scan_pooled(a, (int)rows, nht, st);
+        } else {
+            e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
+                      : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
+        }
         if (e != hipSuccess) return e;
+        if (after_scan) {
+            e = hipEventRecord(after_scan, st);
+            if (e != hipSuccess) return e;
+        }
     }
-    sa::ScanArgs a{};
-    a.q = q;
-    a.w = w;
-    a.keys = keys;
-    a.seq_stride = (long long)s->L * sa::kD;
-    a.heads = heads;
-    a.hsel = hsel;
-    a.T = s->T;
-    a.H = s->H;
-    a.offset = s->causal_offset;
-    a.len_div = 1;
-    a.len_cap = s->L;
-    // Keys per workgroup from the work there is: rows x L, or for ragged
-    // batches the caller's total of the sequence lengths when given.
-    const long long work = total_keys > 0 ? total_keys : rows * (long long)s->L;
-    const int wrk = (int)std::min<long long>(work, 1LL << 30);
-    a.chunk = codes ? sa::scan8_chunk(1, wrk) : sa::scan_chunk(4, 1, wrk);
-    a.scores = scores;
-    a.score_stride = score_stride(s->L);
-    a.state = state;
-    a.k = k;
-    a.codes = codes;
-    a.kscale = kscale;
-    a.seq_lens = seq_lens;
-    a.q_fp8 = q_fp8 ? 1 : 0;
-    if (route_reps) {
-        // the scan routes each row itself and writes the heads to `heads`
-        a.route_reps = route_reps;
-        a.route_B = route_B;
-        a.route_nblk = (s->L + route_B - 1) / route_B;
-        a.route_seq_stride = (long long)a.route_nblk * 2 * sa::kD;
-        a.route_heads_out = const_cast<int32_t*>(heads);
-    }
-    const int nht = ((heads ? hsel : s->H) + 15) / 16;
-    if (pool_small_out) {
-        // chunks of whole large blocks (pool_large divides kScanPoolChunk)
-        const int c = (a.chunk + pool_large - 1) / pool_large * pool_large;
-        a.chunk = std::min(c, sa::kScanPoolChunk);
-        a.pool_out_small = pool_small_out;
-        a.pool_out_large = pool_large_out;
-        a.pool_small = pool_small;
-        a.pool_large = pool_large;
-        a.pool_shift = 0;
-        while ((64 << a.pool_shift) < pool_small) ++a.pool_shift;
-        e = sa::launch_scan_pooled(a, (int)rows, nht, st);
-    } else {
-        e = codes ? sa::launch_scan8(a, (int)rows, nht, st)
-                  : sa::launch_scan(a, (int)rows, nht, 4, heads != nullptr, st);
-    }
-    if (e != hipSuccess) return e;
-    if (after_scan) {
-        e = hipEventRecord(after_scan, st);
-        if (e != hipSuccess) return e;
-    }
+    if (!(phases & 2)) return hipSuccess;
     sa::TopkArgs t{};
     t.dense = scores;
     t.dense_stride = score_stride(s->L);
@@ -626,11 +631,11 @@ int indexer_score_topk_pooled_ws(const sa_shape* s, int32_t small, int32_t large
     return SA_OK;
 }
 
-int indexer_score_topk_pooled(const uint16_t* q, const float* w, const uint16_t* keys,
-                              const sa_shape* s, int32_t small, int32_t large,
-                              uint16_t* out_small, uint16_t* out_large, int32_t* out_idx,
-                              float* out_score, void* ws, size_t ws_bytes, void* pools_ready,
-                              void* stream) {
+static int pooled_phases(const uint16_t* q, const float* w, const uint16_t* keys,
+                         const sa_shape* s, int32_t small, int32_t large, uint16_t* out_small,
+                         uint16_t* out_large, int32_t* out_idx, float* out_score, void* ws,
+                         size_t ws_bytes, void* pools_ready, int32_t phases, void* stream) {
+    if (phases < 1 || phases > 3) return fail(SA_EINVAL, "phases must be 1, 2 or 3");
     int rc = check_pooled(s, small, large);
     if (rc) return rc;
     rc = check_ptrs(q, w, keys, out_idx);
@@ -643,9 +648,27 @@ int indexer_score_topk_pooled(const uint16_t* q, const float* w, const uint16_t*
     hipError_t e = run_dense_topk(q, w, keys, s, nullptr, 0, p.scores, p.state, p.cand, s->topk,
                                   out_idx, out_score, static_cast<hipStream_t>(stream), nullptr,
                                   nullptr, false, nullptr, 0, false, out_small, out_large, small,
-                                  large, static_cast<hipEvent_t>(pools_ready));
+                                  large, static_cast<hipEvent_t>(pools_ready), nullptr, 0, phases);
     if (e != hipSuccess) return hip_fail(e, "pooled decode scan");
     return SA_OK;
+}
+
+int indexer_score_topk_pooled(const uint16_t* q, const float* w, const uint16_t* keys,
+                              const sa_shape* s, int32_t small, int32_t large,
+                              uint16_t* out_small, uint16_t* out_large, int32_t* out_idx,
+                              float* out_score, void* ws, size_t ws_bytes, void* pools_ready,
+                              void* stream) {
+    return pooled_phases(q, w, keys, s, small, large, out_small, out_large, out_idx, out_score,
+                         ws, ws_bytes, pools_ready, 3, stream);
+}
+
+int indexer_score_topk_pooled_phase(const uint16_t* q, const float* w, const uint16_t* keys,
+                                    const sa_shape* s, int32_t small, int32_t large,
+                                    uint16_t* out_small, uint16_t* out_large, int32_t* out_idx,
+                                    float* out_score, void* ws, size_t ws_bytes, int32_t phases,
+                                    void* stream) {
+    return pooled_phases(q, w, keys, s, small, large, out_small, out_large, out_idx, out_score,
+                         ws, ws_bytes, nullptr, phases, stream);
 }
 
 // ------------------------------------------------------------ tidy-up
@@ -1145,9 +1168,10 @@ static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, con
                     const float* kscale, const sa_shape* s, int32_t block_B, int32_t h,
                     int32_t k_prime, const uint16_t* pooled, int32_t* out_heads,
                     int32_t* out_pool, int32_t* out_idx, float* out_score, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, void* stream, int32_t phases = 3) {
     int rc = check_misa(s, block_B, h, k_prime);
     if (rc) return rc;
+    if (phases < 1 || phases > 3) return fail(SA_EINVAL, "phases must be 1, 2 or 3");
     const bool partial = any_partial(s, block_B);
     const size_t need = plan_misa(s, block_B, h, k_prime, pooled != nullptr, partial, nullptr).bytes;
     if (!ws || ws_bytes < need) return fail(SA_EWORKSPACE, "workspace too small");
@@ -1158,22 +1182,25 @@ static int run_misa(const uint16_t* q, const float* w, const uint16_t* keys, con
     hipError_t e;
     int32_t* heads = out_heads ? out_heads : p.heads;
     int32_t* pool_idx = k_prime ? (out_pool ? out_pool : p.pool_idx) : nullptr;
+    if (phases != 3 && (p.prefill || codes || partial))
+        return fail(SA_EUNSUPPORTED,
+                    "calls in phases take decode rows on bf16 keys with whole blocks only");
     if (!p.prefill && !codes && !partial) {
         // Decode rows on bf16 keys, no block cut by the causal bound: the
         // routed scan routes each row itself (no router launch).
         const uint16_t* reps = pooled;
-        if (!reps) {
+        if (!reps && (phases & 1)) {
             e = sa::launch_pool(keys, s->batch, s->L, block_B, p.pooled, st);
             if (e != hipSuccess) return hip_fail(e, "pool");
-            reps = p.pooled;
         }
+        if (!reps) reps = p.pooled;
         const int kk = k_prime ? k_prime : s->topk;
         e = run_dense_topk(q, w, keys, s, heads, h, p.scores, p.state, p.cand, kk,
                            k_prime ? pool_idx : out_idx, k_prime ? nullptr : out_score, st,
                            nullptr, nullptr, /*state_zeroed=*/false, nullptr, 0, false, nullptr,
-                           nullptr, 0, 0, nullptr, reps, block_B);
+                           nullptr, 0, 0, nullptr, reps, block_B, phases);
         if (e != hipSuccess) return hip_fail(e, "routed scan");
-        if (k_prime == 0) return SA_OK;
+        if (k_prime == 0 || !(phases & 2)) return SA_OK;
     } else {
         rc = route_heads(q, w, keys, s, block_B, h, pooled, p.pooled, partial ? p.tail : nullptr,
                          p.flag, heads, st, p.state, codes, kscale, p.qp, p.wp);
@@ -1248,6 +1275,18 @@ int misa_route(const uint16_t* q, const float* w, const uint16_t* keys, const sa
     if (rc) return rc;
     return run_misa(q, w, keys, nullptr, nullptr, s, block_B, h, k_prime, pooled, out_heads,
                     out_pool, out_idx, out_score, ws, ws_bytes, stream);
+}
+
+int misa_route_phase(const uint16_t* q, const float* w, const uint16_t* keys, const sa_shape* s,
+                     int32_t block_B, int32_t h, int32_t k_prime, const uint16_t* pooled,
+                     int32_t* out_heads, int32_t* out_pool, int32_t* out_idx, float* out_score,
+                     void* ws, size_t ws_bytes, int32_t phases, void* stream) {
+    int rc = check_misa(s, block_B, h, k_prime);
+    if (rc) return rc;
+    rc = check_ptrs(q, w, keys, out_idx);
+    if (rc) return rc;
+    return run_misa(q, w, keys, nullptr, nullptr, s, block_B, h, k_prime, pooled, out_heads,
+                    out_pool, out_idx, out_score, ws, ws_bytes, stream, phases);
 }
 
 int misa_route_fp8_ws(const sa_shape* s, int32_t block_B, int32_t h, int32_t k_prime,

@@ -218,6 +218,38 @@ def test_new_entry_points_validate(api):
     assert lib.sa_tidy_indices(p, 4, 1, 64, p, 0, 64, 0, p, None, None) == api.SA_EINVAL
 
 
+def test_phase_entry_points_validate(api):
+    """The decode selectors in phases: bad phase masks, and shapes that cannot
+    be split, are rejected before anything is launched."""
+    lib = api.load()
+    buf = ctypes.create_string_buffer(16)
+    p = ctypes.cast(buf, ctypes.c_void_p)
+    s = shape(api, L=4096, causal_offset=4095)
+    for bad in (0, 4, -1):
+        assert lib.indexer_score_topk_pooled_phase(p, p, p, ctypes.byref(s), 128, 1024, p, p, p,
+                                                   None, p, 1 << 40, bad, None) == api.SA_EINVAL
+        assert lib.misa_route_phase(p, p, p, ctypes.byref(s), 1024, 8, 0, None, None, None, p,
+                                    None, p, 1 << 40, bad, None) == api.SA_EINVAL
+    n = ctypes.c_size_t()
+    # prefill rows (T >= 16) and decode rows with a pooling block cut by the
+    # causal bound (the rows before the last of T = 3) take other paths,
+    # which are not split
+    for s2 in (shape(api, T=32, L=4096, causal_offset=4064),
+               shape(api, T=3, L=4096, causal_offset=4093)):
+        assert lib.misa_route_ws(ctypes.byref(s2), 1024, 8, 0, 1, ctypes.byref(n)) == api.SA_OK
+        for ph in (api.PHASE_SCAN, api.PHASE_SELECT):
+            assert lib.misa_route_phase(p, p, p, ctypes.byref(s2), 1024, 8, 0, p, None, None, p,
+                                        None, p, n.value, ph, None) == api.SA_EUNSUPPORTED
+            assert "phases" in api.last_error()
+    # the binding checks the mask and the workspace before touching tensors
+    with pytest.raises(ValueError):
+        api.indexer_score_topk_pooled(None, None, None, 0, 64, 128, 1024, phases=4)
+    with pytest.raises(ValueError):
+        api.indexer_score_topk_pooled(None, None, None, 0, 64, 128, 1024, phases=api.PHASE_SCAN)
+    with pytest.raises(ValueError):
+        api.misa_route(None, None, None, 0, 64, 1024, 8, phases=api.PHASE_SELECT)
+
+
 def test_bench_refuses_more_than_one_gpu():
     # bench.py measures one GPU; asking for more exits with a message before
     # any device work.
