@@ -4,11 +4,14 @@
 //
 // Every candidate becomes the 64-bit key  ord(score) << 32 | ~index : larger
 // scores win and, among equal scores, the lower index wins.  Keys are
-// distinct, so the selection is exact.  Keys are consumed from the top in
-// digits of 12/10/10 bits (score) then 12/10/10 bits (index, only reached on
-// exact score ties).  Per digit: a histogram, a scan from the top that finds
-// the digit value holding the k-th key, and one pass that emits every key
-// above it and keeps the keys on it for the next digit.
+// distinct, so the selection is exact.  Each level sorts the keys still in
+// play into bins by a map that never decreases along the key order: a
+// histogram, a scan from the top that finds the bin holding the k-th key,
+// and one pass that emits every key above it and keeps the keys in it for
+// the next level.  The filter and the select's general path take fixed
+// digits of the key from the top (12/10/10 bits of the score, then 12/10/10
+// of the index, only reached on exact score ties); the select's register
+// path fits its bins to the range of the keys in play.
 //
 // Two kernels:
 //  * topk_filter_kernel -- long dense score rows (decode scans).  The first
