@@ -318,7 +318,9 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
                                                     const float* dsrc, const float* lsc,
                                                     const int32_t* lid,
                                                     const unsigned long long* ksrc, int nsrc,
-                                                    int32_t* oidx, float* osc, SelShared& S) {
+                                                    int32_t* oidx, float* osc, SelShared& S,
+                                                    const unsigned long long* pre = nullptr,
+                                                    const int* pctl = nullptr) {
     const int tid = threadIdx.x, lane = lane_id();
     const int row = blockIdx.x;
     unsigned long long kr[kRegKeys];
@@ -327,15 +329,19 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
     for (int j = 0; j < kRegKeys; ++j) {
         const int u = tid + j * kTopkThreads;
         bool valid = u < nsrc;
-        kr[j] = valid ? src_key(kind, dsrc, lsc, lid, ksrc, u, valid) : 0ull;
+        if (pre)
+            kr[j] = valid ? pre[j] : 0ull;  // loaded by the caller
+        else
+            kr[j] = valid ? src_key(kind, dsrc, lsc, lid, ksrc, u, valid) : 0ull;
         if (valid) alive |= 1u << j;
     }
     int need = 0, need_rem = 0;
     if (kind == SRC_KEYS) {
         // continue after the filter: its winners are written, its
         // candidates are the keys on the row's first-digit threshold
-        const int* ctl = reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
-                                                      kHist0Bins);
+        const int* ctl = pctl ? pctl
+                              : reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
+                                                             kHist0Bins);
         need = ctl[CTL_NEED];
         const int gt = ctl[CTL_GT];
         for (int u = need + tid; u < a.k; u += kTopkThreads) {
@@ -543,7 +549,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         const int* ctl = reinterpret_cast<const int*>(a.state + (long long)row * kRowState +
                                                       kHist0Bins);
         ksrc = cand + (long long)row * a.cand_cap;
-        nsrc0 = (int)min((long long)ctl[CTL_CANDS], a.cand_cap);
+        // the row's counters in one read
+        const int4 c0 = reinterpret_cast<const int4*>(ctl)[0];
+        const int4 c1 = reinterpret_cast<const int4*>(ctl)[1];
+        const int cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        const int ncand = cv[CTL_CANDS];
+        // The register path's keys are loaded together with the count, not
+        // after it (the candidate array holds cand_cap keys per row, so the
+        // loads stay in bounds); those past the count are dropped.
+        unsigned long long pre[kRegKeys];
+#pragma unroll
+        for (int j = 0; j < kRegKeys; ++j) {
+            const int u = tid + j * kTopkThreads;
+            pre[j] = u < a.cand_cap ? ksrc[u] : 0ull;
+        }
+        nsrc0 = (int)min((long long)ncand, a.cand_cap);
+        if (nsrc0 <= kRegKeys * kTopkThreads) {
+            select_in_registers(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S, pre, cv);
+            return;
+        }
     }
     if (nsrc0 <= kRegKeys * kTopkThreads) {
         select_in_registers(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S);
