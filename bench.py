@@ -797,8 +797,68 @@ def bench_prefill(api, synth, torch, np, dev, iters):
                          "counters": measured_mfma(
                              source_digest(["prefill.hip", "sa_frag.h", "sa_common.h"]))},
             "ragged": bench_prefill_ragged(api, synth, torch, np, dev, iters),
+            "selectors": bench_prefill_selectors(api, torch, dev, q, w, K, shape, iters, pairs,
+                                                 (t1 - t0) * 1e3 / iters),
             "fp8q": bench_prefill_fp8q(api, torch, dev, q, w, K, shape, oi, osc, iters, flops,
                                        pairs)}
+
+
+def bench_prefill_selectors(api, torch, dev, q, w, K, shape, iters, pairs, dsa_ms):
+    """MISA (h = 8 of 64 heads, B = 1024), MISA-dagger (k' = 8192) and HISA
+    (b = 128, r = 64) on the same prefill chunk, block means given (cache-side
+    state, pooled once outside the timing).  Prefill rows are where the
+    indexer is MFMA-bound on this chip, so the head reduction shows here:
+    MISA's rows go through the fused prefill on the routed heads' q rows."""
+    T, off, k = shape.T, shape.causal_offset, shape.topk
+    H, d, L = shape.H, shape.d, shape.L
+    B, h, kp, b, r = 1024, 8, 8192, 128, 64
+    pooled = api.pool_blocks(K, B)
+    reps = api.pool_blocks(K, b)
+    oi = torch.empty((1, T, k), dtype=torch.int32, device=dev)
+    osc = torch.empty((1, T, k), dtype=torch.float32, device=dev)
+    ws_m = torch.empty(api.misa_route_ws(shape, B, h, 0, True), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(api.misa_route_ws(shape, B, h, kp, True), dtype=torch.uint8, device=dev)
+    ws_h = torch.empty(api.hisa_coarse_fine_ws(shape, b, r, True), dtype=torch.uint8,
+                       device=dev)
+    calls = {
+        "misa": lambda: api.misa_route(q, w, K, off, k, B, h, 0, pooled=pooled,
+                                       want_heads=False, out_idx=oi, out_score=osc, ws=ws_m),
+        "misa_dagger": lambda: api.misa_route(q, w, K, off, k, B, h, kp, pooled=pooled,
+                                              want_heads=False, out_idx=oi, out_score=osc,
+                                              ws=ws_d),
+        "hisa": lambda: api.hisa_coarse_fine(q, w, K, off, k, b, r, reps=reps,
+                                             want_blocks=False, out_idx=oi, out_score=osc,
+                                             ws=ws_h),
+    }
+    out = {"workload": "prefill_chunked_T4096_P28672_h64",
+           "config": {"B": B, "h": h, "k_prime": kp, "b": b, "r": r,
+                      "pools": "given (block means of the cached keys)"},
+           "dsa_ms_per_call": dsa_ms}
+    for name, call in calls.items():
+        settle(call, torch, dev)
+        api.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            call()
+        torch.cuda.synchronize(dev)
+        t1 = time.perf_counter()
+        kern = api.profile_read()
+        api.profile_enable(False)
+        ms = (t1 - t0) * 1e3 / iters
+        out[name] = {"ms_per_call": ms, "dsa_over_this": dsa_ms / ms,
+                     "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()}}
+    # the routed prefill's own contraction: h heads per legal pair
+    flops = 2.0 * pairs * h * d
+    us = out["misa"]["kernels_us"].get("prefill_fused")
+    if us:
+        tf = flops / (us * 1e-6) / 1e12
+        out["misa"]["routed_prefill"] = {
+            "kernel": "prefill_fused", "algorithmic_flops_per_launch": flops,
+            "achieved_tflops": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "note": "8 routed heads fill half of the kernel's one 16-row head tile, and the "
+                    "per-pair epilogue, threshold and survivor work does not shrink with the "
+                    "head count"}
+    return out
 
 
 def bench_prefill_fp8q(api, torch, dev, q, w, K, shape, oi, osc, iters, flops, pairs):

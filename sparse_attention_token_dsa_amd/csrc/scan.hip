@@ -451,77 +451,94 @@ __global__ __launch_bounds__(64 * scan_waves<KSTEPS>()) void scan_kernel(ScanArg
 // Rescore a per-row candidate list with all heads.  List mode: candidate u
 // is token list[u]; block mode: candidate u is token list[u / bsz] * bsz +
 // u % bsz.  Candidates past the causal bound, past L or with a negative id
-// get score -inf and index -1.  A workgroup takes kGatherChunk candidates;
-// each wave resolves its kGatherGroups x 16 candidate ids, issues every key
-// load (16 KiB in flight per wave), then runs the MFMA groups.
-template <int NHT, bool BLOCKS, bool F8>
+// get score -inf and index -1.  A workgroup takes one chunk of kGatherChunk
+// candidates of its row, or with SWEEP (many rows) every gridDim.x-th chunk
+// of the row with one load of the query fragments; in a chunk each wave
+// resolves its kGatherGroups x 16 candidate ids, issues every key load
+// (16 KiB in flight per wave), then runs the MFMA groups.  (Prefetching the
+// next chunk's ids during the MFMAs costs a wave per SIMD and was slower.)
+template <int NHT, bool BLOCKS, bool F8, bool SWEEP>
 __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
     constexpr int NG = kGatherGroups;
     const int row = blockIdx.y;
     const int b = row / a.T;
     const int t = a.offset + (row - b * a.T);
-    const int cs = blockIdx.x * kGatherChunk;
-    if (cs >= a.ncand) return;
-    const int ce = min(cs + kGatherChunk, a.ncand);
+    if (blockIdx.x * kGatherChunk >= a.ncand) return;
     const int lane = lane_id(), g = lane >> 4, c = lane & 15;
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int32_t* lrow = a.list + (long long)row * a.list_len;
+    // candidate ids of the chunk at cs (the first chunk's list loads go out
+    // before the query loads: load counters are in order, so a wait for the
+    // keys would otherwise be a wait for the query as well)
     int sid[NG];
+    auto resolve = [&](int cs, int (&ids)[NG]) {
+        const int ce = min(cs + kGatherChunk, a.ncand);
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        const int u = cs + (gi * 4 + wid) * 16 + c;
-        int s = -1;
-        if (u < ce) {
-            if (BLOCKS) {
-                const int q = u / a.bsz;
-                const int blk = lrow[q];
-                s = blk >= 0 ? blk * a.bsz + (u - q * a.bsz) : -1;
-            } else {
-                s = lrow[u];
+        for (int gi = 0; gi < NG; ++gi) {
+            const int u = cs + (gi * 4 + wid) * 16 + c;
+            int s = -1;
+            if (u < ce) {
+                if (BLOCKS) {
+                    const int q = u / a.bsz;
+                    const int blk = lrow[q];
+                    s = blk >= 0 ? blk * a.bsz + (u - q * a.bsz) : -1;
+                } else {
+                    s = lrow[u];
+                }
             }
+            ids[gi] = (s >= 0 && s <= t && s < a.L) ? s : -1;
         }
-        sid[gi] = (s >= 0 && s <= t && s < a.L) ? s : -1;
-    }
+    };
+    int cs = blockIdx.x * kGatherChunk;
+    resolve(cs, sid);
     QFrag<NHT> f;
     load_qfrag<NHT>(f, a.q + (long long)row * a.H * kD, a.w + (long long)row * a.H, a.H,
                     nullptr, 0, g, c);
-    uint4 kb[NG][4];
-    float ks[NG];
-    if (F8) {
-        // FP8 cache: the same dims as load_key (k-step kk, lane group g:
-        // dims 32kk + 8g .. +8), widened exactly; the key's scale multiplies
-        // the head sum.
-        const uint8_t* cseq = a.codes + (long long)b * a.seq_stride;
-        const float* sseq = a.kscale + (long long)b * (a.seq_stride / kD);
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const long long s = sid[gi] >= 0 ? sid[gi] : 0;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const uint2 v = *reinterpret_cast<const uint2*>(cseq + s * kD + 32 * kk + 8 * g);
-                kb[gi][kk] = widen8(v.x, v.y);
-            }
-            ks[gi] = sseq[s];
-        }
-    } else {
-        const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            load_key<4>(kb[gi], kseq + (long long)(sid[gi] >= 0 ? sid[gi] : 0) * kD, g);
-            ks[gi] = 1.f;
-        }
-    }
     float* osc = a.out_score + (long long)row * a.ncand;
     int32_t* oid = a.out_idx + (long long)row * a.ncand;
+    for (;;) {
+        const int ce = min(cs + kGatherChunk, a.ncand);
+        uint4 kb[NG][4];
+        float ks[NG];
+        if (F8) {
+            // FP8 cache: the same dims as load_key (k-step kk, lane group g:
+            // dims 32kk + 8g .. +8), widened exactly; the key's scale
+            // multiplies the head sum.
+            const uint8_t* cseq = a.codes + (long long)b * a.seq_stride;
+            const float* sseq = a.kscale + (long long)b * (a.seq_stride / kD);
 #pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-        const int u = cs + (gi * 4 + wid) * 16 + c;
-        float sc = group_score<NHT, 4>(f, kb[gi]);
-        if (F8) sc *= ks[gi];
-        if (g == 0 && u < ce) {
-            osc[u] = sid[gi] >= 0 ? sc : -INFINITY;
-            oid[u] = sid[gi];
+            for (int gi = 0; gi < NG; ++gi) {
+                const long long s = sid[gi] >= 0 ? sid[gi] : 0;
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const uint2 v =
+                        *reinterpret_cast<const uint2*>(cseq + s * kD + 32 * kk + 8 * g);
+                    kb[gi][kk] = widen8(v.x, v.y);
+                }
+                ks[gi] = sseq[s];
+            }
+        } else {
+            const uint16_t* kseq = a.keys + (long long)b * a.seq_stride;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                load_key<4>(kb[gi], kseq + (long long)(sid[gi] >= 0 ? sid[gi] : 0) * kD, g);
+                ks[gi] = 1.f;
+            }
         }
+        const int nxt = cs + gridDim.x * kGatherChunk;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+            const int u = cs + (gi * 4 + wid) * 16 + c;
+            float sc = group_score<NHT, 4>(f, kb[gi]);
+            if (F8) sc *= ks[gi];
+            if (g == 0 && u < ce) {
+                osc[u] = sid[gi] >= 0 ? sc : -INFINITY;
+                oid[u] = sid[gi];
+            }
+        }
+        if (!SWEEP || nxt >= a.ncand) break;
+        cs = nxt;
+        resolve(cs, sid);
     }
 }
 
@@ -747,18 +764,30 @@ hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool ro
 
 hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode,
                          hipStream_t s) {
-    const dim3 grid((unsigned)((a.ncand + kGatherChunk - 1) / kGatherChunk), (unsigned)rows);
+    // Workgroups per row: every chunk its own for few rows; fewer, each
+    // sweeping several chunks with one query load, once rows alone give
+    // about 8 workgroups per CU.
+    const int chunks = (a.ncand + kGatherChunk - 1) / kGatherChunk;
+    const int want = (8 * cu_count() + rows - 1) / rows;
+    const int per_row = std::max(1, std::min(chunks, want));
+    const dim3 grid((unsigned)per_row, (unsigned)rows);
     prof_begin(K_GATHER, s);
-#define SA_GATHER(N)                                                            \
-    if (a.codes) {                                                              \
-        if (block_mode)                                                         \
-            sa_launch(gather_kernel<N, true, true>, grid, dim3(256), 0, s, a);  \
-        else                                                                    \
-            sa_launch(gather_kernel<N, false, true>, grid, dim3(256), 0, s, a); \
-    } else if (block_mode) {                                                    \
-        sa_launch(gather_kernel<N, true, false>, grid, dim3(256), 0, s, a);     \
-    } else {                                                                    \
-        sa_launch(gather_kernel<N, false, false>, grid, dim3(256), 0, s, a);    \
+#define SA_GATHER4(N, SW)                                                           \
+    if (a.codes) {                                                                  \
+        if (block_mode)                                                             \
+            sa_launch(gather_kernel<N, true, true, SW>, grid, dim3(256), 0, s, a);  \
+        else                                                                        \
+            sa_launch(gather_kernel<N, false, true, SW>, grid, dim3(256), 0, s, a); \
+    } else if (block_mode) {                                                        \
+        sa_launch(gather_kernel<N, true, false, SW>, grid, dim3(256), 0, s, a);     \
+    } else {                                                                        \
+        sa_launch(gather_kernel<N, false, false, SW>, grid, dim3(256), 0, s, a);    \
+    }
+#define SA_GATHER(N)              \
+    if (per_row < chunks) {       \
+        SA_GATHER4(N, true)       \
+    } else {                      \
+        SA_GATHER4(N, false)      \
     }
     switch (nht) {
         case 1: SA_GATHER(1) break;
@@ -766,6 +795,7 @@ hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode
         case 3: SA_GATHER(3) break;
         default: SA_GATHER(4) break;
     }
+#undef SA_GATHER4
 #undef SA_GATHER
     prof_end(K_GATHER, s);
     return hipGetLastError();

@@ -280,6 +280,17 @@ def test_misa_configs(api, name, kp):
     check_misa(p, 2048, 1024, 8, kp, idx, sc, heads, pool, rows_of(p))
 
 
+@pytest.mark.parametrize("kp", [0, 8192])
+def test_misa_prefill_chunked_rows(api, kp):
+    """MISA on the 4096-row prefill chunk over 32768 keys (the routed fused
+    prefill, k' = 0 and the MISA-dagger pool): one row of each 8-row group."""
+    say("misa prefill_chunked k'=%d 512 rows" % kp)
+    p = synth.make_config("prefill_chunked")
+    idx, sc, heads, pool = run_misa(api, p, 2048, 1024, 8, kp)
+    rows = prefill_group_rows(p["T"], 5 + kp)
+    check_misa(p, 2048, 1024, 8, kp, idx, sc, heads, pool, rows)
+
+
 # ----------------------------------------------------------------- HISA
 
 @pytest.mark.parametrize("Bt,T,L,H,b,r,k", [
@@ -294,6 +305,16 @@ def test_hisa(api, Bt, T, L, H, b, r, k):
                            needle_mode="hisa" if T == 1 else "rows", b=b)
     idx, sc, blocks = run_hisa(api, p, k, b, r)
     check_hisa(p, k, b, r, idx, sc, blocks, rows_of(p))
+
+
+def test_hisa_prefill_chunked_rows(api):
+    """HISA (b = 128, r = 64) on the 4096-row prefill chunk over 32768 keys:
+    one row of each 8-row group."""
+    say("hisa prefill_chunked 512 rows")
+    p = synth.make_config("prefill_chunked")
+    idx, sc, blocks = run_hisa(api, p, 2048, 128, 64)
+    rows = prefill_group_rows(p["T"], 9)
+    check_hisa(p, 2048, 128, 64, idx, sc, blocks, rows)
 
 
 def test_hisa_config(api):
