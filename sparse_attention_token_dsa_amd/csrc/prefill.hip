@@ -495,8 +495,14 @@ __device__ __forceinline__ PfRow pf_compact(uint2* L, uint32_t* hr, PfRow st, in
     return st;
 }
 
-template <int NHT, bool F8>
+// PACK2 (bf16 keys, at most 8 heads, NHT = 1): the wave's two rows share one
+// 16-row head tile, row 0's heads on tile rows 0-3 and 8-11, row 1's on 4-7
+// and 12-15, so one MFMA per k-step scores both rows and the head sum of a
+// lane group's row is one lane-group swap away (lane groups g and g ^ 2 hold
+// the same row, and lane group g keeps the row g & 1, as the unpacked form).
+template <int NHT, bool F8, bool PACK2>
 __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
+    static_assert(!PACK2 || (NHT == 1 && !F8), "packed rows: one bf16 head tile");
     // The stages are four distinct LDS objects: the compiler then tracks the
     // direct-to-LDS loads per object and places no wait of its own for the
     // pair in flight before reads of the other pair.
@@ -559,13 +565,15 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         if constexpr (F8) {
             quantize_q8_wave(a.q + rowq[qq] * a.H * kD, a.H, qc, qs);
             load_qfrag_fp8<NHT>(f[qq], qc, qs, wrow, a.H, g, c);
-        } else {
+        } else if constexpr (!PACK2) {
             load_qfrag<NHT>(f[qq], a.q + rowq[qq] * a.H * kD, wrow, a.H, nullptr, 0, g, c);
         }
+        if constexpr (!PACK2)
 #pragma unroll
-        for (int ht = 0; ht < NHT; ++ht)
+            for (int ht = 0; ht < NHT; ++ht)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) f[qq].wv[ht][e] = act[qq] ? 0.5f * f[qq].wv[ht][e] : 0.f;
+                for (int e = 0; e < 4; ++e)
+                    f[qq].wv[ht][e] = act[qq] ? 0.5f * f[qq].wv[ht][e] : 0.f;
         // g = sum_j (w_j / 2) q_j of the row, two dims per lane, heads in
         // order, staged in gk (free until the sweep starts); lanes 0..15 then
         // pack the row's A-fragment entries: lane t holds dims
@@ -611,6 +619,25 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
             }
             gfrag[0][kk][16 * grp + r] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
             gfrag[1][kk][16 * grp + r] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        }
+    }
+    if constexpr (PACK2) {
+        // Tile row c: row (c >> 2) & 1, head (c & 3) + 4 (c >> 3); output row
+        // 4g + e of lane group g: row g & 1, head e + 4 (g >> 1).
+        const int ra = (c >> 2) & 1, ja = (c & 3) + 4 * (c >> 3);
+        const bool va = ja < a.H;
+        const uint16_t* qa =
+            a.q + ((ra ? rowq[1] : rowq[0]) * a.H + (va ? ja : 0)) * kD + g * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            f[0].a[0][kk] = va ? ldg16(qa + kk * 32) : make_uint4(0u, 0u, 0u, 0u);
+        const int rw = g & 1;
+        const float* ww = a.w + (rw ? rowq[1] : rowq[0]) * a.H;
+        const bool aw = rw ? act[1] : act[0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int jw = e + 4 * (g >> 1);
+            f[0].wv[0][e] = aw && jw < a.H ? 0.5f * ww[jw] : 0.f;
         }
     }
     __syncthreads();  // fragments visible; the staging area is free again
@@ -805,6 +832,54 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         }
     };
 
+    // PACK2: one block per 16-key group for both rows; blocks alternate
+    // between the two accumulator sets, each re-reads the next group's B
+    // fragments behind its MFMAs and runs the epilogue of the group before.
+    auto epilogue2 = [&](int set, int j, int gi) __attribute__((always_inline)) {
+        float sc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc = fmaf(f[0].wv[0][e], fabsf(acc[set][0][e]), sc);
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc), __float_as_uint(sc),
+                                                        false, false);
+        sc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+        st[gi] = (g >> 1) == j ? sc : st[gi];
+    };
+    auto block2 = [&](auto reload_c, auto prev_c, int set, const uint4* ntile, int ngi, int pj,
+                      int pgi) __attribute__((always_inline)) {
+        constexpr bool kReload = decltype(reload_c)::value;
+        constexpr bool kPrev = decltype(prev_c)::value;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PACK2) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                acc[set][0] = mfma16x16x32(f[0].a[0][kk], bf[kk],
+                                           kk ? acc[set][0] : f32x4{0.f, 0.f, 0.f, 0.f});
+                if (kReload) bf[kk] = ntile[bbase + ngi * 16 + kk * 4];
+            }
+            if (kPrev) epilogue2(1 - set, pj, pgi);
+            pf_interleave<0, 4, (kPrev ? 8 : 0), 1, kReload>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    auto pair_scores2 = [&](const uint4* ka, const uint4* kb, bool two) __attribute__((always_inline)) {
+        const std::true_type y;
+        const std::false_type n;
+        load_b(ka, 0);
+        block2(y, n, 0, ka, 1, 0, 0);
+        block2(y, y, 1, ka, 2, 0, 0);
+        block2(y, y, 0, ka, 3, 0, 1);
+        block2(y, y, 1, kb, 0, 0, 2);
+        if (two) {
+            block2(y, y, 0, kb, 1, 0, 3);
+            block2(y, y, 1, kb, 2, 1, 0);
+            block2(y, y, 0, kb, 3, 1, 1);
+            block2(n, y, 1, kb, 0, 1, 2);
+            epilogue2(1, 1, 3);
+        } else {
+            epilogue2(1, 0, 3);
+        }
+    };
+
     // Raise tau of row r while the bins at and above tau + 1 still hold k
     // kept scores (the histogram adds of this wave are in LDS order before
     // these reads).
@@ -961,6 +1036,8 @@ __global__ __launch_bounds__(64 * kPfWaves) void prefill_kernel(PrefillArgs a) {
         if (kbase <= tw) {
             if constexpr (F8)
                 pair_scores8(ka, kb, kbase + kPfTile <= tw);
+            else if constexpr (PACK2)
+                pair_scores2(ka, kb, kbase + kPfTile <= tw);
             else
                 pair_scores(ka, kb, kbase + kPfTile <= tw);
             pend_base = kbase;  // keys past a row's last legal one are never kept
@@ -1041,20 +1118,25 @@ hipError_t launch_prefill(const PrefillArgs& a, int rows, hipStream_t s) {
         if (!a.kscale) return hipErrorInvalidValue;
         prof_begin(K_PREFILL_FP8, s);
         switch (nht) {
-            case 1: sa_launch(prefill_kernel<1, true>, grid, block, 0, s, a); break;
-            case 2: sa_launch(prefill_kernel<2, true>, grid, block, 0, s, a); break;
-            case 3: sa_launch(prefill_kernel<3, true>, grid, block, 0, s, a); break;
-            default: sa_launch(prefill_kernel<4, true>, grid, block, 0, s, a); break;
+            case 1: sa_launch(prefill_kernel<1, true, false>, grid, block, 0, s, a); break;
+            case 2: sa_launch(prefill_kernel<2, true, false>, grid, block, 0, s, a); break;
+            case 3: sa_launch(prefill_kernel<3, true, false>, grid, block, 0, s, a); break;
+            default: sa_launch(prefill_kernel<4, true, false>, grid, block, 0, s, a); break;
         }
         prof_end(K_PREFILL_FP8, s);
         return hipGetLastError();
     }
     prof_begin(K_PREFILL, s);
-    switch (nht) {
-        case 1: sa_launch(prefill_kernel<1, false>, grid, block, 0, s, a); break;
-        case 2: sa_launch(prefill_kernel<2, false>, grid, block, 0, s, a); break;
-        case 3: sa_launch(prefill_kernel<3, false>, grid, block, 0, s, a); break;
-        default: sa_launch(prefill_kernel<4, false>, grid, block, 0, s, a); break;
+    // At most 8 heads (MISA's routed heads, LISA's head rows): two rows per tile.
+    if (a.H <= 8) {
+        sa_launch(prefill_kernel<1, false, true>, grid, block, 0, s, a);
+    } else {
+        switch (nht) {
+            case 1: sa_launch(prefill_kernel<1, false, false>, grid, block, 0, s, a); break;
+            case 2: sa_launch(prefill_kernel<2, false, false>, grid, block, 0, s, a); break;
+            case 3: sa_launch(prefill_kernel<3, false, false>, grid, block, 0, s, a); break;
+            default: sa_launch(prefill_kernel<4, false, false>, grid, block, 0, s, a); break;
+        }
     }
     prof_end(K_PREFILL, s);
     return hipGetLastError();

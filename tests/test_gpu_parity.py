@@ -102,6 +102,10 @@ def test_dsa_decode_path(api, Bt, T, L, H, k, needles):
     (1, 77, 1500, 1000, 64, 1000),  # k larger than many rows' survivors
     (1, 32, 6000, 5968, 64, 4000),  # k-th score negative: crowded one-octave bins
     (1, 24, 2000, 1976, 16, 1),     # k = 1, H = 16
+    # at most 8 heads: a wave's two rows share one head tile
+    (2, 37, 1200, 1163, 8, 100),    # H = 8, odd T (a wave with one active row)
+    (1, 64, 4000, 3936, 5, 300),    # H = 5: tile rows of heads 5..7 empty
+    (1, 20, 900, 0, 1, 50),         # H = 1, from position 0
 ])
 def test_dsa_prefill_path(api, Bt, T, L, offset, H, k):
     say("dsa prefill Bt=%d T=%d L=%d off=%d H=%d k=%d" % (Bt, T, L, offset, H, k))
