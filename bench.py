@@ -149,8 +149,8 @@ def main():
         mark(4)
 
     # The same step on two streams (default priority).  The pooled DSA call
-    # records an event as soon as the block means are written; MISA and then
-    # HISA start on the second stream from it, while MISA-dagger (the longest
+    # records an event as soon as the block means are written; HISA and then
+    # MISA start on the second stream from it, while MISA-dagger (the longest
     # chain) follows DSA's top-k on the first.  Each cross-stream edge of a
     # HIP graph costs several microseconds, so the step uses just these two.
     side = torch.cuda.Stream(device=dev)
@@ -164,10 +164,12 @@ def main():
                                       ws=ws_dsa, pools_ready=pools_ready)
         side.wait_event(pools_ready)
         with torch.cuda.stream(side):
-            api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
-                           out_idx=outs["misa"][0], out_score=outs["misa"][1], ws=ws_m1)
+            # HISA's latency-bound kernels first, beside DSA's top-k on the
+            # first stream, then MISA's scan beside MISA-dagger's
             api.hisa_coarse_fine(q, w, K, off, k, b, r, reps=reps_b, want_blocks=False,
                                  out_idx=outs["hisa"][0], out_score=outs["hisa"][1], ws=ws_hi)
+            api.misa_route(q, w, K, off, k, B, h, 0, pooled=reps_B, want_heads=False,
+                           out_idx=outs["misa"][0], out_score=outs["misa"][1], ws=ws_m1)
         api.misa_route(q, w, K, off, k, B, h, kp, pooled=reps_B, want_heads=False,
                        out_idx=outs["misa_dagger"][0], out_score=outs["misa_dagger"][1],
                        ws=ws_m2)
@@ -349,7 +351,7 @@ def main():
                            "MISA-dagger + HISA"},
         "topk_rows_per_s": 4 * rows / (ms_step * 1e-3),
         "timing": "value and ms_per_step: the step replayed as one HIP graph: the pooled DSA "
-                  "scan, then MISA and HISA on a second stream beside DSA's top-k and "
+                  "scan, then HISA and MISA on a second stream beside DSA's top-k and "
                   "MISA-dagger, each step after a 1 GiB read "
                   "that evicts the keys from the "
                   "256 MB infinity cache, timed with its own events; ms_per_step_warm: "

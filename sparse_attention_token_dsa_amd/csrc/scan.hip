@@ -607,11 +607,23 @@ __global__ __launch_bounds__(256) void tail_kernel(const uint16_t* keys, const u
     const uint16_t* kseq = codes ? nullptr : keys + (long long)b * seq_stride;
     const uint8_t* cseq = codes ? codes + (long long)b * seq_stride : nullptr;
     const float* sseq = codes ? scales + (long long)b * (seq_stride / kD) : nullptr;
-    for (int s = lo + kl; s <= t; s += 16) {
-        float x[8];
-        key8_f32(kseq, cseq, sseq, s, c16, x);
+    // four keys per thread in flight (a long cut block is up to block - 1 keys)
+    for (int s0 = lo + kl; s0 <= t; s0 += 64) {
+        float x[4][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+        for (int u = 0; u < 4; ++u) {
+            const int s = s0 + 16 * u;
+            if (s <= t) {
+                key8_f32(kseq, cseq, sseq, s, c16, x[u]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += x[u][e];
     }
     __shared__ float red[16][kD];
 #pragma unroll
