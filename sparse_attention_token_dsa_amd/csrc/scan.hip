@@ -580,6 +580,112 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs a) {
             a.zero_state[(long long)row * kRowState + x] = 0u;
 }
 
+// Many rows with few blocks each (prefill rows): one row per wave.  The
+// wave loads its row's q fragments and 32 representatives per pass (two
+// groups of 16, lane column c = block), sums ReLU(q . rep) over its blocks,
+// then ranks the heads itself, as route_finish does for a workgroup; no
+// workgroup barrier.  (One row per 256-thread workgroup left three of its
+// waves idle at 32 blocks and paid the row's load latency 4096 times.)
+template <int NHT>
+__global__ __launch_bounds__(256) void router_rows_kernel(RouterArgs a, int rows) {
+    const int lane = lane_id(), g = lane >> 4, c = lane & 15;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = blockIdx.x * 4 + wid;
+    if (row >= rows) return;  // wave-uniform
+    const int b = row / a.T;
+    const int t = a.offset + (row - b * a.T);
+    const int Mt = min(t / a.B + 1, a.nblk);
+    const uint16_t* reps = a.reps + (long long)b * a.seq_stride;
+    const uint16_t* tailp =
+        (a.tail && a.tail_flag[row]) ? a.tail + (long long)row * 256 : nullptr;
+    QFrag<NHT> f;
+    const uint32_t qv = load_qfrag_issue<NHT>(f, a.q + (long long)row * a.H * kD,
+                                              a.w + (long long)row * a.H, a.H, nullptr, 0, g, c);
+    uint4 kb[2][8];
+    bool valid[2];
+    auto load_reps = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int m = base + 16 * u + c;
+            valid[u] = m < Mt;
+            const int ml = valid[u] ? m : Mt - 1;
+            const uint16_t* kp = (tailp && ml == Mt - 1) ? tailp : reps + (long long)ml * 256;
+            load_key<8>(kb[u], kp, g);
+        }
+    };
+    load_reps(0);
+    mask_qfrag<NHT>(f, qv);
+    float sum[NHT][4];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[ht][i] = 0.f;
+    for (int base = 0;;) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            f32x4 acc[NHT];
+            group_dots<NHT, 8>(f, kb[u], acc);
+#pragma unroll
+            for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sum[ht][i] += valid[u] ? fmaxf(acc[ht][i], 0.f) : 0.f;
+        }
+        base += 32;
+        if (base >= Mt) break;
+        load_reps(base);
+    }
+    // E_j = |w_j| * mean over the blocks; absent heads rank below every real
+    // head (E >= 0).  Lane j then ranks head j by (E desc, j asc).
+    __shared__ float sE[4][kMaxH];
+    __shared__ int sH[4][kMaxH];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = sum_row16(sum[ht][i]);
+            const int j = ht * 16 + 4 * g + i;
+            if (c == 0) sE[wid][j] = j < a.H ? fabsf(f.wv[ht][i]) * v / (float)Mt : -1.f;
+        }
+    for (int j = NHT * 16 + lane; j < kMaxH; j += 64) sE[wid][j] = -1.f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int j = lane;
+    const float E = sE[wid][j];
+    if (a.E_out && j < a.H) a.E_out[(long long)row * a.H + j] = E;
+    int rank = 0;
+#pragma unroll
+    for (int j4 = 0; j4 < kMaxH; j4 += 4) {
+        const float4 e4 = *reinterpret_cast<const float4*>(&sE[wid][j4]);
+        const float es[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            rank += (int)(es[u] > E) + (int)((es[u] == E) & (j4 + u < j));
+    }
+    const bool sel = j < a.H && rank < a.h;
+    const unsigned long long msk = __ballot(sel);
+    const int pos = __popcll(msk & ((1ull << lane) - 1ull));
+    if (sel) {
+        sH[wid][pos] = j;
+        a.heads_out[(long long)row * a.h + pos] = j;
+    }
+    if (a.qp) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int x = lane; x < a.h * 16; x += 64) {
+            const int u = x >> 4, part = x & 15;
+            const int jj = sH[wid][u];
+            const uint4 v = ldg16(a.q + ((long long)row * a.H + jj) * kD + part * 8);
+            *reinterpret_cast<uint4*>(a.qp + ((long long)row * a.h + u) * kD + part * 8) = v;
+            if (part == 0) a.wp[(long long)row * a.h + u] = a.w[(long long)row * a.H + jj];
+        }
+    }
+    if (a.zero_state)
+        for (int x = lane; x < kRowState; x += 64)
+            a.zero_state[(long long)row * kRowState + x] = 0u;
+}
+
 // ------------------------------------------------------------- tail
 
 // Causal tail of the block pooling: for a row whose last legal block is cut
@@ -816,6 +922,18 @@ hipError_t launch_gather(const GatherArgs& a, int rows, int nht, bool block_mode
 hipError_t launch_router(const RouterArgs& a, int rows, hipStream_t s) {
     const int nht = (a.H + 15) / 16;
     prof_begin(K_ROUTER, s);
+    if (rows >= 4 * cu_count()) {
+        // many rows (prefill): one row per wave
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        switch (nht) {
+            case 1: sa_launch(router_rows_kernel<1>, grid, dim3(256), 0, s, a, rows); break;
+            case 2: sa_launch(router_rows_kernel<2>, grid, dim3(256), 0, s, a, rows); break;
+            case 3: sa_launch(router_rows_kernel<3>, grid, dim3(256), 0, s, a, rows); break;
+            default: sa_launch(router_rows_kernel<4>, grid, dim3(256), 0, s, a, rows); break;
+        }
+        prof_end(K_ROUTER, s);
+        return hipGetLastError();
+    }
     switch (nht) {
         case 1: sa_launch(router_kernel<1>, dim3(rows), dim3(256), 0, s, a); break;
         case 2: sa_launch(router_kernel<2>, dim3(rows), dim3(256), 0, s, a); break;

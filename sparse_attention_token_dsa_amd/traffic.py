@@ -56,8 +56,8 @@ SCAN8_KERNEL = "scan8_kernel<4, true, false>"
 SCAN8Q_KERNEL = "scan8_kernel<4, true, true>"
 SCAN8_SOURCES = ["scan8.hip", "sa_frag.h", "sa_common.h"]
 PREFILL_SOURCES = ["prefill.hip", "sa_frag.h", "sa_common.h"]
-PREFILL_KERNEL = "prefill_kernel<4, false>"
-PREFILL8_KERNEL = "prefill_kernel<4, true>"
+PREFILL_KERNEL = "prefill_kernel<4, false, false>"
+PREFILL8_KERNEL = "prefill_kernel<4, true, false>"
 COPY_BYTES = 256 << 20
 COPY_KERNEL = "CUDAFunctorOnSelf_add<float>"  # torch.add(src, 0.0, out=dst)
 
