@@ -37,6 +37,10 @@ constexpr int kFilterThreads = 512;
 // decode rows against 10.8 us at 4096).
 constexpr int kFilterChunk = 8192;
 constexpr int kLdsCand = 4096;           // keys per LDS candidate buffer
+// Rows per CU from which the select runs 512 threads per row (16 keys per
+// thread, half-size LDS buffers, 4 waves per SIMD at 128 VGPRs: two rows per
+// CU at once) instead of 1024 (one row per CU, shorter per row).
+constexpr int kManyRows = 2;
 constexpr int kBatch = 8;                // keys per thread in flight in a pass over a source
 
 __device__ __forceinline__ unsigned long long make_key(float sc, int idx) {
@@ -175,11 +179,12 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter_kernel(TopkArgs a,
 
 enum SrcKind { SRC_DENSE = 0, SRC_LIST = 1, SRC_KEYS = 2 };
 
+template <int NT, int LC>
 struct SelShared {
     alignas(16) uint32_t hist[kHist0Bins];
-    unsigned long long lbuf[2][kLdsCand];
-    int wave[kTopkThreads / 64];
-    uint32_t wr[4 * (kTopkThreads / 64)];  // per-wave ranges, by field then wave
+    unsigned long long lbuf[2][LC];
+    int wave[NT / 64];
+    uint32_t wr[4 * (NT / 64)];  // per-wave ranges, by field then wave
     Thresh th;
     int out, cand;
 };
@@ -195,7 +200,7 @@ __device__ __forceinline__ unsigned long long src_key(int kind, const float* dsr
     return make_key(lsc[u], id);
 }
 
-// Sources of at most kRegKeys keys per thread (rescored lists, block score
+// Sources of at most kSelMax keys (rescored lists, block score
 // rows, the filter's candidates): every key is loaded once into registers,
 // all loads in flight together, and the selection runs on the registers.
 // Each level sorts the keys still in play into at most kSelBins bins by a
@@ -209,7 +214,7 @@ __device__ __forceinline__ unsigned long long src_key(int kind, const float* dsr
 // bits above the smallest; once the scores are all equal, radix digits of the
 // index part.  When at most kRankMax keys remain, each is placed by its exact
 // rank among them (a cost that grows with the square of their number).
-constexpr int kRegKeys = 8;
+constexpr int kSelMax = 8192;  // keys of a row the register-resident path holds
 constexpr int kRankMax = 256;
 constexpr int kSelBins = 1024;
 
@@ -266,12 +271,13 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
 // Each wave publishes the range of its keys in play (score order bits and
 // index part, as maxima of the value and of its complement) and their count;
 // read_range takes them after the next barrier.
+template <int NT, int NK, class SS>
 __device__ __forceinline__ void publish_range(const unsigned long long* kr, uint32_t alive,
-                                              SelShared& S) {
+                                              SS& S) {
     uint32_t omax = 0u, oinv = 0u, lmax = 0u, linv = 0u;
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kRegKeys; ++j)
+    for (int j = 0; j < NK; ++j)
         if ((alive >> j) & 1u) {
             const uint32_t o = (uint32_t)(kr[j] >> 32), l = (uint32_t)kr[j];
             omax = o > omax ? o : omax;
@@ -286,7 +292,7 @@ __device__ __forceinline__ void publish_range(const unsigned long long* kr, uint
     linv = wave_max_u32(linv);
     cnt = __builtin_amdgcn_readlane(wave_incl_scan(cnt), 63);
     if (lane_id() == 0) {
-        constexpr int NW = kTopkThreads / 64;
+        constexpr int NW = NT / 64;
         const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
         S.wr[w] = omax;
         S.wr[NW + w] = oinv;
@@ -297,37 +303,42 @@ __device__ __forceinline__ void publish_range(const unsigned long long* kr, uint
 }
 
 // Block-wide range of the keys in play, as wave-uniform values: lane l reads
-// field l / 16 of wave l % 16 (one 4-byte read per lane rather than every
-// thread reading all 64 words), each row of 16 lanes takes its maximum.
-__device__ __forceinline__ void read_range(const SelShared& S, uint32_t& omax, uint32_t& oinv,
+// word l of the 4 x NW per-wave ranges (field l / NW, wave l % NW; one 4-byte
+// read per lane rather than every thread reading them all), and each run of
+// NW lanes takes its maximum with DPP row shifts.
+template <int NW, class SS>
+__device__ __forceinline__ void read_range(const SS& S, uint32_t& omax, uint32_t& oinv,
                                            uint32_t& lmax, uint32_t& linv) {
-    static_assert(kTopkThreads / 64 == 16, "one row of 16 lanes per field");
+    static_assert(NW == 16 || NW == 8, "runs of 16 or 8 lanes per field");
     const auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
-    uint32_t x = S.wr[lane_id()];
+    uint32_t x = lane_id() < 4 * NW ? S.wr[lane_id()] : 0u;
     x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true));
     x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true));
     x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true));
-    x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
-    omax = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
-    oinv = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
-    lmax = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
-    linv = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+    if constexpr (NW == 16)
+        x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true));
+    omax = (uint32_t)__builtin_amdgcn_readlane((int)x, NW - 1);
+    oinv = (uint32_t)__builtin_amdgcn_readlane((int)x, 2 * NW - 1);
+    lmax = (uint32_t)__builtin_amdgcn_readlane((int)x, 3 * NW - 1);
+    linv = (uint32_t)__builtin_amdgcn_readlane((int)x, 4 * NW - 1);
 }
 
+template <int NT, class SS>
 __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
                                                     const float* dsrc, const float* lsc,
                                                     const int32_t* lid,
                                                     const unsigned long long* ksrc, int nsrc,
-                                                    int32_t* oidx, float* osc, SelShared& S,
+                                                    int32_t* oidx, float* osc, SS& S,
                                                     const unsigned long long* pre = nullptr,
                                                     const int* pctl = nullptr) {
+    constexpr int NK = kSelMax / NT;  // keys per thread
     const int tid = threadIdx.x, lane = lane_id();
     const int row = blockIdx.x;
-    unsigned long long kr[kRegKeys];
+    unsigned long long kr[NK];
     uint32_t alive = 0u;
 #pragma unroll
-    for (int j = 0; j < kRegKeys; ++j) {
-        const int u = tid + j * kTopkThreads;
+    for (int j = 0; j < NK; ++j) {
+        const int u = tid + j * NT;
         bool valid = u < nsrc;
         if (pre)
             kr[j] = valid ? pre[j] : 0ull;  // loaded by the caller
@@ -344,7 +355,7 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
                                                              kHist0Bins);
         need = ctl[CTL_NEED];
         const int gt = ctl[CTL_GT];
-        for (int u = need + tid; u < a.k; u += kTopkThreads) {
+        for (int u = need + tid; u < a.k; u += NT) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
@@ -354,15 +365,15 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
     } else if (tid == 0) {
         S.out = 0;
     }
-    publish_range(kr, alive, S);
+    publish_range<NT, NK>(kr, alive, S);
     // the first level's bins (two kSelBins halves of S.hist alternate)
-    for (int x = tid; x < kSelBins; x += kTopkThreads) S.hist[x] = 0u;
+    for (int x = tid; x < kSelBins; x += NT) S.hist[x] = 0u;
     lds_barrier();
-    int nalive = lane < kTopkThreads / 64 ? S.wave[lane] : 0;
+    int nalive = lane < NT / 64 ? S.wave[lane] : 0;
     nalive = __builtin_amdgcn_readlane(wave_incl_scan(nalive), 63);
     if (kind != SRC_KEYS) {
         need = min(a.k, nalive);
-        for (int u = need + tid; u < a.k; u += kTopkThreads) {
+        for (int u = need + tid; u < a.k; u += NT) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
@@ -375,7 +386,7 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
     bool slice_ok = true;
     for (;;) {
         uint32_t omax, oinv, lmax, linv;
-        read_range(S, omax, oinv, lmax, linv);
+        read_range<NT / 64>(S, omax, oinv, lmax, linv);
         const uint32_t omin = ~oinv, lmin = ~linv;
         // this level's map (uniform over the block)
         int mode;  // 0: score slices, 1: score-bit radix, 2: index-bit radix
@@ -420,7 +431,7 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
             return (v - base) >> shift;
         };
 #pragma unroll
-        for (int j = 0; j < kRegKeys; ++j)
+        for (int j = 0; j < NK; ++j)
             if ((alive >> j) & 1u) atomicAdd(&hcur[digit(j)], 1u);
         lds_barrier();
         wave0_threshold(hcur, need_rem, &S.th);
@@ -437,14 +448,14 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         };
         int wtot = 0;
 #pragma unroll
-        for (int j = 0; j < kRegKeys; ++j) wtot += __popcll(__ballot(emits(j)));
+        for (int j = 0; j < NK; ++j) wtot += __popcll(__ballot(emits(j)));
         int obase = 0;
         if (wtot) {
             if (lane == 0) obase = atomicAdd(&S.out, wtot);
             obase = __builtin_amdgcn_readlane(obase, 0);
         }
 #pragma unroll
-        for (int j = 0; j < kRegKeys; ++j) {
+        for (int j = 0; j < NK; ++j) {
             const bool e = emits(j);
             const unsigned long long m = __ballot(e);
             if (e) {
@@ -458,7 +469,7 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         }
         // keys on the threshold bin stay in play
 #pragma unroll
-        for (int j = 0; j < kRegKeys; ++j)
+        for (int j = 0; j < NK; ++j)
             if (digit(j) != d) alive &= ~(1u << j);
         need_rem -= gt;
         if (take_all) return;
@@ -469,14 +480,14 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
             lds_barrier();
             int ctot = 0;
 #pragma unroll
-            for (int j = 0; j < kRegKeys; ++j) ctot += __popcll(__ballot((alive >> j) & 1u));
+            for (int j = 0; j < NK; ++j) ctot += __popcll(__ballot((alive >> j) & 1u));
             int cbase = 0;
             if (ctot) {
                 if (lane == 0) cbase = atomicAdd(&S.cand, ctot);
                 cbase = __builtin_amdgcn_readlane(cbase, 0);
             }
 #pragma unroll
-            for (int j = 0; j < kRegKeys; ++j) {
+            for (int j = 0; j < NK; ++j) {
                 const bool al = (alive >> j) & 1u;
                 const unsigned long long cm = __ballot(al);
                 if (al) S.lbuf[0][cbase + __popcll(cm & below)] = kr[j];
@@ -484,7 +495,7 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
             }
             lds_barrier();
             const int done = need - need_rem;  // winners already written
-            for (int c = tid; c < eq; c += kTopkThreads) {
+            for (int c = tid; c < eq; c += NT) {
                 const unsigned long long key = S.lbuf[0][c];
                 int rank = 0;
                 int o = 0;
@@ -507,20 +518,23 @@ __device__ __forceinline__ void select_in_registers(const TopkArgs& a, int kind,
         if (mode == 0 && 2 * eq > nalive) slice_ok = false;
         nalive = eq;
         // the next level's bins, free since the level before this one
-        for (int x = tid; x < kSelBins; x += kTopkThreads) hnext[x] = 0u;
+        for (int x = tid; x < kSelBins; x += NT) hnext[x] = 0u;
         uint32_t* t = hcur;
         hcur = hnext;
         hnext = t;
-        publish_range(kr, alive, S);
+        publish_range<NT, NK>(kr, alive, S);
         lds_barrier();
     }
 }
 
 // mode: SRC_DENSE / SRC_LIST: full selection from level 0.
 //       SRC_KEYS: continue after topk_filter_kernel (its candidates + row state).
-__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, int kind,
+template <int NT, int LC>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4)))
+void topk_select_kernel(TopkArgs a, int kind,
                                                                    const unsigned long long* cand) {
-    __shared__ SelShared S;
+    constexpr int NK = kSelMax / NT;
+    __shared__ SelShared<NT, LC> S;
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     int32_t* oidx = a.out_idx + (long long)row * a.out_stride;
@@ -557,20 +571,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         // The register path's keys are loaded together with the count, not
         // after it (the candidate array holds cand_cap keys per row, so the
         // loads stay in bounds); those past the count are dropped.
-        unsigned long long pre[kRegKeys];
+        unsigned long long pre[NK];
 #pragma unroll
-        for (int j = 0; j < kRegKeys; ++j) {
-            const int u = tid + j * kTopkThreads;
+        for (int j = 0; j < NK; ++j) {
+            const int u = tid + j * NT;
             pre[j] = u < a.cand_cap ? ksrc[u] : 0ull;
         }
         nsrc0 = (int)min((long long)ncand, a.cand_cap);
-        if (nsrc0 <= kRegKeys * kTopkThreads) {
-            select_in_registers(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S, pre, cv);
+        if (nsrc0 <= NK * NT) {
+            select_in_registers<NT>(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S, pre, cv);
             return;
         }
     }
-    if (nsrc0 <= kRegKeys * kTopkThreads) {
-        select_in_registers(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S);
+    if (nsrc0 <= NK * NT) {
+        select_in_registers<NT>(a, kind, dsrc, lsc, lid, ksrc, nsrc0, oidx, osc, S);
         return;
     }
     if (kind == SRC_KEYS) {
@@ -578,7 +592,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
                                                       kHist0Bins);
         need = ctl[CTL_NEED];
         const int gt = ctl[CTL_GT];
-        for (int u = need + tid; u < a.k; u += kTopkThreads) {
+        for (int u = need + tid; u < a.k; u += NT) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
@@ -592,14 +606,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         if (tid == 0) S.out = gt;
         lds_barrier();
     } else {
-        for (int x = tid; x < kHist0Bins; x += kTopkThreads) S.hist[x] = 0u;
+        for (int x = tid; x < kHist0Bins; x += NT) S.hist[x] = 0u;
         lds_barrier();
-        for (int ub = 0; ub < nsrc0; ub += kTopkThreads * kBatch) {
+        for (int ub = 0; ub < nsrc0; ub += NT * kBatch) {
             unsigned long long kb[kBatch];
             bool vb[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const int u = ub + j * kTopkThreads + tid;
+                const int u = ub + j * NT + tid;
                 vb[j] = u < nsrc0;
                 kb[j] = vb[j] ? src_key(kind, dsrc, lsc, lid, nullptr, u, vb[j]) : 0ull;
             }
@@ -609,12 +623,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         }
         lds_barrier();
         int local = 0;
-        for (int j = 0; j < kHist0Bins / kTopkThreads; ++j)
-            local += (int)S.hist[tid * (kHist0Bins / kTopkThreads) + j];
+        for (int j = 0; j < kHist0Bins / NT; ++j)
+            local += (int)S.hist[tid * (kHist0Bins / NT) + j];
         int nvalid;
-        block_excl_scan<kTopkThreads>(local, S.wave, &nvalid);
+        block_excl_scan<NT>(local, S.wave, &nvalid);
         need = min(a.k, nvalid);
-        for (int u = need + tid; u < a.k; u += kTopkThreads) {
+        for (int u = need + tid; u < a.k; u += NT) {
             oidx[u] = -1;
             if (osc) osc[u] = -INFINITY;
         }
@@ -633,16 +647,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         const unsigned long long mask = (unsigned long long)(nbins - 1);
         const bool hist_ready = (level == 0);  // level-0 histogram built above
         if (!hist_ready) {
-            for (int x = tid; x < nbins; x += kTopkThreads) S.hist[x] = 0u;
+            for (int x = tid; x < nbins; x += NT) S.hist[x] = 0u;
             lds_barrier();
             // kBatch keys per thread loaded before any is used, so a pass over
             // a global source costs a few memory round trips, not one per key
-            for (int ub = 0; ub < nsrc; ub += kTopkThreads * kBatch) {
+            for (int ub = 0; ub < nsrc; ub += NT * kBatch) {
                 unsigned long long kb[kBatch];
                 bool vb[kBatch];
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
-                    const int u = ub + j * kTopkThreads + tid;
+                    const int u = ub + j * NT + tid;
                     vb[j] = u < nsrc;
                     kb[j] = 0ull;
                     if (vb[j]) {
@@ -660,20 +674,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
             }
             lds_barrier();
         }
-        find_threshold<kTopkThreads>(S.hist, nbins, need_rem, S.wave, &S.th);
+        find_threshold<NT>(S.hist, nbins, need_rem, S.wave, &S.th);
         const uint32_t d = (uint32_t)S.th.dstar;
         const int gt = S.th.gt;
         const bool take_all = gt + S.th.eq == need_rem;
-        const bool next_fits = !take_all && S.th.eq <= kLdsCand;
+        const bool next_fits = !take_all && S.th.eq <= LC;
         const int dst = cur_lds == 0 ? 1 : 0;
         if (tid == 0) S.cand = 0;
         lds_barrier();
-        for (int ub = 0; ub < nsrc; ub += kTopkThreads * kBatch) {
+        for (int ub = 0; ub < nsrc; ub += NT * kBatch) {
             unsigned long long kb[kBatch];
             bool vb[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const int u = ub + j * kTopkThreads + tid;
+                const int u = ub + j * NT + tid;
                 vb[j] = u < nsrc;
                 kb[j] = 0ull;
                 if (vb[j]) {
@@ -697,7 +711,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
                     if (osc) osc[slot] = key_score(key);
                 }
                 const int cslot = wave_append(app, &S.cand);
-                if (app && cslot < kLdsCand) S.lbuf[dst][cslot] = key;
+                if (app && cslot < LC) S.lbuf[dst][cslot] = key;
             }
         }
         lds_barrier();
@@ -707,7 +721,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkArgs a, i
         pfx_shift = shift;
         if (next_fits) {
             cur_lds = dst;
-            nsrc = min(S.cand, kLdsCand);
+            nsrc = min(S.cand, LC);
         } else {
             cur_lds = -1;
             nsrc = nsrc0;
@@ -726,7 +740,12 @@ hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     prof_begin(K_TOPK, s);
-    sa_launch(topk_select_kernel, dim3(rows), dim3(kTopkThreads), 0, s, a, SRC_KEYS, cand);
+    if (rows >= kManyRows * cu_count())
+        sa_launch(topk_select_kernel<kTopkThreads / 2, kLdsCand / 2>, dim3(rows),
+                  dim3(kTopkThreads / 2), 0, s, a, SRC_KEYS, cand);
+    else
+        sa_launch(topk_select_kernel<kTopkThreads, kLdsCand>, dim3(rows), dim3(kTopkThreads), 0,
+                  s, a, SRC_KEYS, cand);
     prof_end(K_TOPK, s);
     return hipGetLastError();
 }
@@ -735,7 +754,12 @@ hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     const int kind = a.dense ? SRC_DENSE : SRC_LIST;
     prof_begin(K_TOPK, s);
-    sa_launch(topk_select_kernel, dim3(rows), dim3(kTopkThreads), 0, s, a, kind, nullptr);
+    if (rows >= kManyRows * cu_count())
+        sa_launch(topk_select_kernel<kTopkThreads / 2, kLdsCand / 2>, dim3(rows),
+                  dim3(kTopkThreads / 2), 0, s, a, kind, nullptr);
+    else
+        sa_launch(topk_select_kernel<kTopkThreads, kLdsCand>, dim3(rows), dim3(kTopkThreads), 0,
+                  s, a, kind, nullptr);
     prof_end(K_TOPK, s);
     return hipGetLastError();
 }

@@ -339,6 +339,27 @@ def _scaled_keys(p, q_scale, key_scale):
     return p
 
 
+def test_many_rows_select(api):
+    """512 rows or more take the 512-thread select (two rows per CU): ties
+    (all keys equal) in HISA's block and token selects and in MISA-dagger's
+    rerank, then a MISA-dagger pool of 12000 keys (the general path)."""
+    say("many-row select: ties")
+    p = synth.make_problem(71, Bt=1, T=512, L=2048, H=64, offset=1536)
+    p["K"][:] = p["K"][0, 0]
+    idx, sc, blocks = run_hisa(api, p, 128, 64, 8)
+    for i in range(512):
+        assert sorted(idx[0, i].tolist()) == list(range(128))
+        assert sorted(blocks[0, i].tolist()) == list(range(8))
+    idx, sc, heads, pool = run_misa(api, p, 128, 256, 8, 512)
+    for i in range(512):
+        assert sorted(idx[0, i].tolist()) == list(range(128))
+    say("many-row select: pool over 8192 keys")
+    p = synth.make_problem(72, Bt=1, T=512, L=13000, H=64, offset=13000 - 512, needles=8,
+                           needle_mode="rows")
+    idx, sc, heads, pool = run_misa(api, p, 2048, 1024, 8, 12000)
+    check_misa(p, 2048, 1024, 8, 12000, idx, sc, heads, pool, prefill_group_rows(512, 3))
+
+
 def test_select_sources_over_8192_keys(api):
     # Sources of more than 8192 keys take the select's general path, not the
     # register-resident one: every key of a 20000-key row on the filter's
