@@ -781,8 +781,9 @@ def bench_prefill(api, synth, torch, np, dev, iters):
     t1 = time.perf_counter()
     kern = api.profile_read()
     api.profile_enable(False)
-    pairs = sum(off + i + 1 for i in range(T))          # legal (query, key) pairs
-    flops = 2.0 * pairs * H * d
+    from sparse_attention_token_dsa_amd import workload as wl
+    pairs = wl.legal_pairs(T, off)                      # legal (query, key) pairs
+    flops = 2.0 * wl.indexer_macs(pairs, H, d)
     pf_us = 1e3 * kern["prefill_fused"][0] / kern["prefill_fused"][1]
     tflops = flops / (pf_us * 1e-6) / 1e12
     return {"workload": "prefill_chunked_T4096_P28672_h64", "ms_per_call": (t1 - t0) * 1e3 / iters,
@@ -850,7 +851,8 @@ def bench_prefill_selectors(api, torch, dev, q, w, K, shape, iters, pairs, dsa_m
         out[name] = {"ms_per_call": ms, "dsa_over_this": dsa_ms / ms,
                      "kernels_us": {n: round(1e3 * t / c, 2) for n, (t, c) in kern.items()}}
     # the routed prefill's own contraction: h heads per legal pair
-    flops = 2.0 * pairs * h * d
+    from sparse_attention_token_dsa_amd import workload as wl
+    flops = 2.0 * wl.misa_macs(pairs, h, d)
     us = out["misa"]["kernels_us"].get("prefill_fused")
     if us:
         tf = flops / (us * 1e-6) / 1e12
