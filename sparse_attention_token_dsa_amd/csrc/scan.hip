@@ -844,7 +844,16 @@ int cu_count() {
 }
 
 int scan_chunk(int ksteps, long long rows, int maxn) {
-    if (ksteps != 4) return scan_waves<8>() * 16 * scan_groups<8>();
+    if (ksteps != 4) {
+        // Block representatives: one step per workgroup for few rows; a
+        // row's whole block range per workgroup once rows alone give 8
+        // workgroups per CU (prefill rows: the query fragments are loaded
+        // once per row instead of once per 128 blocks).
+        constexpr int step8 = scan_waves<8>() * 16 * scan_groups<8>();
+        if (rows >= 8LL * cu_count())
+            return std::min(kScanMaxChunk, (maxn + step8 - 1) / step8 * step8);
+        return step8;
+    }
     constexpr int step = scan_waves<4>() * 16 * scan_groups<4>();
     const long long wgs = cu_count();
     long long c = (rows * (long long)maxn + wgs - 1) / wgs;
@@ -868,12 +877,21 @@ hipError_t launch_scan(const ScanArgs& a, int rows, int nht, int ksteps, bool ro
             case 3: scan_dispatch_keys<3>(a, grid, s); break;
             default: scan_dispatch_keys<4>(a, grid, s); break;
         }
-    } else {
+    } else if (a.chunk == scan_waves<8>() * 16 * scan_groups<8>()) {
+        // one step per workgroup: the loop unrolled to that step
         switch (nht) {
             case 1: scan_dispatch_hist<1, 8, 1>(a, grid, s); break;
             case 2: scan_dispatch_hist<2, 8, 1>(a, grid, s); break;
             case 3: scan_dispatch_hist<3, 8, 1>(a, grid, s); break;
             default: scan_dispatch_hist<4, 8, 1>(a, grid, s); break;
+        }
+    } else {
+        // a row's whole block range: the stepping loop
+        switch (nht) {
+            case 1: scan_dispatch_hist<1, 8, 0>(a, grid, s); break;
+            case 2: scan_dispatch_hist<2, 8, 0>(a, grid, s); break;
+            case 3: scan_dispatch_hist<3, 8, 0>(a, grid, s); break;
+            default: scan_dispatch_hist<4, 8, 0>(a, grid, s); break;
         }
     }
     prof_end(kid, s);

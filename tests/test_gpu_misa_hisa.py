@@ -49,6 +49,21 @@ def test_misa_hisa(api, Bt, T, L, offset, H, B, h, b, r, k):
     check_misa_hisa(p, k, B, h, b, r, _np(idx), _np(sc), _np(heads), _np(blocks), rows_of(p))
 
 
+def test_misa_hisa_many_prefill_rows(api):
+    # 2048 prefill rows: a router row per wave, the routed block scores with
+    # a row's whole block range per workgroup, the rescoring sweeping each
+    # row's list and the 512-thread selects; one row of each 8-row group.
+    say("misa x hisa T=2048 L=8192")
+    from parity import prefill_group_rows
+    p = synth.make_problem(913, Bt=1, T=2048, L=8192, H=64, offset=8192 - 2048, needles=8,
+                           needle_mode="rows")
+    q, w, K = to_device(p, DEV)
+    idx, sc, heads, blocks = api.misa_hisa(q, w, K, p["offset"], 512, 1024, 8, 128, 16)
+    torch.cuda.synchronize()
+    check_misa_hisa(p, 512, 1024, 8, 128, 16, _np(idx), _np(sc), _np(heads), _np(blocks),
+                    prefill_group_rows(2048, 4))
+
+
 def test_misa_hisa_all_heads_is_hisa(api):
     say("misa x hisa h = H")
     p = synth.make_problem(911, Bt=2, T=1, L=6000, H=64, needles=8, needle_mode="hisa")
