@@ -730,6 +730,75 @@ void topk_select_kernel(TopkArgs a, int kind,
     }
 }
 
+// ------------------------------------------------------ one wave per row
+
+// Many rows with short sources (prefill rows' block scores, short lists):
+// one wave selects one row, KPL keys per lane, with no barrier and no LDS.
+// The need-th largest key T is found bit by bit from the top: T | bit stays
+// when at least need keys are >= it (a count of ballots per step); the keys
+// are distinct, so exactly need keys are >= T and those are emitted.  Four
+// rows per 256-thread workgroup.
+template <int KPL>
+__global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a, int kind, int rows) {
+    const int lane = lane_id();
+    const int row = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    const float* dsrc = nullptr;
+    const float* lsc = nullptr;
+    const int32_t* lid = nullptr;
+    int nsrc;
+    if (kind == SRC_LIST) {
+        nsrc = a.list_count ? a.list_count[row] : a.list_cap;
+        nsrc = max(0, min(nsrc, a.list_cap));
+        lsc = a.list_score + (long long)row * a.list_stride;
+        lid = a.list_idx + (long long)row * a.list_stride;
+    } else {
+        nsrc = dense_len(a, row);
+        dsrc = a.dense + (long long)row * a.dense_stride;
+    }
+    unsigned long long kr[KPL];
+    uint32_t alive = 0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const int u = lane + 64 * j;
+        bool valid = u < nsrc;
+        kr[j] = valid ? src_key(kind, dsrc, lsc, lid, nullptr, u, valid) : 0ull;
+        if (valid) alive |= 1u << j;
+    }
+    int nvalid = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) nvalid += __popcll(__ballot((alive >> j) & 1u));
+    const int need = min(a.k, nvalid);
+    int32_t* oidx = a.out_idx + (long long)row * a.out_stride;
+    float* osc = a.out_score ? a.out_score + (long long)row * a.out_stride : nullptr;
+    for (int u = need + lane; u < a.k; u += 64) {
+        oidx[u] = -1;
+        if (osc) osc[u] = -INFINITY;
+    }
+    if (need <= 0) return;
+    unsigned long long T = 0ull;
+    for (int bit = 63; bit >= 0; --bit) {
+        const unsigned long long cand = T | (1ull << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(((alive >> j) & 1u) && kr[j] >= cand));
+        if (cnt >= need) T = cand;
+    }
+    const unsigned long long below = (1ull << lane) - 1ull;
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+        const bool e = ((alive >> j) & 1u) && kr[j] >= T;
+        const unsigned long long m = __ballot(e);
+        if (e) {
+            const int slot = base + __popcll(m & below);
+            oidx[slot] = key_idx(kr[j]);
+            if (osc) osc[slot] = key_score(kr[j]);
+        }
+        base += __popcll(m);
+    }
+}
+
 hipError_t launch_topk_dense_filtered(const TopkArgs& a, int rows, int maxn,
                                       unsigned long long* cand, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
@@ -754,7 +823,17 @@ hipError_t launch_topk(const TopkArgs& a, int rows, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     const int kind = a.dense ? SRC_DENSE : SRC_LIST;
     prof_begin(K_TOPK, s);
-    if (rows >= kManyRows * cu_count())
+    const int maxsrc = a.dense ? a.len_cap : a.list_cap;
+    if (rows >= kManyRows * cu_count() && maxsrc <= 64 * 16) {
+        // short sources of many rows: a wave per row
+        const dim3 grid((unsigned)((rows + 3) / 4));
+        if (maxsrc <= 64 * 4)
+            sa_launch(topk_wave_kernel<4>, grid, dim3(256), 0, s, a, kind, rows);
+        else if (maxsrc <= 64 * 8)
+            sa_launch(topk_wave_kernel<8>, grid, dim3(256), 0, s, a, kind, rows);
+        else
+            sa_launch(topk_wave_kernel<16>, grid, dim3(256), 0, s, a, kind, rows);
+    } else if (rows >= kManyRows * cu_count())
         sa_launch(topk_select_kernel<kTopkThreads / 2, kLdsCand / 2>, dim3(rows),
                   dim3(kTopkThreads / 2), 0, s, a, kind, nullptr);
     else
