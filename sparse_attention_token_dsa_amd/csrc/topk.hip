@@ -776,13 +776,33 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(TopkArgs a, int kind, in
         if (osc) osc[u] = -INFINITY;
     }
     if (need <= 0) return;
-    unsigned long long T = 0ull;
-    for (int bit = 63; bit >= 0; --bit) {
+    // The bits above the highest one where the largest and the smallest key
+    // differ are common to every key; the search starts below them and ends
+    // as soon as exactly need keys are at or above the candidate.
+    unsigned long long kmax = 0ull, kmin = ~0ull;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+        if ((alive >> j) & 1u) {
+            kmax = kr[j] > kmax ? kr[j] : kmax;
+            kmin = kr[j] < kmin ? kr[j] : kmin;
+        }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const unsigned long long xm = __shfl_xor(kmax, o), xn = __shfl_xor(kmin, o);
+        kmax = xm > kmax ? xm : kmax;
+        kmin = xn < kmin ? xn : kmin;
+    }
+    const unsigned long long diff = kmax ^ kmin;
+    const int top = diff ? 63 - __clzll(diff) : -1;
+    unsigned long long T = top >= 63 ? 0ull : kmax & ~((2ull << top) - 1ull);
+    if (top < 0) T = kmax;  // a single key
+    for (int bit = top; bit >= 0; --bit) {
         const unsigned long long cand = T | (1ull << bit);
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(((alive >> j) & 1u) && kr[j] >= cand));
         if (cnt >= need) T = cand;
+        if (cnt == need) break;
     }
     const unsigned long long below = (1ull << lane) - 1ull;
     int base = 0;
